@@ -1,0 +1,238 @@
+"""Plain, slow, fp64 CPU oracle for gated delta-rule linear attention.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the package smoke check and the
+benchmark's CPU-baseline leg may import or run anything in this directory.  The
+product path (the HIP library and its Python binding) never calls it, shares no
+code with it, and fails loudly when its own native library is missing.
+
+What is computed, and where the pages say so
+--------------------------------------------
+Pages cited (by title and section):
+  [DD]  "Deep Dive: The Next Generation of Ultra-Long Context Sparse MoE LLMs",
+        sec. 3.2 (chunked parallelism, 16-token tiles, intra-chunk parallel /
+        inter-chunk recursion) and sec. 3.3 (bounded decay, g_min = -5).
+  [CT]  "Core Technologies Behind Ultra-Long-Context Sparse MoE Large Models",
+        sec. 2.1 (fixed-size matrix state, per-token decay, diagonal and
+        off-diagonal tiles) and sec. 2.2 (scaled-sigmoid log-decay).
+  [TS]  "How Trillion-Scale Sparse MoE Models Achieve Million-Token Long
+        Context", sec. 3.1 (states propagate between chunks) and sec. 3.2
+        (g = g_min * sigmoid(u), exp(-g) in [1, ~148]).
+  [EV]  "Evaluating Next-Gen Sparse MoE and Long-Context LLMs", sec. 2 item 2
+        (incremental linear attention: a fixed-size matrix state updated token
+        by token with a delta rule; new information written, old information
+        diluted by a data-dependent decay) and item 3 (bounded log-decay).
+
+The pages name the delta rule and the data-dependent decay but do not print the
+update.  The reading taken here is the plain gated delta rule, per (batch,
+head), with a scalar log-decay g_t and a scalar write strength beta_t:
+
+    S_t = exp(g_t) * S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+    o_t = S_t q_t
+
+S_t is d_v x d_k.  Every array here stores its transpose h_t = S_t^T
+(d_k rows, d_v columns), so the same update reads
+
+    h_t = exp(g_t) (h_{t-1} - beta_t k_t (k_t^T h_{t-1})) + beta_t k_t v_t^T
+    o_t = h_t^T q_t
+
+Decay multiplies the erased old state; the new write is not decayed at its own
+step; the output reads the state after the step's update; there is no query
+scale.  The log-decay is the bounded parameterisation g = -G * sigmoid(x) with
+G = 5 ([DD] 3.3, [CT] 2.2, [TS] 3.2, [EV] 2.3).
+
+Functions and their pins (the tests that tie each to something other than
+itself are in tests/test_oracle.py):
+  bounded_gate     values printed on the pages (exp(-5) ~ 0.0067, exp(5) ~ 148,
+                   g in [-5, 0]) and the sigmoid reflection identity.
+  recurrent_fwd    a hand-worked example, a pure-Python brute force in the
+                   S orientation, closed forms (pure decay, orthogonal keys =
+                   masked gated linear attention), invariants (identity step,
+                   write-then-query, split invariance, linearity, norm bound).
+  decode_step      equals recurrent_fwd applied one token at a time.
+  chunked_fwd      equals recurrent_fwd for chunk sizes 1, 3, 16 and 32 (two
+                   independent formulations of the same definition).
+Every function is pinned; none is "parity unpinned".
+
+Layouts (row-major, as the library uses them):
+  q, k  [B, T, H, Dk]    v, o  [B, T, H, Dv]    g, beta  [B, T, H]
+  h0, hT  [B, H, Dk, Dv]  (h = S^T)
+Everything is computed in float64 from the exact values given.
+"""
+
+from __future__ import annotations
+
+import multiprocessing as _mp
+import os
+
+import numpy as np
+
+__all__ = [
+    "bounded_gate",
+    "recurrent_fwd",
+    "decode_step",
+    "chunked_fwd",
+    "recurrent_fwd_heads",
+]
+
+
+def _f64(a):
+    return np.asarray(a, dtype=np.float64)
+
+
+# ----------------------------------------------------------------------------
+# Bounded log-decay.  [DD] 3.3, [CT] 2.2, [TS] 3.2, [EV] 2.3: the log-decay is
+# g_min * sigmoid(.) with g_min = -5, so g lies in [-5, 0] and exp(g) in
+# [exp(-5), 1].
+# ----------------------------------------------------------------------------
+def sigmoid(x):
+    """Logistic function 1 / (1 + exp(-x)) in fp64, evaluated without overflow."""
+    x = _f64(x)
+    out = np.empty_like(x)
+    pos = x >= 0
+    out[pos] = 1.0 / (1.0 + np.exp(-x[pos]))
+    ex = np.exp(x[~pos])
+    out[~pos] = ex / (1.0 + ex)
+    return out
+
+
+def bounded_gate(x, G: float = 5.0):
+    """g = -G * sigmoid(x), the scaled-sigmoid log-decay ([DD] 3.3, [CT] 2.2)."""
+    return -float(G) * sigmoid(x)
+
+
+# ----------------------------------------------------------------------------
+# Token-by-token recurrence ([EV] sec. 2 item 2: fixed-size matrix state,
+# delta-rule write, data-dependent decay).  This is the definition; it is the
+# oracle for every parity test.
+# ----------------------------------------------------------------------------
+def recurrent_fwd(q, k, v, g, beta, h0=None):
+    """Run the gated delta rule over T tokens for every (batch, head).
+
+    Returns (o [B,T,H,Dv], hT [B,H,Dk,Dv]) in float64.  h0 = None means a zero
+    initial state.
+    """
+    q, k, v, g, beta = map(_f64, (q, k, v, g, beta))
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    h = np.zeros((B, H, Dk, Dv)) if h0 is None else _f64(h0).copy()
+    o = np.empty((B, T, H, Dv))
+    for t in range(T):
+        kt = k[:, t]                                        # [B,H,Dk]
+        vt = v[:, t]                                        # [B,H,Dv]
+        a = np.exp(g[:, t])[:, :, None, None]               # decay exp(g_t)
+        b = beta[:, t][:, :, None, None]                    # write strength
+        kh = np.einsum("bhk,bhkv->bhv", kt, h)              # k_t^T h_{t-1}
+        erased = h - b * kt[:, :, :, None] * kh[:, :, None, :]
+        h = a * erased + b * kt[:, :, :, None] * vt[:, :, None, :]
+        o[:, t] = np.einsum("bhk,bhkv->bhv", q[:, t], h)    # h_t^T q_t
+    return o, h
+
+
+def decode_step(q, k, v, g, beta, S):
+    """One token of the same recurrence for every (batch, head).
+
+    q, k [B,H,Dk]; v [B,H,Dv]; g, beta [B,H]; S [B,H,Dk,Dv] (the state, stored as
+    h = S^T).  Returns (o [B,H,Dv], S_new); the input S is not modified.
+    """
+    q, k, v, g, beta, S = map(_f64, (q, k, v, g, beta, S))
+    o, hT = recurrent_fwd(q[:, None], k[:, None], v[:, None], g[:, None],
+                          beta[:, None], S)
+    return o[:, 0], hT
+
+
+# ----------------------------------------------------------------------------
+# Chunked (tiled) form.  [DD] 3.2: tiles of 16 tokens, parallel inside a tile,
+# recursive between tiles.  [CT] 2.1: diagonal blocks carry the in-tile
+# token interactions, off-diagonal blocks the "historical state -> current
+# token" flow.  [TS] 3.1: the recurrent state propagates between chunks.
+#
+# Derived from the recurrence (the pages do not print it).  Inside a chunk
+# that starts from state H, with G_t the in-chunk running sum of g and
+# gamma_t = exp(G_t), write u_t = beta_t (v_t - exp(g_t) h_{t-1}^T k_t).  Then
+# h_t = exp(g_t) h_{t-1} + k_t u_t^T, and stacking the u_t of the chunk:
+#     (I + A) U = diag(beta) V - diag(beta*gamma) K H,
+#     A[t, s] = beta_t exp(G_t - G_s) k_t . k_s   for s < t (0 otherwise),
+#     O       = diag(gamma) Q H + P U,  P[t, s] = exp(G_t - G_s) q_t . k_s, s <= t
+#     H_next  = gamma_C H + K~^T U,     K~[s]   = exp(G_C - G_s) k_s.
+# Only exp of a non-positive number is formed.  The triangular system is solved
+# with a library solver (one step, no blocking of our own).
+# ----------------------------------------------------------------------------
+def chunked_fwd(q, k, v, g, beta, h0=None, chunk: int = 16):
+    """Same result as recurrent_fwd, computed chunk by chunk in fp64."""
+    q, k, v, g, beta = map(_f64, (q, k, v, g, beta))
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    C = int(chunk)
+    # (B,T,H,.) -> (B,H,T,.)
+    qh, kh, vh = (np.moveaxis(a, 2, 1) for a in (q, k, v))
+    gh, bh = np.moveaxis(g, 2, 1), np.moveaxis(beta, 2, 1)
+    Hs = np.zeros((B, H, Dk, Dv)) if h0 is None else _f64(h0).copy()
+    o = np.empty((B, H, T, Dv))
+    for c0 in range(0, T, C):
+        c1 = min(T, c0 + C)
+        n = c1 - c0
+        Q, K, V = qh[:, :, c0:c1], kh[:, :, c0:c1], vh[:, :, c0:c1]
+        beta_c = bh[:, :, c0:c1]
+        Gc = np.cumsum(gh[:, :, c0:c1], axis=-1)            # in-chunk cumsum
+        gam = np.exp(Gc)
+        diff = Gc[..., :, None] - Gc[..., None, :]          # G_t - G_s
+        lower_strict = np.tril(np.ones((n, n)), -1)
+        lower_incl = np.tril(np.ones((n, n)), 0)
+        dec = np.exp(np.where(lower_incl > 0, diff, -np.inf))
+        KK = K @ np.swapaxes(K, -1, -2)
+        QK = Q @ np.swapaxes(K, -1, -2)
+        A = beta_c[..., :, None] * dec * KK * lower_strict
+        P = dec * QK
+        rhs = beta_c[..., None] * V - (beta_c * gam)[..., None] * (K @ Hs)
+        U = np.linalg.solve(np.eye(n) + A, rhs)
+        o[:, :, c0:c1] = gam[..., None] * (Q @ Hs) + P @ U
+        ktil = np.exp(Gc[..., -1:] - Gc)[..., None] * K
+        Hs = np.exp(Gc[..., -1])[..., None, None] * Hs + np.swapaxes(ktil, -1, -2) @ U
+    return np.moveaxis(o, 1, 2), Hs
+
+
+# ----------------------------------------------------------------------------
+# Runner over independent (batch, head) streams on host cores.  Each stream is
+# the same recurrent_fwd on a [1, T, 1, .] slice; the streams share nothing,
+# so a process pool gives the same numbers as one call.
+# ----------------------------------------------------------------------------
+_POOL_DATA = None
+
+
+def _run_one(args):
+    b, h, t0, t1 = args
+    q, k, v, g, beta, h0 = _POOL_DATA
+    sl = (slice(b, b + 1), slice(t0, t1), slice(h, h + 1))
+    init = None if h0 is None else h0[b:b + 1, h:h + 1]
+    o, hT = recurrent_fwd(q[sl], k[sl], v[sl], g[sl], beta[sl], init)
+    return o[0, :, 0], hT[0, 0]
+
+
+def recurrent_fwd_heads(q, k, v, g, beta, h0=None, heads=None, t_range=None,
+                        workers: int | None = None):
+    """recurrent_fwd on selected (b, h) streams, optionally over tokens [t0, t1).
+
+    heads: list of (b, h); default all.  t_range: (t0, t1) with h0 taken as the
+    state before token t0.  Returns {(b, h): (o [t1-t0, Dv], hT [Dk, Dv])}.
+    workers: processes to use (default: all cores, capped by the stream count).
+    """
+    global _POOL_DATA
+    B, T, H, _ = np.shape(q)
+    if heads is None:
+        heads = [(b, h) for b in range(B) for h in range(H)]
+    t0, t1 = (0, T) if t_range is None else t_range
+    jobs = [(b, h, t0, t1) for (b, h) in heads]
+    if workers is None:
+        workers = os.cpu_count() or 1
+    workers = max(1, min(int(workers), len(jobs)))
+    _POOL_DATA = (q, k, v, g, beta, h0)
+    try:
+        if workers == 1:
+            res = [_run_one(j) for j in jobs]
+        else:
+            ctx = _mp.get_context("fork")
+            with ctx.Pool(workers) as pool:
+                res = pool.map(_run_one, jobs, chunksize=1)
+    finally:
+        _POOL_DATA = None
+    return {(b, h): r for (b, h, _, _), r in zip(jobs, res)}
