@@ -1,0 +1,186 @@
+"""Benchmark: chunked gated delta-rule linear-attention forward on one MI355X.
+
+A step is one pass of the whole forward path (bounded gate from logits, the
+in-tile cumulative decay, intra-tile products and solve, state propagation,
+outputs and final state) over one batch of synthetic input resident in HBM.
+Default workload: B=1, H=16, T=65536, d_k=d_v=128, bf16 q/k/v, fp32 gates and
+state, 16-token tiles.  Prints ONE JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload long_64k]
+                    [--decode-steps 1000] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tokens/s + % bf16 MFMA peak, chunked linear-attn fwd H=16 d=128 T=64K"
+PEAK_HBM = 8.0e12           # bytes/s, MI355X HBM3E
+PEAK_BF16 = 2.5e15          # dense bf16 MFMA flop/s (published figure)
+CHUNK = 16
+
+
+def alg_counts(B, T, H, Dk, Dv, ebytes=2, h0=False):
+    """Algorithmic flops and compulsory HBM bytes of one forward call.
+
+    flops/token/head = 6 Dk Dv (state products K H, Q H, K^T U) +
+                       2 C (3 Dk + 2 Dv) (in-tile K K^T, Q K^T, T-products, P U)
+    bytes/token/head = ebytes (2 Dk + Dv) in + ebytes Dv out + 8 (gate, beta fp32)
+    plus the final state (and h0 when given) once per head, fp32.
+    """
+    toks = B * T * H
+    flops = toks * (6 * Dk * Dv + 2 * CHUNK * (3 * Dk + 2 * Dv))
+    byts = toks * (ebytes * (2 * Dk + Dv) + ebytes * Dv + 8)
+    byts += B * H * Dk * Dv * 4 * (2 if h0 else 1)
+    return flops, byts
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="long_64k")
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=65536,
+                    help="tokens per head in the CPU-baseline sample")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(heads and batch would shard across GPUs with no exchange; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from chunked_gated_linear_amd import inputs as I
+    from chunked_gated_linear_amd import lin_attn_chunk_fwd, lin_attn_decode_step
+
+    wl = dict(I.WORKLOADS[args.workload])
+    B, H, T, Dk, Dv, dtype = wl["B"], wl["H"], wl["T"], wl["Dk"], wl["Dv"], wl["dtype"]
+    h0_std = wl.get("h0_std")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = I.make_inputs(B, T, H, Dk, Dv, dtype=dtype, seed=1002, device=dev, h0_std=h0_std)
+    o = torch.empty((B, T, H, Dv), dtype=inp["q"].dtype, device=dev)
+    hT = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev)
+
+    def step():
+        lin_attn_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["x"], inp["beta"], inp["h0"],
+                           gate_mode="logit", G=5.0, o=o, hT=hT)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)          # the stream the kernels run on
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    t = ms * 1e-3
+    ebytes = 2 if dtype == "bf16" else 4
+    flops, byts = alg_counts(B, T, H, Dk, Dv, ebytes, h0_std is not None)
+    tokens_per_s = B * T / t
+
+    result = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "H": H, "T": T, "d_k": Dk, "d_v": Dv,
+                   "chunk": CHUNK, "gate": "bounded logit, x ~ N(0,1), G=5",
+                   "h0": "N(0,0.02)" if h0_std else "zero"},
+        "mfma_pct_of_bf16_peak": 100.0 * flops / t / PEAK_BF16,
+        "tflops": flops / t / 1e12,
+        "roofline": {"bound": "hbm", "achieved": byts / t / 1e9, "peak": PEAK_HBM / 1e9,
+                     "unit": "GB/s", "frac": byts / t / PEAK_HBM, "traffic": None,
+                     "kernel": "chunk_fwd_kernel", "alg_bytes_per_launch": byts,
+                     "alg_flops_per_launch": flops,
+                     "attainable_frac": max(byts / PEAK_HBM, flops / PEAK_BF16) / t},
+    }
+
+    # ---- decode: B=256, H=32, d=128, fresh token every step, state in place
+    if args.decode_steps > 0:
+        dw = I.DECODE_WORKLOAD
+        dB, dH, dD = dw["B"], dw["H"], dw["Dk"]
+        n = args.decode_steps
+        d = I.make_decode_inputs(dB, dH, dD, dD, dtype=dw["dtype"], seed=1004, device=dev,
+                                 steps=n)
+        S = d["S"]
+        od = torch.empty((dB, dH, dD), dtype=d["q"].dtype, device=dev)
+        for s in range(min(3, n)):
+            lin_attn_decode_step(d["q"][s], d["k"][s], d["v"][s], d["x"][s], d["beta"][s], S,
+                                 gate_mode="logit", o=od)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for s in range(n):
+            lin_attn_decode_step(d["q"][s], d["k"][s], d["v"][s], d["x"][s], d["beta"][s], S,
+                                 gate_mode="logit", o=od)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dms = e0.elapsed_time(e1) / n
+        per_head = 2 * dD * dD * 4 + 3 * dD * 2 + dD * 2 + 8
+        dbytes = dB * dH * per_head
+        result["decode"] = {
+            "workload": f"B={dB} H={dH} d={dD} bf16, fp32 state in place, {n} steps",
+            "us_per_step": dms * 1e3, "tokens_per_s": dB / (dms * 1e-3),
+            "roofline": {"bound": "hbm", "achieved": dbytes / (dms * 1e-3) / 1e9,
+                         "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                         "frac": dbytes / (dms * 1e-3) / PEAK_HBM,
+                         "alg_bytes_per_launch": dbytes, "kernel": "decode_kernel"},
+        }
+        del d, S
+
+    # ---- CPU baseline: the fp64 oracle (plain C recurrence) on host cores
+    if not args.no_cpu_baseline:
+        from oracle import c_recurrent as crec
+        from oracle import linattn_oracle as orc
+
+        S_tok = min(T, args.cpu_tokens)
+        f = lambda x: x.detach().float().cpu().numpy()
+        q, k, v = f(inp["q"][:, :S_tok]), f(inp["k"][:, :S_tok]), f(inp["v"][:, :S_tok])
+        x, beta = f(inp["x"][:, :S_tok]), f(inp["beta"][:, :S_tok]).astype(np.float64)
+        h0 = None if inp["h0"] is None else f(inp["h0"]).astype(np.float64)
+        workers = min(16, os.cpu_count() or 1, B * H)
+        c0 = time.perf_counter()
+        g = orc.bounded_gate(x.astype(np.float64))
+        res = crec.recurrent_fwd_c(q, k, v, g, beta, h0, workers=workers)
+        cpu_s = time.perf_counter() - c0
+        result["cpu_baseline"] = {
+            "value": B * S_tok / cpu_s, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "sample": f"all {B * H} heads, first {S_tok} of {T} tokens (fp64 C recurrence, "
+                      f"one thread per head stream), {cpu_s:.1f} s wall"}
+        if S_tok == T:   # the sample is the whole workload: compare every output
+            oh, hh = f(o), f(hT)
+            eo = max(np.max(np.abs(oh[b, :, h] - r[0])) for (b, h), r in res.items())
+            eh = max(np.max(np.abs(hh[b, h] - r[1])) for (b, h), r in res.items())
+            so = max(np.max(np.abs(r[0])) for r in res.values())
+            sh = max(np.max(np.abs(r[1])) for r in res.values())
+            result["parity"] = {"err_o": float(eo / so), "err_hT": float(eh / sh), "tol": 1e-2}
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,10 @@
+"""Gated delta-rule linear attention for AMD Instinct MI355X (gfx950).
+
+The work runs in hand-written HIP kernels behind a C ABI (include/lin_attn.h,
+built into liblinattn.so); this package only marshals torch tensors into it.
+"""
+
+from .api import lin_attn_chunk_fwd, lin_attn_decode_step, lin_attn_gate  # noqa: F401
+from ._native import LinAttnError, lib  # noqa: F401
+
+__all__ = ["lin_attn_chunk_fwd", "lin_attn_decode_step", "lin_attn_gate", "LinAttnError", "lib"]

@@ -1,0 +1,96 @@
+"""Python entry points with the C ABI's names.  Argument marshalling only:
+every step of the computation runs in the library's HIP kernels.
+
+Tensors are torch tensors on the GPU (PyTorch supplies device memory and the
+current stream); shapes and layouts are those of include/lin_attn.h.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import _native as N
+
+_DTYPES = {torch.bfloat16: N.LA_BF16, torch.float32: N.LA_FP32}
+_GATE = {"log": N.LA_GATE_LOG, "logit": N.LA_GATE_BOUNDED_LOGIT}
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t, name, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _stream(t, stream):
+    s = stream if stream is not None else torch.cuda.current_stream(t.device)
+    return s.cuda_stream
+
+
+def lin_attn_chunk_fwd(q, k, v, gate, beta, h0=None, *, gate_mode="log", G=5.0,
+                       o=None, hT=None, output_final_state=True, stream=None):
+    """o [B,T,H,Dv] and final state hT [B,H,Dk,Dv] (None if not requested)."""
+    _need(q, "q")
+    if q.dtype not in _DTYPES:
+        raise TypeError("q, k, v must be bfloat16 or float32")
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    _need(k, "k", q.dtype, (B, T, H, Dk))
+    _need(v, "v", q.dtype, (B, T, H, Dv))
+    _need(gate, "gate", torch.float32, (B, T, H))
+    _need(beta, "beta", torch.float32, (B, T, H))
+    if h0 is not None:
+        _need(h0, "h0", torch.float32, (B, H, Dk, Dv))
+    if o is None:
+        o = torch.empty((B, T, H, Dv), dtype=q.dtype, device=q.device)
+    _need(o, "o", q.dtype, (B, T, H, Dv))
+    if hT is None and output_final_state:
+        hT = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    if hT is not None:
+        _need(hT, "hT", torch.float32, (B, H, Dk, Dv))
+    N.check(N.lib().lin_attn_chunk_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _GATE[gate_mode], float(G), _ptr(beta),
+        _ptr(h0), _ptr(o), _ptr(hT), B, T, H, Dk, Dv, _DTYPES[q.dtype], _stream(q, stream)))
+    return o, hT
+
+
+def lin_attn_decode_step(q, k, v, gate, beta, S, *, gate_mode="log", G=5.0, o=None,
+                         stream=None):
+    """Advance S [B,H,Dk,Dv] by one token in place; returns o [B,H,Dv]."""
+    _need(q, "q")
+    if q.dtype not in _DTYPES:
+        raise TypeError("q, k, v must be bfloat16 or float32")
+    B, H, Dk = q.shape
+    Dv = v.shape[-1]
+    _need(k, "k", q.dtype, (B, H, Dk))
+    _need(v, "v", q.dtype, (B, H, Dv))
+    _need(gate, "gate", torch.float32, (B, H))
+    _need(beta, "beta", torch.float32, (B, H))
+    _need(S, "S", torch.float32, (B, H, Dk, Dv))
+    if o is None:
+        o = torch.empty((B, H, Dv), dtype=q.dtype, device=q.device)
+    _need(o, "o", q.dtype, (B, H, Dv))
+    N.check(N.lib().lin_attn_decode_step(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _GATE[gate_mode], float(G), _ptr(beta),
+        _ptr(S), _ptr(o), B, H, Dk, Dv, _DTYPES[q.dtype], _stream(q, stream)))
+    return o
+
+
+def lin_attn_gate(x, G=5.0, out=None, stream=None):
+    """g = -G * sigmoid(x), float32, same shape as x."""
+    _need(x, "x", torch.float32)
+    if out is None:
+        out = torch.empty_like(x)
+    _need(out, "out", torch.float32, tuple(x.shape))
+    N.check(N.lib().lin_attn_gate(_ptr(x), float(G), _ptr(out), x.numel(), _stream(x, stream)))
+    return out

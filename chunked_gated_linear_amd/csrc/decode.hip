@@ -1,0 +1,169 @@
+// decode.hip -- single-token recurrent update of the d_k x d_v state, in place.
+//
+// Constant-state recurrent inference: each (b, h) advances its state by one
+// token ("Evaluating Next-Gen Sparse MoE and Long-Context LLMs", sec. 2 item 2
+// and sec. 4).  With h = S^T and a = exp(g):
+//     u   = beta * (v - a * h^T k)                      (d_v)
+//     h'  = a * h + k u^T                               (one pass over h)
+//     o   = h'^T q = a * h^T q + (k . q) u
+// so h is read once and written once; both column reductions (h^T k, h^T q)
+// come from the same register-resident copy.
+//
+// Roofline: 2 * Dk * Dv * 4 bytes of state traffic per head and step dominate
+// (about 9 * Dk * Dv flops against 8 * Dk * Dv bytes): HBM-bound.
+//
+// Layout: one 256-thread workgroup per (b, h).  Thread (rg, c4) holds columns
+// 4*c4 .. 4*c4+3 of rows rg, rg + RG, rg + 2*RG, ... as float4, so every row of
+// the state is read and written as 32 consecutive 16-byte pieces.
+#include "la_device.h"
+#include "la_launch.h"
+
+namespace la {
+
+template <typename E, int DK, int DV>
+__global__ __launch_bounds__(256) void decode_kernel(
+    const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
+    const float* __restrict__ gate, int gate_logit, float G,
+    const float* __restrict__ beta, float* __restrict__ S, E* __restrict__ o) {
+  constexpr int NC4 = DV / 4;      // float4 columns per row
+  constexpr int RG = 256 / NC4;    // row groups
+  constexpr int RPT = DK / RG;     // rows per thread
+  static_assert(RG * NC4 == 256 && RPT * RG == DK, "decode tiling");
+
+  __shared__ float sk[DK], sq[DK];
+  __shared__ float4 pa[RG][NC4], pb[RG][NC4];
+  __shared__ float su[DV];
+  __shared__ float skq;
+
+  const int64_t bh = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int c4 = tid % NC4, rg = tid / NC4;
+
+  float gx = gate[bh];
+  const float g = gate_logit ? bounded_gate(gx, G) : gx;
+  const float a = __expf(g);
+  const float bt = beta[bh];
+
+  if (tid < DK) {
+    sk[tid] = Elt<E>::to_f(k[bh * DK + tid]);
+    sq[tid] = Elt<E>::to_f(q[bh * DK + tid]);
+  }
+  float4* Sh = reinterpret_cast<float4*>(S + bh * DK * DV);
+  float4 s[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) s[i] = Sh[(rg + RG * i) * NC4 + c4];
+  __syncthreads();
+
+  float4 pk = make_float4(0.f, 0.f, 0.f, 0.f), pq = pk;
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const float kr = sk[rg + RG * i], qr = sq[rg + RG * i];
+    pk.x += kr * s[i].x; pk.y += kr * s[i].y; pk.z += kr * s[i].z; pk.w += kr * s[i].w;
+    pq.x += qr * s[i].x; pq.y += qr * s[i].y; pq.z += qr * s[i].z; pq.w += qr * s[i].w;
+  }
+  pa[rg][c4] = pk;
+  pb[rg][c4] = pq;
+  if (tid < 64) {  // k . q, one wave, fixed order
+    float p = 0.f;
+    for (int d = tid; d < DK; d += 64) p += sk[d] * sq[d];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) p += __shfl_xor(p, off);
+    if (tid == 0) skq = p;
+  }
+  __syncthreads();
+
+  if (tid < DV) {
+    const int cq = tid >> 2, cr = tid & 3;
+    float hk = 0.f, hq = 0.f;
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+      const float4 x = pa[r][cq], y = pb[r][cq];
+      hk += cr == 0 ? x.x : cr == 1 ? x.y : cr == 2 ? x.z : x.w;
+      hq += cr == 0 ? y.x : cr == 1 ? y.y : cr == 2 ? y.z : y.w;
+    }
+    const float u = bt * (Elt<E>::to_f(v[bh * DV + tid]) - a * hk);
+    su[tid] = u;
+    o[bh * DV + tid] = Elt<E>::from_f(a * hq + skq * u);
+  }
+  __syncthreads();
+
+  const float4 u4 = reinterpret_cast<const float4*>(su)[c4];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const float kr = sk[rg + RG * i];
+    float4 x = s[i];
+    x.x = a * x.x + kr * u4.x; x.y = a * x.y + kr * u4.y;
+    x.z = a * x.z + kr * u4.z; x.w = a * x.w + kr * u4.w;
+    Sh[(rg + RG * i) * NC4 + c4] = x;
+  }
+}
+
+template <typename E, int DK, int DV>
+static hipError_t launch_decode_t(const void* q, const void* k, const void* v,
+                                  const float* gate, int gate_logit, float G,
+                                  const float* beta, float* S, void* o, int BH,
+                                  hipStream_t st) {
+  hipLaunchKernelGGL((decode_kernel<E, DK, DV>), dim3(BH), dim3(256), 0, st,
+                     (const E*)q, (const E*)k, (const E*)v, gate, gate_logit, G,
+                     beta, S, (E*)o);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const void* q, const void* k, const void* v,
+                         const float* gate, int gate_logit, float G,
+                         const float* beta, float* S, void* o, int BH, int Dk,
+                         int Dv, int fp32, hipStream_t st) {
+#define LA_DEC(E, DK, DV) \
+  if (Dk == DK && Dv == DV) return launch_decode_t<E, DK, DV>(q, k, v, gate, gate_logit, G, beta, S, o, BH, st);
+  if (fp32) {
+    LA_DEC(float, 64, 64) LA_DEC(float, 64, 128) LA_DEC(float, 128, 64) LA_DEC(float, 128, 128)
+  } else {
+    LA_DEC(__bf16, 64, 64) LA_DEC(__bf16, 64, 128) LA_DEC(__bf16, 128, 64) LA_DEC(__bf16, 128, 128)
+  }
+#undef LA_DEC
+  return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------
+// Bounded log-decay on its own, g = -G * sigmoid(x) ("Deep Dive: The Next
+// Generation of Ultra-Long Context Sparse MoE LLMs", sec. 3.3).  Elementwise,
+// HBM-bound; grid-stride loop.
+__global__ __launch_bounds__(256) void gate_kernel(const float* x, float G, float* g,
+                                                   long long n) {
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    g[i] = bounded_gate(x[i], G);
+}
+
+hipError_t launch_gate(const float* x, float G, float* g, long long n, hipStream_t st) {
+  long long blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(gate_kernel, dim3((unsigned)blocks), dim3(256), 0, st, x, G, g, n);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void fill_kernel(float* p, long long n, float val) {
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    p[i] = val;
+}
+
+__global__ __launch_bounds__(256) void copy_kernel(const float* s, float* d, long long n) {
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    d[i] = s[i];
+}
+
+hipError_t launch_state_init(const float* h0, float* hT, long long n, hipStream_t st) {
+  long long blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  if (h0)
+    hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(256), 0, st, h0, hT, n);
+  else
+    hipLaunchKernelGGL(fill_kernel, dim3((unsigned)blocks), dim3(256), 0, st, hT, n, 0.0f);
+  return hipGetLastError();
+}
+
+}  // namespace la

@@ -1,0 +1,25 @@
+// la_launch.h -- internal launchers behind the C ABI (include/lin_attn.h).
+// Arguments are already validated by the caller; each returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace la {
+
+hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v,
+                            const float* gate, int gate_logit, float G,
+                            const float* beta, const float* h0, void* o, float* hT,
+                            int B, int T, int H, int Dk, int Dv, int fp32,
+                            hipStream_t st);
+
+hipError_t launch_decode(const void* q, const void* k, const void* v,
+                         const float* gate, int gate_logit, float G,
+                         const float* beta, float* S, void* o, int BH, int Dk,
+                         int Dv, int fp32, hipStream_t st);
+
+hipError_t launch_gate(const float* x, float G, float* g, long long n, hipStream_t st);
+
+// hT <- h0 (or zeros when h0 is NULL), n floats.
+hipError_t launch_state_init(const float* h0, float* hT, long long n, hipStream_t st);
+
+}  // namespace la

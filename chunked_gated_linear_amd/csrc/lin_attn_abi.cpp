@@ -1,0 +1,178 @@
+// lin_attn_abi.cpp -- the C ABI declared in include/lin_attn.h: host-side
+// argument checks, then one launch on the caller's stream.  Nothing here
+// touches the device before every check has passed.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "la_launch.h"
+#include "lin_attn.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return LA_OK;
+}
+
+struct Span {
+  const char* name;
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Span span(const char* name, const void* p, int64_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Span{name, a, a + (uintptr_t)(bytes > 0 ? bytes : 0)};
+}
+
+bool overlap(const Span& a, const Span& b) {
+  if (!a.lo || !b.lo || a.hi == a.lo || b.hi == b.lo) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned(const void* p, unsigned a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1u)) == 0; }
+
+int check_gate_scalars(int gate_mode, float G) {
+  if (gate_mode != LA_GATE_LOG && gate_mode != LA_GATE_BOUNDED_LOGIT)
+    return fail(LA_EINVAL, "gate_mode must be LA_GATE_LOG (0) or LA_GATE_BOUNDED_LOGIT (1), got %d",
+                gate_mode);
+  if (!std::isfinite(G) || G < 0.f || G > 16.f)
+    return fail(LA_ERANGE, "G must be finite and in [0, 16], got %g", (double)G);
+  return LA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(LA_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lin_attn_last_error(void) { return g_err.c_str(); }
+
+int lin_attn_version(void) { return 100; }
+
+int lin_attn_chunk_fwd(const void* q, const void* k, const void* v, const float* gate,
+                       int gate_mode, float G, const float* beta, const float* h0, void* o,
+                       float* hT, int B, int T, int H, int Dk, int Dv, int dtype,
+                       void* stream) {
+  if (B < 0 || T < 0 || H < 0)
+    return fail(LA_EINVAL, "sizes must be >= 0 (B=%d T=%d H=%d)", B, T, H);
+  if (dtype != LA_BF16 && dtype != LA_FP32)
+    return fail(LA_EINVAL, "dtype must be LA_BF16 (0) or LA_FP32 (1), got %d", dtype);
+  if (int rc = check_gate_scalars(gate_mode, G)) return rc;
+  if (Dk != 64 && Dk != 128)
+    return fail(LA_EUNSUPPORTED, "Dk must be 64 or 128, got %d", Dk);
+  if (Dv < 16 || Dv > 256 || Dv % 16 != 0)
+    return fail(LA_EUNSUPPORTED, "Dv must be a multiple of 16 in [16, 256], got %d", Dv);
+  const int64_t es = dtype == LA_BF16 ? 2 : 4;
+  const int64_t ntok = (int64_t)B * T * H;
+  const int64_t nst = (int64_t)B * H * Dk * Dv;
+  if ((int64_t)B * H * (Dv / 16) > INT32_MAX || ntok > (INT64_C(1) << 40))
+    return fail(LA_EINVAL, "problem too large (B*H*Dv/16 = %lld)",
+                (long long)((int64_t)B * H * (Dv / 16)));
+  if ((int64_t)T * H > INT32_MAX || (int64_t)B * T > INT32_MAX)
+    return fail(LA_EINVAL, "problem too large (T*H or B*T exceeds 2^31)");
+  if (B == 0 || H == 0) return ok();
+  const unsigned ea = dtype == LA_BF16 ? 2u : 4u;
+  if (T > 0) {
+    // q and k are read as 16-byte vectors; everything else element-wise
+    const struct { const char* nm; const void* p; unsigned a; } req[] = {
+        {"q", q, 16u}, {"k", k, 16u}, {"v", v, ea}, {"gate", gate, 4u}, {"beta", beta, 4u},
+        {"o", o, ea}};
+    for (const auto& r : req) {
+      if (!r.p) return fail(LA_EINVAL, "%s must not be NULL", r.nm);
+      if (!aligned(r.p, r.a)) return fail(LA_EINVAL, "%s must be %u-byte aligned", r.nm, r.a);
+    }
+  }
+  if (h0 && !aligned(h0, 4u)) return fail(LA_EINVAL, "h0 must be 4-byte aligned");
+  if (hT && !aligned(hT, 4u)) return fail(LA_EINVAL, "hT must be 4-byte aligned");
+
+  const Span sq = span("q", q, ntok * Dk * es), sk = span("k", k, ntok * Dk * es),
+             sv = span("v", v, ntok * Dv * es), sg = span("gate", gate, ntok * 4),
+             sb = span("beta", beta, ntok * 4), sh0 = span("h0", h0, nst * 4),
+             so = span("o", o, T > 0 ? ntok * Dv * es : 0), shT = span("hT", hT, nst * 4);
+  for (const Span& in : {sq, sk, sv, sg, sb, sh0, shT})
+    if (overlap(so, in)) return fail(LA_EINVAL, "o overlaps %s", in.name);
+  for (const Span& in : {sq, sk, sv, sg, sb})
+    if (overlap(shT, in)) return fail(LA_EINVAL, "hT overlaps %s", in.name);
+  if (hT && h0 && hT != h0 && overlap(shT, sh0))
+    return fail(LA_EINVAL, "hT partially overlaps h0 (only hT == h0 is allowed)");
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (T == 0) {
+    if (!hT || hT == h0) return ok();
+    return hip_status(la::launch_state_init(h0, hT, nst, st), "state init launch");
+  }
+  hipError_t e = la::launch_chunk_fwd(q, k, v, gate, gate_mode == LA_GATE_BOUNDED_LOGIT, G,
+                                      beta, h0, o, hT, B, T, H, Dk, Dv, dtype == LA_FP32, st);
+  return hip_status(e, "chunk_fwd launch");
+}
+
+int lin_attn_decode_step(const void* q, const void* k, const void* v, const float* gate,
+                         int gate_mode, float G, const float* beta, float* S, void* o, int B,
+                         int H, int Dk, int Dv, int dtype, void* stream) {
+  if (B < 0 || H < 0) return fail(LA_EINVAL, "sizes must be >= 0 (B=%d H=%d)", B, H);
+  if (dtype != LA_BF16 && dtype != LA_FP32)
+    return fail(LA_EINVAL, "dtype must be LA_BF16 (0) or LA_FP32 (1), got %d", dtype);
+  if (int rc = check_gate_scalars(gate_mode, G)) return rc;
+  if ((Dk != 64 && Dk != 128) || (Dv != 64 && Dv != 128))
+    return fail(LA_EUNSUPPORTED, "decode supports Dk, Dv in {64, 128}, got Dk=%d Dv=%d", Dk, Dv);
+  if ((int64_t)B * H > INT32_MAX) return fail(LA_EINVAL, "B*H exceeds 2^31");
+  if (B == 0 || H == 0) return ok();
+  const int64_t es = dtype == LA_BF16 ? 2 : 4;
+  // S is read and written as 16-byte vectors; everything else element-wise
+  const struct { const char* nm; const void* p; unsigned a; } req[] = {
+      {"q", q, (unsigned)es}, {"k", k, (unsigned)es}, {"v", v, (unsigned)es},
+      {"gate", gate, 4u}, {"beta", beta, 4u}, {"S", S, 16u}, {"o", o, (unsigned)es}};
+  for (const auto& r : req) {
+    if (!r.p) return fail(LA_EINVAL, "%s must not be NULL", r.nm);
+    if (!aligned(r.p, r.a)) return fail(LA_EINVAL, "%s must be %u-byte aligned", r.nm, r.a);
+  }
+  const int64_t bh = (int64_t)B * H;
+  const Span sq = span("q", q, bh * Dk * es), sk = span("k", k, bh * Dk * es),
+             sv = span("v", v, bh * Dv * es), sg = span("gate", gate, bh * 4),
+             sb = span("beta", beta, bh * 4), sS = span("S", S, bh * Dk * Dv * 4),
+             so = span("o", o, bh * Dv * es);
+  for (const Span& in : {sq, sk, sv, sg, sb, sS})
+    if (overlap(so, in)) return fail(LA_EINVAL, "o overlaps %s", in.name);
+  for (const Span& in : {sq, sk, sv, sg, sb})
+    if (overlap(sS, in)) return fail(LA_EINVAL, "S overlaps %s", in.name);
+  hipError_t e = la::launch_decode(q, k, v, gate, gate_mode == LA_GATE_BOUNDED_LOGIT, G, beta,
+                                   S, o, (int)bh, Dk, Dv, dtype == LA_FP32,
+                                   reinterpret_cast<hipStream_t>(stream));
+  return hip_status(e, "decode launch");
+}
+
+int lin_attn_gate(const float* x, float G, float* g, long long n, void* stream) {
+  if (n < 0) return fail(LA_EINVAL, "n must be >= 0, got %lld", n);
+  if (!std::isfinite(G) || G < 0.f || G > 16.f)
+    return fail(LA_ERANGE, "G must be finite and in [0, 16], got %g", (double)G);
+  if (n == 0) return ok();
+  if (!x || !g) return fail(LA_EINVAL, "x and g must not be NULL");
+  if (!aligned(x, 4u) || !aligned(g, 4u)) return fail(LA_EINVAL, "x and g must be 4-byte aligned");
+  if (x != g && overlap(span("x", x, n * 4), span("g", g, n * 4)))
+    return fail(LA_EINVAL, "g partially overlaps x (only g == x is allowed)");
+  return hip_status(la::launch_gate(x, G, g, n, reinterpret_cast<hipStream_t>(stream)),
+                    "gate launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,143 @@
+/*
+ * lin_attn.h -- C ABI of the gated delta-rule linear-attention library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  Per (batch b, head h) the library carries a fixed-size matrix
+ * state and updates it token by token with a delta rule whose old content is
+ * diluted by a data-dependent decay ("Evaluating Next-Gen Sparse MoE and
+ * Long-Context LLMs", sec. 2, incremental linear attention; "Core Technologies
+ * Behind Ultra-Long-Context Sparse MoE Large Models", sec. 2.1).  With the
+ * state stored as h = S^T (d_k rows, d_v columns):
+ *
+ *     h_t = exp(g_t) * (h_{t-1} - beta_t k_t (k_t^T h_{t-1})) + beta_t k_t v_t^T
+ *     o_t = h_t^T q_t
+ *
+ * The log-decay is bounded, g_t = -G * sigmoid(x_t) in [-G, 0] with G = 5 on
+ * the pages ("Deep Dive: The Next Generation of Ultra-Long Context Sparse MoE
+ * LLMs", sec. 3.3; "How Trillion-Scale Sparse MoE Models Achieve Million-Token
+ * Long Context", sec. 3.2).  The forward pass is computed in 16-token tiles,
+ * parallel inside a tile and recursive between tiles ("Deep Dive", sec. 3.2).
+ *
+ * Conventions for every entry point
+ *  - Every array pointer is a DEVICE pointer owned by the caller.  The library
+ *    never frees, keeps or reallocates caller memory, and allocates no device
+ *    memory of its own.
+ *  - Arrays are dense, row-major, last dimension contiguous, and aligned to
+ *    their element size; arrays the kernels read as 16-byte vectors must be
+ *    16-byte aligned (q and k of lin_attn_chunk_fwd, S of
+ *    lin_attn_decode_step).  Element type of q, k, v and o is given by `dtype`
+ *    (LA_BF16 = bfloat16, LA_FP32 = float32); gate, beta, h0, hT and S are
+ *    always float32.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *    the call returns without waiting.  The return code reports host-side
+ *    argument checks and launch errors only; device-side faults surface at the
+ *    caller's next synchronisation.  No C++ exception crosses the ABI.
+ *  - On any error nothing is enqueued and lin_attn_last_error() (thread-local)
+ *    describes the reason.
+ *  - Results are deterministic: the same inputs give bitwise-identical
+ *    outputs on every call (no atomics in any reduction).
+ *  - Calls may be made from several host threads; the library keeps no global
+ *    mutable state besides the thread-local error text.
+ *  - Zero-size work (B, H or T equal to 0) is valid and enqueues nothing except
+ *    that chunk_fwd with T = 0 copies h0 (or zeros) into hT.
+ */
+#ifndef LIN_ATTN_H
+#define LIN_ATTN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define LA_OK            0  /* success (work enqueued) */
+#define LA_EINVAL        1  /* bad argument: NULL pointer, negative size,
+                               misalignment, forbidden aliasing, bad enum */
+#define LA_EUNSUPPORTED  2  /* valid but not built: head sizes outside the
+                               supported set */
+#define LA_ERANGE        3  /* a scalar parameter outside its allowed range */
+#define LA_EHIP          4  /* a HIP launch error; see lin_attn_last_error() */
+
+/* Element types of q, k, v, o. */
+#define LA_BF16 0
+#define LA_FP32 1
+
+/* Meaning of the `gate` array. */
+#define LA_GATE_LOG            0  /* gate holds g_t itself; caller guarantees
+                                     -G <= g_t <= 0 (G only documents it)   */
+#define LA_GATE_BOUNDED_LOGIT  1  /* gate holds x_t; g_t = -G * sigmoid(x_t) */
+
+/*
+ * lin_attn_chunk_fwd -- chunked forward pass over a whole sequence.
+ *
+ * Computes o_t for every token and the final state h_T of the recurrence
+ * above, from the initial state h0, tile by tile (16 tokens per tile): inside
+ * a tile the token interactions (the diagonal block) and the contribution of
+ * the carried state (the "historical state -> current token" block) are
+ * matrix products, and the state is carried from tile to tile ("Core
+ * Technologies ...", sec. 2.1; "How Trillion-Scale ...", sec. 3.1).
+ *
+ *   q     [B, T, H, Dk]  dtype          queries
+ *   k     [B, T, H, Dk]  dtype          keys (expected unit norm; not checked)
+ *   v     [B, T, H, Dv]  dtype          values
+ *   gate  [B, T, H]      float32        g_t or x_t, per gate_mode
+ *   G     float, 0 <= G <= 16           decay bound (5 on the pages)
+ *   beta  [B, T, H]      float32        write strengths, expected in [0, 1]
+ *   h0    [B, H, Dk, Dv] float32 or NULL (NULL = zero initial state)
+ *   o     [B, T, H, Dv]  dtype          output, rounded to nearest-even from
+ *                                       float32 when dtype is LA_BF16
+ *   hT    [B, H, Dk, Dv] float32 or NULL (NULL = final state not written)
+ *   Dk in {64, 128}; Dv a multiple of 16 in [16, 256]; B, T, H >= 0.
+ *
+ * Aliasing: o must not overlap any input.  hT may be the very same pointer as
+ * h0 (the state is then updated in place); any other overlap of hT with an
+ * input or with o is rejected.  T need not be a multiple of 16: the last tile
+ * behaves as if padded with tokens q = k = v = 0, g = 0, beta = 0, which leave
+ * the state unchanged.
+ */
+int lin_attn_chunk_fwd(const void* q, const void* k, const void* v,
+                       const float* gate, int gate_mode, float G,
+                       const float* beta, const float* h0,
+                       void* o, float* hT,
+                       int B, int T, int H, int Dk, int Dv, int dtype,
+                       void* stream);
+
+/*
+ * lin_attn_decode_step -- one new token per (b, h), state updated in place.
+ *
+ * Constant-state recurrent inference: each sequence advances its d_k x d_v
+ * state by one token and reads it out ("Evaluating Next-Gen ...", sec. 2
+ * item 2 and sec. 4, constant-state linear attention layers in serving).
+ * Equivalent to lin_attn_chunk_fwd with T = 1 and hT = h0 = S.
+ *
+ *   q, k  [B, H, Dk] dtype;  v [B, H, Dv] dtype
+ *   gate, beta [B, H] float32 (gate per gate_mode, as above)
+ *   S     [B, H, Dk, Dv] float32, read and overwritten in place
+ *   o     [B, H, Dv] dtype, output (reads the updated state)
+ *   Dk in {64, 128}; Dv in {64, 128}.
+ * o must not overlap any input; S must not overlap q, k, v, gate, beta or o.
+ */
+int lin_attn_decode_step(const void* q, const void* k, const void* v,
+                         const float* gate, int gate_mode, float G,
+                         const float* beta, float* S, void* o,
+                         int B, int H, int Dk, int Dv, int dtype,
+                         void* stream);
+
+/*
+ * lin_attn_gate -- the bounded log-decay on its own: g[i] = -G * sigmoid(x[i])
+ * for i < n ("Deep Dive ...", sec. 3.3; "Core Technologies ...", sec. 2.2).
+ * x and g are float32 device arrays of n elements (g may equal x for an
+ * in-place transform; other overlaps are rejected).  0 <= G <= 16.
+ */
+int lin_attn_gate(const float* x, float G, float* g, long long n, void* stream);
+
+/* Text of the last error on the calling thread ("" if none). */
+const char* lin_attn_last_error(void);
+
+/* Library ABI version (major * 100 + minor). */
+int lin_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIN_ATTN_H */

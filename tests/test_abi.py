@@ -1,0 +1,163 @@
+"""The C ABI library loads, exports every symbol the header declares, and
+rejects bad arguments on the host with the documented codes.  No call here
+reaches a kernel launch, so these run without a GPU."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from chunked_gated_linear_amd import _native as N
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lin_attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lin_attn_\w+)\s*\(", text)))
+
+
+def declared_constants():
+    text = open(HEADER).read()
+    return {m[0]: int(m[1]) for m in re.findall(r"#define\s+(LA_\w+)\s+(\d+)", text)}
+
+
+def test_library_loads_and_exports_header_symbols():
+    L = N.lib()
+    names = declared_functions()
+    assert names == sorted(N.SIGNATURES), "binding and header disagree"
+    for name in names:
+        assert hasattr(L, name), name
+    assert L.lin_attn_version() >= 100
+
+
+def test_binding_constants_match_header():
+    c = declared_constants()
+    assert c["LA_OK"] == N.LA_OK and c["LA_EINVAL"] == N.LA_EINVAL
+    assert c["LA_EUNSUPPORTED"] == N.LA_EUNSUPPORTED and c["LA_ERANGE"] == N.LA_ERANGE
+    assert c["LA_EHIP"] == N.LA_EHIP
+    assert c["LA_BF16"] == N.LA_BF16 and c["LA_FP32"] == N.LA_FP32
+    assert c["LA_GATE_LOG"] == N.LA_GATE_LOG
+    assert c["LA_GATE_BOUNDED_LOGIT"] == N.LA_GATE_BOUNDED_LOGIT
+
+
+# Fake, never-dereferenced device addresses: validation looks at pointer values
+# only, and every case below fails before any launch.
+BASE = 1 << 40
+
+
+def fake(i, size=1 << 30):
+    return BASE + i * size
+
+
+def chunk(**kw):
+    a = dict(q=fake(0), k=fake(1), v=fake(2), gate=fake(3), gate_mode=0, G=5.0,
+             beta=fake(4), h0=None, o=fake(5), hT=fake(6), B=1, T=64, H=2, Dk=128,
+             Dv=128, dtype=0, stream=None)
+    a.update(kw)
+    L = N.lib()
+    rc = L.lin_attn_chunk_fwd(a["q"], a["k"], a["v"], a["gate"], a["gate_mode"], a["G"],
+                              a["beta"], a["h0"], a["o"], a["hT"], a["B"], a["T"], a["H"],
+                              a["Dk"], a["Dv"], a["dtype"], a["stream"])
+    return rc, L.lin_attn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(q=None), N.LA_EINVAL, "q must not be NULL"),
+    (dict(k=None), N.LA_EINVAL, "k must not be NULL"),
+    (dict(beta=None), N.LA_EINVAL, "beta must not be NULL"),
+    (dict(o=None), N.LA_EINVAL, "o must not be NULL"),
+    (dict(B=-1), N.LA_EINVAL, "sizes"),
+    (dict(T=-3), N.LA_EINVAL, "sizes"),
+    (dict(dtype=7), N.LA_EINVAL, "dtype"),
+    (dict(gate_mode=2), N.LA_EINVAL, "gate_mode"),
+    (dict(G=-1.0), N.LA_ERANGE, "G must"),
+    (dict(G=float("nan")), N.LA_ERANGE, "G must"),
+    (dict(G=100.0), N.LA_ERANGE, "G must"),
+    (dict(Dk=96), N.LA_EUNSUPPORTED, "Dk"),
+    (dict(Dv=40), N.LA_EUNSUPPORTED, "Dv"),
+    (dict(Dv=512), N.LA_EUNSUPPORTED, "Dv"),
+    (dict(q=fake(0) + 8), N.LA_EINVAL, "aligned"),
+    (dict(h0=fake(7) + 2), N.LA_EINVAL, "aligned"),
+    (dict(v=fake(2) + 1), N.LA_EINVAL, "aligned"),
+    (dict(o=fake(0) + 1024), N.LA_EINVAL, "o overlaps q"),
+    (dict(o=fake(6)), N.LA_EINVAL, "o overlaps hT"),
+    (dict(hT=fake(3)), N.LA_EINVAL, "hT overlaps gate"),
+    (dict(h0=fake(7), hT=fake(7) + 4096), N.LA_EINVAL, "partially overlaps h0"),
+])
+def test_chunk_fwd_rejects(kw, code, needle):
+    rc, msg = chunk(**kw)
+    assert rc == code, (rc, msg)
+    assert needle in msg
+
+
+def test_chunk_fwd_empty_is_noop():
+    # B = 0 or H = 0: nothing to do, nothing launched, even with NULL arrays.
+    for kw in (dict(B=0), dict(H=0)):
+        rc, msg = chunk(q=None, k=None, v=None, gate=None, beta=None, o=None, hT=None, **kw)
+        assert rc == N.LA_OK, msg
+        assert msg == ""
+
+
+def decode(**kw):
+    a = dict(q=fake(0), k=fake(1), v=fake(2), gate=fake(3), gate_mode=1, G=5.0,
+             beta=fake(4), S=fake(5), o=fake(6), B=4, H=2, Dk=128, Dv=128, dtype=0,
+             stream=None)
+    a.update(kw)
+    L = N.lib()
+    rc = L.lin_attn_decode_step(a["q"], a["k"], a["v"], a["gate"], a["gate_mode"], a["G"],
+                                a["beta"], a["S"], a["o"], a["B"], a["H"], a["Dk"], a["Dv"],
+                                a["dtype"], a["stream"])
+    return rc, L.lin_attn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(S=None), N.LA_EINVAL, "S must not be NULL"),
+    (dict(H=-2), N.LA_EINVAL, "sizes"),
+    (dict(Dv=256), N.LA_EUNSUPPORTED, "decode supports"),
+    (dict(Dk=32), N.LA_EUNSUPPORTED, "decode supports"),
+    (dict(o=fake(5)), N.LA_EINVAL, "o overlaps S"),
+    (dict(S=fake(1)), N.LA_EINVAL, "S overlaps k"),
+    (dict(v=fake(2) + 1), N.LA_EINVAL, "aligned"),
+    (dict(S=fake(5) + 8), N.LA_EINVAL, "aligned"),
+    (dict(G=20.0), N.LA_ERANGE, "G must"),
+])
+def test_decode_rejects(kw, code, needle):
+    rc, msg = decode(**kw)
+    assert rc == code, (rc, msg)
+    assert needle in msg
+
+
+def test_gate_rejects():
+    L = N.lib()
+    assert L.lin_attn_gate(fake(0), 5.0, fake(1), -1, None) == N.LA_EINVAL
+    assert L.lin_attn_gate(None, 5.0, fake(1), 10, None) == N.LA_EINVAL
+    assert L.lin_attn_gate(fake(0), 5.0, fake(0) + 16, 10, None) == N.LA_EINVAL
+    assert "partially overlaps" in L.lin_attn_last_error().decode()
+    assert L.lin_attn_gate(fake(0), -5.0, fake(1), 10, None) == N.LA_ERANGE
+    assert L.lin_attn_gate(fake(0), 5.0, fake(1), 0, None) == N.LA_OK
+
+
+def test_error_text_is_thread_local():
+    import threading
+    chunk(q=None)
+    seen = {}
+
+    def other():
+        seen["msg"] = N.lib().lin_attn_last_error().decode()
+
+    th = threading.Thread(target=other)
+    th.start()
+    th.join()
+    assert seen["msg"] == ""
+    assert "q must not be NULL" in N.lib().lin_attn_last_error().decode()
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(N, "_lib", None)
+    monkeypatch.setattr(N, "LIB_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(RuntimeError, match="no fallback"):
+        N.lib()

@@ -275,6 +275,27 @@ def test_recurrent_pins(name, golden_dir):
     assert run_pin(name, orc.recurrent_fwd, golden_dir)
 
 
+@pytest.mark.parametrize("name", sorted(PINS))
+def test_c_recurrent_pins(name, golden_dir):
+    # The plain-C copy of the recurrence (used for long sequences) answers to
+    # the same pins as the NumPy one.
+    from oracle import c_recurrent
+    fwd = lambda *a: c_recurrent.recurrent_fwd(*a, workers=2)
+    assert run_pin(name, fwd, golden_dir)
+
+
+def test_c_recurrent_matches_numpy_on_windows():
+    from oracle import c_recurrent
+    q, k, v, g, beta, h0 = rand_inputs(2, 50, 3, 16, 8, gate="weak", seed=43, h0=True)
+    o, hT = orc.recurrent_fwd(q, k, v, g, beta, h0)
+    _, hmid = orc.recurrent_fwd(q[:, :20], k[:, :20], v[:, :20], g[:, :20], beta[:, :20], h0)
+    res = c_recurrent.recurrent_fwd_c(q, k, v, g, beta, hmid, heads=[(0, 1), (1, 2)],
+                                      t_range=(20, 50), workers=2)
+    for (b, h), (ob, hb) in res.items():
+        np.testing.assert_allclose(ob, o[b, 20:, h], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(hb, hT[b, h], rtol=1e-12, atol=1e-14)
+
+
 @pytest.mark.parametrize("chunk", [1, 3, 16, 32])
 def test_chunked_pins(chunk, golden_dir):
     fwd = lambda *a: orc.chunked_fwd(*a, chunk=chunk)
@@ -367,6 +388,8 @@ MUTANTS = ["gate_sign", "no_decay", "transposed_write", "decay_after_write",
 
 @pytest.mark.parametrize("kind", MUTANTS)
 def test_mutants_are_caught(kind, golden_dir):
+    # every pin is a function of the implementation under test, so a mutant
+    # copy of the recurrence can be run through all of them
     fwd = _mutant(kind)
     failed = []
     for name in PINS:
