@@ -35,6 +35,9 @@ def flags() -> list[str]:
     return [f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
             # packed fp32 VALU ops stay off (see the project notes on gfx950)
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # keep MFMA accumulators in VGPRs: the state is rescaled by VALU
+            # every tile, and AGPR accumulators would cost a move each way
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-I", INCLUDE, "-I", CSRC]
 
 

@@ -132,6 +132,10 @@ __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_kernel(
     F32 Hb[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) Hb[s] = X::from_acc2(Hacc[2 * s], Hacc[2 * s + 1]);
+    // this lane's output element of token 4*grp in the sequence; tokens are
+    // ostride elements apart
+    const int64_t ostride = (int64_t)H * DV;
+    E* const orow = o + rowk(4 * grp) * DV + v0 + n;
     __syncthreads();  // epoch 0 prepared
 
     for (int ep = 0; ep < NE; ++ep) {
@@ -161,10 +165,14 @@ __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) O[i] = gam[i] * QH[i];
         O = X::mma16(pf, X::from_acc(U), O);
+        E* oc = orow + (int64_t)(16 * c) * ostride;
+        if (16 * c + 16 <= T) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = 16 * c + 4 * grp + i;
-          if (t < T) o[rowk(t) * DV + v0 + n] = X::from_f(O[i]);
+          for (int i = 0; i < 4; ++i) oc[i * ostride] = X::from_f(O[i]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (16 * c + 4 * grp + i < T) oc[i * ostride] = X::from_f(O[i]);
         }
         f32x4 Up;
 #pragma unroll
@@ -198,55 +206,56 @@ __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_kernel(
   float* sA = reinterpret_cast<float*>(scr + C::SA);
   float* sB = reinterpret_cast<float*>(scr + C::SB);
 
+  // Issue the global loads of tile c into r.  Rows past the end are read from
+  // the last valid row (always in bounds) and zeroed later in produce(), so no
+  // loaded value is consumed here and the loads stay in flight for an epoch.
+  // Loads are issued unconditionally (tile index clamped to the last tile) so
+  // the number of loads in flight is the same on every path and the compiler
+  // can wait for exactly the older set.
   auto load = [&](Raw<E, DK>& r, int c) {
-    if (c >= NC) return;
-    const int t = 16 * c + n;
-    const bool ok = t < T;
-    const int64_t base = rowk(ok ? t : 0) * DK;
+    c = min(c, NC - 1);
+    const int t = min(16 * c + n, T - 1);
+    const int64_t base = rowk(t) * DK;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       if constexpr (sizeof(E) == 2) {
-        // base points at a valid row even when t >= T; the values are then
-        // replaced by zeros (padding tokens)
-        const bf16x4 z = {};
         const bf16x4 k0 = *reinterpret_cast<const bf16x4*>(k + base + 32 * s + 4 * grp);
         const bf16x4 k1 = *reinterpret_cast<const bf16x4*>(k + base + 32 * s + 16 + 4 * grp);
         const bf16x4 q0 = *reinterpret_cast<const bf16x4*>(q + base + 32 * s + 4 * grp);
         const bf16x4 q1 = *reinterpret_cast<const bf16x4*>(q + base + 32 * s + 16 + 4 * grp);
-        const bf16x4 a0 = ok ? k0 : z, a1 = ok ? k1 : z, b0 = ok ? q0 : z, b1 = ok ? q1 : z;
-        r.kf[s].v = bf16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-        r.qf[s].v = bf16x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+        r.kf[s].v = bf16x8{k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
+        r.qf[s].v = bf16x8{q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
       } else {
-        const f32x4 z = zero4();
-        const f32x4 k0 = *reinterpret_cast<const f32x4*>(k + base + 32 * s + 4 * grp);
-        const f32x4 k1 = *reinterpret_cast<const f32x4*>(k + base + 32 * s + 16 + 4 * grp);
-        const f32x4 q0 = *reinterpret_cast<const f32x4*>(q + base + 32 * s + 4 * grp);
-        const f32x4 q1 = *reinterpret_cast<const f32x4*>(q + base + 32 * s + 16 + 4 * grp);
-        r.kf[s].lo = ok ? k0 : z;
-        r.kf[s].hi = ok ? k1 : z;
-        r.qf[s].lo = ok ? q0 : z;
-        r.qf[s].hi = ok ? q1 : z;
+        r.kf[s].lo = *reinterpret_cast<const f32x4*>(k + base + 32 * s + 4 * grp);
+        r.kf[s].hi = *reinterpret_cast<const f32x4*>(k + base + 32 * s + 16 + 4 * grp);
+        r.qf[s].lo = *reinterpret_cast<const f32x4*>(q + base + 32 * s + 4 * grp);
+        r.qf[s].hi = *reinterpret_cast<const f32x4*>(q + base + 32 * s + 16 + 4 * grp);
       }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tv = 16 * c + 4 * grp + i;
-      const bool okv = tv < T;
-      const E x = v[rowk(okv ? tv : 0) * DV + v0 + n];     // row index clamped
-      r.vv[i] = okv ? x : X::from_f(0.f);
-    }
-    const float gx = gate[rowk(ok ? t : 0)];
-    const float bx = beta[rowk(ok ? t : 0)];
-    r.gx = ok ? gx : 0.f;
-    r.bt = ok ? bx : 0.f;
+    for (int i = 0; i < 4; ++i)
+      r.vv[i] = v[rowk(min(16 * c + 4 * grp + i, T - 1)) * DV + v0 + n];
+    r.gx = gate[rowk(t)];
+    r.bt = beta[rowk(t)];
   };
 
   auto produce = [&](const Raw<E, DK>& r, int c) {
     if (c >= NC) return;
     char* rec = rec_of(c / NP, c % NP);
+    // padding tokens past T: q = k = v = 0, g = 0, beta = 0 (an identity step)
     const bool ok = 16 * c + n < T;
     const float g = ok ? (gate_logit ? bounded_gate(r.gx, G) : r.gx) : 0.f;
     const float bt = ok ? r.bt : 0.f;
+    F32 kf[NS], qf[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      kf[s] = r.kf[s];
+      qf[s] = r.qf[s];
+      if (!ok) {
+        kf[s] = F32{};
+        qf[s] = F32{};
+      }
+    }
     const float Gi = scan16(g, n);              // G_n, inclusive
     const float Gtot = __shfl(Gi, 15, 16);      // G_15 (padding adds 0)
     if (grp == 0) {
@@ -264,8 +273,8 @@ __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_kernel(
     f32x4 skk = zero4(), sqk = zero4();
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      skk = X::mma32(r.kf[s], r.kf[s], skk);
-      sqk = X::mma32(r.kf[s], r.qf[s], sqk);
+      skk = X::mma32(kf[s], kf[s], skk);
+      sqk = X::mma32(kf[s], qf[s], sqk);
     }
     f32x4 arow, prow;
 #pragma unroll
@@ -286,17 +295,17 @@ __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_kernel(
     const F16 ident = X::from_acc(idv);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const f32x4 kt = X::mma16(X::half(r.kf[t >> 1], t & 1), ident, zero4());
+      const f32x4 kt = X::mma16(X::half(kf[t >> 1], t & 1), ident, zero4());
       reinterpret_cast<F16*>(rec + C::KT)[t * 64 + lane] = X::from_acc(kt);
     }
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      reinterpret_cast<F32*>(rec + C::KF)[s * 64 + lane] = r.kf[s];
-      reinterpret_cast<F32*>(rec + C::QF)[s * 64 + lane] = r.qf[s];
+      reinterpret_cast<F32*>(rec + C::KF)[s * 64 + lane] = kf[s];
+      reinterpret_cast<F32*>(rec + C::QF)[s * 64 + lane] = qf[s];
     }
     F16 vf;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) vf.v[i] = r.vv[i];
+    for (int i = 0; i < 4; ++i) vf.v[i] = (16 * c + 4 * grp + i < T) ? r.vv[i] : X::from_f(0.f);
     reinterpret_cast<F16*>(rec + C::VF)[lane] = vf;
 
     // LDS traffic of one wave is performed in order; the wave barrier keeps the
@@ -341,22 +350,23 @@ __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_kernel(
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
+  // Two register sets, alternating by epoch: while tile (ep+1)*NP + p is
+  // prepared from one set, the loads for tile (ep+2)*NP + p fill the other.
+  // The loop is unrolled by two so each set keeps its own registers.
   Raw<E, DK> ra, rb;
   load(ra, p);
   produce(ra, p);               // epoch 0
   load(ra, NP + p);             // epoch 1, prepared during epoch 0
   __syncthreads();
-  for (int ep = 0; ep < NE; ++ep) {
-    const int cnext = (ep + 1) * NP + p;   // prepared now, consumed next epoch
-    const int cload = (ep + 2) * NP + p;   // prefetched now
-    if (ep & 1) {
-      load(ra, cload);
-      produce(rb, cnext);
-    } else {
-      load(rb, cload);
-      produce(ra, cnext);
-    }
+  for (int ep = 0; ep < NE; ep += 2) {
+    load(rb, (ep + 2) * NP + p);
+    produce(ra, (ep + 1) * NP + p);
     __syncthreads();
+    if (ep + 1 < NE) {
+      load(ra, (ep + 3) * NP + p);
+      produce(rb, (ep + 2) * NP + p);
+      __syncthreads();
+    }
   }
 }
 

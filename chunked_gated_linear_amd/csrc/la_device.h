@@ -93,11 +93,12 @@ template <> struct Elt<float> {
 
 __device__ inline f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
-// Bounded log-decay g = -G * sigmoid(x).  __expf saturates cleanly: for very
-// negative x the exponential is +inf and g is -0; for very positive x it is 0
-// and g is -G.
+// Bounded log-decay g = -G * sigmoid(x) with the hardware exponential and
+// reciprocal (about 1 ulp each).  Saturates cleanly: for very negative x the
+// exponential is +inf, its reciprocal 0 and g = -0; for very positive x it is
+// 0 and g = -G.
 __device__ inline float bounded_gate(float x, float G) {
-  return -G / (1.0f + __expf(-x));
+  return -G * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
 }
 
 // Lane-group (16 lanes) inclusive prefix sum; every 16-lane group scans its
