@@ -115,7 +115,7 @@ def main():
         "tflops": flops / t / 1e12,
         "roofline": {"bound": "hbm", "achieved": byts / t / 1e9, "peak": PEAK_HBM / 1e9,
                      "unit": "GB/s", "frac": byts / t / PEAK_HBM, "traffic": None,
-                     "kernel": "chunk_fwd_kernel", "alg_bytes_per_launch": byts,
+                     "kernel": "chunk_fwd2_kernel (bf16) / chunk_fwd_kernel (fp32)", "alg_bytes_per_launch": byts,
                      "alg_flops_per_launch": flops,
                      "attainable_frac": max(byts / PEAK_HBM, flops / PEAK_BF16) / t},
     }

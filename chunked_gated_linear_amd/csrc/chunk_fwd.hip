@@ -389,8 +389,7 @@ hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v, const f
     if (Dk == 64) return launch_t<float, 64, 2>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, st);
     if (Dk == 128) return launch_t<float, 128, 2>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, st);
   } else {
-    if (Dk == 64) return launch_t<__bf16, 64, 3>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, st);
-    if (Dk == 128) return launch_t<__bf16, 128, 3>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, st);
+    return launch_chunk_fwd_pair(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dk, Dv, st);
   }
   return hipErrorInvalidValue;
 }

@@ -12,6 +12,12 @@ hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v,
                             int B, int T, int H, int Dk, int Dv, int fp32,
                             hipStream_t st);
 
+// bf16 path: the state is carried across pairs of 16-token tiles.
+hipError_t launch_chunk_fwd_pair(const void* q, const void* k, const void* v,
+                                 const float* gate, int gate_logit, float G,
+                                 const float* beta, const float* h0, void* o, float* hT,
+                                 int B, int T, int H, int Dk, int Dv, hipStream_t st);
+
 hipError_t launch_decode(const void* q, const void* k, const void* v,
                          const float* gate, int gate_logit, float G,
                          const float* beta, float* S, void* o, int BH, int Dk,

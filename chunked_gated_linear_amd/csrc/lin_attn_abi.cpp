@@ -89,8 +89,8 @@ int lin_attn_chunk_fwd(const void* q, const void* k, const void* v, const float*
   if ((int64_t)B * H * (Dv / 16) > INT32_MAX || ntok > (INT64_C(1) << 40))
     return fail(LA_EINVAL, "problem too large (B*H*Dv/16 = %lld)",
                 (long long)((int64_t)B * H * (Dv / 16)));
-  if ((int64_t)T * H > INT32_MAX || (int64_t)B * T > INT32_MAX)
-    return fail(LA_EINVAL, "problem too large (T*H or B*T exceeds 2^31)");
+  if ((int64_t)T * H * (Dk > Dv ? Dk : Dv) > INT32_MAX || (int64_t)B * T > INT32_MAX)
+    return fail(LA_EINVAL, "problem too large (T*H*max(Dk,Dv) or B*T exceeds 2^31)");
   if (B == 0 || H == 0) return ok();
   const unsigned ea = dtype == LA_BF16 ? 2u : 4u;
   if (T > 0) {
