@@ -63,7 +63,8 @@ def main():
     import torch
 
     from chunked_gated_linear_amd import inputs as I
-    from chunked_gated_linear_amd import lin_attn_chunk_fwd, lin_attn_decode_step
+    from chunked_gated_linear_amd import (lin_attn_chunk_fwd, lin_attn_chunk_fwd_workspace_size,
+                                          lin_attn_decode_step)
 
     wl = dict(I.WORKLOADS[args.workload])
     B, H, T, Dk, Dv, dtype = wl["B"], wl["H"], wl["T"], wl["Dk"], wl["Dv"], wl["dtype"]
@@ -73,10 +74,12 @@ def main():
     inp = I.make_inputs(B, T, H, Dk, Dv, dtype=dtype, seed=1002, device=dev, h0_std=h0_std)
     o = torch.empty((B, T, H, Dv), dtype=inp["q"].dtype, device=dev)
     hT = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev)
+    nws = lin_attn_chunk_fwd_workspace_size(B, T, H, Dk, Dv, inp["q"].dtype)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
 
     def step():
         lin_attn_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["x"], inp["beta"], inp["h0"],
-                           gate_mode="logit", G=5.0, o=o, hT=hT)
+                           gate_mode="logit", G=5.0, o=o, hT=hT, workspace=ws)
 
     for _ in range(args.warmup):
         step()

@@ -20,7 +20,8 @@ LA_GATE_LOG, LA_GATE_BOUNDED_LOGIT = 0, 1
 _P, _I, _F, _LL = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_longlong
 SIGNATURES = {
     "lin_attn_chunk_fwd": (_I, [_P, _P, _P, _P, _I, _F, _P, _P, _P, _P,
-                                _I, _I, _I, _I, _I, _I, _P]),
+                                _I, _I, _I, _I, _I, _I, _P, _LL, _P]),
+    "lin_attn_chunk_fwd_workspace_size": (_LL, [_I, _I, _I, _I, _I, _I]),
     "lin_attn_decode_step": (_I, [_P, _P, _P, _P, _I, _F, _P, _P, _P,
                                   _I, _I, _I, _I, _I, _P]),
     "lin_attn_gate": (_I, [_P, _F, _P, _LL, _P]),

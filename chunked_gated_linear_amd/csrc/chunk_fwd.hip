@@ -383,14 +383,10 @@ static hipError_t launch_t(const void* q, const void* k, const void* v, const fl
 
 hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v, const float* gate,
                             int gate_logit, float G, const float* beta, const float* h0,
-                            void* o, float* hT, int B, int T, int H, int Dk, int Dv, int fp32,
+                            void* o, float* hT, int B, int T, int H, int Dk, int Dv,
                             hipStream_t st) {
-  if (fp32) {
-    if (Dk == 64) return launch_t<float, 64, 2>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, st);
-    if (Dk == 128) return launch_t<float, 128, 2>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, st);
-  } else {
-    return launch_chunk_fwd_pair(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dk, Dv, st);
-  }
+  if (Dk == 64) return launch_t<float, 64, 2>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, st);
+  if (Dk == 128) return launch_t<float, 128, 2>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, st);
   return hipErrorInvalidValue;
 }
 

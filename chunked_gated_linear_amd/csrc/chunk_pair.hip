@@ -1,0 +1,682 @@
+// chunk_pair.hip -- bf16 chunked forward pass as two kernels: an intra-tile
+// kernel, parallel over every pair of 16-token tiles, and an inter-tile kernel
+// that carries the state across the sequence.
+//
+// Method: the sequence is cut into 16-token tiles; inside a tile the token
+// interactions (K K^T, Q K^T) and the "historical state -> current token"
+// products (K H, Q H) run on the matrix cores, and the state is carried from
+// tile to tile ("Deep Dive: The Next Generation of Ultra-Long Context Sparse
+// MoE LLMs", sec. 3.2; "Core Technologies Behind Ultra-Long-Context Sparse MoE
+// Large Models", sec. 2.1).  The state h = S^T (d_k x d_v) is carried across
+// pairs of tiles a, b (32 tokens).  With G the running sum of g over the pair,
+// gamma = exp(G), delta_p = exp(G_31 - G_p), Gamma = exp(G_31):
+//     A   = [[A00, 0], [A10, A11]],  A[t][s] = beta_t exp(G_t - G_s) k_t.k_s (s < t)
+//     T   = (I + A)^-1 = [[T00, 0], [T10, T11]],  T10 = -T11 A10 T00
+//     Tb  = T diag(beta),  P[t][s] = exp(G_t - G_s) q_t.k_s (s <= t)
+//     U   = Tb (V - diag(gamma) K H)
+//     O   = diag(gamma) Q H + P U
+//     H'  = Gamma H + K^T diag(delta) U
+// Everything but U, O and H' is independent of the state.  Only exponentials
+// of non-positive numbers appear, so with the bounded gate every in-tile
+// factor lies in [exp(-32 G), 1] and no reciprocal is formed.
+//
+// chunk_prep_kernel (intra-tile) -- one wave per (sequence, head, pair): gate,
+//   in-pair cumulative sum, K K^T and K Q^T on MFMA, decay masks, the two
+//   16 x 16 unit-triangular solves in fp32, T10 on fp32 MFMA, and hi/lo bf16
+//   splits of Tb and P.  Its results (6.5 KB per pair) go to a workspace in
+//   HBM, computed once per head rather than once per d_v slice.
+// chunk_state_kernel (inter-tile) -- one workgroup per (sequence, head, 16
+//   columns of d_v), three waves:
+//   wave 0 "chain"   the fp32 state slice (d_k x 16) in registers; per pair:
+//                    K H, U, the 32-deep state update, all on MFMA;
+//   wave 1 "output"  diag(gamma) Q H + P U on MFMA and the bf16 stores, one
+//                    pair behind the chain; q, P and gamma come straight from
+//                    global memory, several pairs ahead;
+//   wave 2 "loader"  streams K, V and the chain's part of the workspace into a
+//                    ring of LDS records with direct global->LDS loads, a few
+//                    pairs ahead of the chain.
+//   One workgroup barrier per pair.  The state (bf16) and U reach the output
+//   wave through LDS, double buffered by pair parity.
+//
+// Precision: Tb, P and U are split into bf16 hi + lo parts and contracted as
+// [X_hi | X_lo] . [Y ; Y] in one 32-deep MFMA (the issue cost of a 16-deep
+// product).  The state is kept in fp32; its bf16 copy feeds K H and Q H.
+//
+// State row order.  Accumulator tile t = 2s + h of the state holds, in lane
+// (n, grp) register i, row rho = 32 s + 8 grp + 4 h + i of the d_k x 16 slice;
+// every 32-deep fragment of K or Q is then 8 consecutive elements of a row and
+// two accumulator tiles form the 32-deep B fragment of H directly.
+#include "la_device.h"
+#include "la_launch.h"
+
+namespace la {
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Workspace record of one pair of tiles of one (sequence, head), in bytes.
+// Fragment fields hold 64 lanes x 16 B in lane order.
+struct WsRec {
+  static constexpr int TB0 = 0;       // [Tb00 hi | Tb00 lo]   row n, columns 4grp..4grp+3
+  static constexpr int TB1H = 1024;   // [Tb10 hi | Tb11 hi]
+  static constexpr int TB1L = 2048;   // [Tb10 lo | Tb11 lo]
+  static constexpr int PF0 = 3072;    // [P00 hi  | P00 lo]
+  static constexpr int PF1H = 4096;   // [P10 hi  | P11 hi]
+  static constexpr int PF1L = 5120;   // [P10 lo  | P11 lo]
+  static constexpr int GM = 6144;     // gamma[32]  f32
+  static constexpr int DL = 6272;     // delta[32]  f32
+  static constexpr int GC = 6400;     // Gamma      f32 (record padded to 256 B)
+  static constexpr int BYTES = 6656;
+};
+
+// K fragment slot inside a 1 KB block: (grp, m) -> grp*16 + (m ^ 4grp).  The
+// XOR keeps the transposing reads of the state update free of bank conflicts;
+// ordinary fragment reads stay lane-contiguous.
+__device__ inline int kslot(int grp, int m) { return grp * 16 + (m ^ (4 * grp)); }
+
+__device__ inline bf16x4 hi4(f32x4 x) {
+  return bf16x4{(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
+}
+__device__ inline bf16x4 lo4(f32x4 x, bf16x4 h) {
+  return bf16x4{(__bf16)(x[0] - (float)h[0]), (__bf16)(x[1] - (float)h[1]),
+                (__bf16)(x[2] - (float)h[2]), (__bf16)(x[3] - (float)h[3])};
+}
+__device__ inline bf16x8 cat8(bf16x4 a, bf16x4 b) {
+  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+__device__ inline f32x4 mma32b(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Inclusive prefix sum over each row of 16 lanes with DPP row shifts (lanes
+// shifted in from outside the row contribute 0).
+__device__ inline float scan16_dpp(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x111, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x112, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x114, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x118, 0xf, 0xf, false));
+  return x;
+}
+
+// Wave-local ordering of LDS traffic (a wave's LDS operations execute in
+// order; this keeps the compiler from reordering across the point).
+__device__ inline void wave_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// s_waitcnt with only the vector-memory count limited (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int N>
+__device__ inline void wait_vmcnt() {
+  constexpr int n = N > 63 ? 63 : N;
+  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
+__device__ inline void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xc07f); }  // vmcnt 63, expcnt 7, lgkmcnt 0
+
+// Workgroup barrier without the implicit "wait for every outstanding memory
+// operation" of __syncthreads: callers wait for exactly what the other waves
+// will read.  The wavefront fences only stop the compiler from moving memory
+// accesses across the barrier.
+__device__ inline void wg_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Direct global -> LDS loads: lane i's `bytes` land at lds + i * bytes.
+__device__ inline void lds_dma16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
+}
+
+// ============================================================== intra-tile
+
+constexpr int kPrepWaves = 4;
+constexpr int kPrepScr = 2304;   // per wave: A00 (then T00), A11 (then T11), beta[32], G[32]
+
+template <int DK>
+__global__ __launch_bounds__(64 * kPrepWaves) void chunk_prep_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+    const float* __restrict__ gate, int gate_logit, float G, const float* __restrict__ beta,
+    char* __restrict__ ws, int B, int T, int H) {
+  constexpr int NS = DK / 32;
+  using F = Elt<float>;
+  __shared__ __attribute__((aligned(16))) char smem[kPrepWaves * kPrepScr];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15, grp = lane >> 4;
+  const int NSC = (T + 31) >> 5;
+  const int64_t job = (int64_t)blockIdx.x * kPrepWaves + wave;   // = head * NSC + pair
+  if (job >= (int64_t)B * H * NSC) return;                        // no barriers in this kernel
+  const int head = (int)(job / NSC);
+  const int c = (int)(job - (int64_t)head * NSC);
+  const int b = head / H, h = head - b * H;
+
+  char* scr = smem + wave * kPrepScr;
+  float* sA0 = reinterpret_cast<float*>(scr);
+  float* sA1 = reinterpret_cast<float*>(scr + 1024);
+  float* sB = reinterpret_cast<float*>(scr + 2048);
+  float* sG = reinterpret_cast<float*>(scr + 2176);
+  char* wr = ws + job * WsRec::BYTES;
+
+  // Loads (rows clamped to T-1: padding tokens need no masking of q or k --
+  // with beta = 0 and g = 0 their rows of T are unit vectors and their columns
+  // of Tb are zero, so they contribute nothing anywhere).
+  const int64_t tok0 = (int64_t)b * T * H + h;   // token (b, 0, h)
+  const __bf16* const kb0 = k + tok0 * DK + 8 * grp;
+  const __bf16* const qb0 = q + tok0 * DK + 8 * grp;
+  bf16x8 kf[2][NS], qf[2][NS];
+  float gx[2], bt[2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const int t = min(32 * c + 16 * x + n, T - 1);
+    const int off = t * H * DK;   // fits in 32 bits (checked on the host)
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      kf[x][s] = *reinterpret_cast<const bf16x8*>(kb0 + off + 32 * s);
+      qf[x][s] = *reinterpret_cast<const bf16x8*>(qb0 + off + 32 * s);
+    }
+    gx[x] = gate[tok0 + (int64_t)t * H];
+    bt[x] = beta[tok0 + (int64_t)t * H];
+  }
+
+  const int t0 = 32 * c;
+  const bool oka = t0 + n < T, okb = t0 + 16 + n < T;
+  // padding tokens past T: g = 0, beta = 0 (an identity step)
+  const float gav = oka ? (gate_logit ? bounded_gate(gx[0], G) : gx[0]) : 0.f;
+  const float gbv = okb ? (gate_logit ? bounded_gate(gx[1], G) : gx[1]) : 0.f;
+  const float ba = oka ? bt[0] : 0.f, bb = okb ? bt[1] : 0.f;
+  const float Ga = scan16_dpp(gav);
+  const float Ga15 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, Ga), 15));
+  const float Gb = Ga15 + scan16_dpp(gbv);
+  const float Gb15 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, Gb), 15));
+  if (grp == 0) {
+    float* gm = reinterpret_cast<float*>(wr + WsRec::GM);
+    float* dl = reinterpret_cast<float*>(wr + WsRec::DL);
+    gm[n] = __expf(Ga);
+    gm[16 + n] = __expf(Gb);
+    dl[n] = __expf(Gb15 - Ga);
+    dl[16 + n] = __expf(Gb15 - Gb);
+    if (n == 0) *reinterpret_cast<float*>(wr + WsRec::GC) = __expf(Gb15);
+    sB[n] = ba;
+    sB[16 + n] = bb;
+    sG[n] = Ga;
+    sG[16 + n] = Gb;
+  }
+  const bf16x8* ka = kf[0];
+  const bf16x8* kb = kf[1];
+  const bf16x8* qa = qf[0];
+  const bf16x8* qb = qf[1];
+  // lane (n, grp) reg i of each product holds block entry [n][4 grp + i]
+  f32x4 s00 = zero4(), s11 = zero4(), s10 = zero4();
+  f32x4 p00 = zero4(), p11 = zero4(), p10 = zero4();
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    s00 = mma32b(ka[s], ka[s], s00);
+    s11 = mma32b(kb[s], kb[s], s11);
+    s10 = mma32b(ka[s], kb[s], s10);     // [n][s] = k_b,n . k_a,s
+    p00 = mma32b(ka[s], qa[s], p00);     // [n][s] = q_a,n . k_a,s
+    p11 = mma32b(kb[s], qb[s], p11);
+    p10 = mma32b(ka[s], qb[s], p10);     // [n][s] = q_b,n . k_a,s
+  }
+  wave_fence();
+  const f32x4 Gca = reinterpret_cast<const f32x4*>(sG)[grp];       // G_a at the 4 columns
+  const f32x4 Gcb = reinterpret_cast<const f32x4*>(sG)[4 + grp];   // G_b at the 4 columns
+  f32x4 a00, a11, a10, pp00, pp11, pp10;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int sc = 4 * grp + i;
+    const float d00 = __expf(fminf(Ga - Gca[i], 0.f));
+    const float d11 = __expf(fminf(Gb - Gcb[i], 0.f));
+    const float d10 = __expf(fminf(Gb - Gca[i], 0.f));
+    a00[i] = sc < n ? ba * d00 * s00[i] : 0.f;
+    a11[i] = sc < n ? bb * d11 * s11[i] : 0.f;
+    a10[i] = bb * d10 * s10[i];
+    pp00[i] = sc <= n ? d00 * p00[i] : 0.f;
+    pp11[i] = sc <= n ? d11 * p11[i] : 0.f;
+    pp10[i] = d10 * p10[i];
+  }
+  reinterpret_cast<f32x4*>(sA0)[n * 4 + grp] = a00;
+  reinterpret_cast<f32x4*>(sA1)[n * 4 + grp] = a11;
+  {
+    const bf16x4 h00 = hi4(pp00), h10 = hi4(pp10), h11 = hi4(pp11);
+    reinterpret_cast<bf16x8*>(wr + WsRec::PF0)[lane] = cat8(h00, lo4(pp00, h00));
+    reinterpret_cast<bf16x8*>(wr + WsRec::PF1H)[lane] = cat8(h10, h11);
+    reinterpret_cast<bf16x8*>(wr + WsRec::PF1L)[lane] = cat8(lo4(pp10, h10), lo4(pp11, h11));
+  }
+  wave_fence();
+
+  // T00 (lane groups 0, 1) and T11 (groups 2, 3), row n per lane:
+  // T[n][s] = delta_ns - sum_{r > s} T[n][r] A[r][s]; rows of A are read one
+  // step ahead of their use.  The rows of T then overwrite A.
+  {
+    // x holds row n of T below the diagonal (it starts at 0; the unit
+    // diagonal enters as x[n] = 1 when step rr reaches n).
+    f32x4* Ab = reinterpret_cast<f32x4*>(grp < 2 ? sA0 : sA1);
+    float x[16];
+#pragma unroll
+    for (int s = 0; s < 16; ++s) x[s] = 0.f;
+    f32x4 cur[4], nxt[4];
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) cur[c4] = Ab[15 * 4 + c4];
+#pragma unroll
+    for (int rr = 15; rr >= 1; --rr) {
+      if (rr > 1) {
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) nxt[c4] = Ab[(rr - 1) * 4 + c4];
+      }
+      const float xr = (rr == n) ? 1.f : x[rr];
+#pragma unroll
+      for (int s = 0; s < rr; ++s) x[s] -= xr * cur[s >> 2][s & 3];
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) cur[c4] = nxt[c4];
+    }
+    wave_fence();   // every lane has read all rows of A before T overwrites it
+    if ((grp & 1) == 0) {
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        f32x4 row;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) row[e] = (4 * c4 + e == n) ? 1.f : x[4 * c4 + e];
+        Ab[n * 4 + c4] = row;
+      }
+    }
+  }
+  wave_fence();
+  const float* sT0 = sA0;
+  const float* sT1 = sA1;
+
+  // M = A10 T00 (fp32 MFMA): A = A10 rows (registers), B = T00 columns.
+  f32x4 t00c;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) t00c[j] = sT0[(4 * grp + j) * 16 + n];
+  const f32x4 M = F::mma16(F::F16{a10}, F::F16{t00c}, zero4());   // lane: M[4grp+i][n]
+  // (T11 M)^T = M^T T11^T: the accumulator of M is the A fragment of M^T;
+  // T11 rows give the B fragment of T11^T.  Lane (n, grp) reg i of the result
+  // is (T11 M)[n][4 grp + i] = -T10[n][4 grp + i].
+  const f32x4 t11r = reinterpret_cast<const f32x4*>(sT1)[n * 4 + grp];
+  const f32x4 TM = F::mma16(F::F16{M}, F::F16{t11r}, zero4());
+  const f32x4 t00r = reinterpret_cast<const f32x4*>(sT0)[n * 4 + grp];
+  const f32x4 bea = reinterpret_cast<const f32x4*>(sB)[grp];
+  const f32x4 beb = reinterpret_cast<const f32x4*>(sB)[4 + grp];
+  f32x4 tb00, tb10, tb11;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    tb00[i] = t00r[i] * bea[i];
+    tb10[i] = -TM[i] * bea[i];
+    tb11[i] = t11r[i] * beb[i];
+  }
+  const bf16x4 h00 = hi4(tb00), h10 = hi4(tb10), h11 = hi4(tb11);
+  reinterpret_cast<bf16x8*>(wr + WsRec::TB0)[lane] = cat8(h00, lo4(tb00, h00));
+  reinterpret_cast<bf16x8*>(wr + WsRec::TB1H)[lane] = cat8(h10, h11);
+  reinterpret_cast<bf16x8*>(wr + WsRec::TB1L)[lane] = cat8(lo4(tb10, h10), lo4(tb11, h11));
+}
+
+// ============================================================== inter-tile
+
+template <int DK>
+struct CfgS {
+  static constexpr int NBUF = 10;              // LDS records in the loader's ring
+  static constexpr int NT = DK / 16, NS = DK / 32;
+  // LDS record of one pair (byte offsets)
+  static constexpr int KF = 0;                 // [tile][NS][64 slots] x 16 B, slots as kslot
+  static constexpr int VF = KF + 2 * NS * 1024;   // [32 tokens][16 columns] bf16
+  static constexpr int TB = VF + 1024;         // TB0 | TB1H | TB1L (workspace bytes 0..3071)
+  static constexpr int GD = TB + 3072;         // gamma | delta | Gamma (workspace bytes 6144..6655)
+  static constexpr int REC = GD + 512;
+  // loads per record: K blocks, V, TB, GD
+  static constexpr int LPP = 2 * NS + 1 + 3 + 1;
+  // chain -> output hand-over, double buffered by pair parity; placed first so
+  // that its addresses fit the 16-bit offset field of LDS instructions
+  static constexpr int OB_H = 0;               // [NS][64] x 16 B   H (bf16)
+  static constexpr int OB_U = NS * 1024;       // [2][64] x 16 B    U_a, U_b (f32)
+  static constexpr int OB = OB_U + 2048;
+  static constexpr int OFF_OB = 0;
+  static constexpr int OFF_REC = 2 * OB;
+  static constexpr int LDS = OFF_REC + NBUF * REC;
+  static_assert(REC % 256 == 0 && OB % 16 == 0, "LDS alignment");
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+__device__ inline void map_block(int n, int NH, int NV, int& head, int& vt) {
+  // Workgroups are dealt to the 8 XCDs round robin; numbering the blocks so
+  // that block n serves head (8a + n % 8) keeps all d_v slices of a head on
+  // one XCD, where they share K, q and the workspace through its L2.
+  const int per = 8 * NV;
+  const int full = NH / 8;
+  const int a = n / per;
+  if (a < full) {
+    const int loc = n - a * per;
+    head = 8 * a + (loc & 7);
+    vt = loc >> 3;
+  } else {
+    const int loc = n - full * per;
+    const int r = NH - 8 * full;
+    head = 8 * full + loc % r;
+    vt = loc / r;
+  }
+}
+
+template <int DK>
+__global__ __launch_bounds__(192) void chunk_state_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const char* __restrict__ ws, const float* h0, __bf16* __restrict__ o, float* hT,
+    int B, int T, int H, int DV) {
+  using C = CfgS<DK>;
+  constexpr int NT = C::NT, NS = C::NS, NBUF = C::NBUF;
+  __shared__ __attribute__((aligned(256))) char smem[C::LDS];
+
+  const int NV = DV / 16;
+  int head, vt;
+  map_block(blockIdx.x, B * H, NV, head, vt);
+  const int b = head / H, h = head % H;
+  const int v0 = vt * 16;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15, grp = lane >> 4;
+  const int NSC = (T + 31) >> 5;                          // pairs of tiles
+  const int64_t tok0 = (int64_t)b * T * H + h;            // token (b, 0, h)
+  const char* const wsh = ws + (int64_t)head * NSC * WsRec::BYTES;
+  // Record of pair c.  The byte offset goes through an empty asm so that the
+  // compiler keeps one scalar base per pair instead of rewriting every LDS
+  // address as its own induction variable.
+  auto rec_of = [&](int c) -> char* {
+    int rb = __builtin_amdgcn_readfirstlane(C::OFF_REC + (c % NBUF) * C::REC);
+    asm volatile("" : "+s"(rb));
+    return smem + rb;
+  };
+
+  // Barriers: one before pair 0, then one after each pair c = 0 .. NSC-1 and
+  // one more that lets the output wave finish the last pair: NSC + 2 in all,
+  // executed by every wave.
+
+  if (wave == 2) {
+    // ------------------------------------------------------------ loader
+    // Ring of NBUF records; pair c lives in record c % NBUF.  During pair c
+    // the chain reads records c and c + 1, so when the barrier before pair c
+    // has passed, pairs c + 1 and c + 2 must have landed and the record of
+    // pair c - 1 is free for pair c + NBUF - 1.  Pair indices are clamped so
+    // that every load is valid and the load count never varies.
+    const __bf16* const kb0 = k + tok0 * DK + 8 * grp;
+    const __bf16* const vb0 = v + tok0 * DV + v0 + 8 * (lane & 1);
+    auto issue = [&](int c) {
+      c = min(c, NSC - 1);
+      char* rec = rec_of(c);
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        // slot (grp, m) of a block holds token m: lane (n, grp) fetches token n ^ 4grp
+        const int t = min(32 * c + 16 * x + (n ^ (4 * grp)), T - 1);
+        const __bf16* src = kb0 + t * H * DK;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) lds_dma16(src + 32 * s, rec + C::KF + (x * NS + s) * 1024);
+      }
+      {  // V: lane L fetches 8 columns (half L % 2) of token L / 2 of the pair
+        const int t = min(32 * c + (lane >> 1), T - 1);
+        lds_dma16(vb0 + t * H * DV, rec + C::VF);
+      }
+      const char* wr = wsh + (int64_t)c * WsRec::BYTES + 16 * lane;
+#pragma unroll
+      for (int i = 0; i < 3; ++i) lds_dma16(wr + i * 1024, rec + C::TB + i * 1024);
+      if (lane < 32) lds_dma16(wr + WsRec::GM, rec + C::GD);
+    };
+    constexpr int kAhead = (NBUF - 3) * C::LPP;   // loads allowed in flight at a barrier
+#pragma unroll 1
+    for (int c = 0; c < NBUF - 1; ++c) issue(c);
+    wait_vmcnt<kAhead>();                          // pairs 0 and 1 landed
+    wg_barrier();
+#pragma unroll 1
+    for (int c = 0; c <= NSC; ++c) {
+      issue(c + NBUF - 1);                         // into the record of pair c - 1
+      wait_vmcnt<kAhead>();                        // pair c + 2 landed
+      wg_barrier();
+    }
+    wait_vmcnt<0>();
+    return;
+  }
+
+  if (wave == 0) {
+    // ------------------------------------------------------------ chain wave
+    f32x4 Hacc[NT];
+    const int64_t sbase = ((int64_t)b * H + h) * DK * DV;
+    auto srow = [&](int t, int i) { return 32 * (t >> 1) + 8 * grp + 4 * (t & 1) + i; };
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        Hacc[t][i] = h0 ? h0[sbase + (int64_t)srow(t, i) * DV + v0 + n] : 0.f;
+    bf16x8 Hb[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) Hb[s] = cat8(hi4(Hacc[2 * s]), hi4(Hacc[2 * s + 1]));
+    // Per-lane byte offsets inside a record (the record base is added per pair).
+    const int o_kf = 16 * kslot(grp, n);                 // K fragment rows
+    // transposing read: lane (j, grp) points at K[4 grp + j/4][rho chunk j%4]
+    const int o_kt = ((n & 3) * 16 + ((4 * grp + (n >> 2)) ^ (4 * (n & 3)))) * 16;
+    const int o_v = C::VF + 8 * lane;                    // V, transposing read
+    const int o_tb = C::TB + 16 * lane;
+    const int o_gd = C::GD + 16 * grp;
+    char* const obh = smem + C::OFF_OB + C::OB_H + 16 * lane;
+
+    struct Ops { bf16x8 ka[NS], kb[NS]; f32x4 ga, gb, da, db; float Gam; s16x4_t va, vb;
+                 bf16x8 tb0, tb1h, tb1l; };
+    auto fetch = [&](int c, Ops& x) {
+      const char* rec = rec_of(c);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        x.ka[s] = *reinterpret_cast<const bf16x8*>(rec + o_kf + s * 1024);
+        x.kb[s] = *reinterpret_cast<const bf16x8*>(rec + o_kf + (NS + s) * 1024);
+      }
+      // V in accumulator layout: lane (n, grp) receives V[4 grp + r][n], r = 0..3
+      x.va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(rec + o_v));
+      x.vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(rec + o_v + 512));
+      x.ga = *reinterpret_cast<const f32x4*>(rec + o_gd);
+      x.gb = *reinterpret_cast<const f32x4*>(rec + o_gd + 64);
+      x.tb0 = *reinterpret_cast<const bf16x8*>(rec + o_tb);
+      x.tb1h = *reinterpret_cast<const bf16x8*>(rec + o_tb + 1024);
+      x.tb1l = *reinterpret_cast<const bf16x8*>(rec + o_tb + 2048);
+      x.da = *reinterpret_cast<const f32x4*>(rec + o_gd + 128);
+      x.db = *reinterpret_cast<const f32x4*>(rec + o_gd + 192);
+      x.Gam = *reinterpret_cast<const float*>(rec + C::GD + 256);
+    };
+
+    // One pair: operands in `cur`, those of the next pair fetched into `nxt`.
+    auto pair = [&](int c, const Ops& cur, Ops& nxt) {
+      const char* rec = rec_of(c);
+      char* ob = obh + (c & 1) * C::OB;
+      wait_lgkm0();                // this pair's operands (fetched during the last pair)
+      // hand H (bf16, the state before this pair) to the output wave
+#pragma unroll
+      for (int s = 0; s < NS; ++s) *reinterpret_cast<bf16x8*>(ob + s * 1024) = Hb[s];
+      // R = K H, both tiles
+      f32x4 Ra = zero4(), Rb = zero4();
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        Ra = mma32b(cur.ka[s], Hb[s], Ra);
+        Rb = mma32b(cur.kb[s], Hb[s], Rb);
+      }
+      // K^T fragments of this pair for the state update (transposing reads)
+      s16x4_t kta[NT], ktb[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int off = o_kt + (t >> 1) * 1024 + 8 * (t & 1);
+        kta[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(rec + off));
+        ktb[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(rec + off + NS * 1024));
+      }
+      // operands of the next pair (its record has landed: see the loader)
+      fetch(c + 1, nxt);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) Hacc[t] = Hacc[t] * cur.Gam;
+      f32x4 Ya, Yb;
+      const bf16x4 va = __builtin_bit_cast(bf16x4, cur.va), vb = __builtin_bit_cast(bf16x4, cur.vb);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        Ya[i] = (float)va[i] - cur.ga[i] * Ra[i];
+        Yb[i] = (float)vb[i] - cur.gb[i] * Rb[i];
+      }
+      const bf16x4 ya = hi4(Ya), yb = hi4(Yb);
+      // U_a = Tb00 Y_a ; U_b = Tb10 Y_a + Tb11 Y_b   (Tb in hi + lo parts)
+      const f32x4 Ua = mma32b(cur.tb0, cat8(ya, ya), zero4());
+      f32x4 Ub = mma32b(cur.tb1h, cat8(ya, yb), zero4());
+      Ub = mma32b(cur.tb1l, cat8(ya, yb), Ub);
+      *reinterpret_cast<f32x4*>(ob + C::OB_U) = Ua;
+      *reinterpret_cast<f32x4*>(ob + C::OB_U + 1024) = Ub;
+      // H' = Gamma H + K^T diag(delta) U, 32-deep over both tiles
+      f32x4 Upa, Upb;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        Upa[i] = cur.da[i] * Ua[i];
+        Upb[i] = cur.db[i] * Ub[i];
+      }
+      const bf16x8 up = cat8(hi4(Upa), hi4(Upb));
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const bf16x8 kt = cat8(__builtin_bit_cast(bf16x4, kta[t]), __builtin_bit_cast(bf16x4, ktb[t]));
+        Hacc[t] = mma32b(kt, up, Hacc[t]);
+      }
+#pragma unroll
+      for (int s = 0; s < NS; ++s) Hb[s] = cat8(hi4(Hacc[2 * s]), hi4(Hacc[2 * s + 1]));
+      wait_lgkm0();                // hand-over written before the barrier
+      wg_barrier();
+    };
+
+    wg_barrier();                  // pairs 0 and 1 landed
+    Ops A, Bo;                     // two operand sets, used in turn
+    fetch(0, A);
+#pragma unroll 1
+    for (int c = 0; c < NSC; c += 2) {
+      pair(c, A, Bo);
+      if (c + 1 < NSC) pair(c + 1, Bo, A);
+    }
+    wg_barrier();                  // the output wave's last pair
+    if (hT) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          hT[sbase + (int64_t)srow(t, i) * DV + v0 + n] = Hacc[t][i];
+    }
+    return;
+  }
+
+  // -------------------------------------------------------------- output wave
+  // Pair c is computed after the barrier that ends the chain's pair c.  Its
+  // q fragments, P and gamma are read straight from global memory (the same
+  // lines are read by every d_v slice of the head), kDepth pairs ahead.
+  // The products are formed transposed, O^T = H^T Q^T diag(gamma) + U^T P^T
+  // (the same fragments with the operands swapped), so that lane (n, grp)
+  // ends with columns 4 grp .. 4 grp + 3 of token n: one 8-byte store per tile.
+  {
+    constexpr int kDepth = 4;
+    const __bf16* const qb0 = q + tok0 * DK + 8 * grp;
+    __bf16* const orow = o + (tok0 + (int64_t)n * H) * DV + v0 + 4 * grp;
+    const int ostride = H * DV;
+    const char* const obh = smem + C::OFF_OB + C::OB_H + 16 * lane;
+    struct Oin { bf16x8 qa[NS], qb[NS]; bf16x8 pf0, pf1h, pf1l; float ga, gb; };
+    auto gload = [&](Oin& x, int c) {
+      c = min(c, NSC - 1);
+#pragma unroll
+      for (int xx = 0; xx < 2; ++xx) {
+        const int t = min(32 * c + 16 * xx + n, T - 1);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const bf16x8 f = *reinterpret_cast<const bf16x8*>(qb0 + t * H * DK + 32 * s);
+          if (xx == 0) x.qa[s] = f; else x.qb[s] = f;
+        }
+      }
+      const char* wr = wsh + (int64_t)c * WsRec::BYTES;
+      x.pf0 = reinterpret_cast<const bf16x8*>(wr + WsRec::PF0)[lane];
+      x.pf1h = reinterpret_cast<const bf16x8*>(wr + WsRec::PF1H)[lane];
+      x.pf1l = reinterpret_cast<const bf16x8*>(wr + WsRec::PF1L)[lane];
+      x.ga = reinterpret_cast<const float*>(wr + WsRec::GM)[n];
+      x.gb = reinterpret_cast<const float*>(wr + WsRec::GM)[16 + n];
+    };
+    auto pair = [&](Oin& x, int c) {
+      const char* ob = obh + (c & 1) * C::OB;
+      f32x4 Oa = zero4(), Ob = zero4();   // lane (n, grp) reg i: O[token n][4 grp + i]
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const bf16x8 hb = *reinterpret_cast<const bf16x8*>(ob + s * 1024);
+        Oa = mma32b(hb, x.qa[s], Oa);
+        Ob = mma32b(hb, x.qb[s], Ob);
+      }
+      const f32x4 Ua = *reinterpret_cast<const f32x4*>(ob + C::OB_U);
+      const f32x4 Ub = *reinterpret_cast<const f32x4*>(ob + C::OB_U + 1024);
+      wait_lgkm0();   // hand-over read: the chain may overwrite it after the next barrier
+      const bf16x4 uah = hi4(Ua), ubh = hi4(Ub);
+      const bf16x4 ual = lo4(Ua, uah), ubl = lo4(Ub, ubh);
+      Oa = Oa * x.ga;
+      Ob = Ob * x.gb;
+      // O_a += P00 U_a ; O_b += P10 U_a + P11 U_b  (P and U in hi + lo parts)
+      Oa = mma32b(cat8(uah, uah), x.pf0, Oa);
+      Oa = mma32b(cat8(ual, bf16x4{}), x.pf0, Oa);
+      Ob = mma32b(cat8(uah, ubh), x.pf1h, Ob);
+      Ob = mma32b(cat8(uah, ubh), x.pf1l, Ob);
+      Ob = mma32b(cat8(ual, ubl), x.pf1h, Ob);
+      __bf16* oc = orow + (int64_t)(32 * c) * ostride;
+      if (32 * c + n < T) *reinterpret_cast<bf16x4*>(oc) = hi4(Oa);
+      if (32 * c + 16 + n < T) *reinterpret_cast<bf16x4*>(oc + 16 * ostride) = hi4(Ob);
+    };
+    Oin s0, s1, s2, s3;
+    static_assert(kDepth == 4, "four register sets below");
+    gload(s0, 0);
+    gload(s1, 1);
+    gload(s2, 2);
+    gload(s3, 3);
+    wg_barrier();    // before pair 0
+    wg_barrier();    // after the chain's pair 0
+    auto step = [&](Oin& x, int c) {
+      pair(x, c);
+      gload(x, c + kDepth);
+      wg_barrier();
+    };
+    // Whole groups of kDepth pairs first: every path around the loop then
+    // issues the loads in the same order, and the compiler's wait before each
+    // pair covers only that pair's loads.
+    int c = 0;
+#pragma unroll 1
+    for (; c + kDepth <= NSC; c += kDepth) {
+      step(s0, c);
+      step(s1, c + 1);
+      step(s2, c + 2);
+      step(s3, c + 3);
+    }
+    if (c < NSC) step(s0, c);
+    if (c + 1 < NSC) step(s1, c + 1);
+    if (c + 2 < NSC) step(s2, c + 2);
+  }
+}
+
+template <int DK>
+static hipError_t launch_pair_t(const void* q, const void* k, const void* v, const float* gate,
+                                int gate_logit, float G, const float* beta, const float* h0,
+                                void* o, float* hT, int B, int T, int H, int Dv, void* ws,
+                                hipStream_t st) {
+  const int64_t jobs = (int64_t)B * H * ((T + 31) / 32);
+  const int64_t pblocks = (jobs + kPrepWaves - 1) / kPrepWaves;
+  hipLaunchKernelGGL((chunk_prep_kernel<DK>), dim3((unsigned)pblocks), dim3(64 * kPrepWaves), 0, st,
+                     (const __bf16*)q, (const __bf16*)k, gate, gate_logit, G, beta, (char*)ws,
+                     B, T, H);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int blocks = B * H * (Dv / 16);
+  hipLaunchKernelGGL((chunk_state_kernel<DK>), dim3(blocks), dim3(192), 0, st,
+                     (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const char*)ws, h0,
+                     (__bf16*)o, hT, B, T, H, Dv);
+  return hipGetLastError();
+}
+
+long long chunk_pair_workspace_bytes(int B, int T, int H) {
+  return (long long)B * H * ((T + 31) / 32) * WsRec::BYTES;
+}
+
+hipError_t launch_chunk_fwd_pair(const void* q, const void* k, const void* v, const float* gate,
+                                 int gate_logit, float G, const float* beta, const float* h0,
+                                 void* o, float* hT, int B, int T, int H, int Dk, int Dv,
+                                 void* ws, hipStream_t st) {
+  if (Dk == 64) return launch_pair_t<64>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, ws, st);
+  if (Dk == 128) return launch_pair_t<128>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, ws, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace la

@@ -6,17 +6,22 @@
 
 namespace la {
 
+// fp32 path: one fused kernel, no workspace.
 hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v,
                             const float* gate, int gate_logit, float G,
                             const float* beta, const float* h0, void* o, float* hT,
-                            int B, int T, int H, int Dk, int Dv, int fp32,
-                            hipStream_t st);
+                            int B, int T, int H, int Dk, int Dv, hipStream_t st);
 
-// bf16 path: the state is carried across pairs of 16-token tiles.
+// bf16 path: intra-tile kernel into the workspace, then the inter-tile kernel;
+// the state is carried across pairs of 16-token tiles.
 hipError_t launch_chunk_fwd_pair(const void* q, const void* k, const void* v,
                                  const float* gate, int gate_logit, float G,
                                  const float* beta, const float* h0, void* o, float* hT,
-                                 int B, int T, int H, int Dk, int Dv, hipStream_t st);
+                                 int B, int T, int H, int Dk, int Dv, void* ws,
+                                 hipStream_t st);
+
+// Workspace bytes the bf16 path needs (0 when T == 0).
+long long chunk_pair_workspace_bytes(int B, int T, int H);
 
 hipError_t launch_decode(const void* q, const void* k, const void* v,
                          const float* gate, int gate_logit, float G,

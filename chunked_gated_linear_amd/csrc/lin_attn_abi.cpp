@@ -62,42 +62,61 @@ int hip_status(hipError_t e, const char* what) {
   return ok();
 }
 
+// Size checks shared by lin_attn_chunk_fwd and its workspace query.
+int check_chunk_sizes(int B, int T, int H, int Dk, int Dv, int dtype) {
+  if (B < 0 || T < 0 || H < 0)
+    return fail(LA_EINVAL, "sizes must be >= 0 (B=%d T=%d H=%d)", B, T, H);
+  if (dtype != LA_BF16 && dtype != LA_FP32)
+    return fail(LA_EINVAL, "dtype must be LA_BF16 (0) or LA_FP32 (1), got %d", dtype);
+  if (Dk != 64 && Dk != 128)
+    return fail(LA_EUNSUPPORTED, "Dk must be 64 or 128, got %d", Dk);
+  if (Dv < 16 || Dv > 256 || Dv % 16 != 0)
+    return fail(LA_EUNSUPPORTED, "Dv must be a multiple of 16 in [16, 256], got %d", Dv);
+  const int64_t ntok = (int64_t)B * T * H;
+  if ((int64_t)B * H * (Dv / 16) > INT32_MAX || ntok > (INT64_C(1) << 40))
+    return fail(LA_EINVAL, "problem too large (B*H*Dv/16 = %lld)",
+                (long long)((int64_t)B * H * (Dv / 16)));
+  if ((int64_t)T * H * (Dk > Dv ? Dk : Dv) > INT32_MAX || (int64_t)B * T > INT32_MAX)
+    return fail(LA_EINVAL, "problem too large (T*H*max(Dk,Dv) or B*T exceeds 2^31)");
+  return LA_OK;
+}
+
+long long chunk_workspace(int B, int T, int H, int dtype) {
+  return dtype == LA_BF16 ? la::chunk_pair_workspace_bytes(B, T, H) : 0;
+}
+
 }  // namespace
 
 extern "C" {
 
 const char* lin_attn_last_error(void) { return g_err.c_str(); }
 
-int lin_attn_version(void) { return 100; }
+int lin_attn_version(void) { return 200; }
+
+long long lin_attn_chunk_fwd_workspace_size(int B, int T, int H, int Dk, int Dv, int dtype) {
+  if (check_chunk_sizes(B, T, H, Dk, Dv, dtype)) return -1;
+  ok();
+  return chunk_workspace(B, T, H, dtype);
+}
 
 int lin_attn_chunk_fwd(const void* q, const void* k, const void* v, const float* gate,
                        int gate_mode, float G, const float* beta, const float* h0, void* o,
                        float* hT, int B, int T, int H, int Dk, int Dv, int dtype,
-                       void* stream) {
-  if (B < 0 || T < 0 || H < 0)
-    return fail(LA_EINVAL, "sizes must be >= 0 (B=%d T=%d H=%d)", B, T, H);
-  if (dtype != LA_BF16 && dtype != LA_FP32)
-    return fail(LA_EINVAL, "dtype must be LA_BF16 (0) or LA_FP32 (1), got %d", dtype);
+                       void* workspace, long long workspace_bytes, void* stream) {
+  if (int rc = check_chunk_sizes(B, T, H, Dk, Dv, dtype)) return rc;
   if (int rc = check_gate_scalars(gate_mode, G)) return rc;
-  if (Dk != 64 && Dk != 128)
-    return fail(LA_EUNSUPPORTED, "Dk must be 64 or 128, got %d", Dk);
-  if (Dv < 16 || Dv > 256 || Dv % 16 != 0)
-    return fail(LA_EUNSUPPORTED, "Dv must be a multiple of 16 in [16, 256], got %d", Dv);
   const int64_t es = dtype == LA_BF16 ? 2 : 4;
   const int64_t ntok = (int64_t)B * T * H;
   const int64_t nst = (int64_t)B * H * Dk * Dv;
-  if ((int64_t)B * H * (Dv / 16) > INT32_MAX || ntok > (INT64_C(1) << 40))
-    return fail(LA_EINVAL, "problem too large (B*H*Dv/16 = %lld)",
-                (long long)((int64_t)B * H * (Dv / 16)));
-  if ((int64_t)T * H * (Dk > Dv ? Dk : Dv) > INT32_MAX || (int64_t)B * T > INT32_MAX)
-    return fail(LA_EINVAL, "problem too large (T*H*max(Dk,Dv) or B*T exceeds 2^31)");
   if (B == 0 || H == 0) return ok();
   const unsigned ea = dtype == LA_BF16 ? 2u : 4u;
+  const long long wsz = T > 0 ? chunk_workspace(B, T, H, dtype) : 0;
   if (T > 0) {
-    // q and k are read as 16-byte vectors; everything else element-wise
+    // q, k and v are read as 16-byte vectors, bf16 o written as 8-byte vectors;
+    // gate and beta element-wise
     const struct { const char* nm; const void* p; unsigned a; } req[] = {
-        {"q", q, 16u}, {"k", k, 16u}, {"v", v, ea}, {"gate", gate, 4u}, {"beta", beta, 4u},
-        {"o", o, ea}};
+        {"q", q, 16u}, {"k", k, 16u}, {"v", v, 16u}, {"gate", gate, 4u}, {"beta", beta, 4u},
+        {"o", o, dtype == LA_BF16 ? 8u : ea}};
     for (const auto& r : req) {
       if (!r.p) return fail(LA_EINVAL, "%s must not be NULL", r.nm);
       if (!aligned(r.p, r.a)) return fail(LA_EINVAL, "%s must be %u-byte aligned", r.nm, r.a);
@@ -105,6 +124,13 @@ int lin_attn_chunk_fwd(const void* q, const void* k, const void* v, const float*
   }
   if (h0 && !aligned(h0, 4u)) return fail(LA_EINVAL, "h0 must be 4-byte aligned");
   if (hT && !aligned(hT, 4u)) return fail(LA_EINVAL, "hT must be 4-byte aligned");
+  if (wsz > 0) {
+    if (!workspace) return fail(LA_EINVAL, "workspace must not be NULL (%lld bytes needed)", wsz);
+    if (!aligned(workspace, 256u)) return fail(LA_EINVAL, "workspace must be 256-byte aligned");
+    if (workspace_bytes < wsz)
+      return fail(LA_EINVAL, "workspace too small: %lld bytes given, %lld needed",
+                  workspace_bytes, wsz);
+  }
 
   const Span sq = span("q", q, ntok * Dk * es), sk = span("k", k, ntok * Dk * es),
              sv = span("v", v, ntok * Dv * es), sg = span("gate", gate, ntok * 4),
@@ -112,6 +138,9 @@ int lin_attn_chunk_fwd(const void* q, const void* k, const void* v, const float*
              so = span("o", o, T > 0 ? ntok * Dv * es : 0), shT = span("hT", hT, nst * 4);
   for (const Span& in : {sq, sk, sv, sg, sb, sh0, shT})
     if (overlap(so, in)) return fail(LA_EINVAL, "o overlaps %s", in.name);
+  const Span sw = span("workspace", workspace, wsz);
+  for (const Span& in : {sq, sk, sv, sg, sb, sh0, so, shT})
+    if (overlap(sw, in)) return fail(LA_EINVAL, "workspace overlaps %s", in.name);
   for (const Span& in : {sq, sk, sv, sg, sb})
     if (overlap(shT, in)) return fail(LA_EINVAL, "hT overlaps %s", in.name);
   if (hT && h0 && hT != h0 && overlap(shT, sh0))
@@ -122,8 +151,11 @@ int lin_attn_chunk_fwd(const void* q, const void* k, const void* v, const float*
     if (!hT || hT == h0) return ok();
     return hip_status(la::launch_state_init(h0, hT, nst, st), "state init launch");
   }
-  hipError_t e = la::launch_chunk_fwd(q, k, v, gate, gate_mode == LA_GATE_BOUNDED_LOGIT, G,
-                                      beta, h0, o, hT, B, T, H, Dk, Dv, dtype == LA_FP32, st);
+  const int logit = gate_mode == LA_GATE_BOUNDED_LOGIT;
+  hipError_t e = dtype == LA_FP32
+      ? la::launch_chunk_fwd(q, k, v, gate, logit, G, beta, h0, o, hT, B, T, H, Dk, Dv, st)
+      : la::launch_chunk_fwd_pair(q, k, v, gate, logit, G, beta, h0, o, hT, B, T, H, Dk, Dv,
+                                  workspace, st);
   return hip_status(e, "chunk_fwd launch");
 }
 

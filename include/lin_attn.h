@@ -21,11 +21,11 @@
  * Conventions for every entry point
  *  - Every array pointer is a DEVICE pointer owned by the caller.  The library
  *    never frees, keeps or reallocates caller memory, and allocates no device
- *    memory of its own.
+ *    memory of its own; scratch space comes in as a caller-owned workspace.
  *  - Arrays are dense, row-major, last dimension contiguous, and aligned to
- *    their element size; arrays the kernels read as 16-byte vectors must be
- *    16-byte aligned (q and k of lin_attn_chunk_fwd, S of
- *    lin_attn_decode_step).  Element type of q, k, v and o is given by `dtype`
+ *    their element size; arrays the kernels access as vectors need more: q, k
+ *    and v of lin_attn_chunk_fwd 16 bytes, its o 8 bytes in bf16, and S of
+ *    lin_attn_decode_step 16 bytes.  Element type of q, k, v and o is given by `dtype`
  *    (LA_BF16 = bfloat16, LA_FP32 = float32); gate, beta, h0, hT and S are
  *    always float32.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
@@ -67,6 +67,17 @@ extern "C" {
 #define LA_GATE_BOUNDED_LOGIT  1  /* gate holds x_t; g_t = -G * sigmoid(x_t) */
 
 /*
+ * lin_attn_chunk_fwd_workspace_size -- bytes of device workspace that
+ * lin_attn_chunk_fwd needs for these sizes: 0 when it needs none (dtype
+ * LA_FP32, or T = 0), and -1 (with lin_attn_last_error() set) when the sizes
+ * are invalid or unsupported.  For LA_BF16 it is B * H * ceil(T / 32) * 6656:
+ * the state-independent per-tile operators (the decay-weighted solve T diag(beta)
+ * and the masked Q K^T block, see below) are computed once per head and kept
+ * there between the two kernels of the pass.
+ */
+long long lin_attn_chunk_fwd_workspace_size(int B, int T, int H, int Dk, int Dv, int dtype);
+
+/*
  * lin_attn_chunk_fwd -- chunked forward pass over a whole sequence.
  *
  * Computes o_t for every token and the final state h_T of the recurrence
@@ -74,7 +85,9 @@ extern "C" {
  * a tile the token interactions (the diagonal block) and the contribution of
  * the carried state (the "historical state -> current token" block) are
  * matrix products, and the state is carried from tile to tile ("Core
- * Technologies ...", sec. 2.1; "How Trillion-Scale ...", sec. 3.1).
+ * Technologies ...", sec. 2.1; "How Trillion-Scale ...", sec. 3.1).  In bf16
+ * an intra-tile kernel first prepares every tile independently into the
+ * workspace, then an inter-tile kernel carries the state.
  *
  *   q     [B, T, H, Dk]  dtype          queries
  *   k     [B, T, H, Dk]  dtype          keys (expected unit norm; not checked)
@@ -86,11 +99,19 @@ extern "C" {
  *   o     [B, T, H, Dv]  dtype          output, rounded to nearest-even from
  *                                       float32 when dtype is LA_BF16
  *   hT    [B, H, Dk, Dv] float32 or NULL (NULL = final state not written)
+ *   workspace, workspace_bytes
+ *                        device scratch of at least
+ *                        lin_attn_chunk_fwd_workspace_size(...) bytes, 256-byte
+ *                        aligned, owned by the caller; its contents on entry do
+ *                        not matter and are overwritten.  May be NULL when the
+ *                        size is 0.  Two calls in flight at the same time must
+ *                        not share a workspace.
  *   Dk in {64, 128}; Dv a multiple of 16 in [16, 256]; B, T, H >= 0.
  *
  * Aliasing: o must not overlap any input.  hT may be the very same pointer as
  * h0 (the state is then updated in place); any other overlap of hT with an
- * input or with o is rejected.  T need not be a multiple of 16: the last tile
+ * input or with o is rejected, and so is any overlap of the workspace with an
+ * argument array.  T need not be a multiple of 16: the last tile
  * behaves as if padded with tokens q = k = v = 0, g = 0, beta = 0, which leave
  * the state unchanged.
  */
@@ -99,6 +120,7 @@ int lin_attn_chunk_fwd(const void* q, const void* k, const void* v,
                        const float* beta, const float* h0,
                        void* o, float* hT,
                        int B, int T, int H, int Dk, int Dv, int dtype,
+                       void* workspace, long long workspace_bytes,
                        void* stream);
 
 /*

@@ -56,12 +56,13 @@ def fake(i, size=1 << 30):
 def chunk(**kw):
     a = dict(q=fake(0), k=fake(1), v=fake(2), gate=fake(3), gate_mode=0, G=5.0,
              beta=fake(4), h0=None, o=fake(5), hT=fake(6), B=1, T=64, H=2, Dk=128,
-             Dv=128, dtype=0, stream=None)
+             Dv=128, dtype=0, ws=fake(8), ws_bytes=1 << 30, stream=None)
     a.update(kw)
     L = N.lib()
     rc = L.lin_attn_chunk_fwd(a["q"], a["k"], a["v"], a["gate"], a["gate_mode"], a["G"],
                               a["beta"], a["h0"], a["o"], a["hT"], a["B"], a["T"], a["H"],
-                              a["Dk"], a["Dv"], a["dtype"], a["stream"])
+                              a["Dk"], a["Dv"], a["dtype"], a["ws"], a["ws_bytes"],
+                              a["stream"])
     return rc, L.lin_attn_last_error().decode()
 
 
@@ -87,11 +88,36 @@ def chunk(**kw):
     (dict(o=fake(6)), N.LA_EINVAL, "o overlaps hT"),
     (dict(hT=fake(3)), N.LA_EINVAL, "hT overlaps gate"),
     (dict(h0=fake(7), hT=fake(7) + 4096), N.LA_EINVAL, "partially overlaps h0"),
+    (dict(v=fake(2) + 8), N.LA_EINVAL, "v must be 16-byte aligned"),
+    (dict(o=fake(5) + 4), N.LA_EINVAL, "o must be 8-byte aligned"),
+    (dict(ws=None), N.LA_EINVAL, "workspace must not be NULL"),
+    (dict(ws=fake(8) + 128), N.LA_EINVAL, "workspace must be 256-byte aligned"),
+    (dict(ws_bytes=2 * 2 * 6656 - 1), N.LA_EINVAL, "workspace too small"),
+    (dict(ws=fake(0) + 4096), N.LA_EINVAL, "workspace overlaps q"),
+    (dict(ws=fake(5)), N.LA_EINVAL, "workspace overlaps o"),
 ])
 def test_chunk_fwd_rejects(kw, code, needle):
     rc, msg = chunk(**kw)
     assert rc == code, (rc, msg)
     assert needle in msg
+
+
+def test_workspace_size():
+    L = N.lib()
+    ws = L.lin_attn_chunk_fwd_workspace_size
+    # bf16: one 6656-byte record per (sequence, head, 32 tokens)
+    assert ws(1, 64, 2, 128, 128, N.LA_BF16) == 2 * 2 * 6656
+    assert ws(4, 8192, 16, 128, 128, N.LA_BF16) == 4 * 16 * 256 * 6656
+    assert ws(1, 33, 3, 64, 16, N.LA_BF16) == 3 * 2 * 6656
+    assert ws(2, 0, 4, 128, 64, N.LA_BF16) == 0
+    # fp32 runs one fused kernel without a workspace
+    assert ws(1, 4096, 8, 128, 128, N.LA_FP32) == 0
+    assert ws(1, 64, 2, 96, 128, N.LA_BF16) == -1
+    assert "Dk" in L.lin_attn_last_error().decode()
+    assert ws(-1, 64, 2, 128, 128, N.LA_BF16) == -1
+    # the fp32 path accepts a NULL workspace
+    rc, msg = chunk(dtype=N.LA_FP32, ws=None, ws_bytes=0, o=fake(5), q=fake(0) + 8)
+    assert rc == N.LA_EINVAL and "q must be 16-byte aligned" in msg
 
 
 def test_chunk_fwd_empty_is_noop():
