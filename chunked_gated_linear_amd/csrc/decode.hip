@@ -12,89 +12,92 @@
 // Roofline: 2 * Dk * Dv * 4 bytes of state traffic per head and step dominate
 // (about 9 * Dk * Dv flops against 8 * Dk * Dv bytes): HBM-bound.
 //
-// Layout: one 256-thread workgroup per (b, h).  Thread (rg, c4) holds columns
-// 4*c4 .. 4*c4+3 of rows rg, rg + RG, rg + 2*RG, ... as float4, so every row of
-// the state is read and written as 32 consecutive 16-byte pieces.
+// Layout: a persistent grid of 512-thread workgroups walks the (b, h) list in
+// steps of the grid size, so that the heads in flight at any time are
+// neighbours in memory.  Thread (rg, c4) holds columns 4*c4 .. 4*c4+3 of rows
+// rg, rg + RG, rg + 2*RG, ... as float4, so every row of the state is read and
+// written as consecutive 16-byte pieces.  The state is streamed once per step
+// (it does not fit the last-level cache), so its loads and stores are marked
+// non-temporal.
 #include "la_device.h"
 #include "la_launch.h"
 
 namespace la {
 
+constexpr int kDecodeThreads = 512;
+constexpr int kDecodeGrid = 2048;
+
 template <typename E, int DK, int DV>
-__global__ __launch_bounds__(256) void decode_kernel(
+__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ gate, int gate_logit, float G,
-    const float* __restrict__ beta, float* __restrict__ S, E* __restrict__ o) {
-  constexpr int NC4 = DV / 4;      // float4 columns per row
-  constexpr int RG = 256 / NC4;    // row groups
-  constexpr int RPT = DK / RG;     // rows per thread
-  static_assert(RG * NC4 == 256 && RPT * RG == DK, "decode tiling");
+    const float* __restrict__ beta, float* __restrict__ S, E* __restrict__ o, int BH) {
+  constexpr int NC4 = DV / 4;                  // float4 columns per row
+  constexpr int RG = kDecodeThreads / NC4;     // row groups
+  constexpr int RPT = DK / RG;                 // rows per thread
+  static_assert(RG * NC4 == kDecodeThreads && RPT * RG == DK, "decode tiling");
+  static_assert(DK <= kDecodeThreads && DV <= kDecodeThreads, "one thread per element of k, q, v");
 
   __shared__ float sk[DK], sq[DK];
-  __shared__ float4 pa[RG][NC4], pb[RG][NC4];
+  __shared__ f32x4 pa[RG][NC4], pb[RG][NC4];
   __shared__ float su[DV];
   __shared__ float skq;
 
-  const int64_t bh = blockIdx.x;
   const int tid = threadIdx.x;
   const int c4 = tid % NC4, rg = tid / NC4;
 
-  float gx = gate[bh];
-  const float g = gate_logit ? bounded_gate(gx, G) : gx;
-  const float a = __expf(g);
-  const float bt = beta[bh];
+  for (int64_t bh = blockIdx.x; bh < BH; bh += gridDim.x) {
+    const float gx = gate[bh];
+    const float g = gate_logit ? bounded_gate(gx, G) : gx;
+    const float a = __expf(g);
+    const float bt = beta[bh];
 
-  if (tid < DK) {
-    sk[tid] = Elt<E>::to_f(k[bh * DK + tid]);
-    sq[tid] = Elt<E>::to_f(q[bh * DK + tid]);
-  }
-  float4* Sh = reinterpret_cast<float4*>(S + bh * DK * DV);
-  float4 s[RPT];
-#pragma unroll
-  for (int i = 0; i < RPT; ++i) s[i] = Sh[(rg + RG * i) * NC4 + c4];
-  __syncthreads();
-
-  float4 pk = make_float4(0.f, 0.f, 0.f, 0.f), pq = pk;
-#pragma unroll
-  for (int i = 0; i < RPT; ++i) {
-    const float kr = sk[rg + RG * i], qr = sq[rg + RG * i];
-    pk.x += kr * s[i].x; pk.y += kr * s[i].y; pk.z += kr * s[i].z; pk.w += kr * s[i].w;
-    pq.x += qr * s[i].x; pq.y += qr * s[i].y; pq.z += qr * s[i].z; pq.w += qr * s[i].w;
-  }
-  pa[rg][c4] = pk;
-  pb[rg][c4] = pq;
-  if (tid < 64) {  // k . q, one wave, fixed order
-    float p = 0.f;
-    for (int d = tid; d < DK; d += 64) p += sk[d] * sq[d];
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) p += __shfl_xor(p, off);
-    if (tid == 0) skq = p;
-  }
-  __syncthreads();
-
-  if (tid < DV) {
-    const int cq = tid >> 2, cr = tid & 3;
-    float hk = 0.f, hq = 0.f;
-#pragma unroll
-    for (int r = 0; r < RG; ++r) {
-      const float4 x = pa[r][cq], y = pb[r][cq];
-      hk += cr == 0 ? x.x : cr == 1 ? x.y : cr == 2 ? x.z : x.w;
-      hq += cr == 0 ? y.x : cr == 1 ? y.y : cr == 2 ? y.z : y.w;
+    if (tid < DK) {
+      sk[tid] = Elt<E>::to_f(k[bh * DK + tid]);
+      sq[tid] = Elt<E>::to_f(q[bh * DK + tid]);
     }
-    const float u = bt * (Elt<E>::to_f(v[bh * DV + tid]) - a * hk);
-    su[tid] = u;
-    o[bh * DV + tid] = Elt<E>::from_f(a * hq + skq * u);
-  }
-  __syncthreads();
-
-  const float4 u4 = reinterpret_cast<const float4*>(su)[c4];
+    f32x4* Sh = reinterpret_cast<f32x4*>(S + bh * DK * DV);
+    f32x4 s[RPT];
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) {
-    const float kr = sk[rg + RG * i];
-    float4 x = s[i];
-    x.x = a * x.x + kr * u4.x; x.y = a * x.y + kr * u4.y;
-    x.z = a * x.z + kr * u4.z; x.w = a * x.w + kr * u4.w;
-    Sh[(rg + RG * i) * NC4 + c4] = x;
+    for (int i = 0; i < RPT; ++i) s[i] = __builtin_nontemporal_load(Sh + (rg + RG * i) * NC4 + c4);
+    __syncthreads();
+
+    f32x4 pk = zero4(), pq = zero4();
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      pk += sk[rg + RG * i] * s[i];
+      pq += sq[rg + RG * i] * s[i];
+    }
+    pa[rg][c4] = pk;
+    pb[rg][c4] = pq;
+    if (tid < 64) {  // k . q, one wave, fixed order
+      float p = 0.f;
+      for (int d = tid; d < DK; d += 64) p += sk[d] * sq[d];
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) p += __shfl_xor(p, off);
+      if (tid == 0) skq = p;
+    }
+    __syncthreads();
+
+    if (tid < DV) {
+      const int cq = tid >> 2, cr = tid & 3;
+      float hk = 0.f, hq = 0.f;
+#pragma unroll
+      for (int r = 0; r < RG; ++r) {
+        hk += pa[r][cq][cr];
+        hq += pb[r][cq][cr];
+      }
+      const float u = bt * (Elt<E>::to_f(v[bh * DV + tid]) - a * hk);
+      su[tid] = u;
+      o[bh * DV + tid] = Elt<E>::from_f(a * hq + skq * u);
+    }
+    __syncthreads();
+
+    const f32x4 u4 = reinterpret_cast<const f32x4*>(su)[c4];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
+      __builtin_nontemporal_store(a * s[i] + sk[rg + RG * i] * u4, Sh + (rg + RG * i) * NC4 + c4);
+    __syncthreads();   // the shared buffers are reused by the next (b, h)
   }
 }
 
@@ -103,9 +106,10 @@ static hipError_t launch_decode_t(const void* q, const void* k, const void* v,
                                   const float* gate, int gate_logit, float G,
                                   const float* beta, float* S, void* o, int BH,
                                   hipStream_t st) {
-  hipLaunchKernelGGL((decode_kernel<E, DK, DV>), dim3(BH), dim3(256), 0, st,
+  const int grid = BH < kDecodeGrid ? BH : kDecodeGrid;
+  hipLaunchKernelGGL((decode_kernel<E, DK, DV>), dim3(grid), dim3(kDecodeThreads), 0, st,
                      (const E*)q, (const E*)k, (const E*)v, gate, gate_logit, G,
-                     beta, S, (E*)o);
+                     beta, S, (E*)o, BH);
   return hipGetLastError();
 }
 
