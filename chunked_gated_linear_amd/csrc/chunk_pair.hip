@@ -30,11 +30,11 @@
 //   wave 0 "chain"   the fp32 state slice (d_k x 16) in registers; per pair:
 //                    K H, U, the 32-deep state update, all on MFMA;
 //   wave 1 "output"  diag(gamma) Q H + P U on MFMA and the bf16 stores, one
-//                    pair behind the chain; q, P and gamma come straight from
-//                    global memory, several pairs ahead;
-//   wave 2 "loader"  streams K, V and the chain's part of the workspace into a
-//                    ring of LDS records with direct global->LDS loads, a few
-//                    pairs ahead of the chain.
+//                    pair behind the chain; q comes through the loader, P and
+//                    gamma straight from global memory, several pairs ahead;
+//   wave 2 "loader"  streams k, q, v and the chain's part of the workspace
+//                    into a ring of LDS records with direct global->LDS loads,
+//                    a few pairs ahead of the chain.
 //   One workgroup barrier per pair.  The state (bf16) and U reach the output
 //   wave through LDS, double buffered by pair parity.
 //
@@ -70,10 +70,15 @@ struct WsRec {
   static constexpr int BYTES = 6656;
 };
 
-// K fragment slot inside a 1 KB block: (grp, m) -> grp*16 + (m ^ 4grp).  The
-// XOR keeps the transposing reads of the state update free of bank conflicts;
-// ordinary fragment reads stay lane-contiguous.
-__device__ inline int kslot(int grp, int m) { return grp * 16 + (m ^ (4 * grp)); }
+// Rows of k or q in LDS: a 1 KB block holds 16 token rows x 64 B (32 elements
+// of d_k); 16-byte chunk g of row t sits in slot rslot(t, g) = 4 t + (g ^ sw(t)),
+// sw(t) = (t >> 1) & 3.  A direct-to-LDS load fills a block with lanes in slot
+// order, so each 16-lane quarter of the load covers 4 whole 64-byte rows (a
+// quarter spanning 16 rows costs the address unit about three times as much);
+// the XOR keeps the fragment reads (row n, chunk grp in lane (n, grp)) free of
+// bank conflicts.
+__device__ inline int rsw(int t) { return (t >> 1) & 3; }
+__device__ inline int rslot(int t, int g) { return 4 * t + (g ^ rsw(t)); }
 
 __device__ inline bf16x4 hi4(f32x4 x) {
   return bf16x4{(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
@@ -318,16 +323,17 @@ __global__ __launch_bounds__(64 * kPrepWaves) void chunk_prep_kernel(
 
 template <int DK>
 struct CfgS {
-  static constexpr int NBUF = 10;              // LDS records in the loader's ring
+  static constexpr int NBUF = 7;               // LDS records in the loader's ring
   static constexpr int NT = DK / 16, NS = DK / 32;
   // LDS record of one pair (byte offsets)
-  static constexpr int KF = 0;                 // [tile][NS][64 slots] x 16 B, slots as kslot
-  static constexpr int VF = KF + 2 * NS * 1024;   // [32 tokens][16 columns] bf16
+  static constexpr int KF = 0;                 // [tile][NS] blocks of k rows, slots as rslot
+  static constexpr int QF = KF + 2 * NS * 1024;   // the same for q
+  static constexpr int VF = QF + 2 * NS * 1024;   // [32 tokens][16 columns] bf16
   static constexpr int TB = VF + 1024;         // TB0 | TB1H | TB1L (workspace bytes 0..3071)
   static constexpr int GD = TB + 3072;         // gamma | delta | Gamma (workspace bytes 6144..6655)
   static constexpr int REC = GD + 512;
-  // loads per record: K blocks, V, TB, GD
-  static constexpr int LPP = 2 * NS + 1 + 3 + 1;
+  // loads per record: k and q blocks, V, TB, GD
+  static constexpr int LPP = 4 * NS + 1 + 3 + 1;
   // chain -> output hand-over, double buffered by pair parity; placed first so
   // that its addresses fit the 16-bit offset field of LDS instructions
   static constexpr int OB_H = 0;               // [NS][64] x 16 B   H (bf16)
@@ -395,22 +401,26 @@ __global__ __launch_bounds__(192) void chunk_state_kernel(
   if (wave == 2) {
     // ------------------------------------------------------------ loader
     // Ring of NBUF records; pair c lives in record c % NBUF.  During pair c
-    // the chain reads records c and c + 1, so when the barrier before pair c
-    // has passed, pairs c + 1 and c + 2 must have landed and the record of
-    // pair c - 1 is free for pair c + NBUF - 1.  Pair indices are clamped so
-    // that every load is valid and the load count never varies.
-    const __bf16* const kb0 = k + tok0 * DK + 8 * grp;
+    // the chain reads records c and c + 1 and the output wave record c - 1,
+    // so the record of pair c - 2 is free for pair c + NBUF - 2, and pairs up
+    // to c + 2 must have landed by the barrier that ends pair c.  Pair indices
+    // are clamped so that every load is valid and the load count never varies.
+    // Lane L fills slot L of a block: row L / 4, chunk (L % 4) ^ sw(row).
+    const int lrow = lane >> 2, lchunk = (lane & 3) ^ rsw(lane >> 2);
+    const __bf16* const kb0 = k + tok0 * DK + 8 * lchunk;
+    const __bf16* const qb0 = q + tok0 * DK + 8 * lchunk;
     const __bf16* const vb0 = v + tok0 * DV + v0 + 8 * (lane & 1);
     auto issue = [&](int c) {
       c = min(c, NSC - 1);
       char* rec = rec_of(c);
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
-        // slot (grp, m) of a block holds token m: lane (n, grp) fetches token n ^ 4grp
-        const int t = min(32 * c + 16 * x + (n ^ (4 * grp)), T - 1);
-        const __bf16* src = kb0 + t * H * DK;
+        const int roff = min(32 * c + 16 * x + lrow, T - 1) * H * DK;
 #pragma unroll
-        for (int s = 0; s < NS; ++s) lds_dma16(src + 32 * s, rec + C::KF + (x * NS + s) * 1024);
+        for (int s = 0; s < NS; ++s) {
+          lds_dma16(kb0 + roff + 32 * s, rec + C::KF + (x * NS + s) * 1024);
+          lds_dma16(qb0 + roff + 32 * s, rec + C::QF + (x * NS + s) * 1024);
+        }
       }
       {  // V: lane L fetches 8 columns (half L % 2) of token L / 2 of the pair
         const int t = min(32 * c + (lane >> 1), T - 1);
@@ -421,14 +431,15 @@ __global__ __launch_bounds__(192) void chunk_state_kernel(
       for (int i = 0; i < 3; ++i) lds_dma16(wr + i * 1024, rec + C::TB + i * 1024);
       if (lane < 32) lds_dma16(wr + WsRec::GM, rec + C::GD);
     };
-    constexpr int kAhead = (NBUF - 3) * C::LPP;   // loads allowed in flight at a barrier
+    constexpr int kAhead = (NBUF - 4) * C::LPP;   // loads allowed in flight at a barrier
+    static_assert(kAhead <= 63, "vmcnt range");
 #pragma unroll 1
-    for (int c = 0; c < NBUF - 1; ++c) issue(c);
+    for (int c = 0; c < NBUF - 2; ++c) issue(c);
     wait_vmcnt<kAhead>();                          // pairs 0 and 1 landed
     wg_barrier();
 #pragma unroll 1
     for (int c = 0; c <= NSC; ++c) {
-      issue(c + NBUF - 1);                         // into the record of pair c - 1
+      issue(c + NBUF - 2);                         // into the record of pair c - 2
       wait_vmcnt<kAhead>();                        // pair c + 2 landed
       wg_barrier();
     }
@@ -450,9 +461,9 @@ __global__ __launch_bounds__(192) void chunk_state_kernel(
 #pragma unroll
     for (int s = 0; s < NS; ++s) Hb[s] = cat8(hi4(Hacc[2 * s]), hi4(Hacc[2 * s + 1]));
     // Per-lane byte offsets inside a record (the record base is added per pair).
-    const int o_kf = 16 * kslot(grp, n);                 // K fragment rows
+    const int o_kf = 16 * rslot(n, grp);                 // K fragment rows
     // transposing read: lane (j, grp) points at K[4 grp + j/4][rho chunk j%4]
-    const int o_kt = ((n & 3) * 16 + ((4 * grp + (n >> 2)) ^ (4 * (n & 3)))) * 16;
+    const int o_kt = 16 * rslot(4 * grp + (n >> 2), n & 3);
     const int o_v = C::VF + 8 * lane;                    // V, transposing read
     const int o_tb = C::TB + 16 * lane;
     const int o_gd = C::GD + 16 * grp;
@@ -560,30 +571,22 @@ __global__ __launch_bounds__(192) void chunk_state_kernel(
   }
 
   // -------------------------------------------------------------- output wave
-  // Pair c is computed after the barrier that ends the chain's pair c.  Its
-  // q fragments, P and gamma are read straight from global memory (the same
-  // lines are read by every d_v slice of the head), kDepth pairs ahead.
+  // Pair c is computed after the barrier that ends the chain's pair c.  Its q
+  // fragments come from the pair's record; P and gamma are read straight from
+  // global memory (contiguous lines, shared by every d_v slice of the head),
+  // kDepth pairs ahead.
   // The products are formed transposed, O^T = H^T Q^T diag(gamma) + U^T P^T
   // (the same fragments with the operands swapped), so that lane (n, grp)
   // ends with columns 4 grp .. 4 grp + 3 of token n: one 8-byte store per tile.
   {
     constexpr int kDepth = 4;
-    const __bf16* const qb0 = q + tok0 * DK + 8 * grp;
     __bf16* const orow = o + (tok0 + (int64_t)n * H) * DV + v0 + 4 * grp;
     const int ostride = H * DV;
     const char* const obh = smem + C::OFF_OB + C::OB_H + 16 * lane;
-    struct Oin { bf16x8 qa[NS], qb[NS]; bf16x8 pf0, pf1h, pf1l; float ga, gb; };
+    const int o_qf = C::QF + 16 * rslot(n, grp);
+    struct Oin { bf16x8 pf0, pf1h, pf1l; float ga, gb; };
     auto gload = [&](Oin& x, int c) {
       c = min(c, NSC - 1);
-#pragma unroll
-      for (int xx = 0; xx < 2; ++xx) {
-        const int t = min(32 * c + 16 * xx + n, T - 1);
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          const bf16x8 f = *reinterpret_cast<const bf16x8*>(qb0 + t * H * DK + 32 * s);
-          if (xx == 0) x.qa[s] = f; else x.qb[s] = f;
-        }
-      }
       const char* wr = wsh + (int64_t)c * WsRec::BYTES;
       x.pf0 = reinterpret_cast<const bf16x8*>(wr + WsRec::PF0)[lane];
       x.pf1h = reinterpret_cast<const bf16x8*>(wr + WsRec::PF1H)[lane];
@@ -593,12 +596,15 @@ __global__ __launch_bounds__(192) void chunk_state_kernel(
     };
     auto pair = [&](Oin& x, int c) {
       const char* ob = obh + (c & 1) * C::OB;
+      const char* qf = rec_of(c) + o_qf;
       f32x4 Oa = zero4(), Ob = zero4();   // lane (n, grp) reg i: O[token n][4 grp + i]
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const bf16x8 hb = *reinterpret_cast<const bf16x8*>(ob + s * 1024);
-        Oa = mma32b(hb, x.qa[s], Oa);
-        Ob = mma32b(hb, x.qb[s], Ob);
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qf + s * 1024);
+        const bf16x8 qb = *reinterpret_cast<const bf16x8*>(qf + (NS + s) * 1024);
+        Oa = mma32b(hb, qa, Oa);
+        Ob = mma32b(hb, qb, Ob);
       }
       const f32x4 Ua = *reinterpret_cast<const f32x4*>(ob + C::OB_U);
       const f32x4 Ub = *reinterpret_cast<const f32x4*>(ob + C::OB_U + 1024);
