@@ -140,6 +140,7 @@ __device__ inline void lds_dma16(const void* g, void* lds) {
 
 constexpr int kPrepWaves = 4;
 constexpr int kPrepScr = 2304;   // per wave: A00 (then T00), A11 (then T11), beta[32], G[32]
+constexpr int kPrepRows = 8192;  // per wave: one pair's rows of k or q, as fragment blocks
 
 template <int DK>
 __global__ __launch_bounds__(64 * kPrepWaves) void chunk_prep_kernel(
@@ -148,7 +149,7 @@ __global__ __launch_bounds__(64 * kPrepWaves) void chunk_prep_kernel(
     char* __restrict__ ws, int B, int T, int H) {
   constexpr int NS = DK / 32;
   using F = Elt<float>;
-  __shared__ __attribute__((aligned(16))) char smem[kPrepWaves * kPrepScr];
+  __shared__ __attribute__((aligned(16))) char smem[kPrepWaves * (kPrepScr + kPrepRows)];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, grp = lane >> 4;
@@ -159,7 +160,8 @@ __global__ __launch_bounds__(64 * kPrepWaves) void chunk_prep_kernel(
   const int c = (int)(job - (int64_t)head * NSC);
   const int b = head / H, h = head - b * H;
 
-  char* scr = smem + wave * kPrepScr;
+  char* scr = smem + wave * (kPrepScr + kPrepRows);
+  char* rows = scr + kPrepScr;
   float* sA0 = reinterpret_cast<float*>(scr);
   float* sA1 = reinterpret_cast<float*>(scr + 1024);
   float* sB = reinterpret_cast<float*>(scr + 2048);
@@ -169,20 +171,45 @@ __global__ __launch_bounds__(64 * kPrepWaves) void chunk_prep_kernel(
   // Loads (rows clamped to T-1: padding tokens need no masking of q or k --
   // with beta = 0 and g = 0 their rows of T are unit vectors and their columns
   // of Tb are zero, so they contribute nothing anywhere).
+  // k and q rows are loaded whole (each 16-lane quarter of a load covers one
+  // 256-byte row, or two 128-byte rows at d_k = 64; a quarter spanning 16
+  // rows would cost the address unit about three times as much) and turned
+  // into MFMA fragments through LDS, in the row blocks of rslot.
   const int64_t tok0 = (int64_t)b * T * H + h;   // token (b, 0, h)
-  const __bf16* const kb0 = k + tok0 * DK + 8 * grp;
-  const __bf16* const qb0 = q + tok0 * DK + 8 * grp;
+  constexpr int NL = DK / 16;                    // 1 KB loads per pair and matrix
+  bf16x8 kr[NL], qr[NL];
+  int lofs[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int f = (64 * i + lane) * 16;           // byte of the pair's 32 x DK block
+    const int r = f / (2 * DK), c16 = (f % (2 * DK)) / 16;
+    const int t = min(32 * c + r, T - 1);
+    const int off = t * H * DK + 8 * c16;         // fits in 32 bits (checked on the host)
+    kr[i] = *reinterpret_cast<const bf16x8*>(k + tok0 * DK + off);
+    qr[i] = *reinterpret_cast<const bf16x8*>(q + tok0 * DK + off);
+    lofs[i] = ((r >> 4) * NS + (c16 >> 2)) * 1024 + 16 * rslot(r & 15, c16 & 3);
+  }
   bf16x8 kf[2][NS], qf[2][NS];
+  const int o_frag = 16 * rslot(n, grp);
+#pragma unroll
+  for (int i = 0; i < NL; ++i) *reinterpret_cast<bf16x8*>(rows + lofs[i]) = kr[i];
+  wave_fence();
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int s = 0; s < NS; ++s) kf[x][s] = *reinterpret_cast<const bf16x8*>(rows + (x * NS + s) * 1024 + o_frag);
+  wave_fence();   // every fragment of k read before q overwrites the block
+#pragma unroll
+  for (int i = 0; i < NL; ++i) *reinterpret_cast<bf16x8*>(rows + lofs[i]) = qr[i];
+  wave_fence();
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int s = 0; s < NS; ++s) qf[x][s] = *reinterpret_cast<const bf16x8*>(rows + (x * NS + s) * 1024 + o_frag);
   float gx[2], bt[2];
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
     const int t = min(32 * c + 16 * x + n, T - 1);
-    const int off = t * H * DK;   // fits in 32 bits (checked on the host)
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      kf[x][s] = *reinterpret_cast<const bf16x8*>(kb0 + off + 32 * s);
-      qf[x][s] = *reinterpret_cast<const bf16x8*>(qb0 + off + 32 * s);
-    }
     gx[x] = gate[tok0 + (int64_t)t * H];
     bt[x] = beta[tok0 + (int64_t)t * H];
   }
