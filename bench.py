@@ -13,6 +13,7 @@ state, 16-token tiles.  Prints ONE JSON line.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -25,6 +26,40 @@ METRIC = "tokens/s + % bf16 MFMA peak, chunked linear-attn fwd H=16 d=128 T=64K"
 PEAK_HBM = 8.0e12           # bytes/s, MI355X HBM3E
 PEAK_BF16 = 2.5e15          # dense bf16 MFMA flop/s (published figure)
 CHUNK = 16
+CSRC = os.path.join(ROOT, "chunked_gated_linear_amd", "csrc")
+
+# HBM traffic per launch from the rocprofv3 FETCH_SIZE and WRITE_SIZE counters,
+# in KiB per dispatch as the counters read them, for the kernels as they stood
+# when the counters were taken (keyed by a hash of their sources).  A plain
+# 1 GiB copy through the library reads 524319 KiB of FETCH_SIZE and 1048576 KiB
+# of WRITE_SIZE, so reads are scaled by 2 and writes by 1.
+FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
+TRAFFIC_KIB = {
+    "chunk": {"sources": ("chunk_pair.hip", "la_device.h", "la_launch.h"),
+              "sha256_16": "2659e6df2bfc6a48",
+              "fetch": 317252 + 499826, "write": 205827 + 263168},   # prep + state
+    "decode": {"sources": ("decode.hip", "la_device.h", "la_launch.h"),
+               "sha256_16": "f5285655c2f323aa",
+               "fetch": 265758, "write": 526674},
+}
+
+
+def source_hash(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(which, workload):
+    """Counter-derived HBM bytes per launch, or None once the kernels changed."""
+    t = TRAFFIC_KIB[which]
+    if which == "chunk" and workload != "long_64k":
+        return None
+    if source_hash(t["sources"]) != t["sha256_16"]:
+        return None
+    return int((t["fetch"] * FETCH_SCALE + t["write"] * WRITE_SCALE) * 1024)
 
 
 def alg_counts(B, T, H, Dk, Dv, ebytes=2, h0=False):
@@ -52,6 +87,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=65536,
                     help="tokens per head in the CPU-baseline sample")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="also run one state copy of this many MiB through the library "
+                         "(lin_attn_chunk_fwd with T = 0): a kernel of known traffic that "
+                         "calibrates the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -117,11 +156,25 @@ def main():
         "mfma_pct_of_bf16_peak": 100.0 * flops / t / PEAK_BF16,
         "tflops": flops / t / 1e12,
         "roofline": {"bound": "hbm", "achieved": byts / t / 1e9, "peak": PEAK_HBM / 1e9,
-                     "unit": "GB/s", "frac": byts / t / PEAK_HBM, "traffic": None,
-                     "kernel": "chunk_fwd2_kernel (bf16) / chunk_fwd_kernel (fp32)", "alg_bytes_per_launch": byts,
+                     "unit": "GB/s", "frac": byts / t / PEAK_HBM,
+                     "traffic": measured_traffic("chunk", args.workload) if dtype == "bf16" else None,
+                     "kernel": ("chunk_prep_kernel + chunk_state_kernel (one lin_attn_chunk_fwd call)"
+                                if dtype == "bf16" else "chunk_fwd_kernel"),
+                     "alg_bytes_per_launch": byts,
                      "alg_flops_per_launch": flops,
                      "attainable_frac": max(byts / PEAK_HBM, flops / PEAK_BF16) / t},
     }
+
+    # ---- optional calibration copy (reads and writes exactly copy_mib MiB)
+    if args.copy_mib > 0:
+        nh = args.copy_mib * 16                       # 64 KiB of fp32 state per head
+        src = torch.ones((1, nh, 128, 128), dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        e16 = torch.empty((1, 0, nh, 128), dtype=torch.bfloat16, device=dev)
+        e32 = torch.empty((1, 0, nh), dtype=torch.float32, device=dev)
+        lin_attn_chunk_fwd(e16, e16, e16, e32, e32, src, gate_mode="logit", hT=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ---- decode: B=256, H=32, d=128, fresh token every step, state in place
     if args.decode_steps > 0:
@@ -151,6 +204,7 @@ def main():
             "roofline": {"bound": "hbm", "achieved": dbytes / (dms * 1e-3) / 1e9,
                          "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                          "frac": dbytes / (dms * 1e-3) / PEAK_HBM,
+                         "traffic": measured_traffic("decode", None),
                          "alg_bytes_per_launch": dbytes, "kernel": "decode_kernel"},
         }
         del d, S
