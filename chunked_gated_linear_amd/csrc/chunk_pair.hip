@@ -26,7 +26,7 @@
 //   splits of Tb and P.  Its results (6.5 KB per pair) go to a workspace in
 //   HBM, computed once per head rather than once per d_v slice.
 // chunk_state_kernel (inter-tile) -- one workgroup per (sequence, head, 16
-//   columns of d_v), three waves:
+//   columns of d_v), four waves:
 //   wave 0 "chain"   the fp32 state slice (d_k x 16) in registers; per pair:
 //                    K H, U, the 32-deep state update, all on MFMA;
 //   wave 1 "output"  diag(gamma) Q H + P U on MFMA and the bf16 stores, one
@@ -34,7 +34,10 @@
 //                    gamma straight from global memory, several pairs ahead;
 //   wave 2 "loader"  streams k, q, v and the chain's part of the workspace
 //                    into a ring of LDS records with direct global->LDS loads,
-//                    a few pairs ahead of the chain.
+//                    a few pairs ahead of the chain;
+//   wave 3 "prefetch" touches the lines of a pair further ahead so that the
+//                    loader's requests hit L2: the d_v slices of a head split
+//                    the lines between them, one 4-byte load per line.
 //   One workgroup barrier per pair.  The state (bf16) and U reach the output
 //   wave through LDS, double buffered by pair parity.
 //
@@ -368,7 +371,9 @@ struct CfgS {
   static constexpr int OB = OB_U + 2048;
   static constexpr int OFF_OB = 0;
   static constexpr int OFF_REC = 2 * OB;
-  static constexpr int LDS = OFF_REC + NBUF * REC;
+  static constexpr int OFF_PF = OFF_REC + NBUF * REC;   // landing slot of the prefetch loads
+  static constexpr int PF_AHEAD = 8;           // pairs between the chain and the prefetch
+  static constexpr int LDS = OFF_PF + 256;
   static_assert(REC % 256 == 0 && OB % 16 == 0, "LDS alignment");
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
@@ -393,7 +398,7 @@ __device__ inline void map_block(int n, int NH, int NV, int& head, int& vt) {
 }
 
 template <int DK>
-__global__ __launch_bounds__(192) void chunk_state_kernel(
+__global__ __launch_bounds__(256) void chunk_state_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const char* __restrict__ ws, const float* h0, __bf16* __restrict__ o, float* hT,
     int B, int T, int H, int DV) {
@@ -424,6 +429,49 @@ __global__ __launch_bounds__(192) void chunk_state_kernel(
   // Barriers: one before pair 0, then one after each pair c = 0 .. NSC-1 and
   // one more that lets the output wave finish the last pair: NSC + 2 in all,
   // executed by every wave.
+
+  if (wave == 3) {
+    // ---------------------------------------------------------- prefetch
+    // Line j of pair p (k rows, then q rows, then v rows, then the workspace
+    // record, in 128-byte lines) belongs to slice j % NV; each lane loads one
+    // word of one of this slice's lines into a scratch slot nobody reads.
+    const int lk = DK / 64, lv = (DV + 63) / 64;
+    const int nk = 32 * lk, nv = 32 * lv, nw = (WsRec::BYTES + 127) / 128;
+    const int total = 2 * nk + nv + nw;
+    const int rounds = (total + 64 * NV - 1) / (64 * NV);
+    lds_void* const junk = (lds_void*)(smem + C::OFF_PF);
+    auto touch = [&](int p) {
+      p = min(p, NSC - 1);
+      for (int r = 0; r < rounds; ++r) {
+        const int j = vt + NV * (lane + 64 * r);
+        if (j >= total) continue;
+        const char* a;
+        if (j < 2 * nk) {
+          const int jj = j < nk ? j : j - nk;
+          const int t = min(32 * p + jj / lk, T - 1);
+          a = (const char*)((j < nk ? k : q) + (tok0 + (int64_t)t * H) * DK) + (jj % lk) * 128;
+        } else if (j < 2 * nk + nv) {
+          const int jj = j - 2 * nk;
+          const int t = min(32 * p + jj / lv, T - 1);
+          a = (const char*)(v + (tok0 + (int64_t)t * H) * DV) + (jj % lv) * 128;
+        } else {
+          a = wsh + (int64_t)p * WsRec::BYTES + (j - 2 * nk - nv) * 128;
+        }
+        __builtin_amdgcn_global_load_lds(a, junk, 4, 0, 0);
+      }
+    };
+#pragma unroll 1
+    for (int c = 0; c < C::PF_AHEAD; ++c) touch(c);
+    wg_barrier();
+#pragma unroll 1
+    for (int c = 0; c <= NSC; ++c) {
+      touch(c + C::PF_AHEAD);
+      wait_vmcnt<48>();            // bound the loads in flight
+      wg_barrier();
+    }
+    wait_vmcnt<0>();               // nothing may land after the workgroup ends
+    return;
+  }
 
   if (wave == 2) {
     // ------------------------------------------------------------ loader
@@ -693,7 +741,7 @@ static hipError_t launch_pair_t(const void* q, const void* k, const void* v, con
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int blocks = B * H * (Dv / 16);
-  hipLaunchKernelGGL((chunk_state_kernel<DK>), dim3(blocks), dim3(192), 0, st,
+  hipLaunchKernelGGL((chunk_state_kernel<DK>), dim3(blocks), dim3(256), 0, st,
                      (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const char*)ws, h0,
                      (__bf16*)o, hT, B, T, H, Dv);
   return hipGetLastError();
