@@ -145,19 +145,39 @@ constexpr int kPrepWaves = 4;
 constexpr int kPrepScr = 2304;   // per wave: A00 (then T00), A11 (then T11), beta[32], G[32]
 constexpr int kPrepRows = 8192;  // per wave: one pair's rows of k or q, as fragment blocks
 
+constexpr int kPrepLDS = kPrepWaves * (kPrepScr + kPrepRows);
+
+// Arguments of the intra-tile work over tokens [0, T) of each sequence; the
+// pointers may be advanced to a later token, TB is the full sequence length
+// (the stride between sequences, in tokens).
+struct PrepArgs {
+  const __bf16* q;
+  const __bf16* k;
+  const float* gate;
+  const float* beta;
+  char* ws;
+  int gate_logit;
+  float G;
+  int B, T, TB, H;
+};
+
 template <int DK>
-__global__ __launch_bounds__(64 * kPrepWaves) void chunk_prep_kernel(
-    const __bf16* __restrict__ q, const __bf16* __restrict__ k,
-    const float* __restrict__ gate, int gate_logit, float G, const float* __restrict__ beta,
-    char* __restrict__ ws, int B, int T, int H) {
+__device__ __forceinline__ void prep_body(char* smem, int64_t blk, const PrepArgs& pa) {
   constexpr int NS = DK / 32;
   using F = Elt<float>;
-  __shared__ __attribute__((aligned(16))) char smem[kPrepWaves * (kPrepScr + kPrepRows)];
+  const __bf16* __restrict__ const q = pa.q;
+  const __bf16* __restrict__ const k = pa.k;
+  const float* __restrict__ const gate = pa.gate;
+  const float* __restrict__ const beta = pa.beta;
+  char* __restrict__ const ws = pa.ws;
+  const int gate_logit = pa.gate_logit;
+  const float G = pa.G;
+  const int B = pa.B, T = pa.T, H = pa.H;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, grp = lane >> 4;
   const int NSC = (T + 31) >> 5;
-  const int64_t job = (int64_t)blockIdx.x * kPrepWaves + wave;   // = head * NSC + pair
+  const int64_t job = blk * kPrepWaves + wave;                   // = head * NSC + pair
   if (job >= (int64_t)B * H * NSC) return;                        // no barriers in this kernel
   const int head = (int)(job / NSC);
   const int c = (int)(job - (int64_t)head * NSC);
@@ -178,7 +198,7 @@ __global__ __launch_bounds__(64 * kPrepWaves) void chunk_prep_kernel(
   // 256-byte row, or two 128-byte rows at d_k = 64; a quarter spanning 16
   // rows would cost the address unit about three times as much) and turned
   // into MFMA fragments through LDS, in the row blocks of rslot.
-  const int64_t tok0 = (int64_t)b * T * H + h;   // token (b, 0, h)
+  const int64_t tok0 = (int64_t)b * pa.TB * H + h;   // token (b, 0, h)
   constexpr int NL = DK / 16;                    // 1 KB loads per pair and matrix
   bf16x8 kr[NL], qr[NL];
   int lofs[NL];
@@ -349,6 +369,12 @@ __global__ __launch_bounds__(64 * kPrepWaves) void chunk_prep_kernel(
   reinterpret_cast<bf16x8*>(wr + WsRec::TB1L)[lane] = cat8(lo4(tb10, h10), lo4(tb11, h11));
 }
 
+template <int DK>
+__global__ __launch_bounds__(64 * kPrepWaves) void chunk_prep_kernel(PrepArgs pa) {
+  __shared__ __attribute__((aligned(16))) char smem[kPrepLDS];
+  prep_body<DK>(smem, blockIdx.x, pa);
+}
+
 // ============================================================== inter-tile
 
 template <int DK>
@@ -397,25 +423,42 @@ __device__ inline void map_block(int n, int NH, int NV, int& head, int& vt) {
   }
 }
 
+// Arguments of the inter-tile work over tokens [0, T) of each sequence (the
+// pointers may be advanced to a later token; TB is the full sequence length).
+struct StateArgs {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  const char* ws;
+  const float* h0;
+  __bf16* o;
+  float* hT;
+  int B, T, TB, H, DV;
+};
+
 template <int DK>
-__global__ __launch_bounds__(256) void chunk_state_kernel(
-    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-    const char* __restrict__ ws, const float* h0, __bf16* __restrict__ o, float* hT,
-    int B, int T, int H, int DV) {
+__device__ __forceinline__ void state_body(char* smem, int blk, const StateArgs& sa) {
   using C = CfgS<DK>;
   constexpr int NT = C::NT, NS = C::NS, NBUF = C::NBUF;
-  __shared__ __attribute__((aligned(256))) char smem[C::LDS];
+  const __bf16* __restrict__ const q = sa.q;
+  const __bf16* __restrict__ const k = sa.k;
+  const __bf16* __restrict__ const v = sa.v;
+  const char* __restrict__ const ws = sa.ws;
+  const float* const h0 = sa.h0;
+  __bf16* __restrict__ const o = sa.o;
+  float* const hT = sa.hT;
+  const int B = sa.B, T = sa.T, H = sa.H, DV = sa.DV;
 
   const int NV = DV / 16;
   int head, vt;
-  map_block(blockIdx.x, B * H, NV, head, vt);
+  map_block(blk, B * H, NV, head, vt);
   const int b = head / H, h = head % H;
   const int v0 = vt * 16;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, grp = lane >> 4;
   const int NSC = (T + 31) >> 5;                          // pairs of tiles
-  const int64_t tok0 = (int64_t)b * T * H + h;            // token (b, 0, h)
+  const int64_t tok0 = (int64_t)b * sa.TB * H + h;       // token (b, 0, h)
   const char* const wsh = ws + (int64_t)head * NSC * WsRec::BYTES;
   // Record of pair c.  The byte offset goes through an empty asm so that the
   // compiler keeps one scalar base per pair instead of rewriting every LDS
@@ -728,27 +771,95 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(
   }
 }
 
+// Blocks [0, nstate) carry the state over one stretch of the sequences; any
+// blocks after them do the intra-tile work of the next stretch on the compute
+// units the state blocks leave idle.  The two share no data within a launch.
+template <int DK>
+__global__ __launch_bounds__(256) void chunk_state_kernel(StateArgs sa, PrepArgs pa, int nstate) {
+  static_assert(kPrepLDS <= CfgS<DK>::LDS, "the intra-tile blocks use the same LDS");
+  __shared__ __attribute__((aligned(256))) char smem[CfgS<DK>::LDS];
+  if ((int)blockIdx.x < nstate) state_body<DK>(smem, blockIdx.x, sa);
+  else prep_body<DK>(smem, (int64_t)blockIdx.x - nstate, pa);
+}
+
+// Long sequences are cut into stretches of whole pairs.  The intra-tile work
+// of stretch 0 runs alone; launch s then carries the state over stretch s
+// while its extra blocks prepare stretch s + 1 on the idle compute units.
+// The fp32 state passes from one stretch to the next through the workspace
+// (read and written in place by the workgroup that owns each slice), so the
+// results are those of a single pass: the state crosses the cut exactly.
+constexpr int kStretchMinPairs = 256;
+constexpr int kMaxStretches = 8;
+
+static bool stretch_area(int NSC) { return NSC >= 2 * kStretchMinPairs; }
+
+static int compute_units() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return n;
+}
+
 template <int DK>
 static hipError_t launch_pair_t(const void* q, const void* k, const void* v, const float* gate,
                                 int gate_logit, float G, const float* beta, const float* h0,
                                 void* o, float* hT, int B, int T, int H, int Dv, void* ws,
                                 hipStream_t st) {
-  const int64_t jobs = (int64_t)B * H * ((T + 31) / 32);
-  const int64_t pblocks = (jobs + kPrepWaves - 1) / kPrepWaves;
-  hipLaunchKernelGGL((chunk_prep_kernel<DK>), dim3((unsigned)pblocks), dim3(64 * kPrepWaves), 0, st,
-                     (const __bf16*)q, (const __bf16*)k, gate, gate_logit, G, beta, (char*)ws,
-                     B, T, H);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int blocks = B * H * (Dv / 16);
-  hipLaunchKernelGGL((chunk_state_kernel<DK>), dim3(blocks), dim3(256), 0, st,
-                     (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const char*)ws, h0,
-                     (__bf16*)o, hT, B, T, H, Dv);
-  return hipGetLastError();
+  const int NSC = (T + 31) / 32;
+  const int nstate = B * H * (Dv / 16);
+  int S = 1;
+  if (stretch_area(NSC) && 2 * nstate <= compute_units())
+    S = min(kMaxStretches, NSC / kStretchMinPairs);
+  char* const wsb = static_cast<char*>(ws);
+  float* const carry = reinterpret_cast<float*>(wsb + (int64_t)B * H * NSC * WsRec::BYTES);
+  auto span = [&](int s, int& p0, int& p1) {
+    p0 = (int)((int64_t)NSC * s / S);
+    p1 = (int)((int64_t)NSC * (s + 1) / S);
+  };
+  auto prep_args = [&](int s) {
+    int p0, p1;
+    span(s, p0, p1);
+    const int64_t t0 = 32 * (int64_t)p0;
+    const int Ts = min(32 * p1, T) - 32 * p0;
+    return PrepArgs{(const __bf16*)q + t0 * H * DK, (const __bf16*)k + t0 * H * DK,
+                    gate + t0 * H, beta + t0 * H, wsb + (int64_t)B * H * p0 * WsRec::BYTES,
+                    gate_logit, G, B, Ts, T, H};
+  };
+  auto prep_blocks = [&](int s) {
+    int p0, p1;
+    span(s, p0, p1);
+    return (int)(((int64_t)B * H * (p1 - p0) + kPrepWaves - 1) / kPrepWaves);
+  };
+  {
+    const PrepArgs pa = prep_args(0);
+    hipLaunchKernelGGL((chunk_prep_kernel<DK>), dim3((unsigned)prep_blocks(0)),
+                       dim3(64 * kPrepWaves), 0, st, pa);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  for (int s = 0; s < S; ++s) {
+    int p0, p1;
+    span(s, p0, p1);
+    const int64_t t0 = 32 * (int64_t)p0;
+    const StateArgs sa{(const __bf16*)q + t0 * H * DK, (const __bf16*)k + t0 * H * DK,
+                       (const __bf16*)v + t0 * H * Dv, wsb + (int64_t)B * H * p0 * WsRec::BYTES,
+                       s == 0 ? h0 : carry, (__bf16*)o + t0 * H * Dv, s == S - 1 ? hT : carry,
+                       B, min(32 * p1, T) - 32 * p0, T, H, Dv};
+    const bool more = s + 1 < S;
+    const PrepArgs pa = more ? prep_args(s + 1) : PrepArgs{};
+    const int blocks = nstate + (more ? prep_blocks(s + 1) : 0);
+    hipLaunchKernelGGL((chunk_state_kernel<DK>), dim3(blocks), dim3(256), 0, st, sa, pa, nstate);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
-long long chunk_pair_workspace_bytes(int B, int T, int H) {
-  return (long long)B * H * ((T + 31) / 32) * WsRec::BYTES;
+long long chunk_pair_workspace_bytes(int B, int T, int H, int Dk, int Dv) {
+  const int NSC = (T + 31) / 32;
+  long long n = (long long)B * H * NSC * WsRec::BYTES;
+  if (stretch_area(NSC)) n += (long long)B * H * Dk * Dv * 4;
+  return n;
 }
 
 hipError_t launch_chunk_fwd_pair(const void* q, const void* k, const void* v, const float* gate,

@@ -20,8 +20,10 @@ hipError_t launch_chunk_fwd_pair(const void* q, const void* k, const void* v,
                                  int B, int T, int H, int Dk, int Dv, void* ws,
                                  hipStream_t st);
 
-// Workspace bytes the bf16 path needs (0 when T == 0).
-long long chunk_pair_workspace_bytes(int B, int T, int H);
+// Workspace bytes the bf16 path needs (0 when T == 0): one record per pair of
+// tiles and head, plus one fp32 state per head for sequences long enough to be
+// cut into stretches.
+long long chunk_pair_workspace_bytes(int B, int T, int H, int Dk, int Dv);
 
 hipError_t launch_decode(const void* q, const void* k, const void* v,
                          const float* gate, int gate_logit, float G,

@@ -81,8 +81,8 @@ int check_chunk_sizes(int B, int T, int H, int Dk, int Dv, int dtype) {
   return LA_OK;
 }
 
-long long chunk_workspace(int B, int T, int H, int dtype) {
-  return dtype == LA_BF16 ? la::chunk_pair_workspace_bytes(B, T, H) : 0;
+long long chunk_workspace(int B, int T, int H, int Dk, int Dv, int dtype) {
+  return dtype == LA_BF16 ? la::chunk_pair_workspace_bytes(B, T, H, Dk, Dv) : 0;
 }
 
 }  // namespace
@@ -96,7 +96,7 @@ int lin_attn_version(void) { return 200; }
 long long lin_attn_chunk_fwd_workspace_size(int B, int T, int H, int Dk, int Dv, int dtype) {
   if (check_chunk_sizes(B, T, H, Dk, Dv, dtype)) return -1;
   ok();
-  return chunk_workspace(B, T, H, dtype);
+  return chunk_workspace(B, T, H, Dk, Dv, dtype);
 }
 
 int lin_attn_chunk_fwd(const void* q, const void* k, const void* v, const float* gate,
@@ -110,7 +110,7 @@ int lin_attn_chunk_fwd(const void* q, const void* k, const void* v, const float*
   const int64_t nst = (int64_t)B * H * Dk * Dv;
   if (B == 0 || H == 0) return ok();
   const unsigned ea = dtype == LA_BF16 ? 2u : 4u;
-  const long long wsz = T > 0 ? chunk_workspace(B, T, H, dtype) : 0;
+  const long long wsz = T > 0 ? chunk_workspace(B, T, H, Dk, Dv, dtype) : 0;
   if (T > 0) {
     // q, k and v are read as 16-byte vectors, bf16 o written as 8-byte vectors;
     // gate and beta element-wise

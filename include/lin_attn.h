@@ -73,7 +73,9 @@ extern "C" {
  * are invalid or unsupported.  For LA_BF16 it is B * H * ceil(T / 32) * 6656:
  * the state-independent per-tile operators (the decay-weighted solve T diag(beta)
  * and the masked Q K^T block, see below) are computed once per head and kept
- * there between the two kernels of the pass.
+ * there between the two kernels of the pass.  When ceil(T / 32) >= 512 another
+ * B * H * Dk * Dv * 4 bytes follow: long sequences may be processed in
+ * stretches, and the fp32 state passes from one stretch to the next there.
  */
 long long lin_attn_chunk_fwd_workspace_size(int B, int T, int H, int Dk, int Dv, int dtype);
 

@@ -109,6 +109,10 @@ def test_workspace_size():
     assert ws(1, 64, 2, 128, 128, N.LA_BF16) == 2 * 2 * 6656
     assert ws(4, 8192, 16, 128, 128, N.LA_BF16) == 4 * 16 * 256 * 6656
     assert ws(1, 33, 3, 64, 16, N.LA_BF16) == 3 * 2 * 6656
+    # from 512 pairs of tiles on, one fp32 state per head follows the records
+    assert ws(1, 32 * 511, 2, 128, 128, N.LA_BF16) == 2 * 511 * 6656
+    assert ws(1, 32 * 511 + 1, 2, 128, 64, N.LA_BF16) == 2 * 512 * 6656 + 2 * 128 * 64 * 4
+    assert ws(1, 65536, 16, 128, 128, N.LA_BF16) == 16 * 2048 * 6656 + 16 * 128 * 128 * 4
     assert ws(2, 0, 4, 128, 64, N.LA_BF16) == 0
     # fp32 runs one fused kernel without a workspace
     assert ws(1, 4096, 8, 128, 128, N.LA_FP32) == 0

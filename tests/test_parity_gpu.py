@@ -166,6 +166,35 @@ def test_deterministic_and_split_invariant():
             assert relerr(host(hb), host(h1).astype(np.float64)) < 1e-2
 
 
+def test_stretches():
+    """Sequences of 512 pairs of tiles and more may run in stretches, the fp32
+    state passing between them through the workspace: every output against
+    the oracle, a cut at a pair boundary inside a stretch bitwise equal, hT in
+    place of h0, and no final state."""
+    name = "stretches B2 H4 T20000 d128 bf16 weak, h0 given"
+    say(name)
+    dev, hst = make_case(2, 20000, 4, 128, 128, "bf16", "weak", "logit", 0.02, seed=13)
+    o, hT = run_gpu(dev)
+    ref_o, ref_h = oracle_full(hst)
+    check(name, "bf16", o, hT, ref_o, ref_h)
+    cut = 32 * 400
+    a = {kk: (vv[:, :cut].contiguous() if kk in ("q", "k", "v", "gate", "beta") else vv)
+         for kk, vv in dev.items()}
+    b = {kk: (vv[:, cut:].contiguous() if kk in ("q", "k", "v", "gate", "beta") else vv)
+         for kk, vv in dev.items()}
+    oa, ha = run_gpu(a)
+    b["h0"] = ha
+    ob, hb = run_gpu(b)
+    assert torch.equal(torch.cat([oa, ob], 1), o) and torch.equal(hb, hT)
+    h = dev["h0"].clone()
+    o2, h2 = lin_attn_chunk_fwd(dev["q"], dev["k"], dev["v"], dev["gate"], dev["beta"], h,
+                                gate_mode="logit", hT=h)
+    torch.cuda.synchronize()
+    assert h2.data_ptr() == h.data_ptr() and torch.equal(o2, o) and torch.equal(h, hT)
+    o3, h3 = run_gpu(dev, hT=False)
+    assert h3 is None and torch.equal(o3, o)
+
+
 def test_state_in_place_and_empty():
     say("properties: hT == h0 in place, T == 0, output_final_state=False")
     dev, hst = make_case(1, 100, 3, 128, 64, "bf16", "std", "logit", 0.02, seed=9)
