@@ -775,11 +775,17 @@ __device__ __forceinline__ void state_body(char* smem, int blk, const StateArgs&
 // blocks after them do the intra-tile work of the next stretch on the compute
 // units the state blocks leave idle.  The two share no data within a launch.
 template <int DK>
-__global__ __launch_bounds__(256) void chunk_state_kernel(StateArgs sa, PrepArgs pa, int nstate) {
+__global__ __launch_bounds__(256) void chunk_state_kernel(StateArgs sa, PrepArgs pa, int nstate,
+                                                          int prep_blocks) {
   static_assert(kPrepLDS <= CfgS<DK>::LDS, "the intra-tile blocks use the same LDS");
   __shared__ __attribute__((aligned(256))) char smem[CfgS<DK>::LDS];
-  if ((int)blockIdx.x < nstate) state_body<DK>(smem, blockIdx.x, sa);
-  else prep_body<DK>(smem, (int64_t)blockIdx.x - nstate, pa);
+  if ((int)blockIdx.x < nstate) {
+    state_body<DK>(smem, blockIdx.x, sa);
+  } else {
+    // the intra-tile blocks each walk the jobs in steps of their number
+    const int step = (int)gridDim.x - nstate;
+    for (int pb = (int)blockIdx.x - nstate; pb < prep_blocks; pb += step) prep_body<DK>(smem, pb, pa);
+  }
 }
 
 // Long sequences are cut into stretches of whole pairs.  The intra-tile work
@@ -789,6 +795,12 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(StateArgs sa, PrepArgs
 // (read and written in place by the workgroup that owns each slice), so the
 // results are those of a single pass: the state crosses the cut exactly.
 constexpr int kStretchMinPairs = 256;
+// Intra-tile blocks launched beside the state blocks: enough to finish the
+// next stretch's records within the current stretch (they loop over the jobs),
+// few enough not to slow the state blocks down (3 per sequence-head measured
+// best at 64K x 16 heads: fewer starve the next stretch, more cost ~2 %).
+constexpr int kPrepResidentPerHead = 3;
+constexpr int kPrepResidentMin = 16;
 constexpr int kMaxStretches = 8;
 
 static bool stretch_area(int NSC) { return NSC >= 2 * kStretchMinPairs; }
@@ -808,8 +820,9 @@ static hipError_t launch_pair_t(const void* q, const void* k, const void* v, con
   const int NSC = (T + 31) / 32;
   const int nstate = B * H * (Dv / 16);
   int S = 1;
-  if (stretch_area(NSC) && 2 * nstate <= compute_units())
-    S = min(kMaxStretches, NSC / kStretchMinPairs);
+  const int cus = stretch_area(NSC) ? compute_units() : 0;
+  if (stretch_area(NSC) && 2 * nstate <= cus) S = min(kMaxStretches, NSC / kStretchMinPairs);
+  const int resident_cap = min(cus - nstate, max(kPrepResidentMin, kPrepResidentPerHead * B * H));
   char* const wsb = static_cast<char*>(ws);
   float* const carry = reinterpret_cast<float*>(wsb + (int64_t)B * H * NSC * WsRec::BYTES);
   auto span = [&](int s, int& p0, int& p1) {
@@ -847,8 +860,10 @@ static hipError_t launch_pair_t(const void* q, const void* k, const void* v, con
                        B, min(32 * p1, T) - 32 * p0, T, H, Dv};
     const bool more = s + 1 < S;
     const PrepArgs pa = more ? prep_args(s + 1) : PrepArgs{};
-    const int blocks = nstate + (more ? prep_blocks(s + 1) : 0);
-    hipLaunchKernelGGL((chunk_state_kernel<DK>), dim3(blocks), dim3(256), 0, st, sa, pa, nstate);
+    const int pblocks = more ? prep_blocks(s + 1) : 0;
+    const int resident = more ? min(pblocks, max(1, resident_cap)) : 0;
+    hipLaunchKernelGGL((chunk_state_kernel<DK>), dim3(nstate + resident), dim3(256), 0, st, sa, pa,
+                       nstate, pblocks);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
