@@ -28,19 +28,20 @@ PEAK_BF16 = 2.5e15          # dense bf16 MFMA flop/s (published figure)
 CHUNK = 16
 CSRC = os.path.join(ROOT, "chunked_gated_linear_amd", "csrc")
 
-# HBM traffic per launch from the rocprofv3 FETCH_SIZE and WRITE_SIZE counters,
-# in KiB per dispatch as the counters read them, for the kernels as they stood
+# HBM traffic per call from the rocprofv3 FETCH_SIZE and WRITE_SIZE counters,
+# in KiB as the counters read them (summed over the call's dispatches), for the kernels as they stood
 # when the counters were taken (keyed by a hash of their sources).  A plain
 # 1 GiB copy through the library reads 524319 KiB of FETCH_SIZE and 1048576 KiB
 # of WRITE_SIZE, so reads are scaled by 2 and writes by 1.
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC_KIB = {
     "chunk": {"sources": ("chunk_pair.hip", "la_device.h", "la_launch.h"),
-              "sha256_16": "2659e6df2bfc6a48",
-              "fetch": 317252 + 499826, "write": 205827 + 263168},   # prep + state
+              "sha256_16": "c822566bdc98cc01",
+              # one call: the intra-tile launch and the 8 state launches of 64K x 16 heads
+              "fetch": 774714, "write": 476171},
     "decode": {"sources": ("decode.hip", "la_device.h", "la_launch.h"),
-               "sha256_16": "f5285655c2f323aa",
-               "fetch": 265758, "write": 526674},
+               "sha256_16": "5d084af209aefbd2",
+               "fetch": 265755, "write": 526852},
 }
 
 
@@ -53,7 +54,7 @@ def source_hash(names):
 
 
 def measured_traffic(which, workload):
-    """Counter-derived HBM bytes per launch, or None once the kernels changed."""
+    """Counter-derived HBM bytes per call, or None once the kernels changed."""
     t = TRAFFIC_KIB[which]
     if which == "chunk" and workload != "long_64k":
         return None
