@@ -134,6 +134,15 @@ def main():
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
     t = ms * 1e-3
+    # per-call spread, in a separate pass (an event pair around each call)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for a, b in evs:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    per_call = sorted(a.elapsed_time(b) for a, b in evs)
     ebytes = 2 if dtype == "bf16" else 4
     flops, byts = alg_counts(B, T, H, Dk, Dv, ebytes, h0_std is not None)
     tokens_per_s = B * T / t
@@ -146,6 +155,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "ms_per_call_median": per_call[len(per_call) // 2],
+        "ms_per_call_min": per_call[0],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

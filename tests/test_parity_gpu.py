@@ -166,14 +166,24 @@ def test_deterministic_and_split_invariant():
             assert relerr(host(hb), host(h1).astype(np.float64)) < 1e-2
 
 
-def test_stretches():
+STRETCH_CASES = [
+    # B, H, T, Dk, Dv: all run in 2 stretches of whole pairs on a 256-CU device
+    (2, 4, 20000, 128, 128),
+    (1, 2, 17001, 64, 64),
+    (1, 3, 16700, 128, 16),     # one slice per head: the prefetch walks several rounds
+]
+
+
+@pytest.mark.parametrize("case", STRETCH_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_stretches(case):
     """Sequences of 512 pairs of tiles and more may run in stretches, the fp32
     state passing between them through the workspace: every output against
     the oracle, a cut at a pair boundary inside a stretch bitwise equal, hT in
     place of h0, and no final state."""
-    name = "stretches B2 H4 T20000 d128 bf16 weak, h0 given"
+    B, H, T, Dk, Dv = case
+    name = f"stretches B{B} H{H} T{T} dk{Dk} dv{Dv} bf16 weak, h0 given"
     say(name)
-    dev, hst = make_case(2, 20000, 4, 128, 128, "bf16", "weak", "logit", 0.02, seed=13)
+    dev, hst = make_case(B, T, H, Dk, Dv, "bf16", "weak", "logit", 0.02, seed=13)
     o, hT = run_gpu(dev)
     ref_o, ref_h = oracle_full(hst)
     check(name, "bf16", o, hT, ref_o, ref_h)
