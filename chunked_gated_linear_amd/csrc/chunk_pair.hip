@@ -377,31 +377,39 @@ __global__ __launch_bounds__(64 * kPrepWaves) void chunk_prep_kernel(PrepArgs pa
 
 // ============================================================== inter-tile
 
-template <int DK>
+// SPW d_v slices of 16 columns per workgroup (1, or 2 when one slice per
+// workgroup would need more than one round of workgroups: the two slices then
+// share the loader's k, q and record traffic).  Waves: chain s = s, output
+// s = SPW + s, loader 2 SPW, prefetch 2 SPW + 1.
+template <int DK, int SPW>
 struct CfgS {
-  static constexpr int NBUF = 7;               // LDS records in the loader's ring
+  static constexpr int NBUF = SPW == 1 ? 7 : 6;   // LDS records in the loader's ring
   static constexpr int NT = DK / 16, NS = DK / 32;
   // LDS record of one pair (byte offsets)
   static constexpr int KF = 0;                 // [tile][NS] blocks of k rows, slots as rslot
   static constexpr int QF = KF + 2 * NS * 1024;   // the same for q
-  static constexpr int VF = QF + 2 * NS * 1024;   // [32 tokens][16 columns] bf16
-  static constexpr int TB = VF + 1024;         // TB0 | TB1H | TB1L (workspace bytes 0..3071)
+  static constexpr int VF = QF + 2 * NS * 1024;   // [SPW][32 tokens][16 columns] bf16
+  static constexpr int TB = VF + SPW * 1024;   // TB0 | TB1H | TB1L (workspace bytes 0..3071)
   static constexpr int GD = TB + 3072;         // gamma | delta | Gamma (workspace bytes 6144..6655)
   static constexpr int REC = GD + 512;
   // loads per record: k and q blocks, V, TB, GD
-  static constexpr int LPP = 4 * NS + 1 + 3 + 1;
-  // chain -> output hand-over, double buffered by pair parity; placed first so
-  // that its addresses fit the 16-bit offset field of LDS instructions
+  static constexpr int LPP = 4 * NS + SPW + 3 + 1;
+  // chain -> output hand-over per slice, double buffered by pair parity;
+  // placed first so that its addresses fit the 16-bit offset field of LDS
+  // instructions
   static constexpr int OB_H = 0;               // [NS][64] x 16 B   H (bf16)
   static constexpr int OB_U = NS * 1024;       // [2][64] x 16 B    U_a, U_b (f32)
   static constexpr int OB = OB_U + 2048;
-  static constexpr int OFF_OB = 0;
-  static constexpr int OFF_REC = 2 * OB;
+  static constexpr int OFF_OB = 0;             // slice s, parity p at OFF_OB + (2 s + p) OB
+  static constexpr int OFF_REC = 2 * SPW * OB;
   static constexpr int OFF_PF = OFF_REC + NBUF * REC;   // landing slot of the prefetch loads
   static constexpr int PF_AHEAD = 8;           // pairs between the chain and the prefetch
   static constexpr int LDS = OFF_PF + 256;
+  static constexpr int W_OUT = SPW, W_LOADER = 2 * SPW, W_PREFETCH = 2 * SPW + 1;
+  static constexpr int THREADS = 64 * (2 * SPW + 2);   // the kernel's launch bound
   static_assert(REC % 256 == 0 && OB % 16 == 0, "LDS alignment");
   static_assert(LDS <= 160 * 1024, "LDS budget");
+  static_assert((NBUF - 4) * LPP <= 63, "vmcnt range");
 };
 
 __device__ inline void map_block(int n, int NH, int NV, int& head, int& vt) {
@@ -436,9 +444,9 @@ struct StateArgs {
   int B, T, TB, H, DV;
 };
 
-template <int DK>
+template <int DK, int SPW>
 __device__ __forceinline__ void state_body(char* smem, int blk, const StateArgs& sa) {
-  using C = CfgS<DK>;
+  using C = CfgS<DK, SPW>;
   constexpr int NT = C::NT, NS = C::NS, NBUF = C::NBUF;
   const __bf16* __restrict__ const q = sa.q;
   const __bf16* __restrict__ const k = sa.k;
@@ -449,12 +457,14 @@ __device__ __forceinline__ void state_body(char* smem, int blk, const StateArgs&
   float* const hT = sa.hT;
   const int B = sa.B, T = sa.T, H = sa.H, DV = sa.DV;
 
-  const int NV = DV / 16;
-  int head, vt;
-  map_block(blk, B * H, NV, head, vt);
+  const int NV = DV / 16, NVG = NV / SPW;       // slices, slice groups per head
+  int head, vg;
+  map_block(blk, B * H, NVG, head, vg);
   const int b = head / H, h = head % H;
-  const int v0 = vt * 16;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // the slice of a chain or output wave
+  const int vt = vg * SPW + (wave < C::W_OUT ? wave : wave < C::W_LOADER ? wave - C::W_OUT : 0);
+  const int v0 = vt * 16;
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, grp = lane >> 4;
   const int NSC = (T + 31) >> 5;                          // pairs of tiles
@@ -473,20 +483,21 @@ __device__ __forceinline__ void state_body(char* smem, int blk, const StateArgs&
   // one more that lets the output wave finish the last pair: NSC + 2 in all,
   // executed by every wave.
 
-  if (wave == 3) {
+  if (wave == C::W_PREFETCH) {
     // ---------------------------------------------------------- prefetch
     // Line j of pair p (k rows, then q rows, then v rows, then the workspace
-    // record, in 128-byte lines) belongs to slice j % NV; each lane loads one
-    // word of one of this slice's lines into a scratch slot nobody reads.
+    // record, in 128-byte lines) belongs to slice group j % NVG; each lane
+    // loads one word of one of this group's lines into a scratch slot nobody
+    // reads.
     const int lk = DK / 64, lv = (DV + 63) / 64;
     const int nk = 32 * lk, nv = 32 * lv, nw = (WsRec::BYTES + 127) / 128;
     const int total = 2 * nk + nv + nw;
-    const int rounds = (total + 64 * NV - 1) / (64 * NV);
+    const int rounds = (total + 64 * NVG - 1) / (64 * NVG);
     lds_void* const junk = (lds_void*)(smem + C::OFF_PF);
     auto touch = [&](int p) {
       p = min(p, NSC - 1);
       for (int r = 0; r < rounds; ++r) {
-        const int j = vt + NV * (lane + 64 * r);
+        const int j = vg + NVG * (lane + 64 * r);
         if (j >= total) continue;
         const char* a;
         if (j < 2 * nk) {
@@ -516,7 +527,7 @@ __device__ __forceinline__ void state_body(char* smem, int blk, const StateArgs&
     return;
   }
 
-  if (wave == 2) {
+  if (wave == C::W_LOADER) {
     // ------------------------------------------------------------ loader
     // Ring of NBUF records; pair c lives in record c % NBUF.  During pair c
     // the chain reads records c and c + 1 and the output wave record c - 1,
@@ -527,7 +538,7 @@ __device__ __forceinline__ void state_body(char* smem, int blk, const StateArgs&
     const int lrow = lane >> 2, lchunk = (lane & 3) ^ rsw(lane >> 2);
     const __bf16* const kb0 = k + tok0 * DK + 8 * lchunk;
     const __bf16* const qb0 = q + tok0 * DK + 8 * lchunk;
-    const __bf16* const vb0 = v + tok0 * DV + v0 + 8 * (lane & 1);
+    const __bf16* const vb0 = v + tok0 * DV + 16 * vg * SPW + 8 * (lane & 1);
     auto issue = [&](int c) {
       c = min(c, NSC - 1);
       char* rec = rec_of(c);
@@ -540,9 +551,10 @@ __device__ __forceinline__ void state_body(char* smem, int blk, const StateArgs&
           lds_dma16(qb0 + roff + 32 * s, rec + C::QF + (x * NS + s) * 1024);
         }
       }
-      {  // V: lane L fetches 8 columns (half L % 2) of token L / 2 of the pair
+      {  // V of each slice: lane L fetches 8 columns (half L % 2) of token L / 2 of the pair
         const int t = min(32 * c + (lane >> 1), T - 1);
-        lds_dma16(vb0 + t * H * DV, rec + C::VF);
+#pragma unroll
+        for (int sl = 0; sl < SPW; ++sl) lds_dma16(vb0 + t * H * DV + 16 * sl, rec + C::VF + sl * 1024);
       }
       const char* wr = wsh + (int64_t)c * WsRec::BYTES + 16 * lane;
 #pragma unroll
@@ -550,7 +562,6 @@ __device__ __forceinline__ void state_body(char* smem, int blk, const StateArgs&
       if (lane < 32) lds_dma16(wr + WsRec::GM, rec + C::GD);
     };
     constexpr int kAhead = (NBUF - 4) * C::LPP;   // loads allowed in flight at a barrier
-    static_assert(kAhead <= 63, "vmcnt range");
 #pragma unroll 1
     for (int c = 0; c < NBUF - 2; ++c) issue(c);
     wait_vmcnt<kAhead>();                          // pairs 0 and 1 landed
@@ -565,7 +576,7 @@ __device__ __forceinline__ void state_body(char* smem, int blk, const StateArgs&
     return;
   }
 
-  if (wave == 0) {
+  if (wave < C::W_OUT) {
     // ------------------------------------------------------------ chain wave
     f32x4 Hacc[NT];
     const int64_t sbase = ((int64_t)b * H + h) * DK * DV;
@@ -582,10 +593,10 @@ __device__ __forceinline__ void state_body(char* smem, int blk, const StateArgs&
     const int o_kf = 16 * rslot(n, grp);                 // K fragment rows
     // transposing read: lane (j, grp) points at K[4 grp + j/4][rho chunk j%4]
     const int o_kt = 16 * rslot(4 * grp + (n >> 2), n & 3);
-    const int o_v = C::VF + 8 * lane;                    // V, transposing read
+    const int o_v = C::VF + (vt - vg * SPW) * 1024 + 8 * lane;   // V, transposing read
     const int o_tb = C::TB + 16 * lane;
     const int o_gd = C::GD + 16 * grp;
-    char* const obh = smem + C::OFF_OB + C::OB_H + 16 * lane;
+    char* const obh = smem + C::OFF_OB + 2 * (vt - vg * SPW) * C::OB + C::OB_H + 16 * lane;
 
     struct Ops { bf16x8 ka[NS], kb[NS]; f32x4 ga, gb, da, db; float Gam; s16x4_t va, vb;
                  bf16x8 tb0, tb1h, tb1l; };
@@ -700,7 +711,7 @@ __device__ __forceinline__ void state_body(char* smem, int blk, const StateArgs&
     constexpr int kDepth = 4;
     __bf16* const orow = o + (tok0 + (int64_t)n * H) * DV + v0 + 4 * grp;
     const int ostride = H * DV;
-    const char* const obh = smem + C::OFF_OB + C::OB_H + 16 * lane;
+    const char* const obh = smem + C::OFF_OB + 2 * (vt - vg * SPW) * C::OB + C::OB_H + 16 * lane;
     const int o_qf = C::QF + 16 * rslot(n, grp);
     struct Oin { bf16x8 pf0, pf1h, pf1l; float ga, gb; };
     auto gload = [&](Oin& x, int c) {
@@ -774,15 +785,16 @@ __device__ __forceinline__ void state_body(char* smem, int blk, const StateArgs&
 // Blocks [0, nstate) carry the state over one stretch of the sequences; any
 // blocks after them do the intra-tile work of the next stretch on the compute
 // units the state blocks leave idle.  The two share no data within a launch.
-template <int DK>
-__global__ __launch_bounds__(256) void chunk_state_kernel(StateArgs sa, PrepArgs pa, int nstate,
-                                                          int prep_blocks) {
-  static_assert(kPrepLDS <= CfgS<DK>::LDS, "the intra-tile blocks use the same LDS");
-  __shared__ __attribute__((aligned(256))) char smem[CfgS<DK>::LDS];
+template <int DK, int SPW>
+__global__ __launch_bounds__(64 * (2 * SPW + 2)) void chunk_state_kernel(
+    StateArgs sa, PrepArgs pa, int nstate, int prep_blocks) {
+  static_assert(kPrepLDS <= CfgS<DK, SPW>::LDS, "the intra-tile blocks use the same LDS");
+  __shared__ __attribute__((aligned(256))) char smem[CfgS<DK, SPW>::LDS];
   if ((int)blockIdx.x < nstate) {
-    state_body<DK>(smem, blockIdx.x, sa);
-  } else {
-    // the intra-tile blocks each walk the jobs in steps of their number
+    state_body<DK, SPW>(smem, blockIdx.x, sa);
+  } else if ((threadIdx.x >> 6) < kPrepWaves) {
+    // the intra-tile blocks (their first kPrepWaves waves) each walk the jobs
+    // in steps of their number
     const int step = (int)gridDim.x - nstate;
     for (int pb = (int)blockIdx.x - nstate; pb < prep_blocks; pb += step) prep_body<DK>(smem, pb, pa);
   }
@@ -818,9 +830,13 @@ static hipError_t launch_pair_t(const void* q, const void* k, const void* v, con
                                 void* o, float* hT, int B, int T, int H, int Dv, void* ws,
                                 hipStream_t st) {
   const int NSC = (T + 31) / 32;
-  const int nstate = B * H * (Dv / 16);
+  const int cus = compute_units();
+  // two slices per workgroup when one per workgroup would take more than one
+  // round of workgroups (one fits per compute unit)
+  const int NV = Dv / 16;
+  const int spw = (NV % 2 == 0 && (int64_t)B * H * NV > cus) ? 2 : 1;
+  const int nstate = B * H * (NV / spw);
   int S = 1;
-  const int cus = stretch_area(NSC) ? compute_units() : 0;
   if (stretch_area(NSC) && 2 * nstate <= cus) S = min(kMaxStretches, NSC / kStretchMinPairs);
   const int resident_cap = min(cus - nstate, max(kPrepResidentMin, kPrepResidentPerHead * B * H));
   char* const wsb = static_cast<char*>(ws);
@@ -862,8 +878,13 @@ static hipError_t launch_pair_t(const void* q, const void* k, const void* v, con
     const PrepArgs pa = more ? prep_args(s + 1) : PrepArgs{};
     const int pblocks = more ? prep_blocks(s + 1) : 0;
     const int resident = more ? min(pblocks, max(1, resident_cap)) : 0;
-    hipLaunchKernelGGL((chunk_state_kernel<DK>), dim3(nstate + resident), dim3(256), 0, st, sa, pa,
-                       nstate, pblocks);
+    constexpr int kThreads1 = CfgS<DK, 1>::THREADS, kThreads2 = CfgS<DK, 2>::THREADS;
+    if (spw == 2)
+      hipLaunchKernelGGL((chunk_state_kernel<DK, 2>), dim3(nstate + resident), dim3(kThreads2), 0,
+                         st, sa, pa, nstate, pblocks);
+    else
+      hipLaunchKernelGGL((chunk_state_kernel<DK, 1>), dim3(nstate + resident), dim3(kThreads1), 0,
+                         st, sa, pa, nstate, pblocks);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

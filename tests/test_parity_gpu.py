@@ -63,6 +63,10 @@ SMALL = [
     ("bf16", 128, 128, 1, 1, 16, "weak", "logit", 0.02),
     ("bf16", 128, 128, 1, 1, 17, "weak", "logit", 0.02),
     ("bf16", 64, 128, 64, 32, 20, "std", "logit", 0.02),        # many heads
+    # more than 256 slices of 16 columns: two slices per workgroup
+    ("bf16", 128, 128, 2, 17, 100, "weak", "logit", 0.02),      # 34 heads: partial XCD group
+    ("bf16", 64, 64, 4, 20, 77, "std", "log", 0.02),
+    ("bf16", 128, 48, 8, 12, 70, "weak", "logit", 0.02),        # 3 slices per head: one per workgroup
 ]
 
 
