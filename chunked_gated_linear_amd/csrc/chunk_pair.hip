@@ -25,21 +25,24 @@
 //   16 x 16 unit-triangular solves in fp32, T10 on fp32 MFMA, and hi/lo bf16
 //   splits of Tb and P.  Its results (6.5 KB per pair) go to a workspace in
 //   HBM, computed once per head rather than once per d_v slice.
-// chunk_state_kernel (inter-tile) -- one workgroup per (sequence, head, 16
-//   columns of d_v), four waves:
-//   wave 0 "chain"   the fp32 state slice (d_k x 16) in registers; per pair:
-//                    K H, U, the 32-deep state update, all on MFMA;
-//   wave 1 "output"  diag(gamma) Q H + P U on MFMA and the bf16 stores, one
-//                    pair behind the chain; q comes through the loader, P and
-//                    gamma straight from global memory, several pairs ahead;
-//   wave 2 "loader"  streams k, q, v and the chain's part of the workspace
+// chunk_state_kernel (inter-tile) -- one workgroup per (sequence, head, one
+//   or two slices of 16 columns of d_v), 2 SPW + 2 waves:
+//   "chain" (one per slice)  the fp32 state slice (d_k x 16) in registers;
+//                    per pair: K H, U, the 32-deep state update, all on MFMA;
+//   "output" (one per slice) diag(gamma) Q H + P U on MFMA and the bf16
+//                    stores, one pair behind the chain; q comes through the
+//                    loader, P and gamma straight from global memory, several
+//                    pairs ahead;
+//   "loader"         streams k, q, v and the chain's part of the workspace
 //                    into a ring of LDS records with direct global->LDS loads,
 //                    a few pairs ahead of the chain;
-//   wave 3 "prefetch" touches the lines of a pair further ahead so that the
-//                    loader's requests hit L2: the d_v slices of a head split
+//   "prefetch"       touches the lines of a pair further ahead so that the
+//                    loader's requests hit L2: the workgroups of a head split
 //                    the lines between them, one 4-byte load per line.
 //   One workgroup barrier per pair.  The state (bf16) and U reach the output
-//   wave through LDS, double buffered by pair parity.
+//   wave through LDS, double buffered by pair parity.  Two slices share one
+//   workgroup only when one slice per workgroup would need more than one
+//   round of workgroups; then they share the loader's traffic.
 //
 // Precision: Tb, P and U are split into bf16 hi + lo parts and contracted as
 // [X_hi | X_lo] . [Y ; Y] in one 32-deep MFMA (the issue cost of a 16-deep
