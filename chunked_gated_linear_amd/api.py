@@ -83,6 +83,53 @@ def lin_attn_chunk_fwd(q, k, v, gate, beta, h0=None, *, gate_mode="log", G=5.0,
     return o, hT
 
 
+def lin_attn_chunk_fwd_varlen_workspace_size(T, nseq, H, Dk, Dv, dtype=torch.bfloat16):
+    """Workspace bytes lin_attn_chunk_fwd_varlen needs for these sizes."""
+    n = N.lib().lin_attn_chunk_fwd_varlen_workspace_size(T, nseq, H, Dk, Dv, _DTYPES[dtype])
+    if n < 0:
+        raise N.LinAttnError(N.LA_EINVAL, N.lib().lin_attn_last_error().decode())
+    return n
+
+
+def lin_attn_chunk_fwd_varlen(q, k, v, gate, beta, cu_seqlens, h0=None, *, gate_mode="log",
+                              G=5.0, o=None, hT=None, output_final_state=True,
+                              workspace=None, stream=None):
+    """Packed sequences: q, k [1,T,H,Dk], v [1,T,H,Dv], gate, beta [1,T,H] hold
+    nseq sequences back to back, sequence s at tokens [cu[s], cu[s+1]) with
+    cu_seqlens an int32 GPU tensor of nseq + 1 offsets.  Returns o [1,T,H,Dv]
+    and the final states hT [nseq,H,Dk,Dv] (None if not requested)."""
+    _need(q, "q", torch.bfloat16)
+    _, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    _need(k, "k", q.dtype, (1, T, H, Dk))
+    _need(v, "v", q.dtype, (1, T, H, Dv))
+    _need(gate, "gate", torch.float32, (1, T, H))
+    _need(beta, "beta", torch.float32, (1, T, H))
+    _need(cu_seqlens, "cu_seqlens", torch.int32)
+    nseq = cu_seqlens.numel() - 1
+    if cu_seqlens.dim() != 1 or nseq < 0:
+        raise ValueError("cu_seqlens must be a 1-D tensor of nseq + 1 offsets")
+    if h0 is not None:
+        _need(h0, "h0", torch.float32, (nseq, H, Dk, Dv))
+    if o is None:
+        o = torch.empty((1, T, H, Dv), dtype=q.dtype, device=q.device)
+    _need(o, "o", q.dtype, (1, T, H, Dv))
+    if hT is None and output_final_state:
+        hT = torch.empty((nseq, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    if hT is not None:
+        _need(hT, "hT", torch.float32, (nseq, H, Dk, Dv))
+    nws = lin_attn_chunk_fwd_varlen_workspace_size(T, nseq, H, Dk, Dv, q.dtype)
+    if workspace is None and nws > 0:
+        workspace = torch.empty(nws, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8)
+    N.check(N.lib().lin_attn_chunk_fwd_varlen(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _GATE[gate_mode], float(G), _ptr(beta),
+        _ptr(h0), _ptr(o), _ptr(hT), _ptr(cu_seqlens), nseq, T, H, Dk, Dv, _DTYPES[q.dtype],
+        _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(q, stream)))
+    return o, hT
+
+
 def lin_attn_decode_step(q, k, v, gate, beta, S, *, gate_mode="log", G=5.0, o=None,
                          stream=None):
     """Advance S [B,H,Dk,Dv] by one token in place; returns o [B,H,Dv]."""

@@ -162,7 +162,19 @@ struct PrepArgs {
   int gate_logit;
   float G;
   int B, T, TB, H;
+  // Packed sequences (cu != nullptr): B sequences, sequence s holds tokens
+  // [cu[s], cu[s+1]) of one packed sequence of TB tokens, and its pair p has
+  // workspace record slot(s, p) = floor(cu[s] / 32) + s + p of nslot per head.
+  const int* cu;
+  int nslot;
 };
+
+// Token range of packed sequence s, clamped to [0, TB] (so that out-of-order
+// offsets stay memory-safe).
+__device__ inline int seq_begin(const int* cu, int s, int TB) { return min(max(cu[s], 0), TB); }
+__device__ inline int seq_end(const int* cu, int s, int TB) {
+  return min(max(cu[s + 1], seq_begin(cu, s, TB)), TB);
+}
 
 template <int DK>
 __device__ __forceinline__ void prep_body(char* smem, int64_t blk, const PrepArgs& pa) {
@@ -175,16 +187,40 @@ __device__ __forceinline__ void prep_body(char* smem, int64_t blk, const PrepArg
   char* __restrict__ const ws = pa.ws;
   const int gate_logit = pa.gate_logit;
   const float G = pa.G;
-  const int B = pa.B, T = pa.T, H = pa.H;
+  const int B = pa.B, H = pa.H;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, grp = lane >> 4;
-  const int NSC = (T + 31) >> 5;
-  const int64_t job = blk * kPrepWaves + wave;                   // = head * NSC + pair
-  if (job >= (int64_t)B * H * NSC) return;                        // no barriers in this kernel
-  const int head = (int)(job / NSC);
-  const int c = (int)(job - (int64_t)head * NSC);
-  const int b = head / H, h = head - b * H;
+  const int64_t job = blk * kPrepWaves + wave;   // no barriers in this kernel: idle waves return
+  int T, b, h, c;
+  int64_t tok0;                                  // token (b, 0, h)
+  if (pa.cu) {
+    // packed sequences: job = h * nslot + slot
+    if (job >= (int64_t)H * pa.nslot) return;
+    h = (int)(job / pa.nslot);
+    const int slot = (int)(job - (int64_t)h * pa.nslot);
+    int lo = 0, hi = B - 1;                      // the last s with slot(s, 0) <= slot
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (seq_begin(pa.cu, mid, pa.TB) / 32 + mid <= slot) lo = mid;
+      else hi = mid - 1;
+    }
+    b = lo;
+    const int tb = seq_begin(pa.cu, b, pa.TB);
+    T = seq_end(pa.cu, b, pa.TB) - tb;
+    c = slot - (tb / 32 + b);
+    if (c < 0 || c >= ((T + 31) >> 5)) return;   // a slot no pair uses
+    tok0 = (int64_t)tb * H + h;
+  } else {
+    T = pa.T;
+    const int NSC = (T + 31) >> 5;
+    if (job >= (int64_t)B * H * NSC) return;
+    const int head = (int)(job / NSC);
+    c = (int)(job - (int64_t)head * NSC);
+    b = head / H;
+    h = head - b * H;
+    tok0 = (int64_t)b * pa.TB * H + h;
+  }
 
   char* scr = smem + wave * (kPrepScr + kPrepRows);
   char* rows = scr + kPrepScr;
@@ -201,7 +237,6 @@ __device__ __forceinline__ void prep_body(char* smem, int64_t blk, const PrepArg
   // 256-byte row, or two 128-byte rows at d_k = 64; a quarter spanning 16
   // rows would cost the address unit about three times as much) and turned
   // into MFMA fragments through LDS, in the row blocks of rslot.
-  const int64_t tok0 = (int64_t)b * pa.TB * H + h;   // token (b, 0, h)
   constexpr int NL = DK / 16;                    // 1 KB loads per pair and matrix
   bf16x8 kr[NL], qr[NL];
   int lofs[NL];
@@ -445,6 +480,8 @@ struct StateArgs {
   __bf16* o;
   float* hT;
   int B, T, TB, H, DV;
+  const int* cu;     // packed sequences, as in PrepArgs
+  int nslot;
 };
 
 template <int DK, int SPW>
@@ -458,7 +495,7 @@ __device__ __forceinline__ void state_body(char* smem, int blk, const StateArgs&
   const float* const h0 = sa.h0;
   __bf16* __restrict__ const o = sa.o;
   float* const hT = sa.hT;
-  const int B = sa.B, T = sa.T, H = sa.H, DV = sa.DV;
+  const int B = sa.B, H = sa.H, DV = sa.DV;
 
   const int NV = DV / 16, NVG = NV / SPW;       // slices, slice groups per head
   int head, vg;
@@ -470,9 +507,29 @@ __device__ __forceinline__ void state_body(char* smem, int blk, const StateArgs&
   const int v0 = vt * 16;
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, grp = lane >> 4;
+  int T;
+  int64_t tok0;                                          // token (b, 0, h)
+  const char* wsh;                                       // record of pair 0
+  if (sa.cu) {
+    const int tb = seq_begin(sa.cu, b, sa.TB);
+    T = seq_end(sa.cu, b, sa.TB) - tb;
+    tok0 = (int64_t)tb * H + h;
+    wsh = ws + ((int64_t)h * sa.nslot + tb / 32 + b) * WsRec::BYTES;
+  } else {
+    T = sa.T;
+    tok0 = (int64_t)b * sa.TB * H + h;
+    wsh = ws + (int64_t)head * ((T + 31) >> 5) * WsRec::BYTES;
+  }
   const int NSC = (T + 31) >> 5;                          // pairs of tiles
-  const int64_t tok0 = (int64_t)b * sa.TB * H + h;       // token (b, 0, h)
-  const char* const wsh = ws + (int64_t)head * NSC * WsRec::BYTES;
+  if (NSC == 0) {
+    // an empty packed sequence: hT = h0 (zeros without h0), by the chain waves
+    if (wave < C::W_OUT && hT) {
+      const int64_t sbase = ((int64_t)b * H + h) * DK * DV;
+      for (int r = 0; r < DK; r += 4)
+        hT[sbase + (int64_t)(r + grp) * DV + v0 + n] = h0 ? h0[sbase + (int64_t)(r + grp) * DV + v0 + n] : 0.f;
+    }
+    return;
+  }
   // Record of pair c.  The byte offset goes through an empty asm so that the
   // compiler keeps one scalar base per pair instead of rewriting every LDS
   // address as its own induction variable.
@@ -899,6 +956,53 @@ long long chunk_pair_workspace_bytes(int B, int T, int H, int Dk, int Dv) {
   long long n = (long long)B * H * NSC * WsRec::BYTES;
   if (stretch_area(NSC)) n += (long long)B * H * Dk * Dv * 4;
   return n;
+}
+
+// Packed sequences: one intra-tile launch over every record slot (idle slots
+// return at once), then one inter-tile launch over (sequence, head, slices).
+static int varlen_slots(int T, int nseq) { return T / 32 + nseq + 1; }
+
+template <int DK>
+static hipError_t launch_varlen_t(const void* q, const void* k, const void* v, const float* gate,
+                                  int gate_logit, float G, const float* beta, const float* h0,
+                                  void* o, float* hT, const int* cu, int nseq, int T, int H, int Dv,
+                                  void* ws, hipStream_t st) {
+  const int nslot = varlen_slots(T, nseq);
+  const int NV = Dv / 16;
+  const int spw = (NV % 2 == 0 && (int64_t)nseq * H * NV > compute_units()) ? 2 : 1;
+  const int nstate = nseq * H * (NV / spw);
+  char* const wsb = static_cast<char*>(ws);
+  const PrepArgs pa{(const __bf16*)q, (const __bf16*)k, gate, beta, wsb, gate_logit, G,
+                    nseq, 0, T, H, cu, nslot};
+  const int64_t pblocks = ((int64_t)H * nslot + kPrepWaves - 1) / kPrepWaves;
+  hipLaunchKernelGGL((chunk_prep_kernel<DK>), dim3((unsigned)pblocks), dim3(64 * kPrepWaves), 0,
+                     st, pa);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const StateArgs sa{(const __bf16*)q, (const __bf16*)k, (const __bf16*)v, wsb, h0, (__bf16*)o,
+                     hT, nseq, 0, T, H, Dv, cu, nslot};
+  constexpr int kThreads1 = CfgS<DK, 1>::THREADS, kThreads2 = CfgS<DK, 2>::THREADS;
+  if (spw == 2)
+    hipLaunchKernelGGL((chunk_state_kernel<DK, 2>), dim3(nstate), dim3(kThreads2), 0, st, sa,
+                       PrepArgs{}, nstate, 0);
+  else
+    hipLaunchKernelGGL((chunk_state_kernel<DK, 1>), dim3(nstate), dim3(kThreads1), 0, st, sa,
+                       PrepArgs{}, nstate, 0);
+  return hipGetLastError();
+}
+
+long long chunk_pair_varlen_workspace_bytes(int T, int nseq, int H) {
+  return (long long)H * varlen_slots(T, nseq) * WsRec::BYTES;
+}
+
+hipError_t launch_chunk_fwd_pair_varlen(const void* q, const void* k, const void* v,
+                                        const float* gate, int gate_logit, float G,
+                                        const float* beta, const float* h0, void* o, float* hT,
+                                        const int* cu, int nseq, int T, int H, int Dk, int Dv,
+                                        void* ws, hipStream_t st) {
+  if (Dk == 64) return launch_varlen_t<64>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, cu, nseq, T, H, Dv, ws, st);
+  if (Dk == 128) return launch_varlen_t<128>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, cu, nseq, T, H, Dv, ws, st);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_chunk_fwd_pair(const void* q, const void* k, const void* v, const float* gate,

@@ -25,6 +25,17 @@ hipError_t launch_chunk_fwd_pair(const void* q, const void* k, const void* v,
 // cut into stretches.
 long long chunk_pair_workspace_bytes(int B, int T, int H, int Dk, int Dv);
 
+// Packed sequences (bf16): sequence s is tokens [cu[s], cu[s+1]) of one packed
+// sequence of T tokens; cu is a device array of nseq + 1 offsets.
+hipError_t launch_chunk_fwd_pair_varlen(const void* q, const void* k, const void* v,
+                                        const float* gate, int gate_logit, float G,
+                                        const float* beta, const float* h0, void* o, float* hT,
+                                        const int* cu, int nseq, int T, int H, int Dk, int Dv,
+                                        void* ws, hipStream_t st);
+
+// Workspace bytes of the packed-sequence path: H * (T / 32 + nseq + 1) records.
+long long chunk_pair_varlen_workspace_bytes(int T, int nseq, int H);
+
 hipError_t launch_decode(const void* q, const void* k, const void* v,
                          const float* gate, int gate_logit, float G,
                          const float* beta, float* S, void* o, int BH, int Dk,

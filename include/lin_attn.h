@@ -126,6 +126,50 @@ int lin_attn_chunk_fwd(const void* q, const void* k, const void* v,
                        void* stream);
 
 /*
+ * lin_attn_chunk_fwd_varlen_workspace_size -- bytes of device workspace that
+ * lin_attn_chunk_fwd_varlen needs: H * (T / 32 + nseq + 1) * 6656 for LA_BF16
+ * (one 6656-byte record slot per 32 tokens of each packed sequence, as in
+ * lin_attn_chunk_fwd, plus one spare slot per sequence for its ragged end),
+ * -1 (with lin_attn_last_error() set) for invalid or unsupported sizes,
+ * including dtype LA_FP32.
+ */
+long long lin_attn_chunk_fwd_varlen_workspace_size(int T, int nseq, int H, int Dk, int Dv,
+                                                   int dtype);
+
+/*
+ * lin_attn_chunk_fwd_varlen -- the same forward pass over packed sequences of
+ * different lengths (chunked prefill of a serving batch, "Evaluating Next-Gen
+ * ...", sec. 4): sequence s is tokens [cu_seqlens[s], cu_seqlens[s + 1]) of
+ * one packed sequence of T tokens, starts from its own initial state h0[s]
+ * and never sees another sequence's state.  Each sequence is processed
+ * exactly as lin_attn_chunk_fwd processes a sequence of its length (its own
+ * tiles start at its first token).
+ *
+ *   q, k        [T, H, Dk]  bf16         (a batch of one packed sequence)
+ *   v, o        [T, H, Dv]  bf16
+ *   gate, beta  [T, H]      float32
+ *   h0, hT      [nseq, H, Dk, Dv] float32, or NULL as in lin_attn_chunk_fwd
+ *   cu_seqlens  DEVICE array of nseq + 1 int32 offsets: 0 = cu[0] <= cu[1] <=
+ *               ... <= cu[nseq] = T.  The values are read on the device only
+ *               (no synchronisation); they are clamped to [0, T] so that any
+ *               values stay memory-safe, but offsets that are not
+ *               non-decreasing give undefined results.  Empty sequences are
+ *               allowed (their hT is h0, or zeros).
+ *   workspace   lin_attn_chunk_fwd_varlen_workspace_size(...) bytes, as in
+ *               lin_attn_chunk_fwd.
+ *   dtype       LA_BF16 only (LA_FP32 returns LA_EUNSUPPORTED).
+ *   Dk in {64, 128}; Dv a multiple of 16 in [16, 256]; T, nseq, H >= 0.
+ * Alignment and aliasing rules are those of lin_attn_chunk_fwd.
+ */
+int lin_attn_chunk_fwd_varlen(const void* q, const void* k, const void* v,
+                              const float* gate, int gate_mode, float G,
+                              const float* beta, const float* h0,
+                              void* o, float* hT, const int* cu_seqlens, int nseq,
+                              int T, int H, int Dk, int Dv, int dtype,
+                              void* workspace, long long workspace_bytes,
+                              void* stream);
+
+/*
  * lin_attn_decode_step -- one new token per (b, h), state updated in place.
  *
  * Constant-state recurrent inference: each sequence advances its d_k x d_v

@@ -97,3 +97,31 @@ def recurrent_fwd(q, k, v, g, beta, h0=None, workers=None):
         o[b, :, h] = ob
         hT[b, h] = hb
     return o, hT
+
+
+def recurrent_fwd_varlen(q, k, v, g, beta, cu_seqlens, h0=None, workers=None):
+    """Packed sequences with the same signature and result as
+    linattn_oracle.recurrent_fwd_varlen, one (sequence, head) stream per task."""
+    cu = [int(x) for x in cu_seqlens]
+    _, T, H, Dk = np.shape(q)
+    Dv = np.shape(v)[-1]
+    N = len(cu) - 1
+    if workers is None:
+        workers = min(16, os.cpu_count() or 1)
+    tasks = [(s, h) for s in range(N) for h in range(H) if cu[s + 1] > cu[s]]
+
+    def one(sh):
+        s, h = sh
+        a, b = cu[s], cu[s + 1]
+        init = None if h0 is None else h0[s, h]
+        return head_fwd(q[0, a:b, h], k[0, a:b, h], v[0, a:b, h], g[0, a:b, h], beta[0, a:b, h], init)
+
+    o = np.empty((1, T, H, Dv))
+    hT = np.zeros((N, H, Dk, Dv))
+    if h0 is not None:
+        hT[:] = np.asarray(h0, dtype=np.float64)
+    with cf.ThreadPoolExecutor(max(1, min(workers, max(1, len(tasks))))) as ex:
+        for (s, h), (os_, hs) in zip(tasks, ex.map(one, tasks)):
+            o[0, cu[s]:cu[s + 1], h] = os_
+            hT[s, h] = hs
+    return o, hT

@@ -49,6 +49,12 @@ itself are in tests/test_oracle.py):
                    masked gated linear attention), invariants (identity step,
                    write-then-query, split invariance, linearity, norm bound).
   decode_step      equals recurrent_fwd applied one token at a time.
+  recurrent_fwd_varlen
+                   packed sequences: a closed form at every boundary (a
+                   sequence whose tokens neither write nor decay returns its own
+                   h0 exactly, whatever came before it; a planted carry-over
+                   fails it), equal lengths equal the batch axis, and the C
+                   copy agrees on mixed lengths with empty sequences.
   chunked_fwd      equals recurrent_fwd for chunk sizes 1, 3, 16 and 32 (two
                    independent formulations of the same definition).
 Every function is pinned; none is "parity unpinned".
@@ -72,6 +78,7 @@ __all__ = [
     "decode_step",
     "chunked_fwd",
     "recurrent_fwd_heads",
+    "recurrent_fwd_varlen",
 ]
 
 
@@ -126,6 +133,37 @@ def recurrent_fwd(q, k, v, g, beta, h0=None):
         h = a * erased + b * kt[:, :, :, None] * vt[:, :, None, :]
         o[:, t] = np.einsum("bhk,bhkv->bhv", q[:, t], h)    # h_t^T q_t
     return o, h
+
+
+def recurrent_fwd_varlen(q, k, v, g, beta, cu_seqlens, h0=None):
+    """Packed sequences, as a serving batch prefills several requests back to
+    back ("Evaluating Next-Gen Sparse MoE and Long-Context LLMs", sec. 4):
+    sequence s is tokens [cu[s], cu[s+1]) of the packed arrays q, k [1,T,H,Dk],
+    v [1,T,H,Dv], g, beta [1,T,H].  It starts from h0[s] (zeros when h0 is
+    None) and its recurrence reads no other sequence's tokens or state.
+
+    Returns (o [1,T,H,Dv], hT [N,H,Dk,Dv]) in float64; an empty sequence has
+    hT = its initial state.
+    """
+    q, k, v, g, beta = map(_f64, (q, k, v, g, beta))
+    cu = [int(x) for x in cu_seqlens]
+    _, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    N = len(cu) - 1
+    if N < 0 or cu[0] != 0 or cu[-1] != T or any(b < a for a, b in zip(cu, cu[1:])):
+        raise ValueError("cu_seqlens must run from 0 to T without decreasing")
+    o = np.empty((1, T, H, Dv))
+    hT = np.zeros((N, H, Dk, Dv))
+    for s in range(N):
+        a, b = cu[s], cu[s + 1]
+        init = None if h0 is None else _f64(h0)[s:s + 1]
+        if b > a:
+            o_s, h_s = recurrent_fwd(q[:, a:b], k[:, a:b], v[:, a:b], g[:, a:b], beta[:, a:b], init)
+            o[:, a:b] = o_s
+            hT[s] = h_s[0]
+        elif init is not None:
+            hT[s] = init[0]
+    return o, hT
 
 
 def decode_step(q, k, v, g, beta, S):

@@ -191,3 +191,48 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(N, "LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(RuntimeError, match="no fallback"):
         N.lib()
+
+
+def varlen(**kw):
+    a = dict(q=fake(0), k=fake(1), v=fake(2), gate=fake(3), gate_mode=0, G=5.0,
+             beta=fake(4), h0=None, o=fake(5), hT=fake(6), cu=fake(9), nseq=3, T=64, H=2,
+             Dk=128, Dv=128, dtype=0, ws=fake(8), ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    L = N.lib()
+    rc = L.lin_attn_chunk_fwd_varlen(a["q"], a["k"], a["v"], a["gate"], a["gate_mode"], a["G"],
+                                     a["beta"], a["h0"], a["o"], a["hT"], a["cu"], a["nseq"],
+                                     a["T"], a["H"], a["Dk"], a["Dv"], a["dtype"], a["ws"],
+                                     a["ws_bytes"], a["stream"])
+    return rc, L.lin_attn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(cu=None), N.LA_EINVAL, "cu_seqlens must not be NULL"),
+    (dict(cu=fake(9) + 2), N.LA_EINVAL, "cu_seqlens must be 4-byte aligned"),
+    (dict(nseq=-1), N.LA_EINVAL, "nseq"),
+    (dict(dtype=1), N.LA_EUNSUPPORTED, "LA_BF16 only"),
+    (dict(Dk=96), N.LA_EUNSUPPORTED, "Dk"),
+    (dict(q=None), N.LA_EINVAL, "q must not be NULL"),
+    (dict(gate_mode=5), N.LA_EINVAL, "gate_mode"),
+    (dict(ws=None), N.LA_EINVAL, "workspace must not be NULL"),
+    (dict(ws_bytes=2 * (64 // 32 + 3 + 1) * 6656 - 1), N.LA_EINVAL, "workspace too small"),
+    (dict(o=fake(0) + 64), N.LA_EINVAL, "o overlaps q"),
+    (dict(cu=fake(6)), N.LA_EINVAL, "hT overlaps cu_seqlens"),
+    (dict(ws=fake(9)), N.LA_EINVAL, "workspace overlaps cu_seqlens"),
+])
+def test_varlen_rejects(kw, code, needle):
+    rc, msg = varlen(**kw)
+    assert rc == code, (rc, msg)
+    assert needle in msg
+
+
+def test_varlen_workspace_size_and_empty():
+    L = N.lib()
+    ws = L.lin_attn_chunk_fwd_varlen_workspace_size
+    # one record slot per 32 tokens per head plus one per sequence and one spare
+    assert ws(65536, 64, 16, 128, 128, N.LA_BF16) == 16 * (2048 + 64 + 1) * 6656
+    assert ws(100, 3, 2, 64, 64, N.LA_BF16) == 2 * (3 + 3 + 1) * 6656
+    assert ws(100, 3, 2, 64, 64, N.LA_FP32) == -1
+    assert "LA_BF16 only" in L.lin_attn_last_error().decode()
+    # no sequences: nothing to do, nothing touched
+    assert varlen(nseq=0, q=None, cu=None, ws=None)[0] == N.LA_OK

@@ -420,3 +420,70 @@ def test_gate_mutants_are_caught(golden_dir):
         g = f(x)
         good = g[1] == -G / 2 and g[2] == -G and g[0] == 0.0
         assert not good, name
+
+
+# ------------------------------------------------------ packed sequences
+def _varlen_case(lengths, H=2, Dk=8, Dv=6, gate="std", seed=0, h0=True):
+    T = int(sum(lengths))
+    q, k, v, g, beta, _ = rand_inputs(1, T, H, Dk, Dv, gate=gate, seed=seed)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    hh = 0.02 * np.random.default_rng(seed + 1).standard_normal((len(lengths), H, Dk, Dv)) if h0 else None
+    return q, k, v, g, beta, cu, hh
+
+
+def _carry_over_mutant(q, k, v, g, beta, cu, h0):
+    """A plausible mistake: the state is not reset where a sequence begins."""
+    o, hlast = orc.recurrent_fwd(q, k, v, g, beta, None if h0 is None else h0[:1])
+    hT = np.stack([orc.recurrent_fwd(q[:, :b], k[:, :b], v[:, :b], g[:, :b], beta[:, :b],
+                                     None if h0 is None else h0[:1])[1][0] for b in cu[1:]])
+    return o, hT
+
+
+def _boundary_pin(fwd):
+    """Closed form at a boundary: the second sequence neither writes (beta = 0)
+    nor decays (g = 0), so its outputs are h0[1]^T q_t exactly and its final
+    state is h0[1], whatever the first sequence did."""
+    q, k, v, g, beta, cu, h0 = _varlen_case([7, 5], gate="std", seed=3)
+    g[:, 7:] = 0.0
+    beta[:, 7:] = 0.0
+    o, hT = fwd(q, k, v, g, beta, cu, h0)
+    want = np.einsum("thk,hkv->thv", q[0, 7:], h0[1])
+    return np.allclose(o[0, 7:], want, rtol=1e-13, atol=1e-15) and np.allclose(hT[1], h0[1], rtol=0, atol=0)
+
+
+def test_varlen_boundary_closed_form():
+    assert _boundary_pin(orc.recurrent_fwd_varlen)
+
+
+def test_varlen_carry_over_mutant_is_caught():
+    assert not _boundary_pin(_carry_over_mutant)
+
+
+def test_varlen_equal_lengths_equal_the_batch_axis():
+    N, L, H, Dk, Dv = 3, 11, 2, 8, 6
+    q, k, v, g, beta, cu, h0 = _varlen_case([L] * N, H, Dk, Dv, gate="weak", seed=5)
+    o, hT = orc.recurrent_fwd_varlen(q, k, v, g, beta, cu, h0)
+    rs = lambda a: a.reshape((N, L) + a.shape[2:])
+    ob, hb = orc.recurrent_fwd(rs(q), rs(k), rs(v), rs(g), rs(beta), h0)
+    np.testing.assert_allclose(o.reshape(ob.shape), ob, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(hT, hb, rtol=1e-13, atol=1e-15)
+
+
+def test_varlen_c_matches_numpy_with_empty_sequences():
+    from oracle import c_recurrent
+    lengths = [0, 1, 17, 0, 33, 5]
+    for h0flag in (True, False):
+        q, k, v, g, beta, cu, h0 = _varlen_case(lengths, 3, 16, 8, gate="weak", seed=7, h0=h0flag)
+        o, hT = orc.recurrent_fwd_varlen(q, k, v, g, beta, cu, h0)
+        oc, hc = c_recurrent.recurrent_fwd_varlen(q, k, v, g, beta, cu, h0, workers=2)
+        np.testing.assert_allclose(oc, o, rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(hc, hT, rtol=1e-12, atol=1e-14)
+        assert np.array_equal(hT[0], np.zeros_like(hT[0]) if h0 is None else h0[0])
+
+
+def test_varlen_rejects_bad_offsets():
+    q, k, v, g, beta, cu, h0 = _varlen_case([3, 4], seed=9)
+    with pytest.raises(ValueError):
+        orc.recurrent_fwd_varlen(q, k, v, g, beta, [0, 5, 4], h0)
+    with pytest.raises(ValueError):
+        orc.recurrent_fwd_varlen(q, k, v, g, beta, [0, 3, 6], h0)

@@ -11,7 +11,8 @@ import numpy as np
 import pytest
 import torch
 
-from chunked_gated_linear_amd import lin_attn_chunk_fwd, lin_attn_decode_step, lin_attn_gate
+from chunked_gated_linear_amd import (lin_attn_chunk_fwd, lin_attn_chunk_fwd_varlen,
+                                      lin_attn_decode_step, lin_attn_gate)
 from chunked_gated_linear_amd import inputs as I
 from oracle import c_recurrent as crec
 from oracle import linattn_oracle as orc
@@ -207,6 +208,56 @@ def test_stretches(case):
     assert h2.data_ptr() == h.data_ptr() and torch.equal(o2, o) and torch.equal(h, hT)
     o3, h3 = run_gpu(dev, hT=False)
     assert h3 is None and torch.equal(o3, o)
+
+
+# ------------------------------------------------------- packed sequences
+VARLEN = [
+    # sequence lengths, H, Dk, Dv, regime, gate mode, with h0
+    ([0, 1, 17, 32, 33, 100, 500, 1000, 2049], 4, 128, 128, "weak", "logit", True),
+    ([5, 0, 64, 77, 300], 3, 64, 64, "std", "log", False),
+    ([40] * 300, 2, 64, 64, "weak", "logit", True),     # 2400 slices: two per workgroup
+]
+
+
+@pytest.mark.parametrize("case", VARLEN, ids=lambda c: f"n{len(c[0])}-H{c[1]}-d{c[2]}x{c[3]}-{c[4]}")
+def test_varlen(case):
+    """Packed sequences of mixed lengths (empty ones included) against the
+    oracle, every output; an empty sequence's final state is its h0 exactly."""
+    lengths, H, Dk, Dv, regime, mode, with_h0 = case
+    T, nseq = int(sum(lengths)), len(lengths)
+    name = f"varlen {nseq} seqs T{T} H{H} dk{Dk} dv{Dv} bf16 {regime}"
+    say(name)
+    dev, hst = make_case(1, T, H, Dk, Dv, "bf16", regime, mode, None, seed=21)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int32, device="cuda")
+    h0 = None
+    if with_h0:
+        gen = torch.Generator(device="cuda").manual_seed(22)
+        h0 = 0.02 * torch.randn((nseq, H, Dk, Dv), generator=gen, device="cuda")
+    o, hT = lin_attn_chunk_fwd_varlen(dev["q"], dev["k"], dev["v"], dev["gate"], dev["beta"], cu,
+                                      h0, gate_mode=mode)
+    torch.cuda.synchronize()
+    q, k, v, g, beta, _ = hst
+    ref_o, ref_h = crec.recurrent_fwd_varlen(q, k, v, g, beta, cu.cpu().numpy(),
+                                             None if h0 is None else host(h0).astype(np.float64))
+    check(name, "bf16", o, hT, ref_o, ref_h)
+    for s_, n_ in enumerate(lengths):
+        if n_ == 0:
+            assert torch.equal(hT[s_], h0[s_] if h0 is not None else torch.zeros_like(hT[s_]))
+
+
+def test_varlen_equal_lengths_match_batched_bitwise():
+    """Equal lengths: the packed call reproduces the batched call bit for bit
+    (the same per-sequence work in the same order)."""
+    say("varlen vs batched: 3 x 1000 tokens H4 d128 bf16 weak")
+    N_, L_, H = 3, 1000, 4
+    dev, hst = make_case(N_, L_, H, 128, 128, "bf16", "weak", "logit", 0.02, seed=23)
+    o_b, h_b = run_gpu(dev)
+    pk = lambda t: t.reshape((1, N_ * L_) + tuple(t.shape[2:]))
+    cu = torch.tensor([0, L_, 2 * L_, 3 * L_], dtype=torch.int32, device="cuda")
+    o_v, h_v = lin_attn_chunk_fwd_varlen(pk(dev["q"]), pk(dev["k"]), pk(dev["v"]), pk(dev["gate"]),
+                                         pk(dev["beta"]), cu, dev["h0"], gate_mode="logit")
+    torch.cuda.synchronize()
+    assert torch.equal(o_v.reshape(o_b.shape), o_b) and torch.equal(h_v, h_b)
 
 
 def test_state_in_place_and_empty():
