@@ -7,7 +7,7 @@ Default workload: B=1, H=16, T=65536, d_k=d_v=128, bf16 q/k/v, fp32 gates and
 state, 16-token tiles.  Prints ONE JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload long_64k]
-                    [--decode-steps 1000] [--no-cpu-baseline]
+                    [--decode-steps 1000] [--varlen-steps 20] [--no-cpu-baseline]
 """
 
 from __future__ import annotations
@@ -85,6 +85,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="long_64k")
     ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--varlen-steps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=65536,
                     help="tokens per head in the CPU-baseline sample")
@@ -103,8 +104,9 @@ def main():
     import torch
 
     from chunked_gated_linear_amd import inputs as I
-    from chunked_gated_linear_amd import (lin_attn_chunk_fwd, lin_attn_chunk_fwd_workspace_size,
-                                          lin_attn_decode_step)
+    from chunked_gated_linear_amd import (lin_attn_chunk_fwd, lin_attn_chunk_fwd_varlen,
+                                          lin_attn_chunk_fwd_varlen_workspace_size,
+                                          lin_attn_chunk_fwd_workspace_size, lin_attn_decode_step)
 
     wl = dict(I.WORKLOADS[args.workload])
     B, H, T, Dk, Dv, dtype = wl["B"], wl["H"], wl["T"], wl["Dk"], wl["Dv"], wl["dtype"]
@@ -176,6 +178,45 @@ def main():
                      "alg_flops_per_launch": flops,
                      "attainable_frac": max(byts / PEAK_HBM, flops / PEAK_BF16) / t},
     }
+
+    # ---- packed prefill batch: 64 requests of mixed lengths, 64K tokens in all
+    if args.varlen_steps > 0:
+        vw = I.VARLEN_WORKLOAD
+        lengths = I.varlen_lengths(vw["nseq"], vw["T"], seed=1006)
+        vin = I.make_inputs(1, vw["T"], vw["H"], vw["Dk"], vw["Dv"], dtype=vw["dtype"], seed=1006,
+                            device=dev)
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int32, device=dev)
+        ov = torch.empty((1, vw["T"], vw["H"], vw["Dv"]), dtype=vin["q"].dtype, device=dev)
+        hv = torch.empty((vw["nseq"], vw["H"], vw["Dk"], vw["Dv"]), dtype=torch.float32, device=dev)
+        wsv = torch.empty(lin_attn_chunk_fwd_varlen_workspace_size(vw["T"], vw["nseq"], vw["H"],
+                                                                    vw["Dk"], vw["Dv"]),
+                          dtype=torch.uint8, device=dev)
+
+        def vstep():
+            lin_attn_chunk_fwd_varlen(vin["q"], vin["k"], vin["v"], vin["x"], vin["beta"], cu,
+                                      gate_mode="logit", G=5.0, o=ov, hT=hv, workspace=wsv)
+
+        for _ in range(2):
+            vstep()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.varlen_steps):
+            vstep()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        vms = e0.elapsed_time(e1) / args.varlen_steps
+        vbytes = vw["T"] * vw["H"] * (2 * (2 * vw["Dk"] + vw["Dv"]) + 2 * vw["Dv"] + 8) \
+            + vw["nseq"] * vw["H"] * vw["Dk"] * vw["Dv"] * 4
+        result["varlen"] = {
+            "workload": (f"{vw['nseq']} packed sequences, lengths {min(lengths)}..{max(lengths)} "
+                         f"(log-normal), {vw['T']} tokens, H={vw['H']} d={vw['Dk']} bf16"),
+            "ms_per_call": vms, "tokens_per_s": vw["T"] / (vms * 1e-3),
+            "roofline": {"bound": "hbm", "achieved": vbytes / (vms * 1e-3) / 1e9,
+                         "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                         "frac": vbytes / (vms * 1e-3) / PEAK_HBM, "alg_bytes_per_launch": vbytes,
+                         "kernel": "chunk_prep_kernel + chunk_state_kernel (packed sequences)"},
+        }
+        del vin, ov, hv, wsv
 
     # ---- optional calibration copy (reads and writes exactly copy_mib MiB)
     if args.copy_mib > 0:

@@ -83,3 +83,24 @@ WORKLOADS = {
     "million_1m": dict(B=1, H=8, T=1048576, Dk=128, Dv=128, dtype="bf16", h0_std=0.02),
 }
 DECODE_WORKLOAD = dict(B=256, H=32, Dk=128, Dv=128, dtype="bf16", steps=1000)
+
+
+# Packed prefill batch (serving): nseq request lengths drawn log-normally
+# (median T / nseq, sigma 1), then scaled and rounded to sum to T exactly with
+# every request at least one token.
+VARLEN_WORKLOAD = dict(nseq=64, T=65536, H=16, Dk=128, Dv=128, dtype="bf16")
+
+
+def varlen_lengths(nseq, T, seed=0):
+    """Seeded request lengths (a list of nseq ints >= 1 summing to T)."""
+    import numpy as np
+    if nseq <= 0 or T < nseq:
+        raise ValueError("need 1 <= nseq <= T")
+    rng = np.random.default_rng(seed)
+    w = rng.lognormal(mean=0.0, sigma=1.0, size=nseq)
+    raw = 1 + (T - nseq) * w / w.sum()
+    lengths = np.floor(raw).astype(np.int64)
+    short = T - int(lengths.sum())
+    order = np.argsort(-(raw - lengths))            # largest remainders first
+    lengths[order[:short]] += 1
+    return [int(x) for x in lengths]
