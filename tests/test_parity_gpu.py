@@ -12,7 +12,8 @@ import pytest
 import torch
 
 from chunked_gated_linear_amd import (lin_attn_chunk_fwd, lin_attn_chunk_fwd_varlen,
-                                      lin_attn_decode_step, lin_attn_gate)
+                                      lin_attn_chunk_fwd_workspace_size, lin_attn_decode_step,
+                                      lin_attn_gate)
 from chunked_gated_linear_amd import inputs as I
 from oracle import c_recurrent as crec
 from oracle import linattn_oracle as orc
@@ -258,6 +259,53 @@ def test_varlen_equal_lengths_match_batched_bitwise():
                                          pk(dev["beta"]), cu, dev["h0"], gate_mode="logit")
     torch.cuda.synchronize()
     assert torch.equal(o_v.reshape(o_b.shape), o_b) and torch.equal(h_v, h_b)
+
+
+def test_graph_capture_replays():
+    """The forward (stretched: several launches) and decode steps captured in
+    one graph replay to the eager results, replay after replay, with eager
+    work and synchronisations between the replays."""
+    say("graph capture: stretched forward B1 H4 T20000 + 3 decode steps, 3 replays")
+    dev, _ = make_case(1, 20000, 4, 128, 128, "bf16", "weak", "logit", 0.02, seed=31)
+    o_ref, h_ref = run_gpu(dev)
+    o = torch.empty_like(o_ref)
+    hT = torch.empty_like(h_ref)
+    ws = torch.empty(lin_attn_chunk_fwd_workspace_size(1, 20000, 4, 128, 128), dtype=torch.uint8,
+                     device="cuda")
+    d = I.make_decode_inputs(8, 4, 128, 128, dtype="bf16", seed=32, device="cuda", steps=3)
+    S0 = d["S"].clone()
+    S = S0.clone()
+    od = torch.empty((8, 4, 128), dtype=torch.bfloat16, device="cuda")
+
+    def work():
+        lin_attn_chunk_fwd(dev["q"], dev["k"], dev["v"], dev["gate"], dev["beta"], dev["h0"],
+                           gate_mode="logit", o=o, hT=hT, workspace=ws)
+        for st in range(3):
+            lin_attn_decode_step(d["q"][st], d["k"][st], d["v"][st], d["x"][st], d["beta"][st], S,
+                                 gate_mode="logit", o=od)
+
+    work()                                  # eager reference of the decode part
+    torch.cuda.synchronize()
+    S_ref, od_ref = S.clone(), od.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        S.copy_(S0)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            work()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        o.zero_()
+        hT.zero_()
+        S.copy_(S0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(hT, h_ref), rep
+        assert torch.equal(S, S_ref) and torch.equal(od, od_ref), rep
+        _ = run_gpu(dev)                    # eager work between replays
 
 
 def test_state_in_place_and_empty():
