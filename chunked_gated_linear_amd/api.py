@@ -47,12 +47,14 @@ def lin_attn_chunk_fwd_workspace_size(B, T, H, Dk, Dv, dtype=torch.bfloat16):
 
 def lin_attn_chunk_fwd(q, k, v, gate, beta, h0=None, *, gate_mode="log", G=5.0,
                        o=None, hT=None, output_final_state=True, workspace=None,
-                       stream=None):
+                       stream=None, raw=False):
     """o [B,T,H,Dv] and final state hT [B,H,Dk,Dv] (None if not requested).
 
     `workspace` is an optional uint8 GPU tensor of at least
     lin_attn_chunk_fwd_workspace_size(...) bytes; without one, a fresh tensor
-    is taken from torch's caching allocator."""
+    is taken from torch's caching allocator.  raw=True calls
+    lin_attn_chunk_fwd_raw: q and k as they come (L2-normalised inside the
+    pass) and `beta` holding logits (bf16 only)."""
     _need(q, "q")
     if q.dtype not in _DTYPES:
         raise TypeError("q, k, v must be bfloat16 or float32")
@@ -76,7 +78,8 @@ def lin_attn_chunk_fwd(q, k, v, gate, beta, h0=None, *, gate_mode="log", G=5.0,
         workspace = torch.empty(nws, dtype=torch.uint8, device=q.device)
     if workspace is not None:
         _need(workspace, "workspace", torch.uint8)
-    N.check(N.lib().lin_attn_chunk_fwd(
+    fn = N.lib().lin_attn_chunk_fwd_raw if raw else N.lib().lin_attn_chunk_fwd
+    N.check(fn(
         _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _GATE[gate_mode], float(G), _ptr(beta),
         _ptr(h0), _ptr(o), _ptr(hT), B, T, H, Dk, Dv, _DTYPES[q.dtype], _ptr(workspace),
         0 if workspace is None else workspace.numel(), _stream(q, stream)))

@@ -62,7 +62,11 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Workspace record of one pair of tiles of one (sequence, head), in bytes.
-// Fragment fields hold 64 lanes x 16 B in lane order.
+// Fragment fields hold 64 lanes x 16 B in lane order.  With raw inputs (q and
+// k to be normalised here) the per-token factors 1/|k_t| and 1/|q_t| are
+// folded into the record: into A and P, into gamma and delta (the chain's K H
+// and K^T updates use the raw k), and into the output's gamma (GMQ, the raw
+// q); without them GMQ equals gamma.
 struct WsRec {
   static constexpr int TB0 = 0;       // [Tb00 hi | Tb00 lo]   row n, columns 4grp..4grp+3
   static constexpr int TB1H = 1024;   // [Tb10 hi | Tb11 hi]
@@ -72,7 +76,8 @@ struct WsRec {
   static constexpr int PF1L = 5120;   // [P10 lo  | P11 lo]
   static constexpr int GM = 6144;     // gamma[32]  f32
   static constexpr int DL = 6272;     // delta[32]  f32
-  static constexpr int GC = 6400;     // Gamma      f32 (record padded to 256 B)
+  static constexpr int GC = 6400;     // Gamma      f32
+  static constexpr int GMQ = 6528;    // gamma[32] for the output, f32 (record padded to 256 B)
   static constexpr int BYTES = 6656;
 };
 
@@ -145,7 +150,8 @@ __device__ inline void lds_dma16(const void* g, void* lds) {
 // ============================================================== intra-tile
 
 constexpr int kPrepWaves = 4;
-constexpr int kPrepScr = 2304;   // per wave: A00 (then T00), A11 (then T11), beta[32], G[32]
+constexpr int kPrepScr = 2560;   // per wave: A00 (then T00), A11 (then T11), beta[32], G[32],
+                                 // 1/|k|[32], 1/|q|[32]
 constexpr int kPrepRows = 8192;  // per wave: one pair's rows of k or q, as fragment blocks
 
 constexpr int kPrepLDS = kPrepWaves * (kPrepScr + kPrepRows);
@@ -162,6 +168,9 @@ struct PrepArgs {
   int gate_logit;
   float G;
   int B, T, TB, H;
+  // Raw inputs: q and k are L2-normalised per token here (a zero vector stays
+  // zero) and beta holds logits, beta = sigmoid(x).
+  int raw;
   // Packed sequences (cu != nullptr): B sequences, sequence s holds tokens
   // [cu[s], cu[s+1]) of one packed sequence of TB tokens, and its pair p has
   // workspace record slot(s, p) = floor(cu[s] / 32) + s + p of nslot per head.
@@ -228,6 +237,8 @@ __device__ __forceinline__ void prep_body(char* smem, int64_t blk, const PrepArg
   float* sA1 = reinterpret_cast<float*>(scr + 1024);
   float* sB = reinterpret_cast<float*>(scr + 2048);
   float* sG = reinterpret_cast<float*>(scr + 2176);
+  float* sNk = reinterpret_cast<float*>(scr + 2304);
+  float* sNq = reinterpret_cast<float*>(scr + 2432);
   char* wr = ws + job * WsRec::BYTES;
 
   // Loads (rows clamped to T-1: padding tokens need no masking of q or k --
@@ -249,6 +260,33 @@ __device__ __forceinline__ void prep_body(char* smem, int64_t blk, const PrepArg
     kr[i] = *reinterpret_cast<const bf16x8*>(k + tok0 * DK + off);
     qr[i] = *reinterpret_cast<const bf16x8*>(q + tok0 * DK + off);
     lofs[i] = ((r >> 4) * NS + (c16 >> 2)) * 1024 + 16 * rslot(r & 15, c16 & 3);
+  }
+  {
+    // 1/|k_t| and 1/|q_t| of the pair's 32 rows (1 without raw inputs): the
+    // lanes that loaded a row reduce the squares of its elements in fp32
+    constexpr int LPR = 2 * DK / 16;             // lanes per row
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      float sk2 = 0.f, sq2 = 0.f;
+      if (pa.raw) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float a = (float)kr[i][e], aq = (float)qr[i][e];
+          sk2 += a * a;
+          sq2 += aq * aq;
+        }
+#pragma unroll
+        for (int m = LPR / 2; m >= 1; m >>= 1) {
+          sk2 += __shfl_xor(sk2, m);
+          sq2 += __shfl_xor(sq2, m);
+        }
+      }
+      if ((lane & (LPR - 1)) == 0) {
+        const int r = (64 * i + lane) * 16 / (2 * DK);
+        sNk[r] = !pa.raw ? 1.f : sk2 > 0.f ? 1.f / sqrtf(sk2) : 0.f;
+        sNq[r] = !pa.raw ? 1.f : sq2 > 0.f ? 1.f / sqrtf(sq2) : 0.f;
+      }
+    }
   }
   bf16x8 kf[2][NS], qf[2][NS];
   const int o_frag = 16 * rslot(n, grp);
@@ -273,6 +311,7 @@ __device__ __forceinline__ void prep_body(char* smem, int64_t blk, const PrepArg
     const int t = min(32 * c + 16 * x + n, T - 1);
     gx[x] = gate[tok0 + (int64_t)t * H];
     bt[x] = beta[tok0 + (int64_t)t * H];
+    if (pa.raw) bt[x] = sigmoid_f(bt[x]);
   }
 
   const int t0 = 32 * c;
@@ -288,10 +327,14 @@ __device__ __forceinline__ void prep_body(char* smem, int64_t blk, const PrepArg
   if (grp == 0) {
     float* gm = reinterpret_cast<float*>(wr + WsRec::GM);
     float* dl = reinterpret_cast<float*>(wr + WsRec::DL);
-    gm[n] = __expf(Ga);
-    gm[16 + n] = __expf(Gb);
-    dl[n] = __expf(Gb15 - Ga);
-    dl[16 + n] = __expf(Gb15 - Gb);
+    float* gq = reinterpret_cast<float*>(wr + WsRec::GMQ);
+    const float ea = __expf(Ga), eb = __expf(Gb);
+    gm[n] = ea * sNk[n];
+    gm[16 + n] = eb * sNk[16 + n];
+    dl[n] = __expf(Gb15 - Ga) * sNk[n];
+    dl[16 + n] = __expf(Gb15 - Gb) * sNk[16 + n];
+    gq[n] = ea * sNq[n];
+    gq[16 + n] = eb * sNq[16 + n];
     if (n == 0) *reinterpret_cast<float*>(wr + WsRec::GC) = __expf(Gb15);
     sB[n] = ba;
     sB[16 + n] = bb;
@@ -317,6 +360,10 @@ __device__ __forceinline__ void prep_body(char* smem, int64_t blk, const PrepArg
   wave_fence();
   const f32x4 Gca = reinterpret_cast<const f32x4*>(sG)[grp];       // G_a at the 4 columns
   const f32x4 Gcb = reinterpret_cast<const f32x4*>(sG)[4 + grp];   // G_b at the 4 columns
+  // inverse norms: rows (token n of each tile) and the 4 columns
+  const f32x4 Kca = reinterpret_cast<const f32x4*>(sNk)[grp];
+  const f32x4 Kcb = reinterpret_cast<const f32x4*>(sNk)[4 + grp];
+  const float Kra = sNk[n], Krb = sNk[16 + n], Qra = sNq[n], Qrb = sNq[16 + n];
   f32x4 a00, a11, a10, pp00, pp11, pp10;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -324,12 +371,12 @@ __device__ __forceinline__ void prep_body(char* smem, int64_t blk, const PrepArg
     const float d00 = __expf(fminf(Ga - Gca[i], 0.f));
     const float d11 = __expf(fminf(Gb - Gcb[i], 0.f));
     const float d10 = __expf(fminf(Gb - Gca[i], 0.f));
-    a00[i] = sc < n ? ba * d00 * s00[i] : 0.f;
-    a11[i] = sc < n ? bb * d11 * s11[i] : 0.f;
-    a10[i] = bb * d10 * s10[i];
-    pp00[i] = sc <= n ? d00 * p00[i] : 0.f;
-    pp11[i] = sc <= n ? d11 * p11[i] : 0.f;
-    pp10[i] = d10 * p10[i];
+    a00[i] = sc < n ? ba * d00 * s00[i] * (Kra * Kca[i]) : 0.f;
+    a11[i] = sc < n ? bb * d11 * s11[i] * (Krb * Kcb[i]) : 0.f;
+    a10[i] = bb * d10 * s10[i] * (Krb * Kca[i]);
+    pp00[i] = sc <= n ? d00 * p00[i] * (Qra * Kca[i]) : 0.f;
+    pp11[i] = sc <= n ? d11 * p11[i] * (Qrb * Kcb[i]) : 0.f;
+    pp10[i] = d10 * p10[i] * (Qrb * Kca[i]);
   }
   reinterpret_cast<f32x4*>(sA0)[n * 4 + grp] = a00;
   reinterpret_cast<f32x4*>(sA1)[n * 4 + grp] = a11;
@@ -780,8 +827,8 @@ __device__ __forceinline__ void state_body(char* smem, int blk, const StateArgs&
       x.pf0 = reinterpret_cast<const bf16x8*>(wr + WsRec::PF0)[lane];
       x.pf1h = reinterpret_cast<const bf16x8*>(wr + WsRec::PF1H)[lane];
       x.pf1l = reinterpret_cast<const bf16x8*>(wr + WsRec::PF1L)[lane];
-      x.ga = reinterpret_cast<const float*>(wr + WsRec::GM)[n];
-      x.gb = reinterpret_cast<const float*>(wr + WsRec::GM)[16 + n];
+      x.ga = reinterpret_cast<const float*>(wr + WsRec::GMQ)[n];
+      x.gb = reinterpret_cast<const float*>(wr + WsRec::GMQ)[16 + n];
     };
     auto pair = [&](Oin& x, int c) {
       const char* ob = obh + (c & 1) * C::OB;
@@ -887,7 +934,7 @@ static int compute_units() {
 template <int DK>
 static hipError_t launch_pair_t(const void* q, const void* k, const void* v, const float* gate,
                                 int gate_logit, float G, const float* beta, const float* h0,
-                                void* o, float* hT, int B, int T, int H, int Dv, void* ws,
+                                void* o, float* hT, int B, int T, int H, int Dv, int raw, void* ws,
                                 hipStream_t st) {
   const int NSC = (T + 31) / 32;
   const int cus = compute_units();
@@ -912,7 +959,7 @@ static hipError_t launch_pair_t(const void* q, const void* k, const void* v, con
     const int Ts = min(32 * p1, T) - 32 * p0;
     return PrepArgs{(const __bf16*)q + t0 * H * DK, (const __bf16*)k + t0 * H * DK,
                     gate + t0 * H, beta + t0 * H, wsb + (int64_t)B * H * p0 * WsRec::BYTES,
-                    gate_logit, G, B, Ts, T, H};
+                    gate_logit, G, B, Ts, T, H, raw};
   };
   auto prep_blocks = [&](int s) {
     int p0, p1;
@@ -966,14 +1013,14 @@ template <int DK>
 static hipError_t launch_varlen_t(const void* q, const void* k, const void* v, const float* gate,
                                   int gate_logit, float G, const float* beta, const float* h0,
                                   void* o, float* hT, const int* cu, int nseq, int T, int H, int Dv,
-                                  void* ws, hipStream_t st) {
+                                  int raw, void* ws, hipStream_t st) {
   const int nslot = varlen_slots(T, nseq);
   const int NV = Dv / 16;
   const int spw = (NV % 2 == 0 && (int64_t)nseq * H * NV > compute_units()) ? 2 : 1;
   const int nstate = nseq * H * (NV / spw);
   char* const wsb = static_cast<char*>(ws);
   const PrepArgs pa{(const __bf16*)q, (const __bf16*)k, gate, beta, wsb, gate_logit, G,
-                    nseq, 0, T, H, cu, nslot};
+                    nseq, 0, T, H, raw, cu, nslot};
   const int64_t pblocks = ((int64_t)H * nslot + kPrepWaves - 1) / kPrepWaves;
   hipLaunchKernelGGL((chunk_prep_kernel<DK>), dim3((unsigned)pblocks), dim3(64 * kPrepWaves), 0,
                      st, pa);
@@ -999,18 +1046,18 @@ hipError_t launch_chunk_fwd_pair_varlen(const void* q, const void* k, const void
                                         const float* gate, int gate_logit, float G,
                                         const float* beta, const float* h0, void* o, float* hT,
                                         const int* cu, int nseq, int T, int H, int Dk, int Dv,
-                                        void* ws, hipStream_t st) {
-  if (Dk == 64) return launch_varlen_t<64>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, cu, nseq, T, H, Dv, ws, st);
-  if (Dk == 128) return launch_varlen_t<128>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, cu, nseq, T, H, Dv, ws, st);
+                                        int raw, void* ws, hipStream_t st) {
+  if (Dk == 64) return launch_varlen_t<64>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, cu, nseq, T, H, Dv, raw, ws, st);
+  if (Dk == 128) return launch_varlen_t<128>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, cu, nseq, T, H, Dv, raw, ws, st);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_chunk_fwd_pair(const void* q, const void* k, const void* v, const float* gate,
                                  int gate_logit, float G, const float* beta, const float* h0,
                                  void* o, float* hT, int B, int T, int H, int Dk, int Dv,
-                                 void* ws, hipStream_t st) {
-  if (Dk == 64) return launch_pair_t<64>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, ws, st);
-  if (Dk == 128) return launch_pair_t<128>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, ws, st);
+                                 int raw, void* ws, hipStream_t st) {
+  if (Dk == 64) return launch_pair_t<64>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, raw, ws, st);
+  if (Dk == 128) return launch_pair_t<128>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, raw, ws, st);
   return hipErrorInvalidValue;
 }
 

@@ -101,6 +101,10 @@ __device__ inline float bounded_gate(float x, float G) {
   return -G * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
 }
 
+// Logistic function 1 / (1 + exp(-x)) with the same hardware exponential and
+// reciprocal as bounded_gate.
+__device__ inline float sigmoid_f(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
+
 // Lane-group (16 lanes) inclusive prefix sum; every 16-lane group scans its
 // own values independently.
 __device__ inline float scan16(float x, int n) {

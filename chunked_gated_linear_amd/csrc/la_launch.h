@@ -13,11 +13,12 @@ hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v,
                             int B, int T, int H, int Dk, int Dv, hipStream_t st);
 
 // bf16 path: intra-tile kernel into the workspace, then the inter-tile kernel;
-// the state is carried across pairs of 16-token tiles.
+// the state is carried across pairs of 16-token tiles.  raw != 0: q and k are
+// L2-normalised per token inside the pass and beta holds logits.
 hipError_t launch_chunk_fwd_pair(const void* q, const void* k, const void* v,
                                  const float* gate, int gate_logit, float G,
                                  const float* beta, const float* h0, void* o, float* hT,
-                                 int B, int T, int H, int Dk, int Dv, void* ws,
+                                 int B, int T, int H, int Dk, int Dv, int raw, void* ws,
                                  hipStream_t st);
 
 // Workspace bytes the bf16 path needs (0 when T == 0): one record per pair of
@@ -31,7 +32,7 @@ hipError_t launch_chunk_fwd_pair_varlen(const void* q, const void* k, const void
                                         const float* gate, int gate_logit, float G,
                                         const float* beta, const float* h0, void* o, float* hT,
                                         const int* cu, int nseq, int T, int H, int Dk, int Dv,
-                                        void* ws, hipStream_t st);
+                                        int raw, void* ws, hipStream_t st);
 
 // Workspace bytes of the packed-sequence path: H * (T / 32 + nseq + 1) records.
 long long chunk_pair_varlen_workspace_bytes(int T, int nseq, int H);

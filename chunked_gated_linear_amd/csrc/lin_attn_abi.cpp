@@ -110,11 +110,18 @@ long long lin_attn_chunk_fwd_workspace_size(int B, int T, int H, int Dk, int Dv,
   return chunk_workspace(B, T, H, Dk, Dv, dtype);
 }
 
-int lin_attn_chunk_fwd(const void* q, const void* k, const void* v, const float* gate,
-                       int gate_mode, float G, const float* beta, const float* h0, void* o,
-                       float* hT, int B, int T, int H, int Dk, int Dv, int dtype,
-                       void* workspace, long long workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// lin_attn_chunk_fwd (raw = 0) and lin_attn_chunk_fwd_raw (raw = 1).
+int chunk_fwd(const void* q, const void* k, const void* v, const float* gate, int gate_mode,
+              float G, const float* beta, const float* h0, void* o, float* hT, int B, int T,
+              int H, int Dk, int Dv, int dtype, void* workspace, long long workspace_bytes,
+              void* stream, int raw) {
   if (int rc = check_chunk_sizes(B, T, H, Dk, Dv, dtype)) return rc;
+  if (raw && dtype != LA_BF16)
+    return fail(LA_EUNSUPPORTED, "raw inputs are supported in LA_BF16 only");
   if (int rc = check_gate_scalars(gate_mode, G)) return rc;
   const int64_t es = dtype == LA_BF16 ? 2 : 4;
   const int64_t ntok = (int64_t)B * T * H;
@@ -166,8 +173,28 @@ int lin_attn_chunk_fwd(const void* q, const void* k, const void* v, const float*
   hipError_t e = dtype == LA_FP32
       ? la::launch_chunk_fwd(q, k, v, gate, logit, G, beta, h0, o, hT, B, T, H, Dk, Dv, st)
       : la::launch_chunk_fwd_pair(q, k, v, gate, logit, G, beta, h0, o, hT, B, T, H, Dk, Dv,
-                                  workspace, st);
+                                  raw, workspace, st);
   return hip_status(e, "chunk_fwd launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int lin_attn_chunk_fwd(const void* q, const void* k, const void* v, const float* gate,
+                       int gate_mode, float G, const float* beta, const float* h0, void* o,
+                       float* hT, int B, int T, int H, int Dk, int Dv, int dtype,
+                       void* workspace, long long workspace_bytes, void* stream) {
+  return chunk_fwd(q, k, v, gate, gate_mode, G, beta, h0, o, hT, B, T, H, Dk, Dv, dtype,
+                   workspace, workspace_bytes, stream, 0);
+}
+
+int lin_attn_chunk_fwd_raw(const void* q, const void* k, const void* v, const float* gate,
+                           int gate_mode, float G, const float* beta_logit, const float* h0,
+                           void* o, float* hT, int B, int T, int H, int Dk, int Dv, int dtype,
+                           void* workspace, long long workspace_bytes, void* stream) {
+  return chunk_fwd(q, k, v, gate, gate_mode, G, beta_logit, h0, o, hT, B, T, H, Dk, Dv, dtype,
+                   workspace, workspace_bytes, stream, 1);
 }
 
 long long lin_attn_chunk_fwd_varlen_workspace_size(int T, int nseq, int H, int Dk, int Dv,
@@ -222,7 +249,7 @@ int lin_attn_chunk_fwd_varlen(const void* q, const void* k, const void* v, const
     return fail(LA_EINVAL, "hT partially overlaps h0 (only hT == h0 is allowed)");
   hipError_t e = la::launch_chunk_fwd_pair_varlen(
       q, k, v, gate, gate_mode == LA_GATE_BOUNDED_LOGIT, G, beta, h0, o, hT, cu_seqlens, nseq, T,
-      H, Dk, Dv, workspace, reinterpret_cast<hipStream_t>(stream));
+      H, Dk, Dv, 0, workspace, reinterpret_cast<hipStream_t>(stream));
   return hip_status(e, "chunk_fwd_varlen launch");
 }
 

@@ -126,6 +126,26 @@ int lin_attn_chunk_fwd(const void* q, const void* k, const void* v,
                        void* stream);
 
 /*
+ * lin_attn_chunk_fwd_raw -- lin_attn_chunk_fwd with the input preparation
+ * fused into its intra-tile kernel: q and k are given as they come from their
+ * projections and are L2-normalised per (token, head) inside the pass, in
+ * fp32 from the given values (a zero vector stays zero), and beta_logit holds
+ * x_beta with beta = sigmoid(x_beta).  The gate is given as for
+ * lin_attn_chunk_fwd (gate_mode).  Same arguments, layouts, workspace, rules
+ * and errors otherwise; dtype LA_BF16 only (LA_FP32 returns
+ * LA_EUNSUPPORTED).  The normalisation is folded into the per-tile operators
+ * (1/|k_t| and 1/|q_t| scale rows and columns of the in-tile products and the
+ * decay factors), so q and k are read as given and never rewritten.
+ */
+int lin_attn_chunk_fwd_raw(const void* q, const void* k, const void* v,
+                           const float* gate, int gate_mode, float G,
+                           const float* beta_logit, const float* h0,
+                           void* o, float* hT,
+                           int B, int T, int H, int Dk, int Dv, int dtype,
+                           void* workspace, long long workspace_bytes,
+                           void* stream);
+
+/*
  * lin_attn_chunk_fwd_varlen_workspace_size -- bytes of device workspace that
  * lin_attn_chunk_fwd_varlen needs: H * (T / 32 + nseq + 1) * 6656 for LA_BF16
  * (one 6656-byte record slot per 32 tokens of each packed sequence, as in

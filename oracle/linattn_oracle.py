@@ -49,6 +49,8 @@ itself are in tests/test_oracle.py):
                    masked gated linear attention), invariants (identity step,
                    write-then-query, split invariance, linearity, norm bound).
   decode_step      equals recurrent_fwd applied one token at a time.
+  prepare_inputs   unit norms, directions kept (q / |q| times |q| gives q back),
+                   zero vectors kept, sigmoid values checked against closed forms.
   recurrent_fwd_varlen
                    packed sequences: a closed form at every boundary (a
                    sequence whose tokens neither write nor decay returns its own
@@ -79,6 +81,7 @@ __all__ = [
     "chunked_fwd",
     "recurrent_fwd_heads",
     "recurrent_fwd_varlen",
+    "prepare_inputs",
 ]
 
 
@@ -133,6 +136,21 @@ def recurrent_fwd(q, k, v, g, beta, h0=None):
         h = a * erased + b * kt[:, :, :, None] * vt[:, :, None, :]
         o[:, t] = np.einsum("bhk,bhkv->bhv", q[:, t], h)    # h_t^T q_t
     return o, h
+
+
+def prepare_inputs(q, k, x_beta):
+    """Input preparation of the raw-input forward pass: q and k L2-normalised
+    over their last axis (a zero vector stays zero) and beta = sigmoid(x_beta),
+    in float64.  The pages' configurations draw q and k from N(0,1) and
+    normalise them per head and token; the raw entry point does this inside the
+    pass."""
+    q, k, x_beta = map(_f64, (q, k, x_beta))
+
+    def unit(a):
+        n = np.linalg.norm(a, axis=-1, keepdims=True)
+        return np.divide(a, n, out=np.zeros_like(a), where=n > 0)
+
+    return unit(q), unit(k), sigmoid(x_beta)
 
 
 def recurrent_fwd_varlen(q, k, v, g, beta, cu_seqlens, h0=None):

@@ -236,3 +236,17 @@ def test_varlen_workspace_size_and_empty():
     assert "LA_BF16 only" in L.lin_attn_last_error().decode()
     # no sequences: nothing to do, nothing touched
     assert varlen(nseq=0, q=None, cu=None, ws=None)[0] == N.LA_OK
+
+
+def test_raw_entry_checks():
+    L = N.lib()
+    base = [fake(0), fake(1), fake(2), fake(3), 0, 5.0, fake(4), None, fake(5), fake(6),
+            1, 64, 2, 128, 128]
+    assert L.lin_attn_chunk_fwd_raw(*base, N.LA_FP32, fake(8), 1 << 30, None) == N.LA_EUNSUPPORTED
+    assert "LA_BF16 only" in L.lin_attn_last_error().decode()
+    bad = list(base)
+    bad[0] = None
+    assert L.lin_attn_chunk_fwd_raw(*bad, N.LA_BF16, fake(8), 1 << 30, None) == N.LA_EINVAL
+    assert "q must not be NULL" in L.lin_attn_last_error().decode()
+    assert L.lin_attn_chunk_fwd_raw(*base, N.LA_BF16, fake(8), 10, None) == N.LA_EINVAL
+    assert "workspace too small" in L.lin_attn_last_error().decode()

@@ -487,3 +487,22 @@ def test_varlen_rejects_bad_offsets():
         orc.recurrent_fwd_varlen(q, k, v, g, beta, [0, 5, 4], h0)
     with pytest.raises(ValueError):
         orc.recurrent_fwd_varlen(q, k, v, g, beta, [0, 3, 6], h0)
+
+
+# ------------------------------------------------------- input preparation
+def test_prepare_inputs_pins():
+    rng = np.random.default_rng(17)
+    q = rng.standard_normal((2, 5, 3, 8)) * 7.0
+    k = rng.standard_normal((2, 5, 3, 8))
+    k[0, 1, 2] = 0.0                                  # a zero key stays zero
+    xb = np.array([0.0, math.log(3.0), -math.log(3.0), 40.0, -40.0])
+    qn, kn, b = orc.prepare_inputs(q, k, xb)
+    np.testing.assert_allclose(np.linalg.norm(qn, axis=-1), 1.0, rtol=1e-14)
+    np.testing.assert_allclose(qn * np.linalg.norm(q, axis=-1, keepdims=True), q, rtol=1e-13)
+    assert np.all(kn[0, 1, 2] == 0.0)
+    mask = np.ones(k.shape[:-1], bool)
+    mask[0, 1, 2] = False
+    np.testing.assert_allclose(np.linalg.norm(kn, axis=-1)[mask], 1.0, rtol=1e-14)
+    # sigmoid(0) = 1/2, sigmoid(ln 3) = 3/4, sigmoid(-ln 3) = 1/4, saturation
+    np.testing.assert_allclose(b[:3], [0.5, 0.75, 0.25], rtol=1e-15)
+    assert b[3] == 1.0 and 0.0 < b[4] < 1e-17
