@@ -86,6 +86,7 @@ def main():
     ap.add_argument("--workload", default="long_64k")
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--varlen-steps", type=int, default=20)
+    ap.add_argument("--raw-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=65536,
                     help="tokens per head in the CPU-baseline sample")
@@ -178,6 +179,27 @@ def main():
                      "alg_flops_per_launch": flops,
                      "attainable_frac": max(byts / PEAK_HBM, flops / PEAK_BF16) / t},
     }
+
+    # ---- the same workload from raw inputs (q, k normalised and beta from
+    # logits inside the pass): what the fused input preparation costs
+    if args.raw_steps > 0 and dtype == "bf16":
+        o_raw, hT_raw = torch.empty_like(o), torch.empty_like(hT)   # o, hT stay for the parity check
+
+        def rstep():
+            lin_attn_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["x"], inp["x"], inp["h0"],
+                               gate_mode="logit", G=5.0, o=o_raw, hT=hT_raw, workspace=ws, raw=True)
+        rstep()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.raw_steps):
+            rstep()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        rms = e0.elapsed_time(e1) / args.raw_steps
+        result["raw_inputs"] = {"workload": f"{args.workload}, q and k unnormalised, beta as logits",
+                                "ms_per_call": rms, "tokens_per_s": B * T / (rms * 1e-3),
+                                "vs_prepared_call": rms / ms}
+        del o_raw, hT_raw
 
     # ---- packed prefill batch: 64 requests of mixed lengths, 64K tokens in all
     if args.varlen_steps > 0:

@@ -261,33 +261,6 @@ __device__ __forceinline__ void prep_body(char* smem, int64_t blk, const PrepArg
     qr[i] = *reinterpret_cast<const bf16x8*>(q + tok0 * DK + off);
     lofs[i] = ((r >> 4) * NS + (c16 >> 2)) * 1024 + 16 * rslot(r & 15, c16 & 3);
   }
-  {
-    // 1/|k_t| and 1/|q_t| of the pair's 32 rows (1 without raw inputs): the
-    // lanes that loaded a row reduce the squares of its elements in fp32
-    constexpr int LPR = 2 * DK / 16;             // lanes per row
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      float sk2 = 0.f, sq2 = 0.f;
-      if (pa.raw) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float a = (float)kr[i][e], aq = (float)qr[i][e];
-          sk2 += a * a;
-          sq2 += aq * aq;
-        }
-#pragma unroll
-        for (int m = LPR / 2; m >= 1; m >>= 1) {
-          sk2 += __shfl_xor(sk2, m);
-          sq2 += __shfl_xor(sq2, m);
-        }
-      }
-      if ((lane & (LPR - 1)) == 0) {
-        const int r = (64 * i + lane) * 16 / (2 * DK);
-        sNk[r] = !pa.raw ? 1.f : sk2 > 0.f ? 1.f / sqrtf(sk2) : 0.f;
-        sNq[r] = !pa.raw ? 1.f : sq2 > 0.f ? 1.f / sqrtf(sq2) : 0.f;
-      }
-    }
-  }
   bf16x8 kf[2][NS], qf[2][NS];
   const int o_frag = 16 * rslot(n, grp);
 #pragma unroll
@@ -325,17 +298,6 @@ __device__ __forceinline__ void prep_body(char* smem, int64_t blk, const PrepArg
   const float Gb = Ga15 + scan16_dpp(gbv);
   const float Gb15 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, Gb), 15));
   if (grp == 0) {
-    float* gm = reinterpret_cast<float*>(wr + WsRec::GM);
-    float* dl = reinterpret_cast<float*>(wr + WsRec::DL);
-    float* gq = reinterpret_cast<float*>(wr + WsRec::GMQ);
-    const float ea = __expf(Ga), eb = __expf(Gb);
-    gm[n] = ea * sNk[n];
-    gm[16 + n] = eb * sNk[16 + n];
-    dl[n] = __expf(Gb15 - Ga) * sNk[n];
-    dl[16 + n] = __expf(Gb15 - Gb) * sNk[16 + n];
-    gq[n] = ea * sNq[n];
-    gq[16 + n] = eb * sNq[16 + n];
-    if (n == 0) *reinterpret_cast<float*>(wr + WsRec::GC) = __expf(Gb15);
     sB[n] = ba;
     sB[16 + n] = bb;
     sG[n] = Ga;
@@ -357,7 +319,46 @@ __device__ __forceinline__ void prep_body(char* smem, int64_t blk, const PrepArg
     p11 = mma32b(kb[s], qb[s], p11);
     p10 = mma32b(ka[s], qb[s], p10);     // [n][s] = q_b,n . k_a,s
   }
+  // 1/|k_t| and 1/|q_t| (1 without raw inputs): |k|^2 is the diagonal of
+  // K K^T above, |q|^2 that of Q Q^T; lane (n, n / 4) holds entry [n][n]
+  {
+    float ika = 1.f, ikb = 1.f, iqa = 1.f, iqb = 1.f;
+    if (pa.raw) {
+      f32x4 qqa = zero4(), qqb = zero4();
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        qqa = mma32b(qa[s], qa[s], qqa);
+        qqb = mma32b(qb[s], qb[s], qqb);
+      }
+      auto inv = [](float x) { return x > 0.f ? 1.f / sqrtf(x) : 0.f; };
+      const int d = n & 3;
+      ika = inv(s00[d]);
+      ikb = inv(s11[d]);
+      iqa = inv(qqa[d]);
+      iqb = inv(qqb[d]);
+    }
+    if (grp == (n >> 2)) {
+      sNk[n] = ika;
+      sNk[16 + n] = ikb;
+      sNq[n] = iqa;
+      sNq[16 + n] = iqb;
+    }
+  }
   wave_fence();
+  if (grp == 0) {
+    float* gm = reinterpret_cast<float*>(wr + WsRec::GM);
+    float* dl = reinterpret_cast<float*>(wr + WsRec::DL);
+    float* gq = reinterpret_cast<float*>(wr + WsRec::GMQ);
+    const float ea = __expf(Ga), eb = __expf(Gb);
+    const float ika = sNk[n], ikb = sNk[16 + n];
+    gm[n] = ea * ika;
+    gm[16 + n] = eb * ikb;
+    dl[n] = __expf(Gb15 - Ga) * ika;
+    dl[16 + n] = __expf(Gb15 - Gb) * ikb;
+    gq[n] = ea * sNq[n];
+    gq[16 + n] = eb * sNq[16 + n];
+    if (n == 0) *reinterpret_cast<float*>(wr + WsRec::GC) = __expf(Gb15);
+  }
   const f32x4 Gca = reinterpret_cast<const f32x4*>(sG)[grp];       // G_a at the 4 columns
   const f32x4 Gcb = reinterpret_cast<const f32x4*>(sG)[4 + grp];   // G_b at the 4 columns
   // inverse norms: rows (token n of each tile) and the 4 columns
