@@ -299,10 +299,19 @@ def main():
         g = orc.bounded_gate(x.astype(np.float64))
         res = crec.recurrent_fwd_c(q, k, v, g, beta, h0, workers=workers)
         cpu_s = time.perf_counter() - c0
+        model = "unknown"
+        try:
+            with open("/proc/cpuinfo") as f:
+                model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")),
+                             model)
+        except OSError:
+            pass
         result["cpu_baseline"] = {
             "value": B * S_tok / cpu_s, "unit": "tokens/s", "cores": workers, "kind": "oracle",
             "sample": f"all {B * H} heads, first {S_tok} of {T} tokens (fp64 C recurrence, "
-                      f"one thread per head stream), {cpu_s:.1f} s wall"}
+                      f"one thread per head stream), {cpu_s:.1f} s wall",
+            "host": {"nproc": os.cpu_count(), "cpu_model": model,
+                     "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}}
         if S_tok == T:   # the sample is the whole workload: compare every output
             oh, hh = f(o), f(hT)
             eo = max(np.max(np.abs(oh[b, :, h] - r[0])) for (b, h), r in res.items())
