@@ -96,11 +96,12 @@ def lin_attn_chunk_fwd_varlen_workspace_size(T, nseq, H, Dk, Dv, dtype=torch.bfl
 
 def lin_attn_chunk_fwd_varlen(q, k, v, gate, beta, cu_seqlens, h0=None, *, gate_mode="log",
                               G=5.0, o=None, hT=None, output_final_state=True,
-                              workspace=None, stream=None):
+                              workspace=None, stream=None, raw=False):
     """Packed sequences: q, k [1,T,H,Dk], v [1,T,H,Dv], gate, beta [1,T,H] hold
     nseq sequences back to back, sequence s at tokens [cu[s], cu[s+1]) with
     cu_seqlens an int32 GPU tensor of nseq + 1 offsets.  Returns o [1,T,H,Dv]
-    and the final states hT [nseq,H,Dk,Dv] (None if not requested)."""
+    and the final states hT [nseq,H,Dk,Dv] (None if not requested).  raw=True:
+    q, k as they come and `beta` holding logits, as in lin_attn_chunk_fwd."""
     _need(q, "q", torch.bfloat16)
     _, T, H, Dk = q.shape
     Dv = v.shape[-1]
@@ -126,7 +127,8 @@ def lin_attn_chunk_fwd_varlen(q, k, v, gate, beta, cu_seqlens, h0=None, *, gate_
         workspace = torch.empty(nws, dtype=torch.uint8, device=q.device)
     if workspace is not None:
         _need(workspace, "workspace", torch.uint8)
-    N.check(N.lib().lin_attn_chunk_fwd_varlen(
+    fn = N.lib().lin_attn_chunk_fwd_varlen_raw if raw else N.lib().lin_attn_chunk_fwd_varlen
+    N.check(fn(
         _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _GATE[gate_mode], float(G), _ptr(beta),
         _ptr(h0), _ptr(o), _ptr(hT), _ptr(cu_seqlens), nseq, T, H, Dk, Dv, _DTYPES[q.dtype],
         _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(q, stream)))

@@ -204,11 +204,16 @@ long long lin_attn_chunk_fwd_varlen_workspace_size(int T, int nseq, int H, int D
   return la::chunk_pair_varlen_workspace_bytes(T, nseq, H);
 }
 
-int lin_attn_chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* gate,
-                              int gate_mode, float G, const float* beta, const float* h0,
-                              void* o, float* hT, const int* cu_seqlens, int nseq, int T, int H,
-                              int Dk, int Dv, int dtype, void* workspace,
-                              long long workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// lin_attn_chunk_fwd_varlen (raw = 0) and lin_attn_chunk_fwd_varlen_raw (raw = 1).
+int chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* gate,
+                     int gate_mode, float G, const float* beta, const float* h0, void* o,
+                     float* hT, const int* cu_seqlens, int nseq, int T, int H, int Dk, int Dv,
+                     int dtype, void* workspace, long long workspace_bytes, void* stream,
+                     int raw) {
   if (int rc = check_varlen_sizes(T, nseq, H, Dk, Dv, dtype)) return rc;
   if (int rc = check_gate_scalars(gate_mode, G)) return rc;
   const long long wsz = la::chunk_pair_varlen_workspace_bytes(T, nseq, H);
@@ -249,8 +254,30 @@ int lin_attn_chunk_fwd_varlen(const void* q, const void* k, const void* v, const
     return fail(LA_EINVAL, "hT partially overlaps h0 (only hT == h0 is allowed)");
   hipError_t e = la::launch_chunk_fwd_pair_varlen(
       q, k, v, gate, gate_mode == LA_GATE_BOUNDED_LOGIT, G, beta, h0, o, hT, cu_seqlens, nseq, T,
-      H, Dk, Dv, 0, workspace, reinterpret_cast<hipStream_t>(stream));
+      H, Dk, Dv, raw, workspace, reinterpret_cast<hipStream_t>(stream));
   return hip_status(e, "chunk_fwd_varlen launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int lin_attn_chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* gate,
+                              int gate_mode, float G, const float* beta, const float* h0,
+                              void* o, float* hT, const int* cu_seqlens, int nseq, int T, int H,
+                              int Dk, int Dv, int dtype, void* workspace,
+                              long long workspace_bytes, void* stream) {
+  return chunk_fwd_varlen(q, k, v, gate, gate_mode, G, beta, h0, o, hT, cu_seqlens, nseq, T, H,
+                          Dk, Dv, dtype, workspace, workspace_bytes, stream, 0);
+}
+
+int lin_attn_chunk_fwd_varlen_raw(const void* q, const void* k, const void* v, const float* gate,
+                                  int gate_mode, float G, const float* beta_logit,
+                                  const float* h0, void* o, float* hT, const int* cu_seqlens,
+                                  int nseq, int T, int H, int Dk, int Dv, int dtype,
+                                  void* workspace, long long workspace_bytes, void* stream) {
+  return chunk_fwd_varlen(q, k, v, gate, gate_mode, G, beta_logit, h0, o, hT, cu_seqlens, nseq,
+                          T, H, Dk, Dv, dtype, workspace, workspace_bytes, stream, 1);
 }
 
 int lin_attn_decode_step(const void* q, const void* k, const void* v, const float* gate,

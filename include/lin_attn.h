@@ -190,6 +190,20 @@ int lin_attn_chunk_fwd_varlen(const void* q, const void* k, const void* v,
                               void* stream);
 
 /*
+ * lin_attn_chunk_fwd_varlen_raw -- lin_attn_chunk_fwd_varlen with the input
+ * preparation of lin_attn_chunk_fwd_raw: q and k as given (L2-normalised per
+ * token and head inside the pass), beta_logit holding x_beta.  Same arguments,
+ * workspace, rules and errors otherwise.
+ */
+int lin_attn_chunk_fwd_varlen_raw(const void* q, const void* k, const void* v,
+                                  const float* gate, int gate_mode, float G,
+                                  const float* beta_logit, const float* h0,
+                                  void* o, float* hT, const int* cu_seqlens, int nseq,
+                                  int T, int H, int Dk, int Dv, int dtype,
+                                  void* workspace, long long workspace_bytes,
+                                  void* stream);
+
+/*
  * lin_attn_decode_step -- one new token per (b, h), state updated in place.
  *
  * Constant-state recurrent inference: each sequence advances its d_k x d_v

@@ -295,6 +295,28 @@ def test_raw_inputs(case):
     check(name, "bf16", o, hT, ref_o, ref_h)
 
 
+def test_varlen_raw_inputs():
+    """Packed sequences from raw inputs: against the oracle on the prepared
+    inputs."""
+    lengths = [0, 3, 40, 333, 1000]
+    H, D = 3, 128
+    T, nseq = sum(lengths), len(lengths)
+    name = f"varlen raw {nseq} seqs T{T} H{H} d{D} bf16 weak"
+    say(name)
+    dev, hst = make_case(1, T, H, D, D, "bf16", "weak", "logit", None, seed=51)
+    gen = torch.Generator(device="cuda").manual_seed(52)
+    q = (dev["q"].float() * (0.5 + 3 * torch.rand((1, T, H, 1), generator=gen, device="cuda"))).to(torch.bfloat16)
+    k = (dev["k"].float() * (0.5 + 3 * torch.rand((1, T, H, 1), generator=gen, device="cuda"))).to(torch.bfloat16)
+    xb = torch.randn((1, T, H), generator=gen, device="cuda")
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int32, device="cuda")
+    o, hT = lin_attn_chunk_fwd_varlen(q, k, dev["v"], dev["gate"], xb, cu, gate_mode="logit", raw=True)
+    torch.cuda.synchronize()
+    _, _, v_h, g_h, _, _ = hst
+    qn, kn, beta = orc.prepare_inputs(host(q), host(k), host(xb))
+    ref_o, ref_h = crec.recurrent_fwd_varlen(qn, kn, v_h, g_h, beta, cu.cpu().numpy(), None)
+    check(name, "bf16", o, hT, ref_o, ref_h)
+
+
 def test_graph_capture_replays():
     """The forward (stretched: several launches) and decode steps captured in
     one graph replay to the eager results, replay after replay, with eager
