@@ -36,13 +36,26 @@ CSRC = os.path.join(ROOT, "chunked_gated_linear_amd", "csrc")
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC_KIB = {
     "chunk": {"sources": ("chunk_pair.hip", "la_device.h", "la_launch.h"),
-              "sha256_16": "163abad635cc922a",
-              # one call: the intra-tile launch and the 8 state launches of 64K x 16 heads
-              "fetch": 774956, "write": 480278},
+              "sha256_16": "5a1521a6bbebeb66",
+              # one call: the intra-tile launch and the 16 state launches of 64K x 16 heads
+              "fetch": 776823, "write": 488454},
     "decode": {"sources": ("decode.hip", "la_device.h", "la_launch.h"),
                "sha256_16": "cbb7b3ef6c1ad4b3",
-               "fetch": 265755, "write": 526921},
+               "fetch": 265755, "write": 526841},
 }
+
+
+def host_info():
+    """CPU model, core count and OpenMP thread setting of the host."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")),
+                         model)
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "cpu_model": model,
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
 
 
 def source_hash(names):
@@ -299,19 +312,11 @@ def main():
         g = orc.bounded_gate(x.astype(np.float64))
         res = crec.recurrent_fwd_c(q, k, v, g, beta, h0, workers=workers)
         cpu_s = time.perf_counter() - c0
-        model = "unknown"
-        try:
-            with open("/proc/cpuinfo") as f:
-                model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")),
-                             model)
-        except OSError:
-            pass
         result["cpu_baseline"] = {
             "value": B * S_tok / cpu_s, "unit": "tokens/s", "cores": workers, "kind": "oracle",
             "sample": f"all {B * H} heads, first {S_tok} of {T} tokens (fp64 C recurrence, "
                       f"one thread per head stream), {cpu_s:.1f} s wall",
-            "host": {"nproc": os.cpu_count(), "cpu_model": model,
-                     "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}}
+            "host": host_info()}
         if S_tok == T:   # the sample is the whole workload: compare every output
             oh, hh = f(o), f(hT)
             eo = max(np.max(np.abs(oh[b, :, h] - r[0])) for (b, h), r in res.items())

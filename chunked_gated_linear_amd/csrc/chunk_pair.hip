@@ -925,8 +925,11 @@ constexpr int kMaxStretches = 16;
 // next stretch's records within the current stretch (they loop over the jobs),
 // few enough not to slow the state blocks down (2 per sequence-head measured
 // best at 64K x 16 heads with 16 stretches; launching one block per job slowed
-// the state blocks by ~10 %).
+// the state blocks by ~10 %).  Preparing raw q and k costs more per job (the
+// Q Q^T chains and the folded norms): 3 per head keep its records on time
+// (2 per head: 1.22 ms per call, 3: 1.13, as for prepared inputs).
 constexpr int kPrepResidentPerHead = 2;
+constexpr int kPrepResidentPerHeadRaw = 3;
 constexpr int kPrepResidentMin = 16;
 
 static bool stretch_area(int NSC) { return NSC >= kStretchAreaPairs; }
@@ -952,7 +955,8 @@ static hipError_t launch_pair_t(const void* q, const void* k, const void* v, con
   const int nstate = B * H * (NV / spw);
   int S = 1;
   if (stretch_area(NSC) && 2 * nstate <= cus) S = min(kMaxStretches, NSC / kStretchMinPairs);
-  const int resident_cap = min(cus - nstate, max(kPrepResidentMin, kPrepResidentPerHead * B * H));
+  const int per_head = raw ? kPrepResidentPerHeadRaw : kPrepResidentPerHead;
+  const int resident_cap = min(cus - nstate, max(kPrepResidentMin, per_head * B * H));
   char* const wsb = static_cast<char*>(ws);
   float* const carry = reinterpret_cast<float*>(wsb + (int64_t)B * H * NSC * WsRec::BYTES);
   auto span = [&](int s, int& p0, int& p1) {
