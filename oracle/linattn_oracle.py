@@ -59,6 +59,12 @@ itself are in tests/test_oracle.py):
                    copy agrees on mixed lengths with empty sequences.
   chunked_fwd      equals recurrent_fwd for chunk sizes 1, 3, 16 and 32 (two
                    independent formulations of the same definition).
+  recurrent_bwd    central finite differences of recurrent_fwd, element by
+                   element on tiny inputs and along random directions on larger
+                   ones; closed forms for pure decay (beta = 0) and for
+                   mutually orthogonal keys (masked gated linear attention);
+                   the zero-upstream case.
+  bounded_gate_bwd central finite differences of bounded_gate.
 Every function is pinned; none is "parity unpinned".
 
 Layouts (row-major, as the library uses them):
@@ -82,6 +88,8 @@ __all__ = [
     "recurrent_fwd_heads",
     "recurrent_fwd_varlen",
     "prepare_inputs",
+    "recurrent_bwd",
+    "bounded_gate_bwd",
 ]
 
 
@@ -182,6 +190,80 @@ def recurrent_fwd_varlen(q, k, v, g, beta, cu_seqlens, h0=None):
         elif init is not None:
             hT[s] = init[0]
     return o, hT
+
+
+def bounded_gate_bwd(x, dg, G: float = 5.0):
+    """Gradient through g = -G * sigmoid(x): dx = -G * s (1 - s) * dg."""
+    s = sigmoid(x)
+    return -float(G) * s * (1.0 - s) * _f64(dg)
+
+
+# ----------------------------------------------------------------------------
+# Reverse mode of the recurrence, for training ("Core Technologies Behind
+# Ultra-Long-Context Sparse MoE Large Models", sec. 2.3: the bounded decay is
+# chosen for BF16 training; the pages print no backward pass, so this is the
+# adjoint of recurrent_fwd, derived by hand).  With a = exp(g_t), b = beta_t,
+# c = k_t^T h_{t-1} and e = h_{t-1} - b k_t c^T (the erased old state), one
+# step is h_t = a e + b k_t v_t^T and o_t = h_t^T q_t.  Walking t from T-1 down
+# to 0 with dh = dL/dh_t (starting from dhT):
+#     dh   += q_t do_t^T                 dq_t  = h_t do_t
+#     dg_t  = a <dh, e>                  dv_t  = b dh^T k_t
+#     de    = a dh
+#     dbeta_t = k_t^T dh v_t - (k_t^T de) . c
+#     dk_t  = b dh v_t - b (de c + h_{t-1} (de^T k_t))
+#     dh_{t-1} = de - b k_t (k_t^T de)
+# and dh0 = dh after the last step.  States are kept every `seg` tokens and
+# recomputed inside a segment, which changes nothing in the arithmetic.
+# ----------------------------------------------------------------------------
+def recurrent_bwd(q, k, v, g, beta, do, dhT=None, h0=None, seg: int = 64):
+    """Gradients of L = <o, do> + <hT, dhT> with respect to every input.
+
+    Returns dq [B,T,H,Dk], dk [B,T,H,Dk], dv [B,T,H,Dv], dg [B,T,H],
+    dbeta [B,T,H], dh0 [B,H,Dk,Dv], all float64.  dhT = None means zero.
+    """
+    q, k, v, g, beta, do = map(_f64, (q, k, v, g, beta, do))
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    seg = max(1, int(seg))
+    h = np.zeros((B, H, Dk, Dv)) if h0 is None else _f64(h0).copy()
+    checkpoints = []
+    for s0 in range(0, T, seg):                 # state before each segment
+        checkpoints.append(h.copy())
+        s1 = min(T, s0 + seg)
+        _, h = recurrent_fwd(q[:, s0:s1], k[:, s0:s1], v[:, s0:s1], g[:, s0:s1],
+                             beta[:, s0:s1], h)
+    dq, dk = np.zeros_like(q), np.zeros_like(k)
+    dv = np.zeros_like(v)
+    dg, dbeta = np.zeros_like(g), np.zeros_like(beta)
+    dh = np.zeros((B, H, Dk, Dv)) if dhT is None else _f64(dhT).copy()
+    for si in range(len(checkpoints) - 1, -1, -1):
+        s0 = si * seg
+        s1 = min(T, s0 + seg)
+        states = [checkpoints[si]]              # h_{s0-1}, h_{s0}, ..., h_{s1-1}
+        for t in range(s0, s1):
+            _, hn = recurrent_fwd(q[:, t:t + 1], k[:, t:t + 1], v[:, t:t + 1], g[:, t:t + 1],
+                                  beta[:, t:t + 1], states[-1])
+            states.append(hn)
+        for t in range(s1 - 1, s0 - 1, -1):
+            h_prev, h_t = states[t - s0], states[t - s0 + 1]
+            kt, vt, qt, dot = k[:, t], v[:, t], q[:, t], do[:, t]
+            a = np.exp(g[:, t])[:, :, None, None]
+            b = beta[:, t][:, :, None, None]
+            dh = dh + qt[:, :, :, None] * dot[:, :, None, :]
+            dq[:, t] = np.einsum("bhkv,bhv->bhk", h_t, dot)
+            c = np.einsum("bhk,bhkv->bhv", kt, h_prev)
+            e = h_prev - b * kt[:, :, :, None] * c[:, :, None, :]
+            dg[:, t] = a[:, :, 0, 0] * np.einsum("bhkv,bhkv->bh", dh, e)
+            dv[:, t] = b[:, :, :, 0] * np.einsum("bhkv,bhk->bhv", dh, kt)
+            de = a * dh
+            kde = np.einsum("bhk,bhkv->bhv", kt, de)            # k_t^T de
+            dbeta[:, t] = (np.einsum("bhk,bhkv,bhv->bh", kt, dh, vt)
+                           - np.einsum("bhv,bhv->bh", kde, c))
+            dk[:, t] = b[:, :, :, 0] * (np.einsum("bhkv,bhv->bhk", dh, vt)
+                                        - np.einsum("bhkv,bhv->bhk", de, c)
+                                        - np.einsum("bhkv,bhv->bhk", h_prev, kde))
+            dh = de - b * kt[:, :, :, None] * kde[:, :, None, :]
+    return dq, dk, dv, dg, dbeta, dh
 
 
 def decode_step(q, k, v, g, beta, S):
