@@ -86,6 +86,54 @@ def lin_attn_chunk_fwd(q, k, v, gate, beta, h0=None, *, gate_mode="log", G=5.0,
     return o, hT
 
 
+def lin_attn_chunk_bwd_workspace_size(B, T, H, Dk, Dv, dtype=torch.bfloat16):
+    """Workspace bytes lin_attn_chunk_bwd needs for these sizes."""
+    n = N.lib().lin_attn_chunk_bwd_workspace_size(B, T, H, Dk, Dv, _DTYPES[dtype])
+    if n < 0:
+        raise N.LinAttnError(N.LA_EINVAL, N.lib().lin_attn_last_error().decode())
+    return n
+
+
+def lin_attn_chunk_bwd(q, k, v, gate, beta, dout, h0=None, dhT=None, *, gate_mode="log",
+                       G=5.0, output_dh0=True, workspace=None, stream=None):
+    """Gradients of <o, dout> + <hT, dhT> for lin_attn_chunk_fwd's inputs.
+
+    Returns float32 tensors (dq, dk, dv, dgate, dbeta, dh0): dgate is dL/dg in
+    "log" mode and dL/dx in "logit" mode; dh0 is None unless output_dh0."""
+    _need(q, "q")
+    if q.dtype not in _DTYPES:
+        raise TypeError("q, k, v, dout must be bfloat16 or float32")
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    _need(k, "k", q.dtype, (B, T, H, Dk))
+    _need(v, "v", q.dtype, (B, T, H, Dv))
+    _need(dout, "dout", q.dtype, (B, T, H, Dv))
+    _need(gate, "gate", torch.float32, (B, T, H))
+    _need(beta, "beta", torch.float32, (B, T, H))
+    if h0 is not None:
+        _need(h0, "h0", torch.float32, (B, H, Dk, Dv))
+    if dhT is not None:
+        _need(dhT, "dhT", torch.float32, (B, H, Dk, Dv))
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq = torch.empty((B, T, H, Dk), **f32)
+    dk = torch.empty((B, T, H, Dk), **f32)
+    dv = torch.empty((B, T, H, Dv), **f32)
+    dgate = torch.empty((B, T, H), **f32)
+    dbeta = torch.empty((B, T, H), **f32)
+    dh0 = torch.empty((B, H, Dk, Dv), **f32) if output_dh0 else None
+    nws = lin_attn_chunk_bwd_workspace_size(B, T, H, Dk, Dv, q.dtype)
+    if workspace is None and nws > 0:
+        workspace = torch.empty(nws, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8)
+    N.check(N.lib().lin_attn_chunk_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _GATE[gate_mode], float(G), _ptr(beta),
+        _ptr(h0), _ptr(dout), _ptr(dhT), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dgate),
+        _ptr(dbeta), _ptr(dh0), B, T, H, Dk, Dv, _DTYPES[q.dtype], _ptr(workspace),
+        0 if workspace is None else workspace.numel(), _stream(q, stream)))
+    return dq, dk, dv, dgate, dbeta, dh0
+
+
 def lin_attn_chunk_fwd_varlen_workspace_size(T, nseq, H, Dk, Dv, dtype=torch.bfloat16):
     """Workspace bytes lin_attn_chunk_fwd_varlen needs for these sizes."""
     n = N.lib().lin_attn_chunk_fwd_varlen_workspace_size(T, nseq, H, Dk, Dv, _DTYPES[dtype])

@@ -37,6 +37,19 @@ hipError_t launch_chunk_fwd_pair_varlen(const void* q, const void* k, const void
 // Workspace bytes of the packed-sequence path: H * (T / 32 + nseq + 1) records.
 long long chunk_pair_varlen_workspace_bytes(int T, int nseq, int H);
 
+// Reverse mode over 16-token tiles (fp32 arithmetic; q, k, v, dout bf16 or
+// fp32 as `fp32` says): gradients of q, k, v, the gate (g, or its logit when
+// gate_logit), beta and h0.  dhT and h0 may be NULL (zeros); dh0 may be NULL.
+hipError_t launch_chunk_bwd(const void* q, const void* k, const void* v, const void* dout,
+                            const float* gate, int gate_logit, float G, const float* beta,
+                            const float* h0, const float* dhT, float* dq, float* dk, float* dv,
+                            float* dgate, float* dbeta, float* dh0, int B, int T, int H, int Dk,
+                            int Dv, int fp32, void* ws, hipStream_t st);
+
+// Workspace bytes of the reverse pass: per tile and head a 3200-byte record,
+// the fp32 state at the tile start and the fp32 gradient of its end state.
+long long chunk_bwd_workspace_bytes(int B, int T, int H, int Dk, int Dv);
+
 hipError_t launch_decode(const void* q, const void* k, const void* v,
                          const float* gate, int gate_logit, float G,
                          const float* beta, float* S, void* o, int BH, int Dk,

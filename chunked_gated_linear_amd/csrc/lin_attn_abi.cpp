@@ -8,6 +8,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <string>
+#include <utility>
 
 #include "la_launch.h"
 #include "lin_attn.h"
@@ -313,6 +314,78 @@ int lin_attn_decode_step(const void* q, const void* k, const void* v, const floa
                                    S, o, (int)bh, Dk, Dv, dtype == LA_FP32,
                                    reinterpret_cast<hipStream_t>(stream));
   return hip_status(e, "decode launch");
+}
+
+long long lin_attn_chunk_bwd_workspace_size(int B, int T, int H, int Dk, int Dv, int dtype) {
+  if (check_chunk_sizes(B, T, H, Dk, Dv, dtype)) return -1;
+  if ((int64_t)B * H * ((T + 15) / 16) > INT32_MAX) {
+    fail(LA_EINVAL, "problem too large (B*H*T/16 exceeds 2^31)");
+    return -1;
+  }
+  ok();
+  return la::chunk_bwd_workspace_bytes(B, T, H, Dk, Dv);
+}
+
+int lin_attn_chunk_bwd(const void* q, const void* k, const void* v, const float* gate,
+                       int gate_mode, float G, const float* beta, const float* h0,
+                       const void* dout, const float* dhT, float* dq, float* dk, float* dv,
+                       float* dgate, float* dbeta, float* dh0, int B, int T, int H, int Dk,
+                       int Dv, int dtype, void* workspace, long long workspace_bytes,
+                       void* stream) {
+  if (int rc = check_chunk_sizes(B, T, H, Dk, Dv, dtype)) return rc;
+  if (int rc = check_gate_scalars(gate_mode, G)) return rc;
+  if ((int64_t)B * H * ((T + 15) / 16) > INT32_MAX)
+    return fail(LA_EINVAL, "problem too large (B*H*T/16 exceeds 2^31)");
+  if (B == 0 || H == 0) return ok();
+  const int64_t es = dtype == LA_BF16 ? 2 : 4;
+  const int64_t ntok = (int64_t)B * T * H;
+  const int64_t nst = (int64_t)B * H * Dk * Dv;
+  const long long wsz = T > 0 ? la::chunk_bwd_workspace_bytes(B, T, H, Dk, Dv) : 0;
+  if (T > 0) {
+    // q, k and dq, dk are read and written in 16-byte vectors of a row;
+    // everything else element-wise
+    const struct { const char* nm; const void* p; unsigned a; } req[] = {
+        {"q", q, 16u}, {"k", k, 16u}, {"v", v, (unsigned)es}, {"gate", gate, 4u},
+        {"beta", beta, 4u}, {"dout", dout, (unsigned)es}, {"dq", dq, 4u}, {"dk", dk, 4u},
+        {"dv", dv, 4u}, {"dgate", dgate, 4u}, {"dbeta", dbeta, 4u}};
+    for (const auto& r : req) {
+      if (!r.p) return fail(LA_EINVAL, "%s must not be NULL", r.nm);
+      if (!aligned(r.p, r.a)) return fail(LA_EINVAL, "%s must be %u-byte aligned", r.nm, r.a);
+    }
+    if (!workspace) return fail(LA_EINVAL, "workspace must not be NULL (%lld bytes needed)", wsz);
+    if (!aligned(workspace, 256u)) return fail(LA_EINVAL, "workspace must be 256-byte aligned");
+    if (workspace_bytes < wsz)
+      return fail(LA_EINVAL, "workspace too small: %lld bytes given, %lld needed",
+                  workspace_bytes, wsz);
+  }
+  for (const auto& r : {std::make_pair("h0", (const void*)h0), std::make_pair("dhT", (const void*)dhT),
+                        std::make_pair("dh0", (const void*)dh0)})
+    if (r.second && !aligned(r.second, 4u)) return fail(LA_EINVAL, "%s must be 4-byte aligned", r.first);
+  const int64_t tk = T > 0 ? ntok : 0;
+  const Span ins[] = {span("q", q, tk * Dk * es),      span("k", k, tk * Dk * es),
+                      span("v", v, tk * Dv * es),      span("gate", gate, tk * 4),
+                      span("beta", beta, tk * 4),      span("h0", h0, nst * 4),
+                      span("dout", dout, tk * Dv * es), span("dhT", dhT, nst * 4)};
+  const Span outs[] = {span("dq", dq, tk * Dk * 4),    span("dk", dk, tk * Dk * 4),
+                       span("dv", dv, tk * Dv * 4),    span("dgate", dgate, tk * 4),
+                       span("dbeta", dbeta, tk * 4),   span("dh0", dh0, nst * 4),
+                       span("workspace", workspace, wsz)};
+  for (size_t i = 0; i < sizeof outs / sizeof outs[0]; ++i) {
+    for (const Span& in : ins)
+      if (overlap(outs[i], in)) return fail(LA_EINVAL, "%s overlaps %s", outs[i].name, in.name);
+    for (size_t j = 0; j < i; ++j)
+      if (overlap(outs[i], outs[j]))
+        return fail(LA_EINVAL, "%s overlaps %s", outs[i].name, outs[j].name);
+  }
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (T == 0) {
+    if (!dh0) return ok();
+    return hip_status(la::launch_state_init(dhT, dh0, nst, st), "state init launch");
+  }
+  hipError_t e = la::launch_chunk_bwd(q, k, v, dout, gate, gate_mode == LA_GATE_BOUNDED_LOGIT, G,
+                                      beta, h0, dhT, dq, dk, dv, dgate, dbeta, dh0, B, T, H, Dk,
+                                      Dv, dtype == LA_FP32, workspace, st);
+  return hip_status(e, "chunk_bwd launch");
 }
 
 int lin_attn_gate(const float* x, float G, float* g, long long n, void* stream) {

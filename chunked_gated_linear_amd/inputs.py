@@ -55,6 +55,15 @@ def make_inputs(B, T, H, Dk, Dv, dtype="bf16", seed=0, device="cpu",
             "x": x.contiguous(), "beta": beta.contiguous(), "h0": h0}
 
 
+def make_upstream_grads(B, T, H, Dk, Dv, dtype="bf16", seed=0, device="cpu", dhT=True):
+    """Upstream gradients for the reverse pass: dict(dout [B,T,H,Dv] in
+    `dtype`, dhT [B,H,Dk,Dv] float32 or None), N(0,1) entries."""
+    gen = _gen(device, seed + 7919)
+    dout = _randn((B, T, H, Dv), gen, device).to(_DT[dtype]).contiguous()
+    dh = _randn((B, H, Dk, Dv), gen, device).contiguous() if dhT else None
+    return {"dout": dout, "dhT": dh}
+
+
 def make_decode_inputs(B, H, Dk, Dv, dtype="bf16", seed=0, device="cpu",
                        steps=1, S_std=0.02, gate_mu=0.0, gate_std=1.0):
     """Decode inputs for `steps` consecutive tokens: dict(q, k, v, x, beta, S).

@@ -225,6 +225,49 @@ int lin_attn_decode_step(const void* q, const void* k, const void* v,
                          void* stream);
 
 /*
+ * lin_attn_chunk_bwd_workspace_size -- device workspace bytes lin_attn_chunk_bwd
+ * needs: for every 16-token tile and head a 3,200-byte record, the float32
+ * state at the tile start and the float32 gradient of the tile's end state
+ * (B * H * ceil(T / 16) * (3200 + 8 * Dk * Dv) bytes).  -1 on invalid sizes
+ * (message in lin_attn_last_error).
+ */
+long long lin_attn_chunk_bwd_workspace_size(int B, int T, int H, int Dk, int Dv, int dtype);
+
+/*
+ * lin_attn_chunk_bwd -- reverse mode of lin_attn_chunk_fwd, for training.
+ *
+ * The pages frame the bounded decay around BF16 training ("Core Technologies
+ * ...", sec. 2.3) and give the tiled forward pass ("Deep Dive ...", sec. 3.2);
+ * they print no backward pass.  This entry point returns the gradients of
+ * L = <o, dout> + <hT, dhT> with respect to every input of the forward pass,
+ * computed over 16-token tiles in float32 (the forward states are recomputed,
+ * the state gradient is carried backwards tile by tile).
+ *
+ *   q, k, v, gate, beta, h0, gate_mode, G, sizes, dtype: as lin_attn_chunk_fwd
+ *     (q and k 16-byte aligned; h0 may be NULL = zeros)
+ *   dout  [B, T, H, Dv] dtype: upstream gradient of o
+ *   dhT   [B, H, Dk, Dv] float32 or NULL (zero): upstream gradient of hT
+ *   dq, dk [B, T, H, Dk], dv [B, T, H, Dv] float32 outputs
+ *   dgate [B, T, H] float32 output: dL/dg (LA_GATE_LOG) or dL/dx
+ *         (LA_GATE_BOUNDED_LOGIT, through g = -G * sigmoid(x))
+ *   dbeta [B, T, H] float32 output
+ *   dh0   [B, H, Dk, Dv] float32 output, or NULL (not written)
+ *   workspace >= lin_attn_chunk_bwd_workspace_size(...) bytes, 256-byte
+ *         aligned, caller-owned, clobbered.
+ * No output may overlap an input, another output or the workspace (LA_EINVAL).
+ * T = 0 writes dh0 = dhT (or zeros) and nothing else.  Deterministic: the
+ * same inputs give bitwise-identical outputs.
+ */
+int lin_attn_chunk_bwd(const void* q, const void* k, const void* v,
+                       const float* gate, int gate_mode, float G,
+                       const float* beta, const float* h0,
+                       const void* dout, const float* dhT,
+                       float* dq, float* dk, float* dv,
+                       float* dgate, float* dbeta, float* dh0,
+                       int B, int T, int H, int Dk, int Dv, int dtype,
+                       void* workspace, long long workspace_bytes, void* stream);
+
+/*
  * lin_attn_gate -- the bounded log-decay on its own: g[i] = -G * sigmoid(x[i])
  * for i < n ("Deep Dive ...", sec. 3.3; "Core Technologies ...", sec. 2.2).
  * x and g are float32 device arrays of n elements (g may equal x for an

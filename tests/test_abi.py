@@ -250,3 +250,55 @@ def test_raw_entry_checks():
     assert "q must not be NULL" in L.lin_attn_last_error().decode()
     assert L.lin_attn_chunk_fwd_raw(*base, N.LA_BF16, fake(8), 10, None) == N.LA_EINVAL
     assert "workspace too small" in L.lin_attn_last_error().decode()
+
+
+def bwd(**kw):
+    a = dict(q=fake(0), k=fake(1), v=fake(2), gate=fake(3), gate_mode=0, G=5.0,
+             beta=fake(4), h0=None, dout=fake(5), dhT=None, dq=fake(6), dk=fake(7),
+             dv=fake(8), dgate=fake(9), dbeta=fake(10), dh0=fake(11), B=1, T=64, H=2,
+             Dk=128, Dv=128, dtype=0, ws=fake(12), ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    L = N.lib()
+    rc = L.lin_attn_chunk_bwd(a["q"], a["k"], a["v"], a["gate"], a["gate_mode"], a["G"],
+                              a["beta"], a["h0"], a["dout"], a["dhT"], a["dq"], a["dk"],
+                              a["dv"], a["dgate"], a["dbeta"], a["dh0"], a["B"], a["T"],
+                              a["H"], a["Dk"], a["Dv"], a["dtype"], a["ws"], a["ws_bytes"],
+                              a["stream"])
+    return rc, L.lin_attn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(dout=None), N.LA_EINVAL, "dout must not be NULL"),
+    (dict(dq=None), N.LA_EINVAL, "dq must not be NULL"),
+    (dict(dgate=None), N.LA_EINVAL, "dgate must not be NULL"),
+    (dict(dbeta=None), N.LA_EINVAL, "dbeta must not be NULL"),
+    (dict(q=fake(0) + 8), N.LA_EINVAL, "q must be 16-byte aligned"),
+    (dict(dv=fake(8) + 2), N.LA_EINVAL, "dv must be 4-byte aligned"),
+    (dict(dh0=fake(11) + 2), N.LA_EINVAL, "dh0 must be 4-byte aligned"),
+    (dict(gate_mode=3), N.LA_EINVAL, "gate_mode"),
+    (dict(Dk=32), N.LA_EUNSUPPORTED, "Dk"),
+    (dict(ws=None), N.LA_EINVAL, "workspace must not be NULL"),
+    (dict(ws_bytes=100), N.LA_EINVAL, "workspace too small"),
+    (dict(dq=fake(0) + 64), N.LA_EINVAL, "dq overlaps q"),
+    (dict(dk=fake(6) + 4096), N.LA_EINVAL, "dk overlaps dq"),
+    (dict(dh0=fake(1)), N.LA_EINVAL, "dh0 overlaps k"),
+    (dict(ws=fake(9)), N.LA_EINVAL, "workspace overlaps dgate"),
+    (dict(dhT=fake(11)), N.LA_EINVAL, "dh0 overlaps dhT"),
+])
+def test_chunk_bwd_rejects(kw, code, needle):
+    rc, msg = bwd(**kw)
+    assert rc == code, (rc, msg)
+    assert needle in msg
+
+
+def test_chunk_bwd_workspace_size_and_empty():
+    L = N.lib()
+    ws = L.lin_attn_chunk_bwd_workspace_size
+    # per 16-token tile and head: a 3200-byte record and two fp32 states
+    assert ws(1, 64, 2, 128, 128, N.LA_BF16) == 2 * 4 * (3200 + 8 * 128 * 128)
+    assert ws(2, 17, 3, 64, 32, N.LA_FP32) == 2 * 3 * 2 * (3200 + 8 * 64 * 32)
+    assert ws(1, 0, 2, 128, 128, N.LA_BF16) == 0
+    assert ws(1, 64, 2, 96, 128, N.LA_BF16) == -1
+    for kw in (dict(B=0), dict(H=0)):
+        rc, msg = bwd(q=None, k=None, v=None, dout=None, dq=None, **kw)
+        assert rc == N.LA_OK, msg

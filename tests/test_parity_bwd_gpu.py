@@ -1,0 +1,123 @@
+"""GPU parity of the reverse pass (lin_attn_chunk_bwd through the C ABI)
+against the oracle's fp64 adjoint of the recurrence.
+
+Small cases compare every gradient element; the 64K x 16-head shape compares
+the last three tiles of every head (their gradients depend only on the tokens
+after them and on dhT, so the oracle runs from the state the fp64 forward
+recurrence reaches there).  The reverse pass computes in float32 from the
+exact input values (bf16 inputs convert to float32 exactly), so both input
+dtypes are held to the float32 bar of the forward pass: max|x - ref| /
+max|ref| <= 1e-5 per gradient tensor.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from chunked_gated_linear_amd import lin_attn_chunk_bwd
+from chunked_gated_linear_amd import inputs as I
+from oracle import c_recurrent as crec
+from oracle import linattn_oracle as orc
+
+from parity_util import host, make_case, relerr, say
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+TOL_BWD = 1e-5
+NAMES = ("dq", "dk", "dv", "dgate", "dbeta", "dh0")
+
+
+def run_bwd(a, up, out_dh0=True):
+    res = lin_attn_chunk_bwd(a["q"], a["k"], a["v"], a["gate"], a["beta"], up["dout"], a["h0"],
+                             up["dhT"], gate_mode=a["gate_mode"], G=5.0, output_dh0=out_dh0)
+    torch.cuda.synchronize()
+    return res
+
+
+def oracle_grads(host_args, dev_args, up, t_range=None, h_start=None):
+    q, k, v, g, beta, h0 = host_args
+    do = host(up["dout"]).astype(np.float64)
+    dhT = None if up["dhT"] is None else host(up["dhT"]).astype(np.float64)
+    sl = slice(None) if t_range is None else slice(*t_range)
+    init = h0 if t_range is None else h_start
+    dq, dk, dv, dg, db, dh0 = orc.recurrent_bwd(q[:, sl], k[:, sl], v[:, sl], g[:, sl],
+                                                beta[:, sl], do[:, sl], dhT, init)
+    if dev_args["gate_mode"] == "logit":
+        dg = orc.bounded_gate_bwd(host(dev_args["gate"]).astype(np.float64)[:, sl], dg)
+    return dq, dk, dv, dg, db, dh0
+
+
+CASES = [
+    # dtype, Dk, Dv, B, H, T, regime, mode, h0_std, dhT
+    ("fp32", 64, 32, 1, 2, 37, "std", "log", 0.02, True),
+    ("fp32", 128, 128, 1, 2, 100, "weak", "logit", 0.02, True),
+    ("bf16", 128, 128, 2, 2, 16 * 9 + 5, "std", "logit", None, False),
+    ("bf16", 128, 128, 1, 2, 300, "weak", "logit", 0.02, True),
+    ("bf16", 128, 128, 1, 2, 200, "stress_plus", "logit", 0.02, True),
+    ("bf16", 128, 128, 1, 2, 200, "stress_minus", "logit", 0.02, True),
+    ("bf16", 128, 64, 1, 2, 64, "zero", "log", 0.02, True),
+    ("bf16", 64, 48, 1, 3, 50, "min", "log", None, True),
+    ("bf16", 128, 128, 1, 1, 1, "std", "logit", 0.02, True),
+    ("bf16", 128, 128, 1, 2, 16, "std", "logit", 0.02, True),
+    ("bf16", 128, 256, 1, 1, 40, "weak", "logit", 0.02, True),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
+def test_bwd_parity(case):
+    dtype, Dk, Dv, B, H, T, regime, mode, h0_std, with_dhT = case
+    say(f"bwd parity {case}")
+    dev_args, host_args = make_case(B, T, H, Dk, Dv, dtype, regime, mode, h0_std=h0_std, seed=T)
+    up = I.make_upstream_grads(B, T, H, Dk, Dv, dtype=dtype, seed=T, device="cuda", dhT=with_dhT)
+    got = run_bwd(dev_args, up)
+    ref = oracle_grads(host_args, dev_args, up)
+    errs = {}
+    for name, x, r in zip(NAMES, got, ref):
+        xh = host(x)
+        assert np.all(np.isfinite(xh)), name
+        errs[name] = relerr(xh, r)
+    say("  " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+    for name, e in errs.items():
+        assert e <= TOL_BWD, f"{name}: error {e}"
+
+
+def test_bwd_empty_sequence_copies_dhT():
+    say("bwd T=0")
+    dev_args, _ = make_case(1, 0, 2, 128, 64, "bf16", "std", "logit", h0_std=0.02, seed=3)
+    up = I.make_upstream_grads(1, 0, 2, 128, 64, dtype="bf16", seed=3, device="cuda")
+    dq, dk, dv, dg, db, dh0 = run_bwd(dev_args, up)
+    assert dq.numel() == 0 and dg.numel() == 0
+    assert torch.equal(dh0, up["dhT"])
+
+
+def test_bwd_is_deterministic_and_dh0_optional():
+    say("bwd determinism")
+    dev_args, _ = make_case(1, 133, 2, 128, 128, "bf16", "weak", "logit", h0_std=0.02, seed=5)
+    up = I.make_upstream_grads(1, 133, 2, 128, 128, dtype="bf16", seed=5, device="cuda")
+    a = run_bwd(dev_args, up)
+    b = run_bwd(dev_args, up, out_dh0=False)
+    for x, y in zip(a[:5], b[:5]):
+        assert torch.equal(x, y)
+    assert b[5] is None
+
+
+def test_bwd_long_64k_tail_tiles():
+    # the 64K x 16-head shape: every gradient finite, and the last 3 tiles of
+    # every head against the oracle started from the fp64 state at T - 48
+    B, T, H, D = 1, 65536, 16, 128
+    say("bwd long_64k")
+    dev_args, host_args = make_case(B, T, H, D, D, "bf16", "std", "logit", seed=1002)
+    up = I.make_upstream_grads(B, T, H, D, D, dtype="bf16", seed=1002, device="cuda")
+    got = run_bwd(dev_args, up)
+    for name, x in zip(NAMES, got):
+        assert bool(torch.isfinite(x).all()), name
+    t0 = T - 48
+    q, k, v, g, beta, _ = host_args
+    _, h_start = crec.recurrent_fwd(q[:, :t0], k[:, :t0], v[:, :t0], g[:, :t0], beta[:, :t0],
+                                    None, workers=16)
+    ref = oracle_grads(host_args, dev_args, up, t_range=(t0, T), h_start=h_start)
+    for name, x, r in zip(NAMES[:5], got[:5], ref[:5]):
+        e = relerr(host(x[:, t0:]), r)
+        say(f"  {name} tail err={e:.2e}")
+        assert e <= TOL_BWD, f"{name}: error {e}"
