@@ -35,12 +35,12 @@ CSRC = os.path.join(ROOT, "chunked_gated_linear_amd", "csrc")
 # of WRITE_SIZE, so reads are scaled by 2 and writes by 1.
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC_KIB = {
-    "chunk": {"sources": ("chunk_pair.hip", "la_device.h", "la_launch.h"),
-              "sha256_16": "5a1521a6bbebeb66",
+    "chunk": {"sources": ("chunk_pair.hip", "la_device.h"),
+              "sha256_16": "a3eacd17eeebd0cb",
               # one call: the intra-tile launch and the 16 state launches of 64K x 16 heads
               "fetch": 776823, "write": 488454},
-    "decode": {"sources": ("decode.hip", "la_device.h", "la_launch.h"),
-               "sha256_16": "cbb7b3ef6c1ad4b3",
+    "decode": {"sources": ("decode.hip", "la_device.h"),
+               "sha256_16": "07feb0a03453c841",
                "fetch": 265755, "write": 526841},
 }
 
@@ -100,6 +100,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--varlen-steps", type=int, default=20)
     ap.add_argument("--raw-steps", type=int, default=10)
+    ap.add_argument("--bwd-steps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=65536,
                     help="tokens per head in the CPU-baseline sample")
@@ -252,6 +253,47 @@ def main():
                          "kernel": "chunk_prep_kernel + chunk_state_kernel (packed sequences)"},
         }
         del vin, ov, hv, wsv
+
+    # ---- reverse pass at the training shape (B=4, H=16, T=8192, d=128): the
+    # gradients of every input for an upstream dout and dhT
+    if args.bwd_steps > 0:
+        from chunked_gated_linear_amd import lin_attn_chunk_bwd, lin_attn_chunk_bwd_workspace_size
+        bw = I.WORKLOADS["train_8k"]
+        bB, bH, bT, bK, bV = bw["B"], bw["H"], bw["T"], bw["Dk"], bw["Dv"]
+        bin_ = I.make_inputs(bB, bT, bH, bK, bV, dtype=bw["dtype"], seed=1001, device=dev)
+        up = I.make_upstream_grads(bB, bT, bH, bK, bV, dtype=bw["dtype"], seed=1001, device=dev)
+        wsb = torch.empty(lin_attn_chunk_bwd_workspace_size(bB, bT, bH, bK, bV),
+                          dtype=torch.uint8, device=dev)
+
+        def bstep():
+            return lin_attn_chunk_bwd(bin_["q"], bin_["k"], bin_["v"], bin_["x"], bin_["beta"],
+                                      up["dout"], None, up["dhT"], gate_mode="logit", G=5.0,
+                                      workspace=wsb)
+
+        for _ in range(2):
+            bstep()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.bwd_steps):
+            bstep()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        bms = e0.elapsed_time(e1) / args.bwd_steps
+        # inputs q, k, v, dout (bf16), x, beta; outputs dq, dk, dv (fp32),
+        # dgate, dbeta; per head dhT in and dh0 out (fp32)
+        per_tok = 2 * (2 * bK + 2 * bV) + 8 + 4 * (2 * bK + bV) + 8
+        bbytes = bB * bT * bH * per_tok + 2 * bB * bH * bK * bV * 4
+        result["backward"] = {
+            "workload": (f"train_8k B={bB} H={bH} T={bT} d={bK} bf16 inputs, fp32 gradients, "
+                         "dout and dhT ~ N(0,1)"),
+            "ms_per_call": bms, "tokens_per_s": bB * bT / (bms * 1e-3),
+            "roofline": {"bound": "hbm", "achieved": bbytes / (bms * 1e-3) / 1e9,
+                         "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                         "frac": bbytes / (bms * 1e-3) / PEAK_HBM, "alg_bytes_per_launch": bbytes,
+                         "kernel": ("bwd_prep_kernel + bwd_hstates_kernel + bwd_dh_kernel + "
+                                    "bwd_grad_kernel (one lin_attn_chunk_bwd call)")},
+        }
+        del bin_, up, wsb
 
     # ---- optional calibration copy (reads and writes exactly copy_mib MiB)
     if args.copy_mib > 0:
