@@ -65,6 +65,18 @@ itself are in tests/test_oracle.py):
                    mutually orthogonal keys (masked gated linear attention);
                    the zero-upstream case.
   bounded_gate_bwd central finite differences of bounded_gate.
+  recurrent_fwd_channel
+                   per-channel gate: equals recurrent_fwd when every channel
+                   has the same g; closed forms for pure decay (beta = 0) and
+                   for keys of disjoint support (masked gated linear attention
+                   with a per-channel decay); write-then-query returns v
+                   exactly under any per-channel decay (this fixes the order
+                   decay -> erase -> write); a pure-Python brute force in the
+                   S orientation; planted mistakes (decay on the value axis,
+                   erase before decay, decayed write, reversed channels) fail.
+  chunked_fwd_channel
+                   equals recurrent_fwd_channel for chunk sizes 1, 3, 16; its
+                   in-tile reciprocals stay finite at the bound.
 Every function is pinned; none is "parity unpinned".
 
 Layouts (row-major, as the library uses them):
@@ -90,6 +102,8 @@ __all__ = [
     "prepare_inputs",
     "recurrent_bwd",
     "bounded_gate_bwd",
+    "recurrent_fwd_channel",
+    "chunked_fwd_channel",
 ]
 
 
@@ -374,3 +388,83 @@ def recurrent_fwd_heads(q, k, v, g, beta, h0=None, heads=None, t_range=None,
     finally:
         _POOL_DATA = None
     return {(b, h): r for (b, h, _, _), r in zip(jobs, res)}
+
+
+# ----------------------------------------------------------------------------
+# Per-channel gate.  The pages call the decay "per-token decay factors"
+# ([CT] 2.1) and bound the log-decay elementwise ([DD] 3.3, [TS] 3.2); with one
+# log-decay per key channel, g_t in [-G, 0]^{d_k}, the scalar exp(g_t) acting
+# on S_{t-1} becomes the diagonal matrix D_t = diag(exp(g_t)) on the key side
+# of S_{t-1}:
+#     S_t = S_{t-1} D_t (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+# i.e. in the h = S^T orientation, with d_t = D_t h_{t-1} (row c of h_{t-1}
+# scaled by exp(g_t[c])):
+#     h_t = d_t - beta_t k_t (k_t^T d_t) + beta_t k_t v_t^T,   o_t = h_t^T q_t.
+# The decay acts first, the delta-rule erase and write then act on the decayed
+# state; with all channels equal this is recurrent_fwd.
+# ----------------------------------------------------------------------------
+def recurrent_fwd_channel(q, k, v, g, beta, h0=None):
+    """Gated delta rule with one log-decay per key channel, token by token.
+
+    g is [B, T, H, Dk]; everything else as recurrent_fwd.  Returns
+    (o [B,T,H,Dv], hT [B,H,Dk,Dv]) in float64.
+    """
+    q, k, v, g, beta = map(_f64, (q, k, v, g, beta))
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    h = np.zeros((B, H, Dk, Dv)) if h0 is None else _f64(h0).copy()
+    o = np.empty((B, T, H, Dv))
+    for t in range(T):
+        kt = k[:, t]
+        vt = v[:, t]
+        b = beta[:, t][:, :, None, None]
+        d = np.exp(g[:, t])[:, :, :, None] * h                   # D_t h_{t-1}
+        kd = np.einsum("bhk,bhkv->bhv", kt, d)                  # k_t^T d_t
+        h = d - b * kt[:, :, :, None] * kd[:, :, None, :] + b * kt[:, :, :, None] * vt[:, :, None, :]
+        o[:, t] = np.einsum("bhk,bhkv->bhv", q[:, t], h)
+    return o, h
+
+
+# Chunked form of the per-channel recurrence, as the pages organise it: inside
+# a 16-token tile the per-channel cumulative decay Gam_t = exp(G_t) (G_t the
+# in-tile running sum of g_t, a vector) no longer factors out of the dot
+# products, so the tile products take the decay into their operands -- queries
+# and keys scaled by Gam_t, keys divided by Gam_s -- and the reciprocal 1/Gam_s
+# appears ([CT] 2.1 and 2.3, [TS] 3.1 and 3.2: the bounded gate keeps it at most
+# exp(16 G) = exp(80) in a 16-token tile, inside the float range).  Derived
+# from the recurrence: with H the state entering the tile and
+# u_t = beta_t (v_t - d_t^T k_t),
+#     (I + A) U = diag(beta) (V - (K o Gam) H),
+#     A[t, s] = beta_t (k_t o Gam_t) . (k_s / Gam_s)   (s < t),
+#     O       = (Q o Gam) H + P U,   P[t, s] = (q_t o Gam_t) . (k_s / Gam_s)  (s <= t),
+#     H_next  = diag(Gam_C) H + (K o (Gam_C / Gam))^T U.
+def chunked_fwd_channel(q, k, v, g, beta, h0=None, chunk: int = 16):
+    """Same result as recurrent_fwd_channel, tile by tile in fp64."""
+    q, k, v, g, beta = map(_f64, (q, k, v, g, beta))
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    C = int(chunk)
+    qh, kh, vh, gh = (np.moveaxis(a, 2, 1) for a in (q, k, v, g))   # (B,H,T,.)
+    bh = np.moveaxis(beta, 2, 1)
+    Hs = np.zeros((B, H, Dk, Dv)) if h0 is None else _f64(h0).copy()
+    o = np.empty((B, H, T, Dv))
+    for c0 in range(0, T, C):
+        c1 = min(T, c0 + C)
+        n = c1 - c0
+        Q, K, V = qh[:, :, c0:c1], kh[:, :, c0:c1], vh[:, :, c0:c1]
+        beta_c = bh[:, :, c0:c1]
+        Gc = np.cumsum(gh[:, :, c0:c1], axis=2)                   # (B,H,n,Dk)
+        gam = np.exp(Gc)
+        inv = np.exp(-Gc)                                          # 1 / Gam_s
+        Kg, Qg, Ki = K * gam, Q * gam, K * inv
+        lower_strict = np.tril(np.ones((n, n)), -1)
+        lower_incl = np.tril(np.ones((n, n)), 0)
+        A = beta_c[..., :, None] * (Kg @ np.swapaxes(Ki, -1, -2)) * lower_strict
+        P = (Qg @ np.swapaxes(Ki, -1, -2)) * lower_incl
+        rhs = beta_c[..., None] * (V - Kg @ Hs)
+        U = np.linalg.solve(np.eye(n) + A, rhs)
+        o[:, :, c0:c1] = Qg @ Hs + P @ U
+        gC = gam[:, :, -1]                                         # (B,H,Dk)
+        Kd = K * (gC[:, :, None, :] * inv)
+        Hs = gC[..., None] * Hs + np.swapaxes(Kd, -1, -2) @ U
+    return np.moveaxis(o, 1, 2), Hs
