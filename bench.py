@@ -101,6 +101,7 @@ def main():
     ap.add_argument("--varlen-steps", type=int, default=20)
     ap.add_argument("--raw-steps", type=int, default=10)
     ap.add_argument("--bwd-steps", type=int, default=5)
+    ap.add_argument("--channel-steps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=65536,
                     help="tokens per head in the CPU-baseline sample")
@@ -253,6 +254,38 @@ def main():
                          "kernel": "chunk_prep_kernel + chunk_state_kernel (packed sequences)"},
         }
         del vin, ov, hv, wsv
+
+    # ---- per-channel gate: the headline shape with one log-decay per key
+    # channel (gate logits [B,T,H,Dk] ~ N(0,1))
+    if args.channel_steps > 0 and dtype == "bf16":
+        from chunked_gated_linear_amd import lin_attn_chunk_fwd_channel
+        xc = I.make_channel_gate(B, T, H, Dk, seed=1002, device=dev)
+        oc, hc = torch.empty_like(o), torch.empty_like(hT)
+
+        def cstep():
+            lin_attn_chunk_fwd_channel(inp["q"], inp["k"], inp["v"], xc, inp["beta"], inp["h0"],
+                                       gate_mode="logit", G=5.0, o=oc, hT=hc)
+
+        cstep()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.channel_steps):
+            cstep()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cms = e0.elapsed_time(e1) / args.channel_steps
+        # q, k, v, o in bf16, gate logits fp32 per channel, beta; hT (and h0) per head
+        cbytes = B * T * H * (2 * (2 * Dk + Dv) + 2 * Dv + 4 * Dk + 4) \
+            + B * H * Dk * Dv * 4 * (2 if h0_std is not None else 1)
+        result["channel_gate"] = {
+            "workload": f"{args.workload} with a per-channel gate (x [B,T,H,Dk] ~ N(0,1), G=5)",
+            "ms_per_call": cms, "tokens_per_s": B * T / (cms * 1e-3),
+            "roofline": {"bound": "hbm", "achieved": cbytes / (cms * 1e-3) / 1e9,
+                         "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                         "frac": cbytes / (cms * 1e-3) / PEAK_HBM, "alg_bytes_per_launch": cbytes,
+                         "kernel": "chunk_fwd_channel_kernel"},
+        }
+        del xc, oc, hc
 
     # ---- reverse pass at the training shape (B=4, H=16, T=8192, d=128): the
     # gradients of every input for an upstream dout and dhT

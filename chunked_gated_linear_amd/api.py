@@ -86,6 +86,34 @@ def lin_attn_chunk_fwd(q, k, v, gate, beta, h0=None, *, gate_mode="log", G=5.0,
     return o, hT
 
 
+def lin_attn_chunk_fwd_channel(q, k, v, gate, beta, h0=None, *, gate_mode="log", G=5.0,
+                               o=None, hT=None, output_final_state=True, stream=None):
+    """lin_attn_chunk_fwd with one log-decay per key channel: gate [B,T,H,Dk]
+    float32.  Returns o [B,T,H,Dv] and hT [B,H,Dk,Dv] (None if not requested)."""
+    _need(q, "q")
+    if q.dtype not in _DTYPES:
+        raise TypeError("q, k, v must be bfloat16 or float32")
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    _need(k, "k", q.dtype, (B, T, H, Dk))
+    _need(v, "v", q.dtype, (B, T, H, Dv))
+    _need(gate, "gate", torch.float32, (B, T, H, Dk))
+    _need(beta, "beta", torch.float32, (B, T, H))
+    if h0 is not None:
+        _need(h0, "h0", torch.float32, (B, H, Dk, Dv))
+    if o is None:
+        o = torch.empty((B, T, H, Dv), dtype=q.dtype, device=q.device)
+    _need(o, "o", q.dtype, (B, T, H, Dv))
+    if hT is None and output_final_state:
+        hT = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    if hT is not None:
+        _need(hT, "hT", torch.float32, (B, H, Dk, Dv))
+    N.check(N.lib().lin_attn_chunk_fwd_channel(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _GATE[gate_mode], float(G), _ptr(beta),
+        _ptr(h0), _ptr(o), _ptr(hT), B, T, H, Dk, Dv, _DTYPES[q.dtype], _stream(q, stream)))
+    return o, hT
+
+
 def lin_attn_chunk_bwd_workspace_size(B, T, H, Dk, Dv, dtype=torch.bfloat16):
     """Workspace bytes lin_attn_chunk_bwd needs for these sizes."""
     n = N.lib().lin_attn_chunk_bwd_workspace_size(B, T, H, Dk, Dv, _DTYPES[dtype])

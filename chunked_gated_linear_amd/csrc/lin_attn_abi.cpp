@@ -119,22 +119,28 @@ namespace {
 int chunk_fwd(const void* q, const void* k, const void* v, const float* gate, int gate_mode,
               float G, const float* beta, const float* h0, void* o, float* hT, int B, int T,
               int H, int Dk, int Dv, int dtype, void* workspace, long long workspace_bytes,
-              void* stream, int raw) {
+              void* stream, int raw, int channel = 0) {
   if (int rc = check_chunk_sizes(B, T, H, Dk, Dv, dtype)) return rc;
   if (raw && dtype != LA_BF16)
     return fail(LA_EUNSUPPORTED, "raw inputs are supported in LA_BF16 only");
   if (int rc = check_gate_scalars(gate_mode, G)) return rc;
+  // per-channel gate: the in-tile operands reach exp(+-8 G); G <= 10 keeps
+  // them at most exp(80), inside the float range
+  if (channel && G > 10.f)
+    return fail(LA_ERANGE, "G must be in [0, 10] for a per-channel gate, got %g", (double)G);
   const int64_t es = dtype == LA_BF16 ? 2 : 4;
   const int64_t ntok = (int64_t)B * T * H;
   const int64_t nst = (int64_t)B * H * Dk * Dv;
   if (B == 0 || H == 0) return ok();
   const unsigned ea = dtype == LA_BF16 ? 2u : 4u;
-  const long long wsz = T > 0 ? chunk_workspace(B, T, H, Dk, Dv, dtype) : 0;
+  const long long wsz = T > 0 && !channel ? chunk_workspace(B, T, H, Dk, Dv, dtype) : 0;
+  const int64_t ngate = channel ? ntok * Dk : ntok;   // gate elements
   if (T > 0) {
     // q, k and v are read as 16-byte vectors, bf16 o written as 8-byte vectors;
     // gate and beta element-wise
     const struct { const char* nm; const void* p; unsigned a; } req[] = {
-        {"q", q, 16u}, {"k", k, 16u}, {"v", v, 16u}, {"gate", gate, 4u}, {"beta", beta, 4u},
+        {"q", q, 16u}, {"k", k, 16u}, {"v", v, 16u}, {"gate", gate, channel ? 16u : 4u},
+        {"beta", beta, 4u},
         {"o", o, dtype == LA_BF16 ? 8u : ea}};
     for (const auto& r : req) {
       if (!r.p) return fail(LA_EINVAL, "%s must not be NULL", r.nm);
@@ -152,7 +158,7 @@ int chunk_fwd(const void* q, const void* k, const void* v, const float* gate, in
   }
 
   const Span sq = span("q", q, ntok * Dk * es), sk = span("k", k, ntok * Dk * es),
-             sv = span("v", v, ntok * Dv * es), sg = span("gate", gate, ntok * 4),
+             sv = span("v", v, ntok * Dv * es), sg = span("gate", gate, ngate * 4),
              sb = span("beta", beta, ntok * 4), sh0 = span("h0", h0, nst * 4),
              so = span("o", o, T > 0 ? ntok * Dv * es : 0), shT = span("hT", hT, nst * 4);
   for (const Span& in : {sq, sk, sv, sg, sb, sh0, shT})
@@ -171,6 +177,10 @@ int chunk_fwd(const void* q, const void* k, const void* v, const float* gate, in
     return hip_status(la::launch_state_init(h0, hT, nst, st), "state init launch");
   }
   const int logit = gate_mode == LA_GATE_BOUNDED_LOGIT;
+  if (channel)
+    return hip_status(la::launch_chunk_fwd_channel(q, k, v, gate, logit, G, beta, h0, o, hT, B,
+                                                   T, H, Dk, Dv, dtype == LA_FP32, st),
+                      "chunk_fwd_channel launch");
   hipError_t e = dtype == LA_FP32
       ? la::launch_chunk_fwd(q, k, v, gate, logit, G, beta, h0, o, hT, B, T, H, Dk, Dv, st)
       : la::launch_chunk_fwd_pair(q, k, v, gate, logit, G, beta, h0, o, hT, B, T, H, Dk, Dv,
@@ -188,6 +198,14 @@ int lin_attn_chunk_fwd(const void* q, const void* k, const void* v, const float*
                        void* workspace, long long workspace_bytes, void* stream) {
   return chunk_fwd(q, k, v, gate, gate_mode, G, beta, h0, o, hT, B, T, H, Dk, Dv, dtype,
                    workspace, workspace_bytes, stream, 0);
+}
+
+int lin_attn_chunk_fwd_channel(const void* q, const void* k, const void* v, const float* gate,
+                               int gate_mode, float G, const float* beta, const float* h0,
+                               void* o, float* hT, int B, int T, int H, int Dk, int Dv,
+                               int dtype, void* stream) {
+  return chunk_fwd(q, k, v, gate, gate_mode, G, beta, h0, o, hT, B, T, H, Dk, Dv, dtype,
+                   nullptr, 0, stream, 0, 1);
 }
 
 int lin_attn_chunk_fwd_raw(const void* q, const void* k, const void* v, const float* gate,

@@ -55,6 +55,14 @@ def make_inputs(B, T, H, Dk, Dv, dtype="bf16", seed=0, device="cpu",
             "x": x.contiguous(), "beta": beta.contiguous(), "h0": h0}
 
 
+def make_channel_gate(B, T, H, Dk, seed=0, device="cpu", mu=0.0, std=1.0):
+    """Per-channel gate logits x [B,T,H,Dk] float32, x = mu + std * N(0, 1), from
+    their own generator stream (seed + 104729), so the other inputs of the same
+    seed are unchanged."""
+    gen = _gen(device, seed + 104729)
+    return (mu + std * _randn((B, T, H, Dk), gen, device)).contiguous()
+
+
 def make_upstream_grads(B, T, H, Dk, Dv, dtype="bf16", seed=0, device="cpu", dhT=True):
     """Upstream gradients for the reverse pass: dict(dout [B,T,H,Dv] in
     `dtype`, dhT [B,H,Dk,Dv] float32 or None), N(0,1) entries."""

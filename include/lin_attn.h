@@ -146,6 +146,32 @@ int lin_attn_chunk_fwd_raw(const void* q, const void* k, const void* v,
                            void* stream);
 
 /*
+ * lin_attn_chunk_fwd_channel -- lin_attn_chunk_fwd with one log-decay per key
+ * channel: gate is [B, T, H, Dk] float32 (16-byte aligned), g_t[c] in [-G, 0]
+ * (LA_GATE_LOG) or g_t[c] = -G * sigmoid(x_t[c]) (LA_GATE_BOUNDED_LOGIT).
+ *
+ * The pages call the decay "per-token decay factors" and bound the log-decay
+ * elementwise so that, inside a 16-token tile, the reciprocal of the
+ * cumulative decay stays finite ("Core Technologies ...", sec. 2.1 and 2.3;
+ * "How Trillion-Scale ...", sec. 3.1 and 3.2).  With a decay per channel that
+ * reciprocal enters the tile products.  The recurrence (h = S^T):
+ *
+ *     d_t = diag(exp(g_t)) h_{t-1}
+ *     h_t = d_t - beta_t k_t (k_t^T d_t) + beta_t k_t v_t^T,   o_t = h_t^T q_t
+ *
+ * i.e. the decay acts on the key side of the old state first, then the
+ * delta-rule erase and write act on the decayed state; with every channel
+ * equal it is lin_attn_chunk_fwd.  Arithmetic is float32 for both dtypes.
+ * Arguments, layouts, alignment, aliasing rules, tail handling and errors as
+ * lin_attn_chunk_fwd, except: no workspace; 0 <= G <= 10 (LA_ERANGE beyond:
+ * the tile operands reach exp(8 G)).
+ */
+int lin_attn_chunk_fwd_channel(const void* q, const void* k, const void* v,
+                               const float* gate, int gate_mode, float G,
+                               const float* beta, const float* h0, void* o, float* hT,
+                               int B, int T, int H, int Dk, int Dv, int dtype, void* stream);
+
+/*
  * lin_attn_chunk_fwd_varlen_workspace_size -- bytes of device workspace that
  * lin_attn_chunk_fwd_varlen needs: H * (T / 32 + nseq + 1) * 6656 for LA_BF16
  * (one 6656-byte record slot per 32 tokens of each packed sequence, as in

@@ -302,3 +302,38 @@ def test_chunk_bwd_workspace_size_and_empty():
     for kw in (dict(B=0), dict(H=0)):
         rc, msg = bwd(q=None, k=None, v=None, dout=None, dq=None, **kw)
         assert rc == N.LA_OK, msg
+
+
+def channel(**kw):
+    a = dict(q=fake(0), k=fake(1), v=fake(2), gate=fake(3), gate_mode=1, G=5.0,
+             beta=fake(4), h0=None, o=fake(5), hT=fake(6), B=1, T=64, H=2, Dk=128,
+             Dv=128, dtype=0, stream=None)
+    a.update(kw)
+    L = N.lib()
+    rc = L.lin_attn_chunk_fwd_channel(a["q"], a["k"], a["v"], a["gate"], a["gate_mode"], a["G"],
+                                      a["beta"], a["h0"], a["o"], a["hT"], a["B"], a["T"],
+                                      a["H"], a["Dk"], a["Dv"], a["dtype"], a["stream"])
+    return rc, L.lin_attn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(gate=None), N.LA_EINVAL, "gate must not be NULL"),
+    (dict(gate=fake(3) + 4), N.LA_EINVAL, "gate must be 16-byte aligned"),
+    (dict(G=10.5), N.LA_ERANGE, "per-channel"),
+    (dict(G=-0.5), N.LA_ERANGE, "G must"),
+    (dict(Dk=96), N.LA_EUNSUPPORTED, "Dk"),
+    (dict(Dv=24), N.LA_EUNSUPPORTED, "Dv"),
+    (dict(dtype=5), N.LA_EINVAL, "dtype"),
+    # the per-channel gate is T*H*Dk floats: an o placed inside it overlaps
+    (dict(o=fake(3) + 64 * 2 * 4 * 64), N.LA_EINVAL, "o overlaps gate"),
+    (dict(hT=fake(3) + 64 * 2 * 4 * 64), N.LA_EINVAL, "hT overlaps gate"),
+])
+def test_chunk_fwd_channel_rejects(kw, code, needle):
+    rc, msg = channel(**kw)
+    assert rc == code and needle in msg, (rc, msg)
+
+
+def test_chunk_fwd_channel_empty_is_noop():
+    # B = 0 or H = 0: nothing to do, nothing dereferenced
+    assert channel(B=0)[0] == N.LA_OK
+    assert channel(H=0, q=None, k=None)[0] == N.LA_OK

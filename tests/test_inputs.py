@@ -23,3 +23,15 @@ def test_make_inputs_shapes_and_unit_keys():
     assert float((n - 1).abs().max()) < 1e-6
     b = inp["beta"]
     assert float(b.min()) > 0 and float(b.max()) < 1
+
+
+def test_channel_gate_shape_seed_and_moments():
+    x = I.make_channel_gate(1, 512, 2, 64, seed=9, mu=-8.0, std=1.0)
+    assert tuple(x.shape) == (1, 512, 2, 64)
+    assert bool((x == I.make_channel_gate(1, 512, 2, 64, seed=9, mu=-8.0, std=1.0)).all())
+    assert abs(float(x.mean()) + 8.0) < 0.05 and abs(float(x.std()) - 1.0) < 0.05
+    # its own stream: the other inputs of the same seed do not move
+    a = I.make_inputs(1, 8, 2, 64, 16, dtype="fp32", seed=9)
+    I.make_channel_gate(1, 8, 2, 64, seed=9)
+    b = I.make_inputs(1, 8, 2, 64, 16, dtype="fp32", seed=9)
+    assert bool((a["q"] == b["q"]).all()) and bool((a["x"] == b["x"]).all())
