@@ -258,13 +258,16 @@ def main():
     # ---- per-channel gate: the headline shape with one log-decay per key
     # channel (gate logits [B,T,H,Dk] ~ N(0,1))
     if args.channel_steps > 0 and dtype == "bf16":
-        from chunked_gated_linear_amd import lin_attn_chunk_fwd_channel
+        from chunked_gated_linear_amd import (lin_attn_chunk_fwd_channel,
+                                              lin_attn_chunk_fwd_channel_workspace_size)
         xc = I.make_channel_gate(B, T, H, Dk, seed=1002, device=dev)
         oc, hc = torch.empty_like(o), torch.empty_like(hT)
+        wsc = torch.empty(lin_attn_chunk_fwd_channel_workspace_size(B, T, H, Dk, Dv),
+                          dtype=torch.uint8, device=dev)
 
         def cstep():
             lin_attn_chunk_fwd_channel(inp["q"], inp["k"], inp["v"], xc, inp["beta"], inp["h0"],
-                                       gate_mode="logit", G=5.0, o=oc, hT=hc)
+                                       gate_mode="logit", G=5.0, o=oc, hT=hc, workspace=wsc)
 
         cstep()
         torch.cuda.synchronize()
@@ -283,9 +286,10 @@ def main():
             "roofline": {"bound": "hbm", "achieved": cbytes / (cms * 1e-3) / 1e9,
                          "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                          "frac": cbytes / (cms * 1e-3) / PEAK_HBM, "alg_bytes_per_launch": cbytes,
-                         "kernel": "chunk_fwd_channel_kernel"},
+                         "kernel": ("chunk_channel_prep_kernel + chunk_fwd_channel_kernel "
+                                    "(one lin_attn_chunk_fwd_channel call)")},
         }
-        del xc, oc, hc
+        del xc, oc, hc, wsc
 
     # ---- reverse pass at the training shape (B=4, H=16, T=8192, d=128): the
     # gradients of every input for an upstream dout and dhT

@@ -86,10 +86,22 @@ def lin_attn_chunk_fwd(q, k, v, gate, beta, h0=None, *, gate_mode="log", G=5.0,
     return o, hT
 
 
+def lin_attn_chunk_fwd_channel_workspace_size(B, T, H, Dk, Dv, dtype=torch.bfloat16):
+    """Workspace bytes lin_attn_chunk_fwd_channel needs for these sizes."""
+    n = N.lib().lin_attn_chunk_fwd_channel_workspace_size(B, T, H, Dk, Dv, _DTYPES[dtype])
+    if n < 0:
+        raise N.LinAttnError(N.LA_EINVAL, N.lib().lin_attn_last_error().decode())
+    return n
+
+
 def lin_attn_chunk_fwd_channel(q, k, v, gate, beta, h0=None, *, gate_mode="log", G=5.0,
-                               o=None, hT=None, output_final_state=True, stream=None):
+                               o=None, hT=None, output_final_state=True, workspace=None,
+                               stream=None):
     """lin_attn_chunk_fwd with one log-decay per key channel: gate [B,T,H,Dk]
-    float32.  Returns o [B,T,H,Dv] and hT [B,H,Dk,Dv] (None if not requested)."""
+    float32.  Returns o [B,T,H,Dv] and hT [B,H,Dk,Dv] (None if not requested).
+    `workspace`: optional uint8 GPU tensor of at least
+    lin_attn_chunk_fwd_channel_workspace_size(...) bytes (else one is taken
+    from torch's caching allocator)."""
     _need(q, "q")
     if q.dtype not in _DTYPES:
         raise TypeError("q, k, v must be bfloat16 or float32")
@@ -108,9 +120,15 @@ def lin_attn_chunk_fwd_channel(q, k, v, gate, beta, h0=None, *, gate_mode="log",
         hT = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device)
     if hT is not None:
         _need(hT, "hT", torch.float32, (B, H, Dk, Dv))
+    nws = lin_attn_chunk_fwd_channel_workspace_size(B, T, H, Dk, Dv, q.dtype)
+    if workspace is None and nws > 0:
+        workspace = torch.empty(nws, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8)
     N.check(N.lib().lin_attn_chunk_fwd_channel(
         _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _GATE[gate_mode], float(G), _ptr(beta),
-        _ptr(h0), _ptr(o), _ptr(hT), B, T, H, Dk, Dv, _DTYPES[q.dtype], _stream(q, stream)))
+        _ptr(h0), _ptr(o), _ptr(hT), B, T, H, Dk, Dv, _DTYPES[q.dtype], _ptr(workspace),
+        0 if workspace is None else workspace.numel(), _stream(q, stream)))
     return o, hT
 
 

@@ -29,67 +29,76 @@
 // overflow or the subnormal range.
 //
 // Arithmetic is fp32 throughout (inputs in bf16 convert exactly); the matrix
-// products run on the fp32 MFMA (16x16x4).  Work split as in the fp32 scalar
-// path: one workgroup per (b, h, 16-column slice of d_v); wave 0 ("chain")
-// owns the fp32 state slice in registers and runs the serial part, waves
-// 1..NP ("producers") prepare upcoming tiles -- loads, the gate, the
-// per-channel in-tile running sums, the scaled operands, A and P on MFMA, the
-// 16 x 16 solve -- and hand them over through LDS, double-buffered by epochs
-// of NP tiles.
+// products run on the fp32 MFMA (16x16x4).  Two launches:
+//   chunk_channel_prep_kernel  one wave per (sequence, head, tile), all in
+//       parallel: the gate, the per-channel in-tile running sums (DPP row
+//       scans), the scaled operands, A and P on MFMA, the 16 x 16 solve; the
+//       tile's record (everything that does not depend on the state) goes to
+//       the workspace once per head;
+//   chunk_fwd_channel_kernel   one workgroup per (sequence, head, 16-column
+//       slice of d_v): wave 0 ("chain") owns the fp32 state slice in
+//       registers and runs the serial part; waves 1..NP ("loaders") copy the
+//       records and the slice's v values into LDS, double-buffered by epochs
+//       of NP tiles, their global loads issued two epochs ahead.
 #include "la_device.h"
 #include "la_launch.h"
 
 namespace la {
 namespace {
 
-template <int DK, int NP>
-struct ChCfg {
+// One tile's record (bytes), in the workspace and in LDS; every field is
+// lane-contiguous in the order the chain wave reads it.  The workspace copy
+// stops at VF: the v values belong to a column slice and are loaded per slice.
+template <int DK>
+struct ChRec {
   static constexpr int NT = DK / 16;   // 16-row tiles of the state slice
   static constexpr int NS = DK / 32;   // 32-deep contraction blocks
-  // One prepared tile in LDS (fp32), every field lane-contiguous.
-  static constexpr int KF = 0;                       // K o Gam:  NS x 64 lanes x 8
+  static constexpr int KF = 0;                       // K o Gam:  NS x 64 lanes x 8 f32
   static constexpr int QF = KF + NS * 64 * 8 * 4;    // Q o Gam:  NS x 64 x 8
   static constexpr int KT = QF + NS * 64 * 8 * 4;    // (K o Gam_C/Gam)^T: NT x 64 x 4
-  static constexpr int VF = KT + NT * 64 * 4 * 4;    // V slice: 64 x 4
-  static constexpr int PF = VF + 64 * 4 * 4;         // P: 64 x 4
+  static constexpr int PF = KT + NT * 64 * 4 * 4;    // P: 64 x 4
   static constexpr int TB = PF + 64 * 4 * 4;         // (I + A)^-1 diag(beta), 16 x 16
   static constexpr int GC = TB + 256 * 4;            // Gam_C[DK]
-  static constexpr int REC = GC + DK * 4;
-  // Producer scratch: A (16 x 16) and beta[16].
-  static constexpr int SA = 0;
-  static constexpr int SB = 1024;
-  static constexpr int SCR = 1024 + 64;
-  static constexpr int LDS = 2 * NP * REC + NP * SCR;
-  static_assert(REC % 16 == 0 && SCR % 16 == 0, "LDS alignment");
+  static constexpr int VF = GC + DK * 4;             // V slice: 64 x 4 (LDS only)
+  static constexpr int GLOBAL = VF;                  // bytes per tile in the workspace
+  static constexpr int LDS = VF + 64 * 4 * 4;        // bytes per tile in LDS
+  static constexpr int CHUNKS = GLOBAL / 16;         // 16-byte pieces of a record
+  static_assert(GLOBAL % 16 == 0 && LDS % 16 == 0, "alignment");
+};
+
+// Producer scratch per wave (LDS): A (16 x 16) and beta[16].
+constexpr int kScrA = 0, kScrB = 1024, kScr = 1024 + 64;
+
+template <int DK, int NP>
+struct ChCfg {
+  static constexpr int LDS = 2 * NP * ChRec<DK>::LDS;
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
-// Flat block index -> (head, d_v slice), the NV slices of a head on one XCD
-// (workgroups are dealt to the 8 XCDs round robin).
-__device__ inline void ch_map_block(int n, int NH, int NV, int& head, int& vt) {
-  const int per = 8 * NV;
-  const int full = NH / 8;
-  const int a = n / per;
-  if (a < full) {
-    const int loc = n - a * per;
-    head = 8 * a + (loc & 7);
-    vt = loc >> 3;
-  } else {
-    const int loc = n - full * per;
-    const int r = NH - 8 * full;
-    head = 8 * full + loc % r;
-    vt = loc / r;
-  }
+// Inclusive prefix sum over the 16 lanes of each row (DPP row shifts by 1, 2,
+// 4, 8; lanes whose source falls outside the row add 0): no LDS traffic.
+__device__ inline float row_scan16(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x111, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x112, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x114, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x118, 0xf, 0xf, false));
+  return x;
 }
 
-// Producer registers for one tile: the lane's 8 * NS channels of its token's
-// k and q (in the input type), the same channels of the gate, four v values.
+// Lane L of each 16-lane row broadcast to the whole row (DPP row_newbcast).
+template <int L>
+__device__ inline float row_bcast(float x) {
+  static_assert(L >= 0 && L < 16, "lane within a row");
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + L, 0xf, 0xf, false));
+}
+
+// Registers for preparing one tile: the lane's 8 * NS channels of its token's
+// k and q (in the input type), the same channels of the gate, beta.
 template <typename E, int DK>
 struct ChRaw {
   typename Elt<E>::F32 kf[DK / 32];
   typename Elt<E>::F32 qf[DK / 32];
   f32x4 glo[DK / 32], ghi[DK / 32];
-  E vv[4];
   float bt;
 };
 
@@ -105,200 +114,102 @@ __device__ inline Elt<float>::F32 to_f32(const Elt<__bf16>::F32& a) {
   return r;
 }
 
-template <typename E, int DK, int NP>
-__global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_channel_kernel(
-    const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
-    const float* __restrict__ gate, int gate_logit, float G,
-    const float* __restrict__ beta, const float* h0, E* __restrict__ o, float* hT,
-    int B, int T, int H, int DV) {
-  using C = ChCfg<DK, NP>;
+// Loads of tile c of sequence-head (b, h) (token rows past the end read the
+// last valid row; prep_tile zeroes them).
+template <typename E, int DK>
+__device__ inline void load_tile(ChRaw<E, DK>& r, const E* __restrict__ q,
+                                 const E* __restrict__ k, const float* __restrict__ gate,
+                                 const float* __restrict__ beta, int b, int h, int c, int T,
+                                 int H, int n, int grp) {
+  constexpr int NS = DK / 32;
+  const int t = min(16 * c + n, T - 1);
+  const int64_t row = ((int64_t)b * T + t) * H + h;
+  const int64_t base = row * DK;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int c0 = 32 * s + 4 * grp, c1 = c0 + 16;
+    if constexpr (sizeof(E) == 2) {
+      const bf16x4 k0 = *reinterpret_cast<const bf16x4*>(k + base + c0);
+      const bf16x4 k1 = *reinterpret_cast<const bf16x4*>(k + base + c1);
+      const bf16x4 q0 = *reinterpret_cast<const bf16x4*>(q + base + c0);
+      const bf16x4 q1 = *reinterpret_cast<const bf16x4*>(q + base + c1);
+      r.kf[s].v = bf16x8{k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
+      r.qf[s].v = bf16x8{q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
+    } else {
+      r.kf[s].lo = *reinterpret_cast<const f32x4*>(k + base + c0);
+      r.kf[s].hi = *reinterpret_cast<const f32x4*>(k + base + c1);
+      r.qf[s].lo = *reinterpret_cast<const f32x4*>(q + base + c0);
+      r.qf[s].hi = *reinterpret_cast<const f32x4*>(q + base + c1);
+    }
+    r.glo[s] = *reinterpret_cast<const f32x4*>(gate + base + c0);
+    r.ghi[s] = *reinterpret_cast<const f32x4*>(gate + base + c1);
+  }
+  r.bt = beta[row];
+}
+
+// Prepare tile c into the record at `rec` (sA, sB: this wave's LDS scratch).
+template <typename E, int DK>
+__device__ inline void prep_tile(const ChRaw<E, DK>& r, int c, int T, char* __restrict__ rec,
+                                 float* sA, float* sB, int gate_logit, float G, int n, int grp,
+                                 int lane) {
+  using R = ChRec<DK>;
   using X = Elt<float>;
   using F16 = X::F16;
   using F32 = X::F32;
-  constexpr int NT = C::NT, NS = C::NS;
-  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
-
-  const int NV = DV / 16;
-  int head, vt;
-  ch_map_block(blockIdx.x, B * H, NV, head, vt);
-  const int b = head / H, h = head % H;
-  const int v0 = vt * 16;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int n = lane & 15, grp = lane >> 4;
-  const int NC = (T + 15) >> 4;
-  const int NE = (NC + NP - 1) / NP;
-
-  auto rowk = [&](int t) -> int64_t { return ((int64_t)b * T + t) * H + h; };
-  auto rec_of = [&](int ep, int j) -> char* { return smem + ((ep & 1) * NP + j) * C::REC; };
-
-  if (wave == 0) {
-    // ------------------------------------------------------------ chain wave
-    f32x4 Hacc[NT];
-    const int64_t sbase = ((int64_t)b * H + h) * DK * DV;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        Hacc[t][i] = h0 ? h0[sbase + (int64_t)(16 * t + 4 * grp + i) * DV + v0 + n] : 0.f;
-    }
-    const int64_t ostride = (int64_t)H * DV;
-    E* const orow = o + rowk(4 * grp) * DV + v0 + n;
-    __syncthreads();  // epoch 0 prepared
-    for (int ep = 0; ep < NE; ++ep) {
-      for (int j = 0; j < NP; ++j) {
-        const int c = ep * NP + j;
-        if (c >= NC) break;
-        const char* rec = rec_of(ep, j);
-        // R = (K o Gam) H and (Q o Gam) H, contraction over d_k
-        f32x4 R = zero4(), QH = zero4();
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          const F32 hb = X::from_acc2(Hacc[2 * s], Hacc[2 * s + 1]);
-          const F32 kf = reinterpret_cast<const F32*>(rec + C::KF)[s * 64 + lane];
-          const F32 qf = reinterpret_cast<const F32*>(rec + C::QF)[s * 64 + lane];
-          R = X::mma32(kf, hb, R);
-          QH = X::mma32(qf, hb, QH);
-        }
-        const F16 vf = reinterpret_cast<const F16*>(rec + C::VF)[lane];
-        const F16 tb = *reinterpret_cast<const F16*>(rec + C::TB + (n * 16 + 4 * grp) * 4);
-        const F16 pf = reinterpret_cast<const F16*>(rec + C::PF)[lane];
-        f32x4 Y;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) Y[i] = vf.v[i] - R[i];
-        const f32x4 U = X::mma16(tb, X::from_acc(Y), zero4());
-        const f32x4 O = X::mma16(pf, X::from_acc(U), QH);
-        E* oc = orow + (int64_t)(16 * c) * ostride;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (16 * c + 4 * grp + i < T) oc[i * ostride] = Elt<E>::from_f(O[i]);
-        const F16 ub = X::from_acc(U);
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const f32x4 gc = reinterpret_cast<const f32x4*>(rec + C::GC)[4 * t + grp];
-          const F16 kt = reinterpret_cast<const F16*>(rec + C::KT)[t * 64 + lane];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) Hacc[t][i] *= gc[i];   // row 16t + 4grp + i
-          Hacc[t] = X::mma16(kt, ub, Hacc[t]);
-        }
-      }
-      __syncthreads();  // this epoch consumed, next epoch prepared
-    }
-    if (hT) {
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          hT[sbase + (int64_t)(16 * t + 4 * grp + i) * DV + v0 + n] = Hacc[t][i];
-      }
-    }
-    return;
-  }
-
-  // -------------------------------------------------------------- producers
-  const int p = wave - 1;
-  char* scr = smem + 2 * NP * C::REC + p * C::SCR;
-  float* sA = reinterpret_cast<float*>(scr + C::SA);
-  float* sB = reinterpret_cast<float*>(scr + C::SB);
-
-  // Global loads of tile c (index clamped to the last tile, rows past the end
-  // read from the last valid row and zeroed in produce()), issued one epoch
-  // before the tile is prepared.
-  auto load = [&](ChRaw<E, DK>& r, int c) {
-    c = min(c, NC - 1);
-    const int t = min(16 * c + n, T - 1);
-    const int64_t base = rowk(t) * DK;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const int c0 = 32 * s + 4 * grp, c1 = c0 + 16;
-      if constexpr (sizeof(E) == 2) {
-        const bf16x4 k0 = *reinterpret_cast<const bf16x4*>(k + base + c0);
-        const bf16x4 k1 = *reinterpret_cast<const bf16x4*>(k + base + c1);
-        const bf16x4 q0 = *reinterpret_cast<const bf16x4*>(q + base + c0);
-        const bf16x4 q1 = *reinterpret_cast<const bf16x4*>(q + base + c1);
-        r.kf[s].v = bf16x8{k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
-        r.qf[s].v = bf16x8{q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
-      } else {
-        r.kf[s].lo = *reinterpret_cast<const f32x4*>(k + base + c0);
-        r.kf[s].hi = *reinterpret_cast<const f32x4*>(k + base + c1);
-        r.qf[s].lo = *reinterpret_cast<const f32x4*>(q + base + c0);
-        r.qf[s].hi = *reinterpret_cast<const f32x4*>(q + base + c1);
-      }
-      r.glo[s] = *reinterpret_cast<const f32x4*>(gate + base + c0);
-      r.ghi[s] = *reinterpret_cast<const f32x4*>(gate + base + c1);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      r.vv[i] = v[rowk(min(16 * c + 4 * grp + i, T - 1)) * DV + v0 + n];
-    r.bt = beta[rowk(t)];
-  };
-
-  auto produce = [&](const ChRaw<E, DK>& r, int c) {
-    if (c >= NC) return;
-    char* rec = rec_of(c / NP, c % NP);
+  constexpr int NS = R::NS;
     // padding tokens past T: q = k = v = 0, g = 0, beta = 0 (an identity step)
     const bool ok = 16 * c + n < T;
     const float bt = ok ? r.bt : 0.f;
-    // per lane: 8 channels per 32-deep block s (j < 4: 32s + 4grp + j,
-    // j >= 4: 32s + 16 + 4grp + j - 4), token t = n
-    float vkg[NS][8], vqg[NS][8], vkd[NS][8], vkm[NS][8], vqm[NS][8], vki[NS][8];
+    if (grp == 0) sB[n] = bt;
+    // One 32-deep channel block s at a time (8 channels per lane: j < 4 is
+    // channel 32s + 4grp + j, j >= 4 is 32s + 16 + 4grp + j - 4; token t = n):
+    // the per-channel running sums, the scaled operands, their share of A and
+    // P (lane (n, grp) register i ends with entry [n][4grp+i], i.e. row n,
+    // column s = 4grp+i, of A before beta and of P), and the record fields.
+    f32x4 sa = zero4(), sp = zero4();
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const F32 k32 = to_f32(r.kf[s]), q32 = to_f32(r.qf[s]);
+      float vkg[8], vqg[8], vkm[8], vqm[8], vki[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float x = j < 4 ? r.glo[s][j] : r.ghi[s][j - 4];
         const float g = ok ? (gate_logit ? bounded_gate(x, G) : x) : 0.f;
-        const float Gt = scan16(g, n);                  // G_t[c], t = n
-        const float Gm = __shfl(Gt, 7, 16);             // G at the middle token
-        const float Gl = __shfl(Gt, 15, 16);            // G at the last token
+        const float Gt = row_scan16(g);                 // G_t[c], t = n
+        const float Gm = row_bcast<7>(Gt);              // G at the middle token
+        const float Gl = row_bcast<15>(Gt);             // G at the last token
         const float kv = ok ? (j < 4 ? k32.lo[j] : k32.hi[j - 4]) : 0.f;
         const float qv = ok ? (j < 4 ? q32.lo[j] : q32.hi[j - 4]) : 0.f;
         const float e_start = __expf(Gt);               // Gam_t            (<= 1)
+        const float e_last = row_bcast<15>(e_start);    // Gam_C = exp(G at the last token)
         const float e_end = __expf(Gl - Gt);            // Gam_C / Gam_t    (<= 1)
         const float e_mid = __expf(Gt - Gm);            // Gam_t / Gam_m
         const float e_imid = __expf(Gm - Gt);           // Gam_m / Gam_t
-        vkg[s][j] = kv * e_start;
-        vqg[s][j] = qv * e_start;
-        vkd[s][j] = kv * e_end;
-        vkm[s][j] = kv * e_mid;
-        vqm[s][j] = qv * e_mid;
-        vki[s][j] = kv * e_imid;
-        if (n == 0) {   // Gam_C of this channel
-          const int ch = 32 * s + (j < 4 ? 4 * grp + j : 16 + 4 * grp + j - 4);
-          reinterpret_cast<float*>(rec + C::GC)[ch] = __expf(Gl);
-        }
+        vkg[j] = kv * e_start;
+        vqg[j] = qv * e_start;
+        vkm[j] = kv * e_mid;
+        vqm[j] = qv * e_mid;
+        vki[j] = kv * e_imid;
+        const int ch = 32 * s + (j < 4 ? 4 * grp + j : 16 + 4 * grp + j - 4);
+        // (K o Gam_C/Gam)^T in the chain's A-fragment order: for state tile
+        // ch / 16, lane (ch % 16, n / 4) register n % 4
+        reinterpret_cast<float*>(rec + R::KT)[((ch >> 4) * 64 + (n >> 2) * 16 + (ch & 15)) * 4 +
+                                              (n & 3)] = kv * e_end;
+        if (n == 0) reinterpret_cast<float*>(rec + R::GC)[ch] = e_last;
       }
-    }
-    auto pack = [](const float (&a)[8]) {
-      F32 f;
+      F32 kg, qg, km, qm, ki;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        f.lo[j] = a[j];
-        f.hi[j] = a[4 + j];
+        kg.lo[j] = vkg[j]; kg.hi[j] = vkg[4 + j];
+        qg.lo[j] = vqg[j]; qg.hi[j] = vqg[4 + j];
+        km.lo[j] = vkm[j]; km.hi[j] = vkm[4 + j];
+        qm.lo[j] = vqm[j]; qm.hi[j] = vqm[4 + j];
+        ki.lo[j] = vki[j]; ki.hi[j] = vki[4 + j];
       }
-      return f;
-    };
-    F32 kg[NS], qg[NS], kd[NS], km[NS], qm[NS], ki[NS];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      kg[s] = pack(vkg[s]);
-      qg[s] = pack(vqg[s]);
-      kd[s] = pack(vkd[s]);
-      km[s] = pack(vkm[s]);
-      qm[s] = pack(vqm[s]);
-      ki[s] = pack(vki[s]);
-    }
-    if (grp == 0) sB[n] = bt;
-
-    // A and P: lane (n, grp) register i gets entry [4grp+i][n] of
-    // (K / Gam_m-scaled) x (K or Q scaled), i.e. row n, column s = 4grp+i of
-    // A (before beta) and of P.
-    f32x4 sa = zero4(), sp = zero4();
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      sa = X::mma32(ki[s], km[s], sa);
-      sp = X::mma32(ki[s], qm[s], sp);
+      reinterpret_cast<F32*>(rec + R::KF)[s * 64 + lane] = kg;
+      reinterpret_cast<F32*>(rec + R::QF)[s * 64 + lane] = qg;
+      sa = X::mma32(ki, km, sa);
+      sp = X::mma32(ki, qm, sp);
     }
     f32x4 arow, prow;
 #pragma unroll
@@ -308,30 +219,7 @@ __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_channel_kernel(
       prow[i] = s_ <= n ? sp[i] : 0.f;
     }
     reinterpret_cast<f32x4*>(sA)[n * 4 + grp] = arow;          // A[n][4grp..4grp+3]
-    reinterpret_cast<F16*>(rec + C::PF)[lane] = X::from_acc(prow);
-
-    // (K o Gam_C/Gam)^T fragments: the 16-column block t of that matrix times
-    // the identity puts entry [4grp+i][16t+n] in lane (n, grp) register i.
-    f32x4 idv;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) idv[j] = (4 * grp + j == n) ? 1.f : 0.f;
-    const F16 ident = X::from_acc(idv);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const f32x4 kt = X::mma16(X::half(kd[t >> 1], t & 1), ident, zero4());
-      reinterpret_cast<F16*>(rec + C::KT)[t * 64 + lane] = X::from_acc(kt);
-    }
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      reinterpret_cast<F32*>(rec + C::KF)[s * 64 + lane] = kg[s];
-      reinterpret_cast<F32*>(rec + C::QF)[s * 64 + lane] = qg[s];
-    }
-    F16 vf;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      vf.v[i] = (16 * c + 4 * grp + i < T) ? Elt<E>::to_f(r.vv[i]) : 0.f;
-    reinterpret_cast<F16*>(rec + C::VF)[lane] = vf;
-
+    reinterpret_cast<F16*>(rec + R::PF)[lane] = X::from_acc(prow);
     // this wave's LDS writes (A, beta) before its reads of them
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -360,29 +248,204 @@ __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_channel_kernel(
       for (int s = 0; s < 16; s += 4) {
         const f32x4 row{x[s] * sB[s], x[s + 1] * sB[s + 1], x[s + 2] * sB[s + 2],
                         x[s + 3] * sB[s + 3]};
-        *reinterpret_cast<f32x4*>(rec + C::TB + (n * 16 + s) * 4) = row;
+        *reinterpret_cast<f32x4*>(rec + R::TB + (n * 16 + s) * 4) = row;
       }
     }
-    // the next tile's writes to A / beta must not pass this tile's reads
+}
+
+// ------------------------------------------------------------- prep kernel
+template <typename E, int DK>
+__global__ __launch_bounds__(256) void chunk_channel_prep_kernel(
+    const E* __restrict__ q, const E* __restrict__ k, const float* __restrict__ gate,
+    int gate_logit, float G, const float* __restrict__ beta, char* __restrict__ ws, int B,
+    int T, int H) {
+  __shared__ __attribute__((aligned(16))) char smem[4 * kScr];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15, grp = lane >> 4;
+  float* sA = reinterpret_cast<float*>(smem + wave * kScr + kScrA);
+  float* sB = reinterpret_cast<float*>(smem + wave * kScr + kScrB);
+  const int NC = (T + 15) >> 4;
+  const int64_t jobs = (int64_t)B * H * NC;
+  for (int64_t job = (int64_t)blockIdx.x * 4 + wave; job < jobs; job += (int64_t)gridDim.x * 4) {
+    const int c = (int)(job % NC);
+    const int64_t bh = job / NC;
+    const int h = (int)(bh % H), b = (int)(bh / H);
+    ChRaw<E, DK> r;
+    load_tile<E, DK>(r, q, k, gate, beta, b, h, c, T, H, n, grp);
+    prep_tile<E, DK>(r, c, T, ws + job * ChRec<DK>::GLOBAL, sA, sB, gate_logit, G, n, grp, lane);
+    // the next job's writes to A / beta must not pass this job's reads
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
+// Flat block index -> (head, d_v slice), the NV slices of a head on one XCD
+// (workgroups are dealt to the 8 XCDs round robin).
+__device__ inline void ch_map_block(int n, int NH, int NV, int& head, int& vt) {
+  const int per = 8 * NV;
+  const int full = NH / 8;
+  const int a = n / per;
+  if (a < full) {
+    const int loc = n - a * per;
+    head = 8 * a + (loc & 7);
+    vt = loc >> 3;
+  } else {
+    const int loc = n - full * per;
+    const int r = NH - 8 * full;
+    head = 8 * full + loc % r;
+    vt = loc / r;
+  }
+}
+
+// A loader's registers for one tile: its share of the record (16-byte pieces
+// lane, lane + 64, ...) and the slice's four v values.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+template <typename E, int DK>
+struct ChCopy {
+  static constexpr int PIECES = (ChRec<DK>::CHUNKS + 63) / 64;
+  u32x4 piece[PIECES];
+  E vv[4];
+};
+
+// ------------------------------------------------------------ chain kernel
+template <typename E, int DK, int NP>
+__global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_channel_kernel(
+    const E* __restrict__ v, const char* __restrict__ ws, const float* h0,
+    E* __restrict__ o, float* hT, int B, int T, int H, int DV) {
+  using R = ChRec<DK>;
+  using C = ChCfg<DK, NP>;
+  using X = Elt<float>;
+  using F16 = X::F16;
+  using F32 = X::F32;
+  constexpr int NT = R::NT, NS = R::NS;
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+
+  const int NV = DV / 16;
+  int head, vt;
+  ch_map_block(blockIdx.x, B * H, NV, head, vt);
+  const int b = head / H, h = head % H;
+  const int v0 = vt * 16;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15, grp = lane >> 4;
+  const int NC = (T + 15) >> 4;
+  const int NE = (NC + NP - 1) / NP;
+
+  auto rowk = [&](int t) -> int64_t { return ((int64_t)b * T + t) * H + h; };
+  auto rec_of = [&](int ep, int j) -> char* { return smem + ((ep & 1) * NP + j) * R::LDS; };
+
+  if (wave == 0) {
+    // ------------------------------------------------------------ chain wave
+    f32x4 Hacc[NT];
+    const int64_t sbase = ((int64_t)b * H + h) * DK * DV;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        Hacc[t][i] = h0 ? h0[sbase + (int64_t)(16 * t + 4 * grp + i) * DV + v0 + n] : 0.f;
+    }
+    const int64_t ostride = (int64_t)H * DV;
+    E* const orow = o + rowk(4 * grp) * DV + v0 + n;
+    __syncthreads();  // epoch 0 loaded
+    for (int ep = 0; ep < NE; ++ep) {
+      for (int j = 0; j < NP; ++j) {
+        const int c = ep * NP + j;
+        if (c >= NC) break;
+        const char* rec = rec_of(ep, j);
+        // R = (K o Gam) H and (Q o Gam) H, contraction over d_k
+        f32x4 Rk = zero4(), QH = zero4();
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const F32 hb = X::from_acc2(Hacc[2 * s], Hacc[2 * s + 1]);
+          const F32 kf = reinterpret_cast<const F32*>(rec + R::KF)[s * 64 + lane];
+          const F32 qf = reinterpret_cast<const F32*>(rec + R::QF)[s * 64 + lane];
+          Rk = X::mma32(kf, hb, Rk);
+          QH = X::mma32(qf, hb, QH);
+        }
+        const F16 vf = reinterpret_cast<const F16*>(rec + R::VF)[lane];
+        const F16 tb = *reinterpret_cast<const F16*>(rec + R::TB + (n * 16 + 4 * grp) * 4);
+        const F16 pf = reinterpret_cast<const F16*>(rec + R::PF)[lane];
+        f32x4 Y;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Y[i] = vf.v[i] - Rk[i];
+        const f32x4 U = X::mma16(tb, X::from_acc(Y), zero4());
+        const f32x4 O = X::mma16(pf, X::from_acc(U), QH);
+        E* oc = orow + (int64_t)(16 * c) * ostride;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (16 * c + 4 * grp + i < T) oc[i * ostride] = Elt<E>::from_f(O[i]);
+        const F16 ub = X::from_acc(U);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const f32x4 gc = reinterpret_cast<const f32x4*>(rec + R::GC)[4 * t + grp];
+          const F16 kt = reinterpret_cast<const F16*>(rec + R::KT)[t * 64 + lane];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) Hacc[t][i] *= gc[i];   // row 16t + 4grp + i
+          Hacc[t] = X::mma16(kt, ub, Hacc[t]);
+        }
+      }
+      __syncthreads();  // this epoch consumed, next epoch loaded
+    }
+    if (hT) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          hT[sbase + (int64_t)(16 * t + 4 * grp + i) * DV + v0 + n] = Hacc[t][i];
+      }
+    }
+    return;
+  }
+
+  // ---------------------------------------------------------------- loaders
+  const int p = wave - 1;
+  const char* recs = ws + ((int64_t)b * H + h) * NC * R::GLOBAL;
+  // Global loads of tile c (clamped to the last tile, so every path issues
+  // the same number of loads and the compiler can wait for the older set).
+  auto load = [&](ChCopy<E, DK>& r, int c) {
+    c = min(c, NC - 1);
+    const u32x4* src = reinterpret_cast<const u32x4*>(recs + (int64_t)c * R::GLOBAL);
+#pragma unroll
+    for (int i = 0; i < ChCopy<E, DK>::PIECES; ++i) {
+      const int x = i * 64 + lane;
+      r.piece[i] = src[x < R::CHUNKS ? x : R::CHUNKS - 1];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      r.vv[i] = v[rowk(min(16 * c + 4 * grp + i, T - 1)) * DV + v0 + n];
+  };
+  auto store = [&](const ChCopy<E, DK>& r, int c) {
+    if (c >= NC) return;
+    char* rec = rec_of(c / NP, c % NP);
+    u32x4* dst = reinterpret_cast<u32x4*>(rec);
+#pragma unroll
+    for (int i = 0; i < ChCopy<E, DK>::PIECES; ++i) {
+      const int x = i * 64 + lane;
+      if (x < R::CHUNKS) dst[x] = r.piece[i];
+    }
+    F16 vf;   // v past the end of the sequence is 0 (padding tokens)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      vf.v[i] = (16 * c + 4 * grp + i < T) ? Elt<E>::to_f(r.vv[i]) : 0.f;
+    reinterpret_cast<F16*>(rec + R::VF)[lane] = vf;
   };
 
   // Two register sets alternating by epoch: while tile (ep+1)*NP + p is
-  // prepared from one, the loads for tile (ep+2)*NP + p fill the other.
-  ChRaw<E, DK> ra, rb;
+  // stored from one, the loads for tile (ep+2)*NP + p fill the other.
+  ChCopy<E, DK> ra, rb;
   load(ra, p);
-  produce(ra, p);               // epoch 0
-  load(ra, NP + p);             // epoch 1, prepared during epoch 0
+  store(ra, p);                 // epoch 0
+  load(ra, NP + p);             // epoch 1, stored during epoch 0
   __syncthreads();
   for (int ep = 0; ep < NE; ep += 2) {
     load(rb, (ep + 2) * NP + p);
-    produce(ra, (ep + 1) * NP + p);
+    store(ra, (ep + 1) * NP + p);
     __syncthreads();
     if (ep + 1 < NE) {
       load(ra, (ep + 3) * NP + p);
-      produce(rb, (ep + 2) * NP + p);
+      store(rb, (ep + 2) * NP + p);
       __syncthreads();
     }
   }
@@ -391,27 +454,39 @@ __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_channel_kernel(
 template <typename E, int DK, int NP>
 hipError_t launch_ch(const void* q, const void* k, const void* v, const float* gate,
                      int gate_logit, float G, const float* beta, const float* h0, void* o,
-                     float* hT, int B, int T, int H, int Dv, hipStream_t st) {
+                     float* hT, int B, int T, int H, int Dv, void* ws, hipStream_t st) {
+  const int NC = (T + 15) / 16;
+  const int64_t jobs = (int64_t)B * H * NC;
+  const int prep_blocks = (int)((jobs + 3) / 4 < 4096 ? (jobs + 3) / 4 : 4096);
+  hipLaunchKernelGGL((chunk_channel_prep_kernel<E, DK>), dim3(prep_blocks), dim3(256), 0, st,
+                     (const E*)q, (const E*)k, gate, gate_logit, G, beta, (char*)ws, B, T, H);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const int blocks = B * H * (Dv / 16);
   hipLaunchKernelGGL((chunk_fwd_channel_kernel<E, DK, NP>), dim3(blocks), dim3(64 * (NP + 1)),
-                     0, st, (const E*)q, (const E*)k, (const E*)v, gate, gate_logit, G, beta,
-                     h0, (E*)o, hT, B, T, H, Dv);
+                     0, st, (const E*)v, (const char*)ws, h0, (E*)o, hT, B, T, H, Dv);
   return hipGetLastError();
 }
 
 }  // namespace
 
+long long chunk_channel_workspace_bytes(int B, int T, int H, int Dk) {
+  const long long nc = (T + 15) / 16;
+  const long long rec = Dk == 64 ? ChRec<64>::GLOBAL : ChRec<128>::GLOBAL;
+  return (long long)B * H * nc * rec;
+}
+
 hipError_t launch_chunk_fwd_channel(const void* q, const void* k, const void* v,
                                     const float* gate, int gate_logit, float G,
                                     const float* beta, const float* h0, void* o, float* hT,
-                                    int B, int T, int H, int Dk, int Dv, int fp32,
+                                    int B, int T, int H, int Dk, int Dv, int fp32, void* ws,
                                     hipStream_t st) {
   if (fp32) {
-    if (Dk == 64) return launch_ch<float, 64, 2>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, st);
-    if (Dk == 128) return launch_ch<float, 128, 2>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, st);
+    if (Dk == 64) return launch_ch<float, 64, 2>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, ws, st);
+    if (Dk == 128) return launch_ch<float, 128, 2>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, ws, st);
   } else {
-    if (Dk == 64) return launch_ch<__bf16, 64, 2>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, st);
-    if (Dk == 128) return launch_ch<__bf16, 128, 2>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, st);
+    if (Dk == 64) return launch_ch<__bf16, 64, 2>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, ws, st);
+    if (Dk == 128) return launch_ch<__bf16, 128, 2>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, ws, st);
   }
   return hipErrorInvalidValue;
 }

@@ -50,13 +50,17 @@ hipError_t launch_chunk_bwd(const void* q, const void* k, const void* v, const v
 // the fp32 state at the tile start and the fp32 gradient of its end state.
 long long chunk_bwd_workspace_bytes(int B, int T, int H, int Dk, int Dv);
 
-// Per-channel gate (gate [B, T, H, Dk]): one fused kernel, fp32 arithmetic,
-// no workspace; q, k, v, o bf16 or fp32 as `fp32` says.
+// Per-channel gate (gate [B, T, H, Dk]), fp32 arithmetic; q, k, v, o bf16 or
+// fp32 as `fp32` says: a parallel tile-preparation kernel into the workspace,
+// then the serial kernel.
 hipError_t launch_chunk_fwd_channel(const void* q, const void* k, const void* v,
                                     const float* gate, int gate_logit, float G,
                                     const float* beta, const float* h0, void* o, float* hT,
-                                    int B, int T, int H, int Dk, int Dv, int fp32,
+                                    int B, int T, int H, int Dk, int Dv, int fp32, void* ws,
                                     hipStream_t st);
+
+// Workspace bytes of the per-channel path: one record per tile and head.
+long long chunk_channel_workspace_bytes(int B, int T, int H, int Dk);
 
 hipError_t launch_decode(const void* q, const void* k, const void* v,
                          const float* gate, int gate_logit, float G,

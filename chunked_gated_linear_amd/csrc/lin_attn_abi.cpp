@@ -97,6 +97,10 @@ long long chunk_workspace(int B, int T, int H, int Dk, int Dv, int dtype) {
   return dtype == LA_BF16 ? la::chunk_pair_workspace_bytes(B, T, H, Dk, Dv) : 0;
 }
 
+long long channel_workspace(int B, int T, int H, int Dk) {
+  return T > 0 ? la::chunk_channel_workspace_bytes(B, T, H, Dk) : 0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -133,7 +137,9 @@ int chunk_fwd(const void* q, const void* k, const void* v, const float* gate, in
   const int64_t nst = (int64_t)B * H * Dk * Dv;
   if (B == 0 || H == 0) return ok();
   const unsigned ea = dtype == LA_BF16 ? 2u : 4u;
-  const long long wsz = T > 0 && !channel ? chunk_workspace(B, T, H, Dk, Dv, dtype) : 0;
+  const long long wsz = T <= 0 ? 0
+                        : channel ? channel_workspace(B, T, H, Dk)
+                                  : chunk_workspace(B, T, H, Dk, Dv, dtype);
   const int64_t ngate = channel ? ntok * Dk : ntok;   // gate elements
   if (T > 0) {
     // q, k and v are read as 16-byte vectors, bf16 o written as 8-byte vectors;
@@ -179,7 +185,8 @@ int chunk_fwd(const void* q, const void* k, const void* v, const float* gate, in
   const int logit = gate_mode == LA_GATE_BOUNDED_LOGIT;
   if (channel)
     return hip_status(la::launch_chunk_fwd_channel(q, k, v, gate, logit, G, beta, h0, o, hT, B,
-                                                   T, H, Dk, Dv, dtype == LA_FP32, st),
+                                                   T, H, Dk, Dv, dtype == LA_FP32, workspace,
+                                                   st),
                       "chunk_fwd_channel launch");
   hipError_t e = dtype == LA_FP32
       ? la::launch_chunk_fwd(q, k, v, gate, logit, G, beta, h0, o, hT, B, T, H, Dk, Dv, st)
@@ -200,12 +207,20 @@ int lin_attn_chunk_fwd(const void* q, const void* k, const void* v, const float*
                    workspace, workspace_bytes, stream, 0);
 }
 
+long long lin_attn_chunk_fwd_channel_workspace_size(int B, int T, int H, int Dk, int Dv,
+                                                   int dtype) {
+  if (check_chunk_sizes(B, T, H, Dk, Dv, dtype)) return -1;
+  ok();
+  return channel_workspace(B, T, H, Dk);
+}
+
 int lin_attn_chunk_fwd_channel(const void* q, const void* k, const void* v, const float* gate,
                                int gate_mode, float G, const float* beta, const float* h0,
                                void* o, float* hT, int B, int T, int H, int Dk, int Dv,
-                               int dtype, void* stream) {
+                               int dtype, void* workspace, long long workspace_bytes,
+                               void* stream) {
   return chunk_fwd(q, k, v, gate, gate_mode, G, beta, h0, o, hT, B, T, H, Dk, Dv, dtype,
-                   nullptr, 0, stream, 0, 1);
+                   workspace, workspace_bytes, stream, 0, 1);
 }
 
 int lin_attn_chunk_fwd_raw(const void* q, const void* k, const void* v, const float* gate,

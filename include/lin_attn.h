@@ -163,13 +163,25 @@ int lin_attn_chunk_fwd_raw(const void* q, const void* k, const void* v,
  * delta-rule erase and write act on the decayed state; with every channel
  * equal it is lin_attn_chunk_fwd.  Arithmetic is float32 for both dtypes.
  * Arguments, layouts, alignment, aliasing rules, tail handling and errors as
- * lin_attn_chunk_fwd, except: no workspace; 0 <= G <= 10 (LA_ERANGE beyond:
- * the tile operands reach exp(8 G)).
+ * lin_attn_chunk_fwd, except: the workspace holds one record per tile and
+ * head (lin_attn_chunk_fwd_channel_workspace_size bytes, for both dtypes), and
+ * 0 <= G <= 10 (LA_ERANGE beyond: the tile operands reach exp(8 G)).
  */
 int lin_attn_chunk_fwd_channel(const void* q, const void* k, const void* v,
                                const float* gate, int gate_mode, float G,
                                const float* beta, const float* h0, void* o, float* hT,
-                               int B, int T, int H, int Dk, int Dv, int dtype, void* stream);
+                               int B, int T, int H, int Dk, int Dv, int dtype,
+                               void* workspace, long long workspace_bytes, void* stream);
+
+/*
+ * lin_attn_chunk_fwd_channel_workspace_size -- device workspace bytes of
+ * lin_attn_chunk_fwd_channel: B * H * ceil(T / 16) * R with R = 27,136 for
+ * Dk = 128 and 14,592 for Dk = 64 (the state-independent operators of each
+ * 16-token tile, prepared once per head); 0 when T = 0; -1 (with
+ * lin_attn_last_error() set) for invalid or unsupported sizes.
+ */
+long long lin_attn_chunk_fwd_channel_workspace_size(int B, int T, int H, int Dk, int Dv,
+                                                   int dtype);
 
 /*
  * lin_attn_chunk_fwd_varlen_workspace_size -- bytes of device workspace that

@@ -307,12 +307,13 @@ def test_chunk_bwd_workspace_size_and_empty():
 def channel(**kw):
     a = dict(q=fake(0), k=fake(1), v=fake(2), gate=fake(3), gate_mode=1, G=5.0,
              beta=fake(4), h0=None, o=fake(5), hT=fake(6), B=1, T=64, H=2, Dk=128,
-             Dv=128, dtype=0, stream=None)
+             Dv=128, dtype=0, ws=fake(8), ws_bytes=1 << 30, stream=None)
     a.update(kw)
     L = N.lib()
     rc = L.lin_attn_chunk_fwd_channel(a["q"], a["k"], a["v"], a["gate"], a["gate_mode"], a["G"],
                                       a["beta"], a["h0"], a["o"], a["hT"], a["B"], a["T"],
-                                      a["H"], a["Dk"], a["Dv"], a["dtype"], a["stream"])
+                                      a["H"], a["Dk"], a["Dv"], a["dtype"], a["ws"],
+                                      a["ws_bytes"], a["stream"])
     return rc, L.lin_attn_last_error().decode()
 
 
@@ -327,6 +328,10 @@ def channel(**kw):
     # the per-channel gate is T*H*Dk floats: an o placed inside it overlaps
     (dict(o=fake(3) + 64 * 2 * 4 * 64), N.LA_EINVAL, "o overlaps gate"),
     (dict(hT=fake(3) + 64 * 2 * 4 * 64), N.LA_EINVAL, "hT overlaps gate"),
+    (dict(ws=None), N.LA_EINVAL, "workspace must not be NULL"),
+    (dict(ws_bytes=1000), N.LA_EINVAL, "workspace too small"),
+    (dict(ws=fake(8) + 16), N.LA_EINVAL, "workspace must be 256-byte aligned"),
+    (dict(ws=fake(3)), N.LA_EINVAL, "workspace overlaps gate"),
 ])
 def test_chunk_fwd_channel_rejects(kw, code, needle):
     rc, msg = channel(**kw)
@@ -337,3 +342,11 @@ def test_chunk_fwd_channel_empty_is_noop():
     # B = 0 or H = 0: nothing to do, nothing dereferenced
     assert channel(B=0)[0] == N.LA_OK
     assert channel(H=0, q=None, k=None)[0] == N.LA_OK
+
+
+def test_chunk_fwd_channel_workspace_size():
+    L = N.lib()
+    assert L.lin_attn_chunk_fwd_channel_workspace_size(1, 64, 2, 128, 128, 0) == 2 * 4 * 27136
+    assert L.lin_attn_chunk_fwd_channel_workspace_size(2, 17, 3, 64, 32, 1) == 2 * 3 * 2 * 14592
+    assert L.lin_attn_chunk_fwd_channel_workspace_size(1, 0, 2, 128, 128, 0) == 0
+    assert L.lin_attn_chunk_fwd_channel_workspace_size(1, 64, 2, 96, 128, 0) == -1
