@@ -122,6 +122,58 @@ __device__ inline void load_tile(float (*dst)[D + 1], const E* src, int b, int c
   }
 }
 
+// The same tile rows in two steps: fetch() issues this thread's share of the
+// loads (8 consecutive elements of one row; threads beyond the tile's
+// 16 * D / 8 pieces hold nothing), put() stores them into LDS.  Splitting the
+// two lets a serial loop issue tile c + 1's loads before working on tile c.
+template <typename E, int D>
+struct TilePiece {
+  float f[8];
+  __device__ inline void fetch(const E* src, int b, int c, int h, const BwdArgs& a) {
+    constexpr int PER_ROW = D / 8;
+    static_assert(kT * PER_ROW <= kBwdThreads, "one piece per thread");
+    const int x = threadIdx.x;
+    const int tok = c * kT + x / PER_ROW;
+    if (x < kT * PER_ROW && tok < a.T) {
+      Ld8<E>::run(src + (((int64_t)b * a.T + tok) * a.H + h) * D + (x % PER_ROW) * 8, f);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) f[i] = 0.f;
+    }
+  }
+  __device__ inline void put(float (*dst)[D + 1]) const {
+    constexpr int PER_ROW = D / 8;
+    const int x = threadIdx.x;
+    if (x < kT * PER_ROW) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dst[x / PER_ROW][(x % PER_ROW) * 8 + i] = f[i];
+    }
+  }
+};
+
+// A tile's per-token scalars from its record, fetched ahead: g and beta for
+// threads < 16, the tile's total decay sum for all.
+struct TileScalars {
+  float g, bt, gC;
+  __device__ inline void fetch(const float* rec) {
+    const int tid = threadIdx.x;
+    g = tid < kT ? rec[BRec::G + tid] : 0.f;
+    bt = tid < kT ? rec[BRec::BETA + tid] : 0.f;
+    gC = rec[BRec::G + kT - 1];
+  }
+  // the values load_scalars would produce
+  __device__ inline void put(float* sG, float* sB, float* sGam, float* sEc, float& gamC) const {
+    const int tid = threadIdx.x;
+    if (tid < kT) {
+      sG[tid] = g;
+      sB[tid] = bt;
+      sGam[tid] = __expf(g);
+      sEc[tid] = __expf(gC - g);
+    }
+    gamC = __expf(gC);
+  }
+};
+
 __device__ inline float gate_at(const BwdArgs& a, int64_t idx) {
   const float x = a.gate[idx];
   return a.gate_logit ? bounded_gate(x, a.G) : x;
@@ -223,6 +275,20 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_hstates_kernel(BwdArgs a) {
   for (int x = 0; x < CPT; ++x)
     Hr[x] = a.h0 ? a.h0[(bh * DK + r) * a.Dv + col + j0 + x] : 0.f;
   const E* vp = static_cast<const E*>(a.v);
+  const E* kp = static_cast<const E*>(a.k);
+  // tile c's loads, issued during tile c - 1
+  TilePiece<E, DK> nk;
+  TileScalars ns;
+  float ntinv, nv;
+  auto fetch = [&](int c) {
+    const float* rec = a.rec + (bh * a.NT + c) * BRec::FLOATS;
+    nk.fetch(kp, b, c, h, a);
+    ns.fetch(rec);
+    ntinv = rec[BRec::TINV + tid];
+    const int tok = c * kT + t;
+    nv = tok < a.T ? ld1(vp + (((int64_t)b * a.T + tok) * a.H + h) * a.Dv + col + j) : 0.f;
+  };
+  fetch(0);
   for (int c = 0; c < a.NT; ++c) {
     float* hsp = a.hs + ((bh * a.NT + c) * DK + r) * a.Dv + col + j0;
 #pragma unroll
@@ -230,13 +296,12 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_hstates_kernel(BwdArgs a) {
       hsp[x] = Hr[x];
       sH[r][j0 + x] = Hr[x];
     }
-    const float* rec = a.rec + (bh * a.NT + c) * BRec::FLOATS;
-    load_tile<E, DK>(sK, static_cast<const E*>(a.k), b, c, h, a);
-    sTi[t][j] = rec[BRec::TINV + tid];
+    nk.put(sK);
+    sTi[t][j] = ntinv;
     float gamC;
-    load_scalars(rec, sG, sB, sGam, sEc, gamC);
-    const int tok = c * kT + t;
-    const float vv = tok < a.T ? ld1(vp + (((int64_t)b * a.T + tok) * a.H + h) * a.Dv + col + j) : 0.f;
+    ns.put(sG, sB, sGam, sEc, gamC);
+    const float vv = nv;
+    if (c + 1 < a.NT) fetch(c + 1);
     __syncthreads();
     float R = 0.f;
 #pragma unroll 8
@@ -280,6 +345,23 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dh_kernel(BwdArgs a) {
   for (int x = 0; x < CPT; ++x)
     D[x] = a.dhT ? a.dhT[(bh * DK + r) * a.Dv + col + j0 + x] : 0.f;
   const E* dop = static_cast<const E*>(a.dout);
+  const E* kp = static_cast<const E*>(a.k);
+  const E* qp = static_cast<const E*>(a.q);
+  // tile c's loads, issued during tile c + 1
+  TilePiece<E, DK> nk, nq;
+  TileScalars ns;
+  float ntinv, np, ndo;
+  auto fetch = [&](int c) {
+    const float* rec = a.rec + (bh * a.NT + c) * BRec::FLOATS;
+    nk.fetch(kp, b, c, h, a);
+    nq.fetch(qp, b, c, h, a);
+    ns.fetch(rec);
+    ntinv = rec[BRec::TINV + tid];
+    np = rec[BRec::P + tid];
+    const int tok = c * kT + t;
+    ndo = tok < a.T ? ld1(dop + (((int64_t)b * a.T + tok) * a.H + h) * a.Dv + col + j) : 0.f;
+  };
+  if (a.NT > 0) fetch(a.NT - 1);
   for (int c = a.NT - 1; c >= 0; --c) {
     float* dsp = a.dhs + ((bh * a.NT + c) * DK + r) * a.Dv + col + j0;
 #pragma unroll
@@ -287,15 +369,14 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dh_kernel(BwdArgs a) {
       dsp[x] = D[x];
       sD[r][j0 + x] = D[x];
     }
-    const float* rec = a.rec + (bh * a.NT + c) * BRec::FLOATS;
-    load_tile<E, DK>(sK, static_cast<const E*>(a.k), b, c, h, a);
-    load_tile<E, DK>(sQ, static_cast<const E*>(a.q), b, c, h, a);
-    sTi[t][j] = rec[BRec::TINV + tid];
-    sP[t][j] = rec[BRec::P + tid];
+    nk.put(sK);
+    nq.put(sQ);
+    sTi[t][j] = ntinv;
+    sP[t][j] = np;
     float gamC;
-    load_scalars(rec, sG, sB, sGam, sEc, gamC);
-    const int tok = c * kT + t;
-    sDO[t][j] = tok < a.T ? ld1(dop + (((int64_t)b * a.T + tok) * a.H + h) * a.Dv + col + j) : 0.f;
+    ns.put(sG, sB, sGam, sEc, gamC);
+    sDO[t][j] = ndo;
+    if (c > 0) fetch(c - 1);
     __syncthreads();
     float KdH = 0.f;
 #pragma unroll 8
@@ -349,7 +430,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grad_kernel(BwdArgs a) {
   const int64_t bh = tile / a.NT;
   const int h = (int)(bh % a.H), b = (int)(bh / a.H);
   const int t = tid >> 4, j = tid & 15;        // (token, column) or (token, token)
-  const int r0 = j * RB;                        // dq / dk rows of this thread
+  // dq / dk rows of this thread: j, j + 16, ..., so the 16 threads of a token
+  // read 16 different LDS banks of a state slice and store 16 adjacent floats
   const float* rec = a.rec + tile * BRec::FLOATS;
   load_tile<E, DK>(sK, static_cast<const E*>(a.k), b, c, h, a);
   load_tile<E, DK>(sQ, static_cast<const E*>(a.q), b, c, h, a);
@@ -422,12 +504,12 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grad_kernel(BwdArgs a) {
       dPacc += p;
       dAacc -= q;
     }
-    // (t, rows r0 ..): dQ += gamma dO H^T; dK += -beta gamma dY H^T + ec U dH'^T
+    // (t, rows j + 16x): dQ += gamma dO H^T; dK += -beta gamma dY H^T + ec U dH'^T
     {
       const float gq = sGam[t], gk = -sB[t] * sGam[t], ek = sEc[t];
 #pragma unroll
       for (int x = 0; x < RB; ++x) {
-        const int rr = r0 + x;
+        const int rr = j + 16 * x;
         float oh = 0.f, yh = 0.f, ud = 0.f;
         for (int jj = 0; jj < 16; ++jj) {
           oh += sDO[t][jj] * sH[rr][jj];
@@ -465,7 +547,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grad_kernel(BwdArgs a) {
   __syncthreads();
 #pragma unroll
   for (int x = 0; x < RB; ++x) {
-    const int rr = r0 + x;
+    const int rr = j + 16 * x;
     float q1 = 0.f, k1 = 0.f;
     for (int i = 0; i < kT; ++i) {
       q1 += sPE[t][i] * sK[i][rr];
@@ -475,12 +557,12 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grad_kernel(BwdArgs a) {
     dK[x] += k1;
   }
   if (live) {
-    float* dqp = a.dq + row_idx * DK + r0;
-    float* dkp = a.dk + row_idx * DK + r0;
+    float* dqp = a.dq + row_idx * DK + j;
+    float* dkp = a.dk + row_idx * DK + j;
 #pragma unroll
     for (int x = 0; x < RB; ++x) {
-      dqp[x] = dQ[x];
-      dkp[x] = dK[x];
+      dqp[16 * x] = dQ[x];
+      dkp[16 * x] = dK[x];
     }
   }
   if (tid < kT) {
