@@ -26,9 +26,10 @@
 //
 // Four kernels:
 //   bwd_prep_kernel     per tile: G, beta, T, P and E*KK^T into a record;
-//   bwd_hstates_kernel  per (sequence, head, 16 columns of d_v), serial over
-//                       tiles: the state at every tile start;
-//   bwd_dh_kernel       same split, serial backwards: dH' at every tile end,
+//   bwd_hstates_mfma_kernel  per (sequence, head, 16 columns of d_v), serial
+//                       over tiles on the fp32 MFMA: the state at every tile
+//                       start;
+//   bwd_dh_mfma_kernel  same split, serial backwards: dH' at every tile end,
 //                       and dh0;
 //   bwd_grad_kernel     per tile, all of d_v: dq, dk, dv, dbeta, dg.
 #include <hip/hip_runtime.h>
@@ -122,58 +123,6 @@ __device__ inline void load_tile(float (*dst)[D + 1], const E* src, int b, int c
   }
 }
 
-// The same tile rows in two steps: fetch() issues this thread's share of the
-// loads (8 consecutive elements of one row; threads beyond the tile's
-// 16 * D / 8 pieces hold nothing), put() stores them into LDS.  Splitting the
-// two lets a serial loop issue tile c + 1's loads before working on tile c.
-template <typename E, int D>
-struct TilePiece {
-  float f[8];
-  __device__ inline void fetch(const E* src, int b, int c, int h, const BwdArgs& a) {
-    constexpr int PER_ROW = D / 8;
-    static_assert(kT * PER_ROW <= kBwdThreads, "one piece per thread");
-    const int x = threadIdx.x;
-    const int tok = c * kT + x / PER_ROW;
-    if (x < kT * PER_ROW && tok < a.T) {
-      Ld8<E>::run(src + (((int64_t)b * a.T + tok) * a.H + h) * D + (x % PER_ROW) * 8, f);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) f[i] = 0.f;
-    }
-  }
-  __device__ inline void put(float (*dst)[D + 1]) const {
-    constexpr int PER_ROW = D / 8;
-    const int x = threadIdx.x;
-    if (x < kT * PER_ROW) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) dst[x / PER_ROW][(x % PER_ROW) * 8 + i] = f[i];
-    }
-  }
-};
-
-// A tile's per-token scalars from its record, fetched ahead: g and beta for
-// threads < 16, the tile's total decay sum for all.
-struct TileScalars {
-  float g, bt, gC;
-  __device__ inline void fetch(const float* rec) {
-    const int tid = threadIdx.x;
-    g = tid < kT ? rec[BRec::G + tid] : 0.f;
-    bt = tid < kT ? rec[BRec::BETA + tid] : 0.f;
-    gC = rec[BRec::G + kT - 1];
-  }
-  // the values load_scalars would produce
-  __device__ inline void put(float* sG, float* sB, float* sGam, float* sEc, float& gamC) const {
-    const int tid = threadIdx.x;
-    if (tid < kT) {
-      sG[tid] = g;
-      sB[tid] = bt;
-      sGam[tid] = __expf(g);
-      sEc[tid] = __expf(gC - g);
-    }
-    gamC = __expf(gC);
-  }
-};
-
 __device__ inline float gate_at(const BwdArgs& a, int64_t idx) {
   const float x = a.gate[idx];
   return a.gate_logit ? bounded_gate(x, a.G) : x;
@@ -252,155 +201,426 @@ __device__ inline void load_scalars(const float* rec, float* sG, float* sB, floa
   gamC = __expf(rec[BRec::G + kT - 1]);
 }
 
-// ------------------------------------------------- states at every tile start
+// ----------------------- states at every tile start, on the matrix cores
+// One workgroup per sequence, head and 16 columns of d_v, serial over tiles,
+// the products on the fp32 MFMA: wave 0 ("chain") keeps the fp32 state slice H (d_k x 16) in
+// registers, in accumulator order (lane (n, grp) register i of tile t holds
+// H[16t + 4grp + i][n]); per tile it stores H, then
+//   R = K H,  Y = diag(beta) (V - diag(gamma) R),  U = T Y,
+//   H' = gamma_C H + K^T diag(ec) U.
+// Waves 1..NP ("loaders") stage tiles in LDS -- K as A fragments and as K^T
+// fragments, T, the slice of V, gamma, ec, beta, gamma_C -- double-buffered by
+// epochs of NP tiles, their global loads issued two epochs ahead.
+template <int DK>
+struct HsRec {
+  static constexpr int NS = DK / 32, NT = DK / 16;
+  static constexpr int KF = 0;                     // K: NS x 64 lanes x 8 f32
+  static constexpr int KT = KF + NS * 64 * 8 * 4;  // K^T: NT x 64 x 4
+  static constexpr int TI = KT + NT * 64 * 4 * 4;  // T: 16 x 16 row-major
+  static constexpr int VF = TI + 256 * 4;          // V slice: 64 x 4
+  static constexpr int GM = VF + 64 * 4 * 4;       // gamma[16]
+  static constexpr int EC = GM + 64;               // ec[16]
+  static constexpr int BT = EC + 64;               // beta[16]
+  static constexpr int GC = BT + 64;               // gamma_C (x4)
+  static constexpr int BYTES = GC + 16;
+  static_assert(BYTES % 16 == 0, "alignment");
+};
+
+// A 32-deep fragment's 8 elements as fp32 (lo = j 0..3, hi = j 4..7).
+__device__ inline Elt<float>::F32 frag_f32(const Elt<float>::F32& x) { return x; }
+__device__ inline Elt<float>::F32 frag_f32(const Elt<__bf16>::F32& x) {
+  Elt<float>::F32 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    r.lo[j] = (float)x.v[j];
+    r.hi[j] = (float)x.v[4 + j];
+  }
+  return r;
+}
+
 template <typename E, int DK>
-__global__ __launch_bounds__(kBwdThreads) void bwd_hstates_kernel(BwdArgs a) {
-  constexpr int TPR = kBwdThreads / DK;   // threads per state row
-  constexpr int CPT = 16 / TPR;           // columns per thread
-  __shared__ float sK[kT][DK + 1];
-  __shared__ float sH[DK][17];
-  __shared__ float sY[kT][17], sU[kT][17];
-  __shared__ float sTi[kT][kT + 1];
-  __shared__ float sG[kT], sB[kT], sGam[kT], sEc[kT];
-  const int tid = threadIdx.x;
+struct HsRaw {
+  typename Elt<E>::F32 kf[DK / 32];
+  f32x4 ti;
+  E vv[4];
+  float g, bt, gC;
+};
+
+template <typename E, int DK, int NP>
+__global__ __launch_bounds__(64 * (NP + 1)) void bwd_hstates_mfma_kernel(BwdArgs a) {
+  using R = HsRec<DK>;
+  using X = Elt<float>;
+  using F16 = X::F16;
+  using F32 = X::F32;
+  constexpr int NS = R::NS, NT = R::NT;
+  __shared__ __attribute__((aligned(16))) char smem[2 * NP * R::BYTES];
   const int NV = a.Dv / 16;
   const int sl = (int)(blockIdx.x % NV);
   const int64_t bh = blockIdx.x / NV;
   const int h = (int)(bh % a.H), b = (int)(bh / a.H);
-  const int r = tid / TPR, j0 = (tid % TPR) * CPT;
-  const int t = tid >> 4, j = tid & 15;
-  const int col = 16 * sl;
-  float Hr[CPT];
+  const int v0 = 16 * sl;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15, grp = lane >> 4;
+  const int NC = a.NT;
+  const int NE = (NC + NP - 1) / NP;
+  auto rec_of = [&](int c) -> char* { return smem + (((c / NP) & 1) * NP + c % NP) * R::BYTES; };
+
+  if (wave == 0) {
+    f32x4 Hacc[NT];
 #pragma unroll
-  for (int x = 0; x < CPT; ++x)
-    Hr[x] = a.h0 ? a.h0[(bh * DK + r) * a.Dv + col + j0 + x] : 0.f;
-  const E* vp = static_cast<const E*>(a.v);
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        Hacc[t][i] = a.h0 ? a.h0[(bh * DK + 16 * t + 4 * grp + i) * a.Dv + v0 + n] : 0.f;
+    }
+    __syncthreads();  // epoch 0 staged
+    for (int ep = 0; ep < NE; ++ep) {
+      for (int j = 0; j < NP; ++j) {
+        const int c = ep * NP + j;
+        if (c >= NC) break;
+        const char* rec = rec_of(c);
+        float* hsp = a.hs + (bh * NC + c) * (int64_t)DK * a.Dv + v0 + n;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) hsp[(int64_t)(16 * t + 4 * grp + i) * a.Dv] = Hacc[t][i];
+        }
+        f32x4 Rk = zero4();
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const F32 kf = reinterpret_cast<const F32*>(rec + R::KF)[s * 64 + lane];
+          Rk = X::mma32(kf, X::from_acc2(Hacc[2 * s], Hacc[2 * s + 1]), Rk);
+        }
+        const f32x4 vf = reinterpret_cast<const f32x4*>(rec + R::VF)[lane];
+        const f32x4 gm = reinterpret_cast<const f32x4*>(rec + R::GM)[grp];
+        const f32x4 ec = reinterpret_cast<const f32x4*>(rec + R::EC)[grp];
+        const f32x4 bt = reinterpret_cast<const f32x4*>(rec + R::BT)[grp];
+        const float gC = *reinterpret_cast<const float*>(rec + R::GC);
+        f32x4 Y;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Y[i] = bt[i] * (vf[i] - gm[i] * Rk[i]);
+        const F16 ti = *reinterpret_cast<const F16*>(rec + R::TI + (n * 16 + 4 * grp) * 4);
+        const f32x4 U = X::mma16(ti, X::from_acc(Y), zero4());
+        f32x4 Up;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Up[i] = ec[i] * U[i];
+        const F16 ub = X::from_acc(Up);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const F16 kt = reinterpret_cast<const F16*>(rec + R::KT)[t * 64 + lane];
+          Hacc[t] = Hacc[t] * gC;
+          Hacc[t] = X::mma16(kt, ub, Hacc[t]);
+        }
+      }
+      __syncthreads();  // this epoch consumed, the next one staged
+    }
+    return;
+  }
+
+  // ---------------------------------------------------------------- loaders
+  const int p = wave - 1;
   const E* kp = static_cast<const E*>(a.k);
-  // tile c's loads, issued during tile c - 1
-  TilePiece<E, DK> nk;
-  TileScalars ns;
-  float ntinv, nv;
-  auto fetch = [&](int c) {
-    const float* rec = a.rec + (bh * a.NT + c) * BRec::FLOATS;
-    nk.fetch(kp, b, c, h, a);
-    ns.fetch(rec);
-    ntinv = rec[BRec::TINV + tid];
-    const int tok = c * kT + t;
-    nv = tok < a.T ? ld1(vp + (((int64_t)b * a.T + tok) * a.H + h) * a.Dv + col + j) : 0.f;
+  const E* vp = static_cast<const E*>(a.v);
+  auto rowk = [&](int t) -> int64_t { return ((int64_t)b * a.T + t) * a.H + h; };
+  auto load = [&](HsRaw<E, DK>& r, int c) {
+    c = min(c, NC - 1);
+    const int t = min(c * kT + n, a.T - 1);
+    const int64_t base = rowk(t) * DK;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int c0 = 32 * s + 4 * grp, c1 = c0 + 16;
+      if constexpr (sizeof(E) == 2) {
+        const bf16x4 k0 = *reinterpret_cast<const bf16x4*>(kp + base + c0);
+        const bf16x4 k1 = *reinterpret_cast<const bf16x4*>(kp + base + c1);
+        r.kf[s].v = bf16x8{k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
+      } else {
+        r.kf[s].lo = *reinterpret_cast<const f32x4*>(kp + base + c0);
+        r.kf[s].hi = *reinterpret_cast<const f32x4*>(kp + base + c1);
+      }
+    }
+    const float* rec = a.rec + (bh * NC + c) * BRec::FLOATS;
+    r.ti = reinterpret_cast<const f32x4*>(rec + BRec::TINV)[lane];
+    r.g = rec[BRec::G + n];
+    r.bt = rec[BRec::BETA + n];
+    r.gC = rec[BRec::G + kT - 1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.vv[i] = vp[rowk(min(c * kT + 4 * grp + i, a.T - 1)) * a.Dv + v0 + n];
   };
-  fetch(0);
-  for (int c = 0; c < a.NT; ++c) {
-    float* hsp = a.hs + ((bh * a.NT + c) * DK + r) * a.Dv + col + j0;
+  auto store = [&](const HsRaw<E, DK>& r, int c) {
+    if (c >= NC) return;
+    char* rec = rec_of(c);
+    const bool ok = c * kT + n < a.T;        // token row n of this tile exists
 #pragma unroll
-    for (int x = 0; x < CPT; ++x) {
-      hsp[x] = Hr[x];
-      sH[r][j0 + x] = Hr[x];
-    }
-    nk.put(sK);
-    sTi[t][j] = ntinv;
-    float gamC;
-    ns.put(sG, sB, sGam, sEc, gamC);
-    const float vv = nv;
-    if (c + 1 < a.NT) fetch(c + 1);
-    __syncthreads();
-    float R = 0.f;
-#pragma unroll 8
-    for (int rr = 0; rr < DK; ++rr) R += sK[t][rr] * sH[rr][j];
-    sY[t][j] = sB[t] * (vv - sGam[t] * R);
-    __syncthreads();
-    float U = 0.f;
-    for (int i = 0; i <= t; ++i) U += sTi[t][i] * sY[i][j];
-    sU[t][j] = U;
-    __syncthreads();
+    for (int s = 0; s < NS; ++s) {
+      F32 k32 = frag_f32(r.kf[s]);
 #pragma unroll
-    for (int x = 0; x < CPT; ++x) {
-      float acc = gamC * Hr[x];
-      for (int i = 0; i < kT; ++i) acc += sEc[i] * sK[i][r] * sU[i][j0 + x];
-      Hr[x] = acc;
+      for (int jj = 0; jj < 4; ++jj) {
+        k32.lo[jj] = ok ? k32.lo[jj] : 0.f;
+        k32.hi[jj] = ok ? k32.hi[jj] : 0.f;
+      }
+      reinterpret_cast<F32*>(rec + R::KF)[s * 64 + lane] = k32;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int ch = 32 * s + (jj < 4 ? 4 * grp + jj : 16 + 4 * grp + jj - 4);
+        const float kv = jj < 4 ? k32.lo[jj] : k32.hi[jj - 4];
+        // K^T in the chain's A-fragment order: tile ch / 16, lane (ch % 16, n / 4), register n % 4
+        reinterpret_cast<float*>(rec + R::KT)[((ch >> 4) * 64 + (n >> 2) * 16 + (ch & 15)) * 4 +
+                                              (n & 3)] = kv;
+      }
     }
+    reinterpret_cast<f32x4*>(rec + R::TI)[lane] = r.ti;
+    f32x4 vf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vf[i] = (c * kT + 4 * grp + i < a.T) ? Elt<E>::to_f(r.vv[i]) : 0.f;
+    reinterpret_cast<f32x4*>(rec + R::VF)[lane] = vf;
+    if (grp == 0) {
+      reinterpret_cast<float*>(rec + R::GM)[n] = __expf(r.g);
+      reinterpret_cast<float*>(rec + R::EC)[n] = __expf(r.gC - r.g);
+      reinterpret_cast<float*>(rec + R::BT)[n] = r.bt;
+      if (n == 0) *reinterpret_cast<float*>(rec + R::GC) = __expf(r.gC);
+    }
+  };
+  HsRaw<E, DK> ra, rb;
+  load(ra, p);
+  store(ra, p);                 // epoch 0
+  load(ra, NP + p);             // epoch 1, staged during epoch 0
+  __syncthreads();
+  for (int ep = 0; ep < NE; ep += 2) {
+    load(rb, (ep + 2) * NP + p);
+    store(ra, (ep + 1) * NP + p);
     __syncthreads();
+    if (ep + 1 < NE) {
+      load(ra, (ep + 3) * NP + p);
+      store(rb, (ep + 2) * NP + p);
+      __syncthreads();
+    }
   }
 }
 
-// ------------------------------------- gradients of every tile's end state
+// --------------- gradients of every tile's end state, on the matrix cores
+// One workgroup per sequence, head and 16 columns of d_v, tiles from last to
+// first, the products on the fp32 MFMA: wave 0 keeps D = dL/dH' of the current tile (d_k x 16) in
+// registers in accumulator order; per tile it stores D, then
+//   dU = diag(ec) K D + P^T dO,  dY = T^T dU,
+//   D' = gamma_C D + Q^T diag(gamma) dO - K^T diag(beta gamma) dY,
+// and after the first tile writes dh0.  Loader waves stage K (A fragments and
+// K^T fragments), Q^T fragments, P^T, T^T, the slice of dO and the per-token
+// factors, double-buffered by epochs in processing order (m = 0 is the last
+// tile).
+template <int DK>
+struct HdRec {
+  static constexpr int NS = DK / 32, NT = DK / 16;
+  static constexpr int KF = 0;                     // K: NS x 64 lanes x 8 f32
+  static constexpr int KT = KF + NS * 64 * 8 * 4;  // K^T: NT x 64 x 4
+  static constexpr int QT = KT + NT * 64 * 4 * 4;  // Q^T: NT x 64 x 4
+  static constexpr int PT = QT + NT * 64 * 4 * 4;  // P^T: 16 x 16 row-major
+  static constexpr int TT = PT + 256 * 4;          // T^T: 16 x 16 row-major
+  static constexpr int DO = TT + 256 * 4;          // dO slice: 64 x 4
+  static constexpr int GM = DO + 64 * 4 * 4;       // gamma[16]
+  static constexpr int EC = GM + 64;               // ec[16]
+  static constexpr int BT = EC + 64;               // beta[16]
+  static constexpr int GC = BT + 64;               // gamma_C (x4)
+  static constexpr int BYTES = GC + 16;
+  static_assert(BYTES % 16 == 0, "alignment");
+};
+
 template <typename E, int DK>
-__global__ __launch_bounds__(kBwdThreads) void bwd_dh_kernel(BwdArgs a) {
-  constexpr int TPR = kBwdThreads / DK;
-  constexpr int CPT = 16 / TPR;
-  __shared__ float sK[kT][DK + 1], sQ[kT][DK + 1];
-  __shared__ float sD[DK][17];
-  __shared__ float sDO[kT][17], sDU[kT][17], sZ[kT][17], sOg[kT][17];
-  __shared__ float sTi[kT][kT + 1], sP[kT][kT + 1];
-  __shared__ float sG[kT], sB[kT], sGam[kT], sEc[kT];
-  const int tid = threadIdx.x;
+struct HdRaw {
+  typename Elt<E>::F32 kf[DK / 32];
+  typename Elt<E>::F32 qf[DK / 32];
+  f32x4 pm, tm;
+  E dd[4];
+  float g, bt, gC;
+};
+
+template <typename E, int DK, int NP>
+__global__ __launch_bounds__(64 * (NP + 1)) void bwd_dh_mfma_kernel(BwdArgs a) {
+  using R = HdRec<DK>;
+  using X = Elt<float>;
+  using F16 = X::F16;
+  using F32 = X::F32;
+  constexpr int NS = R::NS, NT = R::NT;
+  __shared__ __attribute__((aligned(16))) char smem[2 * NP * R::BYTES];
   const int NV = a.Dv / 16;
   const int sl = (int)(blockIdx.x % NV);
   const int64_t bh = blockIdx.x / NV;
   const int h = (int)(bh % a.H), b = (int)(bh / a.H);
-  const int r = tid / TPR, j0 = (tid % TPR) * CPT;
-  const int t = tid >> 4, j = tid & 15;
-  const int col = 16 * sl;
-  float D[CPT];
+  const int v0 = 16 * sl;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15, grp = lane >> 4;
+  const int NC = a.NT;
+  const int NE = (NC + NP - 1) / NP;
+  // records by processing index m (tile NC - 1 - m)
+  auto rec_of = [&](int m) -> char* { return smem + (((m / NP) & 1) * NP + m % NP) * R::BYTES; };
+
+  if (wave == 0) {
+    f32x4 D[NT];
 #pragma unroll
-  for (int x = 0; x < CPT; ++x)
-    D[x] = a.dhT ? a.dhT[(bh * DK + r) * a.Dv + col + j0 + x] : 0.f;
-  const E* dop = static_cast<const E*>(a.dout);
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        D[t][i] = a.dhT ? a.dhT[(bh * DK + 16 * t + 4 * grp + i) * a.Dv + v0 + n] : 0.f;
+    }
+    __syncthreads();  // epoch 0 staged
+    for (int ep = 0; ep < NE; ++ep) {
+      for (int j = 0; j < NP; ++j) {
+        const int m = ep * NP + j;
+        if (m >= NC) break;
+        const int c = NC - 1 - m;
+        const char* rec = rec_of(m);
+        float* dsp = a.dhs + (bh * NC + c) * (int64_t)DK * a.Dv + v0 + n;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dsp[(int64_t)(16 * t + 4 * grp + i) * a.Dv] = D[t][i];
+        }
+        f32x4 KD = zero4();
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const F32 kf = reinterpret_cast<const F32*>(rec + R::KF)[s * 64 + lane];
+          KD = X::mma32(kf, X::from_acc2(D[2 * s], D[2 * s + 1]), KD);
+        }
+        const f32x4 dO = reinterpret_cast<const f32x4*>(rec + R::DO)[lane];
+        const f32x4 gm = reinterpret_cast<const f32x4*>(rec + R::GM)[grp];
+        const f32x4 ec = reinterpret_cast<const f32x4*>(rec + R::EC)[grp];
+        const f32x4 bt = reinterpret_cast<const f32x4*>(rec + R::BT)[grp];
+        const float gC = *reinterpret_cast<const float*>(rec + R::GC);
+        f32x4 eKD;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) eKD[i] = ec[i] * KD[i];
+        const F16 pt = *reinterpret_cast<const F16*>(rec + R::PT + (n * 16 + 4 * grp) * 4);
+        const F16 tt = *reinterpret_cast<const F16*>(rec + R::TT + (n * 16 + 4 * grp) * 4);
+        const f32x4 dU = X::mma16(pt, X::from_acc(dO), eKD);
+        const f32x4 dY = X::mma16(tt, X::from_acc(dU), zero4());
+        f32x4 nZ, Og;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          nZ[i] = -(bt[i] * gm[i] * dY[i]);
+          Og[i] = gm[i] * dO[i];
+        }
+        const F16 zb = X::from_acc(nZ), ob = X::from_acc(Og);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const F16 qt = reinterpret_cast<const F16*>(rec + R::QT)[t * 64 + lane];
+          const F16 kt = reinterpret_cast<const F16*>(rec + R::KT)[t * 64 + lane];
+          D[t] = D[t] * gC;
+          D[t] = X::mma16(qt, ob, D[t]);
+          D[t] = X::mma16(kt, zb, D[t]);
+        }
+      }
+      __syncthreads();  // this epoch consumed, the next one staged
+    }
+    if (a.dh0) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          a.dh0[(bh * DK + 16 * t + 4 * grp + i) * a.Dv + v0 + n] = D[t][i];
+      }
+    }
+    return;
+  }
+
+  // ---------------------------------------------------------------- loaders
+  const int p = wave - 1;
   const E* kp = static_cast<const E*>(a.k);
   const E* qp = static_cast<const E*>(a.q);
-  // tile c's loads, issued during tile c + 1
-  TilePiece<E, DK> nk, nq;
-  TileScalars ns;
-  float ntinv, np, ndo;
-  auto fetch = [&](int c) {
-    const float* rec = a.rec + (bh * a.NT + c) * BRec::FLOATS;
-    nk.fetch(kp, b, c, h, a);
-    nq.fetch(qp, b, c, h, a);
-    ns.fetch(rec);
-    ntinv = rec[BRec::TINV + tid];
-    np = rec[BRec::P + tid];
-    const int tok = c * kT + t;
-    ndo = tok < a.T ? ld1(dop + (((int64_t)b * a.T + tok) * a.H + h) * a.Dv + col + j) : 0.f;
+  const E* dp = static_cast<const E*>(a.dout);
+  auto rowk = [&](int t) -> int64_t { return ((int64_t)b * a.T + t) * a.H + h; };
+  auto load = [&](HdRaw<E, DK>& r, int m) {
+    const int c = NC - 1 - min(m, NC - 1);
+    const int t = min(c * kT + n, a.T - 1);
+    const int64_t base = rowk(t) * DK;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int c0 = 32 * s + 4 * grp, c1 = c0 + 16;
+      if constexpr (sizeof(E) == 2) {
+        const bf16x4 k0 = *reinterpret_cast<const bf16x4*>(kp + base + c0);
+        const bf16x4 k1 = *reinterpret_cast<const bf16x4*>(kp + base + c1);
+        const bf16x4 q0 = *reinterpret_cast<const bf16x4*>(qp + base + c0);
+        const bf16x4 q1 = *reinterpret_cast<const bf16x4*>(qp + base + c1);
+        r.kf[s].v = bf16x8{k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
+        r.qf[s].v = bf16x8{q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
+      } else {
+        r.kf[s].lo = *reinterpret_cast<const f32x4*>(kp + base + c0);
+        r.kf[s].hi = *reinterpret_cast<const f32x4*>(kp + base + c1);
+        r.qf[s].lo = *reinterpret_cast<const f32x4*>(qp + base + c0);
+        r.qf[s].hi = *reinterpret_cast<const f32x4*>(qp + base + c1);
+      }
+    }
+    const float* rec = a.rec + (bh * NC + c) * BRec::FLOATS;
+    r.pm = reinterpret_cast<const f32x4*>(rec + BRec::P)[lane];
+    r.tm = reinterpret_cast<const f32x4*>(rec + BRec::TINV)[lane];
+    r.g = rec[BRec::G + n];
+    r.bt = rec[BRec::BETA + n];
+    r.gC = rec[BRec::G + kT - 1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.dd[i] = dp[rowk(min(c * kT + 4 * grp + i, a.T - 1)) * a.Dv + v0 + n];
   };
-  if (a.NT > 0) fetch(a.NT - 1);
-  for (int c = a.NT - 1; c >= 0; --c) {
-    float* dsp = a.dhs + ((bh * a.NT + c) * DK + r) * a.Dv + col + j0;
+  auto store = [&](const HdRaw<E, DK>& r, int m) {
+    if (m >= NC) return;
+    const int c = NC - 1 - m;
+    char* rec = rec_of(m);
+    const bool ok = c * kT + n < a.T;        // token row n of this tile exists
+    float* kt = reinterpret_cast<float*>(rec + R::KT);
+    float* qt = reinterpret_cast<float*>(rec + R::QT);
 #pragma unroll
-    for (int x = 0; x < CPT; ++x) {
-      dsp[x] = D[x];
-      sD[r][j0 + x] = D[x];
+    for (int s = 0; s < NS; ++s) {
+      F32 k32 = frag_f32(r.kf[s]), q32 = frag_f32(r.qf[s]);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        k32.lo[jj] = ok ? k32.lo[jj] : 0.f;
+        k32.hi[jj] = ok ? k32.hi[jj] : 0.f;
+        q32.lo[jj] = ok ? q32.lo[jj] : 0.f;
+        q32.hi[jj] = ok ? q32.hi[jj] : 0.f;
+      }
+      reinterpret_cast<F32*>(rec + R::KF)[s * 64 + lane] = k32;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int ch = 32 * s + (jj < 4 ? 4 * grp + jj : 16 + 4 * grp + jj - 4);
+        // transposed A fragments: tile ch / 16, lane (ch % 16, n / 4), register n % 4
+        const int at = ((ch >> 4) * 64 + (n >> 2) * 16 + (ch & 15)) * 4 + (n & 3);
+        kt[at] = jj < 4 ? k32.lo[jj] : k32.hi[jj - 4];
+        qt[at] = jj < 4 ? q32.lo[jj] : q32.hi[jj - 4];
+      }
     }
-    nk.put(sK);
-    nq.put(sQ);
-    sTi[t][j] = ntinv;
-    sP[t][j] = np;
-    float gamC;
-    ns.put(sG, sB, sGam, sEc, gamC);
-    sDO[t][j] = ndo;
-    if (c > 0) fetch(c - 1);
-    __syncthreads();
-    float KdH = 0.f;
-#pragma unroll 8
-    for (int rr = 0; rr < DK; ++rr) KdH += sK[t][rr] * sD[rr][j];
-    float dU = sEc[t] * KdH;
-    for (int s = t; s < kT; ++s) dU += sP[s][t] * sDO[s][j];
-    sDU[t][j] = dU;
-    sOg[t][j] = sGam[t] * sDO[t][j];
-    __syncthreads();
-    float dY = 0.f;
-    for (int s = t; s < kT; ++s) dY += sTi[s][t] * sDU[s][j];
-    sZ[t][j] = sB[t] * sGam[t] * dY;
-    __syncthreads();
+    // P and T arrive row-major (lane l holds row l / 4, columns 4 (l % 4) ..);
+    // store them transposed
+    float* pt = reinterpret_cast<float*>(rec + R::PT);
+    float* tt = reinterpret_cast<float*>(rec + R::TT);
+    const int row = lane >> 2, col = 4 * (lane & 3);
 #pragma unroll
-    for (int x = 0; x < CPT; ++x) {
-      float acc = gamC * D[x];
-      for (int s = 0; s < kT; ++s) acc += sQ[s][r] * sOg[s][j0 + x] - sK[s][r] * sZ[s][j0 + x];
-      D[x] = acc;
+    for (int i = 0; i < 4; ++i) {
+      pt[(col + i) * 16 + row] = r.pm[i];
+      tt[(col + i) * 16 + row] = r.tm[i];
     }
-    __syncthreads();
-  }
-  if (a.dh0) {
+    f32x4 dd;
 #pragma unroll
-    for (int x = 0; x < CPT; ++x) a.dh0[(bh * DK + r) * a.Dv + col + j0 + x] = D[x];
+    for (int i = 0; i < 4; ++i) dd[i] = (c * kT + 4 * grp + i < a.T) ? Elt<E>::to_f(r.dd[i]) : 0.f;
+    reinterpret_cast<f32x4*>(rec + R::DO)[lane] = dd;
+    if (grp == 0) {
+      reinterpret_cast<float*>(rec + R::GM)[n] = __expf(r.g);
+      reinterpret_cast<float*>(rec + R::EC)[n] = __expf(r.gC - r.g);
+      reinterpret_cast<float*>(rec + R::BT)[n] = r.bt;
+      if (n == 0) *reinterpret_cast<float*>(rec + R::GC) = __expf(r.gC);
+    }
+  };
+  HdRaw<E, DK> ra, rb;
+  load(ra, p);
+  store(ra, p);                 // epoch 0
+  load(ra, NP + p);             // epoch 1, staged during epoch 0
+  __syncthreads();
+  for (int ep = 0; ep < NE; ep += 2) {
+    load(rb, (ep + 2) * NP + p);
+    store(ra, (ep + 1) * NP + p);
+    __syncthreads();
+    if (ep + 1 < NE) {
+      load(ra, (ep + 3) * NP + p);
+      store(rb, (ep + 2) * NP + p);
+      __syncthreads();
+    }
   }
 }
 
@@ -601,9 +821,11 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((bwd_prep_kernel<E, DK>), dim3((unsigned)tiles), dim3(kBwdThreads), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_hstates_kernel<E, DK>), dim3((unsigned)slices), dim3(kBwdThreads), 0, st, a);
+  hipLaunchKernelGGL((bwd_hstates_mfma_kernel<E, DK, 2>), dim3((unsigned)slices), dim3(64 * 3), 0,
+                     st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dh_kernel<E, DK>), dim3((unsigned)slices), dim3(kBwdThreads), 0, st, a);
+  hipLaunchKernelGGL((bwd_dh_mfma_kernel<E, DK, 2>), dim3((unsigned)slices), dim3(64 * 3), 0, st,
+                     a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_grad_kernel<E, DK>), dim3((unsigned)tiles), dim3(kBwdThreads), 0, st, a);
   return hipGetLastError();
