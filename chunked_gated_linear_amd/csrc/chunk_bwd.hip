@@ -102,10 +102,10 @@ template <> struct Ld8<float> {
 
 template <typename E> __device__ inline float ld1(const E* p) { return (float)*p; }
 
-// Rows of one tile of a [B, T, H, D] tensor into LDS (fp32, row pitch D + 1),
+// Rows of one tile of a [B, T, H, D] tensor into LDS (fp32, row pitch P),
 // zeros past the end of the sequence.
-template <typename E, int D>
-__device__ inline void load_tile(float (*dst)[D + 1], const E* src, int b, int c, int h,
+template <typename E, int D, int P = D + 1>
+__device__ inline void load_tile(float (*dst)[P], const E* src, int b, int c, int h,
                                  const BwdArgs& a) {
   constexpr int PER_ROW = D / 8;
   for (int x = threadIdx.x; x < kT * PER_ROW; x += kBwdThreads) {
@@ -635,9 +635,13 @@ __device__ inline float sum16(float x) {
 
 template <typename E, int DK>
 __global__ __launch_bounds__(kBwdThreads) void bwd_grad_kernel(BwdArgs a) {
-  constexpr int RB = DK / 16;   // rows of dq / dk per thread
-  __shared__ float sK[kT][DK + 1], sQ[kT][DK + 1];
+  // K and Q rows padded by 4 floats: the MFMA A-fragment reads (row n,
+  // column 4kk + grp) then spread over the LDS banks
+  constexpr int KP = DK + 4;
+  constexpr int RT = DK / 64;   // 16-row blocks of dq / dk per wave
+  __shared__ float sK[kT][KP], sQ[kT][KP];
   __shared__ float sH[DK][17], sD[DK][17];
+  __shared__ float sKH[kT][17], sQH[kT][17], sKdH[kT][17];
   __shared__ float sV[kT][17], sDO[kT][17], sY[kT][17], sU[kT][17], sDU[kT][17], sDY[kT][17];
   __shared__ float sTi[kT][kT + 1], sP[kT][kT + 1];
   __shared__ float sPE[kT][kT + 1], sM[kT][kT + 1], sPP[kT][kT + 1], sAA[kT][kT + 1];
@@ -650,11 +654,12 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grad_kernel(BwdArgs a) {
   const int64_t bh = tile / a.NT;
   const int h = (int)(bh % a.H), b = (int)(bh / a.H);
   const int t = tid >> 4, j = tid & 15;        // (token, column) or (token, token)
-  // dq / dk rows of this thread: j, j + 16, ..., so the 16 threads of a token
-  // read 16 different LDS banks of a state slice and store 16 adjacent floats
+  // MFMA view of the same threads: wave w, lane (n, grp)
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = tid & 15, grp = (tid >> 4) & 3;
   const float* rec = a.rec + tile * BRec::FLOATS;
-  load_tile<E, DK>(sK, static_cast<const E*>(a.k), b, c, h, a);
-  load_tile<E, DK>(sQ, static_cast<const E*>(a.q), b, c, h, a);
+  load_tile<E, DK, KP>(sK, static_cast<const E*>(a.k), b, c, h, a);
+  load_tile<E, DK, KP>(sQ, static_cast<const E*>(a.q), b, c, h, a);
   sTi[t][j] = rec[BRec::TINV + tid];
   sP[t][j] = rec[BRec::P + tid];
   const float ekk = rec[BRec::EKK + tid];
@@ -671,9 +676,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grad_kernel(BwdArgs a) {
   float dPacc = 0.f, dAacc = 0.f;               // (t, i = j)
   float accB = 0.f, accG = 0.f, accW = 0.f;     // (t, column) partial sums
   float hdh = 0.f;
-  float dQ[RB], dK[RB];
+  // dq, dk rows 16 (RT w + r) .. + 15 of this wave, accumulator order: lane
+  // (n, grp) register i holds token 4grp + i, row 16 (RT w + r) + n
+  f32x4 dQa[RT], dKa[RT];
 #pragma unroll
-  for (int x = 0; x < RB; ++x) dQ[x] = dK[x] = 0.f;
+  for (int r = 0; r < RT; ++r) dQa[r] = dKa[r] = zero4();
 
   const int NV = a.Dv / 16;
   for (int jb = 0; jb < NV; ++jb) {
@@ -689,13 +696,21 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grad_kernel(BwdArgs a) {
     sV[t][j] = live ? ld1(vp + row_idx * a.Dv + col + j) : 0.f;
     sDO[t][j] = live ? ld1(dop + row_idx * a.Dv + col + j) : 0.f;
     __syncthreads();
-    float KH = 0.f, QH = 0.f, KdH = 0.f;
+    // K H, Q H and K dH' of this column slice (16 x 16, over d_k), one wave each
+    if (w < 3) {
+      const float (*Am)[KP] = w == 1 ? sQ : sK;
+      const float (*Bm)[17] = w == 2 ? sD : sH;
+      f32x4 acc = zero4();
 #pragma unroll 8
-    for (int rr = 0; rr < DK; ++rr) {
-      KH += sK[t][rr] * sH[rr][j];
-      QH += sQ[t][rr] * sH[rr][j];
-      KdH += sK[t][rr] * sD[rr][j];
+      for (int kk = 0; kk < DK / 4; ++kk)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(Am[n][4 * kk + grp], Bm[4 * kk + grp][n], acc,
+                                                   0, 0, 0);
+      float (*Om)[17] = w == 0 ? sKH : w == 1 ? sQH : sKdH;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Om[4 * grp + i][n] = acc[i];
     }
+    __syncthreads();
+    const float KH = sKH[t][j], QH = sQH[t][j], KdH = sKdH[t][j];
     const float vres = sV[t][j] - sGam[t] * KH;
     sY[t][j] = sB[t] * vres;
     __syncthreads();
@@ -724,20 +739,21 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grad_kernel(BwdArgs a) {
       dPacc += p;
       dAacc -= q;
     }
-    // (t, rows j + 16x): dQ += gamma dO H^T; dK += -beta gamma dY H^T + ec U dH'^T
-    {
-      const float gq = sGam[t], gk = -sB[t] * sGam[t], ek = sEc[t];
+    // dQ += diag(gamma) dO H^T; dK += -diag(beta gamma) dY H^T + diag(ec) U dH'^T
+    // (16 x d_k, over the 16 columns of this slice)
 #pragma unroll
-      for (int x = 0; x < RB; ++x) {
-        const int rr = j + 16 * x;
-        float oh = 0.f, yh = 0.f, ud = 0.f;
-        for (int jj = 0; jj < 16; ++jj) {
-          oh += sDO[t][jj] * sH[rr][jj];
-          yh += sDY[t][jj] * sH[rr][jj];
-          ud += sU[t][jj] * sD[rr][jj];
-        }
-        dQ[x] += gq * oh;
-        dK[x] += gk * yh + ek * ud;
+    for (int kk = 0; kk < 4; ++kk) {
+      const int jj = 4 * kk + grp;
+      const float aO = sGam[n] * sDO[n][jj];
+      const float aY = -sB[n] * sGam[n] * sDY[n][jj];
+      const float aU = sEc[n] * sU[n][jj];
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        const int row = 16 * (RT * w + r) + n;
+        const float bH = sH[row][jj], bD = sD[row][jj];
+        dQa[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(aO, bH, dQa[r], 0, 0, 0);
+        dKa[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(aY, bH, dKa[r], 0, 0, 0);
+        dKa[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(aU, bD, dKa[r], 0, 0, 0);
       }
     }
     __syncthreads();
@@ -765,24 +781,30 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grad_kernel(BwdArgs a) {
     if ((tid & 63) == 0) sHdH[tid >> 6] = hw;
   }
   __syncthreads();
+  // in-tile terms: dQ += (dP o E) K, dK += (dP o E)^T Q + (M + M^T) K
 #pragma unroll
-  for (int x = 0; x < RB; ++x) {
-    const int rr = j + 16 * x;
-    float q1 = 0.f, k1 = 0.f;
-    for (int i = 0; i < kT; ++i) {
-      q1 += sPE[t][i] * sK[i][rr];
-      k1 += sPE[i][t] * sQ[i][rr] + sM[t][i] * sK[i][rr] + sM[i][t] * sK[i][rr];
+  for (int kk = 0; kk < 4; ++kk) {
+    const int i = 4 * kk + grp;
+    const float aPE = sPE[n][i], aPEt = sPE[i][n], aMM = sM[n][i] + sM[i][n];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      const int col = 16 * (RT * w + r) + n;
+      const float bK = sK[i][col], bQ = sQ[i][col];
+      dQa[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(aPE, bK, dQa[r], 0, 0, 0);
+      dKa[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(aPEt, bQ, dKa[r], 0, 0, 0);
+      dKa[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(aMM, bK, dKa[r], 0, 0, 0);
     }
-    dQ[x] += q1;
-    dK[x] += k1;
   }
-  if (live) {
-    float* dqp = a.dq + row_idx * DK + j;
-    float* dkp = a.dk + row_idx * DK + j;
 #pragma unroll
-    for (int x = 0; x < RB; ++x) {
-      dqp[16 * x] = dQ[x];
-      dkp[16 * x] = dK[x];
+  for (int i = 0; i < 4; ++i) {
+    const int tk = c * kT + 4 * grp + i;
+    if (tk < a.T) {
+      const int64_t ro = (((int64_t)b * a.T + tk) * a.H + h) * DK;
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        a.dq[ro + 16 * (RT * w + r) + n] = dQa[r][i];
+        a.dk[ro + 16 * (RT * w + r) + n] = dKa[r][i];
+      }
     }
   }
   if (tid < kT) {
