@@ -404,11 +404,12 @@ __global__ __launch_bounds__(64 * (NP + 1)) void bwd_hstates_mfma_kernel(BwdArgs
 // registers in accumulator order; per tile it stores D, then
 //   dU = diag(ec) K D + P^T dO,  dY = T^T dU,
 //   D' = gamma_C D + Q^T diag(gamma) dO - K^T diag(beta gamma) dY,
-// and after the first tile writes dh0.  Loader waves stage K (A fragments and
+// and after the first tile writes dh0.  SPW chain waves per workgroup (one
+// per 16-column slice) share what the loader waves stage: K (A fragments and
 // K^T fragments), Q^T fragments, P^T, T^T, the slice of dO and the per-token
 // factors, double-buffered by epochs in processing order (m = 0 is the last
 // tile).
-template <int DK>
+template <int DK, int SPW>
 struct HdRec {
   static constexpr int NS = DK / 32, NT = DK / 16;
   static constexpr int KF = 0;                     // K: NS x 64 lanes x 8 f32
@@ -416,8 +417,8 @@ struct HdRec {
   static constexpr int QT = KT + NT * 64 * 4 * 4;  // Q^T: NT x 64 x 4
   static constexpr int PT = QT + NT * 64 * 4 * 4;  // P^T: 16 x 16 row-major
   static constexpr int TT = PT + 256 * 4;          // T^T: 16 x 16 row-major
-  static constexpr int DO = TT + 256 * 4;          // dO slice: 64 x 4
-  static constexpr int GM = DO + 64 * 4 * 4;       // gamma[16]
+  static constexpr int DO = TT + 256 * 4;          // dO slices: SPW x 64 x 4
+  static constexpr int GM = DO + SPW * 64 * 4 * 4; // gamma[16]
   static constexpr int EC = GM + 64;               // ec[16]
   static constexpr int BT = EC + 64;               // beta[16]
   static constexpr int GC = BT + 64;               // gamma_C (x4)
@@ -425,28 +426,28 @@ struct HdRec {
   static_assert(BYTES % 16 == 0, "alignment");
 };
 
-template <typename E, int DK>
+template <typename E, int DK, int SPW>
 struct HdRaw {
   typename Elt<E>::F32 kf[DK / 32];
   typename Elt<E>::F32 qf[DK / 32];
   f32x4 pm, tm;
-  E dd[4];
+  E dd[SPW][4];
   float g, bt, gC;
 };
 
-template <typename E, int DK, int NP>
-__global__ __launch_bounds__(64 * (NP + 1)) void bwd_dh_mfma_kernel(BwdArgs a) {
-  using R = HdRec<DK>;
+template <typename E, int DK, int NP, int SPW>
+__global__ __launch_bounds__(64 * (NP + SPW)) void bwd_dh_mfma_kernel(BwdArgs a) {
+  using R = HdRec<DK, SPW>;
   using X = Elt<float>;
   using F16 = X::F16;
   using F32 = X::F32;
   constexpr int NS = R::NS, NT = R::NT;
   __shared__ __attribute__((aligned(16))) char smem[2 * NP * R::BYTES];
-  const int NV = a.Dv / 16;
-  const int sl = (int)(blockIdx.x % NV);
-  const int64_t bh = blockIdx.x / NV;
+  // SPW column slices of 16 per workgroup, one chain wave each
+  const int NW = a.Dv / (16 * SPW);
+  const int sl = (int)(blockIdx.x % NW);
+  const int64_t bh = blockIdx.x / NW;
   const int h = (int)(bh % a.H), b = (int)(bh / a.H);
-  const int v0 = 16 * sl;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, grp = lane >> 4;
@@ -455,7 +456,8 @@ __global__ __launch_bounds__(64 * (NP + 1)) void bwd_dh_mfma_kernel(BwdArgs a) {
   // records by processing index m (tile NC - 1 - m)
   auto rec_of = [&](int m) -> char* { return smem + (((m / NP) & 1) * NP + m % NP) * R::BYTES; };
 
-  if (wave == 0) {
+  if (wave < SPW) {
+    const int v0 = 16 * (SPW * sl + wave);
     f32x4 D[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -482,7 +484,7 @@ __global__ __launch_bounds__(64 * (NP + 1)) void bwd_dh_mfma_kernel(BwdArgs a) {
           const F32 kf = reinterpret_cast<const F32*>(rec + R::KF)[s * 64 + lane];
           KD = X::mma32(kf, X::from_acc2(D[2 * s], D[2 * s + 1]), KD);
         }
-        const f32x4 dO = reinterpret_cast<const f32x4*>(rec + R::DO)[lane];
+        const f32x4 dO = reinterpret_cast<const f32x4*>(rec + R::DO)[wave * 64 + lane];
         const f32x4 gm = reinterpret_cast<const f32x4*>(rec + R::GM)[grp];
         const f32x4 ec = reinterpret_cast<const f32x4*>(rec + R::EC)[grp];
         const f32x4 bt = reinterpret_cast<const f32x4*>(rec + R::BT)[grp];
@@ -524,12 +526,13 @@ __global__ __launch_bounds__(64 * (NP + 1)) void bwd_dh_mfma_kernel(BwdArgs a) {
   }
 
   // ---------------------------------------------------------------- loaders
-  const int p = wave - 1;
+  const int p = wave - SPW;
   const E* kp = static_cast<const E*>(a.k);
   const E* qp = static_cast<const E*>(a.q);
   const E* dp = static_cast<const E*>(a.dout);
+  const int v0 = 16 * SPW * sl;
   auto rowk = [&](int t) -> int64_t { return ((int64_t)b * a.T + t) * a.H + h; };
-  auto load = [&](HdRaw<E, DK>& r, int m) {
+  auto load = [&](HdRaw<E, DK, SPW>& r, int m) {
     const int c = NC - 1 - min(m, NC - 1);
     const int t = min(c * kT + n, a.T - 1);
     const int64_t base = rowk(t) * DK;
@@ -557,9 +560,13 @@ __global__ __launch_bounds__(64 * (NP + 1)) void bwd_dh_mfma_kernel(BwdArgs a) {
     r.bt = rec[BRec::BETA + n];
     r.gC = rec[BRec::G + kT - 1];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r.dd[i] = dp[rowk(min(c * kT + 4 * grp + i, a.T - 1)) * a.Dv + v0 + n];
+    for (int w = 0; w < SPW; ++w) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        r.dd[w][i] = dp[rowk(min(c * kT + 4 * grp + i, a.T - 1)) * a.Dv + v0 + 16 * w + n];
+    }
   };
-  auto store = [&](const HdRaw<E, DK>& r, int m) {
+  auto store = [&](const HdRaw<E, DK, SPW>& r, int m) {
     if (m >= NC) return;
     const int c = NC - 1 - m;
     char* rec = rec_of(m);
@@ -596,10 +603,14 @@ __global__ __launch_bounds__(64 * (NP + 1)) void bwd_dh_mfma_kernel(BwdArgs a) {
       pt[(col + i) * 16 + row] = r.pm[i];
       tt[(col + i) * 16 + row] = r.tm[i];
     }
-    f32x4 dd;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dd[i] = (c * kT + 4 * grp + i < a.T) ? Elt<E>::to_f(r.dd[i]) : 0.f;
-    reinterpret_cast<f32x4*>(rec + R::DO)[lane] = dd;
+    for (int w = 0; w < SPW; ++w) {
+      f32x4 dd;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        dd[i] = (c * kT + 4 * grp + i < a.T) ? Elt<E>::to_f(r.dd[w][i]) : 0.f;
+      reinterpret_cast<f32x4*>(rec + R::DO)[w * 64 + lane] = dd;
+    }
     if (grp == 0) {
       reinterpret_cast<float*>(rec + R::GM)[n] = __expf(r.g);
       reinterpret_cast<float*>(rec + R::EC)[n] = __expf(r.gC - r.g);
@@ -607,7 +618,7 @@ __global__ __launch_bounds__(64 * (NP + 1)) void bwd_dh_mfma_kernel(BwdArgs a) {
       if (n == 0) *reinterpret_cast<float*>(rec + R::GC) = __expf(r.gC);
     }
   };
-  HdRaw<E, DK> ra, rb;
+  HdRaw<E, DK, SPW> ra, rb;
   load(ra, p);
   store(ra, p);                 // epoch 0
   load(ra, NP + p);             // epoch 1, staged during epoch 0
@@ -846,8 +857,15 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((bwd_hstates_mfma_kernel<E, DK, 2>), dim3((unsigned)slices), dim3(64 * 3), 0,
                      st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dh_mfma_kernel<E, DK, 2>), dim3((unsigned)slices), dim3(64 * 3), 0, st,
-                     a);
+  // two column slices per workgroup when the slice count is even: the staged
+  // tile then serves two chain waves, and half as many workgroups (at one per
+  // compute unit, for the LDS they take) fit in one round
+  if ((a.Dv / 16) % 2 == 0)
+    hipLaunchKernelGGL((bwd_dh_mfma_kernel<E, DK, 2, 2>), dim3((unsigned)(slices / 2)),
+                       dim3(64 * 4), 0, st, a);
+  else
+    hipLaunchKernelGGL((bwd_dh_mfma_kernel<E, DK, 2, 1>), dim3((unsigned)slices), dim3(64 * 3), 0,
+                       st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_grad_kernel<E, DK>), dim3((unsigned)tiles), dim3(kBwdThreads), 0, st, a);
   return hipGetLastError();
