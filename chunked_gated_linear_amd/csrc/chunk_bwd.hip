@@ -694,16 +694,29 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grad_kernel(BwdArgs a) {
   for (int r = 0; r < RT; ++r) dQa[r] = dKa[r] = zero4();
 
   const int NV = a.Dv / 16;
+  // this thread's share of a slice of H and dH' (rows tid / 16 + 16 x, column
+  // tid % 16), loaded one slice ahead
+  constexpr int SP = DK * 16 / kBwdThreads;
+  float nh[SP], nd[SP];
+  auto fetch_slice = [&](int jb) {
+#pragma unroll
+    for (int x = 0; x < SP; ++x) {
+      const int64_t at = (int64_t)((tid >> 4) + 16 * x) * a.Dv + 16 * jb + (tid & 15);
+      nh[x] = Hb[at];
+      nd[x] = Db[at];
+    }
+  };
+  fetch_slice(0);
   for (int jb = 0; jb < NV; ++jb) {
     const int col = 16 * jb;
-    for (int x = tid; x < DK * 16; x += kBwdThreads) {
-      const int rr = x >> 4, jj = x & 15;
-      const float hv = Hb[(int64_t)rr * a.Dv + col + jj];
-      const float dv = Db[(int64_t)rr * a.Dv + col + jj];
-      sH[rr][jj] = hv;
-      sD[rr][jj] = dv;
-      hdh += hv * dv;
+#pragma unroll
+    for (int x = 0; x < SP; ++x) {
+      const int rr = (tid >> 4) + 16 * x, jj = tid & 15;
+      sH[rr][jj] = nh[x];
+      sD[rr][jj] = nd[x];
+      hdh += nh[x] * nd[x];
     }
+    if (jb + 1 < NV) fetch_slice(jb + 1);
     sV[t][j] = live ? ld1(vp + row_idx * a.Dv + col + j) : 0.f;
     sDO[t][j] = live ? ld1(dop + row_idx * a.Dv + col + j) : 0.f;
     __syncthreads();
