@@ -327,8 +327,9 @@ def main():
             "roofline": {"bound": "hbm", "achieved": bbytes / (bms * 1e-3) / 1e9,
                          "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                          "frac": bbytes / (bms * 1e-3) / PEAK_HBM, "alg_bytes_per_launch": bbytes,
-                         "kernel": ("bwd_prep_kernel + bwd_hstates_kernel + bwd_dh_kernel + "
-                                    "bwd_grad_kernel (one lin_attn_chunk_bwd call)")},
+                         "kernel": ("bwd_prep_kernel + bwd_hstates_mfma_kernel + "
+                                    "bwd_dh_mfma_kernel + bwd_grad_kernel "
+                                    "(one lin_attn_chunk_bwd call)")},
         }
         del bin_, up, wsb
 
