@@ -377,6 +377,40 @@ def main():
         }
         del d, S
 
+    # ---- decode with a per-channel gate: same shape, gate logits [B,H,Dk]
+    if args.decode_steps > 0:
+        from chunked_gated_linear_amd import lin_attn_decode_step_channel
+        dw = I.DECODE_WORKLOAD
+        dB, dH, dD = dw["B"], dw["H"], dw["Dk"]
+        n = min(args.decode_steps, 200)
+        d = I.make_decode_inputs(dB, dH, dD, dD, dtype=dw["dtype"], seed=1005, device=dev,
+                                 steps=n)
+        xg = I.make_channel_gate(n, dB, dH, dD, seed=1005, device=dev)   # [steps, B, H, Dk]
+        S = d["S"]
+        od = torch.empty((dB, dH, dD), dtype=d["q"].dtype, device=dev)
+        for s_ in range(min(3, n)):
+            lin_attn_decode_step_channel(d["q"][s_], d["k"][s_], d["v"][s_], xg[s_], d["beta"][s_],
+                                         S, gate_mode="logit", o=od)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for s_ in range(n):
+            lin_attn_decode_step_channel(d["q"][s_], d["k"][s_], d["v"][s_], xg[s_], d["beta"][s_],
+                                         S, gate_mode="logit", o=od)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cms = e0.elapsed_time(e1) / n
+        per_head = 2 * dD * dD * 4 + 3 * dD * 2 + dD * 2 + 4 * dD + 4
+        cbytes = dB * dH * per_head
+        result["decode_channel"] = {
+            "workload": f"B={dB} H={dH} d={dD} bf16, per-channel gate, fp32 state in place, {n} steps",
+            "us_per_step": cms * 1e3, "tokens_per_s": dB / (cms * 1e-3),
+            "roofline": {"bound": "hbm", "achieved": cbytes / (cms * 1e-3) / 1e9,
+                         "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                         "frac": cbytes / (cms * 1e-3) / PEAK_HBM,
+                         "alg_bytes_per_launch": cbytes, "kernel": "decode_channel_kernel"},
+        }
+        del d, S, xg
+
     # ---- CPU baseline: the fp64 oracle (plain C recurrence) on host cores
     if not args.no_cpu_baseline:
         from oracle import c_recurrent as crec

@@ -9,7 +9,7 @@ from .api import (lin_attn_chunk_bwd, lin_attn_chunk_bwd_workspace_size,  # noqa
                   lin_attn_chunk_fwd_channel_workspace_size,
                   lin_attn_chunk_fwd_workspace_size,
                   lin_attn_chunk_fwd_varlen, lin_attn_chunk_fwd_varlen_workspace_size,
-                  lin_attn_decode_step, lin_attn_gate)
+                  lin_attn_decode_step, lin_attn_decode_step_channel, lin_attn_gate)
 from ._native import LinAttnError, lib  # noqa: F401
 
 __all__ = ["lin_attn_chunk_bwd", "lin_attn_chunk_bwd_workspace_size",
@@ -17,4 +17,4 @@ __all__ = ["lin_attn_chunk_bwd", "lin_attn_chunk_bwd_workspace_size",
            "lin_attn_chunk_fwd_channel_workspace_size",
            "lin_attn_chunk_fwd_workspace_size",
            "lin_attn_chunk_fwd_varlen", "lin_attn_chunk_fwd_varlen_workspace_size",
-           "lin_attn_decode_step", "lin_attn_gate", "LinAttnError", "lib"]
+           "lin_attn_decode_step", "lin_attn_decode_step_channel", "lin_attn_gate", "LinAttnError", "lib"]

@@ -229,9 +229,7 @@ def lin_attn_chunk_fwd_varlen(q, k, v, gate, beta, cu_seqlens, h0=None, *, gate_
     return o, hT
 
 
-def lin_attn_decode_step(q, k, v, gate, beta, S, *, gate_mode="log", G=5.0, o=None,
-                         stream=None):
-    """Advance S [B,H,Dk,Dv] by one token in place; returns o [B,H,Dv]."""
+def _decode(fn, channel, q, k, v, gate, beta, S, gate_mode, G, o, stream):
     _need(q, "q")
     if q.dtype not in _DTYPES:
         raise TypeError("q, k, v must be bfloat16 or float32")
@@ -239,16 +237,29 @@ def lin_attn_decode_step(q, k, v, gate, beta, S, *, gate_mode="log", G=5.0, o=No
     Dv = v.shape[-1]
     _need(k, "k", q.dtype, (B, H, Dk))
     _need(v, "v", q.dtype, (B, H, Dv))
-    _need(gate, "gate", torch.float32, (B, H))
+    _need(gate, "gate", torch.float32, (B, H, Dk) if channel else (B, H))
     _need(beta, "beta", torch.float32, (B, H))
     _need(S, "S", torch.float32, (B, H, Dk, Dv))
     if o is None:
         o = torch.empty((B, H, Dv), dtype=q.dtype, device=q.device)
     _need(o, "o", q.dtype, (B, H, Dv))
-    N.check(N.lib().lin_attn_decode_step(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _GATE[gate_mode], float(G), _ptr(beta),
-        _ptr(S), _ptr(o), B, H, Dk, Dv, _DTYPES[q.dtype], _stream(q, stream)))
+    N.check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _GATE[gate_mode], float(G), _ptr(beta),
+               _ptr(S), _ptr(o), B, H, Dk, Dv, _DTYPES[q.dtype], _stream(q, stream)))
     return o
+
+
+def lin_attn_decode_step(q, k, v, gate, beta, S, *, gate_mode="log", G=5.0, o=None,
+                         stream=None):
+    """Advance S [B,H,Dk,Dv] by one token in place; returns o [B,H,Dv]."""
+    return _decode(N.lib().lin_attn_decode_step, False, q, k, v, gate, beta, S, gate_mode, G, o,
+                   stream)
+
+
+def lin_attn_decode_step_channel(q, k, v, gate, beta, S, *, gate_mode="log", G=5.0, o=None,
+                                 stream=None):
+    """lin_attn_decode_step with one log-decay per key channel: gate [B,H,Dk]."""
+    return _decode(N.lib().lin_attn_decode_step_channel, True, q, k, v, gate, beta, S,
+                   gate_mode, G, o, stream)
 
 
 def lin_attn_gate(x, G=5.0, out=None, stream=None):

@@ -468,6 +468,104 @@ hipError_t launch_ch(const void* q, const void* k, const void* v, const float* g
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------ decode step
+// One new token per (b, h) with a per-channel decay a = exp(g) (d_k values),
+// state updated in place.  With d = diag(a) h:
+//     u  = beta (v - h^T (a o k)),   h' = diag(a) h + k u^T,
+//     o  = h'^T q = h^T (a o q) + (k . q) u
+// so h is read once and written once, as in the scalar-gate decode step.
+// Layout as there: a persistent grid of 1024-thread workgroups walks the
+// (b, h) list; thread (rg, c4) holds columns 4 c4 .. 4 c4 + 3 of rows rg,
+// rg + RG, ... as float4; the state is streamed with non-temporal accesses.
+constexpr int kDecThreads = 1024;
+
+template <typename E, int DK, int DV>
+__global__ __launch_bounds__(kDecThreads) void decode_channel_kernel(
+    const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
+    const float* __restrict__ gate, int gate_logit, float G,
+    const float* __restrict__ beta, float* __restrict__ S, E* __restrict__ o, int BH) {
+  constexpr int NC4 = DV / 4;
+  constexpr int RG = kDecThreads / NC4;
+  constexpr int RPT = DK / RG;
+  static_assert(RG * NC4 == kDecThreads && RPT * RG == DK, "decode tiling");
+  __shared__ float sk[DK], sa[DK], ska[DK], sqa[DK];
+  __shared__ f32x4 pa[RG][NC4], pb[RG][NC4];
+  __shared__ float su[DV];
+  __shared__ float skq;
+  const int tid = threadIdx.x;
+  const int c4 = tid % NC4, rg = tid / NC4;
+  for (int64_t bh = blockIdx.x; bh < BH; bh += gridDim.x) {
+    const float bt = beta[bh];
+    if (tid < DK) {
+      const float gx = gate[bh * DK + tid];
+      const float a = __expf(gate_logit ? bounded_gate(gx, G) : gx);
+      const float kv = Elt<E>::to_f(k[bh * DK + tid]);
+      sk[tid] = kv;
+      sa[tid] = a;
+      ska[tid] = a * kv;
+      sqa[tid] = a * Elt<E>::to_f(q[bh * DK + tid]);
+    }
+    f32x4* Sh = reinterpret_cast<f32x4*>(S + bh * DK * DV);
+    f32x4 s[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) s[i] = __builtin_nontemporal_load(Sh + (rg + RG * i) * NC4 + c4);
+    __syncthreads();
+    f32x4 pk = zero4(), pq = zero4();
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      pk += ska[rg + RG * i] * s[i];
+      pq += sqa[rg + RG * i] * s[i];
+    }
+    pa[rg][c4] = pk;
+    pb[rg][c4] = pq;
+    if (tid < 64) {  // k . q, one wave, fixed order
+      float p = 0.f;
+      for (int d = tid; d < DK; d += 64) p += sk[d] * Elt<E>::to_f(q[bh * DK + d]);
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) p += __shfl_xor(p, off);
+      if (tid == 0) skq = p;
+    }
+    __syncthreads();
+    if (tid < DV) {
+      const int cq = tid >> 2, cr = tid & 3;
+      float hk = 0.f, hq = 0.f;
+#pragma unroll
+      for (int r = 0; r < RG; ++r) {
+        hk += pa[r][cq][cr];
+        hq += pb[r][cq][cr];
+      }
+      const float u = bt * (Elt<E>::to_f(v[bh * DV + tid]) - hk);
+      su[tid] = u;
+      o[bh * DV + tid] = Elt<E>::from_f(hq + skq * u);
+    }
+    __syncthreads();
+    const f32x4 u4 = reinterpret_cast<const f32x4*>(su)[c4];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int row = rg + RG * i;
+      __builtin_nontemporal_store(sa[row] * s[i] + sk[row] * u4, Sh + row * NC4 + c4);
+    }
+    __syncthreads();   // the shared buffers are reused by the next (b, h)
+  }
+}
+
+template <typename E, int DK, int DV>
+hipError_t launch_dec_ch(const void* q, const void* k, const void* v, const float* gate,
+                         int gate_logit, float G, const float* beta, float* S, void* o, int BH,
+                         hipStream_t st) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    cus = 256;
+  const int cap = 4 * cus;
+  const int grid = BH < cap ? BH : cap;
+  hipLaunchKernelGGL((decode_channel_kernel<E, DK, DV>), dim3(grid), dim3(kDecThreads), 0, st,
+                     (const E*)q, (const E*)k, (const E*)v, gate, gate_logit, G, beta, S, (E*)o,
+                     BH);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 long long chunk_channel_workspace_bytes(int B, int T, int H, int Dk) {
@@ -488,6 +586,21 @@ hipError_t launch_chunk_fwd_channel(const void* q, const void* k, const void* v,
     if (Dk == 64) return launch_ch<__bf16, 64, 2>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, ws, st);
     if (Dk == 128) return launch_ch<__bf16, 128, 2>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, ws, st);
   }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_channel(const void* q, const void* k, const void* v,
+                                 const float* gate, int gate_logit, float G, const float* beta,
+                                 float* S, void* o, int BH, int Dk, int Dv, int fp32,
+                                 hipStream_t st) {
+#define LA_DECC(E, DK, DV) \
+  if (Dk == DK && Dv == DV) return launch_dec_ch<E, DK, DV>(q, k, v, gate, gate_logit, G, beta, S, o, BH, st);
+  if (fp32) {
+    LA_DECC(float, 64, 64) LA_DECC(float, 64, 128) LA_DECC(float, 128, 64) LA_DECC(float, 128, 128)
+  } else {
+    LA_DECC(__bf16, 64, 64) LA_DECC(__bf16, 64, 128) LA_DECC(__bf16, 128, 64) LA_DECC(__bf16, 128, 128)
+  }
+#undef LA_DECC
   return hipErrorInvalidValue;
 }
 

@@ -62,6 +62,12 @@ hipError_t launch_chunk_fwd_channel(const void* q, const void* k, const void* v,
 // Workspace bytes of the per-channel path: one record per tile and head.
 long long chunk_channel_workspace_bytes(int B, int T, int H, int Dk);
 
+// Decode step with a per-channel gate (gate [B*H, Dk]), state in place.
+hipError_t launch_decode_channel(const void* q, const void* k, const void* v,
+                                 const float* gate, int gate_logit, float G, const float* beta,
+                                 float* S, void* o, int BH, int Dk, int Dv, int fp32,
+                                 hipStream_t st);
+
 hipError_t launch_decode(const void* q, const void* k, const void* v,
                          const float* gate, int gate_logit, float G,
                          const float* beta, float* S, void* o, int BH, int Dk,

@@ -314,9 +314,14 @@ int lin_attn_chunk_fwd_varlen_raw(const void* q, const void* k, const void* v, c
                           T, H, Dk, Dv, dtype, workspace, workspace_bytes, stream, 1);
 }
 
-int lin_attn_decode_step(const void* q, const void* k, const void* v, const float* gate,
-                         int gate_mode, float G, const float* beta, float* S, void* o, int B,
-                         int H, int Dk, int Dv, int dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// lin_attn_decode_step (channel = 0) and lin_attn_decode_step_channel (1).
+int decode_step(const void* q, const void* k, const void* v, const float* gate, int gate_mode,
+                float G, const float* beta, float* S, void* o, int B, int H, int Dk, int Dv,
+                int dtype, void* stream, int channel) {
   if (B < 0 || H < 0) return fail(LA_EINVAL, "sizes must be >= 0 (B=%d H=%d)", B, H);
   if (dtype != LA_BF16 && dtype != LA_FP32)
     return fail(LA_EINVAL, "dtype must be LA_BF16 (0) or LA_FP32 (1), got %d", dtype);
@@ -330,23 +335,41 @@ int lin_attn_decode_step(const void* q, const void* k, const void* v, const floa
   const struct { const char* nm; const void* p; unsigned a; } req[] = {
       {"q", q, (unsigned)es}, {"k", k, (unsigned)es}, {"v", v, (unsigned)es},
       {"gate", gate, 4u}, {"beta", beta, 4u}, {"S", S, 16u}, {"o", o, (unsigned)es}};
+  if (channel && G > 10.f)
+    return fail(LA_ERANGE, "G must be in [0, 10] for a per-channel gate, got %g", (double)G);
   for (const auto& r : req) {
     if (!r.p) return fail(LA_EINVAL, "%s must not be NULL", r.nm);
     if (!aligned(r.p, r.a)) return fail(LA_EINVAL, "%s must be %u-byte aligned", r.nm, r.a);
   }
   const int64_t bh = (int64_t)B * H;
   const Span sq = span("q", q, bh * Dk * es), sk = span("k", k, bh * Dk * es),
-             sv = span("v", v, bh * Dv * es), sg = span("gate", gate, bh * 4),
+             sv = span("v", v, bh * Dv * es), sg = span("gate", gate, bh * (channel ? Dk : 1) * 4),
              sb = span("beta", beta, bh * 4), sS = span("S", S, bh * Dk * Dv * 4),
              so = span("o", o, bh * Dv * es);
   for (const Span& in : {sq, sk, sv, sg, sb, sS})
     if (overlap(so, in)) return fail(LA_EINVAL, "o overlaps %s", in.name);
   for (const Span& in : {sq, sk, sv, sg, sb})
     if (overlap(sS, in)) return fail(LA_EINVAL, "S overlaps %s", in.name);
-  hipError_t e = la::launch_decode(q, k, v, gate, gate_mode == LA_GATE_BOUNDED_LOGIT, G, beta,
-                                   S, o, (int)bh, Dk, Dv, dtype == LA_FP32,
-                                   reinterpret_cast<hipStream_t>(stream));
+  hipError_t e = (channel ? la::launch_decode_channel : la::launch_decode)(
+      q, k, v, gate, gate_mode == LA_GATE_BOUNDED_LOGIT, G, beta, S, o, (int)bh, Dk, Dv,
+      dtype == LA_FP32, reinterpret_cast<hipStream_t>(stream));
   return hip_status(e, "decode launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int lin_attn_decode_step(const void* q, const void* k, const void* v, const float* gate,
+                         int gate_mode, float G, const float* beta, float* S, void* o, int B,
+                         int H, int Dk, int Dv, int dtype, void* stream) {
+  return decode_step(q, k, v, gate, gate_mode, G, beta, S, o, B, H, Dk, Dv, dtype, stream, 0);
+}
+
+int lin_attn_decode_step_channel(const void* q, const void* k, const void* v, const float* gate,
+                                 int gate_mode, float G, const float* beta, float* S, void* o,
+                                 int B, int H, int Dk, int Dv, int dtype, void* stream) {
+  return decode_step(q, k, v, gate, gate_mode, G, beta, S, o, B, H, Dk, Dv, dtype, stream, 1);
 }
 
 long long lin_attn_chunk_bwd_workspace_size(int B, int T, int H, int Dk, int Dv, int dtype) {

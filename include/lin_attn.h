@@ -263,6 +263,20 @@ int lin_attn_decode_step(const void* q, const void* k, const void* v,
                          void* stream);
 
 /*
+ * lin_attn_decode_step_channel -- lin_attn_decode_step with one log-decay per
+ * key channel: gate is [B, H, Dk] float32 (g or its logit, per gate_mode), and
+ * the step is the per-channel recurrence of lin_attn_chunk_fwd_channel
+ * (decay on the key side of the old state, then erase and write), so a
+ * per-channel prefill hands its hT to this step unchanged.  Arguments, layouts,
+ * in-place S, supported sizes and errors as lin_attn_decode_step, except
+ * 0 <= G <= 10.
+ */
+int lin_attn_decode_step_channel(const void* q, const void* k, const void* v,
+                                 const float* gate, int gate_mode, float G, const float* beta,
+                                 float* S, void* o, int B, int H, int Dk, int Dv, int dtype,
+                                 void* stream);
+
+/*
  * lin_attn_chunk_bwd_workspace_size -- device workspace bytes lin_attn_chunk_bwd
  * needs: for every 16-token tile and head a 3,200-byte record, the float32
  * state at the tile start and the float32 gradient of the tile's end state

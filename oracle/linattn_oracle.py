@@ -77,6 +77,9 @@ itself are in tests/test_oracle.py):
   chunked_fwd_channel
                    equals recurrent_fwd_channel for chunk sizes 1, 3, 16; its
                    in-tile reciprocals stay finite at the bound.
+  decode_step_channel
+                   steps applied one token at a time equal recurrent_fwd_channel
+                   over the same tokens.
 Every function is pinned; none is "parity unpinned".
 
 Layouts (row-major, as the library uses them):
@@ -104,6 +107,7 @@ __all__ = [
     "bounded_gate_bwd",
     "recurrent_fwd_channel",
     "chunked_fwd_channel",
+    "decode_step_channel",
 ]
 
 
@@ -468,3 +472,15 @@ def chunked_fwd_channel(q, k, v, g, beta, h0=None, chunk: int = 16):
         Kd = K * (gC[:, :, None, :] * inv)
         Hs = gC[..., None] * Hs + np.swapaxes(Kd, -1, -2) @ U
     return np.moveaxis(o, 1, 2), Hs
+
+
+def decode_step_channel(q, k, v, g, beta, S):
+    """One token of the per-channel recurrence for every (batch, head).
+
+    q, k [B,H,Dk]; v [B,H,Dv]; g [B,H,Dk]; beta [B,H]; S [B,H,Dk,Dv] (h = S^T).
+    Returns (o [B,H,Dv], S_new); the input S is not modified.
+    """
+    q, k, v, g, beta, S = map(_f64, (q, k, v, g, beta, S))
+    o, hT = recurrent_fwd_channel(q[:, None], k[:, None], v[:, None], g[:, None],
+                                  beta[:, None], S)
+    return o[:, 0], hT

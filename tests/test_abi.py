@@ -350,3 +350,31 @@ def test_chunk_fwd_channel_workspace_size():
     assert L.lin_attn_chunk_fwd_channel_workspace_size(2, 17, 3, 64, 32, 1) == 2 * 3 * 2 * 14592
     assert L.lin_attn_chunk_fwd_channel_workspace_size(1, 0, 2, 128, 128, 0) == 0
     assert L.lin_attn_chunk_fwd_channel_workspace_size(1, 64, 2, 96, 128, 0) == -1
+
+
+def decode_ch(**kw):
+    a = dict(q=fake(0), k=fake(1), v=fake(2), gate=fake(3), gate_mode=1, G=5.0, beta=fake(4),
+             S=fake(5), o=fake(6), B=2, H=4, Dk=128, Dv=128, dtype=0, stream=None)
+    a.update(kw)
+    L = N.lib()
+    rc = L.lin_attn_decode_step_channel(a["q"], a["k"], a["v"], a["gate"], a["gate_mode"], a["G"],
+                                        a["beta"], a["S"], a["o"], a["B"], a["H"], a["Dk"],
+                                        a["Dv"], a["dtype"], a["stream"])
+    return rc, L.lin_attn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(gate=None), N.LA_EINVAL, "gate must not be NULL"),
+    (dict(G=12.0), N.LA_ERANGE, "per-channel"),
+    (dict(Dk=96), N.LA_EUNSUPPORTED, "decode supports"),
+    # the per-channel gate is B*H*Dk floats: an o placed inside it overlaps
+    (dict(o=fake(3) + 2 * 4 * 4 * 64), N.LA_EINVAL, "o overlaps gate"),
+    (dict(S=fake(3) + 2 * 4 * 4 * 64), N.LA_EINVAL, "S overlaps gate"),
+])
+def test_decode_channel_rejects(kw, code, needle):
+    rc, msg = decode_ch(**kw)
+    assert rc == code and needle in msg, (rc, msg)
+
+
+def test_decode_channel_empty_is_noop():
+    assert decode_ch(B=0)[0] == N.LA_OK

@@ -206,3 +206,13 @@ def test_channel_mutants_are_caught(kind):
 def test_unmutated_channel_control_passes_every_pin():
     f = _mutant("none")
     assert all(p(f) for p in PINS.values())
+
+
+def test_decode_channel_steps_equal_the_forward():
+    q, k, v, g, beta, h0 = _inputs(2, 9, 3, 8, 5, gate="std", seed=8, h0=True)
+    ro, rh = orc.recurrent_fwd_channel(q, k, v, g, beta, h0)
+    S = h0.copy()
+    for t in range(9):
+        o, S = orc.decode_step_channel(q[:, t], k[:, t], v[:, t], g[:, t], beta[:, t], S)
+        assert np.abs(o - ro[:, t]).max() < 1e-12
+    assert np.abs(S - rh).max() < 1e-12

@@ -15,7 +15,8 @@ import pytest
 import torch
 
 from chunked_gated_linear_amd import inputs as I
-from chunked_gated_linear_amd import lin_attn_chunk_fwd, lin_attn_chunk_fwd_channel
+from chunked_gated_linear_amd import (lin_attn_chunk_fwd, lin_attn_chunk_fwd_channel,
+                                      lin_attn_decode_step_channel)
 from oracle import linattn_oracle as orc
 
 from parity_util import host, relerr, say
@@ -130,3 +131,62 @@ def test_channel_long_64k_sampled_heads(regime):
         eh = relerr(host(hT[:, h:h + 1]), rh)
         say(f"  head {h}: err(o)={eo:.2e} err(hT)={eh:.2e}")
         assert eo <= 1e-2 and eh <= 1e-5
+
+
+def test_channel_hT_in_place_of_h0():
+    inp, gate, host_args = make(1, 70, 2, 128, 64, "fp32", "weak", "logit", 0.02, seed=45)
+    h = inp["h0"].clone()
+    o, hT = lin_attn_chunk_fwd_channel(inp["q"], inp["k"], inp["v"], gate, inp["beta"], h,
+                                       gate_mode="logit", hT=h)
+    torch.cuda.synchronize()
+    ro, rh = orc.recurrent_fwd_channel(*host_args)
+    assert hT.data_ptr() == h.data_ptr()
+    assert relerr(host(o), ro) <= 1e-5 and relerr(host(h), rh) <= 1e-5
+
+
+@pytest.mark.parametrize("dtype,Dk,Dv", [("fp32", 64, 64), ("fp32", 128, 64), ("bf16", 64, 128),
+                                         ("bf16", 128, 128)])
+def test_decode_channel_parity(dtype, Dk, Dv):
+    # three decode steps from a random state, every output and the state
+    # against the fp64 per-channel step
+    B, H, steps = 3, 5, 3
+    say(f"decode channel {dtype} {Dk} {Dv}")
+    inp = I.make_inputs(B, steps, H, Dk, Dv, dtype=dtype, seed=46, device="cuda", h0_std=0.02)
+    x = I.make_channel_gate(B, steps, H, Dk, seed=46, device="cuda")
+    S = inp["h0"].clone()
+    S_ref = host(S).astype(np.float64)
+    tol = 1e-5 if dtype == "fp32" else 1e-2
+    for t in range(steps):
+        o = lin_attn_decode_step_channel(inp["q"][:, t].contiguous(), inp["k"][:, t].contiguous(),
+                                         inp["v"][:, t].contiguous(), x[:, t].contiguous(),
+                                         inp["beta"][:, t].contiguous(), S, gate_mode="logit")
+        torch.cuda.synchronize()
+        ro, S_ref = orc.decode_step_channel(host(inp["q"][:, t]), host(inp["k"][:, t]),
+                                            host(inp["v"][:, t]),
+                                            orc.bounded_gate(host(x[:, t]).astype(np.float64)),
+                                            host(inp["beta"][:, t]), S_ref)
+        assert relerr(host(o), ro) <= tol
+    assert relerr(host(S), S_ref) <= 1e-5
+
+
+def test_channel_prefill_hands_off_to_decode():
+    # per-channel prefill of 40 tokens, then 3 decode steps from its hT: the
+    # same outputs as one prefill over the 43 tokens (the oracle decides both)
+    B, T1, T2, H, D = 2, 40, 3, 2, 128
+    inp = I.make_inputs(B, T1 + T2, H, D, D, dtype="bf16", seed=47, device="cuda")
+    x = I.make_channel_gate(B, T1 + T2, H, D, seed=47, device="cuda", mu=-3.0)
+    sl = lambda a: a[:, :T1].contiguous()
+    _, hT = lin_attn_chunk_fwd_channel(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(x),
+                                       sl(inp["beta"]), None, gate_mode="logit")
+    outs = []
+    for t in range(T1, T1 + T2):
+        outs.append(lin_attn_decode_step_channel(
+            inp["q"][:, t].contiguous(), inp["k"][:, t].contiguous(), inp["v"][:, t].contiguous(),
+            x[:, t].contiguous(), inp["beta"][:, t].contiguous(), hT, gate_mode="logit"))
+    torch.cuda.synchronize()
+    g = orc.bounded_gate(host(x).astype(np.float64))
+    ro, rh = orc.recurrent_fwd_channel(host(inp["q"]), host(inp["k"]), host(inp["v"]), g,
+                                       host(inp["beta"]).astype(np.float64), None)
+    got = np.stack([host(o) for o in outs], axis=1)
+    assert relerr(got, ro[:, T1:]) <= 1e-2
+    assert relerr(host(hT), rh) <= 1e-5
