@@ -103,6 +103,8 @@ def main():
     ap.add_argument("--bwd-steps", type=int, default=5)
     ap.add_argument("--channel-steps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the copy and GEMM ceiling measurements")
     ap.add_argument("--cpu-tokens", type=int, default=65536,
                     help="tokens per head in the CPU-baseline sample")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -410,6 +412,40 @@ def main():
                          "alg_bytes_per_launch": cbytes, "kernel": "decode_channel_kernel"},
         }
         del d, S, xg
+
+    # ---- measured ceilings of this GPU beside the published peaks: a device
+    # copy (reads and writes every byte once) and a large bf16 GEMM (torch's
+    # library GEMM, contiguous operands)
+    if not args.no_ceilings:
+        nbytes = 2 << 30
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(10):
+            dst.copy_(src)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        copy_s = e0.elapsed_time(e1) / 10 * 1e-3
+        del src, dst
+        n = 8192
+        a = torch.randn((n, n), device=dev, dtype=torch.bfloat16)
+        bm = torch.randn((n, n), device=dev, dtype=torch.bfloat16)
+        c = a @ bm
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(10):
+            c = a @ bm
+        e1.record(stream)
+        torch.cuda.synchronize()
+        gemm_s = e0.elapsed_time(e1) / 10 * 1e-3
+        del a, bm, c
+        result["ceilings"] = {
+            "copy_GBps": 2 * nbytes / copy_s / 1e9, "copy_frac_of_peak": 2 * nbytes / copy_s / PEAK_HBM,
+            "bf16_gemm_TFLOPs": 2 * n ** 3 / gemm_s / 1e12,
+            "bf16_gemm_frac_of_peak": 2 * n ** 3 / gemm_s / PEAK_BF16,
+            "what": "device copy of 2 GiB (read + write) and an 8192^3 bf16 GEMM (torch), HIP events"}
 
     # ---- CPU baseline: the fp64 oracle (plain C recurrence) on host cores
     if not args.no_cpu_baseline:
