@@ -49,14 +49,18 @@ namespace {
 // One tile's record (bytes), in the workspace and in LDS; every field is
 // lane-contiguous in the order the chain wave reads it.  The workspace copy
 // stops at VF: the v values belong to a column slice and are loaded per slice.
-template <int DK>
+// EB is the byte size of the state-facing operands: 4 (fp32 fragments for the
+// fp32 MFMA) for fp32 inputs, 2 (bf16 fragments for the bf16 MFMA) for bf16
+// inputs; (K o Gam_C/Gam)^T takes 16 bytes per lane and state tile either way
+// (4 fp32, or 4 bf16 tokens twice, the A side of a hi/lo product).
+template <int DK, int EB>
 struct ChRec {
   static constexpr int NT = DK / 16;   // 16-row tiles of the state slice
   static constexpr int NS = DK / 32;   // 32-deep contraction blocks
-  static constexpr int KF = 0;                       // K o Gam:  NS x 64 lanes x 8 f32
-  static constexpr int QF = KF + NS * 64 * 8 * 4;    // Q o Gam:  NS x 64 x 8
-  static constexpr int KT = QF + NS * 64 * 8 * 4;    // (K o Gam_C/Gam)^T: NT x 64 x 4
-  static constexpr int PF = KT + NT * 64 * 4 * 4;    // P: 64 x 4
+  static constexpr int KF = 0;                       // K o Gam:  NS x 64 lanes x 8
+  static constexpr int QF = KF + NS * 64 * 8 * EB;   // Q o Gam:  NS x 64 x 8
+  static constexpr int KT = QF + NS * 64 * 8 * EB;   // (K o Gam_C/Gam)^T: NT x 64 x 16 B
+  static constexpr int PF = KT + NT * 64 * 16;       // P: 64 x 4 f32
   static constexpr int TB = PF + 64 * 4 * 4;         // (I + A)^-1 diag(beta), 16 x 16
   static constexpr int GC = TB + 256 * 4;            // Gam_C[DK]
   static constexpr int VF = GC + DK * 4;             // V slice: 64 x 4 (LDS only)
@@ -71,7 +75,7 @@ constexpr int kScrA = 0, kScrB = 1024, kScr = 1024 + 64;
 
 template <int DK, int NP>
 struct ChCfg {
-  static constexpr int LDS = 2 * NP * ChRec<DK>::LDS;
+  static constexpr int LDS = 2 * NP * ChRec<DK, 4>::LDS;   // the larger (fp32) layout
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
@@ -152,7 +156,7 @@ template <typename E, int DK>
 __device__ inline void prep_tile(const ChRaw<E, DK>& r, int c, int T, char* __restrict__ rec,
                                  float* sA, float* sB, int gate_logit, float G, int n, int grp,
                                  int lane) {
-  using R = ChRec<DK>;
+  using R = ChRec<DK, sizeof(E)>;
   using X = Elt<float>;
   using F16 = X::F16;
   using F32 = X::F32;
@@ -193,8 +197,14 @@ __device__ inline void prep_tile(const ChRaw<E, DK>& r, int c, int T, char* __re
         const int ch = 32 * s + (j < 4 ? 4 * grp + j : 16 + 4 * grp + j - 4);
         // (K o Gam_C/Gam)^T in the chain's A-fragment order: for state tile
         // ch / 16, lane (ch % 16, n / 4) register n % 4
-        reinterpret_cast<float*>(rec + R::KT)[((ch >> 4) * 64 + (n >> 2) * 16 + (ch & 15)) * 4 +
-                                              (n & 3)] = kv * e_end;
+        const int kt_lane = (ch >> 4) * 64 + (n >> 2) * 16 + (ch & 15);
+        if constexpr (sizeof(E) == 4) {
+          reinterpret_cast<float*>(rec + R::KT)[kt_lane * 4 + (n & 3)] = kv * e_end;
+        } else {   // token n in registers n % 4 and 4 + n % 4 of its lane
+          const __bf16 kd = (__bf16)(kv * e_end);
+          reinterpret_cast<__bf16*>(rec + R::KT)[kt_lane * 8 + (n & 3)] = kd;
+          reinterpret_cast<__bf16*>(rec + R::KT)[kt_lane * 8 + 4 + (n & 3)] = kd;
+        }
         if (n == 0) reinterpret_cast<float*>(rec + R::GC)[ch] = e_last;
       }
       F32 kg, qg, km, qm, ki;
@@ -206,8 +216,19 @@ __device__ inline void prep_tile(const ChRaw<E, DK>& r, int c, int T, char* __re
         qm.lo[j] = vqm[j]; qm.hi[j] = vqm[4 + j];
         ki.lo[j] = vki[j]; ki.hi[j] = vki[4 + j];
       }
-      reinterpret_cast<F32*>(rec + R::KF)[s * 64 + lane] = kg;
-      reinterpret_cast<F32*>(rec + R::QF)[s * 64 + lane] = qg;
+      if constexpr (sizeof(E) == 4) {
+        reinterpret_cast<F32*>(rec + R::KF)[s * 64 + lane] = kg;
+        reinterpret_cast<F32*>(rec + R::QF)[s * 64 + lane] = qg;
+      } else {
+        Elt<__bf16>::F32 kb, qb;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          kb.v[j] = (__bf16)vkg[j];
+          qb.v[j] = (__bf16)vqg[j];
+        }
+        reinterpret_cast<Elt<__bf16>::F32*>(rec + R::KF)[s * 64 + lane] = kb;
+        reinterpret_cast<Elt<__bf16>::F32*>(rec + R::QF)[s * 64 + lane] = qb;
+      }
       sa = X::mma32(ki, km, sa);
       sp = X::mma32(ki, qm, sp);
     }
@@ -273,7 +294,8 @@ __global__ __launch_bounds__(256) void chunk_channel_prep_kernel(
     const int h = (int)(bh % H), b = (int)(bh / H);
     ChRaw<E, DK> r;
     load_tile<E, DK>(r, q, k, gate, beta, b, h, c, T, H, n, grp);
-    prep_tile<E, DK>(r, c, T, ws + job * ChRec<DK>::GLOBAL, sA, sB, gate_logit, G, n, grp, lane);
+    prep_tile<E, DK>(r, c, T, ws + job * ChRec<DK, sizeof(E)>::GLOBAL, sA, sB, gate_logit, G, n,
+                     grp, lane);
     // the next job's writes to A / beta must not pass this job's reads
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -304,7 +326,7 @@ __device__ inline void ch_map_block(int n, int NH, int NV, int& head, int& vt) {
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 template <typename E, int DK>
 struct ChCopy {
-  static constexpr int PIECES = (ChRec<DK>::CHUNKS + 63) / 64;
+  static constexpr int PIECES = (ChRec<DK, sizeof(E)>::CHUNKS + 63) / 64;
   u32x4 piece[PIECES];
   E vv[4];
 };
@@ -314,7 +336,7 @@ template <typename E, int DK, int NP>
 __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_channel_kernel(
     const E* __restrict__ v, const char* __restrict__ ws, const float* h0,
     E* __restrict__ o, float* hT, int B, int T, int H, int DV) {
-  using R = ChRec<DK>;
+  using R = ChRec<DK, sizeof(E)>;
   using C = ChCfg<DK, NP>;
   using X = Elt<float>;
   using F16 = X::F16;
@@ -354,15 +376,26 @@ __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_channel_kernel(
         const int c = ep * NP + j;
         if (c >= NC) break;
         const char* rec = rec_of(ep, j);
-        // R = (K o Gam) H and (Q o Gam) H, contraction over d_k
+        // R = (K o Gam) H and (Q o Gam) H, contraction over d_k: fp32 MFMA
+        // for fp32 inputs; bf16 MFMA on the bf16 operands and a bf16 copy of
+        // the state for bf16 inputs
         f32x4 Rk = zero4(), QH = zero4();
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-          const F32 hb = X::from_acc2(Hacc[2 * s], Hacc[2 * s + 1]);
-          const F32 kf = reinterpret_cast<const F32*>(rec + R::KF)[s * 64 + lane];
-          const F32 qf = reinterpret_cast<const F32*>(rec + R::QF)[s * 64 + lane];
-          Rk = X::mma32(kf, hb, Rk);
-          QH = X::mma32(qf, hb, QH);
+          if constexpr (sizeof(E) == 4) {
+            const F32 hb = X::from_acc2(Hacc[2 * s], Hacc[2 * s + 1]);
+            const F32 kf = reinterpret_cast<const F32*>(rec + R::KF)[s * 64 + lane];
+            const F32 qf = reinterpret_cast<const F32*>(rec + R::QF)[s * 64 + lane];
+            Rk = X::mma32(kf, hb, Rk);
+            QH = X::mma32(qf, hb, QH);
+          } else {
+            using XB = Elt<__bf16>;
+            const XB::F32 hb = XB::from_acc2(Hacc[2 * s], Hacc[2 * s + 1]);
+            const XB::F32 kf = reinterpret_cast<const XB::F32*>(rec + R::KF)[s * 64 + lane];
+            const XB::F32 qf = reinterpret_cast<const XB::F32*>(rec + R::QF)[s * 64 + lane];
+            Rk = XB::mma32(kf, hb, Rk);
+            QH = XB::mma32(qf, hb, QH);
+          }
         }
         const F16 vf = reinterpret_cast<const F16*>(rec + R::VF)[lane];
         const F16 tb = *reinterpret_cast<const F16*>(rec + R::TB + (n * 16 + 4 * grp) * 4);
@@ -376,14 +409,35 @@ __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_channel_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           if (16 * c + 4 * grp + i < T) oc[i * ostride] = Elt<E>::from_f(O[i]);
-        const F16 ub = X::from_acc(U);
+        if constexpr (sizeof(E) == 4) {
+          const F16 ub = X::from_acc(U);
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const f32x4 gc = reinterpret_cast<const f32x4*>(rec + R::GC)[4 * t + grp];
-          const F16 kt = reinterpret_cast<const F16*>(rec + R::KT)[t * 64 + lane];
+          for (int t = 0; t < NT; ++t) {
+            const f32x4 gc = reinterpret_cast<const f32x4*>(rec + R::GC)[4 * t + grp];
+            const F16 kt = reinterpret_cast<const F16*>(rec + R::KT)[t * 64 + lane];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) Hacc[t][i] *= gc[i];   // row 16t + 4grp + i
-          Hacc[t] = X::mma16(kt, ub, Hacc[t]);
+            for (int i = 0; i < 4; ++i) Hacc[t][i] *= gc[i];   // row 16t + 4grp + i
+            Hacc[t] = X::mma16(kt, ub, Hacc[t]);
+          }
+        } else {
+          // H' += (K o Gam_C/Gam)^T (U_hi + U_lo): U split into bf16 high and
+          // low parts, one 32-deep bf16 MFMA per state tile
+          using XB = Elt<__bf16>;
+          XB::F32 ub;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const __bf16 hi = (__bf16)U[i];
+            ub.v[i] = hi;
+            ub.v[4 + i] = (__bf16)(U[i] - (float)hi);
+          }
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            const f32x4 gc = reinterpret_cast<const f32x4*>(rec + R::GC)[4 * t + grp];
+            const XB::F32 kt = reinterpret_cast<const XB::F32*>(rec + R::KT)[t * 64 + lane];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Hacc[t][i] *= gc[i];   // row 16t + 4grp + i
+            Hacc[t] = XB::mma32(kt, ub, Hacc[t]);
+          }
         }
       }
       __syncthreads();  // this epoch consumed, next epoch loaded
@@ -568,9 +622,10 @@ hipError_t launch_dec_ch(const void* q, const void* k, const void* v, const floa
 
 }  // namespace
 
-long long chunk_channel_workspace_bytes(int B, int T, int H, int Dk) {
+long long chunk_channel_workspace_bytes(int B, int T, int H, int Dk, int fp32) {
   const long long nc = (T + 15) / 16;
-  const long long rec = Dk == 64 ? ChRec<64>::GLOBAL : ChRec<128>::GLOBAL;
+  const long long rec = fp32 ? (Dk == 64 ? ChRec<64, 4>::GLOBAL : ChRec<128, 4>::GLOBAL)
+                             : (Dk == 64 ? ChRec<64, 2>::GLOBAL : ChRec<128, 2>::GLOBAL);
   return (long long)B * H * nc * rec;
 }
 

@@ -50,9 +50,10 @@ hipError_t launch_chunk_bwd(const void* q, const void* k, const void* v, const v
 // the fp32 state at the tile start and the fp32 gradient of its end state.
 long long chunk_bwd_workspace_bytes(int B, int T, int H, int Dk, int Dv);
 
-// Per-channel gate (gate [B, T, H, Dk]), fp32 arithmetic; q, k, v, o bf16 or
-// fp32 as `fp32` says: a parallel tile-preparation kernel into the workspace,
-// then the serial kernel.
+// Per-channel gate (gate [B, T, H, Dk]); q, k, v, o bf16 or fp32 as `fp32`
+// says: a parallel tile-preparation kernel into the workspace, then the
+// serial kernel (fp32 MFMA throughout for fp32 inputs; bf16 MFMA for the
+// state products, hi/lo for U, for bf16 inputs).
 hipError_t launch_chunk_fwd_channel(const void* q, const void* k, const void* v,
                                     const float* gate, int gate_logit, float G,
                                     const float* beta, const float* h0, void* o, float* hT,
@@ -60,7 +61,7 @@ hipError_t launch_chunk_fwd_channel(const void* q, const void* k, const void* v,
                                     hipStream_t st);
 
 // Workspace bytes of the per-channel path: one record per tile and head.
-long long chunk_channel_workspace_bytes(int B, int T, int H, int Dk);
+long long chunk_channel_workspace_bytes(int B, int T, int H, int Dk, int fp32);
 
 // Decode step with a per-channel gate (gate [B*H, Dk]), state in place.
 hipError_t launch_decode_channel(const void* q, const void* k, const void* v,

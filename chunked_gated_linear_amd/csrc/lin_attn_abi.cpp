@@ -97,8 +97,8 @@ long long chunk_workspace(int B, int T, int H, int Dk, int Dv, int dtype) {
   return dtype == LA_BF16 ? la::chunk_pair_workspace_bytes(B, T, H, Dk, Dv) : 0;
 }
 
-long long channel_workspace(int B, int T, int H, int Dk) {
-  return T > 0 ? la::chunk_channel_workspace_bytes(B, T, H, Dk) : 0;
+long long channel_workspace(int B, int T, int H, int Dk, int dtype) {
+  return T > 0 ? la::chunk_channel_workspace_bytes(B, T, H, Dk, dtype == LA_FP32) : 0;
 }
 
 }  // namespace
@@ -138,7 +138,7 @@ int chunk_fwd(const void* q, const void* k, const void* v, const float* gate, in
   if (B == 0 || H == 0) return ok();
   const unsigned ea = dtype == LA_BF16 ? 2u : 4u;
   const long long wsz = T <= 0 ? 0
-                        : channel ? channel_workspace(B, T, H, Dk)
+                        : channel ? channel_workspace(B, T, H, Dk, dtype)
                                   : chunk_workspace(B, T, H, Dk, Dv, dtype);
   const int64_t ngate = channel ? ntok * Dk : ntok;   // gate elements
   if (T > 0) {
@@ -211,7 +211,7 @@ long long lin_attn_chunk_fwd_channel_workspace_size(int B, int T, int H, int Dk,
                                                    int dtype) {
   if (check_chunk_sizes(B, T, H, Dk, Dv, dtype)) return -1;
   ok();
-  return channel_workspace(B, T, H, Dk);
+  return channel_workspace(B, T, H, Dk, dtype);
 }
 
 int lin_attn_chunk_fwd_channel(const void* q, const void* k, const void* v, const float* gate,

@@ -161,7 +161,9 @@ int lin_attn_chunk_fwd_raw(const void* q, const void* k, const void* v,
  *
  * i.e. the decay acts on the key side of the old state first, then the
  * delta-rule erase and write act on the decayed state; with every channel
- * equal it is lin_attn_chunk_fwd.  Arithmetic is float32 for both dtypes.
+ * equal it is lin_attn_chunk_fwd.  LA_FP32 computes in float32 throughout;
+ * LA_BF16 forms the tile operators in float32 and runs the products with the
+ * carried state on bf16 matrix cores (float32 state and accumulation).
  * Arguments, layouts, alignment, aliasing rules, tail handling and errors as
  * lin_attn_chunk_fwd, except: the workspace holds one record per tile and
  * head (lin_attn_chunk_fwd_channel_workspace_size bytes, for both dtypes), and
@@ -175,9 +177,10 @@ int lin_attn_chunk_fwd_channel(const void* q, const void* k, const void* v,
 
 /*
  * lin_attn_chunk_fwd_channel_workspace_size -- device workspace bytes of
- * lin_attn_chunk_fwd_channel: B * H * ceil(T / 16) * R with R = 27,136 for
- * Dk = 128 and 14,592 for Dk = 64 (the state-independent operators of each
- * 16-token tile, prepared once per head); 0 when T = 0; -1 (with
+ * lin_attn_chunk_fwd_channel: B * H * ceil(T / 16) * R, with R (Dk = 128 / 64)
+ * = 27,136 / 14,592 for LA_FP32 and 18,944 / 10,496 for LA_BF16 (the
+ * state-independent operators of each 16-token tile, prepared once per head);
+ * 0 when T = 0; -1 (with
  * lin_attn_last_error() set) for invalid or unsupported sizes.
  */
 long long lin_attn_chunk_fwd_channel_workspace_size(int B, int T, int H, int Dk, int Dv,

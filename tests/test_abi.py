@@ -346,7 +346,9 @@ def test_chunk_fwd_channel_empty_is_noop():
 
 def test_chunk_fwd_channel_workspace_size():
     L = N.lib()
-    assert L.lin_attn_chunk_fwd_channel_workspace_size(1, 64, 2, 128, 128, 0) == 2 * 4 * 27136
+    assert L.lin_attn_chunk_fwd_channel_workspace_size(1, 64, 2, 128, 128, 0) == 2 * 4 * 18944
+    assert L.lin_attn_chunk_fwd_channel_workspace_size(1, 64, 2, 128, 128, 1) == 2 * 4 * 27136
+    assert L.lin_attn_chunk_fwd_channel_workspace_size(1, 16, 1, 64, 64, 0) == 10496
     assert L.lin_attn_chunk_fwd_channel_workspace_size(2, 17, 3, 64, 32, 1) == 2 * 3 * 2 * 14592
     assert L.lin_attn_chunk_fwd_channel_workspace_size(1, 0, 2, 128, 128, 0) == 0
     assert L.lin_attn_chunk_fwd_channel_workspace_size(1, 64, 2, 96, 128, 0) == -1

@@ -2,9 +2,8 @@
 through the C ABI) against the fp64 oracle recurrent_fwd_channel.
 
 Error per output tensor: max |x - ref| / max |ref|.  Bars: 1e-5 for fp32
-inputs; for bf16 inputs 1e-2 on o (rounded to bf16 on output) and 1e-5 on hT
-(the pass computes in float32 from the exact input values, and hT stays
-float32).  Gate regimes per channel: x ~ N(0,1) (sum of g per tile ~ -40),
+inputs (float32 throughout); 1e-2 on o and hT for bf16 inputs (the products
+with the carried state run on bf16 matrix cores with a float32 state).  Gate regimes per channel: x ~ N(0,1) (sum of g per tile ~ -40),
 x ~ N(-8,1) (weak decay: the state carries over thousands of tokens),
 x ~ N(+4,2) and N(-4,2) (the stress variants), g = -5 and g = 0 exactly, and
 channels alternating between -5 and 0.
@@ -83,8 +82,8 @@ def test_channel_parity(case):
     eo, eh = relerr(host(o), ro), relerr(host(hT), rh)
     say(f"  err(o)={eo:.2e} err(hT)={eh:.2e}")
     assert np.isfinite(host(o)).all() and np.isfinite(host(hT)).all()
-    assert eo <= (1e-5 if dtype == "fp32" else 1e-2)
-    assert eh <= 1e-5
+    tol = 1e-5 if dtype == "fp32" else 1e-2
+    assert eo <= tol and eh <= tol
 
 
 def test_channel_constant_gate_matches_scalar_path():
@@ -130,7 +129,7 @@ def test_channel_long_64k_sampled_heads(regime):
         eo = relerr(host(o[sl]), ro)
         eh = relerr(host(hT[:, h:h + 1]), rh)
         say(f"  head {h}: err(o)={eo:.2e} err(hT)={eh:.2e}")
-        assert eo <= 1e-2 and eh <= 1e-5
+        assert eo <= 1e-2 and eh <= 1e-2
 
 
 def test_channel_hT_in_place_of_h0():
@@ -189,4 +188,4 @@ def test_channel_prefill_hands_off_to_decode():
                                        host(inp["beta"]).astype(np.float64), None)
     got = np.stack([host(o) for o in outs], axis=1)
     assert relerr(got, ro[:, T1:]) <= 1e-2
-    assert relerr(host(hT), rh) <= 1e-5
+    assert relerr(host(hT), rh) <= 1e-2
