@@ -694,11 +694,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grad_kernel(BwdArgs a) {
   for (int r = 0; r < RT; ++r) dQa[r] = dKa[r] = zero4();
 
   const int NV = a.Dv / 16;
-  // this thread's share of a slice of H and dH' (rows tid / 16 + 16 x, column
-  // tid % 16), loaded one slice ahead
+  // this thread's share of a slice -- H and dH' (rows tid / 16 + 16 x, column
+  // tid % 16), and v and dO of token t, column j -- loaded one slice ahead
   constexpr int SP = DK * 16 / kBwdThreads;
-  float nh[SP], nd[SP];
+  float nh[SP], nd[SP], nv, ndo;
   auto fetch_slice = [&](int jb) {
+    nv = live ? ld1(vp + row_idx * a.Dv + 16 * jb + j) : 0.f;
+    ndo = live ? ld1(dop + row_idx * a.Dv + 16 * jb + j) : 0.f;
 #pragma unroll
     for (int x = 0; x < SP; ++x) {
       const int64_t at = (int64_t)((tid >> 4) + 16 * x) * a.Dv + 16 * jb + (tid & 15);
@@ -716,9 +718,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grad_kernel(BwdArgs a) {
       sD[rr][jj] = nd[x];
       hdh += nh[x] * nd[x];
     }
+    sV[t][j] = nv;
+    sDO[t][j] = ndo;
     if (jb + 1 < NV) fetch_slice(jb + 1);
-    sV[t][j] = live ? ld1(vp + row_idx * a.Dv + col + j) : 0.f;
-    sDO[t][j] = live ? ld1(dop + row_idx * a.Dv + col + j) : 0.f;
     __syncthreads();
     // K H, Q H and K dH' of this column slice (16 x 16, over d_k), one wave each
     if (w < 3) {
