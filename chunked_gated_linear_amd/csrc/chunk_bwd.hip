@@ -45,6 +45,12 @@ namespace {
 constexpr int kT = 16;          // tokens per tile
 constexpr int kBwdThreads = 256;
 
+// Workspace: per tile and head a record (below), then the fp32 state at every
+// tile start (hs) and the gradient of every tile's end state (dhs), each
+// d_k x d_v per tile and head, stored per 16-column slice in MFMA fragment
+// order: element (row r, column 16 jb + n) of tile block (bh, c) sits at
+// float ((jb * d_k / 16 + r / 16) * 64 + 16 ((r % 16) / 4) + n) * 4 + r % 4,
+// so the serial kernels store whole 16-byte fragments.
 // Record of one tile (floats).
 struct BRec {
   static constexpr int TINV = 0;     // (I + A)^-1, row-major 16 x 16
@@ -280,12 +286,11 @@ __global__ __launch_bounds__(64 * (NP + 1)) void bwd_hstates_mfma_kernel(BwdArgs
         const int c = ep * NP + j;
         if (c >= NC) break;
         const char* rec = rec_of(c);
-        float* hsp = a.hs + (bh * NC + c) * (int64_t)DK * a.Dv + v0 + n;
+        // the state at the tile start, in fragment order (see BRec)
+        f32x4* hsp = reinterpret_cast<f32x4*>(a.hs + (bh * NC + c) * (int64_t)DK * a.Dv +
+                                              (int64_t)(v0 / 16) * DK * 16);
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) hsp[(int64_t)(16 * t + 4 * grp + i) * a.Dv] = Hacc[t][i];
-        }
+        for (int t = 0; t < NT; ++t) hsp[t * 64 + lane] = Hacc[t];
         f32x4 Rk = zero4();
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
@@ -472,12 +477,10 @@ __global__ __launch_bounds__(64 * (NP + SPW)) void bwd_dh_mfma_kernel(BwdArgs a)
         if (m >= NC) break;
         const int c = NC - 1 - m;
         const char* rec = rec_of(m);
-        float* dsp = a.dhs + (bh * NC + c) * (int64_t)DK * a.Dv + v0 + n;
+        f32x4* dsp = reinterpret_cast<f32x4*>(a.dhs + (bh * NC + c) * (int64_t)DK * a.Dv +
+                                              (int64_t)(v0 / 16) * DK * 16);
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) dsp[(int64_t)(16 * t + 4 * grp + i) * a.Dv] = D[t][i];
-        }
+        for (int t = 0; t < NT; ++t) dsp[t * 64 + lane] = D[t];
         f32x4 KD = zero4();
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
@@ -694,29 +697,37 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grad_kernel(BwdArgs a) {
   for (int r = 0; r < RT; ++r) dQa[r] = dKa[r] = zero4();
 
   const int NV = a.Dv / 16;
-  // this thread's share of a slice -- H and dH' (rows tid / 16 + 16 x, column
-  // tid % 16), and v and dO of token t, column j -- loaded one slice ahead
-  constexpr int SP = DK * 16 / kBwdThreads;
-  float nh[SP], nd[SP], nv, ndo;
+  // this thread's share of a slice -- fragments tid and tid + 256 of H and of
+  // dH' (16 bytes each: rows 16 (f / 64) + 4 ((f % 64) / 16) + 0..3, column
+  // f % 16, for fragment f), and v and dO of token t, column j -- loaded one
+  // slice ahead
+  constexpr int SF = DK * 16 / 4 / kBwdThreads;   // fragments per thread
+  f32x4 nh[SF], nd[SF];
+  float nv, ndo;
   auto fetch_slice = [&](int jb) {
     nv = live ? ld1(vp + row_idx * a.Dv + 16 * jb + j) : 0.f;
     ndo = live ? ld1(dop + row_idx * a.Dv + 16 * jb + j) : 0.f;
+    const f32x4* hf = reinterpret_cast<const f32x4*>(Hb + (int64_t)jb * DK * 16);
+    const f32x4* df = reinterpret_cast<const f32x4*>(Db + (int64_t)jb * DK * 16);
 #pragma unroll
-    for (int x = 0; x < SP; ++x) {
-      const int64_t at = (int64_t)((tid >> 4) + 16 * x) * a.Dv + 16 * jb + (tid & 15);
-      nh[x] = Hb[at];
-      nd[x] = Db[at];
+    for (int y = 0; y < SF; ++y) {
+      nh[y] = hf[tid + kBwdThreads * y];
+      nd[y] = df[tid + kBwdThreads * y];
     }
   };
   fetch_slice(0);
   for (int jb = 0; jb < NV; ++jb) {
     const int col = 16 * jb;
 #pragma unroll
-    for (int x = 0; x < SP; ++x) {
-      const int rr = (tid >> 4) + 16 * x, jj = tid & 15;
-      sH[rr][jj] = nh[x];
-      sD[rr][jj] = nd[x];
-      hdh += nh[x] * nd[x];
+    for (int y = 0; y < SF; ++y) {
+      const int f = tid + kBwdThreads * y;
+      const int r0 = 16 * (f >> 6) + 4 * ((f & 63) >> 4), cc = f & 15;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sH[r0 + i][cc] = nh[y][i];
+        sD[r0 + i][cc] = nd[y][i];
+        hdh += nh[y][i] * nd[y][i];
+      }
     }
     sV[t][j] = nv;
     sDO[t][j] = ndo;
