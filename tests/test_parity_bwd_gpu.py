@@ -121,3 +121,40 @@ def test_bwd_long_64k_tail_tiles():
         e = relerr(host(x[:, t0:]), r)
         say(f"  {name} tail err={e:.2e}")
         assert e <= TOL_BWD, f"{name}: error {e}"
+
+
+def test_bwd_graph_capture_replays():
+    """The reverse pass (four launches) captured in a graph replays to the
+    eager gradients, replay after replay, with eager work between replays."""
+    from chunked_gated_linear_amd import lin_attn_chunk_bwd_workspace_size
+    say("graph capture: reverse pass B1 H2 T600, 3 replays")
+    B, T, H, D = 1, 600, 2, 128
+    dev_args, _ = make_case(B, T, H, D, D, "bf16", "weak", "logit", 0.02, seed=50)
+    up = I.make_upstream_grads(B, T, H, D, D, dtype="bf16", seed=50, device="cuda")
+    ws = torch.empty(lin_attn_chunk_bwd_workspace_size(B, T, H, D, D), dtype=torch.uint8,
+                     device="cuda")
+
+    def work():
+        return lin_attn_chunk_bwd(dev_args["q"], dev_args["k"], dev_args["v"], dev_args["gate"],
+                                  dev_args["beta"], up["dout"], dev_args["h0"], up["dhT"],
+                                  gate_mode="logit", G=5.0, workspace=ws)
+
+    ref = [x.clone() for x in work()]
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            outs = work()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for x in outs:
+            x.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, x, r in zip(NAMES, outs, ref):
+            assert torch.equal(x, r), (name, rep)
+        run_bwd(dev_args, up)                     # eager work between replays

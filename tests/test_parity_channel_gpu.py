@@ -189,3 +189,52 @@ def test_channel_prefill_hands_off_to_decode():
     got = np.stack([host(o) for o in outs], axis=1)
     assert relerr(got, ro[:, T1:]) <= 1e-2
     assert relerr(host(hT), rh) <= 1e-2
+
+
+def test_channel_graph_capture_replays():
+    """The per-channel forward (two launches) and decode steps captured in one
+    graph replay to the eager results, replay after replay, with eager work
+    and synchronisations between the replays."""
+    from chunked_gated_linear_amd import lin_attn_chunk_fwd_channel_workspace_size
+    say("graph capture: per-channel forward B1 H4 T3000 + 2 decode steps, 3 replays")
+    inp, gate, _ = make(1, 3000, 4, 128, 128, "bf16", "weak", "logit", 0.02, seed=48)
+    ws = torch.empty(lin_attn_chunk_fwd_channel_workspace_size(1, 3000, 4, 128, 128),
+                     dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(inp["v"])
+    hT = torch.empty((1, 4, 128, 128), dtype=torch.float32, device="cuda")
+    d = I.make_decode_inputs(8, 4, 128, 128, dtype="bf16", seed=49, device="cuda", steps=2)
+    xd = I.make_channel_gate(2, 8, 4, 128, seed=49, device="cuda")
+    S0 = d["S"].clone()
+    S = S0.clone()
+    od = torch.empty((8, 4, 128), dtype=torch.bfloat16, device="cuda")
+
+    def work():
+        lin_attn_chunk_fwd_channel(inp["q"], inp["k"], inp["v"], gate, inp["beta"], inp["h0"],
+                                   gate_mode="logit", o=o, hT=hT, workspace=ws)
+        for st in range(2):
+            lin_attn_decode_step_channel(d["q"][st], d["k"][st], d["v"][st], xd[st], d["beta"][st],
+                                         S, gate_mode="logit", o=od)
+
+    work()
+    torch.cuda.synchronize()
+    o_ref, h_ref, S_ref, od_ref = o.clone(), hT.clone(), S.clone(), od.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        S.copy_(S0)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            work()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        o.zero_()
+        hT.zero_()
+        S.copy_(S0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(hT, h_ref), rep
+        assert torch.equal(S, S_ref) and torch.equal(od, od_ref), rep
+        lin_attn_chunk_fwd_channel(inp["q"], inp["k"], inp["v"], gate, inp["beta"], None,
+                                   gate_mode="logit")          # eager work between replays
