@@ -27,6 +27,9 @@ SIGNATURES = {
     "lin_attn_chunk_fwd_channel": (_I, [_P, _P, _P, _P, _I, _F, _P, _P, _P, _P,
                                         _I, _I, _I, _I, _I, _I, _P, _LL, _P]),
     "lin_attn_chunk_fwd_channel_workspace_size": (_LL, [_I, _I, _I, _I, _I, _I]),
+    "lin_attn_chunk_fwd_channel_varlen": (_I, [_P, _P, _P, _P, _I, _F, _P, _P, _P, _P, _P, _I,
+                                               _I, _I, _I, _I, _I, _P, _LL, _P]),
+    "lin_attn_chunk_fwd_channel_varlen_workspace_size": (_LL, [_I, _I, _I, _I, _I, _I]),
     "lin_attn_chunk_fwd_varlen": (_I, [_P, _P, _P, _P, _I, _F, _P, _P, _P, _P, _P, _I,
                                        _I, _I, _I, _I, _I, _P, _LL, _P]),
     "lin_attn_chunk_fwd_varlen_workspace_size": (_LL, [_I, _I, _I, _I, _I, _I]),

@@ -132,6 +132,53 @@ def lin_attn_chunk_fwd_channel(q, k, v, gate, beta, h0=None, *, gate_mode="log",
     return o, hT
 
 
+def lin_attn_chunk_fwd_channel_varlen_workspace_size(T, nseq, H, Dk, Dv, dtype=torch.bfloat16):
+    """Workspace bytes lin_attn_chunk_fwd_channel_varlen needs for these sizes."""
+    n = N.lib().lin_attn_chunk_fwd_channel_varlen_workspace_size(T, nseq, H, Dk, Dv,
+                                                                 _DTYPES[dtype])
+    if n < 0:
+        raise N.LinAttnError(N.LA_EINVAL, N.lib().lin_attn_last_error().decode())
+    return n
+
+
+def lin_attn_chunk_fwd_channel_varlen(q, k, v, gate, beta, cu_seqlens, h0=None, *,
+                                      gate_mode="log", G=5.0, o=None, hT=None,
+                                      output_final_state=True, workspace=None, stream=None):
+    """Per-channel gate over packed sequences: q, k [1,T,H,Dk], v [1,T,H,Dv],
+    gate [1,T,H,Dk], beta [1,T,H], cu_seqlens int32 [nseq+1] on the device.
+    Returns o [1,T,H,Dv] and hT [nseq,H,Dk,Dv] (None if not requested)."""
+    _need(q, "q")
+    if q.dtype not in _DTYPES:
+        raise TypeError("q, k, v must be bfloat16 or float32")
+    one, T, H, Dk = q.shape
+    if one != 1:
+        raise ValueError("packed sequences come as one batch entry: q is [1, T, H, Dk]")
+    Dv = v.shape[-1]
+    _need(k, "k", q.dtype, (1, T, H, Dk))
+    _need(v, "v", q.dtype, (1, T, H, Dv))
+    _need(gate, "gate", torch.float32, (1, T, H, Dk))
+    _need(beta, "beta", torch.float32, (1, T, H))
+    _need(cu_seqlens, "cu_seqlens", torch.int32)
+    nseq = cu_seqlens.numel() - 1
+    if h0 is not None:
+        _need(h0, "h0", torch.float32, (nseq, H, Dk, Dv))
+    if o is None:
+        o = torch.empty((1, T, H, Dv), dtype=q.dtype, device=q.device)
+    _need(o, "o", q.dtype, (1, T, H, Dv))
+    if hT is None and output_final_state:
+        hT = torch.empty((nseq, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    if hT is not None:
+        _need(hT, "hT", torch.float32, (nseq, H, Dk, Dv))
+    nws = lin_attn_chunk_fwd_channel_varlen_workspace_size(T, nseq, H, Dk, Dv, q.dtype)
+    if workspace is None and nws > 0:
+        workspace = torch.empty(nws, dtype=torch.uint8, device=q.device)
+    N.check(N.lib().lin_attn_chunk_fwd_channel_varlen(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _GATE[gate_mode], float(G), _ptr(beta), _ptr(h0),
+        _ptr(o), _ptr(hT), _ptr(cu_seqlens), nseq, T, H, Dk, Dv, _DTYPES[q.dtype],
+        _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(q, stream)))
+    return o, hT
+
+
 def lin_attn_chunk_bwd_workspace_size(B, T, H, Dk, Dv, dtype=torch.bfloat16):
     """Workspace bytes lin_attn_chunk_bwd needs for these sizes."""
     n = N.lib().lin_attn_chunk_bwd_workspace_size(B, T, H, Dk, Dv, _DTYPES[dtype])

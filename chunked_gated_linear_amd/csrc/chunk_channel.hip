@@ -118,16 +118,17 @@ __device__ inline Elt<float>::F32 to_f32(const Elt<__bf16>::F32& a) {
   return r;
 }
 
-// Loads of tile c of sequence-head (b, h) (token rows past the end read the
-// last valid row; prep_tile zeroes them).
+// Loads of tile c of a sequence of T tokens whose token t is row
+// (tok0 + t) * H + h of the arrays (token rows past the end read the last
+// valid row; prep_tile zeroes them).
 template <typename E, int DK>
 __device__ inline void load_tile(ChRaw<E, DK>& r, const E* __restrict__ q,
                                  const E* __restrict__ k, const float* __restrict__ gate,
-                                 const float* __restrict__ beta, int b, int h, int c, int T,
-                                 int H, int n, int grp) {
+                                 const float* __restrict__ beta, int64_t tok0, int h, int c,
+                                 int T, int H, int n, int grp) {
   constexpr int NS = DK / 32;
   const int t = min(16 * c + n, T - 1);
-  const int64_t row = ((int64_t)b * T + t) * H + h;
+  const int64_t row = (tok0 + t) * H + h;
   const int64_t base = row * DK;
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
@@ -274,12 +275,27 @@ __device__ inline void prep_tile(const ChRaw<E, DK>& r, int c, int T, char* __re
     }
 }
 
+static inline int channel_varlen_slots(int T, int nseq) { return T / 16 + nseq + 1; }
+
+// Packed sequences: sequence s is tokens [cu[s], cu[s+1]) of one packed
+// sequence of TB tokens (offsets clamped to [0, TB] so that any values stay
+// memory-safe); its tile c has workspace record slot(s, c) = floor(cu[s] / 16)
+// + s + c of nslot per head (slots of different sequences do not overlap for
+// non-decreasing offsets, and nslot = TB / 16 + nseq + 1 covers them all).
+__device__ inline int ch_seq_begin(const int* cu, int s, int TB) { return min(max(cu[s], 0), TB); }
+__device__ inline int ch_seq_end(const int* cu, int s, int TB) {
+  return min(max(cu[s + 1], ch_seq_begin(cu, s, TB)), TB);
+}
+
 // ------------------------------------------------------------- prep kernel
+// Batched (cu == nullptr): job = (b H + h) NC + c.  Packed: job = h nslot +
+// slot, the sequence found by binary search over the offsets, unused slots
+// skipped.
 template <typename E, int DK>
 __global__ __launch_bounds__(256) void chunk_channel_prep_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const float* __restrict__ gate,
     int gate_logit, float G, const float* __restrict__ beta, char* __restrict__ ws, int B,
-    int T, int H) {
+    int T, int H, const int* __restrict__ cu, int nslot) {
   __shared__ __attribute__((aligned(16))) char smem[4 * kScr];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -287,15 +303,35 @@ __global__ __launch_bounds__(256) void chunk_channel_prep_kernel(
   float* sA = reinterpret_cast<float*>(smem + wave * kScr + kScrA);
   float* sB = reinterpret_cast<float*>(smem + wave * kScr + kScrB);
   const int NC = (T + 15) >> 4;
-  const int64_t jobs = (int64_t)B * H * NC;
+  const int64_t jobs = cu ? (int64_t)H * nslot : (int64_t)B * H * NC;
   for (int64_t job = (int64_t)blockIdx.x * 4 + wave; job < jobs; job += (int64_t)gridDim.x * 4) {
-    const int c = (int)(job % NC);
-    const int64_t bh = job / NC;
-    const int h = (int)(bh % H), b = (int)(bh / H);
+    int c, h, Ts;
+    int64_t tok0;
+    if (cu) {
+      h = (int)(job / nslot);
+      const int slot = (int)(job - (int64_t)h * nslot);
+      int lo = 0, hi = B - 1;                    // the last s with slot(s, 0) <= slot
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (ch_seq_begin(cu, mid, T) / 16 + mid <= slot) lo = mid;
+        else hi = mid - 1;
+      }
+      const int tb = ch_seq_begin(cu, lo, T);
+      Ts = ch_seq_end(cu, lo, T) - tb;
+      c = slot - (tb / 16 + lo);
+      if (c < 0 || c >= ((Ts + 15) >> 4)) continue;   // a slot no tile uses
+      tok0 = tb;
+    } else {
+      c = (int)(job % NC);
+      const int64_t bh = job / NC;
+      h = (int)(bh % H);
+      tok0 = (bh / H) * (int64_t)T;
+      Ts = T;
+    }
     ChRaw<E, DK> r;
-    load_tile<E, DK>(r, q, k, gate, beta, b, h, c, T, H, n, grp);
-    prep_tile<E, DK>(r, c, T, ws + job * ChRec<DK, sizeof(E)>::GLOBAL, sA, sB, gate_logit, G, n,
-                     grp, lane);
+    load_tile<E, DK>(r, q, k, gate, beta, tok0, h, c, Ts, H, n, grp);
+    prep_tile<E, DK>(r, c, Ts, ws + job * ChRec<DK, sizeof(E)>::GLOBAL, sA, sB, gate_logit, G,
+                     n, grp, lane);
     // the next job's writes to A / beta must not pass this job's reads
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -335,7 +371,8 @@ struct ChCopy {
 template <typename E, int DK, int NP>
 __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_channel_kernel(
     const E* __restrict__ v, const char* __restrict__ ws, const float* h0,
-    E* __restrict__ o, float* hT, int B, int T, int H, int DV) {
+    E* __restrict__ o, float* hT, int B, int TA, int H, int DV, const int* __restrict__ cu,
+    int nslot) {
   using R = ChRec<DK, sizeof(E)>;
   using C = ChCfg<DK, NP>;
   using X = Elt<float>;
@@ -352,10 +389,24 @@ __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_channel_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, grp = lane >> 4;
+  // this sequence: T tokens whose token t is row (tok0 + t) * H + h, tile c's
+  // record at recs + c * GLOBAL
+  int T;
+  int64_t tok0, rec0;
+  if (cu) {
+    const int tb = ch_seq_begin(cu, b, TA);
+    T = ch_seq_end(cu, b, TA) - tb;
+    tok0 = tb;
+    rec0 = (int64_t)h * nslot + tb / 16 + b;
+  } else {
+    T = TA;
+    tok0 = (int64_t)b * TA;
+    rec0 = ((int64_t)b * H + h) * ((TA + 15) >> 4);
+  }
   const int NC = (T + 15) >> 4;
   const int NE = (NC + NP - 1) / NP;
 
-  auto rowk = [&](int t) -> int64_t { return ((int64_t)b * T + t) * H + h; };
+  auto rowk = [&](int t) -> int64_t { return (tok0 + t) * H + h; };
   auto rec_of = [&](int ep, int j) -> char* { return smem + ((ep & 1) * NP + j) * R::LDS; };
 
   if (wave == 0) {
@@ -455,10 +506,12 @@ __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_channel_kernel(
 
   // ---------------------------------------------------------------- loaders
   const int p = wave - 1;
-  const char* recs = ws + ((int64_t)b * H + h) * NC * R::GLOBAL;
+  const char* recs = ws + rec0 * R::GLOBAL;
   // Global loads of tile c (clamped to the last tile, so every path issues
-  // the same number of loads and the compiler can wait for the older set).
+  // the same number of loads and the compiler can wait for the older set; an
+  // empty sequence loads nothing).
   auto load = [&](ChCopy<E, DK>& r, int c) {
+    if (NC == 0) return;
     c = min(c, NC - 1);
     const u32x4* src = reinterpret_cast<const u32x4*>(recs + (int64_t)c * R::GLOBAL);
 #pragma unroll
@@ -505,20 +558,27 @@ __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_channel_kernel(
   }
 }
 
+// B sequences of T tokens (cu == nullptr), or B packed sequences with device
+// offsets cu in one sequence of T tokens.
 template <typename E, int DK, int NP>
 hipError_t launch_ch(const void* q, const void* k, const void* v, const float* gate,
                      int gate_logit, float G, const float* beta, const float* h0, void* o,
-                     float* hT, int B, int T, int H, int Dv, void* ws, hipStream_t st) {
+                     float* hT, int B, int T, int H, int Dv, const int* cu, void* ws,
+                     hipStream_t st) {
   const int NC = (T + 15) / 16;
-  const int64_t jobs = (int64_t)B * H * NC;
+  const int nslot = channel_varlen_slots(T, B);
+  const int64_t jobs = cu ? (int64_t)H * nslot : (int64_t)B * H * NC;
   const int prep_blocks = (int)((jobs + 3) / 4 < 4096 ? (jobs + 3) / 4 : 4096);
-  hipLaunchKernelGGL((chunk_channel_prep_kernel<E, DK>), dim3(prep_blocks), dim3(256), 0, st,
-                     (const E*)q, (const E*)k, gate, gate_logit, G, beta, (char*)ws, B, T, H);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (prep_blocks > 0) {
+    hipLaunchKernelGGL((chunk_channel_prep_kernel<E, DK>), dim3(prep_blocks), dim3(256), 0, st,
+                       (const E*)q, (const E*)k, gate, gate_logit, G, beta, (char*)ws, B, T, H,
+                       cu, nslot);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const int blocks = B * H * (Dv / 16);
   hipLaunchKernelGGL((chunk_fwd_channel_kernel<E, DK, NP>), dim3(blocks), dim3(64 * (NP + 1)),
-                     0, st, (const E*)v, (const char*)ws, h0, (E*)o, hT, B, T, H, Dv);
+                     0, st, (const E*)v, (const char*)ws, h0, (E*)o, hT, B, T, H, Dv, cu, nslot);
   return hipGetLastError();
 }
 
@@ -634,14 +694,32 @@ hipError_t launch_chunk_fwd_channel(const void* q, const void* k, const void* v,
                                     const float* beta, const float* h0, void* o, float* hT,
                                     int B, int T, int H, int Dk, int Dv, int fp32, void* ws,
                                     hipStream_t st) {
+  return launch_chunk_fwd_channel_varlen(q, k, v, gate, gate_logit, G, beta, h0, o, hT, nullptr,
+                                         B, T, H, Dk, Dv, fp32, ws, st);
+}
+
+hipError_t launch_chunk_fwd_channel_varlen(const void* q, const void* k, const void* v,
+                                           const float* gate, int gate_logit, float G,
+                                           const float* beta, const float* h0, void* o,
+                                           float* hT, const int* cu, int B, int T, int H, int Dk,
+                                           int Dv, int fp32, void* ws, hipStream_t st) {
+#define LA_CH(E, DK) \
+  return launch_ch<E, DK, 2>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, cu, ws, st)
   if (fp32) {
-    if (Dk == 64) return launch_ch<float, 64, 2>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, ws, st);
-    if (Dk == 128) return launch_ch<float, 128, 2>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, ws, st);
+    if (Dk == 64) LA_CH(float, 64);
+    if (Dk == 128) LA_CH(float, 128);
   } else {
-    if (Dk == 64) return launch_ch<__bf16, 64, 2>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, ws, st);
-    if (Dk == 128) return launch_ch<__bf16, 128, 2>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, ws, st);
+    if (Dk == 64) LA_CH(__bf16, 64);
+    if (Dk == 128) LA_CH(__bf16, 128);
   }
+#undef LA_CH
   return hipErrorInvalidValue;
+}
+
+long long chunk_channel_varlen_workspace_bytes(int T, int nseq, int H, int Dk, int fp32) {
+  const long long rec = fp32 ? (Dk == 64 ? ChRec<64, 4>::GLOBAL : ChRec<128, 4>::GLOBAL)
+                             : (Dk == 64 ? ChRec<64, 2>::GLOBAL : ChRec<128, 2>::GLOBAL);
+  return (long long)H * channel_varlen_slots(T, nseq) * rec;
 }
 
 hipError_t launch_decode_channel(const void* q, const void* k, const void* v,

@@ -60,6 +60,17 @@ hipError_t launch_chunk_fwd_channel(const void* q, const void* k, const void* v,
                                     int B, int T, int H, int Dk, int Dv, int fp32, void* ws,
                                     hipStream_t st);
 
+// The same over packed sequences: sequence s is tokens [cu[s], cu[s+1]) of one
+// packed sequence of T tokens (cu: device array of nseq + 1 offsets).
+hipError_t launch_chunk_fwd_channel_varlen(const void* q, const void* k, const void* v,
+                                           const float* gate, int gate_logit, float G,
+                                           const float* beta, const float* h0, void* o,
+                                           float* hT, const int* cu, int nseq, int T, int H,
+                                           int Dk, int Dv, int fp32, void* ws, hipStream_t st);
+
+// Workspace bytes of the packed per-channel path: H * (T / 16 + nseq + 1) records.
+long long chunk_channel_varlen_workspace_bytes(int T, int nseq, int H, int Dk, int fp32);
+
 // Workspace bytes of the per-channel path: one record per tile and head.
 long long chunk_channel_workspace_bytes(int B, int T, int H, int Dk, int fp32);
 

@@ -296,6 +296,92 @@ int chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* g
 
 extern "C" {
 
+}  // extern "C"
+
+namespace {
+
+int check_channel_varlen_sizes(int T, int nseq, int H, int Dk, int Dv, int dtype) {
+  if (nseq < 0) return fail(LA_EINVAL, "nseq must be >= 0, got %d", nseq);
+  if (int rc = check_chunk_sizes(nseq > 0 ? 1 : 0, T, H, Dk, Dv, dtype)) return rc;
+  if ((int64_t)nseq * H * (Dv / 16) > INT32_MAX || (int64_t)T / 16 + nseq + 1 > INT32_MAX / 2)
+    return fail(LA_EINVAL, "problem too large (nseq = %d)", nseq);
+  return LA_OK;
+}
+
+// lin_attn_chunk_fwd_channel_varlen: the per-channel gate over packed sequences.
+int chunk_fwd_channel_varlen(const void* q, const void* k, const void* v, const float* gate,
+                             int gate_mode, float G, const float* beta, const float* h0, void* o,
+                             float* hT, const int* cu_seqlens, int nseq, int T, int H, int Dk,
+                             int Dv, int dtype, void* workspace, long long workspace_bytes,
+                             void* stream) {
+  if (int rc = check_channel_varlen_sizes(T, nseq, H, Dk, Dv, dtype)) return rc;
+  if (int rc = check_gate_scalars(gate_mode, G)) return rc;
+  if (G > 10.f)
+    return fail(LA_ERANGE, "G must be in [0, 10] for a per-channel gate, got %g", (double)G);
+  const long long wsz = la::chunk_channel_varlen_workspace_bytes(T, nseq, H, Dk, dtype == LA_FP32);
+  if (nseq == 0 || H == 0) return ok();
+  const int64_t es = dtype == LA_BF16 ? 2 : 4;
+  const int64_t ntok = (int64_t)T * H;
+  const int64_t nst = (int64_t)nseq * H * Dk * Dv;
+  if (!cu_seqlens) return fail(LA_EINVAL, "cu_seqlens must not be NULL");
+  if (!aligned(cu_seqlens, 4u)) return fail(LA_EINVAL, "cu_seqlens must be 4-byte aligned");
+  if (T > 0) {
+    const struct { const char* nm; const void* p; unsigned a; } req[] = {
+        {"q", q, 16u}, {"k", k, 16u}, {"v", v, 16u}, {"gate", gate, 16u}, {"beta", beta, 4u},
+        {"o", o, dtype == LA_BF16 ? 8u : 4u}};
+    for (const auto& r : req) {
+      if (!r.p) return fail(LA_EINVAL, "%s must not be NULL", r.nm);
+      if (!aligned(r.p, r.a)) return fail(LA_EINVAL, "%s must be %u-byte aligned", r.nm, r.a);
+    }
+  }
+  if (h0 && !aligned(h0, 4u)) return fail(LA_EINVAL, "h0 must be 4-byte aligned");
+  if (hT && !aligned(hT, 4u)) return fail(LA_EINVAL, "hT must be 4-byte aligned");
+  if (!workspace) return fail(LA_EINVAL, "workspace must not be NULL (%lld bytes needed)", wsz);
+  if (!aligned(workspace, 256u)) return fail(LA_EINVAL, "workspace must be 256-byte aligned");
+  if (workspace_bytes < wsz)
+    return fail(LA_EINVAL, "workspace too small: %lld bytes given, %lld needed", workspace_bytes,
+                wsz);
+  const Span sq = span("q", q, ntok * Dk * es), sk = span("k", k, ntok * Dk * es),
+             sv = span("v", v, ntok * Dv * es), sg = span("gate", gate, ntok * Dk * 4),
+             sb = span("beta", beta, ntok * 4), sh0 = span("h0", h0, nst * 4),
+             so = span("o", o, ntok * Dv * es), shT = span("hT", hT, nst * 4),
+             sc = span("cu_seqlens", cu_seqlens, ((int64_t)nseq + 1) * 4);
+  for (const Span& in : {sq, sk, sv, sg, sb, sh0, shT, sc})
+    if (overlap(so, in)) return fail(LA_EINVAL, "o overlaps %s", in.name);
+  const Span sw = span("workspace", workspace, wsz);
+  for (const Span& in : {sq, sk, sv, sg, sb, sh0, so, shT, sc})
+    if (overlap(sw, in)) return fail(LA_EINVAL, "workspace overlaps %s", in.name);
+  for (const Span& in : {sq, sk, sv, sg, sb, sc})
+    if (overlap(shT, in)) return fail(LA_EINVAL, "hT overlaps %s", in.name);
+  if (hT && h0 && hT != h0 && overlap(shT, sh0))
+    return fail(LA_EINVAL, "hT partially overlaps h0 (only hT == h0 is allowed)");
+  hipError_t e = la::launch_chunk_fwd_channel_varlen(
+      q, k, v, gate, gate_mode == LA_GATE_BOUNDED_LOGIT, G, beta, h0, o, hT, cu_seqlens, nseq, T,
+      H, Dk, Dv, dtype == LA_FP32, workspace, reinterpret_cast<hipStream_t>(stream));
+  return hip_status(e, "chunk_fwd_channel_varlen launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+long long lin_attn_chunk_fwd_channel_varlen_workspace_size(int T, int nseq, int H, int Dk,
+                                                           int Dv, int dtype) {
+  if (check_channel_varlen_sizes(T, nseq, H, Dk, Dv, dtype)) return -1;
+  ok();
+  return la::chunk_channel_varlen_workspace_bytes(T, nseq, H, Dk, dtype == LA_FP32);
+}
+
+int lin_attn_chunk_fwd_channel_varlen(const void* q, const void* k, const void* v,
+                                      const float* gate, int gate_mode, float G,
+                                      const float* beta, const float* h0, void* o, float* hT,
+                                      const int* cu_seqlens, int nseq, int T, int H, int Dk,
+                                      int Dv, int dtype, void* workspace,
+                                      long long workspace_bytes, void* stream) {
+  return chunk_fwd_channel_varlen(q, k, v, gate, gate_mode, G, beta, h0, o, hT, cu_seqlens, nseq,
+                                  T, H, Dk, Dv, dtype, workspace, workspace_bytes, stream);
+}
+
 int lin_attn_chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* gate,
                               int gate_mode, float G, const float* beta, const float* h0,
                               void* o, float* hT, const int* cu_seqlens, int nseq, int T, int H,

@@ -266,6 +266,35 @@ int lin_attn_decode_step(const void* q, const void* k, const void* v,
                          void* stream);
 
 /*
+ * lin_attn_chunk_fwd_channel_varlen_workspace_size -- device workspace bytes of
+ * lin_attn_chunk_fwd_channel_varlen: H * (T / 16 + nseq + 1) * R with R as in
+ * lin_attn_chunk_fwd_channel_workspace_size (one record slot per 16 tokens of
+ * each packed sequence plus one spare slot per sequence for its ragged end);
+ * -1 (with lin_attn_last_error() set) for invalid or unsupported sizes.
+ */
+long long lin_attn_chunk_fwd_channel_varlen_workspace_size(int T, int nseq, int H, int Dk,
+                                                           int Dv, int dtype);
+
+/*
+ * lin_attn_chunk_fwd_channel_varlen -- lin_attn_chunk_fwd_channel over packed
+ * sequences of different lengths (chunked prefill of a serving batch,
+ * "Evaluating Next-Gen ...", sec. 4): sequence s is tokens [cu_seqlens[s],
+ * cu_seqlens[s + 1]) of one packed sequence of T tokens, starts from its own
+ * h0[s] and is computed exactly as lin_attn_chunk_fwd_channel computes a
+ * sequence of its length.  Arguments and rules as lin_attn_chunk_fwd_varlen
+ * (q, k [T, H, Dk]; v, o [T, H, Dv]; beta [T, H]; h0, hT [nseq, H, Dk, Dv];
+ * device offsets, clamped to [0, T], read only on the device; empty sequences
+ * allowed), except: gate is [T, H, Dk] float32 (16-byte aligned); both dtypes
+ * are supported; 0 <= G <= 10.
+ */
+int lin_attn_chunk_fwd_channel_varlen(const void* q, const void* k, const void* v,
+                                      const float* gate, int gate_mode, float G,
+                                      const float* beta, const float* h0, void* o, float* hT,
+                                      const int* cu_seqlens, int nseq, int T, int H, int Dk,
+                                      int Dv, int dtype, void* workspace,
+                                      long long workspace_bytes, void* stream);
+
+/*
  * lin_attn_decode_step_channel -- lin_attn_decode_step with one log-decay per
  * key channel: gate is [B, H, Dk] float32 (g or its logit, per gate_mode), and
  * the step is the per-channel recurrence of lin_attn_chunk_fwd_channel

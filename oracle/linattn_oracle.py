@@ -80,6 +80,11 @@ itself are in tests/test_oracle.py):
   decode_step_channel
                    steps applied one token at a time equal recurrent_fwd_channel
                    over the same tokens.
+  recurrent_fwd_channel_varlen
+                   packed sequences with a per-channel gate: the boundary closed
+                   form (a sequence whose tokens neither write nor decay returns
+                   its own h0, and outputs h0^T q_t, exactly, whatever precedes
+                   it), equal lengths equal the batch axis.
 Every function is pinned; none is "parity unpinned".
 
 Layouts (row-major, as the library uses them):
@@ -108,6 +113,7 @@ __all__ = [
     "recurrent_fwd_channel",
     "chunked_fwd_channel",
     "decode_step_channel",
+    "recurrent_fwd_channel_varlen",
 ]
 
 
@@ -484,3 +490,30 @@ def decode_step_channel(q, k, v, g, beta, S):
     o, hT = recurrent_fwd_channel(q[:, None], k[:, None], v[:, None], g[:, None],
                                   beta[:, None], S)
     return o[:, 0], hT
+
+
+def recurrent_fwd_channel_varlen(q, k, v, g, beta, cu_seqlens, h0=None):
+    """Packed sequences with a per-channel gate: sequence s is tokens
+    [cu[s], cu[s+1]) of q, k [1,T,H,Dk], v [1,T,H,Dv], g [1,T,H,Dk], beta [1,T,H];
+    it starts from h0[s] (zeros when h0 is None) and reads nothing of another
+    sequence.  Returns (o [1,T,H,Dv], hT [N,H,Dk,Dv]) in float64."""
+    q, k, v, g, beta = map(_f64, (q, k, v, g, beta))
+    cu = [int(x) for x in cu_seqlens]
+    _, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    N = len(cu) - 1
+    if N < 0 or cu[0] != 0 or cu[-1] != T or any(b < a for a, b in zip(cu, cu[1:])):
+        raise ValueError("cu_seqlens must run from 0 to T without decreasing")
+    o = np.empty((1, T, H, Dv))
+    hT = np.zeros((N, H, Dk, Dv))
+    for s in range(N):
+        a, b = cu[s], cu[s + 1]
+        init = None if h0 is None else _f64(h0)[s:s + 1]
+        if b > a:
+            o_s, h_s = recurrent_fwd_channel(q[:, a:b], k[:, a:b], v[:, a:b], g[:, a:b],
+                                             beta[:, a:b], init)
+            o[:, a:b] = o_s
+            hT[s] = h_s[0]
+        elif init is not None:
+            hT[s] = init[0]
+    return o, hT

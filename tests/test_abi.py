@@ -380,3 +380,39 @@ def test_decode_channel_rejects(kw, code, needle):
 
 def test_decode_channel_empty_is_noop():
     assert decode_ch(B=0)[0] == N.LA_OK
+
+
+def channel_varlen(**kw):
+    a = dict(q=fake(0), k=fake(1), v=fake(2), gate=fake(3), gate_mode=1, G=5.0, beta=fake(4),
+             h0=None, o=fake(5), hT=fake(6), cu=fake(7), nseq=3, T=64, H=2, Dk=128, Dv=128,
+             dtype=0, ws=fake(8), ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    L = N.lib()
+    rc = L.lin_attn_chunk_fwd_channel_varlen(a["q"], a["k"], a["v"], a["gate"], a["gate_mode"],
+                                             a["G"], a["beta"], a["h0"], a["o"], a["hT"], a["cu"],
+                                             a["nseq"], a["T"], a["H"], a["Dk"], a["Dv"],
+                                             a["dtype"], a["ws"], a["ws_bytes"], a["stream"])
+    return rc, L.lin_attn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(cu=None), N.LA_EINVAL, "cu_seqlens must not be NULL"),
+    (dict(nseq=-1), N.LA_EINVAL, "nseq"),
+    (dict(G=11.0), N.LA_ERANGE, "per-channel"),
+    (dict(gate=fake(3) + 8), N.LA_EINVAL, "gate must be 16-byte aligned"),
+    (dict(ws_bytes=100), N.LA_EINVAL, "workspace too small"),
+    (dict(o=fake(3) + 64 * 2 * 4 * 64), N.LA_EINVAL, "o overlaps gate"),
+    (dict(hT=fake(7)), N.LA_EINVAL, "hT overlaps cu_seqlens"),
+])
+def test_channel_varlen_rejects(kw, code, needle):
+    rc, msg = channel_varlen(**kw)
+    assert rc == code and needle in msg, (rc, msg)
+
+
+def test_channel_varlen_workspace_size_and_empty():
+    L = N.lib()
+    assert L.lin_attn_chunk_fwd_channel_varlen_workspace_size(100, 3, 2, 128, 128, 0) == \
+        2 * (100 // 16 + 3 + 1) * 18944
+    assert L.lin_attn_chunk_fwd_channel_varlen_workspace_size(100, 3, 2, 64, 32, 1) == \
+        2 * (100 // 16 + 3 + 1) * 14592
+    assert channel_varlen(nseq=0)[0] == N.LA_OK

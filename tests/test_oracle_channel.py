@@ -216,3 +216,42 @@ def test_decode_channel_steps_equal_the_forward():
         o, S = orc.decode_step_channel(q[:, t], k[:, t], v[:, t], g[:, t], beta[:, t], S)
         assert np.abs(o - ro[:, t]).max() < 1e-12
     assert np.abs(S - rh).max() < 1e-12
+
+
+def test_channel_varlen_boundary_closed_form():
+    # sequence 1 neither writes (beta = 0) nor decays (g = 0): it returns its
+    # own h0 and outputs h0^T q_t exactly, whatever sequence 0 left behind
+    q, k, v, g, beta, _ = _inputs(1, 20, 2, 8, 5, seed=9)
+    cu = [0, 12, 20]
+    h0 = np.random.default_rng(9).standard_normal((2, 2, 8, 5))
+    beta[:, 12:] = 0.0
+    g[:, 12:] = 0.0
+    o, hT = orc.recurrent_fwd_channel_varlen(q, k, v, g, beta, cu, h0)
+    assert np.array_equal(hT[1], h0[1])
+    ref = np.einsum("thc,hcv->thv", q[0, 12:], h0[1])
+    assert np.abs(o[0, 12:] - ref).max() < 1e-12
+
+
+def test_channel_varlen_equal_lengths_equal_the_batch_axis():
+    q, k, v, g, beta, h0 = _inputs(3, 7, 2, 8, 5, seed=10, h0=True)
+    ro, rh = orc.recurrent_fwd_channel(q, k, v, g, beta, h0)
+    pk = lambda a: a.reshape((1, 3 * 7) + a.shape[2:])
+    o, hT = orc.recurrent_fwd_channel_varlen(pk(q), pk(k), pk(v), pk(g), pk(beta), [0, 7, 14, 21],
+                                             h0)
+    assert np.abs(o.reshape(ro.shape) - ro).max() < 1e-12
+    assert np.abs(hT - rh).max() < 1e-12
+
+
+def test_channel_varlen_carry_over_mutant_is_caught():
+    # a packed runner that carries the state across the boundary fails the
+    # boundary closed form
+    q, k, v, g, beta, _ = _inputs(1, 20, 2, 8, 5, seed=9)
+    h0 = np.random.default_rng(9).standard_normal((2, 2, 8, 5))
+    beta[:, 12:] = 0.0
+    g[:, 12:] = 0.0
+    _, h_first = orc.recurrent_fwd_channel(q[:, :12], k[:, :12], v[:, :12], g[:, :12],
+                                           beta[:, :12], h0[0:1])
+    o_bad, _ = orc.recurrent_fwd_channel(q[:, 12:], k[:, 12:], v[:, 12:], g[:, 12:],
+                                         beta[:, 12:], h_first)
+    ref = np.einsum("thc,hcv->thv", q[0, 12:], h0[1])
+    assert np.abs(o_bad[0] - ref).max() > 1e-3

@@ -238,3 +238,78 @@ def test_channel_graph_capture_replays():
         assert torch.equal(S, S_ref) and torch.equal(od, od_ref), rep
         lin_attn_chunk_fwd_channel(inp["q"], inp["k"], inp["v"], gate, inp["beta"], None,
                                    gate_mode="logit")          # eager work between replays
+
+
+def _packed(lengths, H, Dk, Dv, dtype, seed, mu=-3.0, h0_std=0.02):
+    T = int(sum(lengths))
+    inp = I.make_inputs(1, T, H, Dk, Dv, dtype=dtype, seed=seed, device="cuda")
+    x = I.make_channel_gate(1, T, H, Dk, seed=seed, device="cuda", mu=mu)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int32, device="cuda")
+    h0 = h0_std * torch.randn((len(lengths), H, Dk, Dv), device="cuda",
+                              generator=torch.Generator("cuda").manual_seed(seed))
+    return inp, x, cu, h0
+
+
+@pytest.mark.parametrize("dtype,Dk,Dv,lengths", [
+    ("fp32", 64, 32, [17, 0, 40, 1, 33]),
+    ("bf16", 128, 128, [100, 0, 16, 5, 250, 0]),
+    ("bf16", 64, 256, [48, 31]),
+])
+def test_channel_varlen_parity(dtype, Dk, Dv, lengths):
+    from chunked_gated_linear_amd import lin_attn_chunk_fwd_channel_varlen
+    say(f"channel varlen {dtype} {Dk} {Dv} {lengths}")
+    H = 2
+    inp, x, cu, h0 = _packed(lengths, H, Dk, Dv, dtype, seed=51)
+    o, hT = lin_attn_chunk_fwd_channel_varlen(inp["q"], inp["k"], inp["v"], x, inp["beta"], cu,
+                                              h0, gate_mode="logit")
+    torch.cuda.synchronize()
+    g = orc.bounded_gate(host(x).astype(np.float64))
+    ro, rh = orc.recurrent_fwd_channel_varlen(host(inp["q"]), host(inp["k"]), host(inp["v"]), g,
+                                              host(inp["beta"]).astype(np.float64),
+                                              host(cu).astype(np.int64),
+                                              host(h0).astype(np.float64))
+    tol = 1e-5 if dtype == "fp32" else 1e-2
+    eo, eh = relerr(host(o), ro), relerr(host(hT), rh)
+    say(f"  err(o)={eo:.2e} err(hT)={eh:.2e}")
+    assert eo <= tol and eh <= tol
+
+
+def test_channel_varlen_equal_lengths_match_the_batched_call_bitwise():
+    from chunked_gated_linear_amd import lin_attn_chunk_fwd_channel_varlen
+    B, T, H, D = 3, 70, 2, 128
+    inp = I.make_inputs(B, T, H, D, D, dtype="bf16", seed=52, device="cuda", h0_std=0.02)
+    x = I.make_channel_gate(B, T, H, D, seed=52, device="cuda", mu=-3.0)
+    ob, hb = lin_attn_chunk_fwd_channel(inp["q"], inp["k"], inp["v"], x, inp["beta"], inp["h0"],
+                                        gate_mode="logit")
+    pk = lambda a: a.reshape((1, B * T) + tuple(a.shape[2:])).contiguous()
+    cu = torch.arange(0, B * T + 1, T, dtype=torch.int32, device="cuda")
+    ov, hv = lin_attn_chunk_fwd_channel_varlen(pk(inp["q"]), pk(inp["k"]), pk(inp["v"]), pk(x),
+                                               pk(inp["beta"]), cu, inp["h0"], gate_mode="logit")
+    torch.cuda.synchronize()
+    assert torch.equal(ov.reshape(ob.shape), ob) and torch.equal(hv, hb)
+
+
+def test_channel_varlen_serving_batch_sampled():
+    # the packed prefill workload (64 log-normal requests, 64K tokens, 16 heads)
+    # with a per-channel gate: three requests of head 5 against the oracle
+    from chunked_gated_linear_amd import lin_attn_chunk_fwd_channel_varlen
+    vw = I.VARLEN_WORKLOAD
+    lengths = I.varlen_lengths(vw["nseq"], vw["T"], seed=1006)
+    say("channel varlen serving batch")
+    inp, x, cu, _ = _packed(lengths, vw["H"], vw["Dk"], vw["Dv"], "bf16", seed=1006, mu=0.0)
+    o, hT = lin_attn_chunk_fwd_channel_varlen(inp["q"], inp["k"], inp["v"], x, inp["beta"], cu,
+                                              None, gate_mode="logit")
+    torch.cuda.synchronize()
+    cuh = [0] + list(np.cumsum(lengths))
+    h = 5
+    for s in (0, 17, 63):
+        a, b = cuh[s], cuh[s + 1]
+        sl = (slice(None), slice(a, b), slice(h, h + 1))
+        ro, rh = orc.recurrent_fwd_channel(host(inp["q"][sl]), host(inp["k"][sl]),
+                                           host(inp["v"][sl]),
+                                           orc.bounded_gate(host(x[sl]).astype(np.float64)),
+                                           host(inp["beta"][sl]).astype(np.float64), None)
+        eo = relerr(host(o[sl]), ro)
+        eh = relerr(host(hT[s:s + 1, h:h + 1]), rh)
+        say(f"  request {s} ({b - a} tokens): err(o)={eo:.2e} err(hT)={eh:.2e}")
+        assert eo <= 1e-2 and eh <= 1e-2
