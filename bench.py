@@ -293,6 +293,47 @@ def main():
         }
         del xc, oc, hc, wsc
 
+    # ---- the packed prefill batch with a per-channel gate
+    if args.channel_steps > 0 and args.varlen_steps > 0:
+        from chunked_gated_linear_amd import (lin_attn_chunk_fwd_channel_varlen,
+                                              lin_attn_chunk_fwd_channel_varlen_workspace_size)
+        vw = I.VARLEN_WORKLOAD
+        lengths = I.varlen_lengths(vw["nseq"], vw["T"], seed=1006)
+        vin = I.make_inputs(1, vw["T"], vw["H"], vw["Dk"], vw["Dv"], dtype=vw["dtype"], seed=1006,
+                            device=dev)
+        xv = I.make_channel_gate(1, vw["T"], vw["H"], vw["Dk"], seed=1006, device=dev)
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int32, device=dev)
+        ov = torch.empty((1, vw["T"], vw["H"], vw["Dv"]), dtype=vin["q"].dtype, device=dev)
+        hv = torch.empty((vw["nseq"], vw["H"], vw["Dk"], vw["Dv"]), dtype=torch.float32, device=dev)
+        wsv = torch.empty(lin_attn_chunk_fwd_channel_varlen_workspace_size(
+            vw["T"], vw["nseq"], vw["H"], vw["Dk"], vw["Dv"]), dtype=torch.uint8, device=dev)
+
+        def cvstep():
+            lin_attn_chunk_fwd_channel_varlen(vin["q"], vin["k"], vin["v"], xv, vin["beta"], cu,
+                                              gate_mode="logit", G=5.0, o=ov, hT=hv, workspace=wsv)
+
+        cvstep()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.channel_steps):
+            cvstep()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cvms = e0.elapsed_time(e1) / args.channel_steps
+        cvbytes = vw["T"] * vw["H"] * (2 * (2 * vw["Dk"] + vw["Dv"]) + 2 * vw["Dv"] + 4 * vw["Dk"] + 4) \
+            + vw["nseq"] * vw["H"] * vw["Dk"] * vw["Dv"] * 4
+        result["channel_gate_varlen"] = {
+            "workload": (f"{vw['nseq']} packed sequences, lengths {min(lengths)}..{max(lengths)}, "
+                         f"{vw['T']} tokens, H={vw['H']} d={vw['Dk']} bf16, per-channel gate"),
+            "ms_per_call": cvms, "tokens_per_s": vw["T"] / (cvms * 1e-3),
+            "roofline": {"bound": "hbm", "achieved": cvbytes / (cvms * 1e-3) / 1e9,
+                         "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                         "frac": cvbytes / (cvms * 1e-3) / PEAK_HBM,
+                         "alg_bytes_per_launch": cvbytes,
+                         "kernel": "chunk_channel_prep_kernel + chunk_fwd_channel_kernel (packed)"},
+        }
+        del vin, xv, ov, hv, wsv
+
     # ---- reverse pass at the training shape (B=4, H=16, T=8192, d=128): the
     # gradients of every input for an upstream dout and dhT
     if args.bwd_steps > 0:
