@@ -72,6 +72,9 @@ struct ChRec {
 
 // Producer scratch per wave (LDS): A (16 x 16) and beta[16].
 constexpr int kScrA = 0, kScrB = 1024, kScr = 1024 + 64;
+// Per-wave LDS of the preparation kernel: the scratch above, then the staged
+// transposed key block (at most 8 tiles x 64 lanes x 16 bytes).
+constexpr int kKts = kScr, kPrepWave = kScr + 8 * 64 * 16;
 
 template <int DK, int NP>
 struct ChCfg {
@@ -154,9 +157,12 @@ __device__ inline void load_tile(ChRaw<E, DK>& r, const E* __restrict__ q,
 
 // Prepare tile c into the record at `rec` (sA, sB: this wave's LDS scratch).
 template <typename E, int DK>
+// The transposed key block (NT x 64 lanes x 16 bytes) is assembled in `kts`,
+// this wave's LDS staging area, and copied to the record as whole 16-byte
+// fragments.
 __device__ inline void prep_tile(const ChRaw<E, DK>& r, int c, int T, char* __restrict__ rec,
-                                 float* sA, float* sB, int gate_logit, float G, int n, int grp,
-                                 int lane) {
+                                 float* sA, float* sB, char* kts, int gate_logit, float G, int n,
+                                 int grp, int lane) {
   using R = ChRec<DK, sizeof(E)>;
   using X = Elt<float>;
   using F16 = X::F16;
@@ -200,11 +206,11 @@ __device__ inline void prep_tile(const ChRaw<E, DK>& r, int c, int T, char* __re
         // ch / 16, lane (ch % 16, n / 4) register n % 4
         const int kt_lane = (ch >> 4) * 64 + (n >> 2) * 16 + (ch & 15);
         if constexpr (sizeof(E) == 4) {
-          reinterpret_cast<float*>(rec + R::KT)[kt_lane * 4 + (n & 3)] = kv * e_end;
+          reinterpret_cast<float*>(kts)[kt_lane * 4 + (n & 3)] = kv * e_end;
         } else {   // token n in registers n % 4 and 4 + n % 4 of its lane
           const __bf16 kd = (__bf16)(kv * e_end);
-          reinterpret_cast<__bf16*>(rec + R::KT)[kt_lane * 8 + (n & 3)] = kd;
-          reinterpret_cast<__bf16*>(rec + R::KT)[kt_lane * 8 + 4 + (n & 3)] = kd;
+          reinterpret_cast<__bf16*>(kts)[kt_lane * 8 + (n & 3)] = kd;
+          reinterpret_cast<__bf16*>(kts)[kt_lane * 8 + 4 + (n & 3)] = kd;
         }
         if (n == 0) reinterpret_cast<float*>(rec + R::GC)[ch] = e_last;
       }
@@ -242,10 +248,15 @@ __device__ inline void prep_tile(const ChRaw<E, DK>& r, int c, int T, char* __re
     }
     reinterpret_cast<f32x4*>(sA)[n * 4 + grp] = arow;          // A[n][4grp..4grp+3]
     reinterpret_cast<F16*>(rec + R::PF)[lane] = X::from_acc(prow);
-    // this wave's LDS writes (A, beta) before its reads of them
+    // this wave's LDS writes (A, beta, the staged key block) before its reads
+    // of them
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int t = 0; t < R::NT; ++t)
+      reinterpret_cast<f32x4*>(rec + R::KT)[t * 64 + lane] =
+          reinterpret_cast<const f32x4*>(kts)[t * 64 + lane];
 
     // (I + A)^-1, row n per lane: T[n][s] = delta_ns - sum_{r > s} T[n][r] A[r][s],
     // eliminating from the bottom row up.
@@ -296,12 +307,13 @@ __global__ __launch_bounds__(256) void chunk_channel_prep_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const float* __restrict__ gate,
     int gate_logit, float G, const float* __restrict__ beta, char* __restrict__ ws, int B,
     int T, int H, const int* __restrict__ cu, int nslot) {
-  __shared__ __attribute__((aligned(16))) char smem[4 * kScr];
+  __shared__ __attribute__((aligned(16))) char smem[4 * kPrepWave];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, grp = lane >> 4;
-  float* sA = reinterpret_cast<float*>(smem + wave * kScr + kScrA);
-  float* sB = reinterpret_cast<float*>(smem + wave * kScr + kScrB);
+  float* sA = reinterpret_cast<float*>(smem + wave * kPrepWave + kScrA);
+  float* sB = reinterpret_cast<float*>(smem + wave * kPrepWave + kScrB);
+  char* kts = smem + wave * kPrepWave + kKts;
   const int NC = (T + 15) >> 4;
   const int64_t jobs = cu ? (int64_t)H * nslot : (int64_t)B * H * NC;
   for (int64_t job = (int64_t)blockIdx.x * 4 + wave; job < jobs; job += (int64_t)gridDim.x * 4) {
@@ -330,8 +342,8 @@ __global__ __launch_bounds__(256) void chunk_channel_prep_kernel(
     }
     ChRaw<E, DK> r;
     load_tile<E, DK>(r, q, k, gate, beta, tok0, h, c, Ts, H, n, grp);
-    prep_tile<E, DK>(r, c, Ts, ws + job * ChRec<DK, sizeof(E)>::GLOBAL, sA, sB, gate_logit, G,
-                     n, grp, lane);
+    prep_tile<E, DK>(r, c, Ts, ws + job * ChRec<DK, sizeof(E)>::GLOBAL, sA, sB, kts, gate_logit,
+                     G, n, grp, lane);
     // the next job's writes to A / beta must not pass this job's reads
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
