@@ -73,8 +73,10 @@ struct ChRec {
 // Producer scratch per wave (LDS): A (16 x 16) and beta[16].
 constexpr int kScrA = 0, kScrB = 1024, kScr = 1024 + 64;
 // Per-wave LDS of the preparation kernel: the scratch above, then the staged
-// transposed key block (at most 8 tiles x 64 lanes x 16 bytes).
-constexpr int kKts = kScr, kPrepWave = kScr + 8 * 64 * 16;
+// transposed key block (at most 8 tiles x 64 lanes x 16 bytes) and Gam_C (at
+// most 128 floats, kGcs bytes into the staging area).
+constexpr int kGcs = 8 * 64 * 16;
+constexpr int kKts = kScr, kPrepWave = kScr + kGcs + 128 * 4;
 
 template <int DK, int NP>
 struct ChCfg {
@@ -157,9 +159,9 @@ __device__ inline void load_tile(ChRaw<E, DK>& r, const E* __restrict__ q,
 
 // Prepare tile c into the record at `rec` (sA, sB: this wave's LDS scratch).
 template <typename E, int DK>
-// The transposed key block (NT x 64 lanes x 16 bytes) is assembled in `kts`,
-// this wave's LDS staging area, and copied to the record as whole 16-byte
-// fragments.
+// The transposed key block (NT x 64 lanes x 16 bytes) and Gam_C are assembled
+// in `kts`, this wave's LDS staging area, and copied to the record as whole
+// 16-byte fragments.
 __device__ inline void prep_tile(const ChRaw<E, DK>& r, int c, int T, char* __restrict__ rec,
                                  float* sA, float* sB, char* kts, int gate_logit, float G, int n,
                                  int grp, int lane) {
@@ -212,7 +214,7 @@ __device__ inline void prep_tile(const ChRaw<E, DK>& r, int c, int T, char* __re
           reinterpret_cast<__bf16*>(kts)[kt_lane * 8 + (n & 3)] = kd;
           reinterpret_cast<__bf16*>(kts)[kt_lane * 8 + 4 + (n & 3)] = kd;
         }
-        if (n == 0) reinterpret_cast<float*>(rec + R::GC)[ch] = e_last;
+        if (n == 0) reinterpret_cast<float*>(kts + kGcs)[ch] = e_last;
       }
       F32 kg, qg, km, qm, ki;
 #pragma unroll
@@ -257,6 +259,9 @@ __device__ inline void prep_tile(const ChRaw<E, DK>& r, int c, int T, char* __re
     for (int t = 0; t < R::NT; ++t)
       reinterpret_cast<f32x4*>(rec + R::KT)[t * 64 + lane] =
           reinterpret_cast<const f32x4*>(kts)[t * 64 + lane];
+    if (lane < DK / 4)
+      reinterpret_cast<f32x4*>(rec + R::GC)[lane] =
+          reinterpret_cast<const f32x4*>(kts + kGcs)[lane];
 
     // (I + A)^-1, row n per lane: T[n][s] = delta_ns - sum_{r > s} T[n][r] A[r][s],
     // eliminating from the bottom row up.
