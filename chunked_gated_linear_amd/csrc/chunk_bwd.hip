@@ -31,7 +31,8 @@
 //                       start;
 //   bwd_dh_mfma_kernel  same split, serial backwards: dH' at every tile end,
 //                       and dh0;
-//   bwd_grad_kernel     per tile, all of d_v: dq, dk, dv, dbeta, dg.
+//   bwd_grad_kernel     per tile, all of d_v (one 16-column slice per wave at a
+//                       time): dq, dk, dv, dbeta, dg.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -647,31 +648,76 @@ __device__ inline float sum16(float x) {
   return x;
 }
 
+// Column slices need no workgroup barriers: wave w takes the 16-column slices
+// w, w + 4, ... of d_v end to end.  Per slice, straight from the
+// fragment-order states in registers:
+//   K H, Q H, K dH' (fp32 MFMA over d_k),  Y, U = T Y, dU = diag(ec) K dH' +
+//   P^T dO, dY = T^T dU (MFMA), dv, and the wave's partial sums of dP = dO U^T,
+//   dA = -dY U^T, dq += diag(gamma) dO H^T, dk += -diag(beta gamma) dY H^T +
+//   diag(ec) U dH'^T and of the per-token row terms.
+// The contractions over the slice's columns need row fragments of dO, dY, U
+// and of each 16-row block of H and dH': 16 x 16 transposes through a
+// wave-private LDS tile.  One cross-wave reduction per tile, then the in-tile
+// terms and the gate / beta gradients.  Two workgroups share a compute unit
+// (registers and LDS are sized for that): one's loads and barriers overlap the
+// other's matrix products.
 template <typename E, int DK>
-__global__ __launch_bounds__(kBwdThreads) void bwd_grad_kernel(BwdArgs a) {
-  // K and Q rows padded by 4 floats: the MFMA A-fragment reads (row n,
-  // column 4kk + grp) then spread over the LDS banks
+__global__ __launch_bounds__(kBwdThreads, 2) void bwd_grad_kernel(BwdArgs a) {
   constexpr int KP = DK + 4;
-  constexpr int RT = DK / 64;   // 16-row blocks of dq / dk per wave
-  __shared__ float sK[kT][KP], sQ[kT][KP];
-  __shared__ float sH[DK][17], sD[DK][17];
-  __shared__ float sKH[kT][17], sQH[kT][17], sKdH[kT][17];
-  __shared__ float sV[kT][17], sDO[kT][17], sY[kT][17], sU[kT][17], sDU[kT][17], sDY[kT][17];
+  constexpr int NT = DK / 16;          // 16-row blocks of d_k
+  constexpr int RT = DK / 64;          // of them, owned by each wave at the end
+  constexpr int TP = 20;               // transposition tile pitch (floats)
+  using X = Elt<float>;
+  using F16 = X::F16;
+  __shared__ __attribute__((aligned(16))) float sK[kT][KP];
+  __shared__ __attribute__((aligned(16))) float sQ[kT][KP];
   __shared__ float sTi[kT][kT + 1], sP[kT][kT + 1];
-  __shared__ float sPE[kT][kT + 1], sM[kT][kT + 1], sPP[kT][kT + 1], sAA[kT][kT + 1];
   __shared__ float sG[kT], sB[kT], sGam[kT], sEc[kT];
+  // per-wave transposition tiles during the slices; the cross-wave reduction
+  // of the dq / dk partials afterwards
+  constexpr int TR_BYTES = 4 * 2 * kT * TP * 4, RED_BYTES = 4 * NT * 64 * 16;
+  __shared__ __attribute__((aligned(16))) char sU8[TR_BYTES > RED_BYTES ? TR_BYTES : RED_BYTES];
+  __shared__ __attribute__((aligned(16))) f32x4 sRedS[4][2][64];   // dP, dA partials
+  __shared__ float sRow[4][3][kT];                                    // row sums B, G, W
+  __shared__ float sPE[kT][kT + 1], sM[kT][kT + 1], sPP[kT][kT + 1], sAA[kT][kT + 1];
   __shared__ float sRowB[kT], sRowG[kT], sRowW[kT], sRowAK[kT];
-  __shared__ float sHdH[kBwdThreads / 64];
+  __shared__ float sHdH[4];
   const int tid = threadIdx.x;
   const int64_t tile = blockIdx.x;
   const int c = (int)(tile % a.NT);
   const int64_t bh = tile / a.NT;
   const int h = (int)(bh % a.H), b = (int)(bh / a.H);
-  const int t = tid >> 4, j = tid & 15;        // (token, column) or (token, token)
-  // MFMA view of the same threads: wave w, lane (n, grp)
+  const int t = tid >> 4, j = tid & 15;        // (token, column) / (token, token) view
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n = tid & 15, grp = (tid >> 4) & 3;
+  const int lane = tid & 63, n = tid & 15, grp = (tid >> 4) & 3;
   const float* rec = a.rec + tile * BRec::FLOATS;
+  const E* vp = static_cast<const E*>(a.v);
+  const E* dop = static_cast<const E*>(a.dout);
+  const float* Hb = a.hs + tile * (int64_t)DK * a.Dv;
+  const float* Db = a.dhs + tile * (int64_t)DK * a.Dv;
+  const int NV = a.Dv / 16;
+  // the slice in hand: H and dH' fragments (accumulator order), v and dO of
+  // tokens 4 grp + i, column 16 jb + n; the first is requested before the
+  // tile is staged.
+  f32x4 Hf[NT], Df[NT], vv, dd;
+  auto fetch_hd = [&](int jb, int r) {
+    Hf[r] = reinterpret_cast<const f32x4*>(Hb + (int64_t)jb * DK * 16)[r * 64 + lane];
+    Df[r] = reinterpret_cast<const f32x4*>(Db + (int64_t)jb * DK * 16)[r * 64 + lane];
+  };
+  auto fetch_vd = [&](int jb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tk = c * kT + 4 * grp + i;
+      const int64_t ro = (((int64_t)b * a.T + tk) * a.H + h) * a.Dv + 16 * jb + n;
+      vv[i] = tk < a.T ? ld1(vp + ro) : 0.f;
+      dd[i] = tk < a.T ? ld1(dop + ro) : 0.f;
+    }
+  };
+  if (w < NV) {
+#pragma unroll
+    for (int r = 0; r < NT; ++r) fetch_hd(w, r);
+    fetch_vd(w);
+  }
   load_tile<E, DK, KP>(sK, static_cast<const E*>(a.k), b, c, h, a);
   load_tile<E, DK, KP>(sQ, static_cast<const E*>(a.q), b, c, h, a);
   sTi[t][j] = rec[BRec::TINV + tid];
@@ -679,124 +725,151 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grad_kernel(BwdArgs a) {
   const float ekk = rec[BRec::EKK + tid];
   float gamC;
   load_scalars(rec, sG, sB, sGam, sEc, gamC);
-  const int tok = c * kT + t;
-  const bool live = tok < a.T;
-  const int64_t row_idx = ((int64_t)b * a.T + tok) * a.H + h;   // (b, tok, h)
-  const E* vp = static_cast<const E*>(a.v);
-  const E* dop = static_cast<const E*>(a.dout);
-  const float* Hb = a.hs + tile * (int64_t)DK * a.Dv;
-  const float* Db = a.dhs + tile * (int64_t)DK * a.Dv;
+  __syncthreads();
 
-  float dPacc = 0.f, dAacc = 0.f;               // (t, i = j)
-  float accB = 0.f, accG = 0.f, accW = 0.f;     // (t, column) partial sums
-  float hdh = 0.f;
-  // dq, dk rows 16 (RT w + r) .. + 15 of this wave, accumulator order: lane
-  // (n, grp) register i holds token 4grp + i, row 16 (RT w + r) + n
-  f32x4 dQa[RT], dKa[RT];
+  const int tkn = c * kT + n;                          // token of row fragments
+  const int64_t ron = ((int64_t)b * a.T + tkn) * a.H + h;
+  float (*tr)[TP] = reinterpret_cast<float (*)[TP]>(sU8 + w * 2 * kT * TP * 4);
+  float (*tr2)[TP] = tr + kT;
+  // X in accumulator order -> row fragment (lane (n, grp) register jj =
+  // X[n][4 grp + jj]) through the tile
+  auto transpose = [&](float (*tl)[TP], const f32x4& x) -> f32x4 {
 #pragma unroll
-  for (int r = 0; r < RT; ++r) dQa[r] = dKa[r] = zero4();
-
-  const int NV = a.Dv / 16;
-  // this thread's share of a slice -- fragments tid and tid + 256 of H and of
-  // dH' (16 bytes each: rows 16 (f / 64) + 4 ((f % 64) / 16) + 0..3, column
-  // f % 16, for fragment f), and v and dO of token t, column j -- loaded one
-  // slice ahead
-  constexpr int SF = DK * 16 / 4 / kBwdThreads;   // fragments per thread
-  f32x4 nh[SF], nd[SF];
-  float nv, ndo;
-  auto fetch_slice = [&](int jb) {
-    nv = live ? ld1(vp + row_idx * a.Dv + 16 * jb + j) : 0.f;
-    ndo = live ? ld1(dop + row_idx * a.Dv + 16 * jb + j) : 0.f;
-    const f32x4* hf = reinterpret_cast<const f32x4*>(Hb + (int64_t)jb * DK * 16);
-    const f32x4* df = reinterpret_cast<const f32x4*>(Db + (int64_t)jb * DK * 16);
-#pragma unroll
-    for (int y = 0; y < SF; ++y) {
-      nh[y] = hf[tid + kBwdThreads * y];
-      nd[y] = df[tid + kBwdThreads * y];
-    }
+    for (int i = 0; i < 4; ++i) tl[4 * grp + i][n] = x[i];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const f32x4 r = *reinterpret_cast<const f32x4*>(&tl[n][4 * grp]);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    return r;
   };
-  fetch_slice(0);
-  for (int jb = 0; jb < NV; ++jb) {
-    const int col = 16 * jb;
+
+  f32x4 dQp[NT], dKp[NT];
 #pragma unroll
-    for (int y = 0; y < SF; ++y) {
-      const int f = tid + kBwdThreads * y;
-      const int r0 = 16 * (f >> 6) + 4 * ((f & 63) >> 4), cc = f & 15;
+  for (int r = 0; r < NT; ++r) dQp[r] = dKp[r] = zero4();
+  f32x4 pB = zero4(), pG = zero4(), pW = zero4(), dPp = zero4(), dAp = zero4();
+  float hdh = 0.f;
+  for (int jb = w; jb < NV; jb += 4) {
+    if (jb != w) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sH[r0 + i][cc] = nh[y][i];
-        sD[r0 + i][cc] = nd[y][i];
-        hdh += nh[y][i] * nd[y][i];
-      }
+      for (int r = 0; r < NT; ++r) fetch_hd(jb, r);
+      fetch_vd(jb);
     }
-    sV[t][j] = nv;
-    sDO[t][j] = ndo;
-    if (jb + 1 < NV) fetch_slice(jb + 1);
-    __syncthreads();
-    // K H, Q H and K dH' of this column slice (16 x 16, over d_k), one wave each
-    if (w < 3) {
-      const float (*Am)[KP] = w == 1 ? sQ : sK;
-      const float (*Bm)[17] = w == 2 ? sD : sH;
-      f32x4 acc = zero4();
-#pragma unroll 8
-      for (int kk = 0; kk < DK / 4; ++kk)
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(Am[n][4 * kk + grp], Bm[4 * kk + grp][n], acc,
-                                                   0, 0, 0);
-      float (*Om)[17] = w == 0 ? sKH : w == 1 ? sQH : sKdH;
+    f32x4 KH = zero4(), QH = zero4(), KdH = zero4();
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Om[4 * grp + i][n] = acc[i];
-    }
-    __syncthreads();
-    const float KH = sKH[t][j], QH = sQH[t][j], KdH = sKdH[t][j];
-    const float vres = sV[t][j] - sGam[t] * KH;
-    sY[t][j] = sB[t] * vres;
-    __syncthreads();
-    float U = 0.f;
-    for (int i = 0; i <= t; ++i) U += sTi[t][i] * sY[i][j];
-    float dU = sEc[t] * KdH;
-    for (int s = t; s < kT; ++s) dU += sP[s][t] * sDO[s][j];
-    sU[t][j] = U;
-    sDU[t][j] = dU;
-    __syncthreads();
-    float dY = 0.f;
-    for (int s = t; s < kT; ++s) dY += sTi[s][t] * sDU[s][j];
-    sDY[t][j] = dY;
-    accB += dY * vres;
-    accG += sGam[t] * QH * sDO[t][j] - sB[t] * sGam[t] * dY * KH;
-    accW += sEc[t] * KdH * U;
-    if (live) a.dv[row_idx * a.Dv + col + j] = sB[t] * dY;
-    __syncthreads();
-    // (t, i = j): dP = dO U^T, dA = -dY U^T
-    {
-      float p = 0.f, q = 0.f;
-      for (int jj = 0; jj < 16; ++jj) {
-        p += sDO[t][jj] * sU[j][jj];
-        q += sDY[t][jj] * sU[j][jj];
-      }
-      dPacc += p;
-      dAacc -= q;
-    }
-    // dQ += diag(gamma) dO H^T; dK += -diag(beta gamma) dY H^T + diag(ec) U dH'^T
-    // (16 x d_k, over the 16 columns of this slice)
+    for (int r = 0; r < NT; ++r) {
+      const F16 kf{*reinterpret_cast<const f32x4*>(&sK[n][16 * r + 4 * grp])};
+      const F16 qf{*reinterpret_cast<const f32x4*>(&sQ[n][16 * r + 4 * grp])};
+      KH = X::mma16(kf, F16{Hf[r]}, KH);
+      QH = X::mma16(qf, F16{Hf[r]}, QH);
+      KdH = X::mma16(kf, F16{Df[r]}, KdH);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int jj = 4 * kk + grp;
-      const float aO = sGam[n] * sDO[n][jj];
-      const float aY = -sB[n] * sGam[n] * sDY[n][jj];
-      const float aU = sEc[n] * sU[n][jj];
-#pragma unroll
-      for (int r = 0; r < RT; ++r) {
-        const int row = 16 * (RT * w + r) + n;
-        const float bH = sH[row][jj], bD = sD[row][jj];
-        dQa[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(aO, bH, dQa[r], 0, 0, 0);
-        dKa[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(aY, bH, dKa[r], 0, 0, 0);
-        dKa[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(aU, bD, dKa[r], 0, 0, 0);
-      }
+      for (int i = 0; i < 4; ++i) hdh += Hf[r][i] * Df[r][i];
     }
-    __syncthreads();
+    // this lane's tokens in accumulator order (4 grp + i) and in row order (n),
+    // and T, P^T, T^T as A fragments, re-read from LDS per slice (registers
+    // are what limits the waves per SIMD here)
+    f32x4 gm4, bt4, ec4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      gm4[i] = sGam[4 * grp + i];
+      bt4[i] = sB[4 * grp + i];
+      ec4[i] = sEc[4 * grp + i];
+    }
+    const float gmn = sGam[n], btn = sB[n], ecn = sEc[n];
+    F16 Tf, PTf, TTf;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      Tf.v[jj] = sTi[n][4 * grp + jj];
+      PTf.v[jj] = sP[4 * grp + jj][n];
+      TTf.v[jj] = sTi[4 * grp + jj][n];
+    }
+    f32x4 vres, Y, eKD;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      vres[i] = vv[i] - gm4[i] * KH[i];
+      Y[i] = bt4[i] * vres[i];
+      eKD[i] = ec4[i] * KdH[i];
+    }
+    const f32x4 U = X::mma16(Tf, F16{Y}, zero4());
+    const f32x4 dU = X::mma16(PTf, F16{dd}, eKD);
+    const f32x4 dY = X::mma16(TTf, F16{dU}, zero4());
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pB[i] += dY[i] * vres[i];
+      pG[i] += gm4[i] * QH[i] * dd[i] - bt4[i] * gm4[i] * dY[i] * KH[i];
+      pW[i] += eKD[i] * U[i];
+    }
+    const f32x4 Ur = transpose(tr, U);
+    const f32x4 DOr = transpose(tr, dd);
+    const f32x4 DYr = transpose(tr, dY);
+    // dv = diag(beta) dY, a row fragment: token n, columns 16 jb + 4 grp + 0..3
+    if (tkn < a.T)
+      *reinterpret_cast<f32x4*>(a.dv + ron * a.Dv + 16 * jb + 4 * grp) = btn * DYr;
+    dPp = X::mma16(F16{DOr}, F16{Ur}, dPp);
+    dAp = X::mma16(F16{DYr}, F16{Ur}, dAp);
+    f32x4 aO, aY, aU;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      aO[jj] = gmn * DOr[jj];
+      aY[jj] = -btn * gmn * DYr[jj];
+      aU[jj] = ecn * Ur[jj];
+    }
+#pragma unroll
+    for (int r = 0; r < NT; ++r) {
+      const f32x4 Hr = transpose(tr, Hf[r]);
+      const f32x4 Dr = transpose(tr2, Df[r]);
+      dQp[r] = X::mma16(F16{aO}, F16{Hr}, dQp[r]);
+      dKp[r] = X::mma16(F16{aY}, F16{Hr}, dKp[r]);
+      dKp[r] = X::mma16(F16{aU}, F16{Dr}, dKp[r]);
+    }
   }
 
-  // intra-tile terms
+  // ---- cross-wave reduction
+  // row sums over the 16 columns of a lane row, then over the waves
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) {
+      pB[i] += __shfl_xor(pB[i], m, 16);
+      pG[i] += __shfl_xor(pG[i], m, 16);
+      pW[i] += __shfl_xor(pW[i], m, 16);
+    }
+  }
+  for (int m = 1; m < 64; m <<= 1) hdh += __shfl_xor(hdh, m, 64);
+  __syncthreads();                       // every wave is done with its tiles
+  f32x4* red = reinterpret_cast<f32x4*>(sU8);
+#pragma unroll
+  for (int r = 0; r < NT; ++r) red[(w * NT + r) * 64 + lane] = dQp[r];
+  sRedS[w][0][lane] = dPp;
+  sRedS[w][1][lane] = dAp;
+  if (n == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sRow[w][0][4 * grp + i] = pB[i];
+      sRow[w][1][4 * grp + i] = pG[i];
+      sRow[w][2][4 * grp + i] = pW[i];
+    }
+  }
+  if (lane == 0) sHdH[w] = hdh;
+  __syncthreads();
+  f32x4 dQa[RT], dKa[RT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    dQa[r] = zero4();
+    for (int v = 0; v < 4; ++v) dQa[r] += red[(v * NT + RT * w + r) * 64 + lane];
+  }
+  // dP, dA at (token t, token i = j): accumulator lane 16 (t / 4) + j, register t % 4
+  float dPacc = 0.f, dAacc = 0.f;
+  for (int v = 0; v < 4; ++v) {
+    dPacc += sRedS[v][0][16 * (t >> 2) + j][t & 3];
+    dAacc -= sRedS[v][1][16 * (t >> 2) + j][t & 3];
+  }
+  __syncthreads();                       // the dq partials are read
+#pragma unroll
+  for (int r = 0; r < NT; ++r) red[(w * NT + r) * 64 + lane] = dKp[r];
   {
     const int i = j;
     const float e = i <= t ? __expf(sG[t] - sG[i]) : 0.f;
@@ -806,18 +879,20 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grad_kernel(BwdArgs a) {
     sM[t][i] = dA * sB[t] * e;
     sPP[t][i] = dP * sP[t][i];
     sAA[t][i] = dA * sB[t] * ekk;
-    const float rb = sum16(accB), rg = sum16(accG), rw = sum16(accW), rak = sum16(dA * ekk);
+    const float rak = sum16(dA * ekk);
     if (j == 0) {
-      sRowB[t] = rb;
-      sRowG[t] = rg;
-      sRowW[t] = rw;
+      sRowB[t] = sRow[0][0][t] + sRow[1][0][t] + sRow[2][0][t] + sRow[3][0][t];
+      sRowG[t] = sRow[0][1][t] + sRow[1][1][t] + sRow[2][1][t] + sRow[3][1][t];
+      sRowW[t] = sRow[0][2][t] + sRow[1][2][t] + sRow[2][2][t] + sRow[3][2][t];
       sRowAK[t] = rak;
     }
-    float hw = hdh;
-    for (int m = 1; m < 64; m <<= 1) hw += __shfl_xor(hw, m, 64);
-    if ((tid & 63) == 0) sHdH[tid >> 6] = hw;
   }
   __syncthreads();
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    dKa[r] = zero4();
+    for (int v = 0; v < 4; ++v) dKa[r] += red[(v * NT + RT * w + r) * 64 + lane];
+  }
   // in-tile terms: dQ += (dP o E) K, dK += (dP o E)^T Q + (M + M^T) K
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
@@ -832,35 +907,39 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grad_kernel(BwdArgs a) {
       dKa[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(aMM, bK, dKa[r], 0, 0, 0);
     }
   }
+  // dq, dk rows as 16-byte pieces: transposed through a tile in this wave's
+  // share of sRedS, whose dP / dA partials were read before the last barrier
+  {
+    float (*tq)[TP] = reinterpret_cast<float (*)[TP]>(&sRedS[w][0][0]);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int tk = c * kT + 4 * grp + i;
-    if (tk < a.T) {
-      const int64_t ro = (((int64_t)b * a.T + tk) * a.H + h) * DK;
-#pragma unroll
-      for (int r = 0; r < RT; ++r) {
-        a.dq[ro + 16 * (RT * w + r) + n] = dQa[r][i];
-        a.dk[ro + 16 * (RT * w + r) + n] = dKa[r][i];
+    for (int r = 0; r < RT; ++r) {
+      const f32x4 q4 = transpose(tq, dQa[r]);
+      const f32x4 k4 = transpose(tq, dKa[r]);
+      if (tkn < a.T) {
+        *reinterpret_cast<f32x4*>(a.dq + ron * DK + 16 * (RT * w + r) + 4 * grp) = q4;
+        *reinterpret_cast<f32x4*>(a.dk + ron * DK + 16 * (RT * w + r) + 4 * grp) = k4;
       }
     }
   }
-  if (tid < kT) {
+  {
     // dg_u = sum_{t >= u} dG_t, with dG_t the gradient of the in-tile running
     // sum G_t.  The E-terms of P and A enter dG_t with + for the row and - for
     // the column, so their sum over t >= u keeps exactly the entries with row
     // >= u and column < u; the ec-terms keep the tokens before u; gamma_C
-    // enters every u.  Summed in this form nothing large cancels.
-    const int u = tid;
-    float hd = 0.f;
-    for (int w = 0; w < kBwdThreads / 64; ++w) hd += sHdH[w];
-    float dg = gamC * hd;
-    for (int i = 0; i < u; ++i) dg += sRowW[i];
-    for (int t2 = u; t2 < kT; ++t2) {
-      dg += sRowG[t2];
-      for (int i = 0; i < u; ++i) dg += sPP[t2][i] + sAA[t2][i];
+    // enters every u.  Summed in this form nothing large cancels.  Lane (u, i)
+    // takes W_i (i < u) or G_i (i >= u) and column i of PP + AA over the rows
+    // t >= u when i < u; a 16-lane sum then gives dg_u - gamma_C <H, dH'>.
+    const int u = tid >> 4, i = tid & 15;
+    float x = i < u ? sRowW[i] : sRowG[i];
+#pragma unroll
+    for (int t2 = 0; t2 < kT; ++t2) {
+      const float y = sPP[t2][i] + sAA[t2][i];
+      x += (t2 >= u && i < u) ? y : 0.f;
     }
+    x = sum16(x);
     const int tk = c * kT + u;
-    if (tk < a.T) {
+    if (i == 0 && tk < a.T) {
+      const float dg = gamC * (sHdH[0] + sHdH[1] + sHdH[2] + sHdH[3]) + x;
       const int64_t idx = ((int64_t)b * a.T + tk) * a.H + h;
       float out = dg;
       if (a.gate_logit) {

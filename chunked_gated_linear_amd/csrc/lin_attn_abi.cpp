@@ -484,12 +484,12 @@ int lin_attn_chunk_bwd(const void* q, const void* k, const void* v, const float*
   const int64_t nst = (int64_t)B * H * Dk * Dv;
   const long long wsz = T > 0 ? la::chunk_bwd_workspace_bytes(B, T, H, Dk, Dv) : 0;
   if (T > 0) {
-    // q, k and dq, dk are read and written in 16-byte vectors of a row;
+    // q, k are read and dq, dk, dv written in 16-byte vectors of a row;
     // everything else element-wise
     const struct { const char* nm; const void* p; unsigned a; } req[] = {
         {"q", q, 16u}, {"k", k, 16u}, {"v", v, (unsigned)es}, {"gate", gate, 4u},
-        {"beta", beta, 4u}, {"dout", dout, (unsigned)es}, {"dq", dq, 4u}, {"dk", dk, 4u},
-        {"dv", dv, 4u}, {"dgate", dgate, 4u}, {"dbeta", dbeta, 4u}};
+        {"beta", beta, 4u}, {"dout", dout, (unsigned)es}, {"dq", dq, 16u}, {"dk", dk, 16u},
+        {"dv", dv, 16u}, {"dgate", dgate, 4u}, {"dbeta", dbeta, 4u}};
     for (const auto& r : req) {
       if (!r.p) return fail(LA_EINVAL, "%s must not be NULL", r.nm);
       if (!aligned(r.p, r.a)) return fail(LA_EINVAL, "%s must be %u-byte aligned", r.nm, r.a);

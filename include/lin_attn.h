@@ -331,7 +331,7 @@ long long lin_attn_chunk_bwd_workspace_size(int B, int T, int H, int Dk, int Dv,
  *     (q and k 16-byte aligned; h0 may be NULL = zeros)
  *   dout  [B, T, H, Dv] dtype: upstream gradient of o
  *   dhT   [B, H, Dk, Dv] float32 or NULL (zero): upstream gradient of hT
- *   dq, dk [B, T, H, Dk], dv [B, T, H, Dv] float32 outputs
+ *   dq, dk [B, T, H, Dk], dv [B, T, H, Dv] float32 outputs, 16-byte aligned
  *   dgate [B, T, H] float32 output: dL/dg (LA_GATE_LOG) or dL/dx
  *         (LA_GATE_BOUNDED_LOGIT, through g = -G * sigmoid(x))
  *   dbeta [B, T, H] float32 output

@@ -273,7 +273,8 @@ def bwd(**kw):
     (dict(dgate=None), N.LA_EINVAL, "dgate must not be NULL"),
     (dict(dbeta=None), N.LA_EINVAL, "dbeta must not be NULL"),
     (dict(q=fake(0) + 8), N.LA_EINVAL, "q must be 16-byte aligned"),
-    (dict(dv=fake(8) + 2), N.LA_EINVAL, "dv must be 4-byte aligned"),
+    (dict(dv=fake(8) + 2), N.LA_EINVAL, "dv must be 16-byte aligned"),
+    (dict(dq=fake(6) + 4), N.LA_EINVAL, "dq must be 16-byte aligned"),
     (dict(dh0=fake(11) + 2), N.LA_EINVAL, "dh0 must be 4-byte aligned"),
     (dict(gate_mode=3), N.LA_EINVAL, "gate_mode"),
     (dict(Dk=32), N.LA_EUNSUPPORTED, "Dk"),
