@@ -673,9 +673,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_grad_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float sQ[kT][KP];
   __shared__ float sTi[kT][kT + 1], sP[kT][kT + 1];
   __shared__ float sG[kT], sB[kT], sGam[kT], sEc[kT];
-  // per-wave transposition tiles during the slices; the cross-wave reduction
-  // of the dq / dk partials afterwards
-  constexpr int TR_BYTES = 4 * 2 * kT * TP * 4, RED_BYTES = 4 * NT * 64 * 16;
+  // per-wave transposition tiles (four per wave) during the slices; the
+  // cross-wave reduction of the dq / dk partials afterwards
+  constexpr int TR_BYTES = 4 * 4 * kT * TP * 4, RED_BYTES = 4 * NT * 64 * 16;
   __shared__ __attribute__((aligned(16))) char sU8[TR_BYTES > RED_BYTES ? TR_BYTES : RED_BYTES];
   __shared__ __attribute__((aligned(16))) f32x4 sRedS[4][2][64];   // dP, dA partials
   __shared__ float sRow[4][3][kT];                                    // row sums B, G, W
@@ -729,10 +729,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_grad_kernel(BwdArgs a) {
 
   const int tkn = c * kT + n;                          // token of row fragments
   const int64_t ron = ((int64_t)b * a.T + tkn) * a.H + h;
-  float (*tr)[TP] = reinterpret_cast<float (*)[TP]>(sU8 + w * 2 * kT * TP * 4);
-  float (*tr2)[TP] = tr + kT;
+  float (*tr)[TP] = reinterpret_cast<float (*)[TP]>(sU8 + w * 4 * kT * TP * 4);
   // X in accumulator order -> row fragment (lane (n, grp) register jj =
-  // X[n][4 grp + jj]) through the tile
+  // X[n][4 grp + jj]) through 16 x 16 tiles, up to four per LDS round trip
   auto transpose = [&](float (*tl)[TP], const f32x4& x) -> f32x4 {
 #pragma unroll
     for (int i = 0; i < 4; ++i) tl[4 * grp + i][n] = x[i];
@@ -744,6 +743,22 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_grad_kernel(BwdArgs a) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     return r;
+  };
+  auto transpose_n = [&](auto& x, auto& y) {
+    constexpr int M = sizeof(x) / sizeof(x[0]);
+    static_assert(M <= 4, "four tiles per wave");
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tr[m * kT + 4 * grp + i][n] = x[m][i];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int m = 0; m < M; ++m) y[m] = *reinterpret_cast<const f32x4*>(&tr[m * kT + n][4 * grp]);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
   f32x4 dQp[NT], dKp[NT];
@@ -802,9 +817,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_grad_kernel(BwdArgs a) {
       pG[i] += gm4[i] * QH[i] * dd[i] - bt4[i] * gm4[i] * dY[i] * KH[i];
       pW[i] += eKD[i] * U[i];
     }
-    const f32x4 Ur = transpose(tr, U);
-    const f32x4 DOr = transpose(tr, dd);
-    const f32x4 DYr = transpose(tr, dY);
+    f32x4 acc3[3] = {U, dd, dY}, row3[3];
+    transpose_n(acc3, row3);
+    const f32x4 Ur = row3[0], DOr = row3[1], DYr = row3[2];
     // dv = diag(beta) dY, a row fragment: token n, columns 16 jb + 4 grp + 0..3
     if (tkn < a.T)
       *reinterpret_cast<f32x4*>(a.dv + ron * a.Dv + 16 * jb + 4 * grp) = btn * DYr;
@@ -818,12 +833,15 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_grad_kernel(BwdArgs a) {
       aU[jj] = ecn * Ur[jj];
     }
 #pragma unroll
-    for (int r = 0; r < NT; ++r) {
-      const f32x4 Hr = transpose(tr, Hf[r]);
-      const f32x4 Dr = transpose(tr2, Df[r]);
-      dQp[r] = X::mma16(F16{aO}, F16{Hr}, dQp[r]);
-      dKp[r] = X::mma16(F16{aY}, F16{Hr}, dKp[r]);
-      dKp[r] = X::mma16(F16{aU}, F16{Dr}, dKp[r]);
+    for (int r = 0; r < NT; r += 2) {
+      f32x4 acc4[4] = {Hf[r], Df[r], Hf[r + 1], Df[r + 1]}, row4[4];
+      transpose_n(acc4, row4);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        dQp[r + e] = X::mma16(F16{aO}, F16{row4[2 * e]}, dQp[r + e]);
+        dKp[r + e] = X::mma16(F16{aY}, F16{row4[2 * e]}, dKp[r + e]);
+        dKp[r + e] = X::mma16(F16{aU}, F16{row4[2 * e + 1]}, dKp[r + e]);
+      }
     }
   }
 
