@@ -444,40 +444,26 @@ __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_channel_kernel(
         const int c = ep * NP + j;
         if (c >= NC) break;
         const char* rec = rec_of(ep, j);
-        // R = (K o Gam) H and (Q o Gam) H, contraction over d_k: fp32 MFMA
-        // for fp32 inputs; bf16 MFMA on the bf16 operands and a bf16 copy of
-        // the state for bf16 inputs
-        f32x4 Rk = zero4(), QH = zero4();
+        f32x4 O;
+        if constexpr (sizeof(E) == 4) {
+          // R = (K o Gam) H and (Q o Gam) H, contraction over d_k, then
+          // U = T (V - R), H' = diag(Gam_C) H + (K o Gam_C/Gam)^T U: fp32 MFMA
+          f32x4 Rk = zero4(), QH = zero4();
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          if constexpr (sizeof(E) == 4) {
+          for (int s = 0; s < NS; ++s) {
             const F32 hb = X::from_acc2(Hacc[2 * s], Hacc[2 * s + 1]);
             const F32 kf = reinterpret_cast<const F32*>(rec + R::KF)[s * 64 + lane];
             const F32 qf = reinterpret_cast<const F32*>(rec + R::QF)[s * 64 + lane];
             Rk = X::mma32(kf, hb, Rk);
             QH = X::mma32(qf, hb, QH);
-          } else {
-            using XB = Elt<__bf16>;
-            const XB::F32 hb = XB::from_acc2(Hacc[2 * s], Hacc[2 * s + 1]);
-            const XB::F32 kf = reinterpret_cast<const XB::F32*>(rec + R::KF)[s * 64 + lane];
-            const XB::F32 qf = reinterpret_cast<const XB::F32*>(rec + R::QF)[s * 64 + lane];
-            Rk = XB::mma32(kf, hb, Rk);
-            QH = XB::mma32(qf, hb, QH);
           }
-        }
-        const F16 vf = reinterpret_cast<const F16*>(rec + R::VF)[lane];
-        const F16 tb = *reinterpret_cast<const F16*>(rec + R::TB + (n * 16 + 4 * grp) * 4);
-        const F16 pf = reinterpret_cast<const F16*>(rec + R::PF)[lane];
-        f32x4 Y;
+          const F16 vf = reinterpret_cast<const F16*>(rec + R::VF)[lane];
+          const F16 tb = *reinterpret_cast<const F16*>(rec + R::TB + (n * 16 + 4 * grp) * 4);
+          const F16 pf = reinterpret_cast<const F16*>(rec + R::PF)[lane];
+          f32x4 Y;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Y[i] = vf.v[i] - Rk[i];
-        const f32x4 U = X::mma16(tb, X::from_acc(Y), zero4());
-        const f32x4 O = X::mma16(pf, X::from_acc(U), QH);
-        E* oc = orow + (int64_t)(16 * c) * ostride;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (16 * c + 4 * grp + i < T) oc[i * ostride] = Elt<E>::from_f(O[i]);
-        if constexpr (sizeof(E) == 4) {
+          for (int i = 0; i < 4; ++i) Y[i] = vf.v[i] - Rk[i];
+          const f32x4 U = X::mma16(tb, X::from_acc(Y), zero4());
           const F16 ub = X::from_acc(U);
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
@@ -487,10 +473,41 @@ __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_channel_kernel(
             for (int i = 0; i < 4; ++i) Hacc[t][i] *= gc[i];   // row 16t + 4grp + i
             Hacc[t] = X::mma16(kt, ub, Hacc[t]);
           }
+          O = X::mma16(pf, X::from_acc(U), QH);
         } else {
-          // H' += (K o Gam_C/Gam)^T (U_hi + U_lo): U split into bf16 high and
-          // low parts, one 32-deep bf16 MFMA per state tile
+          // bf16 MFMA on the bf16 operands and a bf16 copy of the state.  Every
+          // operand of the tile is requested from LDS at once, in order of
+          // first use, so that no read waits inside the chain R -> U -> H'.
           using XB = Elt<__bf16>;
+          XB::F32 kf[NS], qf[NS], kt[NT];
+          f32x4 gc[NT];
+#pragma unroll
+          for (int s = 0; s < NS; ++s) kf[s] = reinterpret_cast<const XB::F32*>(rec + R::KF)[s * 64 + lane];
+          const F16 vf = reinterpret_cast<const F16*>(rec + R::VF)[lane];
+          const F16 tb = *reinterpret_cast<const F16*>(rec + R::TB + (n * 16 + 4 * grp) * 4);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            kt[t] = reinterpret_cast<const XB::F32*>(rec + R::KT)[t * 64 + lane];
+            gc[t] = reinterpret_cast<const f32x4*>(rec + R::GC)[4 * t + grp];
+          }
+#pragma unroll
+          for (int s = 0; s < NS; ++s) qf[s] = reinterpret_cast<const XB::F32*>(rec + R::QF)[s * 64 + lane];
+          const F16 pf = reinterpret_cast<const F16*>(rec + R::PF)[lane];
+          __builtin_amdgcn_sched_barrier(0);
+          // R = (K o Gam) H
+          XB::F32 hb[NS];
+          f32x4 Rk = zero4();
+#pragma unroll
+          for (int s = 0; s < NS; ++s) {
+            hb[s] = XB::from_acc2(Hacc[2 * s], Hacc[2 * s + 1]);
+            Rk = XB::mma32(kf[s], hb[s], Rk);
+          }
+          f32x4 Y;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) Y[i] = vf.v[i] - Rk[i];
+          const f32x4 U = X::mma16(tb, X::from_acc(Y), zero4());
+          // H' = diag(Gam_C) H + (K o Gam_C/Gam)^T (U_hi + U_lo): U split into
+          // bf16 high and low parts, one 32-deep bf16 MFMA per state tile
           XB::F32 ub;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -500,13 +517,21 @@ __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_channel_kernel(
           }
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
-            const f32x4 gc = reinterpret_cast<const f32x4*>(rec + R::GC)[4 * t + grp];
-            const XB::F32 kt = reinterpret_cast<const XB::F32*>(rec + R::KT)[t * 64 + lane];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) Hacc[t][i] *= gc[i];   // row 16t + 4grp + i
-            Hacc[t] = XB::mma32(kt, ub, Hacc[t]);
+            for (int i = 0; i < 4; ++i) Hacc[t][i] *= gc[t][i];   // row 16t + 4grp + i
+            Hacc[t] = XB::mma32(kt[t], ub, Hacc[t]);
           }
+          // the output after the state update (the next tile does not wait
+          // for it): O = (Q o Gam) H + P U
+          f32x4 QH = zero4();
+#pragma unroll
+          for (int s = 0; s < NS; ++s) QH = XB::mma32(qf[s], hb[s], QH);
+          O = X::mma16(pf, X::from_acc(U), QH);
         }
+        E* oc = orow + (int64_t)(16 * c) * ostride;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (16 * c + 4 * grp + i < T) oc[i * ostride] = Elt<E>::from_f(O[i]);
       }
       __syncthreads();  // this epoch consumed, next epoch loaded
     }
