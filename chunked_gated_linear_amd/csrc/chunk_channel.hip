@@ -78,9 +78,14 @@ constexpr int kScrA = 0, kScrB = 1024, kScr = 1024 + 64;
 constexpr int kGcs = 8 * 64 * 16;
 constexpr int kKts = kScr, kPrepWave = kScr + kGcs + 128 * 4;
 
-template <int DK, int NP>
+// Records of two epochs of NP tiles; for bf16 inputs also the hand-off from
+// the chain to the loader wave that computes a tile's output: the tile's bf16
+// starting state and U, two epochs of NP tiles.
+template <typename E, int DK, int NP>
 struct ChCfg {
-  static constexpr int LDS = 2 * NP * ChRec<DK, 4>::LDS;   // the larger (fp32) layout
+  static constexpr int HAND = sizeof(E) == 2 ? (DK / 32 + 1) * 64 * 16 : 0;   // bytes per tile
+  static constexpr int HAND_AT = 2 * NP * ChRec<DK, sizeof(E)>::LDS;
+  static constexpr int LDS = HAND_AT + 2 * NP * HAND;
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
@@ -391,7 +396,7 @@ __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_channel_kernel(
     E* __restrict__ o, float* hT, int B, int TA, int H, int DV, const int* __restrict__ cu,
     int nslot) {
   using R = ChRec<DK, sizeof(E)>;
-  using C = ChCfg<DK, NP>;
+  using C = ChCfg<E, DK, NP>;
   using X = Elt<float>;
   using F16 = X::F16;
   using F32 = X::F32;
@@ -425,6 +430,11 @@ __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_channel_kernel(
 
   auto rowk = [&](int t) -> int64_t { return (tok0 + t) * H + h; };
   auto rec_of = [&](int ep, int j) -> char* { return smem + ((ep & 1) * NP + j) * R::LDS; };
+  auto hand_of = [&](int ep, int j) -> char* {
+    return smem + C::HAND_AT + ((ep & 1) * NP + j) * C::HAND;
+  };
+  const int64_t ostride = (int64_t)H * DV;
+  E* const orow = o + rowk(4 * grp) * DV + v0 + n;   // token 4 grp of the tile, column v0 + n
 
   if (wave == 0) {
     // ------------------------------------------------------------ chain wave
@@ -436,15 +446,12 @@ __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_channel_kernel(
       for (int i = 0; i < 4; ++i)
         Hacc[t][i] = h0 ? h0[sbase + (int64_t)(16 * t + 4 * grp + i) * DV + v0 + n] : 0.f;
     }
-    const int64_t ostride = (int64_t)H * DV;
-    E* const orow = o + rowk(4 * grp) * DV + v0 + n;
     __syncthreads();  // epoch 0 loaded
     for (int ep = 0; ep < NE; ++ep) {
       for (int j = 0; j < NP; ++j) {
         const int c = ep * NP + j;
         if (c >= NC) break;
         const char* rec = rec_of(ep, j);
-        f32x4 O;
         if constexpr (sizeof(E) == 4) {
           // R = (K o Gam) H and (Q o Gam) H, contraction over d_k, then
           // U = T (V - R), H' = diag(Gam_C) H + (K o Gam_C/Gam)^T U: fp32 MFMA
@@ -473,13 +480,17 @@ __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_channel_kernel(
             for (int i = 0; i < 4; ++i) Hacc[t][i] *= gc[i];   // row 16t + 4grp + i
             Hacc[t] = X::mma16(kt, ub, Hacc[t]);
           }
-          O = X::mma16(pf, X::from_acc(U), QH);
+          const f32x4 O = X::mma16(pf, X::from_acc(U), QH);
+          E* oc = orow + (int64_t)(16 * c) * ostride;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (16 * c + 4 * grp + i < T) oc[i * ostride] = Elt<E>::from_f(O[i]);
         } else {
           // bf16 MFMA on the bf16 operands and a bf16 copy of the state.  Every
-          // operand of the tile is requested from LDS at once, in order of
-          // first use, so that no read waits inside the chain R -> U -> H'.
+          // operand of the chain R -> U -> H' is requested from LDS at once, in
+          // order of first use, so that no read waits inside it.
           using XB = Elt<__bf16>;
-          XB::F32 kf[NS], qf[NS], kt[NT];
+          XB::F32 kf[NS], kt[NT];
           f32x4 gc[NT];
 #pragma unroll
           for (int s = 0; s < NS; ++s) kf[s] = reinterpret_cast<const XB::F32*>(rec + R::KF)[s * 64 + lane];
@@ -490,9 +501,6 @@ __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_channel_kernel(
             kt[t] = reinterpret_cast<const XB::F32*>(rec + R::KT)[t * 64 + lane];
             gc[t] = reinterpret_cast<const f32x4*>(rec + R::GC)[4 * t + grp];
           }
-#pragma unroll
-          for (int s = 0; s < NS; ++s) qf[s] = reinterpret_cast<const XB::F32*>(rec + R::QF)[s * 64 + lane];
-          const F16 pf = reinterpret_cast<const F16*>(rec + R::PF)[lane];
           __builtin_amdgcn_sched_barrier(0);
           // R = (K o Gam) H
           XB::F32 hb[NS];
@@ -521,17 +529,13 @@ __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_channel_kernel(
             for (int i = 0; i < 4; ++i) Hacc[t][i] *= gc[t][i];   // row 16t + 4grp + i
             Hacc[t] = XB::mma32(kt[t], ub, Hacc[t]);
           }
-          // the output after the state update (the next tile does not wait
-          // for it): O = (Q o Gam) H + P U
-          f32x4 QH = zero4();
+          // the output, O = (Q o Gam) H + P U, is the loader's: hand over the
+          // state the tile started from and U
+          char* hand = hand_of(ep, j);
 #pragma unroll
-          for (int s = 0; s < NS; ++s) QH = XB::mma32(qf[s], hb[s], QH);
-          O = X::mma16(pf, X::from_acc(U), QH);
+          for (int s2 = 0; s2 < NS; ++s2) reinterpret_cast<XB::F32*>(hand)[s2 * 64 + lane] = hb[s2];
+          reinterpret_cast<f32x4*>(hand + NS * 1024)[lane] = U;
         }
-        E* oc = orow + (int64_t)(16 * c) * ostride;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (16 * c + 4 * grp + i < T) oc[i * ostride] = Elt<E>::from_f(O[i]);
       }
       __syncthreads();  // this epoch consumed, next epoch loaded
     }
@@ -581,8 +585,35 @@ __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_channel_kernel(
     reinterpret_cast<F16*>(rec + R::VF)[lane] = vf;
   };
 
+  // bf16 inputs: the output of tile e NP + p, from the chain's hand-off and
+  // the record still in this loader's slot (it is refilled only afterwards,
+  // by this same wave): O = (Q o Gam) H + P U on this wave's matrix core.
+  auto output = [&](int e) {
+    if constexpr (sizeof(E) == 2) {
+      const int c = e * NP + p;
+      if (e < 0 || c >= NC) return;
+      using XB = Elt<__bf16>;
+      const char* rec = rec_of(e, p);
+      const char* hand = hand_of(e, p);
+      f32x4 QH = zero4();
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+        QH = XB::mma32(reinterpret_cast<const XB::F32*>(rec + R::QF)[s * 64 + lane],
+                       reinterpret_cast<const XB::F32*>(hand)[s * 64 + lane], QH);
+      const f32x4 U = reinterpret_cast<const f32x4*>(hand + NS * 1024)[lane];
+      const F16 pf = reinterpret_cast<const F16*>(rec + R::PF)[lane];
+      const f32x4 O = X::mma16(pf, X::from_acc(U), QH);
+      E* oc = orow + (int64_t)(16 * c) * ostride;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (16 * c + 4 * grp + i < T) oc[i * ostride] = Elt<E>::from_f(O[i]);
+    }
+  };
+
   // Two register sets alternating by epoch: while tile (ep+1)*NP + p is
-  // stored from one, the loads for tile (ep+2)*NP + p fill the other.
+  // stored from one, the loads for tile (ep+2)*NP + p fill the other.  The
+  // slot being refilled held epoch ep - 1, whose output is formed first.
+  // (Loads issued two epochs ahead, from a third set, measured no faster.)
   ChCopy<E, DK> ra, rb;
   load(ra, p);
   store(ra, p);                 // epoch 0
@@ -590,14 +621,17 @@ __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_channel_kernel(
   __syncthreads();
   for (int ep = 0; ep < NE; ep += 2) {
     load(rb, (ep + 2) * NP + p);
+    output(ep - 1);
     store(ra, (ep + 1) * NP + p);
     __syncthreads();
     if (ep + 1 < NE) {
       load(ra, (ep + 3) * NP + p);
+      output(ep);
       store(rb, (ep + 2) * NP + p);
       __syncthreads();
     }
   }
+  output(NE - 1);               // the last epoch: its slot is not refilled
 }
 
 // B sequences of T tokens (cu == nullptr), or B packed sequences with device
@@ -745,8 +779,11 @@ hipError_t launch_chunk_fwd_channel_varlen(const void* q, const void* k, const v
                                            const float* beta, const float* h0, void* o,
                                            float* hT, const int* cu, int B, int T, int H, int Dk,
                                            int Dv, int fp32, void* ws, hipStream_t st) {
+// tiles per epoch (= loader waves): three for bf16 records, two for the
+// larger fp32 ones (LDS)
 #define LA_CH(E, DK) \
-  return launch_ch<E, DK, 2>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, cu, ws, st)
+  return launch_ch<E, DK, sizeof(E) == 2 ? 3 : 2>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, \
+                                                  B, T, H, Dv, cu, ws, st)
   if (fp32) {
     if (Dk == 64) LA_CH(float, 64);
     if (Dk == 128) LA_CH(float, 128);
