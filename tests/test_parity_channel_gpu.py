@@ -67,6 +67,12 @@ CASES = [
     ("bf16", 64, 256, 1, 1, 33, "weak", "logit", 0.02),
     ("bf16", 128, 128, 1, 2, 1, "std", "logit", 0.02),
     ("bf16", 128, 128, 1, 2, 16, "std", "logit", 0.02),
+    # bf16 records are consumed three tiles per epoch: tile counts of every
+    # residue mod 3, one partial epoch, and whole epochs only
+    ("bf16", 128, 128, 1, 2, 32, "weak", "logit", 0.02),       # 2 tiles
+    ("bf16", 128, 128, 2, 1, 64, "std", "logit", 0.02),        # 4 tiles
+    ("bf16", 128, 64, 1, 2, 80, "std", "log", 0.02),           # 5 tiles
+    ("bf16", 64, 128, 1, 2, 96, "weak", "logit", None),        # 6 tiles, two whole epochs
 ]
 
 
@@ -254,6 +260,7 @@ def _packed(lengths, H, Dk, Dv, dtype, seed, mu=-3.0, h0_std=0.02):
     ("fp32", 64, 32, [17, 0, 40, 1, 33]),
     ("bf16", 128, 128, [100, 0, 16, 5, 250, 0]),
     ("bf16", 64, 256, [48, 31]),
+    ("bf16", 128, 128, [32, 80, 96, 64, 1, 47]),               # 2, 5, 6, 4, 1, 3 tiles
 ])
 def test_channel_varlen_parity(dtype, Dk, Dv, lengths):
     from chunked_gated_linear_amd import lin_attn_chunk_fwd_channel_varlen
