@@ -242,8 +242,9 @@ def lin_attn_chunk_fwd_varlen(q, k, v, gate, beta, cu_seqlens, h0=None, *, gate_
     nseq sequences back to back, sequence s at tokens [cu[s], cu[s+1]) with
     cu_seqlens an int32 GPU tensor of nseq + 1 offsets.  Returns o [1,T,H,Dv]
     and the final states hT [nseq,H,Dk,Dv] (None if not requested).  raw=True:
-    q, k as they come and `beta` holding logits, as in lin_attn_chunk_fwd."""
-    _need(q, "q", torch.bfloat16)
+    q, k as they come and `beta` holding logits, as in lin_attn_chunk_fwd
+    (bf16 only).  bf16 or float32 q, k, v; float32 needs no workspace."""
+    _need(q, "q")
     _, T, H, Dk = q.shape
     Dv = v.shape[-1]
     _need(k, "k", q.dtype, (1, T, H, Dk))

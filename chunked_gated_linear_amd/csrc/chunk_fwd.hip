@@ -96,7 +96,7 @@ __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ gate, int gate_logit, float G,
     const float* __restrict__ beta, const float* h0, E* __restrict__ o, float* hT,
-    int B, int T, int H, int DV) {
+    int B, int TA, int H, int DV, const int* __restrict__ cu) {
   using C = Cfg<E, DK, NP>;
   using X = Elt<E>;
   using F16 = typename X::F16;
@@ -112,11 +112,24 @@ __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, grp = lane >> 4;
+  // sequence b: T tokens from token tok0 of the token axis -- B sequences of
+  // TA tokens (cu == NULL), or tokens [cu[b], cu[b+1]) of one packed sequence
+  // of TA tokens (offsets clamped to [0, TA] and made non-decreasing)
+  int T;
+  int64_t tok0;
+  if (cu) {
+    const int tb = min(max(cu[b], 0), TA);
+    T = min(max(cu[b + 1], tb), TA) - tb;
+    tok0 = tb;
+  } else {
+    T = TA;
+    tok0 = (int64_t)b * TA;
+  }
   const int NC = (T + 15) >> 4;
   const int NE = (NC + NP - 1) / NP;
 
-  // element offsets of token (b, t, h)
-  auto rowk = [&](int t) -> int64_t { return ((int64_t)b * T + t) * H + h; };
+  // element offsets of token t of the sequence, head h
+  auto rowk = [&](int t) -> int64_t { return (tok0 + t) * H + h; };
   auto rec_of = [&](int ep, int j) -> char* { return smem + ((ep & 1) * NP + j) * C::REC; };
 
   if (wave == 0) {
@@ -213,6 +226,7 @@ __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_kernel(
   // the number of loads in flight is the same on every path and the compiler
   // can wait for exactly the older set.
   auto load = [&](Raw<E, DK>& r, int c) {
+    if (NC == 0) return;          // an empty sequence loads nothing
     c = min(c, NC - 1);
     const int t = min(16 * c + n, T - 1);
     const int64_t base = rowk(t) * DK;
@@ -370,14 +384,17 @@ __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_kernel(
   }
 }
 
+// B sequences of T tokens (cu == NULL), or B packed sequences with device
+// offsets cu in one sequence of T tokens.
 template <typename E, int DK, int NP>
 static hipError_t launch_t(const void* q, const void* k, const void* v, const float* gate,
                            int gate_logit, float G, const float* beta, const float* h0,
-                           void* o, float* hT, int B, int T, int H, int Dv, hipStream_t st) {
+                           void* o, float* hT, int B, int T, int H, int Dv, const int* cu,
+                           hipStream_t st) {
   const int blocks = B * H * (Dv / 16);
   hipLaunchKernelGGL((chunk_fwd_kernel<E, DK, NP>), dim3(blocks), dim3(64 * (NP + 1)), 0, st,
                      (const E*)q, (const E*)k, (const E*)v, gate, gate_logit, G, beta, h0,
-                     (E*)o, hT, B, T, H, Dv);
+                     (E*)o, hT, B, T, H, Dv, cu);
   return hipGetLastError();
 }
 
@@ -385,8 +402,19 @@ hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v, const f
                             int gate_logit, float G, const float* beta, const float* h0,
                             void* o, float* hT, int B, int T, int H, int Dk, int Dv,
                             hipStream_t st) {
-  if (Dk == 64) return launch_t<float, 64, 2>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, st);
-  if (Dk == 128) return launch_t<float, 128, 2>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, st);
+  return launch_chunk_fwd_varlen(q, k, v, gate, gate_logit, G, beta, h0, o, hT, nullptr, B, T, H,
+                                 Dk, Dv, st);
+}
+
+hipError_t launch_chunk_fwd_varlen(const void* q, const void* k, const void* v,
+                                   const float* gate, int gate_logit, float G,
+                                   const float* beta, const float* h0, void* o, float* hT,
+                                   const int* cu, int B, int T, int H, int Dk, int Dv,
+                                   hipStream_t st) {
+  if (Dk == 64)
+    return launch_t<float, 64, 2>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, cu, st);
+  if (Dk == 128)
+    return launch_t<float, 128, 2>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, cu, st);
   return hipErrorInvalidValue;
 }
 

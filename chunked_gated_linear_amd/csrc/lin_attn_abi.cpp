@@ -86,8 +86,6 @@ int check_chunk_sizes(int B, int T, int H, int Dk, int Dv, int dtype) {
 int check_varlen_sizes(int T, int nseq, int H, int Dk, int Dv, int dtype) {
   if (nseq < 0) return fail(LA_EINVAL, "nseq must be >= 0, got %d", nseq);
   if (int rc = check_chunk_sizes(nseq > 0 ? 1 : 0, T, H, Dk, Dv, dtype)) return rc;
-  if (dtype != LA_BF16)
-    return fail(LA_EUNSUPPORTED, "packed sequences are supported in LA_BF16 only");
   if ((int64_t)nseq * H * (Dv / 16) > INT32_MAX || (int64_t)T / 32 + nseq + 1 > INT32_MAX / 2)
     return fail(LA_EINVAL, "problem too large (nseq = %d)", nseq);
   return LA_OK;
@@ -235,7 +233,8 @@ long long lin_attn_chunk_fwd_varlen_workspace_size(int T, int nseq, int H, int D
                                                    int dtype) {
   if (check_varlen_sizes(T, nseq, H, Dk, Dv, dtype)) return -1;
   ok();
-  return la::chunk_pair_varlen_workspace_bytes(T, nseq, H);
+  // the fp32 path needs no workspace
+  return dtype == LA_BF16 ? la::chunk_pair_varlen_workspace_bytes(T, nseq, H) : 0;
 }
 
 }  // extern "C"
@@ -249,9 +248,13 @@ int chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* g
                      int dtype, void* workspace, long long workspace_bytes, void* stream,
                      int raw) {
   if (int rc = check_varlen_sizes(T, nseq, H, Dk, Dv, dtype)) return rc;
+  if (raw && dtype != LA_BF16)
+    return fail(LA_EUNSUPPORTED, "raw inputs are supported in LA_BF16 only");
   if (int rc = check_gate_scalars(gate_mode, G)) return rc;
-  const long long wsz = la::chunk_pair_varlen_workspace_bytes(T, nseq, H);
+  // the fp32 path needs no workspace
+  const long long wsz = dtype == LA_BF16 ? la::chunk_pair_varlen_workspace_bytes(T, nseq, H) : 0;
   if (nseq == 0 || H == 0) return ok();
+  const int64_t es = dtype == LA_BF16 ? 2 : 4;
   const int64_t ntok = (int64_t)T * H;
   const int64_t nst = (int64_t)nseq * H * Dk * Dv;
   if (!cu_seqlens) return fail(LA_EINVAL, "cu_seqlens must not be NULL");
@@ -259,7 +262,7 @@ int chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* g
   if (T > 0) {
     const struct { const char* nm; const void* p; unsigned a; } req[] = {
         {"q", q, 16u}, {"k", k, 16u}, {"v", v, 16u}, {"gate", gate, 4u}, {"beta", beta, 4u},
-        {"o", o, 8u}};
+        {"o", o, dtype == LA_BF16 ? 8u : 4u}};
     for (const auto& r : req) {
       if (!r.p) return fail(LA_EINVAL, "%s must not be NULL", r.nm);
       if (!aligned(r.p, r.a)) return fail(LA_EINVAL, "%s must be %u-byte aligned", r.nm, r.a);
@@ -267,15 +270,17 @@ int chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* g
   }
   if (h0 && !aligned(h0, 4u)) return fail(LA_EINVAL, "h0 must be 4-byte aligned");
   if (hT && !aligned(hT, 4u)) return fail(LA_EINVAL, "hT must be 4-byte aligned");
-  if (!workspace) return fail(LA_EINVAL, "workspace must not be NULL (%lld bytes needed)", wsz);
-  if (!aligned(workspace, 256u)) return fail(LA_EINVAL, "workspace must be 256-byte aligned");
-  if (workspace_bytes < wsz)
-    return fail(LA_EINVAL, "workspace too small: %lld bytes given, %lld needed", workspace_bytes,
-                wsz);
-  const Span sq = span("q", q, ntok * Dk * 2), sk = span("k", k, ntok * Dk * 2),
-             sv = span("v", v, ntok * Dv * 2), sg = span("gate", gate, ntok * 4),
+  if (wsz > 0) {
+    if (!workspace) return fail(LA_EINVAL, "workspace must not be NULL (%lld bytes needed)", wsz);
+    if (!aligned(workspace, 256u)) return fail(LA_EINVAL, "workspace must be 256-byte aligned");
+    if (workspace_bytes < wsz)
+      return fail(LA_EINVAL, "workspace too small: %lld bytes given, %lld needed",
+                  workspace_bytes, wsz);
+  }
+  const Span sq = span("q", q, ntok * Dk * es), sk = span("k", k, ntok * Dk * es),
+             sv = span("v", v, ntok * Dv * es), sg = span("gate", gate, ntok * 4),
              sb = span("beta", beta, ntok * 4), sh0 = span("h0", h0, nst * 4),
-             so = span("o", o, ntok * Dv * 2), shT = span("hT", hT, nst * 4),
+             so = span("o", o, ntok * Dv * es), shT = span("hT", hT, nst * 4),
              sc = span("cu_seqlens", cu_seqlens, ((int64_t)nseq + 1) * 4);
   for (const Span& in : {sq, sk, sv, sg, sb, sh0, shT, sc})
     if (overlap(so, in)) return fail(LA_EINVAL, "o overlaps %s", in.name);
@@ -286,9 +291,14 @@ int chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* g
     if (overlap(shT, in)) return fail(LA_EINVAL, "hT overlaps %s", in.name);
   if (hT && h0 && hT != h0 && overlap(shT, sh0))
     return fail(LA_EINVAL, "hT partially overlaps h0 (only hT == h0 is allowed)");
-  hipError_t e = la::launch_chunk_fwd_pair_varlen(
-      q, k, v, gate, gate_mode == LA_GATE_BOUNDED_LOGIT, G, beta, h0, o, hT, cu_seqlens, nseq, T,
-      H, Dk, Dv, raw, workspace, reinterpret_cast<hipStream_t>(stream));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e =
+      dtype == LA_BF16
+          ? la::launch_chunk_fwd_pair_varlen(q, k, v, gate, gate_mode == LA_GATE_BOUNDED_LOGIT, G,
+                                             beta, h0, o, hT, cu_seqlens, nseq, T, H, Dk, Dv, raw,
+                                             workspace, st)
+          : la::launch_chunk_fwd_varlen(q, k, v, gate, gate_mode == LA_GATE_BOUNDED_LOGIT, G, beta,
+                                        h0, o, hT, cu_seqlens, nseq, T, H, Dk, Dv, st);
   return hip_status(e, "chunk_fwd_varlen launch");
 }
 

@@ -191,8 +191,8 @@ long long lin_attn_chunk_fwd_channel_workspace_size(int B, int T, int H, int Dk,
  * lin_attn_chunk_fwd_varlen needs: H * (T / 32 + nseq + 1) * 6656 for LA_BF16
  * (one 6656-byte record slot per 32 tokens of each packed sequence, as in
  * lin_attn_chunk_fwd, plus one spare slot per sequence for its ragged end),
- * -1 (with lin_attn_last_error() set) for invalid or unsupported sizes,
- * including dtype LA_FP32.
+ * 0 for LA_FP32, -1 (with lin_attn_last_error() set) for invalid or
+ * unsupported sizes.
  */
 long long lin_attn_chunk_fwd_varlen_workspace_size(int T, int nseq, int H, int Dk, int Dv,
                                                    int dtype);
@@ -206,8 +206,8 @@ long long lin_attn_chunk_fwd_varlen_workspace_size(int T, int nseq, int H, int D
  * exactly as lin_attn_chunk_fwd processes a sequence of its length (its own
  * tiles start at its first token).
  *
- *   q, k        [T, H, Dk]  bf16         (a batch of one packed sequence)
- *   v, o        [T, H, Dv]  bf16
+ *   q, k        [T, H, Dk]  dtype        (a batch of one packed sequence)
+ *   v, o        [T, H, Dv]  dtype
  *   gate, beta  [T, H]      float32
  *   h0, hT      [nseq, H, Dk, Dv] float32, or NULL as in lin_attn_chunk_fwd
  *   cu_seqlens  DEVICE array of nseq + 1 int32 offsets: 0 = cu[0] <= cu[1] <=
@@ -217,8 +217,9 @@ long long lin_attn_chunk_fwd_varlen_workspace_size(int T, int nseq, int H, int D
  *               non-decreasing give undefined results.  Empty sequences are
  *               allowed (their hT is h0, or zeros).
  *   workspace   lin_attn_chunk_fwd_varlen_workspace_size(...) bytes, as in
- *               lin_attn_chunk_fwd.
- *   dtype       LA_BF16 only (LA_FP32 returns LA_EUNSUPPORTED).
+ *               lin_attn_chunk_fwd (none, and may be NULL, for LA_FP32).
+ *   dtype       LA_BF16 or LA_FP32 (the fp32 path: one fused kernel, one
+ *               workgroup per sequence, head and 16 columns of d_v).
  *   Dk in {64, 128}; Dv a multiple of 16 in [16, 256]; T, nseq, H >= 0.
  * Alignment and aliasing rules are those of lin_attn_chunk_fwd.
  */
@@ -234,7 +235,8 @@ int lin_attn_chunk_fwd_varlen(const void* q, const void* k, const void* v,
  * lin_attn_chunk_fwd_varlen_raw -- lin_attn_chunk_fwd_varlen with the input
  * preparation of lin_attn_chunk_fwd_raw: q and k as given (L2-normalised per
  * token and head inside the pass), beta_logit holding x_beta.  Same arguments,
- * workspace, rules and errors otherwise.
+ * workspace, rules and errors otherwise, except that dtype is LA_BF16 only
+ * (LA_FP32 returns LA_EUNSUPPORTED).
  */
 int lin_attn_chunk_fwd_varlen_raw(const void* q, const void* k, const void* v,
                                   const float* gate, int gate_mode, float G,

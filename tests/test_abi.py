@@ -210,7 +210,6 @@ def varlen(**kw):
     (dict(cu=None), N.LA_EINVAL, "cu_seqlens must not be NULL"),
     (dict(cu=fake(9) + 2), N.LA_EINVAL, "cu_seqlens must be 4-byte aligned"),
     (dict(nseq=-1), N.LA_EINVAL, "nseq"),
-    (dict(dtype=1), N.LA_EUNSUPPORTED, "LA_BF16 only"),
     (dict(Dk=96), N.LA_EUNSUPPORTED, "Dk"),
     (dict(q=None), N.LA_EINVAL, "q must not be NULL"),
     (dict(gate_mode=5), N.LA_EINVAL, "gate_mode"),
@@ -232,10 +231,18 @@ def test_varlen_workspace_size_and_empty():
     # one record slot per 32 tokens per head plus one per sequence and one spare
     assert ws(65536, 64, 16, 128, 128, N.LA_BF16) == 16 * (2048 + 64 + 1) * 6656
     assert ws(100, 3, 2, 64, 64, N.LA_BF16) == 2 * (3 + 3 + 1) * 6656
-    assert ws(100, 3, 2, 64, 64, N.LA_FP32) == -1
-    assert "LA_BF16 only" in L.lin_attn_last_error().decode()
+    assert ws(100, 3, 2, 64, 64, N.LA_FP32) == 0        # the fp32 path needs none
     # no sequences: nothing to do, nothing touched
     assert varlen(nseq=0, q=None, cu=None, ws=None)[0] == N.LA_OK
+
+
+def test_varlen_raw_is_bf16_only():
+    a = dict(q=fake(0), k=fake(1), v=fake(2), gate=fake(3), gate_mode=0, G=5.0, beta=fake(4),
+             h0=None, o=fake(5), hT=fake(6), cu=fake(7), nseq=3, T=64, H=2, Dk=64, Dv=64)
+    L = N.lib()
+    rc = L.lin_attn_chunk_fwd_varlen_raw(*a.values(), N.LA_FP32, None, 0, None)
+    assert rc == N.LA_EUNSUPPORTED
+    assert "LA_BF16 only" in L.lin_attn_last_error().decode()
 
 
 def test_raw_entry_checks():

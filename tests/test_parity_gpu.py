@@ -261,6 +261,54 @@ def test_varlen_equal_lengths_match_batched_bitwise():
     assert torch.equal(o_v.reshape(o_b.shape), o_b) and torch.equal(h_v, h_b)
 
 
+VARLEN_FP32 = [
+    # sequence lengths, H, Dk, Dv, regime, gate mode, with h0
+    ([0, 1, 17, 32, 33, 100, 250], 2, 128, 128, "weak", "logit", True),
+    ([5, 0, 64, 77, 48], 3, 64, 32, "std", "log", False),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN_FP32,
+                         ids=lambda c: f"n{len(c[0])}-H{c[1]}-d{c[2]}x{c[3]}-{c[4]}")
+def test_varlen_fp32(case):
+    """The fp32 path over packed sequences (no workspace) against the oracle,
+    every output; an empty sequence's final state is its h0 exactly."""
+    lengths, H, Dk, Dv, regime, mode, with_h0 = case
+    T, nseq = int(sum(lengths)), len(lengths)
+    name = f"varlen {nseq} seqs T{T} H{H} dk{Dk} dv{Dv} fp32 {regime}"
+    say(name)
+    dev, hst = make_case(1, T, H, Dk, Dv, "fp32", regime, mode, None, seed=25)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int32, device="cuda")
+    h0 = None
+    if with_h0:
+        gen = torch.Generator(device="cuda").manual_seed(26)
+        h0 = 0.02 * torch.randn((nseq, H, Dk, Dv), generator=gen, device="cuda")
+    o, hT = lin_attn_chunk_fwd_varlen(dev["q"], dev["k"], dev["v"], dev["gate"], dev["beta"], cu,
+                                      h0, gate_mode=mode)
+    torch.cuda.synchronize()
+    q, k, v, g, beta, _ = hst
+    ref_o, ref_h = crec.recurrent_fwd_varlen(q, k, v, g, beta, cu.cpu().numpy(),
+                                             None if h0 is None else host(h0).astype(np.float64))
+    check(name, "fp32", o, hT, ref_o, ref_h)
+    for s_, n_ in enumerate(lengths):
+        if n_ == 0:
+            assert torch.equal(hT[s_], h0[s_] if h0 is not None else torch.zeros_like(hT[s_]))
+
+
+def test_varlen_fp32_equal_lengths_match_batched_bitwise():
+    """fp32, equal lengths: the packed call reproduces the batched call bit for bit."""
+    say("varlen vs batched: 3 x 200 tokens H2 d64 fp32 weak")
+    N_, L_, H = 3, 200, 2
+    dev, _ = make_case(N_, L_, H, 64, 64, "fp32", "weak", "logit", 0.02, seed=27)
+    o_b, h_b = run_gpu(dev)
+    pk = lambda t: t.reshape((1, N_ * L_) + tuple(t.shape[2:]))
+    cu = torch.tensor([0, L_, 2 * L_, 3 * L_], dtype=torch.int32, device="cuda")
+    o_v, h_v = lin_attn_chunk_fwd_varlen(pk(dev["q"]), pk(dev["k"]), pk(dev["v"]), pk(dev["gate"]),
+                                         pk(dev["beta"]), cu, dev["h0"], gate_mode="logit")
+    torch.cuda.synchronize()
+    assert torch.equal(o_v.reshape(o_b.shape), o_b) and torch.equal(h_v, h_b)
+
+
 # ------------------------------------------------- raw inputs (fused prep)
 RAW = [
     # B, H, T, Dk, Dv, regime, with h0
