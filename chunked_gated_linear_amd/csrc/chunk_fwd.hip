@@ -96,7 +96,7 @@ __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ gate, int gate_logit, float G,
     const float* __restrict__ beta, const float* h0, E* __restrict__ o, float* hT,
-    int B, int TA, int H, int DV, const int* __restrict__ cu) {
+    int B, int TA, int H, int DV, const int* __restrict__ cu, int raw) {
   using C = Cfg<E, DK, NP>;
   using X = Elt<E>;
   using F16 = typename X::F16;
@@ -259,7 +259,8 @@ __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_kernel(
     // padding tokens past T: q = k = v = 0, g = 0, beta = 0 (an identity step)
     const bool ok = 16 * c + n < T;
     const float g = ok ? (gate_logit ? bounded_gate(r.gx, G) : r.gx) : 0.f;
-    const float bt = ok ? r.bt : 0.f;
+    // raw inputs: beta from its logit
+    const float bt = ok ? (raw ? sigmoid_f(r.bt) : r.bt) : 0.f;
     F32 kf[NS], qf[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
@@ -268,6 +269,32 @@ __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_kernel(
       if (!ok) {
         kf[s] = F32{};
         qf[s] = F32{};
+      }
+    }
+    if (raw) {
+      // raw inputs: q and k L2-normalised per token (a zero vector stays
+      // zero); lanes (n, grp = 0..3) together hold all d_k channels of token n
+      float sk = 0.f, sq = 0.f;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sk += kf[s].lo[i] * kf[s].lo[i] + kf[s].hi[i] * kf[s].hi[i];
+          sq += qf[s].lo[i] * qf[s].lo[i] + qf[s].hi[i] * qf[s].hi[i];
+        }
+      }
+      sk += __shfl_xor(sk, 16);
+      sk += __shfl_xor(sk, 32);
+      sq += __shfl_xor(sq, 16);
+      sq += __shfl_xor(sq, 32);
+      const float ik = sk > 0.f ? 1.f / sqrtf(sk) : 0.f;
+      const float iq = sq > 0.f ? 1.f / sqrtf(sq) : 0.f;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        kf[s].lo *= ik;
+        kf[s].hi *= ik;
+        qf[s].lo *= iq;
+        qf[s].hi *= iq;
       }
     }
     const float Gi = scan16(g, n);              // G_n, inclusive
@@ -390,31 +417,33 @@ template <typename E, int DK, int NP>
 static hipError_t launch_t(const void* q, const void* k, const void* v, const float* gate,
                            int gate_logit, float G, const float* beta, const float* h0,
                            void* o, float* hT, int B, int T, int H, int Dv, const int* cu,
-                           hipStream_t st) {
+                           int raw, hipStream_t st) {
   const int blocks = B * H * (Dv / 16);
   hipLaunchKernelGGL((chunk_fwd_kernel<E, DK, NP>), dim3(blocks), dim3(64 * (NP + 1)), 0, st,
                      (const E*)q, (const E*)k, (const E*)v, gate, gate_logit, G, beta, h0,
-                     (E*)o, hT, B, T, H, Dv, cu);
+                     (E*)o, hT, B, T, H, Dv, cu, raw);
   return hipGetLastError();
 }
 
 hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v, const float* gate,
                             int gate_logit, float G, const float* beta, const float* h0,
-                            void* o, float* hT, int B, int T, int H, int Dk, int Dv,
+                            void* o, float* hT, int B, int T, int H, int Dk, int Dv, int raw,
                             hipStream_t st) {
   return launch_chunk_fwd_varlen(q, k, v, gate, gate_logit, G, beta, h0, o, hT, nullptr, B, T, H,
-                                 Dk, Dv, st);
+                                 Dk, Dv, raw, st);
 }
 
 hipError_t launch_chunk_fwd_varlen(const void* q, const void* k, const void* v,
                                    const float* gate, int gate_logit, float G,
                                    const float* beta, const float* h0, void* o, float* hT,
-                                   const int* cu, int B, int T, int H, int Dk, int Dv,
+                                   const int* cu, int B, int T, int H, int Dk, int Dv, int raw,
                                    hipStream_t st) {
   if (Dk == 64)
-    return launch_t<float, 64, 2>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, cu, st);
+    return launch_t<float, 64, 2>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, cu,
+                                  raw, st);
   if (Dk == 128)
-    return launch_t<float, 128, 2>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, cu, st);
+    return launch_t<float, 128, 2>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, cu,
+                                   raw, st);
   return hipErrorInvalidValue;
 }
 

@@ -6,11 +6,12 @@
 
 namespace la {
 
-// fp32 path: one fused kernel, no workspace.
+// fp32 path: one fused kernel, no workspace.  raw != 0: q and k are
+// L2-normalised per token inside the pass and beta holds logits.
 hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v,
                             const float* gate, int gate_logit, float G,
                             const float* beta, const float* h0, void* o, float* hT,
-                            int B, int T, int H, int Dk, int Dv, hipStream_t st);
+                            int B, int T, int H, int Dk, int Dv, int raw, hipStream_t st);
 
 // The fp32 path over packed sequences: sequence s is tokens [cu[s], cu[s+1])
 // of one packed sequence of T tokens (cu: device array of nseq + 1 offsets).
@@ -18,7 +19,7 @@ hipError_t launch_chunk_fwd_varlen(const void* q, const void* k, const void* v,
                                    const float* gate, int gate_logit, float G,
                                    const float* beta, const float* h0, void* o, float* hT,
                                    const int* cu, int nseq, int T, int H, int Dk, int Dv,
-                                   hipStream_t st);
+                                   int raw, hipStream_t st);
 
 // bf16 path: intra-tile kernel into the workspace, then the inter-tile kernel;
 // the state is carried across pairs of 16-token tiles.  raw != 0: q and k are

@@ -123,8 +123,6 @@ int chunk_fwd(const void* q, const void* k, const void* v, const float* gate, in
               int H, int Dk, int Dv, int dtype, void* workspace, long long workspace_bytes,
               void* stream, int raw, int channel = 0) {
   if (int rc = check_chunk_sizes(B, T, H, Dk, Dv, dtype)) return rc;
-  if (raw && dtype != LA_BF16)
-    return fail(LA_EUNSUPPORTED, "raw inputs are supported in LA_BF16 only");
   if (int rc = check_gate_scalars(gate_mode, G)) return rc;
   // per-channel gate: the in-tile operands reach exp(+-8 G); G <= 10 keeps
   // them at most exp(80), inside the float range
@@ -187,7 +185,7 @@ int chunk_fwd(const void* q, const void* k, const void* v, const float* gate, in
                                                    st),
                       "chunk_fwd_channel launch");
   hipError_t e = dtype == LA_FP32
-      ? la::launch_chunk_fwd(q, k, v, gate, logit, G, beta, h0, o, hT, B, T, H, Dk, Dv, st)
+      ? la::launch_chunk_fwd(q, k, v, gate, logit, G, beta, h0, o, hT, B, T, H, Dk, Dv, raw, st)
       : la::launch_chunk_fwd_pair(q, k, v, gate, logit, G, beta, h0, o, hT, B, T, H, Dk, Dv,
                                   raw, workspace, st);
   return hip_status(e, "chunk_fwd launch");
@@ -248,8 +246,6 @@ int chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* g
                      int dtype, void* workspace, long long workspace_bytes, void* stream,
                      int raw) {
   if (int rc = check_varlen_sizes(T, nseq, H, Dk, Dv, dtype)) return rc;
-  if (raw && dtype != LA_BF16)
-    return fail(LA_EUNSUPPORTED, "raw inputs are supported in LA_BF16 only");
   if (int rc = check_gate_scalars(gate_mode, G)) return rc;
   // the fp32 path needs no workspace
   const long long wsz = dtype == LA_BF16 ? la::chunk_pair_varlen_workspace_bytes(T, nseq, H) : 0;
@@ -298,7 +294,7 @@ int chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* g
                                              beta, h0, o, hT, cu_seqlens, nseq, T, H, Dk, Dv, raw,
                                              workspace, st)
           : la::launch_chunk_fwd_varlen(q, k, v, gate, gate_mode == LA_GATE_BOUNDED_LOGIT, G, beta,
-                                        h0, o, hT, cu_seqlens, nseq, T, H, Dk, Dv, st);
+                                        h0, o, hT, cu_seqlens, nseq, T, H, Dk, Dv, raw, st);
   return hip_status(e, "chunk_fwd_varlen launch");
 }
 

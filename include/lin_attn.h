@@ -132,10 +132,11 @@ int lin_attn_chunk_fwd(const void* q, const void* k, const void* v,
  * fp32 from the given values (a zero vector stays zero), and beta_logit holds
  * x_beta with beta = sigmoid(x_beta).  The gate is given as for
  * lin_attn_chunk_fwd (gate_mode).  Same arguments, layouts, workspace, rules
- * and errors otherwise; dtype LA_BF16 only (LA_FP32 returns
- * LA_EUNSUPPORTED).  The normalisation is folded into the per-tile operators
- * (1/|k_t| and 1/|q_t| scale rows and columns of the in-tile products and the
- * decay factors), so q and k are read as given and never rewritten.
+ * and errors otherwise; dtype LA_BF16 or LA_FP32.  For LA_BF16 the
+ * normalisation is folded into the per-tile operators (1/|k_t| and 1/|q_t|
+ * scale rows and columns of the in-tile products and the decay factors); for
+ * LA_FP32 the fused kernel scales the rows as it loads them.  Either way q
+ * and k are read as given and never rewritten.
  */
 int lin_attn_chunk_fwd_raw(const void* q, const void* k, const void* v,
                            const float* gate, int gate_mode, float G,
@@ -235,8 +236,7 @@ int lin_attn_chunk_fwd_varlen(const void* q, const void* k, const void* v,
  * lin_attn_chunk_fwd_varlen_raw -- lin_attn_chunk_fwd_varlen with the input
  * preparation of lin_attn_chunk_fwd_raw: q and k as given (L2-normalised per
  * token and head inside the pass), beta_logit holding x_beta.  Same arguments,
- * workspace, rules and errors otherwise, except that dtype is LA_BF16 only
- * (LA_FP32 returns LA_EUNSUPPORTED).
+ * workspace, rules and errors otherwise (both dtypes).
  */
 int lin_attn_chunk_fwd_varlen_raw(const void* q, const void* k, const void* v,
                                   const float* gate, int gate_mode, float G,

@@ -236,21 +236,14 @@ def test_varlen_workspace_size_and_empty():
     assert varlen(nseq=0, q=None, cu=None, ws=None)[0] == N.LA_OK
 
 
-def test_varlen_raw_is_bf16_only():
-    a = dict(q=fake(0), k=fake(1), v=fake(2), gate=fake(3), gate_mode=0, G=5.0, beta=fake(4),
-             h0=None, o=fake(5), hT=fake(6), cu=fake(7), nseq=3, T=64, H=2, Dk=64, Dv=64)
-    L = N.lib()
-    rc = L.lin_attn_chunk_fwd_varlen_raw(*a.values(), N.LA_FP32, None, 0, None)
-    assert rc == N.LA_EUNSUPPORTED
-    assert "LA_BF16 only" in L.lin_attn_last_error().decode()
-
-
 def test_raw_entry_checks():
     L = N.lib()
     base = [fake(0), fake(1), fake(2), fake(3), 0, 5.0, fake(4), None, fake(5), fake(6),
             1, 64, 2, 128, 128]
-    assert L.lin_attn_chunk_fwd_raw(*base, N.LA_FP32, fake(8), 1 << 30, None) == N.LA_EUNSUPPORTED
-    assert "LA_BF16 only" in L.lin_attn_last_error().decode()
+    bad = list(base)
+    bad[13] = 96                                         # Dk
+    assert L.lin_attn_chunk_fwd_raw(*bad, N.LA_FP32, None, 0, None) == N.LA_EUNSUPPORTED
+    assert "Dk" in L.lin_attn_last_error().decode()
     bad = list(base)
     bad[0] = None
     assert L.lin_attn_chunk_fwd_raw(*bad, N.LA_BF16, fake(8), 1 << 30, None) == N.LA_EINVAL

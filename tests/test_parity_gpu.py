@@ -365,6 +365,59 @@ def test_varlen_raw_inputs():
     check(name, "bf16", o, hT, ref_o, ref_h)
 
 
+RAW_FP32 = [
+    # B, H, T, Dk, Dv, regime, with h0
+    (2, 2, 301, 128, 128, "std", True),
+    (1, 3, 77, 64, 32, "weak", False),
+]
+
+
+@pytest.mark.parametrize("case", RAW_FP32, ids=lambda c: "-".join(map(str, c)))
+def test_raw_inputs_fp32(case):
+    """The fp32 path from raw inputs (scaled q, k with some zero vectors, beta
+    logits) against the oracle on the fp64-prepared inputs, batched."""
+    B, H, T, Dk, Dv, regime, with_h0 = case
+    name = f"raw inputs B{B} H{H} T{T} dk{Dk} dv{Dv} fp32 {regime}"
+    say(name)
+    dev, hst = make_case(B, T, H, Dk, Dv, "fp32", regime, "logit", 0.02 if with_h0 else None,
+                         seed=61)
+    gen = torch.Generator(device="cuda").manual_seed(62)
+    q = dev["q"] * (0.5 + 3.0 * torch.rand((B, T, H, 1), generator=gen, device="cuda"))
+    k = dev["k"] * (0.5 + 3.0 * torch.rand((B, T, H, 1), generator=gen, device="cuda"))
+    q[0, 5, 0] = 0
+    k[0, 7, H - 1] = 0
+    xb = torch.randn((B, T, H), generator=gen, device="cuda")
+    o, hT = lin_attn_chunk_fwd(q, k, dev["v"], dev["gate"], xb, dev["h0"], gate_mode="logit",
+                               raw=True)
+    torch.cuda.synchronize()
+    _, _, v_h, g_h, _, h0_h = hst
+    qn, kn, beta = orc.prepare_inputs(host(q), host(k), host(xb))
+    ref_o, ref_h = crec.recurrent_fwd(qn, kn, v_h, g_h, beta, h0_h)
+    check(name, "fp32", o, hT, ref_o, ref_h)
+
+
+def test_varlen_raw_inputs_fp32():
+    """Packed sequences on the fp32 path from raw inputs, against the oracle."""
+    lengths = [0, 3, 40, 333, 100]
+    H, D = 2, 64
+    T, nseq = sum(lengths), len(lengths)
+    name = f"varlen raw {nseq} seqs T{T} H{H} d{D} fp32 weak"
+    say(name)
+    dev, hst = make_case(1, T, H, D, D, "fp32", "weak", "logit", None, seed=63)
+    gen = torch.Generator(device="cuda").manual_seed(64)
+    q = dev["q"] * (0.5 + 3 * torch.rand((1, T, H, 1), generator=gen, device="cuda"))
+    k = dev["k"] * (0.5 + 3 * torch.rand((1, T, H, 1), generator=gen, device="cuda"))
+    xb = torch.randn((1, T, H), generator=gen, device="cuda")
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int32, device="cuda")
+    o, hT = lin_attn_chunk_fwd_varlen(q, k, dev["v"], dev["gate"], xb, cu, gate_mode="logit",
+                                      raw=True)
+    torch.cuda.synchronize()
+    _, _, v_h, g_h, _, _ = hst
+    qn, kn, beta = orc.prepare_inputs(host(q), host(k), host(xb))
+    ref_o, ref_h = crec.recurrent_fwd_varlen(qn, kn, v_h, g_h, beta, cu.cpu().numpy(), None)
+    check(name, "fp32", o, hT, ref_o, ref_h)
+
+
 def test_graph_capture_replays():
     """The forward (stretched: several launches) and decode steps captured in
     one graph replay to the eager results, replay after replay, with eager
