@@ -39,6 +39,10 @@ SIGNATURES = {
                                 _P, _P, _P, _P, _P, _P,
                                 _I, _I, _I, _I, _I, _I, _P, _LL, _P]),
     "lin_attn_chunk_bwd_workspace_size": (_LL, [_I, _I, _I, _I, _I, _I]),
+    "lin_attn_chunk_bwd_varlen": (_I, [_P, _P, _P, _P, _I, _F, _P, _P, _P, _P,
+                                       _P, _P, _P, _P, _P, _P, _P,
+                                       _I, _I, _I, _I, _I, _I, _P, _LL, _P]),
+    "lin_attn_chunk_bwd_varlen_workspace_size": (_LL, [_I, _I, _I, _I, _I, _I]),
     "lin_attn_decode_step": (_I, [_P, _P, _P, _P, _I, _F, _P, _P, _P,
                                   _I, _I, _I, _I, _I, _P]),
     "lin_attn_decode_step_channel": (_I, [_P, _P, _P, _P, _I, _F, _P, _P, _P,

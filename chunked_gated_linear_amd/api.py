@@ -227,6 +227,60 @@ def lin_attn_chunk_bwd(q, k, v, gate, beta, dout, h0=None, dhT=None, *, gate_mod
     return dq, dk, dv, dgate, dbeta, dh0
 
 
+def lin_attn_chunk_bwd_varlen_workspace_size(T, nseq, H, Dk, Dv, dtype=torch.bfloat16):
+    """Workspace bytes lin_attn_chunk_bwd_varlen needs for these sizes."""
+    n = N.lib().lin_attn_chunk_bwd_varlen_workspace_size(T, nseq, H, Dk, Dv, _DTYPES[dtype])
+    if n < 0:
+        raise N.LinAttnError(N.LA_EINVAL, N.lib().lin_attn_last_error().decode())
+    return n
+
+
+def lin_attn_chunk_bwd_varlen(q, k, v, gate, beta, dout, cu_seqlens, h0=None, dhT=None, *,
+                              gate_mode="log", G=5.0, output_dh0=True, workspace=None,
+                              stream=None):
+    """Gradients of <o, dout> + <hT, dhT> for lin_attn_chunk_fwd_varlen's
+    inputs: packed q, k [1,T,H,Dk], v, dout [1,T,H,Dv], gate, beta [1,T,H],
+    sequence s at tokens [cu[s], cu[s+1]) (cu_seqlens an int32 GPU tensor of
+    nseq + 1 offsets), h0, dhT [nseq,H,Dk,Dv].  Returns float32 (dq, dk, dv,
+    dgate, dbeta, dh0) as lin_attn_chunk_bwd does."""
+    _need(q, "q")
+    if q.dtype not in _DTYPES:
+        raise TypeError("q, k, v, dout must be bfloat16 or float32")
+    _, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    _need(k, "k", q.dtype, (1, T, H, Dk))
+    _need(v, "v", q.dtype, (1, T, H, Dv))
+    _need(dout, "dout", q.dtype, (1, T, H, Dv))
+    _need(gate, "gate", torch.float32, (1, T, H))
+    _need(beta, "beta", torch.float32, (1, T, H))
+    _need(cu_seqlens, "cu_seqlens", torch.int32)
+    nseq = cu_seqlens.numel() - 1
+    if cu_seqlens.dim() != 1 or nseq < 0:
+        raise ValueError("cu_seqlens must be a 1-D tensor of nseq + 1 offsets")
+    if h0 is not None:
+        _need(h0, "h0", torch.float32, (nseq, H, Dk, Dv))
+    if dhT is not None:
+        _need(dhT, "dhT", torch.float32, (nseq, H, Dk, Dv))
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq = torch.empty((1, T, H, Dk), **f32)
+    dk = torch.empty((1, T, H, Dk), **f32)
+    dv = torch.empty((1, T, H, Dv), **f32)
+    dgate = torch.empty((1, T, H), **f32)
+    dbeta = torch.empty((1, T, H), **f32)
+    dh0 = torch.empty((nseq, H, Dk, Dv), **f32) if output_dh0 else None
+    nws = lin_attn_chunk_bwd_varlen_workspace_size(T, nseq, H, Dk, Dv, q.dtype)
+    if workspace is None and nws > 0:
+        workspace = torch.empty(nws, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8)
+    N.check(N.lib().lin_attn_chunk_bwd_varlen(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _GATE[gate_mode], float(G), _ptr(beta),
+        _ptr(h0), _ptr(dout), _ptr(dhT), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dgate),
+        _ptr(dbeta), _ptr(dh0), _ptr(cu_seqlens), nseq, T, H, Dk, Dv, _DTYPES[q.dtype],
+        _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(q, stream)))
+    return dq, dk, dv, dgate, dbeta, dh0
+
+
 def lin_attn_chunk_fwd_varlen_workspace_size(T, nseq, H, Dk, Dv, dtype=torch.bfloat16):
     """Workspace bytes lin_attn_chunk_fwd_varlen needs for these sizes."""
     n = N.lib().lin_attn_chunk_fwd_varlen_workspace_size(T, nseq, H, Dk, Dv, _DTYPES[dtype])
@@ -242,8 +296,8 @@ def lin_attn_chunk_fwd_varlen(q, k, v, gate, beta, cu_seqlens, h0=None, *, gate_
     nseq sequences back to back, sequence s at tokens [cu[s], cu[s+1]) with
     cu_seqlens an int32 GPU tensor of nseq + 1 offsets.  Returns o [1,T,H,Dv]
     and the final states hT [nseq,H,Dk,Dv] (None if not requested).  raw=True:
-    q, k as they come and `beta` holding logits, as in lin_attn_chunk_fwd
-    (bf16 only).  bf16 or float32 q, k, v; float32 needs no workspace."""
+    q, k as they come and `beta` holding logits, as in lin_attn_chunk_fwd.
+    bf16 or float32 q, k, v; float32 needs no workspace."""
     _need(q, "q")
     _, T, H, Dk = q.shape
     Dv = v.shape[-1]

@@ -83,7 +83,60 @@ struct BwdArgs {
   int gate_logit;
   float G;
   int B, T, H, Dv, NT;
+  const int* cu;   // packed sequences: nseq + 1 device offsets (B = nseq), or NULL
+  int nslot;       // packed sequences: tile slots per head
 };
+
+// One sequence of the call: T tokens from token tok0 of the token axis, NC
+// tiles whose records, states and state gradients sit at tile indices rbase,
+// rbase + 1, ...  Batched: sequence b of a.T tokens.  Packed (a.cu): tokens
+// [cu[b], cu[b+1]) of one sequence of a.T tokens (offsets clamped to [0, a.T]
+// and made non-decreasing); its tile c takes slot floor(cu[b] / 16) + b + c of
+// the a.nslot = a.T / 16 + nseq + 1 per head (slots of different sequences do
+// not overlap for non-decreasing offsets).
+struct BSeq {
+  int T, NC;
+  int64_t tok0, rbase;
+};
+__device__ inline int bwd_begin(const BwdArgs& a, int s) { return min(max(a.cu[s], 0), a.T); }
+__device__ inline BSeq bwd_seq(const BwdArgs& a, int b, int h) {
+  BSeq q;
+  if (a.cu) {
+    const int tb = bwd_begin(a, b);
+    q.T = min(max(a.cu[b + 1], tb), a.T) - tb;
+    q.tok0 = tb;
+    q.rbase = (int64_t)h * a.nslot + tb / 16 + b;
+  } else {
+    q.T = a.T;
+    q.tok0 = (int64_t)b * a.T;
+    q.rbase = ((int64_t)b * a.H + h) * a.NT;
+  }
+  q.NC = (q.T + 15) / 16;
+  return q;
+}
+// A tile index of a grid over all tiles -> (sequence b, head h, tile c);
+// false for a slot of a packed call that no tile uses.
+__device__ inline bool bwd_tile(const BwdArgs& a, int64_t tile, int& b, int& h, int& c) {
+  if (!a.cu) {
+    c = (int)(tile % a.NT);
+    const int64_t bh = tile / a.NT;
+    h = (int)(bh % a.H);
+    b = (int)(bh / a.H);
+    return true;
+  }
+  h = (int)(tile / a.nslot);
+  const int slot = (int)(tile - (int64_t)h * a.nslot);
+  int lo = 0, hi = a.B - 1;                  // the last s with slot(s, 0) <= slot
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (bwd_begin(a, mid) / 16 + mid <= slot) lo = mid;
+    else hi = mid - 1;
+  }
+  b = lo;
+  const BSeq q = bwd_seq(a, b, h);
+  c = (int)(tile - q.rbase);
+  return c >= 0 && c < q.NC;
+}
 
 // Eight consecutive elements as fp32 (16-byte aligned source).
 template <typename E> struct Ld8;
@@ -112,15 +165,15 @@ template <typename E> __device__ inline float ld1(const E* p) { return (float)*p
 // Rows of one tile of a [B, T, H, D] tensor into LDS (fp32, row pitch P),
 // zeros past the end of the sequence.
 template <typename E, int D, int P = D + 1>
-__device__ inline void load_tile(float (*dst)[P], const E* src, int b, int c, int h,
+__device__ inline void load_tile(float (*dst)[P], const E* src, const BSeq& sq, int c, int h,
                                  const BwdArgs& a) {
   constexpr int PER_ROW = D / 8;
   for (int x = threadIdx.x; x < kT * PER_ROW; x += kBwdThreads) {
     const int t = x / PER_ROW, c8 = (x % PER_ROW) * 8;
     const int tok = c * kT + t;
     float f[8];
-    if (tok < a.T) {
-      Ld8<E>::run(src + (((int64_t)b * a.T + tok) * a.H + h) * D + c8, f);
+    if (tok < sq.T) {
+      Ld8<E>::run(src + ((sq.tok0 + tok) * a.H + h) * D + c8, f);
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i) f[i] = 0.f;
@@ -143,16 +196,16 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(BwdArgs a) {
   __shared__ float sA[kT][kT + 1], sTi[kT][kT + 1];
   const int tid = threadIdx.x;
   const int64_t tile = blockIdx.x;
-  const int c = (int)(tile % a.NT);
-  const int64_t bh = tile / a.NT;
-  const int h = (int)(bh % a.H), b = (int)(bh / a.H);
-  load_tile<E, DK>(sK, static_cast<const E*>(a.k), b, c, h, a);
-  load_tile<E, DK>(sQ, static_cast<const E*>(a.q), b, c, h, a);
+  int b, h, c;
+  if (!bwd_tile(a, tile, b, h, c)) return;   // an unused slot: the whole block
+  const BSeq sq = bwd_seq(a, b, h);
+  load_tile<E, DK>(sK, static_cast<const E*>(a.k), sq, c, h, a);
+  load_tile<E, DK>(sQ, static_cast<const E*>(a.q), sq, c, h, a);
   if (tid < kT) {
     const int tok = c * kT + tid;
-    const int64_t idx = ((int64_t)b * a.T + tok) * a.H + h;
-    sG[tid] = tok < a.T ? gate_at(a, idx) : 0.f;
-    sB[tid] = tok < a.T ? a.beta[idx] : 0.f;
+    const int64_t idx = (sq.tok0 + tok) * a.H + h;
+    sG[tid] = tok < sq.T ? gate_at(a, idx) : 0.f;
+    sB[tid] = tok < sq.T ? a.beta[idx] : 0.f;
   }
   __syncthreads();
   if (tid == 0) {
@@ -269,7 +322,8 @@ __global__ __launch_bounds__(64 * (NP + 1)) void bwd_hstates_mfma_kernel(BwdArgs
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, grp = lane >> 4;
-  const int NC = a.NT;
+  const BSeq sq = bwd_seq(a, b, h);
+  const int NC = sq.NC;
   const int NE = (NC + NP - 1) / NP;
   auto rec_of = [&](int c) -> char* { return smem + (((c / NP) & 1) * NP + c % NP) * R::BYTES; };
 
@@ -288,7 +342,7 @@ __global__ __launch_bounds__(64 * (NP + 1)) void bwd_hstates_mfma_kernel(BwdArgs
         if (c >= NC) break;
         const char* rec = rec_of(c);
         // the state at the tile start, in fragment order (see BRec)
-        f32x4* hsp = reinterpret_cast<f32x4*>(a.hs + (bh * NC + c) * (int64_t)DK * a.Dv +
+        f32x4* hsp = reinterpret_cast<f32x4*>(a.hs + (sq.rbase + c) * (int64_t)DK * a.Dv +
                                               (int64_t)(v0 / 16) * DK * 16);
 #pragma unroll
         for (int t = 0; t < NT; ++t) hsp[t * 64 + lane] = Hacc[t];
@@ -328,10 +382,11 @@ __global__ __launch_bounds__(64 * (NP + 1)) void bwd_hstates_mfma_kernel(BwdArgs
   const int p = wave - 1;
   const E* kp = static_cast<const E*>(a.k);
   const E* vp = static_cast<const E*>(a.v);
-  auto rowk = [&](int t) -> int64_t { return ((int64_t)b * a.T + t) * a.H + h; };
+  auto rowk = [&](int t) -> int64_t { return (sq.tok0 + t) * a.H + h; };
   auto load = [&](HsRaw<E, DK>& r, int c) {
+    if (NC == 0) return;          // an empty sequence loads nothing
     c = min(c, NC - 1);
-    const int t = min(c * kT + n, a.T - 1);
+    const int t = min(c * kT + n, sq.T - 1);
     const int64_t base = rowk(t) * DK;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
@@ -345,18 +400,18 @@ __global__ __launch_bounds__(64 * (NP + 1)) void bwd_hstates_mfma_kernel(BwdArgs
         r.kf[s].hi = *reinterpret_cast<const f32x4*>(kp + base + c1);
       }
     }
-    const float* rec = a.rec + (bh * NC + c) * BRec::FLOATS;
+    const float* rec = a.rec + (sq.rbase + c) * BRec::FLOATS;
     r.ti = reinterpret_cast<const f32x4*>(rec + BRec::TINV)[lane];
     r.g = rec[BRec::G + n];
     r.bt = rec[BRec::BETA + n];
     r.gC = rec[BRec::G + kT - 1];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r.vv[i] = vp[rowk(min(c * kT + 4 * grp + i, a.T - 1)) * a.Dv + v0 + n];
+    for (int i = 0; i < 4; ++i) r.vv[i] = vp[rowk(min(c * kT + 4 * grp + i, sq.T - 1)) * a.Dv + v0 + n];
   };
   auto store = [&](const HsRaw<E, DK>& r, int c) {
     if (c >= NC) return;
     char* rec = rec_of(c);
-    const bool ok = c * kT + n < a.T;        // token row n of this tile exists
+    const bool ok = c * kT + n < sq.T;        // token row n of this tile exists
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       F32 k32 = frag_f32(r.kf[s]);
@@ -378,7 +433,7 @@ __global__ __launch_bounds__(64 * (NP + 1)) void bwd_hstates_mfma_kernel(BwdArgs
     reinterpret_cast<f32x4*>(rec + R::TI)[lane] = r.ti;
     f32x4 vf;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) vf[i] = (c * kT + 4 * grp + i < a.T) ? Elt<E>::to_f(r.vv[i]) : 0.f;
+    for (int i = 0; i < 4; ++i) vf[i] = (c * kT + 4 * grp + i < sq.T) ? Elt<E>::to_f(r.vv[i]) : 0.f;
     reinterpret_cast<f32x4*>(rec + R::VF)[lane] = vf;
     if (grp == 0) {
       reinterpret_cast<float*>(rec + R::GM)[n] = __expf(r.g);
@@ -457,7 +512,8 @@ __global__ __launch_bounds__(64 * (NP + SPW)) void bwd_dh_mfma_kernel(BwdArgs a)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, grp = lane >> 4;
-  const int NC = a.NT;
+  const BSeq sq = bwd_seq(a, b, h);
+  const int NC = sq.NC;
   const int NE = (NC + NP - 1) / NP;
   // records by processing index m (tile NC - 1 - m)
   auto rec_of = [&](int m) -> char* { return smem + (((m / NP) & 1) * NP + m % NP) * R::BYTES; };
@@ -478,7 +534,7 @@ __global__ __launch_bounds__(64 * (NP + SPW)) void bwd_dh_mfma_kernel(BwdArgs a)
         if (m >= NC) break;
         const int c = NC - 1 - m;
         const char* rec = rec_of(m);
-        f32x4* dsp = reinterpret_cast<f32x4*>(a.dhs + (bh * NC + c) * (int64_t)DK * a.Dv +
+        f32x4* dsp = reinterpret_cast<f32x4*>(a.dhs + (sq.rbase + c) * (int64_t)DK * a.Dv +
                                               (int64_t)(v0 / 16) * DK * 16);
 #pragma unroll
         for (int t = 0; t < NT; ++t) dsp[t * 64 + lane] = D[t];
@@ -535,10 +591,11 @@ __global__ __launch_bounds__(64 * (NP + SPW)) void bwd_dh_mfma_kernel(BwdArgs a)
   const E* qp = static_cast<const E*>(a.q);
   const E* dp = static_cast<const E*>(a.dout);
   const int v0 = 16 * SPW * sl;
-  auto rowk = [&](int t) -> int64_t { return ((int64_t)b * a.T + t) * a.H + h; };
+  auto rowk = [&](int t) -> int64_t { return (sq.tok0 + t) * a.H + h; };
   auto load = [&](HdRaw<E, DK, SPW>& r, int m) {
+    if (NC == 0) return;          // an empty sequence loads nothing
     const int c = NC - 1 - min(m, NC - 1);
-    const int t = min(c * kT + n, a.T - 1);
+    const int t = min(c * kT + n, sq.T - 1);
     const int64_t base = rowk(t) * DK;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
@@ -557,7 +614,7 @@ __global__ __launch_bounds__(64 * (NP + SPW)) void bwd_dh_mfma_kernel(BwdArgs a)
         r.qf[s].hi = *reinterpret_cast<const f32x4*>(qp + base + c1);
       }
     }
-    const float* rec = a.rec + (bh * NC + c) * BRec::FLOATS;
+    const float* rec = a.rec + (sq.rbase + c) * BRec::FLOATS;
     r.pm = reinterpret_cast<const f32x4*>(rec + BRec::P)[lane];
     r.tm = reinterpret_cast<const f32x4*>(rec + BRec::TINV)[lane];
     r.g = rec[BRec::G + n];
@@ -567,14 +624,14 @@ __global__ __launch_bounds__(64 * (NP + SPW)) void bwd_dh_mfma_kernel(BwdArgs a)
     for (int w = 0; w < SPW; ++w) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        r.dd[w][i] = dp[rowk(min(c * kT + 4 * grp + i, a.T - 1)) * a.Dv + v0 + 16 * w + n];
+        r.dd[w][i] = dp[rowk(min(c * kT + 4 * grp + i, sq.T - 1)) * a.Dv + v0 + 16 * w + n];
     }
   };
   auto store = [&](const HdRaw<E, DK, SPW>& r, int m) {
     if (m >= NC) return;
     const int c = NC - 1 - m;
     char* rec = rec_of(m);
-    const bool ok = c * kT + n < a.T;        // token row n of this tile exists
+    const bool ok = c * kT + n < sq.T;        // token row n of this tile exists
     float* kt = reinterpret_cast<float*>(rec + R::KT);
     float* qt = reinterpret_cast<float*>(rec + R::QT);
 #pragma unroll
@@ -612,7 +669,7 @@ __global__ __launch_bounds__(64 * (NP + SPW)) void bwd_dh_mfma_kernel(BwdArgs a)
       f32x4 dd;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        dd[i] = (c * kT + 4 * grp + i < a.T) ? Elt<E>::to_f(r.dd[w][i]) : 0.f;
+        dd[i] = (c * kT + 4 * grp + i < sq.T) ? Elt<E>::to_f(r.dd[w][i]) : 0.f;
       reinterpret_cast<f32x4*>(rec + R::DO)[w * 64 + lane] = dd;
     }
     if (grp == 0) {
@@ -684,9 +741,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_grad_kernel(BwdArgs a) {
   __shared__ float sHdH[4];
   const int tid = threadIdx.x;
   const int64_t tile = blockIdx.x;
-  const int c = (int)(tile % a.NT);
-  const int64_t bh = tile / a.NT;
-  const int h = (int)(bh % a.H), b = (int)(bh / a.H);
+  int b, h, c;
+  if (!bwd_tile(a, tile, b, h, c)) return;   // an unused slot: the whole block
+  const BSeq sq = bwd_seq(a, b, h);
   const int t = tid >> 4, j = tid & 15;        // (token, column) / (token, token) view
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, n = tid & 15, grp = (tid >> 4) & 3;
@@ -708,9 +765,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int tk = c * kT + 4 * grp + i;
-      const int64_t ro = (((int64_t)b * a.T + tk) * a.H + h) * a.Dv + 16 * jb + n;
-      vv[i] = tk < a.T ? ld1(vp + ro) : 0.f;
-      dd[i] = tk < a.T ? ld1(dop + ro) : 0.f;
+      const int64_t ro = ((sq.tok0 + tk) * a.H + h) * a.Dv + 16 * jb + n;
+      vv[i] = tk < sq.T ? ld1(vp + ro) : 0.f;
+      dd[i] = tk < sq.T ? ld1(dop + ro) : 0.f;
     }
   };
   if (w < NV) {
@@ -718,8 +775,8 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_grad_kernel(BwdArgs a) {
     for (int r = 0; r < NT; ++r) fetch_hd(w, r);
     fetch_vd(w);
   }
-  load_tile<E, DK, KP>(sK, static_cast<const E*>(a.k), b, c, h, a);
-  load_tile<E, DK, KP>(sQ, static_cast<const E*>(a.q), b, c, h, a);
+  load_tile<E, DK, KP>(sK, static_cast<const E*>(a.k), sq, c, h, a);
+  load_tile<E, DK, KP>(sQ, static_cast<const E*>(a.q), sq, c, h, a);
   sTi[t][j] = rec[BRec::TINV + tid];
   sP[t][j] = rec[BRec::P + tid];
   const float ekk = rec[BRec::EKK + tid];
@@ -728,7 +785,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_grad_kernel(BwdArgs a) {
   __syncthreads();
 
   const int tkn = c * kT + n;                          // token of row fragments
-  const int64_t ron = ((int64_t)b * a.T + tkn) * a.H + h;
+  const int64_t ron = (sq.tok0 + tkn) * a.H + h;
   float (*tr)[TP] = reinterpret_cast<float (*)[TP]>(sU8 + w * 4 * kT * TP * 4);
   // X in accumulator order -> row fragment (lane (n, grp) register jj =
   // X[n][4 grp + jj]) through 16 x 16 tiles, up to four per LDS round trip
@@ -821,7 +878,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_grad_kernel(BwdArgs a) {
     transpose_n(acc3, row3);
     const f32x4 Ur = row3[0], DOr = row3[1], DYr = row3[2];
     // dv = diag(beta) dY, a row fragment: token n, columns 16 jb + 4 grp + 0..3
-    if (tkn < a.T)
+    if (tkn < sq.T)
       *reinterpret_cast<f32x4*>(a.dv + ron * a.Dv + 16 * jb + 4 * grp) = btn * DYr;
     dPp = X::mma16(F16{DOr}, F16{Ur}, dPp);
     dAp = X::mma16(F16{DYr}, F16{Ur}, dAp);
@@ -933,7 +990,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_grad_kernel(BwdArgs a) {
     for (int r = 0; r < RT; ++r) {
       const f32x4 q4 = transpose(tq, dQa[r]);
       const f32x4 k4 = transpose(tq, dKa[r]);
-      if (tkn < a.T) {
+      if (tkn < sq.T) {
         *reinterpret_cast<f32x4*>(a.dq + ron * DK + 16 * (RT * w + r) + 4 * grp) = q4;
         *reinterpret_cast<f32x4*>(a.dk + ron * DK + 16 * (RT * w + r) + 4 * grp) = k4;
       }
@@ -956,9 +1013,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_grad_kernel(BwdArgs a) {
     }
     x = sum16(x);
     const int tk = c * kT + u;
-    if (i == 0 && tk < a.T) {
+    if (i == 0 && tk < sq.T) {
       const float dg = gamC * (sHdH[0] + sHdH[1] + sHdH[2] + sHdH[3]) + x;
-      const int64_t idx = ((int64_t)b * a.T + tk) * a.H + h;
+      const int64_t idx = (sq.tok0 + tk) * a.H + h;
       float out = dg;
       if (a.gate_logit) {
         const float s = sigmoid_f(a.gate[idx]);
@@ -972,7 +1029,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_grad_kernel(BwdArgs a) {
 
 template <typename E, int DK>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
-  const int64_t tiles = (int64_t)a.B * a.H * a.NT;
+  // batched: every tile of every sequence; packed: every slot (unused ones
+  // return at once)
+  const int64_t tiles = a.cu ? (int64_t)a.H * a.nslot : (int64_t)a.B * a.H * a.NT;
   const int64_t slices = (int64_t)a.B * a.H * (a.Dv / 16);
   hipLaunchKernelGGL((bwd_prep_kernel<E, DK>), dim3((unsigned)tiles), dim3(kBwdThreads), 0, st, a);
   hipError_t e = hipGetLastError();
@@ -1007,8 +1066,24 @@ hipError_t launch_chunk_bwd(const void* q, const void* k, const void* v, const v
                             const float* h0, const float* dhT, float* dq, float* dk, float* dv,
                             float* dgate, float* dbeta, float* dh0, int B, int T, int H, int Dk,
                             int Dv, int fp32, void* ws, hipStream_t st) {
+  return launch_chunk_bwd_varlen(q, k, v, dout, gate, gate_logit, G, beta, h0, dhT, dq, dk, dv,
+                                 dgate, dbeta, dh0, nullptr, B, T, H, Dk, Dv, fp32, ws, st);
+}
+
+long long chunk_bwd_varlen_workspace_bytes(int T, int nseq, int H, int Dk, int Dv) {
+  const long long tiles = (long long)H * (T / kT + nseq + 1);
+  return tiles * (BRec::FLOATS * 4LL + 2LL * Dk * Dv * 4LL);
+}
+
+hipError_t launch_chunk_bwd_varlen(const void* q, const void* k, const void* v, const void* dout,
+                                   const float* gate, int gate_logit, float G, const float* beta,
+                                   const float* h0, const float* dhT, float* dq, float* dk,
+                                   float* dv, float* dgate, float* dbeta, float* dh0,
+                                   const int* cu, int B, int T, int H, int Dk, int Dv, int fp32,
+                                   void* ws, hipStream_t st) {
   const int NT = (T + kT - 1) / kT;
-  const int64_t tiles = (int64_t)B * H * NT;
+  const int nslot = cu ? T / kT + B + 1 : 0;
+  const int64_t tiles = cu ? (int64_t)H * nslot : (int64_t)B * H * NT;
   char* w = static_cast<char*>(ws);
   BwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.dout = dout;
@@ -1019,6 +1094,7 @@ hipError_t launch_chunk_bwd(const void* q, const void* k, const void* v, const v
   a.dhs = a.hs + tiles * (int64_t)Dk * Dv;
   a.gate_logit = gate_logit; a.G = G;
   a.B = B; a.T = T; a.H = H; a.Dv = Dv; a.NT = NT;
+  a.cu = cu; a.nslot = nslot;
   if (fp32) return Dk == 128 ? launch_bwd_t<float, 128>(a, st) : launch_bwd_t<float, 64>(a, st);
   return Dk == 128 ? launch_bwd_t<__bf16, 128>(a, st) : launch_bwd_t<__bf16, 64>(a, st);
 }

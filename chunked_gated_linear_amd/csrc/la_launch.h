@@ -59,6 +59,20 @@ hipError_t launch_chunk_bwd(const void* q, const void* k, const void* v, const v
 // the fp32 state at the tile start and the fp32 gradient of its end state.
 long long chunk_bwd_workspace_bytes(int B, int T, int H, int Dk, int Dv);
 
+// The reverse pass over packed sequences: sequence s is tokens
+// [cu[s], cu[s+1]) of one packed sequence of T tokens (cu: device array of
+// B + 1 offsets); its tiles take per-head slots floor(cu[s] / 16) + s + c.
+hipError_t launch_chunk_bwd_varlen(const void* q, const void* k, const void* v, const void* dout,
+                                   const float* gate, int gate_logit, float G, const float* beta,
+                                   const float* h0, const float* dhT, float* dq, float* dk,
+                                   float* dv, float* dgate, float* dbeta, float* dh0,
+                                   const int* cu, int B, int T, int H, int Dk, int Dv, int fp32,
+                                   void* ws, hipStream_t st);
+
+// Workspace bytes of the packed reverse pass: H * (T / 16 + nseq + 1) tiles,
+// each as in chunk_bwd_workspace_bytes.
+long long chunk_bwd_varlen_workspace_bytes(int T, int nseq, int H, int Dk, int Dv);
+
 // Per-channel gate (gate [B, T, H, Dk]); q, k, v, o bf16 or fp32 as `fp32`
 // says: a parallel tile-preparation kernel into the workspace, then the
 // serial kernel (fp32 MFMA throughout for fp32 inputs; bf16 MFMA for the

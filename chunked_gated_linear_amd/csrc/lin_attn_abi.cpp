@@ -536,6 +536,78 @@ int lin_attn_chunk_bwd(const void* q, const void* k, const void* v, const float*
   return hip_status(e, "chunk_bwd launch");
 }
 
+long long lin_attn_chunk_bwd_varlen_workspace_size(int T, int nseq, int H, int Dk, int Dv,
+                                                   int dtype) {
+  if (check_varlen_sizes(T, nseq, H, Dk, Dv, dtype)) return -1;
+  if ((int64_t)H * (T / 16 + nseq + 1) > INT32_MAX) {
+    fail(LA_EINVAL, "problem too large (H*(T/16+nseq+1) exceeds 2^31)");
+    return -1;
+  }
+  ok();
+  return la::chunk_bwd_varlen_workspace_bytes(T, nseq, H, Dk, Dv);
+}
+
+int lin_attn_chunk_bwd_varlen(const void* q, const void* k, const void* v, const float* gate,
+                              int gate_mode, float G, const float* beta, const float* h0,
+                              const void* dout, const float* dhT, float* dq, float* dk,
+                              float* dv, float* dgate, float* dbeta, float* dh0,
+                              const int* cu_seqlens, int nseq, int T, int H, int Dk, int Dv,
+                              int dtype, void* workspace, long long workspace_bytes,
+                              void* stream) {
+  if (int rc = check_varlen_sizes(T, nseq, H, Dk, Dv, dtype)) return rc;
+  if (int rc = check_gate_scalars(gate_mode, G)) return rc;
+  if ((int64_t)H * (T / 16 + nseq + 1) > INT32_MAX)
+    return fail(LA_EINVAL, "problem too large (H*(T/16+nseq+1) exceeds 2^31)");
+  if (nseq == 0 || H == 0) return ok();
+  if (!cu_seqlens) return fail(LA_EINVAL, "cu_seqlens must not be NULL");
+  if (!aligned(cu_seqlens, 4u)) return fail(LA_EINVAL, "cu_seqlens must be 4-byte aligned");
+  const int64_t es = dtype == LA_BF16 ? 2 : 4;
+  const int64_t ntok = (int64_t)T * H;
+  const int64_t nst = (int64_t)nseq * H * Dk * Dv;
+  const long long wsz = la::chunk_bwd_varlen_workspace_bytes(T, nseq, H, Dk, Dv);
+  if (T > 0) {
+    // q, k are read and dq, dk, dv written in 16-byte vectors of a row;
+    // everything else element-wise
+    const struct { const char* nm; const void* p; unsigned a; } req[] = {
+        {"q", q, 16u}, {"k", k, 16u}, {"v", v, (unsigned)es}, {"gate", gate, 4u},
+        {"beta", beta, 4u}, {"dout", dout, (unsigned)es}, {"dq", dq, 16u}, {"dk", dk, 16u},
+        {"dv", dv, 16u}, {"dgate", dgate, 4u}, {"dbeta", dbeta, 4u}};
+    for (const auto& r : req) {
+      if (!r.p) return fail(LA_EINVAL, "%s must not be NULL", r.nm);
+      if (!aligned(r.p, r.a)) return fail(LA_EINVAL, "%s must be %u-byte aligned", r.nm, r.a);
+    }
+  }
+  for (const auto& r : {std::make_pair("h0", (const void*)h0), std::make_pair("dhT", (const void*)dhT),
+                        std::make_pair("dh0", (const void*)dh0)})
+    if (r.second && !aligned(r.second, 4u)) return fail(LA_EINVAL, "%s must be 4-byte aligned", r.first);
+  if (!workspace) return fail(LA_EINVAL, "workspace must not be NULL (%lld bytes needed)", wsz);
+  if (!aligned(workspace, 256u)) return fail(LA_EINVAL, "workspace must be 256-byte aligned");
+  if (workspace_bytes < wsz)
+    return fail(LA_EINVAL, "workspace too small: %lld bytes given, %lld needed", workspace_bytes,
+                wsz);
+  const Span ins[] = {span("q", q, ntok * Dk * es),      span("k", k, ntok * Dk * es),
+                      span("v", v, ntok * Dv * es),      span("gate", gate, ntok * 4),
+                      span("beta", beta, ntok * 4),      span("h0", h0, nst * 4),
+                      span("dout", dout, ntok * Dv * es), span("dhT", dhT, nst * 4),
+                      span("cu_seqlens", cu_seqlens, ((int64_t)nseq + 1) * 4)};
+  const Span outs[] = {span("dq", dq, ntok * Dk * 4),    span("dk", dk, ntok * Dk * 4),
+                       span("dv", dv, ntok * Dv * 4),    span("dgate", dgate, ntok * 4),
+                       span("dbeta", dbeta, ntok * 4),   span("dh0", dh0, nst * 4),
+                       span("workspace", workspace, wsz)};
+  for (size_t i = 0; i < sizeof outs / sizeof outs[0]; ++i) {
+    for (const Span& in : ins)
+      if (overlap(outs[i], in)) return fail(LA_EINVAL, "%s overlaps %s", outs[i].name, in.name);
+    for (size_t j = 0; j < i; ++j)
+      if (overlap(outs[i], outs[j]))
+        return fail(LA_EINVAL, "%s overlaps %s", outs[i].name, outs[j].name);
+  }
+  hipError_t e = la::launch_chunk_bwd_varlen(
+      q, k, v, dout, gate, gate_mode == LA_GATE_BOUNDED_LOGIT, G, beta, h0, dhT, dq, dk, dv, dgate,
+      dbeta, dh0, cu_seqlens, nseq, T, H, Dk, Dv, dtype == LA_FP32, workspace,
+      reinterpret_cast<hipStream_t>(stream));
+  return hip_status(e, "chunk_bwd_varlen launch");
+}
+
 int lin_attn_gate(const float* x, float G, float* g, long long n, void* stream) {
   if (n < 0) return fail(LA_EINVAL, "n must be >= 0, got %lld", n);
   if (!std::isfinite(G) || G < 0.f || G > 16.f)

@@ -354,6 +354,47 @@ int lin_attn_chunk_bwd(const void* q, const void* k, const void* v,
                        void* workspace, long long workspace_bytes, void* stream);
 
 /*
+ * lin_attn_chunk_bwd_varlen_workspace_size -- bytes of device workspace that
+ * lin_attn_chunk_bwd_varlen needs: H * (T / 16 + nseq + 1) tile slots (one per
+ * 16 tokens of each packed sequence plus one spare per sequence for its
+ * ragged end), each holding what lin_attn_chunk_bwd keeps per tile (3200 +
+ * 8 * Dk * Dv bytes); -1 (with lin_attn_last_error() set) for invalid sizes.
+ */
+long long lin_attn_chunk_bwd_varlen_workspace_size(int T, int nseq, int H, int Dk, int Dv,
+                                                   int dtype);
+
+/*
+ * lin_attn_chunk_bwd_varlen -- the reverse pass of lin_attn_chunk_fwd_varlen
+ * (training on packed sequences): sequence s is tokens [cu_seqlens[s],
+ * cu_seqlens[s + 1]) of one packed sequence of T tokens, with its own h0[s]
+ * and dhT[s]; gradients never cross from one sequence to another.  Each
+ * sequence gets exactly the gradients lin_attn_chunk_bwd gives a sequence of
+ * its length.
+ *
+ *   q, k, dq, dk            [T, H, Dk]   (q, k dtype; dq, dk float32)
+ *   v, dout, dv             [T, H, Dv]   (v, dout dtype; dv float32)
+ *   gate, beta, dgate, dbeta [T, H]      float32
+ *   h0, dhT, dh0            [nseq, H, Dk, Dv] float32, or NULL as in
+ *                           lin_attn_chunk_bwd
+ *   cu_seqlens  DEVICE array of nseq + 1 int32 offsets, as in
+ *               lin_attn_chunk_fwd_varlen (read on the device only, clamped
+ *               to [0, T]; empty sequences allowed: their dh0 is dhT).
+ *   workspace   lin_attn_chunk_bwd_varlen_workspace_size(...) bytes,
+ *               256-byte aligned, caller-owned, clobbered.
+ * dtype LA_BF16 or LA_FP32; sizes, alignment, aliasing rules and errors as
+ * lin_attn_chunk_bwd.  Deterministic.
+ */
+int lin_attn_chunk_bwd_varlen(const void* q, const void* k, const void* v,
+                              const float* gate, int gate_mode, float G,
+                              const float* beta, const float* h0,
+                              const void* dout, const float* dhT,
+                              float* dq, float* dk, float* dv,
+                              float* dgate, float* dbeta, float* dh0,
+                              const int* cu_seqlens, int nseq,
+                              int T, int H, int Dk, int Dv, int dtype,
+                              void* workspace, long long workspace_bytes, void* stream);
+
+/*
  * lin_attn_gate -- the bounded log-decay on its own: g[i] = -G * sigmoid(x[i])
  * for i < n ("Deep Dive ...", sec. 3.3; "Core Technologies ...", sec. 2.2).
  * x and g are float32 device arrays of n elements (g may equal x for an

@@ -417,3 +417,42 @@ def test_channel_varlen_workspace_size_and_empty():
     assert L.lin_attn_chunk_fwd_channel_varlen_workspace_size(100, 3, 2, 64, 32, 1) == \
         2 * (100 // 16 + 3 + 1) * 14592
     assert channel_varlen(nseq=0)[0] == N.LA_OK
+
+
+def bwd_varlen(**kw):
+    a = dict(q=fake(0), k=fake(1), v=fake(2), gate=fake(3), gate_mode=0, G=5.0, beta=fake(4),
+             h0=None, dout=fake(5), dhT=None, dq=fake(6), dk=fake(7), dv=fake(8),
+             dgate=fake(9), dbeta=fake(10), dh0=None, cu=fake(11), nseq=3, T=64, H=2, Dk=128,
+             Dv=128, dtype=N.LA_BF16, ws=fake(12), ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    L = N.lib()
+    rc = L.lin_attn_chunk_bwd_varlen(*a.values())
+    return rc, L.lin_attn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(cu=None), N.LA_EINVAL, "cu_seqlens must not be NULL"),
+    (dict(cu=fake(11) + 2), N.LA_EINVAL, "cu_seqlens must be 4-byte aligned"),
+    (dict(nseq=-1), N.LA_EINVAL, "nseq"),
+    (dict(Dk=96), N.LA_EUNSUPPORTED, "Dk"),
+    (dict(dq=fake(6) + 4), N.LA_EINVAL, "dq must be 16-byte aligned"),
+    (dict(ws=None), N.LA_EINVAL, "workspace must not be NULL"),
+    (dict(ws_bytes=10), N.LA_EINVAL, "workspace too small"),
+    (dict(dq=fake(0) + 64), N.LA_EINVAL, "dq overlaps q"),
+    (dict(dh0=fake(11)), N.LA_EINVAL, "dh0 overlaps cu_seqlens"),
+    (dict(gate_mode=7), N.LA_EINVAL, "gate_mode"),
+])
+def test_bwd_varlen_rejects(kw, code, needle):
+    rc, msg = bwd_varlen(**kw)
+    assert rc == code, (rc, msg)
+    assert needle in msg
+
+
+def test_bwd_varlen_workspace_size_and_empty():
+    ws = N.lib().lin_attn_chunk_bwd_varlen_workspace_size
+    per_tile = 3200 + 8 * 128 * 128
+    assert ws(64, 3, 2, 128, 128, N.LA_BF16) == 2 * (64 // 16 + 3 + 1) * per_tile
+    assert ws(64, 3, 2, 128, 128, N.LA_FP32) == 2 * (64 // 16 + 3 + 1) * per_tile
+    assert ws(64, -1, 2, 128, 128, N.LA_BF16) == -1
+    # no sequences: nothing to do, nothing touched
+    assert bwd_varlen(nseq=0, q=None, cu=None, ws=None)[0] == N.LA_OK
