@@ -28,8 +28,11 @@
 // at G = 5) instead of reaching exp(80), so no product comes near the float
 // overflow or the subnormal range.
 //
-// Arithmetic is fp32 throughout (inputs in bf16 convert exactly); the matrix
-// products run on the fp32 MFMA (16x16x4).  Two launches:
+// The state and every accumulation are fp32.  fp32 inputs run every product
+// on the fp32 MFMA (16x16x4).  bf16 inputs run A, P, the solve, T Y and P U in
+// fp32 too, and the state products (K o Gam) H, (Q o Gam) H and the update on
+// the bf16 MFMA: the state as a bf16 copy, U as bf16 high and low parts.
+// Two launches:
 //   chunk_channel_prep_kernel  one wave per (sequence, head, tile), all in
 //       parallel: the gate, the per-channel in-tile running sums (DPP row
 //       scans), the scaled operands, A and P on MFMA, the 16 x 16 solve; the
@@ -39,7 +42,11 @@
 //       slice of d_v): wave 0 ("chain") owns the fp32 state slice in
 //       registers and runs the serial part; waves 1..NP ("loaders") copy the
 //       records and the slice's v values into LDS, double-buffered by epochs
-//       of NP tiles, their global loads issued two epochs ahead.
+//       of NP tiles, their global loads issued two epochs before the chain
+//       reads them.  bf16 inputs: NP = 3, and each loader also forms the
+//       output of the tile its slot held, one epoch later, from a hand-off of
+//       the tile's bf16 starting state and U; fp32 inputs: NP = 2, the chain
+//       forms the output itself.
 #include "la_device.h"
 #include "la_launch.h"
 
