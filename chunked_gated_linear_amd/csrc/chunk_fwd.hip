@@ -36,6 +36,11 @@
 //
 // Blocks are numbered so that all d_v slices of one head share an XCD (and its
 // L2): the hardware deals workgroups to the 8 XCDs round robin.
+//
+// The same kernel serves packed sequences (device offsets: each workgroup
+// takes its sequence's start and length from them; an empty sequence only
+// copies h0 to hT) and raw inputs (the producers L2-normalise each token's q
+// and k rows as they load them and take beta = sigmoid of the given logit).
 #include "la_device.h"
 #include "la_launch.h"
 
