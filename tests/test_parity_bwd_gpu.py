@@ -236,3 +236,19 @@ def test_bwd_varlen_equal_lengths_match_batched_bitwise():
     torch.cuda.synchronize()
     for name, x, r in zip(NAMES, got, ref):
         assert torch.equal(x.reshape(r.shape), r), name
+
+
+def test_bwd_varlen_all_empty_passes_dhT():
+    """A packed batch of empty sequences (T = 0): dh0 is dhT, nothing else."""
+    from chunked_gated_linear_amd import lin_attn_chunk_bwd_varlen
+    say("bwd varlen: 3 empty sequences")
+    nseq, H, D = 3, 2, 64
+    e = lambda *s_, dt=torch.bfloat16: torch.empty(s_, dtype=dt, device="cuda")
+    gen = torch.Generator(device="cuda").manual_seed(74)
+    dhT = torch.randn((nseq, H, D, D), generator=gen, device="cuda")
+    cu = torch.zeros(nseq + 1, dtype=torch.int32, device="cuda")
+    got = lin_attn_chunk_bwd_varlen(e(1, 0, H, D), e(1, 0, H, D), e(1, 0, H, D),
+                                    e(1, 0, H, dt=torch.float32), e(1, 0, H, dt=torch.float32),
+                                    e(1, 0, H, D), cu, None, dhT, gate_mode="logit")
+    torch.cuda.synchronize()
+    assert got[0].numel() == 0 and torch.equal(got[5], dhT)

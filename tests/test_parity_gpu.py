@@ -295,6 +295,20 @@ def test_varlen_fp32(case):
             assert torch.equal(hT[s_], h0[s_] if h0 is not None else torch.zeros_like(hT[s_]))
 
 
+def test_varlen_fp32_all_empty_copies_h0():
+    """fp32, a packed batch of empty sequences (T = 0): hT is h0."""
+    say("varlen fp32: 3 empty sequences")
+    nseq, H, D = 3, 2, 64
+    e = lambda *s_: torch.empty(s_, dtype=torch.float32, device="cuda")
+    gen = torch.Generator(device="cuda").manual_seed(28)
+    h0 = torch.randn((nseq, H, D, D), generator=gen, device="cuda")
+    cu = torch.zeros(nseq + 1, dtype=torch.int32, device="cuda")
+    o, hT = lin_attn_chunk_fwd_varlen(e(1, 0, H, D), e(1, 0, H, D), e(1, 0, H, D), e(1, 0, H),
+                                      e(1, 0, H), cu, h0, gate_mode="logit")
+    torch.cuda.synchronize()
+    assert o.numel() == 0 and torch.equal(hT, h0)
+
+
 def test_varlen_fp32_equal_lengths_match_batched_bitwise():
     """fp32, equal lengths: the packed call reproduces the batched call bit for bit."""
     say("varlen vs batched: 3 x 200 tokens H2 d64 fp32 weak")
