@@ -114,7 +114,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(heads and batch would shard across GPUs with no exchange; see DESIGN.md)",
+              "(heads and batch would shard across GPUs with no exchange)",
               file=sys.stderr)
         sys.exit(2)
 
