@@ -113,7 +113,7 @@ def main():
                          "calibrates the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(heads and batch would shard across GPUs with no exchange)",
               file=sys.stderr)
         sys.exit(2)
