@@ -43,10 +43,11 @@
 //       registers and runs the serial part; waves 1..NP ("loaders") copy the
 //       records and the slice's v values into LDS, double-buffered by epochs
 //       of NP tiles, their global loads issued two epochs before the chain
-//       reads them.  bf16 inputs: NP = 3, and each loader also forms the
-//       output of the tile its slot held, one epoch later, from a hand-off of
-//       the tile's bf16 starting state and U; fp32 inputs: NP = 2, the chain
-//       forms the output itself.
+//       reads them.  bf16 inputs with few workgroups: NP = 3, and each loader
+//       also forms the output of the tile its slot held, one epoch later,
+//       from a hand-off of the tile's bf16 starting state and U; otherwise
+//       NP = 2 and the chain forms the output itself (for bf16 in 78 KB of
+//       LDS, so that two workgroups share a compute unit).
 #include "la_device.h"
 #include "la_launch.h"
 
@@ -85,12 +86,14 @@ constexpr int kScrA = 0, kScrB = 1024, kScr = 1024 + 64;
 constexpr int kGcs = 8 * 64 * 16;
 constexpr int kKts = kScr, kPrepWave = kScr + kGcs + 128 * 4;
 
-// Records of two epochs of NP tiles; for bf16 inputs also the hand-off from
-// the chain to the loader wave that computes a tile's output: the tile's bf16
-// starting state and U, two epochs of NP tiles.
-template <typename E, int DK, int NP>
+// Records of two epochs of NP tiles; with OUTL (loaders form the outputs, bf16
+// inputs only) also the hand-off from the chain to the loader wave that
+// computes a tile's output: the tile's bf16 starting state and U, two epochs
+// of NP tiles.
+template <typename E, int DK, int NP, bool OUTL>
 struct ChCfg {
-  static constexpr int HAND = sizeof(E) == 2 ? (DK / 32 + 1) * 64 * 16 : 0;   // bytes per tile
+  static_assert(!OUTL || sizeof(E) == 2, "loader outputs use the bf16 state copy");
+  static constexpr int HAND = OUTL ? (DK / 32 + 1) * 64 * 16 : 0;   // bytes per tile
   static constexpr int HAND_AT = 2 * NP * ChRec<DK, sizeof(E)>::LDS;
   static constexpr int LDS = HAND_AT + 2 * NP * HAND;
   static_assert(LDS <= 160 * 1024, "LDS budget");
@@ -397,13 +400,13 @@ struct ChCopy {
 };
 
 // ------------------------------------------------------------ chain kernel
-template <typename E, int DK, int NP>
+template <typename E, int DK, int NP, bool OUTL>
 __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_channel_kernel(
     const E* __restrict__ v, const char* __restrict__ ws, const float* h0,
     E* __restrict__ o, float* hT, int B, int TA, int H, int DV, const int* __restrict__ cu,
     int nslot) {
   using R = ChRec<DK, sizeof(E)>;
-  using C = ChCfg<E, DK, NP>;
+  using C = ChCfg<E, DK, NP, OUTL>;
   using X = Elt<float>;
   using F16 = X::F16;
   using F32 = X::F32;
@@ -536,12 +539,26 @@ __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_channel_kernel(
             for (int i = 0; i < 4; ++i) Hacc[t][i] *= gc[t][i];   // row 16t + 4grp + i
             Hacc[t] = XB::mma32(kt[t], ub, Hacc[t]);
           }
-          // the output, O = (Q o Gam) H + P U, is the loader's: hand over the
-          // state the tile started from and U
-          char* hand = hand_of(ep, j);
+          if constexpr (OUTL) {
+            // the output, O = (Q o Gam) H + P U, is the loader's: hand over
+            // the state the tile started from and U
+            char* hand = hand_of(ep, j);
 #pragma unroll
-          for (int s2 = 0; s2 < NS; ++s2) reinterpret_cast<XB::F32*>(hand)[s2 * 64 + lane] = hb[s2];
-          reinterpret_cast<f32x4*>(hand + NS * 1024)[lane] = U;
+            for (int s2 = 0; s2 < NS; ++s2) reinterpret_cast<XB::F32*>(hand)[s2 * 64 + lane] = hb[s2];
+            reinterpret_cast<f32x4*>(hand + NS * 1024)[lane] = U;
+          } else {
+            // the output after the state update: O = (Q o Gam) H + P U
+            f32x4 QH = zero4();
+#pragma unroll
+            for (int s2 = 0; s2 < NS; ++s2)
+              QH = XB::mma32(reinterpret_cast<const XB::F32*>(rec + R::QF)[s2 * 64 + lane], hb[s2], QH);
+            const F16 pf = reinterpret_cast<const F16*>(rec + R::PF)[lane];
+            const f32x4 O = X::mma16(pf, X::from_acc(U), QH);
+            E* oc = orow + (int64_t)(16 * c) * ostride;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (16 * c + 4 * grp + i < T) oc[i * ostride] = Elt<E>::from_f(O[i]);
+          }
         }
       }
       __syncthreads();  // this epoch consumed, next epoch loaded
@@ -596,7 +613,7 @@ __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_channel_kernel(
   // the record still in this loader's slot (it is refilled only afterwards,
   // by this same wave): O = (Q o Gam) H + P U on this wave's matrix core.
   auto output = [&](int e) {
-    if constexpr (sizeof(E) == 2) {
+    if constexpr (OUTL) {
       const int c = e * NP + p;
       if (e < 0 || c >= NC) return;
       using XB = Elt<__bf16>;
@@ -641,9 +658,17 @@ __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_channel_kernel(
   output(NE - 1);               // the last epoch: its slot is not refilled
 }
 
+// Compute units of the current device (0 if the query fails).
+static int ch_compute_units() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return n;
+}
+
 // B sequences of T tokens (cu == nullptr), or B packed sequences with device
 // offsets cu in one sequence of T tokens.
-template <typename E, int DK, int NP>
+template <typename E, int DK, int NP, bool OUTL>
 hipError_t launch_ch(const void* q, const void* k, const void* v, const float* gate,
                      int gate_logit, float G, const float* beta, const float* h0, void* o,
                      float* hT, int B, int T, int H, int Dv, const int* cu, void* ws,
@@ -660,7 +685,7 @@ hipError_t launch_ch(const void* q, const void* k, const void* v, const float* g
     if (e != hipSuccess) return e;
   }
   const int blocks = B * H * (Dv / 16);
-  hipLaunchKernelGGL((chunk_fwd_channel_kernel<E, DK, NP>), dim3(blocks), dim3(64 * (NP + 1)),
+  hipLaunchKernelGGL((chunk_fwd_channel_kernel<E, DK, NP, OUTL>), dim3(blocks), dim3(64 * (NP + 1)),
                      0, st, (const E*)v, (const char*)ws, h0, (E*)o, hT, B, T, H, Dv, cu, nslot);
   return hipGetLastError();
 }
@@ -786,17 +811,27 @@ hipError_t launch_chunk_fwd_channel_varlen(const void* q, const void* k, const v
                                            const float* beta, const float* h0, void* o,
                                            float* hT, const int* cu, int B, int T, int H, int Dk,
                                            int Dv, int fp32, void* ws, hipStream_t st) {
-// tiles per epoch (= loader waves): three for bf16 records, two for the
-// larger fp32 ones (LDS)
-#define LA_CH(E, DK) \
-  return launch_ch<E, DK, sizeof(E) == 2 ? 3 : 2>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, \
-                                                  B, T, H, Dv, cu, ws, st)
+// Tiles per epoch (= loader waves) and who forms the outputs.  fp32: two, the
+// chain (the fp32 records take 110 KB).  bf16 with fewer workgroups than two
+// per compute unit (a few long sequences): three, the loaders (147 KB, one
+// workgroup per unit, each as fast as it can go).  bf16 with more (many
+// sequences or heads): two, the chain (78 KB: two workgroups share a unit).
+#define LA_CH(E, DK, NP, OUTL) \
+  return launch_ch<E, DK, NP, OUTL>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, \
+                                    cu, ws, st)
   if (fp32) {
-    if (Dk == 64) LA_CH(float, 64);
-    if (Dk == 128) LA_CH(float, 128);
+    if (Dk == 64) LA_CH(float, 64, 2, false);
+    if (Dk == 128) LA_CH(float, 128, 2, false);
   } else {
-    if (Dk == 64) LA_CH(__bf16, 64);
-    if (Dk == 128) LA_CH(__bf16, 128);
+    const bool dense = (int64_t)B * H * (Dv / 16) >= 2 * (int64_t)ch_compute_units();
+    if (Dk == 64) {
+      if (dense) LA_CH(__bf16, 64, 2, false);
+      LA_CH(__bf16, 64, 3, true);
+    }
+    if (Dk == 128) {
+      if (dense) LA_CH(__bf16, 128, 2, false);
+      LA_CH(__bf16, 128, 3, true);
+    }
   }
 #undef LA_CH
   return hipErrorInvalidValue;

@@ -73,6 +73,10 @@ CASES = [
     ("bf16", 128, 128, 2, 1, 64, "std", "logit", 0.02),        # 4 tiles
     ("bf16", 128, 64, 1, 2, 80, "std", "log", 0.02),           # 5 tiles
     ("bf16", 64, 128, 1, 2, 96, "weak", "logit", None),        # 6 tiles, two whole epochs
+    # at least two workgroups per compute unit: two tiles per epoch, the chain
+    # forms the outputs, two workgroups share a unit
+    ("bf16", 128, 128, 4, 16, 70, "weak", "logit", 0.02),
+    ("bf16", 64, 128, 2, 32, 40, "std", "log", None),
 ]
 
 
