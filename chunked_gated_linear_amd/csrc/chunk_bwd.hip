@@ -46,10 +46,11 @@ namespace {
 constexpr int kT = 16;          // tokens per tile
 constexpr int kBwdThreads = 256;
 
-// Workspace: per tile and head a record (below), then the fp32 state at every
-// tile start (hs) and the gradient of every tile's end state (dhs), each
-// d_k x d_v per tile and head, stored per 16-column slice in MFMA fragment
-// order: element (row r, column 16 jb + n) of tile block (bh, c) sits at
+// Workspace: per tile index (below: (b H + h) NT + c for a batch, h nslot +
+// slot for packed sequences) a record, then the fp32 state at every tile
+// start (hs) and the gradient of every tile's end state (dhs), each d_k x d_v
+// per tile index, stored per 16-column slice in MFMA fragment order: element
+// (row r, column 16 jb + n) of a tile's block sits at
 // float ((jb * d_k / 16 + r / 16) * 64 + 16 ((r % 16) / 4) + n) * 4 + r % 4,
 // so the serial kernels store whole 16-byte fragments.
 // Record of one tile (floats).
@@ -78,8 +79,8 @@ struct BwdArgs {
   float* dbeta;
   float* dh0;
   float* rec;
-  float* hs;    // [B, H, NT, Dk, Dv] state at each tile start
-  float* dhs;   // [B, H, NT, Dk, Dv] gradient of each tile's end state
+  float* hs;    // [tile index][Dk x Dv] state at each tile start
+  float* dhs;   // [tile index][Dk x Dv] gradient of each tile's end state
   int gate_logit;
   float G;
   int B, T, H, Dv, NT;
