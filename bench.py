@@ -102,6 +102,8 @@ def main():
     ap.add_argument("--raw-steps", type=int, default=10)
     ap.add_argument("--bwd-steps", type=int, default=5)
     ap.add_argument("--channel-steps", type=int, default=5)
+    ap.add_argument("--ladder-steps", type=int, default=5,
+                    help="timed calls per rung of the context ladder (8K, 256K, 1M); 0 skips it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the copy and GEMM ceiling measurements")
@@ -196,6 +198,73 @@ def main():
                      "alg_flops_per_launch": flops,
                      "attainable_frac": max(byts / PEAK_HBM, flops / PEAK_BF16) / t},
     }
+
+    # ---- the rest of the context ladder (8K, 256K and 1M tokens; the headline
+    # above is the 64K rung): one object per rung with its own roofline and a
+    # CPU baseline of the oracle on a bounded sample of the same rung
+    if args.ladder_steps > 0:
+        from oracle import c_recurrent as crec
+        from oracle import linattn_oracle as orc
+        ladder = {}
+        for name, seed, cpu_tok in (("train_8k", 1001, 8192), ("long_256k", 1007, 262144),
+                                    ("million_1m", 1003, 262144)):
+            if name == args.workload:
+                continue
+            lw = dict(I.WORKLOADS[name])
+            lB, lH, lT, lK, lV = lw["B"], lw["H"], lw["T"], lw["Dk"], lw["Dv"]
+            lh0 = lw.get("h0_std")
+            lin = I.make_inputs(lB, lT, lH, lK, lV, dtype=lw["dtype"], seed=seed, device=dev,
+                                h0_std=lh0)
+            lo = torch.empty((lB, lT, lH, lV), dtype=lin["q"].dtype, device=dev)
+            lh = torch.empty((lB, lH, lK, lV), dtype=torch.float32, device=dev)
+            lws = torch.empty(max(1, lin_attn_chunk_fwd_workspace_size(lB, lT, lH, lK, lV)),
+                              dtype=torch.uint8, device=dev)
+
+            def lstep():
+                lin_attn_chunk_fwd(lin["q"], lin["k"], lin["v"], lin["x"], lin["beta"], lin["h0"],
+                                   gate_mode="logit", G=5.0, o=lo, hT=lh, workspace=lws)
+
+            nsteps = args.ladder_steps if lT <= 262144 else max(2, args.ladder_steps // 2)
+            lstep()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(nsteps):
+                lstep()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            lms = e0.elapsed_time(e1) / nsteps
+            lt = lms * 1e-3
+            lfl, lby = alg_counts(lB, lT, lH, lK, lV, 2, lh0 is not None)
+            rung = {
+                "workload": (f"{name} B={lB} H={lH} T={lT} d={lK} bf16, gate x ~ N(0,1) G=5, "
+                             f"h0 {'N(0,0.02)' if lh0 else 'zero'}"),
+                "steps": nsteps, "ms_per_call": lms, "tokens_per_s": lB * lT / lt,
+                "tflops": lfl / lt / 1e12, "mfma_pct_of_bf16_peak": 100.0 * lfl / lt / PEAK_BF16,
+                "roofline": {"bound": "hbm", "achieved": lby / lt / 1e9, "peak": PEAK_HBM / 1e9,
+                             "unit": "GB/s", "frac": lby / lt / PEAK_HBM, "traffic": None,
+                             "alg_bytes_per_launch": lby, "alg_flops_per_launch": lfl,
+                             "kernel": "chunk_prep_kernel + chunk_state_kernel (one call)",
+                             "attainable_frac": max(lby / PEAK_HBM, lfl / PEAK_BF16) / lt},
+            }
+            if not args.no_cpu_baseline:
+                S_tok = min(lT, cpu_tok)
+                f = lambda x: x.detach().float().cpu().numpy()
+                q_, k_, v_ = (f(lin[n_][:, :S_tok]) for n_ in ("q", "k", "v"))
+                x_ = f(lin["x"][:, :S_tok]).astype(np.float64)
+                b_ = f(lin["beta"][:, :S_tok]).astype(np.float64)
+                h_ = None if lin["h0"] is None else f(lin["h0"]).astype(np.float64)
+                workers = min(16, os.cpu_count() or 1, lB * lH)
+                c0 = time.perf_counter()
+                crec.recurrent_fwd_c(q_, k_, v_, orc.bounded_gate(x_), b_, h_, workers=workers)
+                cs = time.perf_counter() - c0
+                rung["cpu_baseline"] = {
+                    "value": lB * S_tok / cs, "unit": "tokens/s", "cores": workers,
+                    "kind": "oracle",
+                    "sample": (f"all {lB * lH} heads, first {S_tok} of {lT} tokens (fp64 C "
+                               f"recurrence, one thread per head stream), {cs:.1f} s wall")}
+            ladder[name] = rung
+            del lin, lo, lh, lws
+        result["ladder"] = ladder
 
     # ---- the same workload from raw inputs (q, k normalised and beta from
     # logits inside the pass): what the fused input preparation costs

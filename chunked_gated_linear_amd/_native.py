@@ -48,6 +48,8 @@ SIGNATURES = {
     "lin_attn_decode_step_channel": (_I, [_P, _P, _P, _P, _I, _F, _P, _P, _P,
                                           _I, _I, _I, _I, _I, _P]),
     "lin_attn_gate": (_I, [_P, _F, _P, _LL, _P]),
+    "lin_attn_check_inputs": (_I, [_P, _P, _P, _P, _I, _F, _P, _P, _LL, _I, _I, _I, _I, _I, _I,
+                                   _P, _P]),
     "lin_attn_last_error": (ctypes.c_char_p, []),
     "lin_attn_version": (_I, []),
 }

@@ -3,9 +3,17 @@ every step of the computation runs in the library's HIP kernels.
 
 Tensors are torch tensors on the GPU (PyTorch supplies device memory and the
 current stream); shapes and layouts are those of include/lin_attn.h.
+
+Streams: with stream=None the kernels run on torch's current stream.  With
+stream=s every tensor a wrapper allocates (outputs and a missing workspace)
+is taken from the caching allocator while s is current, so torch reuses that
+memory only in s's order, after the library's kernels; tensors the caller
+passes in stay the caller's to order.
 """
 
 from __future__ import annotations
+
+import functools
 
 import torch
 
@@ -32,6 +40,19 @@ def _need(t, name, dtype=None, shape=None):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
+def _on_stream(fn):
+    """Run the wrapper with `stream` (keyword) current, so that its
+    allocations belong to that stream."""
+    @functools.wraps(fn)
+    def wrapper(*args, **kwargs):
+        stream = kwargs.get("stream")
+        if stream is None:
+            return fn(*args, **kwargs)
+        with torch.cuda.stream(stream):
+            return fn(*args, **kwargs)
+    return wrapper
+
+
 def _stream(t, stream):
     s = stream if stream is not None else torch.cuda.current_stream(t.device)
     return s.cuda_stream
@@ -45,6 +66,7 @@ def lin_attn_chunk_fwd_workspace_size(B, T, H, Dk, Dv, dtype=torch.bfloat16):
     return n
 
 
+@_on_stream
 def lin_attn_chunk_fwd(q, k, v, gate, beta, h0=None, *, gate_mode="log", G=5.0,
                        o=None, hT=None, output_final_state=True, workspace=None,
                        stream=None, raw=False):
@@ -94,6 +116,7 @@ def lin_attn_chunk_fwd_channel_workspace_size(B, T, H, Dk, Dv, dtype=torch.bfloa
     return n
 
 
+@_on_stream
 def lin_attn_chunk_fwd_channel(q, k, v, gate, beta, h0=None, *, gate_mode="log", G=5.0,
                                o=None, hT=None, output_final_state=True, workspace=None,
                                stream=None):
@@ -141,6 +164,7 @@ def lin_attn_chunk_fwd_channel_varlen_workspace_size(T, nseq, H, Dk, Dv, dtype=t
     return n
 
 
+@_on_stream
 def lin_attn_chunk_fwd_channel_varlen(q, k, v, gate, beta, cu_seqlens, h0=None, *,
                                       gate_mode="log", G=5.0, o=None, hT=None,
                                       output_final_state=True, workspace=None, stream=None):
@@ -187,6 +211,7 @@ def lin_attn_chunk_bwd_workspace_size(B, T, H, Dk, Dv, dtype=torch.bfloat16):
     return n
 
 
+@_on_stream
 def lin_attn_chunk_bwd(q, k, v, gate, beta, dout, h0=None, dhT=None, *, gate_mode="log",
                        G=5.0, output_dh0=True, workspace=None, stream=None):
     """Gradients of <o, dout> + <hT, dhT> for lin_attn_chunk_fwd's inputs.
@@ -235,6 +260,7 @@ def lin_attn_chunk_bwd_varlen_workspace_size(T, nseq, H, Dk, Dv, dtype=torch.bfl
     return n
 
 
+@_on_stream
 def lin_attn_chunk_bwd_varlen(q, k, v, gate, beta, dout, cu_seqlens, h0=None, dhT=None, *,
                               gate_mode="log", G=5.0, output_dh0=True, workspace=None,
                               stream=None):
@@ -289,6 +315,7 @@ def lin_attn_chunk_fwd_varlen_workspace_size(T, nseq, H, Dk, Dv, dtype=torch.bfl
     return n
 
 
+@_on_stream
 def lin_attn_chunk_fwd_varlen(q, k, v, gate, beta, cu_seqlens, h0=None, *, gate_mode="log",
                               G=5.0, o=None, hT=None, output_final_state=True,
                               workspace=None, stream=None, raw=False):
@@ -350,6 +377,7 @@ def _decode(fn, channel, q, k, v, gate, beta, S, gate_mode, G, o, stream):
     return o
 
 
+@_on_stream
 def lin_attn_decode_step(q, k, v, gate, beta, S, *, gate_mode="log", G=5.0, o=None,
                          stream=None):
     """Advance S [B,H,Dk,Dv] by one token in place; returns o [B,H,Dv]."""
@@ -357,6 +385,7 @@ def lin_attn_decode_step(q, k, v, gate, beta, S, *, gate_mode="log", G=5.0, o=No
                    stream)
 
 
+@_on_stream
 def lin_attn_decode_step_channel(q, k, v, gate, beta, S, *, gate_mode="log", G=5.0, o=None,
                                  stream=None):
     """lin_attn_decode_step with one log-decay per key channel: gate [B,H,Dk]."""
@@ -364,7 +393,8 @@ def lin_attn_decode_step_channel(q, k, v, gate, beta, S, *, gate_mode="log", G=5
                    gate_mode, G, o, stream)
 
 
-def lin_attn_gate(x, G=5.0, out=None, stream=None):
+@_on_stream
+def lin_attn_gate(x, G=5.0, out=None, *, stream=None):
     """g = -G * sigmoid(x), float32, same shape as x."""
     _need(x, "x", torch.float32)
     if out is None:
@@ -372,3 +402,34 @@ def lin_attn_gate(x, G=5.0, out=None, stream=None):
     _need(out, "out", torch.float32, tuple(x.shape))
     N.check(N.lib().lin_attn_gate(_ptr(x), float(G), _ptr(out), x.numel(), _stream(x, stream)))
     return out
+
+
+@_on_stream
+def lin_attn_check_inputs(q, k, v, gate, beta, h0=None, *, gate_mode="log", G=5.0,
+                          stream=None):
+    """Opt-in debug range check of a forward pass's inputs (blocks until done):
+    raises LinAttnError with code LA_ERANGE when a q, k, v or h0 element is not
+    finite, a beta lies outside [0, 1], or a gate value lies outside [-G, 0]
+    (log mode) or is NaN (logit mode).  q, k [B,T,H,Dk], v [B,T,H,Dv], gate
+    [B,T,H] or [B,T,H,Dk] (per-channel), beta [B,T,H], h0 [nstate,H,Dk,Dv]."""
+    _need(q, "q")
+    if q.dtype not in _DTYPES:
+        raise TypeError("q, k, v must be bfloat16 or float32")
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    _need(k, "k", q.dtype, (B, T, H, Dk))
+    _need(v, "v", q.dtype, (B, T, H, Dv))
+    channel = gate.dim() == 4
+    _need(gate, "gate", torch.float32, (B, T, H, Dk) if channel else (B, T, H))
+    _need(beta, "beta", torch.float32, (B, T, H))
+    nstate = 0
+    if h0 is not None:
+        _need(h0, "h0", torch.float32)
+        nstate = h0.shape[0]
+        if tuple(h0.shape[1:]) != (H, Dk, Dv):
+            raise ValueError(f"h0 must be [nstate, {H}, {Dk}, {Dv}]")
+    flags = torch.empty(1, dtype=torch.int32, device=q.device)
+    N.check(N.lib().lin_attn_check_inputs(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _GATE[gate_mode], float(G), _ptr(beta), _ptr(h0),
+        B * T, nstate, H, Dk, Dv, int(channel), _DTYPES[q.dtype], _ptr(flags),
+        _stream(q, stream)))

@@ -202,7 +202,9 @@ __device__ inline void prep_tile(const ChRaw<E, DK>& r, int c, int T, char* __re
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float x = j < 4 ? r.glo[s][j] : r.ghi[s][j - 4];
-        const float g = ok ? (gate_logit ? bounded_gate(x, G) : x) : 0.f;
+        // log mode: clamped to [-G, 0], so that the in-tile factors stay
+        // within exp(+-8 G) whatever the caller passes
+        const float g = ok ? (gate_logit ? bounded_gate(x, G) : fminf(fmaxf(x, -G), 0.f)) : 0.f;
         const float Gt = row_scan16(g);                 // G_t[c], t = n
         const float Gm = row_bcast<7>(Gt);              // G at the middle token
         const float Gl = row_bcast<15>(Gt);             // G at the last token
@@ -658,13 +660,6 @@ __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_channel_kernel(
   output(NE - 1);               // the last epoch: its slot is not refilled
 }
 
-// Compute units of the current device (0 if the query fails).
-static int ch_compute_units() {
-  int dev = 0, n = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  return n;
-}
 
 // B sequences of T tokens (cu == nullptr), or B packed sequences with device
 // offsets cu in one sequence of T tokens.
@@ -720,7 +715,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_channel_kernel(
     const float bt = beta[bh];
     if (tid < DK) {
       const float gx = gate[bh * DK + tid];
-      const float a = __expf(gate_logit ? bounded_gate(gx, G) : gx);
+      const float a = __expf(gate_logit ? bounded_gate(gx, G) : fminf(fmaxf(gx, -G), 0.f));
       const float kv = Elt<E>::to_f(k[bh * DK + tid]);
       sk[tid] = kv;
       sa[tid] = a;
@@ -775,12 +770,7 @@ template <typename E, int DK, int DV>
 hipError_t launch_dec_ch(const void* q, const void* k, const void* v, const float* gate,
                          int gate_logit, float G, const float* beta, float* S, void* o, int BH,
                          hipStream_t st) {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus < 1)
-    cus = 256;
-  const int cap = 4 * cus;
+  const int cap = 4 * device_cus();
   const int grid = BH < cap ? BH : cap;
   hipLaunchKernelGGL((decode_channel_kernel<E, DK, DV>), dim3(grid), dim3(kDecThreads), 0, st,
                      (const E*)q, (const E*)k, (const E*)v, gate, gate_logit, G, beta, S, (E*)o,
@@ -823,7 +813,7 @@ hipError_t launch_chunk_fwd_channel_varlen(const void* q, const void* k, const v
     if (Dk == 64) LA_CH(float, 64, 2, false);
     if (Dk == 128) LA_CH(float, 128, 2, false);
   } else {
-    const bool dense = (int64_t)B * H * (Dv / 16) >= 2 * (int64_t)ch_compute_units();
+    const bool dense = (int64_t)B * H * (Dv / 16) >= 2 * (int64_t)device_cus();
     if (Dk == 64) {
       if (dense) LA_CH(__bf16, 64, 2, false);
       LA_CH(__bf16, 64, 3, true);

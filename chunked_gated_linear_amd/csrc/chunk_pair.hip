@@ -934,12 +934,6 @@ constexpr int kPrepResidentMin = 16;
 
 static bool stretch_area(int NSC) { return NSC >= kStretchAreaPairs; }
 
-static int compute_units() {
-  int dev = 0, n = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  return n;
-}
 
 template <int DK>
 static hipError_t launch_pair_t(const void* q, const void* k, const void* v, const float* gate,
@@ -947,7 +941,7 @@ static hipError_t launch_pair_t(const void* q, const void* k, const void* v, con
                                 void* o, float* hT, int B, int T, int H, int Dv, int raw, void* ws,
                                 hipStream_t st) {
   const int NSC = (T + 31) / 32;
-  const int cus = compute_units();
+  const int cus = device_cus();
   // two slices per workgroup when one per workgroup would take more than one
   // round of workgroups (one fits per compute unit)
   const int NV = Dv / 16;
@@ -1027,7 +1021,7 @@ static hipError_t launch_varlen_t(const void* q, const void* k, const void* v, c
                                   int raw, void* ws, hipStream_t st) {
   const int nslot = varlen_slots(T, nseq);
   const int NV = Dv / 16;
-  const int spw = (NV % 2 == 0 && (int64_t)nseq * H * NV > compute_units()) ? 2 : 1;
+  const int spw = (NV % 2 == 0 && (int64_t)nseq * H * NV > device_cus()) ? 2 : 1;
   const int nstate = nseq * H * (NV / spw);
   char* const wsb = static_cast<char*>(ws);
   const PrepArgs pa{(const __bf16*)q, (const __bf16*)k, gate, beta, wsb, gate_logit, G,

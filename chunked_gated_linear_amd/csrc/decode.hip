@@ -20,10 +20,28 @@
 // written as consecutive 16-byte pieces.  The state is streamed once per step
 // (it does not fit the last-level cache), so its loads and stores are marked
 // non-temporal.
+#include <atomic>
+
 #include "la_device.h"
 #include "la_launch.h"
 
 namespace la {
+
+int device_cus() {
+  static std::atomic<int> cache[64];   // 0 = not queried yet
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  const bool slot = dev >= 0 && dev < 64;
+  if (slot) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+    return 256;
+  if (slot) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
 
 constexpr int kDecodeThreads = 1024;
 constexpr int kDecodeBlocksPerCU = 4;
@@ -107,11 +125,7 @@ static hipError_t launch_decode_t(const void* q, const void* k, const void* v,
                                   const float* gate, int gate_logit, float G,
                                   const float* beta, float* S, void* o, int BH,
                                   hipStream_t st) {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-    cus = 256;
-  const int cap = kDecodeBlocksPerCU * cus;
+  const int cap = kDecodeBlocksPerCU * device_cus();
   const int grid = BH < cap ? BH : cap;
   hipLaunchKernelGGL((decode_kernel<E, DK, DV>), dim3(grid), dim3(kDecodeThreads), 0, st,
                      (const E*)q, (const E*)k, (const E*)v, gate, gate_logit, G,
@@ -173,6 +187,66 @@ hipError_t launch_state_init(const float* h0, float* hT, long long n, hipStream_
     hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(256), 0, st, h0, hT, n);
   else
     hipLaunchKernelGGL(fill_kernel, dim3((unsigned)blocks), dim3(256), 0, st, hT, n, 0.0f);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Debug range check of a forward pass's inputs: the bounded log-decay lies in
+// [-G, 0] ("Deep Dive: The Next Generation of Ultra-Long Context Sparse MoE
+// LLMs", sec. 3.3), beta in [0, 1], everything finite.  Grid-stride over each
+// array; per-wave OR of the flags, then one atomic OR per wave that found
+// anything (the result does not depend on the order).
+__global__ void clear_flag_kernel(unsigned* flags) { flags[0] = 0u; }
+
+template <typename E>
+__device__ inline bool fin(E x) { return __builtin_isfinite((float)x); }
+
+template <typename E>
+__global__ __launch_bounds__(256) void range_kernel(const E* q, const E* k, long long nqk,
+                                                    const E* v, long long nv, const float* gate,
+                                                    long long ngate, int gate_logit, float G,
+                                                    const float* beta, long long nbeta,
+                                                    const float* h0, long long nh0,
+                                                    unsigned* flags) {
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  const long long i0 = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  unsigned f = 0;
+  for (long long i = i0; i < nqk; i += stride)
+    if (!fin(q[i]) || !fin(k[i])) f |= 1u;
+  for (long long i = i0; i < nv; i += stride)
+    if (!fin(v[i])) f |= 1u;
+  for (long long i = i0; i < ngate; i += stride) {
+    const float x = gate[i];
+    if (gate_logit ? x != x : !(x >= -G && x <= 0.f)) f |= 2u;
+  }
+  for (long long i = i0; i < nbeta; i += stride) {
+    const float x = beta[i];
+    if (!(x >= 0.f && x <= 1.f)) f |= 4u;
+  }
+  for (long long i = i0; i < nh0; i += stride)
+    if (!__builtin_isfinite(h0[i])) f |= 8u;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) f |= (unsigned)__shfl_xor((int)f, d);
+  if ((threadIdx.x & 63) == 0 && f) atomicOr(flags, f);
+}
+
+hipError_t launch_range_check(const void* q, const void* k, const void* v, const float* gate,
+                              int gate_logit, float G, const float* beta, const float* h0,
+                              long long nqk, long long nv, long long ngate, long long nbeta,
+                              long long nh0, int fp32, unsigned* flags, hipStream_t st) {
+  hipLaunchKernelGGL(clear_flag_kernel, dim3(1), dim3(1), 0, st, flags);
+  const long long n = nqk > ngate ? nqk : ngate;
+  long long blocks = (n + 255) / 256;
+  if (blocks > 2048) blocks = 2048;
+  if (blocks < 1) blocks = 1;
+  if (fp32)
+    hipLaunchKernelGGL(range_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, st,
+                       (const float*)q, (const float*)k, nqk, (const float*)v, nv, gate, ngate,
+                       gate_logit, G, beta, nbeta, h0, h0 ? nh0 : 0, flags);
+  else
+    hipLaunchKernelGGL(range_kernel<__bf16>, dim3((unsigned)blocks), dim3(256), 0, st,
+                       (const __bf16*)q, (const __bf16*)k, nqk, (const __bf16*)v, nv, gate, ngate,
+                       gate_logit, G, beta, nbeta, h0, h0 ? nh0 : 0, flags);
   return hipGetLastError();
 }
 

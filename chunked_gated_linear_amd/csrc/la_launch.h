@@ -110,6 +110,21 @@ hipError_t launch_decode(const void* q, const void* k, const void* v,
 
 hipError_t launch_gate(const float* x, float G, float* g, long long n, hipStream_t st);
 
+// Compute units of the current device, queried once per device and then
+// served from a per-device cache (the count never changes while the process
+// runs); 256 if the query fails.
+int device_cus();
+
+// Range check of a forward pass's inputs (the caller synchronises): flags[0]
+// gets bit 1 for a non-finite q, k or v element, bit 2 for a gate value
+// outside [-G, 0] or non-finite (log mode) or NaN (logit mode), bit 4 for a
+// beta outside [0, 1] or non-finite, bit 8 for a non-finite h0 element.
+// flags must hold one unsigned int; it is cleared first.
+hipError_t launch_range_check(const void* q, const void* k, const void* v, const float* gate,
+                              int gate_logit, float G, const float* beta, const float* h0,
+                              long long nqk, long long nv, long long ngate, long long nbeta,
+                              long long nh0, int fp32, unsigned* flags, hipStream_t st);
+
 // hT <- h0 (or zeros when h0 is NULL), n floats.
 hipError_t launch_state_init(const float* h0, float* hT, long long n, hipStream_t st);
 

@@ -105,6 +105,48 @@ extern "C" {
 
 const char* lin_attn_last_error(void) { return g_err.c_str(); }
 
+int lin_attn_check_inputs(const void* q, const void* k, const void* v, const float* gate,
+                          int gate_mode, float G, const float* beta, const float* h0,
+                          long long ntok, int nstate, int H, int Dk, int Dv, int channel,
+                          int dtype, unsigned* flags, void* stream) {
+  if (int rc = check_gate_scalars(gate_mode, G)) return rc;
+  if (ntok < 0 || nstate < 0 || H < 0 || Dk < 1 || Dv < 1 || Dk > 4096 || Dv > 4096)
+    return fail(LA_EINVAL, "bad sizes (ntok=%lld nstate=%d H=%d Dk=%d Dv=%d)", ntok, nstate, H,
+                Dk, Dv);
+  if (dtype != LA_BF16 && dtype != LA_FP32)
+    return fail(LA_EINVAL, "dtype must be LA_BF16 (0) or LA_FP32 (1), got %d", dtype);
+  if (!flags || !aligned(flags, 4u)) return fail(LA_EINVAL, "flags must be a 4-byte aligned pointer");
+  const int64_t nqk = (int64_t)ntok * H * Dk, nv = (int64_t)ntok * H * Dv;
+  const int64_t ngate = (int64_t)ntok * H * (channel ? Dk : 1), nbeta = (int64_t)ntok * H;
+  const int64_t nh0 = (int64_t)nstate * H * Dk * Dv;
+  if (nqk > 0) {
+    const struct { const char* nm; const void* p; } req[] = {
+        {"q", q}, {"k", k}, {"v", v}, {"gate", gate}, {"beta", beta}};
+    for (const auto& r : req) {
+      if (!r.p) return fail(LA_EINVAL, "%s must not be NULL", r.nm);
+      if (!aligned(r.p, dtype == LA_BF16 ? 2u : 4u)) return fail(LA_EINVAL, "%s misaligned", r.nm);
+    }
+  }
+  if (h0 && !aligned(h0, 4u)) return fail(LA_EINVAL, "h0 must be 4-byte aligned");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (int rc = hip_status(la::launch_range_check(q, k, v, gate, gate_mode == LA_GATE_BOUNDED_LOGIT,
+                                                 G, beta, h0, nqk, nv, ngate, nbeta, nh0,
+                                                 dtype == LA_FP32, flags, st),
+                          "range check launch"))
+    return rc;
+  unsigned f = 0;
+  if (int rc = hip_status(hipStreamSynchronize(st), "range check")) return rc;
+  if (int rc = hip_status(hipMemcpy(&f, flags, sizeof f, hipMemcpyDeviceToHost), "range check copy"))
+    return rc;
+  if (!f) return ok();
+  std::string m = "inputs out of range:";
+  if (f & 1u) m += " non-finite q, k or v;";
+  if (f & 2u) m += gate_mode == LA_GATE_LOG ? " gate outside [-G, 0] or non-finite;" : " NaN gate logit;";
+  if (f & 4u) m += " beta outside [0, 1];";
+  if (f & 8u) m += " non-finite h0;";
+  return fail(LA_ERANGE, "%s", m.c_str());
+}
+
 int lin_attn_version(void) { return 200; }
 
 long long lin_attn_chunk_fwd_workspace_size(int B, int T, int H, int Dk, int Dv, int dtype) {

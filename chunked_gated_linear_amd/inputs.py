@@ -91,12 +91,13 @@ def make_decode_inputs(B, H, Dk, Dv, dtype="bf16", seed=0, device="cpu",
             "x": x.contiguous(), "beta": beta.contiguous(), "S": S.contiguous()}
 
 
-# Named workloads.  Shapes follow the pages' context ladder (8K, 64K, 1M tokens)
-# and 16-token tiles; the value distributions are the recipe above.
+# Named workloads.  Shapes follow the pages' context ladder (8K, 64K, 256K, 1M
+# tokens) and 16-token tiles; the value distributions are the recipe above.
 WORKLOADS = {
     "tiny_fp32": dict(B=1, H=2, T=256, Dk=64, Dv=64, dtype="fp32"),
     "train_8k": dict(B=4, H=16, T=8192, Dk=128, Dv=128, dtype="bf16"),
     "long_64k": dict(B=1, H=16, T=65536, Dk=128, Dv=128, dtype="bf16"),
+    "long_256k": dict(B=1, H=16, T=262144, Dk=128, Dv=128, dtype="bf16"),
     "million_1m": dict(B=1, H=8, T=1048576, Dk=128, Dv=128, dtype="bf16", h0_std=0.02),
 }
 DECODE_WORKLOAD = dict(B=256, H=32, Dk=128, Dv=128, dtype="bf16", steps=1000)

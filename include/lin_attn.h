@@ -37,7 +37,8 @@
  *  - Results are deterministic: the same inputs give bitwise-identical
  *    outputs on every call (no atomics in any reduction).
  *  - Calls may be made from several host threads; the library keeps no global
- *    mutable state besides the thread-local error text.
+ *    mutable state besides the thread-local error text and a per-device cache
+ *    of the compute-unit count (written once per device, read-only after).
  *  - Zero-size work (B, H or T equal to 0) is valid and enqueues nothing except
  *    that chunk_fwd with T = 0 copies h0 (or zeros) into hT.
  */
@@ -54,7 +55,9 @@ extern "C" {
                                misalignment, forbidden aliasing, bad enum */
 #define LA_EUNSUPPORTED  2  /* valid but not built: head sizes outside the
                                supported set */
-#define LA_ERANGE        3  /* a scalar parameter outside its allowed range */
+#define LA_ERANGE        3  /* a scalar parameter outside its allowed range,
+                               or (lin_attn_check_inputs only) an input
+                               value outside its range */
 #define LA_EHIP          4  /* a HIP launch error; see lin_attn_last_error() */
 
 /* Element types of q, k, v, o. */
@@ -63,7 +66,9 @@ extern "C" {
 
 /* Meaning of the `gate` array. */
 #define LA_GATE_LOG            0  /* gate holds g_t itself; caller guarantees
-                                     -G <= g_t <= 0 (G only documents it)   */
+                                     -G <= g_t <= 0 (checked only by
+                                     lin_attn_check_inputs; the per-channel
+                                     entry points clamp to [-G, 0])         */
 #define LA_GATE_BOUNDED_LOGIT  1  /* gate holds x_t; g_t = -G * sigmoid(x_t) */
 
 /*
@@ -401,6 +406,34 @@ int lin_attn_chunk_bwd_varlen(const void* q, const void* k, const void* v,
  * in-place transform; other overlaps are rejected).  0 <= G <= 16.
  */
 int lin_attn_gate(const float* x, float G, float* g, long long n, void* stream);
+
+/*
+ * lin_attn_check_inputs -- opt-in debug range check of a forward pass's inputs
+ * (the bounded log-decay lies in [-G, 0]: "Deep Dive: The Next Generation of
+ * Ultra-Long Context Sparse MoE LLMs", sec. 3.3; beta is a write strength in
+ * [0, 1]).  The hot entry points never read their inputs on the host and do
+ * not check values; a caller that wants the check calls this first.
+ *
+ *   q, k   [ntok, H, Dk] dtype;  v [ntok, H, Dv] dtype
+ *   gate   [ntok, H] float32, or [ntok, H, Dk] when channel != 0
+ *   beta   [ntok, H] float32;  h0 [nstate, H, Dk, Dv] float32 or NULL
+ *   ntok   tokens (B * T for a batch, T for packed sequences); nstate the
+ *          number of initial states (B, or nseq)
+ *   flags  DEVICE pointer to one caller-owned unsigned int (scratch; cleared
+ *          and written by the check)
+ * Returns LA_ERANGE when any q, k, v or h0 element is not finite, any beta is
+ * outside [0, 1] (or NaN), or any gate value is outside [-G, 0] or not finite
+ * (LA_GATE_LOG) or NaN (LA_GATE_BOUNDED_LOGIT: +-inf logits are in range, they
+ * give g = 0 and g = -G); the message names every class found.  LA_OK when
+ * everything is in range.  Unlike every other entry point this one BLOCKS: it
+ * enqueues two small kernels on `stream`, then synchronises the stream and
+ * copies the flag to the host.  Sizes and dtype as lin_attn_chunk_fwd
+ * (alignment: 4 bytes).
+ */
+int lin_attn_check_inputs(const void* q, const void* k, const void* v, const float* gate,
+                          int gate_mode, float G, const float* beta, const float* h0,
+                          long long ntok, int nstate, int H, int Dk, int Dv, int channel,
+                          int dtype, unsigned* flags, void* stream);
 
 /* Text of the last error on the calling thread ("" if none). */
 const char* lin_attn_last_error(void);

@@ -456,3 +456,27 @@ def test_bwd_varlen_workspace_size_and_empty():
     assert ws(64, -1, 2, 128, 128, N.LA_BF16) == -1
     # no sequences: nothing to do, nothing touched
     assert bwd_varlen(nseq=0, q=None, cu=None, ws=None)[0] == N.LA_OK
+
+
+def test_check_inputs_host_validation():
+    # host-side rejections happen before any device work (no GPU needed)
+    L = N.lib()
+    P = 0x10000
+    args = dict(q=P, k=P, v=P, gate=P, gm=N.LA_GATE_LOG, G=5.0, beta=P, h0=None, ntok=4,
+                nstate=1, H=2, Dk=128, Dv=128, ch=0, dt=N.LA_BF16, flags=P, st=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.lin_attn_check_inputs(a["q"], a["k"], a["v"], a["gate"], a["gm"], a["G"],
+                                       a["beta"], a["h0"], a["ntok"], a["nstate"], a["H"],
+                                       a["Dk"], a["Dv"], a["ch"], a["dt"], a["flags"], a["st"])
+
+    assert call(flags=None) == N.LA_EINVAL
+    assert b"flags" in L.lin_attn_last_error()
+    assert call(flags=P + 2) == N.LA_EINVAL
+    assert call(G=20.0) == N.LA_ERANGE
+    assert call(gm=7) == N.LA_EINVAL
+    assert call(ntok=-1) == N.LA_EINVAL
+    assert call(dt=5) == N.LA_EINVAL
+    assert call(q=None) == N.LA_EINVAL
+    assert b"q must not be NULL" in L.lin_attn_last_error()

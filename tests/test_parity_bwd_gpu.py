@@ -252,3 +252,109 @@ def test_bwd_varlen_all_empty_passes_dhT():
                                     e(1, 0, H, D), cu, None, dhT, gate_mode="logit")
     torch.cuda.synchronize()
     assert got[0].numel() == 0 and torch.equal(got[5], dhT)
+
+
+# ------------------------------------------- long chains, every gradient
+def _c_grads(host_args, dev_args, up, heads):
+    """The C adjoint on the listed (b, h) streams; in logit mode dg is taken
+    through the bounded gate to dx."""
+    q, k, v, g, beta, h0 = host_args
+    do = host(up["dout"]).astype(np.float64)
+    dhT = None if up["dhT"] is None else host(up["dhT"]).astype(np.float64)
+    res = crec.recurrent_bwd_c(q, k, v, g, beta, do, dhT, h0, heads=heads, workers=16)
+    if dev_args["gate_mode"] == "logit":
+        x = host(dev_args["gate"]).astype(np.float64)
+        for (b, h), r in res.items():
+            r = list(r)
+            r[3] = orc.bounded_gate_bwd(x[b, :, h], r[3])
+            res[(b, h)] = tuple(r)
+    return res
+
+
+def _compare_heads(got, res):
+    gh = [host(x) for x in got]
+    worst = dict.fromkeys(NAMES, 0.0)
+    for (b, h), r in res.items():
+        for i, name in enumerate(NAMES):
+            x = gh[i][b, h] if name == "dh0" else gh[i][b, :, h]
+            assert np.all(np.isfinite(x)), name
+            worst[name] = max(worst[name], relerr(x, r[i]))
+    return worst
+
+
+@pytest.mark.parametrize("shape", [(1, 4096, 2, "weak", 0.02, 1005),
+                                   (4, 8192, 16, "std", None, 1001)],
+                         ids=["weak_4k_B1_H2", "train_8k_B4_H16"])
+def test_bwd_every_gradient_long(shape):
+    """Every gradient of every head against the C adjoint: a weak-decay chain
+    of 256 tiles (g ~ -0.002, the state gradient carried through every tile)
+    and the benchmarked training shape."""
+    B, T, H, regime, h0s, seed = shape
+    say(f"bwd every gradient B{B} T{T} H{H} d128 bf16 {regime}")
+    dev_args, host_args = make_case(B, T, H, 128, 128, "bf16", regime, "logit", h0_std=h0s,
+                                    seed=seed)
+    up = I.make_upstream_grads(B, T, H, 128, 128, dtype="bf16", seed=seed, device="cuda")
+    got = run_bwd(dev_args, up)
+    res = _c_grads(host_args, dev_args, up, [(b, h) for b in range(B) for h in range(H)])
+    worst = _compare_heads(got, res)
+    say("  " + " ".join(f"{n}={e:.2e}" for n, e in worst.items()))
+    for name, e in worst.items():
+        assert e <= TOL_BWD, f"{name}: error {e}"
+
+
+def test_bwd_train_8k_weak_sampled_heads():
+    """The training shape under weak decay (the state gradient carried through
+    all 512 tiles), h0 and dhT given: three heads, every gradient and dh0."""
+    B, T, H = 4, 8192, 16
+    say("bwd train_8k weak, heads (0,0) (1,7) (3,15)")
+    dev_args, host_args = make_case(B, T, H, 128, 128, "bf16", "weak", "logit", h0_std=0.02,
+                                    seed=1011)
+    up = I.make_upstream_grads(B, T, H, 128, 128, dtype="bf16", seed=1011, device="cuda")
+    got = run_bwd(dev_args, up)
+    res = _c_grads(host_args, dev_args, up, [(0, 0), (1, 7), (3, 15)])
+    worst = _compare_heads(got, res)
+    say("  " + " ".join(f"{n}={e:.2e}" for n, e in worst.items()))
+    for name, e in worst.items():
+        assert e <= TOL_BWD, f"{name}: error {e}"
+
+
+def test_bwd_varlen_weak_8k():
+    """A packed training batch of 8192 tokens (five sequences, one empty)
+    under weak decay with h0 and dhT: every gradient of every sequence and
+    head against the C adjoint run on each sequence alone."""
+    from chunked_gated_linear_amd import lin_attn_chunk_bwd_varlen
+    lengths, H, D = [3000, 17, 0, 4100, 1075], 4, 128
+    T, nseq = int(sum(lengths)), len(lengths)
+    say(f"bwd varlen weak {nseq} seqs T{T} H{H}")
+    dev_args, host_args = make_case(1, T, H, D, D, "bf16", "weak", "logit", h0_std=None,
+                                    seed=1012)
+    up = I.make_upstream_grads(1, T, H, D, D, dtype="bf16", seed=1012, device="cuda", dhT=False)
+    gen = torch.Generator(device="cuda").manual_seed(1013)
+    h0 = 0.02 * torch.randn((nseq, H, D, D), generator=gen, device="cuda")
+    dhT = torch.randn((nseq, H, D, D), generator=gen, device="cuda")
+    cu_h = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    cu = torch.tensor(cu_h, dtype=torch.int32, device="cuda")
+    got = lin_attn_chunk_bwd_varlen(dev_args["q"], dev_args["k"], dev_args["v"], dev_args["gate"],
+                                    dev_args["beta"], up["dout"], cu, h0, dhT, gate_mode="logit")
+    torch.cuda.synchronize()
+    q, k, v, g, beta, _ = host_args
+    do = host(up["dout"]).astype(np.float64)
+    x = host(dev_args["gate"]).astype(np.float64)
+    h0_h, dhT_h = host(h0).astype(np.float64), host(dhT).astype(np.float64)
+    gh = [host(t) for t in got]
+    worst = dict.fromkeys(NAMES, 0.0)
+    for s_ in range(nseq):
+        a_, b_ = int(cu_h[s_]), int(cu_h[s_ + 1])
+        for h in range(H):
+            if a_ == b_:
+                assert np.array_equal(gh[5][s_, h], host(dhT)[s_, h])
+                continue
+            r = list(crec.head_bwd(q[0, a_:b_, h], k[0, a_:b_, h], v[0, a_:b_, h], g[0, a_:b_, h],
+                                   beta[0, a_:b_, h], do[0, a_:b_, h], dhT_h[s_, h], h0_h[s_, h]))
+            r[3] = orc.bounded_gate_bwd(x[0, a_:b_, h], r[3])
+            for i, name in enumerate(NAMES):
+                xg = gh[i][s_, h] if name == "dh0" else gh[i][0, a_:b_, h]
+                worst[name] = max(worst[name], relerr(xg, r[i]))
+    say("  " + " ".join(f"{n}={e:.2e}" for n, e in worst.items()))
+    for name, e in worst.items():
+        assert e <= TOL_BWD, f"{name}: error {e}"

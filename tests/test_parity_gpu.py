@@ -104,6 +104,20 @@ def test_long_64k(regime):
     check(name, "bf16", o, hT, ref_o, ref_h)
 
 
+@pytest.mark.parametrize("regime", ["std", "weak"])
+def test_long_256k(regime):
+    """The 256K rung of the context ladder, B1 H16 T262144 (16 stretches of
+    512 pairs): every output and the final state of every head against the C
+    oracle.  Under weak decay (g ~ -0.002) the state carries across all 15
+    stretch cuts."""
+    name = f"long_256k B1 H16 T262144 d128 bf16 {regime}"
+    say(name)
+    dev, hst = make_case(1, 262144, 16, 128, 128, "bf16", regime, "logit", None, seed=1007)
+    o, hT = run_gpu(dev)
+    ref_o, ref_h = oracle_full(hst)
+    check(name, "bf16", o, hT, ref_o, ref_h)
+
+
 def test_weak_decay_4k():
     name = "weak 4k B1 H2 T4096 d128 bf16"
     say(name)
@@ -570,8 +584,10 @@ def test_decode_small(case):
 
 def test_decode_workload():
     """B=256, H=32, d=128, bf16, S ~ N(0, 0.02): every head after step 1, and
-    64 strided heads after 200 consecutive steps (fresh tokens each step)."""
-    B, H, D, steps = 256, 32, 128, 200
+    256 strided heads (every 8th sequence, every 4th head) after the full 1000
+    consecutive steps of the workload (fresh tokens each step), outputs of
+    every step and the final state."""
+    B, H, D, steps = 256, 32, 128, 1000
     say(f"decode workload B{B} H{H} d{D} bf16, {steps} steps")
     d = I.make_decode_inputs(B, H, D, D, dtype="bf16", seed=1004, device="cuda", steps=steps)
     S = d["S"].clone()
@@ -591,7 +607,7 @@ def test_decode_workload():
         outs.append(lin_attn_decode_step(d["q"][s], d["k"][s], d["v"][s], d["x"][s],
                                          d["beta"][s], S, gate_mode="logit"))
     torch.cuda.synchronize()
-    heads = [(b, h) for b in range(0, B, 16) for h in range(0, H, 8)]   # 64 heads
+    heads = [(b, h) for b in range(0, B, 8) for h in range(0, H, 4)]    # 256 heads
     # oracle: the same tokens as a [B, steps, H, .] sequence from S0
     sel_b = sorted({b for b, _ in heads})
     q = np.moveaxis(host(d["q"][:, sel_b]), 0, 1)
@@ -608,5 +624,93 @@ def test_decode_workload():
         ob, hb = res[(sel_b.index(b), h)]
         worst_o = max(worst_o, relerr(o_all[:, b, h], ob))
         worst_s = max(worst_s, relerr(S_h[b, h], hb))
-    say(f"  after {steps} steps, 64 heads: err(o)={worst_o:.3e} err(S)={worst_s:.3e}")
+    say(f"  after {steps} steps, {len(heads)} heads: err(o)={worst_o:.3e} err(S)={worst_s:.3e}")
     assert worst_o <= TOL["bf16"] and worst_s <= TOL["bf16"]
+
+
+def test_side_stream_with_allocations_on_the_current_stream():
+    """stream=s: the workspace and outputs the wrapper allocates belong to s,
+    so the current stream allocating and writing fresh memory while the
+    library's kernels still run on s cannot take them over.  Forward
+    (stretched, workspace-backed) and reverse pass, bitwise against eager
+    calls on the current stream."""
+    from chunked_gated_linear_amd import lin_attn_chunk_bwd
+    say("side stream: stretched forward B1 H4 T20000 and reverse pass B1 H2 T3000")
+    dev, _ = make_case(1, 20000, 4, 128, 128, "bf16", "weak", "logit", 0.02, seed=81)
+    o_ref, h_ref = run_gpu(dev)
+    bdev, _ = make_case(1, 3000, 2, 128, 128, "bf16", "weak", "logit", 0.02, seed=82)
+    up = I.make_upstream_grads(1, 3000, 2, 128, 128, dtype="bf16", seed=82, device="cuda")
+    g_ref = lin_attn_chunk_bwd(bdev["q"], bdev["k"], bdev["v"], bdev["gate"], bdev["beta"],
+                               up["dout"], bdev["h0"], up["dhT"], gate_mode="logit")
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    for rep in range(3):
+        side.wait_stream(torch.cuda.current_stream())
+        o, hT = lin_attn_chunk_fwd(dev["q"], dev["k"], dev["v"], dev["gate"], dev["beta"],
+                                   dev["h0"], gate_mode="logit", stream=side)
+        grads = lin_attn_chunk_bwd(bdev["q"], bdev["k"], bdev["v"], bdev["gate"], bdev["beta"],
+                                   up["dout"], bdev["h0"], up["dhT"], gate_mode="logit",
+                                   stream=side)
+        junk = [torch.full((32 << 20,), 0x7f, dtype=torch.uint8, device="cuda") for _ in range(12)]
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(hT, h_ref), rep
+        for x, r in zip(grads, g_ref):
+            assert torch.equal(x, r), rep
+        del junk
+
+
+def test_range_check():
+    """lin_attn_check_inputs: in-range inputs pass; each class of out-of-range
+    value (a gate above 0 or below -G in log mode, a NaN logit, beta above 1,
+    a NaN in q, an inf in h0) is reported as LA_ERANGE.  The values are only
+    read by the check's own kernel (no attention kernel runs on them)."""
+    from chunked_gated_linear_amd import LinAttnError, lin_attn_check_inputs
+    from chunked_gated_linear_amd import _native as N
+    say("range check: in-range and planted out-of-range values")
+    dev, _ = make_case(2, 100, 3, 128, 64, "bf16", "std", "logit", 0.02, seed=91)
+    a = dict(gate_mode="logit", G=5.0)
+    lin_attn_check_inputs(dev["q"], dev["k"], dev["v"], dev["gate"], dev["beta"], dev["h0"], **a)
+    g_log = lin_attn_gate(dev["gate"], 5.0)
+    lin_attn_check_inputs(dev["q"], dev["k"], dev["v"], g_log, dev["beta"], dev["h0"],
+                          gate_mode="log", G=5.0)
+    xc = I.make_channel_gate(2, 100, 3, 128, seed=91, device="cuda")
+    lin_attn_check_inputs(dev["q"], dev["k"], dev["v"], xc, dev["beta"], None, **a)
+
+    def bad(fn, what):
+        with pytest.raises(LinAttnError) as ei:
+            fn()
+        assert ei.value.code == N.LA_ERANGE and what in str(ei.value), str(ei.value)
+
+    g1 = g_log.clone()
+    g1[1, 50, 2] = 0.25
+    bad(lambda: lin_attn_check_inputs(dev["q"], dev["k"], dev["v"], g1, dev["beta"], None,
+                                      gate_mode="log", G=5.0), "gate outside")
+    g2 = g_log.clone()
+    g2[0, 0, 0] = -5.5
+    bad(lambda: lin_attn_check_inputs(dev["q"], dev["k"], dev["v"], g2, dev["beta"], None,
+                                      gate_mode="log", G=5.0), "gate outside")
+    x3 = dev["gate"].clone()
+    x3[1, 99, 0] = float("nan")
+    bad(lambda: lin_attn_check_inputs(dev["q"], dev["k"], dev["v"], x3, dev["beta"], None, **a),
+        "NaN gate")
+    x4 = dev["gate"].clone()
+    x4[0, 3, 1] = float("inf")          # an infinite logit is in range: g = -G
+    lin_attn_check_inputs(dev["q"], dev["k"], dev["v"], x4, dev["beta"], None, **a)
+    b5 = dev["beta"].clone()
+    b5[0, 7, 2] = 1.5
+    bad(lambda: lin_attn_check_inputs(dev["q"], dev["k"], dev["v"], dev["gate"], b5, None, **a),
+        "beta outside")
+    q6 = dev["q"].clone()
+    q6[1, 20, 1, 5] = float("nan")
+    bad(lambda: lin_attn_check_inputs(q6, dev["k"], dev["v"], dev["gate"], dev["beta"], None, **a),
+        "non-finite q")
+    h7 = dev["h0"].clone()
+    h7[1, 2, 3, 4] = float("inf")
+    bad(lambda: lin_attn_check_inputs(dev["q"], dev["k"], dev["v"], dev["gate"], dev["beta"], h7,
+                                      **a), "non-finite h0")
+    # several classes at once are all named
+    with pytest.raises(LinAttnError) as ei:
+        lin_attn_check_inputs(q6, dev["k"], dev["v"], dev["gate"], b5, h7, **a)
+    m = str(ei.value)
+    assert "non-finite q" in m and "beta outside" in m and "non-finite h0" in m
