@@ -22,6 +22,8 @@ SIGNATURES = {
     "lin_attn_chunk_fwd": (_I, [_P, _P, _P, _P, _I, _F, _P, _P, _P, _P,
                                 _I, _I, _I, _I, _I, _I, _P, _LL, _P]),
     "lin_attn_chunk_fwd_workspace_size": (_LL, [_I, _I, _I, _I, _I, _I]),
+    "lin_attn_chunk_fwd_noalloc": (_I, [_P, _P, _P, _P, _I, _F, _P, _P, _P, _P,
+                                        _I, _I, _I, _I, _I, _I, _P]),
     "lin_attn_chunk_fwd_raw": (_I, [_P, _P, _P, _P, _I, _F, _P, _P, _P, _P,
                                     _I, _I, _I, _I, _I, _I, _P, _LL, _P]),
     "lin_attn_chunk_fwd_channel": (_I, [_P, _P, _P, _P, _I, _F, _P, _P, _P, _P,

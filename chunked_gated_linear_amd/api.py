@@ -108,6 +108,33 @@ def lin_attn_chunk_fwd(q, k, v, gate, beta, h0=None, *, gate_mode="log", G=5.0,
     return o, hT
 
 
+def lin_attn_chunk_fwd_noalloc(q, k, v, gate, beta, h0=None, *, o, hT=None, gate_mode="log",
+                               G=5.0, stream=None):
+    """lin_attn_chunk_fwd without a workspace, for callers that cannot
+    allocate: the library's own 64 MiB scratch per GPU serves it, and this
+    wrapper allocates nothing either (o, and hT if wanted, come from the
+    caller).  Calls on one GPU must not overlap in time."""
+    _need(q, "q")
+    if q.dtype not in _DTYPES:
+        raise TypeError("q, k, v must be bfloat16 or float32")
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    _need(k, "k", q.dtype, (B, T, H, Dk))
+    _need(v, "v", q.dtype, (B, T, H, Dv))
+    _need(gate, "gate", torch.float32, (B, T, H))
+    _need(beta, "beta", torch.float32, (B, T, H))
+    if h0 is not None:
+        _need(h0, "h0", torch.float32, (B, H, Dk, Dv))
+    _need(o, "o", q.dtype, (B, T, H, Dv))
+    if hT is not None:
+        _need(hT, "hT", torch.float32, (B, H, Dk, Dv))
+    s = (stream if stream is not None else torch.cuda.current_stream(q.device)).cuda_stream
+    N.check(N.lib().lin_attn_chunk_fwd_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _GATE[gate_mode], float(G), _ptr(beta),
+        _ptr(h0), _ptr(o), _ptr(hT), B, T, H, Dk, Dv, _DTYPES[q.dtype], s))
+    return o, hT
+
+
 def lin_attn_chunk_fwd_channel_workspace_size(B, T, H, Dk, Dv, dtype=torch.bfloat16):
     """Workspace bytes lin_attn_chunk_fwd_channel needs for these sizes."""
     n = N.lib().lin_attn_chunk_fwd_channel_workspace_size(B, T, H, Dk, Dv, _DTYPES[dtype])

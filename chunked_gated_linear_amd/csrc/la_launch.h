@@ -125,6 +125,12 @@ hipError_t launch_range_check(const void* q, const void* k, const void* v, const
                               long long nqk, long long nv, long long ngate, long long nbeta,
                               long long nh0, int fp32, unsigned* flags, hipStream_t st);
 
+// Size of the library-owned scratch of lin_attn_chunk_fwd_noalloc (one copy
+// per GPU), and its device address on the current device, resolved with
+// hipGetSymbolAddress on first use per device.
+constexpr long long kNoAllocScratchBytes = 64ll << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 // hT <- h0 (or zeros when h0 is NULL), n floats.
 hipError_t launch_state_init(const float* h0, float* hT, long long n, hipStream_t st);
 

@@ -245,6 +245,25 @@ int lin_attn_chunk_fwd(const void* q, const void* k, const void* v, const float*
                    workspace, workspace_bytes, stream, 0);
 }
 
+int lin_attn_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const float* gate,
+                               int gate_mode, float G, const float* beta, const float* h0,
+                               void* o, float* hT, int B, int T, int H, int Dk, int Dv,
+                               int dtype, void* stream) {
+  if (int rc = check_chunk_sizes(B, T, H, Dk, Dv, dtype)) return rc;
+  const long long need = chunk_workspace(B, T, H, Dk, Dv, dtype);
+  if (need > la::kNoAllocScratchBytes)
+    return fail(LA_EINVAL,
+                "these sizes need %lld bytes of scratch; lin_attn_chunk_fwd_noalloc holds at "
+                "most %lld (use lin_attn_chunk_fwd with a workspace)",
+                need, la::kNoAllocScratchBytes);
+  void* scratch = nullptr;
+  if (need > 0 && B > 0 && H > 0) {
+    if (int rc = hip_status(la::noalloc_scratch(&scratch), "scratch address")) return rc;
+  }
+  return chunk_fwd(q, k, v, gate, gate_mode, G, beta, h0, o, hT, B, T, H, Dk, Dv, dtype,
+                   scratch, scratch ? la::kNoAllocScratchBytes : 0, stream, 0);
+}
+
 long long lin_attn_chunk_fwd_channel_workspace_size(int B, int T, int H, int Dk, int Dv,
                                                    int dtype) {
   if (check_chunk_sizes(B, T, H, Dk, Dv, dtype)) return -1;

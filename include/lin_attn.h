@@ -21,7 +21,8 @@
  * Conventions for every entry point
  *  - Every array pointer is a DEVICE pointer owned by the caller.  The library
  *    never frees, keeps or reallocates caller memory, and allocates no device
- *    memory of its own; scratch space comes in as a caller-owned workspace.
+ *    memory at run time; scratch space comes in as a caller-owned workspace
+ *    (lin_attn_chunk_fwd_noalloc alone uses a buffer the library holds).
  *  - Arrays are dense, row-major, last dimension contiguous, and aligned to
  *    their element size; arrays the kernels access as vectors need more: q, k
  *    and v of lin_attn_chunk_fwd 16 bytes, its o 8 bytes in bf16, and S of
@@ -37,8 +38,9 @@
  *  - Results are deterministic: the same inputs give bitwise-identical
  *    outputs on every call (no atomics in any reduction).
  *  - Calls may be made from several host threads; the library keeps no global
- *    mutable state besides the thread-local error text and a per-device cache
- *    of the compute-unit count (written once per device, read-only after).
+ *    mutable state besides the thread-local error text, a per-device cache
+ *    of the compute-unit count (written once per device, read-only after) and
+ *    the scratch buffer of lin_attn_chunk_fwd_noalloc.
  *  - Zero-size work (B, H or T equal to 0) is valid and enqueues nothing except
  *    that chunk_fwd with T = 0 copies h0 (or zeros) into hT.
  */
@@ -129,6 +131,27 @@ int lin_attn_chunk_fwd(const void* q, const void* k, const void* v,
                        int B, int T, int H, int Dk, int Dv, int dtype,
                        void* workspace, long long workspace_bytes,
                        void* stream);
+
+/*
+ * lin_attn_chunk_fwd_noalloc -- lin_attn_chunk_fwd for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same computation, arguments, rules
+ * and errors, without the workspace arguments.  The scratch comes from a
+ * buffer the library owns, 64 MiB per GPU (held from the library's load on
+ * that GPU until the process ends); sizes whose workspace
+ * (lin_attn_chunk_fwd_workspace_size) exceeds 64 MiB are rejected with
+ * LA_EINVAL.  Allocates nothing (no hipMalloc, hipFree or allocating library
+ * call).  Every call on one GPU shares that GPU's buffer and the buffer keeps
+ * the last call's contents (nothing in it needs to start at zero): calls that
+ * may overlap in time on the same GPU race, so serialise them, e.g. on one
+ * stream.
+ */
+int lin_attn_chunk_fwd_noalloc(const void* q, const void* k, const void* v,
+                               const float* gate, int gate_mode, float G,
+                               const float* beta, const float* h0,
+                               void* o, float* hT,
+                               int B, int T, int H, int Dk, int Dv, int dtype,
+                               void* stream);
 
 /*
  * lin_attn_chunk_fwd_raw -- lin_attn_chunk_fwd with the input preparation
