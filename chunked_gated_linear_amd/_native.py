@@ -26,6 +26,8 @@ SIGNATURES = {
                                         _I, _I, _I, _I, _I, _I, _P]),
     "lin_attn_chunk_fwd_raw": (_I, [_P, _P, _P, _P, _I, _F, _P, _P, _P, _P,
                                     _I, _I, _I, _I, _I, _I, _P, _LL, _P]),
+    "lin_attn_chunk_fwd_raw_affine": (_I, [_P, _P, _P, _P, _F, _P, _P, _P, _P, _P, _P,
+                                           _I, _I, _I, _I, _I, _I, _P, _LL, _P]),
     "lin_attn_chunk_fwd_channel": (_I, [_P, _P, _P, _P, _I, _F, _P, _P, _P, _P,
                                         _I, _I, _I, _I, _I, _I, _P, _LL, _P]),
     "lin_attn_chunk_fwd_channel_workspace_size": (_LL, [_I, _I, _I, _I, _I, _I]),
@@ -37,6 +39,8 @@ SIGNATURES = {
     "lin_attn_chunk_fwd_varlen_workspace_size": (_LL, [_I, _I, _I, _I, _I, _I]),
     "lin_attn_chunk_fwd_varlen_raw": (_I, [_P, _P, _P, _P, _I, _F, _P, _P, _P, _P, _P, _I,
                                            _I, _I, _I, _I, _I, _P, _LL, _P]),
+    "lin_attn_chunk_fwd_varlen_raw_affine": (_I, [_P, _P, _P, _P, _F, _P, _P, _P, _P, _P, _P,
+                                                  _P, _I, _I, _I, _I, _I, _I, _P, _LL, _P]),
     "lin_attn_chunk_bwd": (_I, [_P, _P, _P, _P, _I, _F, _P, _P, _P, _P,
                                 _P, _P, _P, _P, _P, _P,
                                 _I, _I, _I, _I, _I, _I, _P, _LL, _P]),

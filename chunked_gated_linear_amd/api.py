@@ -69,14 +69,16 @@ def lin_attn_chunk_fwd_workspace_size(B, T, H, Dk, Dv, dtype=torch.bfloat16):
 @_on_stream
 def lin_attn_chunk_fwd(q, k, v, gate, beta, h0=None, *, gate_mode="log", G=5.0,
                        o=None, hT=None, output_final_state=True, workspace=None,
-                       stream=None, raw=False):
+                       stream=None, raw=False, gate_scale=None, gate_bias=None):
     """o [B,T,H,Dv] and final state hT [B,H,Dk,Dv] (None if not requested).
 
     `workspace` is an optional uint8 GPU tensor of at least
     lin_attn_chunk_fwd_workspace_size(...) bytes; without one, a fresh tensor
     is taken from torch's caching allocator.  raw=True calls
     lin_attn_chunk_fwd_raw: q and k as they come (L2-normalised inside the
-    pass) and `beta` holding logits (bf16 only)."""
+    pass) and `beta` holding logits.  gate_scale / gate_bias (float32 [H],
+    with raw=True and gate_mode="logit") call lin_attn_chunk_fwd_raw_affine:
+    g = -G * sigmoid(gate_scale[h] * gate + gate_bias[h])."""
     _need(q, "q")
     if q.dtype not in _DTYPES:
         raise TypeError("q, k, v must be bfloat16 or float32")
@@ -100,12 +102,30 @@ def lin_attn_chunk_fwd(q, k, v, gate, beta, h0=None, *, gate_mode="log", G=5.0,
         workspace = torch.empty(nws, dtype=torch.uint8, device=q.device)
     if workspace is not None:
         _need(workspace, "workspace", torch.uint8)
+    if _affine(gate_scale, gate_bias, raw, gate_mode, H):
+        N.check(N.lib().lin_attn_chunk_fwd_raw_affine(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(gate), float(G), _ptr(gate_scale), _ptr(gate_bias),
+            _ptr(beta), _ptr(h0), _ptr(o), _ptr(hT), B, T, H, Dk, Dv, _DTYPES[q.dtype],
+            _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(q, stream)))
+        return o, hT
     fn = N.lib().lin_attn_chunk_fwd_raw if raw else N.lib().lin_attn_chunk_fwd
     N.check(fn(
         _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _GATE[gate_mode], float(G), _ptr(beta),
         _ptr(h0), _ptr(o), _ptr(hT), B, T, H, Dk, Dv, _DTYPES[q.dtype], _ptr(workspace),
         0 if workspace is None else workspace.numel(), _stream(q, stream)))
     return o, hT
+
+
+def _affine(gate_scale, gate_bias, raw, gate_mode, H):
+    """True when a per-head affine gate pre-activation is asked for (checked)."""
+    if gate_scale is None and gate_bias is None:
+        return False
+    if not raw or gate_mode != "logit":
+        raise ValueError("gate_scale / gate_bias need raw=True and gate_mode='logit'")
+    for t, nm in ((gate_scale, "gate_scale"), (gate_bias, "gate_bias")):
+        if t is not None:
+            _need(t, nm, torch.float32, (H,))
+    return True
 
 
 def lin_attn_chunk_fwd_noalloc(q, k, v, gate, beta, h0=None, *, o, hT=None, gate_mode="log",
@@ -345,12 +365,14 @@ def lin_attn_chunk_fwd_varlen_workspace_size(T, nseq, H, Dk, Dv, dtype=torch.bfl
 @_on_stream
 def lin_attn_chunk_fwd_varlen(q, k, v, gate, beta, cu_seqlens, h0=None, *, gate_mode="log",
                               G=5.0, o=None, hT=None, output_final_state=True,
-                              workspace=None, stream=None, raw=False):
+                              workspace=None, stream=None, raw=False, gate_scale=None,
+                              gate_bias=None):
     """Packed sequences: q, k [1,T,H,Dk], v [1,T,H,Dv], gate, beta [1,T,H] hold
     nseq sequences back to back, sequence s at tokens [cu[s], cu[s+1]) with
     cu_seqlens an int32 GPU tensor of nseq + 1 offsets.  Returns o [1,T,H,Dv]
     and the final states hT [nseq,H,Dk,Dv] (None if not requested).  raw=True:
-    q, k as they come and `beta` holding logits, as in lin_attn_chunk_fwd.
+    q, k as they come and `beta` holding logits, and gate_scale / gate_bias
+    (lin_attn_chunk_fwd_varlen_raw_affine), as in lin_attn_chunk_fwd.
     bf16 or float32 q, k, v; float32 needs no workspace."""
     _need(q, "q")
     _, T, H, Dk = q.shape
@@ -377,6 +399,13 @@ def lin_attn_chunk_fwd_varlen(q, k, v, gate, beta, cu_seqlens, h0=None, *, gate_
         workspace = torch.empty(nws, dtype=torch.uint8, device=q.device)
     if workspace is not None:
         _need(workspace, "workspace", torch.uint8)
+    if _affine(gate_scale, gate_bias, raw, gate_mode, H):
+        N.check(N.lib().lin_attn_chunk_fwd_varlen_raw_affine(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(gate), float(G), _ptr(gate_scale), _ptr(gate_bias),
+            _ptr(beta), _ptr(h0), _ptr(o), _ptr(hT), _ptr(cu_seqlens), nseq, T, H, Dk, Dv,
+            _DTYPES[q.dtype], _ptr(workspace), 0 if workspace is None else workspace.numel(),
+            _stream(q, stream)))
+        return o, hT
     fn = N.lib().lin_attn_chunk_fwd_varlen_raw if raw else N.lib().lin_attn_chunk_fwd_varlen
     N.check(fn(
         _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _GATE[gate_mode], float(G), _ptr(beta),

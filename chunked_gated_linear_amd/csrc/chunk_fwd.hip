@@ -101,7 +101,8 @@ __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ gate, int gate_logit, float G,
     const float* __restrict__ beta, const float* h0, E* __restrict__ o, float* hT,
-    int B, int TA, int H, int DV, const int* __restrict__ cu, int raw) {
+    int B, int TA, int H, int DV, const int* __restrict__ cu, int raw,
+    const float* __restrict__ gsc, const float* __restrict__ gbi) {
   using C = Cfg<E, DK, NP>;
   using X = Elt<E>;
   using F16 = typename X::F16;
@@ -113,6 +114,8 @@ __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_kernel(
   int head, vt;
   map_block(blockIdx.x, B * H, NV, head, vt);
   const int b = head / H, h = head % H;
+  // affine gate pre-activation (logit mode): logit = gsc[h] * x + gbi[h]
+  const float gsc_h = gsc ? gsc[h] : 1.f, gbi_h = gbi ? gbi[h] : 0.f;
   const int v0 = vt * 16;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -263,7 +266,7 @@ __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_kernel(
     char* rec = rec_of(c / NP, c % NP);
     // padding tokens past T: q = k = v = 0, g = 0, beta = 0 (an identity step)
     const bool ok = 16 * c + n < T;
-    const float g = ok ? (gate_logit ? bounded_gate(r.gx, G) : r.gx) : 0.f;
+    const float g = ok ? (gate_logit ? bounded_gate(fmaf(gsc_h, r.gx, gbi_h), G) : r.gx) : 0.f;
     // raw inputs: beta from its logit
     const float bt = ok ? (raw ? sigmoid_f(r.bt) : r.bt) : 0.f;
     F32 kf[NS], qf[NS];
@@ -422,33 +425,33 @@ template <typename E, int DK, int NP>
 static hipError_t launch_t(const void* q, const void* k, const void* v, const float* gate,
                            int gate_logit, float G, const float* beta, const float* h0,
                            void* o, float* hT, int B, int T, int H, int Dv, const int* cu,
-                           int raw, hipStream_t st) {
+                           int raw, hipStream_t st, const float* gsc, const float* gbi) {
   const int blocks = B * H * (Dv / 16);
   hipLaunchKernelGGL((chunk_fwd_kernel<E, DK, NP>), dim3(blocks), dim3(64 * (NP + 1)), 0, st,
                      (const E*)q, (const E*)k, (const E*)v, gate, gate_logit, G, beta, h0,
-                     (E*)o, hT, B, T, H, Dv, cu, raw);
+                     (E*)o, hT, B, T, H, Dv, cu, raw, gsc, gbi);
   return hipGetLastError();
 }
 
 hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v, const float* gate,
                             int gate_logit, float G, const float* beta, const float* h0,
                             void* o, float* hT, int B, int T, int H, int Dk, int Dv, int raw,
-                            hipStream_t st) {
+                            hipStream_t st, const float* gsc, const float* gbi) {
   return launch_chunk_fwd_varlen(q, k, v, gate, gate_logit, G, beta, h0, o, hT, nullptr, B, T, H,
-                                 Dk, Dv, raw, st);
+                                 Dk, Dv, raw, st, gsc, gbi);
 }
 
 hipError_t launch_chunk_fwd_varlen(const void* q, const void* k, const void* v,
                                    const float* gate, int gate_logit, float G,
                                    const float* beta, const float* h0, void* o, float* hT,
                                    const int* cu, int B, int T, int H, int Dk, int Dv, int raw,
-                                   hipStream_t st) {
+                                   hipStream_t st, const float* gsc, const float* gbi) {
   if (Dk == 64)
     return launch_t<float, 64, 2>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, cu,
-                                  raw, st);
+                                  raw, st, gsc, gbi);
   if (Dk == 128)
     return launch_t<float, 128, 2>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, cu,
-                                   raw, st);
+                                   raw, st, gsc, gbi);
   return hipErrorInvalidValue;
 }
 

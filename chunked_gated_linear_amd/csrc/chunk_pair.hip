@@ -176,6 +176,10 @@ struct PrepArgs {
   // workspace record slot(s, p) = floor(cu[s] / 32) + s + p of nslot per head.
   const int* cu;
   int nslot;
+  // Affine gate pre-activation (logit mode): the logit of head h is
+  // gsc[h] * x + gbi[h] (NULL: scale 1, shift 0).
+  const float* gsc;
+  const float* gbi;
 };
 
 // Token range of packed sequence s, clamped to [0, TB] (so that out-of-order
@@ -285,6 +289,11 @@ __device__ __forceinline__ void prep_body(char* smem, int64_t blk, const PrepArg
     gx[x] = gate[tok0 + (int64_t)t * H];
     bt[x] = beta[tok0 + (int64_t)t * H];
     if (pa.raw) bt[x] = sigmoid_f(bt[x]);
+  }
+  if (gate_logit && (pa.gsc || pa.gbi)) {
+    const float sc = pa.gsc ? pa.gsc[h] : 1.f, sh = pa.gbi ? pa.gbi[h] : 0.f;
+#pragma unroll
+    for (int x = 0; x < 2; ++x) gx[x] = fmaf(sc, gx[x], sh);
   }
 
   const int t0 = 32 * c;
@@ -939,7 +948,7 @@ template <int DK>
 static hipError_t launch_pair_t(const void* q, const void* k, const void* v, const float* gate,
                                 int gate_logit, float G, const float* beta, const float* h0,
                                 void* o, float* hT, int B, int T, int H, int Dv, int raw, void* ws,
-                                hipStream_t st) {
+                                hipStream_t st, const float* gsc, const float* gbi) {
   const int NSC = (T + 31) / 32;
   const int cus = device_cus();
   // two slices per workgroup when one per workgroup would take more than one
@@ -962,9 +971,12 @@ static hipError_t launch_pair_t(const void* q, const void* k, const void* v, con
     span(s, p0, p1);
     const int64_t t0 = 32 * (int64_t)p0;
     const int Ts = min(32 * p1, T) - 32 * p0;
-    return PrepArgs{(const __bf16*)q + t0 * H * DK, (const __bf16*)k + t0 * H * DK,
-                    gate + t0 * H, beta + t0 * H, wsb + (int64_t)B * H * p0 * WsRec::BYTES,
-                    gate_logit, G, B, Ts, T, H, raw};
+    PrepArgs a{(const __bf16*)q + t0 * H * DK, (const __bf16*)k + t0 * H * DK,
+               gate + t0 * H, beta + t0 * H, wsb + (int64_t)B * H * p0 * WsRec::BYTES,
+               gate_logit, G, B, Ts, T, H, raw};
+    a.gsc = gsc;
+    a.gbi = gbi;
+    return a;
   };
   auto prep_blocks = [&](int s) {
     int p0, p1;
@@ -1018,14 +1030,15 @@ template <int DK>
 static hipError_t launch_varlen_t(const void* q, const void* k, const void* v, const float* gate,
                                   int gate_logit, float G, const float* beta, const float* h0,
                                   void* o, float* hT, const int* cu, int nseq, int T, int H, int Dv,
-                                  int raw, void* ws, hipStream_t st) {
+                                  int raw, void* ws, hipStream_t st, const float* gsc,
+                                  const float* gbi) {
   const int nslot = varlen_slots(T, nseq);
   const int NV = Dv / 16;
   const int spw = (NV % 2 == 0 && (int64_t)nseq * H * NV > device_cus()) ? 2 : 1;
   const int nstate = nseq * H * (NV / spw);
   char* const wsb = static_cast<char*>(ws);
   const PrepArgs pa{(const __bf16*)q, (const __bf16*)k, gate, beta, wsb, gate_logit, G,
-                    nseq, 0, T, H, raw, cu, nslot};
+                    nseq, 0, T, H, raw, cu, nslot, gsc, gbi};
   const int64_t pblocks = ((int64_t)H * nslot + kPrepWaves - 1) / kPrepWaves;
   hipLaunchKernelGGL((chunk_prep_kernel<DK>), dim3((unsigned)pblocks), dim3(64 * kPrepWaves), 0,
                      st, pa);
@@ -1051,18 +1064,20 @@ hipError_t launch_chunk_fwd_pair_varlen(const void* q, const void* k, const void
                                         const float* gate, int gate_logit, float G,
                                         const float* beta, const float* h0, void* o, float* hT,
                                         const int* cu, int nseq, int T, int H, int Dk, int Dv,
-                                        int raw, void* ws, hipStream_t st) {
-  if (Dk == 64) return launch_varlen_t<64>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, cu, nseq, T, H, Dv, raw, ws, st);
-  if (Dk == 128) return launch_varlen_t<128>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, cu, nseq, T, H, Dv, raw, ws, st);
+                                        int raw, void* ws, hipStream_t st, const float* gsc,
+                                        const float* gbi) {
+  if (Dk == 64) return launch_varlen_t<64>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, cu, nseq, T, H, Dv, raw, ws, st, gsc, gbi);
+  if (Dk == 128) return launch_varlen_t<128>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, cu, nseq, T, H, Dv, raw, ws, st, gsc, gbi);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_chunk_fwd_pair(const void* q, const void* k, const void* v, const float* gate,
                                  int gate_logit, float G, const float* beta, const float* h0,
                                  void* o, float* hT, int B, int T, int H, int Dk, int Dv,
-                                 int raw, void* ws, hipStream_t st) {
-  if (Dk == 64) return launch_pair_t<64>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, raw, ws, st);
-  if (Dk == 128) return launch_pair_t<128>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, raw, ws, st);
+                                 int raw, void* ws, hipStream_t st, const float* gsc,
+                                 const float* gbi) {
+  if (Dk == 64) return launch_pair_t<64>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, raw, ws, st, gsc, gbi);
+  if (Dk == 128) return launch_pair_t<128>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, raw, ws, st, gsc, gbi);
   return hipErrorInvalidValue;
 }
 

@@ -7,11 +7,14 @@
 namespace la {
 
 // fp32 path: one fused kernel, no workspace.  raw != 0: q and k are
-// L2-normalised per token inside the pass and beta holds logits.
+// L2-normalised per token inside the pass and beta holds logits.  gsc, gbi
+// (the forward launchers, logit mode): per-head scale and shift of the gate
+// logit, NULL for 1 and 0.
 hipError_t launch_chunk_fwd(const void* q, const void* k, const void* v,
                             const float* gate, int gate_logit, float G,
                             const float* beta, const float* h0, void* o, float* hT,
-                            int B, int T, int H, int Dk, int Dv, int raw, hipStream_t st);
+                            int B, int T, int H, int Dk, int Dv, int raw, hipStream_t st,
+                            const float* gsc = nullptr, const float* gbi = nullptr);
 
 // The fp32 path over packed sequences: sequence s is tokens [cu[s], cu[s+1])
 // of one packed sequence of T tokens (cu: device array of nseq + 1 offsets).
@@ -19,7 +22,8 @@ hipError_t launch_chunk_fwd_varlen(const void* q, const void* k, const void* v,
                                    const float* gate, int gate_logit, float G,
                                    const float* beta, const float* h0, void* o, float* hT,
                                    const int* cu, int nseq, int T, int H, int Dk, int Dv,
-                                   int raw, hipStream_t st);
+                                   int raw, hipStream_t st, const float* gsc = nullptr,
+                                   const float* gbi = nullptr);
 
 // bf16 path: intra-tile kernel into the workspace, then the inter-tile kernel;
 // the state is carried across pairs of 16-token tiles.  raw != 0: q and k are
@@ -28,7 +32,8 @@ hipError_t launch_chunk_fwd_pair(const void* q, const void* k, const void* v,
                                  const float* gate, int gate_logit, float G,
                                  const float* beta, const float* h0, void* o, float* hT,
                                  int B, int T, int H, int Dk, int Dv, int raw, void* ws,
-                                 hipStream_t st);
+                                 hipStream_t st, const float* gsc = nullptr,
+                                 const float* gbi = nullptr);
 
 // Workspace bytes the bf16 path needs (0 when T == 0): one record per pair of
 // tiles and head, plus one fp32 state per head for sequences long enough to be
@@ -41,7 +46,8 @@ hipError_t launch_chunk_fwd_pair_varlen(const void* q, const void* k, const void
                                         const float* gate, int gate_logit, float G,
                                         const float* beta, const float* h0, void* o, float* hT,
                                         const int* cu, int nseq, int T, int H, int Dk, int Dv,
-                                        int raw, void* ws, hipStream_t st);
+                                        int raw, void* ws, hipStream_t st,
+                                        const float* gsc = nullptr, const float* gbi = nullptr);
 
 // Workspace bytes of the packed-sequence path: H * (T / 32 + nseq + 1) records.
 long long chunk_pair_varlen_workspace_bytes(int T, int nseq, int H);

@@ -91,6 +91,24 @@ int check_varlen_sizes(int T, int nseq, int H, int Dk, int Dv, int dtype) {
   return LA_OK;
 }
 
+// The per-head scale and shift of the gate logit (either may be NULL):
+// 4-byte aligned device arrays of H floats, disjoint from every output.
+int check_gate_affine(const float* gsc, const float* gbi, int H, const void* o, int64_t o_bytes,
+                      const float* hT, int64_t hT_bytes, const void* ws, int64_t ws_bytes) {
+  const struct { const char* nm; const float* p; } arr[] = {{"gate_scale", gsc},
+                                                           {"gate_bias", gbi}};
+  for (const auto& a : arr) {
+    if (!a.p) continue;
+    if (!aligned(a.p, 4u)) return fail(LA_EINVAL, "%s must be 4-byte aligned", a.nm);
+    const Span sa = span(a.nm, a.p, (int64_t)H * 4);
+    const Span outs[] = {span("o", o, o_bytes), span("hT", hT, hT_bytes),
+                         span("workspace", ws, ws_bytes)};
+    for (const Span& out : outs)
+      if (overlap(out, sa)) return fail(LA_EINVAL, "%s overlaps %s", out.name, a.nm);
+  }
+  return LA_OK;
+}
+
 long long chunk_workspace(int B, int T, int H, int Dk, int Dv, int dtype) {
   return dtype == LA_BF16 ? la::chunk_pair_workspace_bytes(B, T, H, Dk, Dv) : 0;
 }
@@ -163,7 +181,8 @@ namespace {
 int chunk_fwd(const void* q, const void* k, const void* v, const float* gate, int gate_mode,
               float G, const float* beta, const float* h0, void* o, float* hT, int B, int T,
               int H, int Dk, int Dv, int dtype, void* workspace, long long workspace_bytes,
-              void* stream, int raw, int channel = 0) {
+              void* stream, int raw, int channel = 0, const float* gsc = nullptr,
+              const float* gbi = nullptr) {
   if (int rc = check_chunk_sizes(B, T, H, Dk, Dv, dtype)) return rc;
   if (int rc = check_gate_scalars(gate_mode, G)) return rc;
   // per-channel gate: the in-tile operands reach exp(+-8 G); G <= 10 keeps
@@ -214,6 +233,9 @@ int chunk_fwd(const void* q, const void* k, const void* v, const float* gate, in
     if (overlap(shT, in)) return fail(LA_EINVAL, "hT overlaps %s", in.name);
   if (hT && h0 && hT != h0 && overlap(shT, sh0))
     return fail(LA_EINVAL, "hT partially overlaps h0 (only hT == h0 is allowed)");
+  if (int rc = check_gate_affine(gsc, gbi, H, o, T > 0 ? ntok * Dv * es : 0, hT, nst * 4,
+                                 workspace, wsz))
+    return rc;
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (T == 0) {
@@ -227,9 +249,10 @@ int chunk_fwd(const void* q, const void* k, const void* v, const float* gate, in
                                                    st),
                       "chunk_fwd_channel launch");
   hipError_t e = dtype == LA_FP32
-      ? la::launch_chunk_fwd(q, k, v, gate, logit, G, beta, h0, o, hT, B, T, H, Dk, Dv, raw, st)
+      ? la::launch_chunk_fwd(q, k, v, gate, logit, G, beta, h0, o, hT, B, T, H, Dk, Dv, raw, st,
+                             gsc, gbi)
       : la::launch_chunk_fwd_pair(q, k, v, gate, logit, G, beta, h0, o, hT, B, T, H, Dk, Dv,
-                                  raw, workspace, st);
+                                  raw, workspace, st, gsc, gbi);
   return hip_status(e, "chunk_fwd launch");
 }
 
@@ -288,6 +311,16 @@ int lin_attn_chunk_fwd_raw(const void* q, const void* k, const void* v, const fl
                    workspace, workspace_bytes, stream, 1);
 }
 
+int lin_attn_chunk_fwd_raw_affine(const void* q, const void* k, const void* v,
+                                  const float* gate_x, float G, const float* gate_scale,
+                                  const float* gate_bias, const float* beta_logit,
+                                  const float* h0, void* o, float* hT, int B, int T, int H,
+                                  int Dk, int Dv, int dtype, void* workspace,
+                                  long long workspace_bytes, void* stream) {
+  return chunk_fwd(q, k, v, gate_x, LA_GATE_BOUNDED_LOGIT, G, beta_logit, h0, o, hT, B, T, H, Dk,
+                   Dv, dtype, workspace, workspace_bytes, stream, 1, 0, gate_scale, gate_bias);
+}
+
 long long lin_attn_chunk_fwd_varlen_workspace_size(int T, int nseq, int H, int Dk, int Dv,
                                                    int dtype) {
   if (check_varlen_sizes(T, nseq, H, Dk, Dv, dtype)) return -1;
@@ -305,7 +338,7 @@ int chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* g
                      int gate_mode, float G, const float* beta, const float* h0, void* o,
                      float* hT, const int* cu_seqlens, int nseq, int T, int H, int Dk, int Dv,
                      int dtype, void* workspace, long long workspace_bytes, void* stream,
-                     int raw) {
+                     int raw, const float* gsc = nullptr, const float* gbi = nullptr) {
   if (int rc = check_varlen_sizes(T, nseq, H, Dk, Dv, dtype)) return rc;
   if (int rc = check_gate_scalars(gate_mode, G)) return rc;
   // the fp32 path needs no workspace
@@ -348,14 +381,17 @@ int chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* g
     if (overlap(shT, in)) return fail(LA_EINVAL, "hT overlaps %s", in.name);
   if (hT && h0 && hT != h0 && overlap(shT, sh0))
     return fail(LA_EINVAL, "hT partially overlaps h0 (only hT == h0 is allowed)");
+  if (int rc = check_gate_affine(gsc, gbi, H, o, ntok * Dv * es, hT, nst * 4, workspace, wsz))
+    return rc;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipError_t e =
       dtype == LA_BF16
           ? la::launch_chunk_fwd_pair_varlen(q, k, v, gate, gate_mode == LA_GATE_BOUNDED_LOGIT, G,
                                              beta, h0, o, hT, cu_seqlens, nseq, T, H, Dk, Dv, raw,
-                                             workspace, st)
+                                             workspace, st, gsc, gbi)
           : la::launch_chunk_fwd_varlen(q, k, v, gate, gate_mode == LA_GATE_BOUNDED_LOGIT, G, beta,
-                                        h0, o, hT, cu_seqlens, nseq, T, H, Dk, Dv, raw, st);
+                                        h0, o, hT, cu_seqlens, nseq, T, H, Dk, Dv, raw, st, gsc,
+                                        gbi);
   return hip_status(e, "chunk_fwd_varlen launch");
 }
 
@@ -465,6 +501,18 @@ int lin_attn_chunk_fwd_varlen_raw(const void* q, const void* k, const void* v, c
                                   void* workspace, long long workspace_bytes, void* stream) {
   return chunk_fwd_varlen(q, k, v, gate, gate_mode, G, beta_logit, h0, o, hT, cu_seqlens, nseq,
                           T, H, Dk, Dv, dtype, workspace, workspace_bytes, stream, 1);
+}
+
+int lin_attn_chunk_fwd_varlen_raw_affine(const void* q, const void* k, const void* v,
+                                         const float* gate_x, float G, const float* gate_scale,
+                                         const float* gate_bias, const float* beta_logit,
+                                         const float* h0, void* o, float* hT,
+                                         const int* cu_seqlens, int nseq, int T, int H, int Dk,
+                                         int Dv, int dtype, void* workspace,
+                                         long long workspace_bytes, void* stream) {
+  return chunk_fwd_varlen(q, k, v, gate_x, LA_GATE_BOUNDED_LOGIT, G, beta_logit, h0, o, hT,
+                          cu_seqlens, nseq, T, H, Dk, Dv, dtype, workspace, workspace_bytes,
+                          stream, 1, gate_scale, gate_bias);
 }
 
 }  // extern "C"

@@ -175,6 +175,34 @@ int lin_attn_chunk_fwd_raw(const void* q, const void* k, const void* v,
                            void* stream);
 
 /*
+ * lin_attn_chunk_fwd_raw_affine -- lin_attn_chunk_fwd_raw with the gate's
+ * per-head affine pre-activation fused in: gate_x holds x_t [B, T, H] float32
+ * and
+ *
+ *     g_t = -G * sigmoid(a_h * x_t + b_h)
+ *
+ * with a = gate_scale[h], b = gate_bias[h] (device arrays of H float32, 4-byte
+ * aligned; NULL stands for a = 1, resp. b = 0, and both NULL is
+ * lin_attn_chunk_fwd_raw in LA_GATE_BOUNDED_LOGIT mode).  The pages write the
+ * bounded decay as a sigmoid of an affine function of the layer's input,
+ * scaled by the bound ("Evaluating Next-Gen ...", sec. 2 item 3; "Core
+ * Technologies ...", sec. 2.2); a and b scale and shift the logit of each
+ * head, so that a caller holding x needs no separate pass over it.  The
+ * affine map and the sigmoid are evaluated in float32 inside the intra-tile
+ * kernel.  Arguments, layouts, workspace (lin_attn_chunk_fwd_workspace_size),
+ * rules and errors as lin_attn_chunk_fwd_raw; LA_EINVAL also when gate_scale
+ * or gate_bias is misaligned or overlaps o, hT or the workspace.  Non-finite
+ * a or b give what the formula gives (a NaN logit gives a NaN decay).
+ */
+int lin_attn_chunk_fwd_raw_affine(const void* q, const void* k, const void* v,
+                                  const float* gate_x, float G, const float* gate_scale,
+                                  const float* gate_bias, const float* beta_logit,
+                                  const float* h0, void* o, float* hT,
+                                  int B, int T, int H, int Dk, int Dv, int dtype,
+                                  void* workspace, long long workspace_bytes,
+                                  void* stream);
+
+/*
  * lin_attn_chunk_fwd_channel -- lin_attn_chunk_fwd with one log-decay per key
  * channel: gate is [B, T, H, Dk] float32 (16-byte aligned), g_t[c] in [-G, 0]
  * (LA_GATE_LOG) or g_t[c] = -G * sigmoid(x_t[c]) (LA_GATE_BOUNDED_LOGIT).
@@ -273,6 +301,22 @@ int lin_attn_chunk_fwd_varlen_raw(const void* q, const void* k, const void* v,
                                   int T, int H, int Dk, int Dv, int dtype,
                                   void* workspace, long long workspace_bytes,
                                   void* stream);
+
+/*
+ * lin_attn_chunk_fwd_varlen_raw_affine -- lin_attn_chunk_fwd_varlen_raw with
+ * the gate of lin_attn_chunk_fwd_raw_affine: gate_x [T, H] holds x_t and
+ * g_t = -G * sigmoid(gate_scale[h] * x_t + gate_bias[h]).  Arguments,
+ * workspace, rules and errors as lin_attn_chunk_fwd_varlen_raw and
+ * lin_attn_chunk_fwd_raw_affine.
+ */
+int lin_attn_chunk_fwd_varlen_raw_affine(const void* q, const void* k, const void* v,
+                                         const float* gate_x, float G,
+                                         const float* gate_scale, const float* gate_bias,
+                                         const float* beta_logit, const float* h0,
+                                         void* o, float* hT, const int* cu_seqlens, int nseq,
+                                         int T, int H, int Dk, int Dv, int dtype,
+                                         void* workspace, long long workspace_bytes,
+                                         void* stream);
 
 /*
  * lin_attn_decode_step -- one new token per (b, h), state updated in place.

@@ -44,6 +44,10 @@ Functions and their pins (the tests that tie each to something other than
 itself are in tests/test_oracle.py):
   bounded_gate     values printed on the pages (exp(-5) ~ 0.0067, exp(5) ~ 148,
                    g in [-5, 0]) and the sigmoid reflection identity.
+  bounded_gate_affine
+                   closed forms at x = 0 (g = -G sigmoid(b)) and at a scaled
+                   logit (sigmoid(ln 3) = 3/4), the reflection a, b -> -a, -b,
+                   and per-head broadcast checked head by head.
   recurrent_fwd    a hand-worked example, a pure-Python brute force in the
                    S orientation, closed forms (pure decay, orthogonal keys =
                    masked gated linear attention), invariants (identity step,
@@ -140,6 +144,18 @@ def sigmoid(x):
 def bounded_gate(x, G: float = 5.0):
     """g = -G * sigmoid(x), the scaled-sigmoid log-decay ([DD] 3.3, [CT] 2.2)."""
     return -float(G) * sigmoid(x)
+
+
+def bounded_gate_affine(x, a=None, b=None, G: float = 5.0):
+    """g = -G * sigmoid(a_h * x + b_h): the bounded log-decay of an affine
+    function of the input ([EV] 2 item 3, [CT] 2.2), with one scale a_h and one
+    shift b_h per head.  x has heads on its last axis; a and b are [H] arrays
+    (None: a = 1, b = 0)."""
+    x = _f64(x)
+    H = x.shape[-1]
+    a = np.ones(H) if a is None else _f64(a).reshape(H)
+    b = np.zeros(H) if b is None else _f64(b).reshape(H)
+    return bounded_gate(a * x + b, G)
 
 
 # ----------------------------------------------------------------------------

@@ -252,6 +252,30 @@ def test_raw_entry_checks():
     assert "workspace too small" in L.lin_attn_last_error().decode()
 
 
+def test_raw_affine_entry_checks():
+    """The affine-gate entry points check their extra arrays on the host
+    before anything touches the device."""
+    L = N.lib()
+    f = L.lin_attn_chunk_fwd_raw_affine
+    args = lambda sc, bi, G=5.0: [fake(0), fake(1), fake(2), fake(3), G, sc, bi, fake(4), None,
+                                  fake(5), fake(6), 1, 64, 2, 128, 128, N.LA_BF16, fake(8),
+                                  1 << 30, None]
+    misaligned = ctypes.c_void_p(fake(9) + 2)
+    assert f(*args(misaligned, None)) == N.LA_EINVAL
+    assert "gate_scale must be 4-byte aligned" in L.lin_attn_last_error().decode()
+    assert f(*args(None, misaligned)) == N.LA_EINVAL
+    assert "gate_bias must be 4-byte aligned" in L.lin_attn_last_error().decode()
+    # an output that overlaps the scale array
+    assert f(*args(ctypes.c_void_p(fake(5) + 64), None)) == N.LA_EINVAL
+    assert "o overlaps gate_scale" in L.lin_attn_last_error().decode()
+    assert f(*args(None, None, G=-1.0)) == N.LA_ERANGE
+    fv = L.lin_attn_chunk_fwd_varlen_raw_affine
+    cu = fake(10)
+    assert fv(fake(0), fake(1), fake(2), fake(3), 5.0, misaligned, None, fake(4), None, fake(5),
+              fake(6), cu, 2, 64, 2, 128, 128, N.LA_BF16, fake(8), 1 << 30, None) == N.LA_EINVAL
+    assert "gate_scale must be 4-byte aligned" in L.lin_attn_last_error().decode()
+
+
 def bwd(**kw):
     a = dict(q=fake(0), k=fake(1), v=fake(2), gate=fake(3), gate_mode=0, G=5.0,
              beta=fake(4), h0=None, dout=fake(5), dhT=None, dq=fake(6), dk=fake(7),

@@ -97,6 +97,57 @@ def test_gate_reflection_identity():
                                    -G, rtol=0, atol=1e-13)
 
 
+def test_gate_affine_closed_forms():
+    # x = 0: g = -G sigmoid(b); sigmoid(ln 3) = 3/4 exactly, so b = ln 3 gives
+    # -3G/4 and a scale a = 2 at x = ln(3) / 2 gives the same logit
+    G = 5.0
+    a = np.array([2.0, -0.5, 3.0])
+    b = np.array([math.log(3.0), 0.0, -math.log(3.0)])
+    g0 = orc.bounded_gate_affine(np.zeros((1, 2, 3)), a, b, G)
+    np.testing.assert_allclose(g0[0, 0], [-0.75 * G, -0.5 * G, -0.25 * G], rtol=0, atol=1e-14)
+    x = np.full((1, 1, 3), math.log(3.0) / 2)
+    np.testing.assert_allclose(orc.bounded_gate_affine(x, [2.0, 2.0, 2.0], None, G)[0, 0],
+                               -0.75 * G, rtol=0, atol=1e-14)
+    # both None is the plain bounded gate
+    xr = RNG.standard_normal((2, 5, 3)) * 4
+    np.testing.assert_array_equal(orc.bounded_gate_affine(xr, None, None, G), orc.bounded_gate(xr, G))
+
+
+def test_gate_affine_reflection_and_heads():
+    # sigmoid(z) + sigmoid(-z) = 1: flipping a and b gives -G - g
+    G = 5.0
+    x = RNG.standard_normal((2, 7, 4)) * 6
+    a, b = RNG.standard_normal(4) * 2, RNG.standard_normal(4) * 3
+    np.testing.assert_allclose(orc.bounded_gate_affine(x, a, b, G) + orc.bounded_gate_affine(x, -a, -b, G),
+                               -G, rtol=0, atol=1e-13)
+    # head h uses a[h], b[h] at every token and batch (T != H, so a broadcast
+    # over the wrong axis cannot pass)
+    g = orc.bounded_gate_affine(x, a, b, G)
+    for h in range(4):
+        for bb in range(2):
+            for t in range(7):
+                z = a[h] * x[bb, t, h] + b[h]
+                assert abs(g[bb, t, h] - (-G / (1.0 + math.exp(-z)))) <= 1e-13
+
+
+def test_gate_affine_mutants_are_caught():
+    G = 5.0
+    a, b = np.array([2.0]), np.array([math.log(3.0)])
+    x0, x1 = np.zeros((1, 1, 1)), np.full((1, 1, 1), -math.log(3.0))
+    wrong = {
+        "swapped": lambda x: orc.bounded_gate(b * x + a, G),
+        "scale_outside": lambda x: a * orc.bounded_gate(x + b, G),
+        "shift_outside": lambda x: orc.bounded_gate(a * x, G) + b,
+        "shift_sign": lambda x: orc.bounded_gate(a * x - b, G),
+    }
+    for name, f in wrong.items():
+        # the right gate: -3G/4 at x = 0 and -G sigmoid(-ln 3) = -G/4 at x = -ln 3
+        good = (abs(f(x0).item() + 0.75 * G) < 1e-12 and abs(f(x1).item() + 0.25 * G) < 1e-12)
+        assert not good, name
+    assert abs(orc.bounded_gate_affine(x0, a, b, G).item() + 0.75 * G) < 1e-12
+    assert abs(orc.bounded_gate_affine(x1, a, b, G).item() + 0.25 * G) < 1e-12
+
+
 # --------------------------------------------------------------- the pins
 def pin_hand_example(fwd, golden_dir):
     ex = _read_kv(os.path.join(golden_dir, "hand_example.txt"))

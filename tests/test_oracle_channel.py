@@ -13,6 +13,8 @@ plausible mistakes in copies of the recurrence and checks that each fails at
 least one pin.
 """
 
+import math
+
 import numpy as np
 import pytest
 
@@ -158,6 +160,70 @@ def test_in_tile_reciprocal_stays_finite_at_the_bound():
     ro, rh = orc.recurrent_fwd_channel(q, k, v, g, beta, h0)
     assert np.isfinite(co).all() and np.isfinite(ch).all()
     assert np.abs(co - ro).max() <= 1e-10 * max(1.0, np.abs(ro).max())
+
+
+def _tile_operands_f32(k, g, chunk=16):
+    """The per-channel in-tile operands in float32, tile by tile: keys scaled
+    by the cumulative decay Gam_t and keys divided by it (Gam_s^-1), and their
+    products A[t, s] = (k_t o Gam_t) . (k_s / Gam_s), s < t.  Returns the
+    largest |log| of 1/Gam in any tile and whether every operand and product
+    is finite."""
+    k32, g32 = np.asarray(k, np.float32), np.asarray(g, np.float32)
+    B, T, H, Dk = k32.shape
+    worst, finite = 0.0, True
+    with np.errstate(over="ignore", invalid="ignore"):
+        for c0 in range(0, T, chunk):
+            Gc = np.cumsum(g32[:, c0:c0 + chunk], axis=1, dtype=np.float32)
+            worst = max(worst, float(-Gc.min()))
+            inv = np.exp(-Gc)
+            kg, ki = k32[:, c0:c0 + chunk] * np.exp(Gc), k32[:, c0:c0 + chunk] * inv
+            A = np.einsum("bthc,bshc->bhts", kg, ki)
+            finite &= bool(np.isfinite(inv).all() and np.isfinite(ki).all() and np.isfinite(A).all())
+    return worst, finite
+
+
+def test_softplus_contrast_overflows_where_the_bound_stays_finite():
+    """The pages bound the log-decay so that inside a 16-token tile the
+    reciprocal of the cumulative decay stays finite ("Deep Dive ...", sec. 3.2
+    and 3.3; "How Trillion-Scale ...", sec. 3.2).  Contrast: the same logits
+    x ~ N(mu, 1) through g = -softplus(x) (unbounded below) and through
+    g = -5 sigmoid(x).  A tile's operand 1/Gam reaches exp(-sum g); float32
+    overflows past ln(FLT_MAX) ~ 88.72, i.e. a mean decay above ~5.55 per
+    token over 16 tokens -- just beyond the bound's 16 * 5 = 80."""
+    ln_max = math.log(float(np.finfo(np.float32).max))
+    assert 16 * 5.0 < ln_max < 16 * 5.6
+    rng = np.random.default_rng(23)
+    k = rng.standard_normal((1, 128, 2, 16))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    seen = {}
+    for mu in (0.0, 2.0, 4.0, 6.0, 8.0):
+        x = mu + rng.standard_normal((1, 128, 2, 16))
+        sp_worst, sp_finite = _tile_operands_f32(k, -np.logaddexp(0.0, x))
+        bd_worst, bd_finite = _tile_operands_f32(k, orc.bounded_gate(x, 5.0))
+        seen[mu] = (sp_worst, sp_finite, bd_worst, bd_finite)
+        # the bound: finite at every shift, never beyond exp(80)
+        assert bd_finite and bd_worst <= 80.0 + 1e-3, (mu, bd_worst)
+        # -softplus: finite exactly while every tile's summed decay stays below
+        # ln(FLT_MAX) (a margin of 1 for float32 rounding of the sums)
+        if sp_worst < ln_max - 1.0:
+            assert sp_finite, (mu, sp_worst)
+        if sp_worst > ln_max + 1.0:
+            assert not sp_finite, (mu, sp_worst)
+    # the contrast itself: small shifts are fine both ways, large ones
+    # overflow without the bound
+    assert seen[0.0][1] and seen[2.0][1]
+    assert not seen[6.0][1] and not seen[8.0][1]
+    # with the bound the float32 tile products agree with fp64 ones
+    x = 8.0 + rng.standard_normal((1, 32, 2, 16))
+    g = orc.bounded_gate(x, 5.0)
+    Gc = np.cumsum(g[:, :16], axis=1)
+    A64 = np.einsum("bthc,bshc->bhts", k[:, :16] * np.exp(Gc), k[:, :16] * np.exp(-Gc))
+    Gc32 = np.cumsum(g[:, :16].astype(np.float32), axis=1, dtype=np.float32)
+    k32 = k[:, :16].astype(np.float32)
+    A32 = np.einsum("bthc,bshc->bhts", k32 * np.exp(Gc32), k32 * np.exp(-Gc32))
+    low = np.tril(np.ones((16, 16)), -1).astype(bool)
+    rel = np.abs(A32 - A64)[..., low] / np.maximum(np.abs(A64)[..., low], 1e-30)
+    assert np.isfinite(A32).all() and np.median(rel) < 1e-4
 
 
 # ------------------------------------------------------- planted mistakes

@@ -446,6 +446,74 @@ def test_varlen_raw_inputs_fp32():
     check(name, "fp32", o, hT, ref_o, ref_h)
 
 
+# ------------------------------------ affine gate pre-activation (fused prep)
+AFFINE = [
+    # B, H, T, Dk, Dv, dtype, regime
+    (2, 3, 1013, 128, 128, "bf16", "std"),
+    (1, 4, 20000, 128, 128, "bf16", "weak"),     # stretched
+    (1, 2, 333, 64, 64, "fp32", "weak"),
+]
+
+
+def _affine_params(H, seed):
+    gen = torch.Generator(device="cuda").manual_seed(seed)
+    a = 0.5 + 1.5 * torch.rand(H, generator=gen, device="cuda")
+    a[0] = -a[0]                                  # a negative scale flips the gate
+    b = 1.5 * torch.randn(H, generator=gen, device="cuda")
+    return a, b
+
+
+@pytest.mark.parametrize("case", AFFINE, ids=lambda c: "-".join(map(str, c)))
+def test_raw_affine_gate(case):
+    """g = -G sigmoid(a_h x + b_h) fused into the raw entry point: against the
+    oracle on the fp64-prepared inputs and the fp64 affine gate."""
+    B, H, T, Dk, Dv, dt, regime = case
+    name = f"raw affine B{B} H{H} T{T} dk{Dk} dv{Dv} {dt} {regime}"
+    say(name)
+    dev, hst = make_case(B, T, H, Dk, Dv, dt, regime, "logit", 0.02, seed=71)
+    gen = torch.Generator(device="cuda").manual_seed(72)
+    xb = torch.randn((B, T, H), generator=gen, device="cuda")
+    a, b = _affine_params(H, 73)
+    o, hT = lin_attn_chunk_fwd(dev["q"], dev["k"], dev["v"], dev["gate"], xb, dev["h0"],
+                               gate_mode="logit", raw=True, gate_scale=a, gate_bias=b)
+    torch.cuda.synchronize()
+    q_h, k_h, v_h, _, _, h0_h = hst
+    qn, kn, beta = orc.prepare_inputs(q_h, k_h, host(xb))
+    g = orc.bounded_gate_affine(host(dev["gate"]), host(a), host(b), 5.0)
+    ref_o, ref_h = crec.recurrent_fwd(qn, kn, v_h, g, beta, h0_h)
+    check(name, dt, o, hT, ref_o, ref_h)
+
+
+def test_raw_affine_gate_identity_and_varlen():
+    """Scale 1 and shift 0 (as arrays, or either one NULL) reproduce the raw
+    entry point bitwise; packed sequences take the head's a and b."""
+    B, H, T, D = 1, 3, 700, 128
+    name = f"raw affine identity + varlen H{H} T{T} d{D} bf16"
+    say(name)
+    dev, hst = make_case(B, T, H, D, D, "bf16", "weak", "logit", None, seed=81)
+    gen = torch.Generator(device="cuda").manual_seed(82)
+    xb = torch.randn((B, T, H), generator=gen, device="cuda")
+    o0, h0_ = lin_attn_chunk_fwd(dev["q"], dev["k"], dev["v"], dev["gate"], xb, gate_mode="logit",
+                                 raw=True)
+    ones, zeros = torch.ones(H, device="cuda"), torch.zeros(H, device="cuda")
+    for sc, bi in ((ones, zeros), (ones, None), (None, zeros)):
+        o1, h1 = lin_attn_chunk_fwd(dev["q"], dev["k"], dev["v"], dev["gate"], xb,
+                                    gate_mode="logit", raw=True, gate_scale=sc, gate_bias=bi)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o0) and torch.equal(h1, h0_)
+    lengths = [0, 5, 200, 495]
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int32, device="cuda")
+    a, b = _affine_params(H, 83)
+    o, hT = lin_attn_chunk_fwd_varlen(dev["q"], dev["k"], dev["v"], dev["gate"], xb, cu,
+                                      gate_mode="logit", raw=True, gate_scale=a, gate_bias=b)
+    torch.cuda.synchronize()
+    q_h, k_h, v_h, _, _, _ = hst
+    qn, kn, beta = orc.prepare_inputs(q_h, k_h, host(xb))
+    g = orc.bounded_gate_affine(host(dev["gate"]), host(a), host(b), 5.0)
+    ref_o, ref_h = crec.recurrent_fwd_varlen(qn, kn, v_h, g, beta, cu.cpu().numpy(), None)
+    check(name, "bf16", o, hT, ref_o, ref_h)
+
+
 def test_graph_capture_replays():
     """The forward (stretched: several launches) and decode steps captured in
     one graph replay to the eager results, replay after replay, with eager
