@@ -1,0 +1,1167 @@
+// chunk_bwd_bf16.hip -- the reverse pass for bf16 q, k, v and dout on the bf16
+// matrix cores, with the forward states and the state gradients kept only at
+// every kGS-th tile.
+//
+// Same algebra as chunk_bwd.hip (the adjoint of the tiled forward form; the
+// pages -- "Deep Dive: The Next Generation of Ultra-Long Context Sparse MoE
+// LLMs", sec. 3.2, and "Core Technologies Behind Ultra-Long-Context Sparse MoE
+// Large Models", sec. 2.1 and 2.3 -- give the tiled forward pass and frame the
+// bounded decay around BF16 training, and print no backward pass).  What
+// differs is where the work runs and what goes through memory:
+//
+//  * Products.  q, k, v and dout are bf16, so they enter the bf16 MFMA
+//    exactly.  Every float32 operand X (the state H, its gradient D, T, P, Y,
+//    U, dU, dY and their scaled forms) is split into bf16 parts X = X_hi +
+//    X_lo + e with |e| <= 2^-16 |X|, and a product of two split operands keeps
+//    the three terms hi.hi + lo.hi + hi.lo; a product with an exact bf16
+//    operand keeps both parts.  A 16-deep contraction runs as 32-deep MFMAs:
+//    [X, X] . [Y_hi ; Y_lo] with one split operand, [X_hi | X_lo] . [Y_hi ;
+//    Y_hi] then [X_hi | X_lo] . [Y_lo ; 0] with two.
+//    Accumulation is float32 throughout and the state and state gradient are
+//    carried in float32.
+//  * Checkpoints.  The state chain stores H only at the start of every group
+//    of kGS tiles and the gradient chain stores D = dL/dH' only at the end of
+//    every group, each as packed (hi, lo) bf16 words (4 bytes per element,
+//    the float32 size).  The gradient kernel takes one group per workgroup and
+//    walks its tiles backwards: it rebuilds H at the start of tile j by
+//    stepping the forward recurrence j times from the group's checkpoint, and
+//    carries D backwards tile by tile,
+//        D_{j-1} = gamma_C D_j + Q^T diag(gamma) dO - K^T diag(beta gamma) dY,
+//    from the group's stored end.  A quarter of the state traffic of storing
+//    both at every tile, for 1.5 extra forward steps per tile.
+//
+// Three kernels after the shared per-tile preparation (la_bwd.h):
+//   bwd2_hstates_kernel  per (sequence, head, SPW slices of 16 columns of
+//                        d_v), serial over tiles: H at every group start;
+//   bwd2_dh_kernel       same split, serial backwards: D at every group end,
+//                        and dh0;
+//   bwd2_grad_kernel     per group of kGS tiles, all of d_v (one 16-column
+//                        slice per wave): dq, dk, dv, dbeta, dg.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "la_bwd.h"
+#include "la_device.h"
+#include "la_launch.h"
+
+namespace la {
+namespace {
+
+constexpr int kGS = 4;          // tiles per checkpoint group
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+
+// ------------------------------------------------------------- helpers
+__device__ inline bf16x4 hi4(f32x4 x) {
+  return bf16x4{(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
+}
+__device__ inline bf16x4 lo4(f32x4 x, bf16x4 h) {
+  return bf16x4{(__bf16)(x[0] - (float)h[0]), (__bf16)(x[1] - (float)h[1]),
+                (__bf16)(x[2] - (float)h[2]), (__bf16)(x[3] - (float)h[3])};
+}
+__device__ inline bf16x8 cat8(bf16x4 a, bf16x4 b) {
+  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+__device__ inline bf16x4 first4(bf16x8 a) { return bf16x4{a[0], a[1], a[2], a[3]}; }
+__device__ inline bf16x4 second4(bf16x8 a) { return bf16x4{a[4], a[5], a[6], a[7]}; }
+__device__ inline f32x4 mma32b(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// [A_hi | A_lo] . [B_lo ; 0] = A_hi B_lo: the third term of a split-by-split
+// 16-deep product, as a 32-deep MFMA with a zero half.  Every product here is
+// a 16x16x32 MFMA: a 16x16x16 one reading, as its accumulator, the result of a
+// 16x16x32 MFMA issued just before came out wrong in accumulator registers 0
+// and 1 in this build (the instructions between them did not cover the
+// dependency).
+__device__ inline f32x4 mma32b_lo(bf16x8 a, bf16x4 blo, f32x4 c) {
+  return mma32b(a, cat8(blo, bf16x4{(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f}), c);
+}
+__device__ inline f32x4 to_f4(bf16x4 x) {
+  return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+}
+
+// A float32 fragment as bf16 hi + lo parts.
+struct Sp4 {
+  bf16x4 h, l;
+};
+__device__ inline Sp4 split4(f32x4 x) {
+  Sp4 r;
+  r.h = hi4(x);
+  r.l = lo4(x, r.h);
+  return r;
+}
+
+// Packed checkpoint words: element = bf16 hi in bits 0..15, bf16 lo in 16..31.
+__device__ inline uint4 pack_words(bf16x4 h, bf16x4 l) {
+  const s16x4 hs = __builtin_bit_cast(s16x4, h), ls = __builtin_bit_cast(s16x4, l);
+  uint4 w;
+  w.x = (unsigned)(unsigned short)hs[0] | ((unsigned)(unsigned short)ls[0] << 16);
+  w.y = (unsigned)(unsigned short)hs[1] | ((unsigned)(unsigned short)ls[1] << 16);
+  w.z = (unsigned)(unsigned short)hs[2] | ((unsigned)(unsigned short)ls[2] << 16);
+  w.w = (unsigned)(unsigned short)hs[3] | ((unsigned)(unsigned short)ls[3] << 16);
+  return w;
+}
+__device__ inline float word_f(unsigned w) {
+  return __uint_as_float(w << 16) + __uint_as_float(w & 0xffff0000u);
+}
+__device__ inline f32x4 words_f4(uint4 w) {
+  return f32x4{word_f(w.x), word_f(w.y), word_f(w.z), word_f(w.w)};
+}
+
+// Packed words -> the bf16 hi and lo parts of four elements.
+__device__ inline void words_split(uint4 w, bf16x4& h, bf16x4& l) {
+  const unsigned h01 = (w.x & 0xffffu) | (w.y << 16), h23 = (w.z & 0xffffu) | (w.w << 16);
+  const unsigned l01 = (w.x >> 16) | (w.y & 0xffff0000u), l23 = (w.z >> 16) | (w.w & 0xffff0000u);
+  h = __builtin_bit_cast(bf16x4, uint2{h01, h23});
+  l = __builtin_bit_cast(bf16x4, uint2{l01, l23});
+}
+// The split fragments of a state stored as packed words (tile t at w[t]).
+template <int NS>
+__device__ inline void words_state(const uint4* w, int stride, bf16x8* sh, bf16x8* sl) {
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    bf16x4 ah, al, bh, bl;
+    words_split(w[(2 * s) * stride], ah, al);
+    words_split(w[(2 * s + 1) * stride], bh, bl);
+    sh[s] = cat8(ah, bh);
+    sl[s] = cat8(al, bl);
+  }
+}
+
+// The split fragments of a d_k x 16 state held as NT float32 accumulator
+// tiles: 32-deep B fragments of contraction block s (tiles 2s and 2s + 1).
+template <int NS>
+__device__ inline void split_state(const f32x4* acc, bf16x8* sh, bf16x8* sl) {
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const Sp4 a = split4(acc[2 * s]), b = split4(acc[2 * s + 1]);
+    sh[s] = cat8(a.h, b.h);
+    sl[s] = cat8(a.l, b.l);
+  }
+}
+
+// 16 x 16 bf16 tile, accumulator layout (lane (n, grp) holds X[4 grp + i][n])
+// -> row layout (lane (n, grp) holds X[n][4 grp + j]) through 512 bytes of
+// this wave's LDS: a lane-order write, then a transposing read in which lane
+// (n, grp) points at the 8 bytes written by lane (4 grp + n / 4, n % 4).
+__device__ inline void tr_put(char* buf, int lane, bf16x4 x) {
+  *reinterpret_cast<bf16x4*>(buf + 8 * lane) = x;
+}
+__device__ inline bf16x4 tr_get(char* buf, int n, int grp) {
+  const s16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(buf + 8 * (16 * (n & 3) + 4 * grp + (n >> 2))));
+  return __builtin_bit_cast(bf16x4, r);
+}
+__device__ inline void wave_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Token rows of one tile of k or q in LDS, bf16, row pitch 2 DK + 16 bytes
+// (the pad spreads the rows of a fragment read over the banks).
+//   A fragment of block s (32-deep over d_k): lane (n, grp) holds
+//     K[n][32 s + kappa32(grp, j)]: two 8-byte reads of row n;
+//   transposed A fragment of 16-row block t (16-deep over tokens): lane
+//     (n, grp) holds K[4 grp + j][16 t + n]: one transposing read in which
+//     lane (n, grp) points at row 4 grp + n / 4, columns 16 t + 4 (n % 4).
+template <int DK>
+struct Rows {
+  static constexpr int PITCH = 2 * DK + 16;
+  static constexpr int BYTES = 16 * PITCH;
+  __device__ static inline bf16x8 afrag(const char* rows, int s, int n, int grp) {
+    const char* p = rows + n * PITCH + 2 * (32 * s + 4 * grp);
+    return cat8(*reinterpret_cast<const bf16x4*>(p), *reinterpret_cast<const bf16x4*>(p + 32));
+  }
+  __device__ static inline bf16x4 tfrag(const char* rows, int t, int n, int grp) {
+    const s16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)(rows + (4 * grp + (n >> 2)) * PITCH + 32 * t + 8 * (n & 3)));
+    return __builtin_bit_cast(bf16x4, r);
+  }
+  // Cooperative copy of one tile's rows from global memory (zeros past the
+  // sequence end): `nthr` threads, thread `tid`.
+  template <typename Src>
+  __device__ static inline void stage(char* rows, const Src* src, const BSeq& sq, int c, int h,
+                                      int H, int tid, int nthr) {
+    constexpr int PER_ROW = 2 * DK / 16;
+    for (int x = tid; x < 16 * PER_ROW; x += nthr) {
+      const int r = x / PER_ROW, p = x % PER_ROW;
+      const int tok = 16 * c + r;
+      uint4 u = uint4{0u, 0u, 0u, 0u};
+      if (tok < sq.T)
+        u = *reinterpret_cast<const uint4*>(src + ((sq.tok0 + tok) * H + h) * DK + 8 * p);
+      *reinterpret_cast<uint4*>(rows + r * PITCH + 16 * p) = u;
+    }
+  }
+};
+
+// Index of group 0 of sequence b, head h in the checkpoint arrays.
+__device__ inline int64_t grp_base(const BwdArgs& a, int b, int h) {
+  if (a.cu) return (int64_t)h * a.nslotG + bwd_begin(a, b) / (16 * kGS) + b;
+  return ((int64_t)b * a.H + h) * a.NG;
+}
+
+// A group slot of the gradient grid -> (sequence b, head h, group g); false
+// for a slot no group uses.
+__device__ inline bool bwd2_group(const BwdArgs& a, int64_t blk, int& b, int& h, int& g) {
+  if (!a.cu) {
+    g = (int)(blk % a.NG);
+    const int64_t bh = blk / a.NG;
+    h = (int)(bh % a.H);
+    b = (int)(bh / a.H);
+    return 16 * kGS * g < a.T;
+  }
+  h = (int)(blk / a.nslotG);
+  const int slot = (int)(blk - (int64_t)h * a.nslotG);
+  int lo = 0, hi = a.B - 1;                  // the last s whose group 0 sits at or before slot
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (bwd_begin(a, mid) / (16 * kGS) + mid <= slot) lo = mid;
+    else hi = mid - 1;
+  }
+  b = lo;
+  const BSeq sq = bwd_seq(a, b, h);
+  g = slot - (bwd_begin(a, b) / (16 * kGS) + b);
+  return g >= 0 && kGS * g < sq.NC;
+}
+
+// Per-tile operator fragments built from the record's row-major float32 16 x
+// 16 matrices: element (t, i) of M as a split A fragment [M_hi | M_lo] (lane
+// (n = t, grp = i / 4), register i % 4), or of M^T (lane (n = i, grp = t / 4),
+// register t % 4).  `frag` is 64 lanes x 16 bytes.
+__device__ inline void put_op(char* frag, int t, int i, float x, bool transposed) {
+  const int n = transposed ? i : t, c = transposed ? t : i;
+  char* p = frag + 16 * (16 * (c >> 2) + n) + 2 * (c & 3);
+  const __bf16 hb = (__bf16)x;
+  *reinterpret_cast<__bf16*>(p) = hb;
+  *reinterpret_cast<__bf16*>(p + 8) = (__bf16)(x - (float)hb);
+}
+
+// ------------------------------------------- states at every group start
+// Record of one staged tile (bytes).
+template <int DK, int SPW>
+struct H2Rec {
+  static constexpr int KR = 0;                       // K rows
+  static constexpr int TF = Rows<DK>::BYTES;         // [T hi | T lo] A fragments
+  static constexpr int VF = TF + 1024;               // V slices, accumulator layout, bf16
+  static constexpr int GM = VF + SPW * 512;          // gamma[16]
+  static constexpr int EC = GM + 64;                 // ec[16]
+  static constexpr int BT = EC + 64;                 // beta[16]
+  static constexpr int GC = BT + 64;                 // gamma_C
+  static constexpr int BYTES = GC + 16;
+  static_assert(BYTES % 16 == 0, "alignment");
+};
+
+template <int DK, int SPW>
+struct H2Raw {
+  uint4 kr[DK / 32];     // K row pieces (2 DK / 16 pieces per row, 16 rows, 64 lanes)
+  f32x4 ti;
+  bf16x4 vv[SPW];
+  float g, bt, gC;
+};
+
+template <int DK, int NP, int SPW>
+__global__ __launch_bounds__(64 * (NP + SPW)) void bwd2_hstates_kernel(BwdArgs a) {
+  using R = H2Rec<DK, SPW>;
+  using RW = Rows<DK>;
+  constexpr int NS = DK / 32, NT = DK / 16;
+  __shared__ __attribute__((aligned(16))) char smem[2 * NP * R::BYTES];
+  const int NW = a.Dv / (16 * SPW);
+  const int sl = (int)(blockIdx.x % NW);
+  const int64_t bh = blockIdx.x / NW;
+  const int h = (int)(bh % a.H), b = (int)(bh / a.H);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15, grp = lane >> 4;
+  const BSeq sq = bwd_seq(a, b, h);
+  const int NC = sq.NC;
+  const int NE = (NC + NP - 1) / NP;
+  auto rec_of = [&](int c) -> char* { return smem + (((c / NP) & 1) * NP + c % NP) * R::BYTES; };
+
+  if (wave < SPW) {
+    const int v0 = 16 * (SPW * sl + wave);
+    f32x4 Hacc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        Hacc[t][i] = a.h0 ? a.h0[(bh * DK + 16 * t + 4 * grp + i) * a.Dv + v0 + n] : 0.f;
+    }
+    bf16x8 Hh[NS], Hl[NS];
+    split_state<NS>(Hacc, Hh, Hl);
+    unsigned* const hw = a.hw + grp_base(a, b, h) * DK * a.Dv + (int64_t)(v0 / 16) * DK * 16;
+    __syncthreads();  // epoch 0 staged
+    for (int ep = 0; ep < NE; ++ep) {
+      for (int j = 0; j < NP; ++j) {
+        const int c = ep * NP + j;
+        if (c >= NC) break;
+        const char* rec = rec_of(c);
+        if (c % kGS == 0) {
+          uint4* dst = reinterpret_cast<uint4*>(hw + (int64_t)(c / kGS) * DK * a.Dv);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            const bf16x8 hh = Hh[t >> 1], hl = Hl[t >> 1];
+            dst[t * 64 + lane] = (t & 1) ? pack_words(second4(hh), second4(hl))
+                                         : pack_words(first4(hh), first4(hl));
+          }
+        }
+        // R = K H
+        f32x4 Rk = zero4();
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const bf16x8 ka = RW::afrag(rec + R::KR, s, n, grp);
+          Rk = mma32b(ka, Hl[s], Rk);
+          Rk = mma32b(ka, Hh[s], Rk);
+        }
+        const f32x4 vf = to_f4(*reinterpret_cast<const bf16x4*>(rec + R::VF + wave * 512 + 8 * lane));
+        const f32x4 gm = *reinterpret_cast<const f32x4*>(rec + R::GM + 16 * grp);
+        const f32x4 ec = *reinterpret_cast<const f32x4*>(rec + R::EC + 16 * grp);
+        const f32x4 bt = *reinterpret_cast<const f32x4*>(rec + R::BT + 16 * grp);
+        const float gC = *reinterpret_cast<const float*>(rec + R::GC);
+        const bf16x8 tf = *reinterpret_cast<const bf16x8*>(rec + R::TF + 16 * lane);
+        f32x4 Y;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Y[i] = bt[i] * (vf[i] - gm[i] * Rk[i]);
+        const Sp4 sy = split4(Y);
+        f32x4 U = mma32b(tf, cat8(sy.h, sy.h), zero4());
+        U = mma32b_lo(tf, sy.l, U);
+        f32x4 Up;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Up[i] = ec[i] * U[i];
+        const Sp4 su = split4(Up);
+        const bf16x8 ub = cat8(su.h, su.l);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const bf16x4 kt = RW::tfrag(rec + R::KR, t, n, grp);
+          Hacc[t] = Hacc[t] * gC;
+          Hacc[t] = mma32b(cat8(kt, kt), ub, Hacc[t]);
+        }
+        split_state<NS>(Hacc, Hh, Hl);
+      }
+      __syncthreads();  // this epoch consumed, the next one staged
+    }
+    return;
+  }
+
+  // ---------------------------------------------------------------- loaders
+  const int p = wave - SPW;
+  const __bf16* kp = static_cast<const __bf16*>(a.k);
+  const __bf16* vp = static_cast<const __bf16*>(a.v);
+  const int v0 = 16 * SPW * sl;
+  constexpr int PER_ROW = 2 * DK / 16;
+  auto load = [&](H2Raw<DK, SPW>& r, int c) {
+    if (NC == 0) return;          // an empty sequence loads nothing
+    c = min(c, NC - 1);
+#pragma unroll
+    for (int x = 0; x < DK / 32; ++x) {
+      const int idx = 64 * x + lane, row = idx / PER_ROW, pc = idx % PER_ROW;
+      const int tok = 16 * c + row;
+      r.kr[x] = tok < sq.T
+                    ? *reinterpret_cast<const uint4*>(kp + ((sq.tok0 + tok) * a.H + h) * DK + 8 * pc)
+                    : uint4{0u, 0u, 0u, 0u};
+    }
+    const float* rec = a.rec + (sq.rbase + c) * BRec::FLOATS;
+    r.ti = reinterpret_cast<const f32x4*>(rec + BRec::TINV)[lane];
+    r.g = rec[BRec::G + n];
+    r.bt = rec[BRec::BETA + n];
+    r.gC = rec[BRec::G + kT - 1];
+#pragma unroll
+    for (int w = 0; w < SPW; ++w) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = 16 * c + 4 * grp + i;
+        r.vv[w][i] = tok < sq.T ? vp[((sq.tok0 + tok) * a.H + h) * a.Dv + v0 + 16 * w + n]
+                                : (__bf16)0.f;
+      }
+    }
+  };
+  auto store = [&](const H2Raw<DK, SPW>& r, int c) {
+    if (c >= NC) return;
+    char* rec = rec_of(c);
+#pragma unroll
+    for (int x = 0; x < DK / 32; ++x) {
+      const int idx = 64 * x + lane, row = idx / PER_ROW, pc = idx % PER_ROW;
+      *reinterpret_cast<uint4*>(rec + R::KR + row * RW::PITCH + 16 * pc) = r.kr[x];
+    }
+    // T arrives row-major: lane l holds T[l / 4][4 (l % 4) + e]
+#pragma unroll
+    for (int e = 0; e < 4; ++e) put_op(rec + R::TF, lane >> 2, 4 * (lane & 3) + e, r.ti[e], false);
+#pragma unroll
+    for (int w = 0; w < SPW; ++w) *reinterpret_cast<bf16x4*>(rec + R::VF + w * 512 + 8 * lane) = r.vv[w];
+    if (grp == 0) {
+      reinterpret_cast<float*>(rec + R::GM)[n] = __expf(r.g);
+      reinterpret_cast<float*>(rec + R::EC)[n] = __expf(r.gC - r.g);
+      reinterpret_cast<float*>(rec + R::BT)[n] = r.bt;
+      if (n == 0) *reinterpret_cast<float*>(rec + R::GC) = __expf(r.gC);
+    }
+  };
+  H2Raw<DK, SPW> ra, rb;
+  load(ra, p);
+  store(ra, p);                 // epoch 0
+  load(ra, NP + p);             // epoch 1, staged during epoch 0
+  __syncthreads();
+  for (int ep = 0; ep < NE; ep += 2) {
+    load(rb, (ep + 2) * NP + p);
+    store(ra, (ep + 1) * NP + p);
+    __syncthreads();
+    if (ep + 1 < NE) {
+      load(ra, (ep + 3) * NP + p);
+      store(rb, (ep + 2) * NP + p);
+      __syncthreads();
+    }
+  }
+}
+
+// ------------------------------------ state gradients at every group end
+template <int DK, int SPW>
+struct D2Rec {
+  static constexpr int KR = 0;                       // K rows
+  static constexpr int QR = Rows<DK>::BYTES;         // Q rows
+  static constexpr int PT = 2 * Rows<DK>::BYTES;     // [P^T hi | P^T lo] A fragments
+  static constexpr int TT = PT + 1024;               // [T^T hi | T^T lo]
+  static constexpr int DO = TT + 1024;               // dO slices, accumulator layout, bf16
+  static constexpr int GM = DO + SPW * 512;          // gamma[16]
+  static constexpr int EC = GM + 64;                 // ec[16]
+  static constexpr int BT = EC + 64;                 // beta[16]
+  static constexpr int GC = BT + 64;                 // gamma_C
+  static constexpr int BYTES = GC + 16;
+  static_assert(BYTES % 16 == 0, "alignment");
+};
+
+template <int DK, int SPW>
+struct D2Raw {
+  uint4 kr[DK / 32], qr[DK / 32];
+  f32x4 pm, tm;
+  bf16x4 dd[SPW];
+  float g, bt, gC;
+};
+
+template <int DK, int NP, int SPW>
+__global__ __launch_bounds__(64 * (NP + SPW)) void bwd2_dh_kernel(BwdArgs a) {
+  using R = D2Rec<DK, SPW>;
+  using RW = Rows<DK>;
+  constexpr int NS = DK / 32, NT = DK / 16;
+  __shared__ __attribute__((aligned(16))) char smem[2 * NP * R::BYTES];
+  const int NW = a.Dv / (16 * SPW);
+  const int sl = (int)(blockIdx.x % NW);
+  const int64_t bh = blockIdx.x / NW;
+  const int h = (int)(bh % a.H), b = (int)(bh / a.H);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15, grp = lane >> 4;
+  const BSeq sq = bwd_seq(a, b, h);
+  const int NC = sq.NC;
+  const int NE = (NC + NP - 1) / NP;
+  // records by processing index m (tile NC - 1 - m)
+  auto rec_of = [&](int m) -> char* { return smem + (((m / NP) & 1) * NP + m % NP) * R::BYTES; };
+
+  if (wave < SPW) {
+    const int v0 = 16 * (SPW * sl + wave);
+    f32x4 D[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        D[t][i] = a.dhT ? a.dhT[(bh * DK + 16 * t + 4 * grp + i) * a.Dv + v0 + n] : 0.f;
+    }
+    bf16x8 Dh[NS], Dl[NS];
+    split_state<NS>(D, Dh, Dl);
+    unsigned* const dw = a.dw + grp_base(a, b, h) * DK * a.Dv + (int64_t)(v0 / 16) * DK * 16;
+    __syncthreads();  // epoch 0 staged
+    for (int ep = 0; ep < NE; ++ep) {
+      for (int j = 0; j < NP; ++j) {
+        const int m = ep * NP + j;
+        if (m >= NC) break;
+        const int c = NC - 1 - m;
+        const char* rec = rec_of(m);
+        if (c % kGS == kGS - 1 || c == NC - 1) {
+          uint4* dst = reinterpret_cast<uint4*>(dw + (int64_t)(c / kGS) * DK * a.Dv);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            const bf16x8 dh = Dh[t >> 1], dl = Dl[t >> 1];
+            dst[t * 64 + lane] = (t & 1) ? pack_words(second4(dh), second4(dl))
+                                         : pack_words(first4(dh), first4(dl));
+          }
+        }
+        f32x4 KD = zero4();
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const bf16x8 ka = RW::afrag(rec + R::KR, s, n, grp);
+          KD = mma32b(ka, Dl[s], KD);
+          KD = mma32b(ka, Dh[s], KD);
+        }
+        const bf16x4 dob = *reinterpret_cast<const bf16x4*>(rec + R::DO + wave * 512 + 8 * lane);
+        const f32x4 dO = to_f4(dob);
+        const f32x4 gm = *reinterpret_cast<const f32x4*>(rec + R::GM + 16 * grp);
+        const f32x4 ec = *reinterpret_cast<const f32x4*>(rec + R::EC + 16 * grp);
+        const f32x4 bt = *reinterpret_cast<const f32x4*>(rec + R::BT + 16 * grp);
+        const float gC = *reinterpret_cast<const float*>(rec + R::GC);
+        const bf16x8 pt = *reinterpret_cast<const bf16x8*>(rec + R::PT + 16 * lane);
+        const bf16x8 tt = *reinterpret_cast<const bf16x8*>(rec + R::TT + 16 * lane);
+        f32x4 eKD;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) eKD[i] = ec[i] * KD[i];
+        const f32x4 dU = mma32b(pt, cat8(dob, dob), eKD);
+        const Sp4 su = split4(dU);
+        f32x4 dY = mma32b(tt, cat8(su.h, su.h), zero4());
+        dY = mma32b_lo(tt, su.l, dY);
+        f32x4 Og, Z;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          Og[i] = gm[i] * dO[i];
+          Z[i] = -(bt[i] * gm[i] * dY[i]);
+        }
+        const Sp4 so = split4(Og), sz = split4(Z);
+        const bf16x8 ob = cat8(so.h, so.l), zb = cat8(sz.h, sz.l);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const bf16x4 qt = RW::tfrag(rec + R::QR, t, n, grp);
+          const bf16x4 kt = RW::tfrag(rec + R::KR, t, n, grp);
+          D[t] = D[t] * gC;
+          D[t] = mma32b(cat8(qt, qt), ob, D[t]);
+          D[t] = mma32b(cat8(kt, kt), zb, D[t]);
+        }
+        split_state<NS>(D, Dh, Dl);
+      }
+      __syncthreads();  // this epoch consumed, the next one staged
+    }
+    if (a.dh0) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          a.dh0[(bh * DK + 16 * t + 4 * grp + i) * a.Dv + v0 + n] = D[t][i];
+      }
+    }
+    return;
+  }
+
+  // ---------------------------------------------------------------- loaders
+  const int p = wave - SPW;
+  const __bf16* kp = static_cast<const __bf16*>(a.k);
+  const __bf16* qp = static_cast<const __bf16*>(a.q);
+  const __bf16* dp = static_cast<const __bf16*>(a.dout);
+  const int v0 = 16 * SPW * sl;
+  constexpr int PER_ROW = 2 * DK / 16;
+  auto load = [&](D2Raw<DK, SPW>& r, int m) {
+    if (NC == 0) return;          // an empty sequence loads nothing
+    const int c = NC - 1 - min(m, NC - 1);
+#pragma unroll
+    for (int x = 0; x < DK / 32; ++x) {
+      const int idx = 64 * x + lane, row = idx / PER_ROW, pc = idx % PER_ROW;
+      const int tok = 16 * c + row;
+      const int64_t off = ((sq.tok0 + tok) * a.H + h) * DK + 8 * pc;
+      const bool ok = tok < sq.T;
+      r.kr[x] = ok ? *reinterpret_cast<const uint4*>(kp + off) : uint4{0u, 0u, 0u, 0u};
+      r.qr[x] = ok ? *reinterpret_cast<const uint4*>(qp + off) : uint4{0u, 0u, 0u, 0u};
+    }
+    const float* rec = a.rec + (sq.rbase + c) * BRec::FLOATS;
+    r.pm = reinterpret_cast<const f32x4*>(rec + BRec::P)[lane];
+    r.tm = reinterpret_cast<const f32x4*>(rec + BRec::TINV)[lane];
+    r.g = rec[BRec::G + n];
+    r.bt = rec[BRec::BETA + n];
+    r.gC = rec[BRec::G + kT - 1];
+#pragma unroll
+    for (int w = 0; w < SPW; ++w) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = 16 * c + 4 * grp + i;
+        r.dd[w][i] = tok < sq.T ? dp[((sq.tok0 + tok) * a.H + h) * a.Dv + v0 + 16 * w + n]
+                                : (__bf16)0.f;
+      }
+    }
+  };
+  auto store = [&](const D2Raw<DK, SPW>& r, int m) {
+    if (m >= NC) return;
+    char* rec = rec_of(m);
+#pragma unroll
+    for (int x = 0; x < DK / 32; ++x) {
+      const int idx = 64 * x + lane, row = idx / PER_ROW, pc = idx % PER_ROW;
+      *reinterpret_cast<uint4*>(rec + R::KR + row * RW::PITCH + 16 * pc) = r.kr[x];
+      *reinterpret_cast<uint4*>(rec + R::QR + row * RW::PITCH + 16 * pc) = r.qr[x];
+    }
+    // P and T arrive row-major (lane l holds row l / 4, columns 4 (l % 4) + e)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      put_op(rec + R::PT, lane >> 2, 4 * (lane & 3) + e, r.pm[e], true);
+      put_op(rec + R::TT, lane >> 2, 4 * (lane & 3) + e, r.tm[e], true);
+    }
+#pragma unroll
+    for (int w = 0; w < SPW; ++w) *reinterpret_cast<bf16x4*>(rec + R::DO + w * 512 + 8 * lane) = r.dd[w];
+    if (grp == 0) {
+      reinterpret_cast<float*>(rec + R::GM)[n] = __expf(r.g);
+      reinterpret_cast<float*>(rec + R::EC)[n] = __expf(r.gC - r.g);
+      reinterpret_cast<float*>(rec + R::BT)[n] = r.bt;
+      if (n == 0) *reinterpret_cast<float*>(rec + R::GC) = __expf(r.gC);
+    }
+  };
+  D2Raw<DK, SPW> ra, rb;
+  load(ra, p);
+  store(ra, p);                 // epoch 0
+  load(ra, NP + p);             // epoch 1, staged during epoch 0
+  __syncthreads();
+  for (int ep = 0; ep < NE; ep += 2) {
+    load(rb, (ep + 2) * NP + p);
+    store(ra, (ep + 1) * NP + p);
+    __syncthreads();
+    if (ep + 1 < NE) {
+      load(ra, (ep + 3) * NP + p);
+      store(rb, (ep + 2) * NP + p);
+      __syncthreads();
+    }
+  }
+}
+
+// --------------------------------------------------- per-group gradients
+// LDS of the gradient kernel (bytes).
+template <int DK>
+struct G2Lds {
+  static constexpr int NT = DK / 16;
+  static constexpr int ROWS = Rows<DK>::BYTES;
+  static constexpr int KR = 0;                         // K rows of the group's tiles
+  static constexpr int QR = KR + kGS * ROWS;           // Q rows
+  static constexpr int TF = QR + kGS * ROWS;           // [T hi | T lo] A fragments, 1 KB per tile
+  static constexpr int TT = TF + kGS * 1024;           // [T^T hi | T^T lo]
+  static constexpr int PT = TT + kGS * 1024;           // [P^T hi | P^T lo]
+  static constexpr int PM = PT + kGS * 1024;           // P float32, 16 x 17 per tile
+  static constexpr int EK = PM + kGS * 1088;           // E o K K^T float32, 16 x 16 per tile
+  static constexpr int SC = EK + kGS * 1024;           // per tile G, beta, gamma, ec, dg/dg' [16] each
+  static constexpr int XR = SC + kGS * 512;            // transposition tiles / reduction
+  static constexpr int XW = 9 * 512;                   // transposition bytes per wave
+  static constexpr int XBYTES = 8 * XW > 8 * NT * 1024 ? 8 * XW : 8 * NT * 1024;
+  static constexpr int RS = XR + XBYTES;               // dP, dA partials: 8 waves x 2 x 1 KB
+  static constexpr int RW = RS + 8 * 2 * 1024;         // row sums: 8 waves x 3 x 16 floats
+  static constexpr int TL = RW + 8 * 3 * 64;           // PE, M, PP, AA: 4 x 16 x 17 floats
+  static constexpr int TR = TL + 4 * 1088;             // row B, G, W, AK [16] each
+  static constexpr int HD = TR + 256;                  // <H, dH'> per wave
+  static constexpr int BYTES = HD + 32;
+};
+
+template <int DK>
+__global__ __launch_bounds__(512) void bwd2_grad_kernel(BwdArgs a) {
+  using L = G2Lds<DK>;
+  using RW = Rows<DK>;
+  constexpr int NS = DK / 32, NT = DK / 16;
+  __shared__ __attribute__((aligned(16))) char sm[L::BYTES];
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, n = lane & 15, grp = lane >> 4;
+  int b, h, g;
+  if (!bwd2_group(a, blockIdx.x, b, h, g)) return;   // a slot no group uses: the whole block
+  const BSeq sq = bwd_seq(a, b, h);
+  const int c0 = kGS * g;
+  const int GSn = min(kGS, sq.NC - c0);
+  const int64_t gi = grp_base(a, b, h) + g;
+  const int NV = a.Dv / 16;
+  const bool act = w < NV;            // waves beyond the slices only join the reductions
+  const int v0 = 16 * w;
+  const __bf16* vp = static_cast<const __bf16*>(a.v);
+  const __bf16* dop = static_cast<const __bf16*>(a.dout);
+
+  // ---- this wave's slice: the end-state gradient of the group, v and dO of
+  // its tiles (the start state is re-read per tile: an L2 hit after the first)
+  const uint4* const hp =
+      reinterpret_cast<const uint4*>(a.hw + gi * DK * a.Dv + (int64_t)w * DK * 16);
+  // dH' of the tile in hand, as split fragments (carried backwards tile by
+  // tile; each step rounds it to hi + lo, as the stored checkpoints are)
+  bf16x8 Dh[NS], Dl[NS];
+  if (act) {
+    const uint4* dp = reinterpret_cast<const uint4*>(a.dw + gi * DK * a.Dv + (int64_t)w * DK * 16);
+    words_state<NS>(dp + lane, 64, Dh, Dl);
+  }
+  // v or dO of tile c of this wave's slice, accumulator layout (zeros past the
+  // sequence end)
+  auto slice4 = [&](const __bf16* src, int c) {
+    bf16x4 x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tok = 16 * c + 4 * grp + i;
+      x[i] = tok < sq.T ? src[((sq.tok0 + tok) * a.H + h) * a.Dv + v0 + n] : (__bf16)0.f;
+    }
+    return x;
+  };
+
+  // ---- stage the group's rows and tile operators
+  for (int j = 0; j < GSn; ++j) {
+    RW::stage(sm + L::KR + j * L::ROWS, static_cast<const __bf16*>(a.k), sq, c0 + j, h, a.H, tid, 512);
+    RW::stage(sm + L::QR + j * L::ROWS, static_cast<const __bf16*>(a.q), sq, c0 + j, h, a.H, tid, 512);
+  }
+  for (int x = tid; x < GSn * 256; x += 512) {
+    const int j = x >> 8, e = x & 255, t = e >> 4, i = e & 15;
+    const float* rec = a.rec + (sq.rbase + c0 + j) * BRec::FLOATS;
+    const float tv = rec[BRec::TINV + e], pv = rec[BRec::P + e];
+    put_op(sm + L::TF + j * 1024, t, i, tv, false);
+    put_op(sm + L::TT + j * 1024, t, i, tv, true);
+    put_op(sm + L::PT + j * 1024, t, i, pv, true);
+    reinterpret_cast<float*>(sm + L::PM + j * 1088)[t * 17 + i] = pv;
+    reinterpret_cast<float*>(sm + L::EK + j * 1024)[e] = rec[BRec::EKK + e];
+  }
+  if (tid < GSn * 16) {
+    const int j = tid >> 4, t = tid & 15;
+    const float* rec = a.rec + (sq.rbase + c0 + j) * BRec::FLOATS;
+    const float gv = rec[BRec::G + t], gC = rec[BRec::G + kT - 1];
+    float* sc = reinterpret_cast<float*>(sm + L::SC + j * 512);
+    sc[t] = gv;
+    sc[16 + t] = rec[BRec::BETA + t];
+    sc[32 + t] = __expf(gv);
+    sc[48 + t] = __expf(gC - gv);
+    // dL/dx = dg/dx * dL/dg in logit mode (g = -G sigmoid(x)), 1 in log mode
+    const int tok = 16 * (c0 + j) + t;
+    float dgx = 1.f;
+    if (a.gate_logit && tok < sq.T) {
+      const float sg = sigmoid_f(a.gate[(sq.tok0 + tok) * a.H + h]);
+      dgx = -a.G * sg * (1.f - sg);
+    }
+    sc[64 + t] = dgx;
+  }
+  __syncthreads();
+
+  char* const xr = sm + L::XR + w * L::XW;         // this wave's transposition tiles
+  f32x4* const red = reinterpret_cast<f32x4*>(sm + L::XR);
+  f32x4* const rs = reinterpret_cast<f32x4*>(sm + L::RS);
+  float* const rw = reinterpret_cast<float*>(sm + L::RW);
+  float (*const sPE)[17] = reinterpret_cast<float (*)[17]>(sm + L::TL);
+  float (*const sM)[17] = reinterpret_cast<float (*)[17]>(sm + L::TL + 1088);
+  float (*const sPP)[17] = reinterpret_cast<float (*)[17]>(sm + L::TL + 2 * 1088);
+  float (*const sAA)[17] = reinterpret_cast<float (*)[17]>(sm + L::TL + 3 * 1088);
+  float* const sRowB = reinterpret_cast<float*>(sm + L::TR);
+  float* const sRowG = sRowB + 16;
+  float* const sRowW = sRowB + 32;
+  float* const sRowAK = sRowB + 48;
+  float* const sHdH = reinterpret_cast<float*>(sm + L::HD);
+
+  for (int j = GSn - 1; j >= 0; --j) {
+    const int c = c0 + j;
+    const char* kr = sm + L::KR + j * L::ROWS;
+    const char* qr = sm + L::QR + j * L::ROWS;
+    const float* sc = reinterpret_cast<const float*>(sm + L::SC + j * 512);
+    const float gamC = __expf(sc[kT - 1]);
+    f32x4 pB = zero4(), pG = zero4(), pW = zero4(), dPp = zero4(), dAp = zero4();
+    float hdh = 0.f;
+    bf16x8 ob, zb;               // [gamma dO] and [-beta gamma dY] split, for the step to j - 1
+    bf16x8 dO8, aY8, aU8;        // row fragments: [dO, dO], [aY hi | lo], [aU hi | lo]
+    bf16x8 Hh[NS], Hl[NS];       // H at the start of tile j, split
+    if (act) {
+      // H at the start of tile j: j forward steps from the group's checkpoint
+      // v of the next forward step and dO of this tile, requested ahead of use
+      bf16x4 vnext = slice4(vp, c0);
+      const bf16x4 dob = slice4(dop, c);
+      f32x4 Hacc[NT];
+      {
+        uint4 hw8[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) hw8[t] = hp[t * 64 + lane];
+        words_state<NS>(hw8, 1, Hh, Hl);
+        if (j > 0) {
+#pragma unroll
+          for (int t = 0; t < NT; ++t) Hacc[t] = words_f4(hw8[t]);
+        }
+      }
+      for (int m = 0; m < j; ++m) {
+        const char* km = sm + L::KR + m * L::ROWS;
+        const float* scm = reinterpret_cast<const float*>(sm + L::SC + m * 512);
+        f32x4 Rk = zero4();
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const bf16x8 ka = RW::afrag(km, s, n, grp);
+          Rk = mma32b(ka, Hl[s], Rk);
+          Rk = mma32b(ka, Hh[s], Rk);
+        }
+        const f32x4 vf = to_f4(vnext);
+        vnext = slice4(vp, c0 + m + 1);
+        const f32x4 gm = *reinterpret_cast<const f32x4*>(scm + 32 + 4 * grp);
+        const f32x4 ec = *reinterpret_cast<const f32x4*>(scm + 48 + 4 * grp);
+        const f32x4 bt = *reinterpret_cast<const f32x4*>(scm + 16 + 4 * grp);
+        const float gCm = __expf(scm[kT - 1]);
+        const bf16x8 tf = *reinterpret_cast<const bf16x8*>(sm + L::TF + m * 1024 + 16 * lane);
+        f32x4 Y;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Y[i] = bt[i] * (vf[i] - gm[i] * Rk[i]);
+        const Sp4 sy = split4(Y);
+        f32x4 U = mma32b(tf, cat8(sy.h, sy.h), zero4());
+        U = mma32b_lo(tf, sy.l, U);
+        f32x4 Up;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Up[i] = ec[i] * U[i];
+        const Sp4 su = split4(Up);
+        const bf16x8 ub = cat8(su.h, su.l);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const bf16x4 kt = RW::tfrag(km, t, n, grp);
+          Hacc[t] = Hacc[t] * gCm;
+          Hacc[t] = mma32b(cat8(kt, kt), ub, Hacc[t]);
+        }
+        split_state<NS>(Hacc, Hh, Hl);
+      }
+
+      // K H, Q H, K dH' and H^T dH' (its trace is <H, dH'>)
+      f32x4 KH = zero4(), QH = zero4(), KdH = zero4(), HtD = zero4();
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const bf16x8 ka = RW::afrag(kr, s, n, grp);
+        const bf16x8 qa = RW::afrag(qr, s, n, grp);
+        KH = mma32b(ka, Hl[s], KH);
+        KH = mma32b(ka, Hh[s], KH);
+        QH = mma32b(qa, Hl[s], QH);
+        QH = mma32b(qa, Hh[s], QH);
+        KdH = mma32b(ka, Dl[s], KdH);
+        KdH = mma32b(ka, Dh[s], KdH);
+        HtD = mma32b(Hl[s], Dh[s], HtD);
+        HtD = mma32b(Hh[s], Dl[s], HtD);
+        HtD = mma32b(Hh[s], Dh[s], HtD);
+      }
+      hdh = (n >> 2) == grp ? HtD[n & 3] : 0.f;
+      const f32x4 gm4 = *reinterpret_cast<const f32x4*>(sc + 32 + 4 * grp);
+      const f32x4 bt4 = *reinterpret_cast<const f32x4*>(sc + 16 + 4 * grp);
+      const f32x4 ec4 = *reinterpret_cast<const f32x4*>(sc + 48 + 4 * grp);
+      const f32x4 vf = to_f4(vnext), dd = to_f4(dob);
+      const bf16x8 tf = *reinterpret_cast<const bf16x8*>(sm + L::TF + j * 1024 + 16 * lane);
+      const bf16x8 tt = *reinterpret_cast<const bf16x8*>(sm + L::TT + j * 1024 + 16 * lane);
+      const bf16x8 pt = *reinterpret_cast<const bf16x8*>(sm + L::PT + j * 1024 + 16 * lane);
+      f32x4 vres, Y, eKD;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        vres[i] = vf[i] - gm4[i] * KH[i];
+        Y[i] = bt4[i] * vres[i];
+        eKD[i] = ec4[i] * KdH[i];
+      }
+      const Sp4 sy = split4(Y);
+      f32x4 U = mma32b(tf, cat8(sy.h, sy.h), zero4());
+      U = mma32b_lo(tf, sy.l, U);
+      const f32x4 dU = mma32b(pt, cat8(dob, dob), eKD);
+      const Sp4 sdu = split4(dU);
+      f32x4 dY = mma32b(tt, cat8(sdu.h, sdu.h), zero4());
+      dY = mma32b_lo(tt, sdu.l, dY);
+      f32x4 aY, aU;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pB[i] = dY[i] * vres[i];
+        pG[i] = gm4[i] * QH[i] * dd[i] - bt4[i] * gm4[i] * dY[i] * KH[i];
+        pW[i] = eKD[i] * U[i];
+        aY[i] = -(bt4[i] * gm4[i] * dY[i]);
+        aU[i] = ec4[i] * U[i];
+      }
+      // dv = diag(beta) dY: row 4 grp + i, columns v0 .. v0 + 15
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = 16 * c + 4 * grp + i;
+        if (tok < sq.T) a.dv[((sq.tok0 + tok) * a.H + h) * a.Dv + v0 + n] = bt4[i] * dY[i];
+      }
+      // row fragments of dO, U, dY, aY, aU
+      const Sp4 su = split4(U), sdy = split4(dY), say = split4(aY), sau = split4(aU);
+      {
+        f32x4 Og;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Og[i] = gm4[i] * dd[i];
+        const Sp4 so = split4(Og);
+        ob = cat8(so.h, so.l);
+        zb = cat8(say.h, say.l);
+      }
+      tr_put(xr + 0 * 512, lane, dob);
+      tr_put(xr + 1 * 512, lane, su.h);
+      tr_put(xr + 2 * 512, lane, su.l);
+      tr_put(xr + 3 * 512, lane, sdy.h);
+      tr_put(xr + 4 * 512, lane, sdy.l);
+      tr_put(xr + 5 * 512, lane, say.h);
+      tr_put(xr + 6 * 512, lane, say.l);
+      tr_put(xr + 7 * 512, lane, sau.h);
+      tr_put(xr + 8 * 512, lane, sau.l);
+      wave_fence();
+      const bf16x4 dOr = tr_get(xr + 0 * 512, n, grp);
+      const bf16x4 Urh = tr_get(xr + 1 * 512, n, grp), Url = tr_get(xr + 2 * 512, n, grp);
+      const bf16x4 dYrh = tr_get(xr + 3 * 512, n, grp), dYrl = tr_get(xr + 4 * 512, n, grp);
+      const bf16x4 aYrh = tr_get(xr + 5 * 512, n, grp), aYrl = tr_get(xr + 6 * 512, n, grp);
+      const bf16x4 aUrh = tr_get(xr + 7 * 512, n, grp), aUrl = tr_get(xr + 8 * 512, n, grp);
+      wave_fence();
+      dPp = mma32b(cat8(dOr, dOr), cat8(Urh, Url), dPp);
+      dAp = mma32b(cat8(dYrh, dYrl), cat8(Urh, Urh), dAp);
+      dAp = mma32b_lo(cat8(dYrh, dYrl), Url, dAp);
+      aY8 = cat8(aYrh, aYrl);
+      aU8 = cat8(aUrh, aUrl);
+      dO8 = cat8(dOr, dOr);
+    }
+
+    // ---- cross-wave reduction
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) {
+        pB[i] += __shfl_xor(pB[i], m, 16);
+        pG[i] += __shfl_xor(pG[i], m, 16);
+        pW[i] += __shfl_xor(pW[i], m, 16);
+      }
+    }
+    for (int m = 1; m < 64; m <<= 1) hdh += __shfl_xor(hdh, m, 64);
+    // dq partials over this wave's slice: dO H^T, through row fragments of H
+    // (one 32-row block of d_k per LDS round trip)
+    f32x4 dQp[NT];
+#pragma unroll
+    for (int r = 0; r < NT; ++r) dQp[r] = zero4();
+    if (act) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        tr_put(xr + 0 * 512, lane, first4(Hh[s]));
+        tr_put(xr + 1 * 512, lane, first4(Hl[s]));
+        tr_put(xr + 2 * 512, lane, second4(Hh[s]));
+        tr_put(xr + 3 * 512, lane, second4(Hl[s]));
+        wave_fence();
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const bf16x4 hrh = tr_get(xr + (2 * e) * 512, n, grp);
+          const bf16x4 hrl = tr_get(xr + (2 * e + 1) * 512, n, grp);
+          dQp[2 * s + e] = mma32b(dO8, cat8(hrh, hrl), dQp[2 * s + e]);
+        }
+        wave_fence();
+      }
+    }
+    __syncthreads();                       // every wave is done with its transposition tiles
+#pragma unroll
+    for (int r = 0; r < NT; ++r) red[(w * NT + r) * 64 + lane] = dQp[r];
+    rs[(w * 2 + 0) * 64 + lane] = dPp;
+    rs[(w * 2 + 1) * 64 + lane] = dAp;
+    if (n == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        rw[(w * 3 + 0) * 16 + 4 * grp + i] = pB[i];
+        rw[(w * 3 + 1) * 16 + 4 * grp + i] = pG[i];
+        rw[(w * 3 + 2) * 16 + 4 * grp + i] = pW[i];
+      }
+    }
+    if (lane == 0) sHdH[w] = hdh;
+    __syncthreads();
+    // wave w < NT owns 16-row block w of d_k for dq and dk
+    f32x4 dQa = zero4(), dKa = zero4();
+    if (w < NT) {
+      for (int v = 0; v < 8; ++v) dQa += red[(v * NT + w) * 64 + lane];
+      // dq = diag(gamma) dO H^T + ...: the row scale after the sum over slices
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dQa[i] *= sc[32 + 4 * grp + i];
+    }
+    const int t = (tid >> 4) & 15, jj = tid & 15;      // (token, token) view, threads < 256
+    float dPacc = 0.f, dAacc = 0.f;
+    if (tid < 256) {
+      for (int v = 0; v < 8; ++v) {
+        dPacc += rs[(v * 2 + 0) * 64 + 16 * (t >> 2) + jj][t & 3];
+        dAacc -= rs[(v * 2 + 1) * 64 + 16 * (t >> 2) + jj][t & 3];
+      }
+    }
+    __syncthreads();                       // the dq partials are read
+    // dk partials over this wave's slice: aY H^T + aU dH'^T
+    f32x4 dKp[NT];
+#pragma unroll
+    for (int r = 0; r < NT; ++r) dKp[r] = zero4();
+    if (act) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        tr_put(xr + 0 * 512, lane, first4(Hh[s]));
+        tr_put(xr + 1 * 512, lane, first4(Hl[s]));
+        tr_put(xr + 2 * 512, lane, first4(Dh[s]));
+        tr_put(xr + 3 * 512, lane, first4(Dl[s]));
+        tr_put(xr + 4 * 512, lane, second4(Hh[s]));
+        tr_put(xr + 5 * 512, lane, second4(Hl[s]));
+        tr_put(xr + 6 * 512, lane, second4(Dh[s]));
+        tr_put(xr + 7 * 512, lane, second4(Dl[s]));
+        wave_fence();
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int r = 2 * s + e;
+          const bf16x4 hrh = tr_get(xr + (4 * e + 0) * 512, n, grp);
+          const bf16x4 hrl = tr_get(xr + (4 * e + 1) * 512, n, grp);
+          const bf16x4 drh = tr_get(xr + (4 * e + 2) * 512, n, grp);
+          const bf16x4 drl = tr_get(xr + (4 * e + 3) * 512, n, grp);
+          dKp[r] = mma32b(aY8, cat8(hrh, hrh), dKp[r]);
+          dKp[r] = mma32b_lo(aY8, hrl, dKp[r]);
+          dKp[r] = mma32b(aU8, cat8(drh, drh), dKp[r]);
+          dKp[r] = mma32b_lo(aU8, drl, dKp[r]);
+        }
+        wave_fence();
+      }
+    }
+    __syncthreads();                       // every wave is done with its transposition tiles
+#pragma unroll
+    for (int r = 0; r < NT; ++r) red[(w * NT + r) * 64 + lane] = dKp[r];
+    const float* pm = reinterpret_cast<const float*>(sm + L::PM + j * 1088);
+    const float* ek = reinterpret_cast<const float*>(sm + L::EK + j * 1024);
+    if (tid < 256) {
+      const int i = jj;
+      const float e = i <= t ? __expf(sc[t] - sc[i]) : 0.f;
+      const float dP = i <= t ? dPacc : 0.f;
+      const float dA = i < t ? dAacc : 0.f;
+      const float ekk = ek[16 * t + i];
+      sPE[t][i] = dP * e;
+      sM[t][i] = dA * sc[16 + t] * e;
+      sPP[t][i] = dP * pm[17 * t + i];
+      sAA[t][i] = dA * sc[16 + t] * ekk;
+      float rak = dA * ekk;
+      rak += __shfl_xor(rak, 1, 16);
+      rak += __shfl_xor(rak, 2, 16);
+      rak += __shfl_xor(rak, 4, 16);
+      rak += __shfl_xor(rak, 8, 16);
+      if (jj == 0) {
+        float sb = 0.f, sg = 0.f, sw = 0.f;
+        for (int v = 0; v < 8; ++v) {
+          sb += rw[(v * 3 + 0) * 16 + t];
+          sg += rw[(v * 3 + 1) * 16 + t];
+          sw += rw[(v * 3 + 2) * 16 + t];
+        }
+        sRowB[t] = sb;
+        sRowG[t] = sg;
+        sRowW[t] = sw;
+        sRowAK[t] = rak;
+      }
+    }
+    __syncthreads();
+    if (w < NT) {
+      for (int v = 0; v < 8; ++v) dKa += red[(v * NT + w) * 64 + lane];
+      // in-tile terms: dQ += (dP o E) K, dK += (dP o E)^T Q + (M + M^T) K, over
+      // the 16 columns of d_k block w
+      f32x4 pe, pet, mm;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = 4 * grp + q;
+        pe[q] = sPE[n][i];
+        pet[q] = sPE[i][n];
+        mm[q] = sM[n][i] + sM[i][n];
+      }
+      const Sp4 spe = split4(pe), spet = split4(pet), smm = split4(mm);
+      const bf16x4 kt = RW::tfrag(kr, w, n, grp);
+      const bf16x4 qt = RW::tfrag(qr, w, n, grp);
+      dQa = mma32b(cat8(spe.h, spe.l), cat8(kt, kt), dQa);
+      dKa = mma32b(cat8(spet.h, spet.l), cat8(qt, qt), dKa);
+      dKa = mma32b(cat8(smm.h, smm.l), cat8(kt, kt), dKa);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = 16 * c + 4 * grp + i;
+        if (tok < sq.T) {
+          const int64_t ro = ((sq.tok0 + tok) * a.H + h) * DK + 16 * w + n;
+          a.dq[ro] = dQa[i];
+          a.dk[ro] = dKa[i];
+        }
+      }
+    }
+    if (tid < 256) {
+      // dg_u = sum_{t >= u} dG_t (see chunk_bwd.hip): lane (u, i) takes W_i
+      // (i < u) or G_i (i >= u) and column i of PP + AA over the rows t >= u
+      // when i < u; a 16-lane sum then gives dg_u - gamma_C <H, dH'>.
+      const int u = t, i = jj;
+      float x = i < u ? sRowW[i] : sRowG[i];
+#pragma unroll
+      for (int t2 = 0; t2 < kT; ++t2) {
+        const float y = sPP[t2][i] + sAA[t2][i];
+        x += (t2 >= u && i < u) ? y : 0.f;
+      }
+      x += __shfl_xor(x, 1, 16);
+      x += __shfl_xor(x, 2, 16);
+      x += __shfl_xor(x, 4, 16);
+      x += __shfl_xor(x, 8, 16);
+      const int tk = 16 * c + u;
+      if (i == 0 && tk < sq.T) {
+        float hs = 0.f;
+        for (int v = 0; v < 8; ++v) hs += sHdH[v];
+        const float dg = gamC * hs + x;
+        const int64_t idx = (sq.tok0 + tk) * a.H + h;
+        a.dgate[idx] = sc[64 + u] * dg;
+        a.dbeta[idx] = sRowB[u] + sRowAK[u];
+      }
+    }
+    // dH' at the end of tile j - 1:
+    //   D' = gamma_C D + Q^T diag(gamma) dO - K^T diag(beta gamma) dY
+    if (act && j > 0) {
+      f32x4 Dn[NT];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        Dn[2 * s] = (to_f4(first4(Dh[s])) + to_f4(first4(Dl[s]))) * gamC;
+        Dn[2 * s + 1] = (to_f4(second4(Dh[s])) + to_f4(second4(Dl[s]))) * gamC;
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const bf16x4 qt = RW::tfrag(qr, t, n, grp);
+        const bf16x4 kt = RW::tfrag(kr, t, n, grp);
+        Dn[t] = mma32b(cat8(qt, qt), ob, Dn[t]);
+        Dn[t] = mma32b(cat8(kt, kt), zb, Dn[t]);
+      }
+      split_state<NS>(Dn, Dh, Dl);
+    }
+    __syncthreads();                       // the tile's shared values are consumed
+  }
+}
+
+template <int DK>
+hipError_t launch_bwd2_t(const BwdArgs& a, hipStream_t st) {
+  const int64_t tiles = a.cu ? (int64_t)a.H * a.nslot : (int64_t)a.B * a.H * a.NT;
+  const int64_t groups = a.cu ? (int64_t)a.H * a.nslotG : (int64_t)a.B * a.H * a.NG;
+  const int64_t slices = (int64_t)a.B * a.H * (a.Dv / 16);
+  hipLaunchKernelGGL((bwd_prep_kernel<__bf16, DK>), dim3((unsigned)tiles), dim3(kBwdThreads), 0,
+                     st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // two column slices per workgroup when the slice count is even: the staged
+  // tile then serves two chain waves
+  if ((a.Dv / 16) % 2 == 0) {
+    hipLaunchKernelGGL((bwd2_hstates_kernel<DK, 2, 2>), dim3((unsigned)(slices / 2)), dim3(64 * 4),
+                       0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd2_dh_kernel<DK, 2, 2>), dim3((unsigned)(slices / 2)), dim3(64 * 4), 0,
+                       st, a);
+  } else {
+    hipLaunchKernelGGL((bwd2_hstates_kernel<DK, 2, 1>), dim3((unsigned)slices), dim3(64 * 3), 0,
+                       st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd2_dh_kernel<DK, 2, 1>), dim3((unsigned)slices), dim3(64 * 3), 0, st,
+                       a);
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd2_grad_kernel<DK>), dim3((unsigned)groups), dim3(512), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool chunk_bwd_bf16_path(int Dk, int Dv, int fp32) {
+  return !fp32 && (Dk == 64 || Dk == 128) && Dv % 16 == 0 && Dv >= 16 && Dv <= 128;
+}
+
+// Workspace of the bf16 path: the per-tile records, then H words at every
+// group start and D words at every group end.
+long long chunk_bwd_bf16_workspace_bytes(int B, int T, int H, int Dk, int Dv) {
+  const long long nt = (T + kT - 1) / kT;
+  const long long tiles = (long long)B * H * nt;
+  const long long groups = (long long)B * H * ((nt + kGS - 1) / kGS);
+  return tiles * (BRec::FLOATS * 4LL) + groups * 2LL * Dk * Dv * 4LL;
+}
+
+long long chunk_bwd_bf16_varlen_workspace_bytes(int T, int nseq, int H, int Dk, int Dv) {
+  const long long tiles = (long long)H * (T / kT + nseq + 1);
+  const long long groups = (long long)H * (T / (kT * kGS) + nseq + 1);
+  return tiles * (BRec::FLOATS * 4LL) + groups * 2LL * Dk * Dv * 4LL;
+}
+
+hipError_t launch_chunk_bwd_bf16(const void* q, const void* k, const void* v, const void* dout,
+                                 const float* gate, int gate_logit, float G, const float* beta,
+                                 const float* h0, const float* dhT, float* dq, float* dk,
+                                 float* dv, float* dgate, float* dbeta, float* dh0, const int* cu,
+                                 int B, int T, int H, int Dk, int Dv, void* ws, hipStream_t st) {
+  const int NT = (T + kT - 1) / kT;
+  const int nslot = cu ? T / kT + B + 1 : 0;
+  const int64_t tiles = cu ? (int64_t)H * nslot : (int64_t)B * H * NT;
+  const int NG = (NT + kGS - 1) / kGS;
+  const int nslotG = cu ? T / (kT * kGS) + B + 1 : 0;
+  const int64_t groups = cu ? (int64_t)H * nslotG : (int64_t)B * H * NG;
+  char* w = static_cast<char*>(ws);
+  BwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.dout = dout;
+  a.gate = gate; a.beta = beta; a.h0 = h0; a.dhT = dhT;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dgate = dgate; a.dbeta = dbeta; a.dh0 = dh0;
+  a.rec = reinterpret_cast<float*>(w);
+  a.hw = reinterpret_cast<unsigned*>(w + tiles * BRec::FLOATS * 4);
+  a.dw = a.hw + groups * (int64_t)Dk * Dv;
+  a.gate_logit = gate_logit; a.G = G;
+  a.B = B; a.T = T; a.H = H; a.Dv = Dv; a.NT = NT;
+  a.cu = cu; a.nslot = nslot;
+  a.NG = NG; a.nslotG = nslotG;
+  return Dk == 128 ? launch_bwd2_t<128>(a, st) : launch_bwd2_t<64>(a, st);
+}
+
+}  // namespace la

@@ -580,7 +580,7 @@ long long lin_attn_chunk_bwd_workspace_size(int B, int T, int H, int Dk, int Dv,
     return -1;
   }
   ok();
-  return la::chunk_bwd_workspace_bytes(B, T, H, Dk, Dv);
+  return la::chunk_bwd_workspace_bytes(B, T, H, Dk, Dv, dtype == LA_FP32);
 }
 
 int lin_attn_chunk_bwd(const void* q, const void* k, const void* v, const float* gate,
@@ -597,7 +597,7 @@ int lin_attn_chunk_bwd(const void* q, const void* k, const void* v, const float*
   const int64_t es = dtype == LA_BF16 ? 2 : 4;
   const int64_t ntok = (int64_t)B * T * H;
   const int64_t nst = (int64_t)B * H * Dk * Dv;
-  const long long wsz = T > 0 ? la::chunk_bwd_workspace_bytes(B, T, H, Dk, Dv) : 0;
+  const long long wsz = T > 0 ? la::chunk_bwd_workspace_bytes(B, T, H, Dk, Dv, dtype == LA_FP32) : 0;
   if (T > 0) {
     // q, k are read and dq, dk, dv written in 16-byte vectors of a row;
     // everything else element-wise
@@ -653,7 +653,7 @@ long long lin_attn_chunk_bwd_varlen_workspace_size(int T, int nseq, int H, int D
     return -1;
   }
   ok();
-  return la::chunk_bwd_varlen_workspace_bytes(T, nseq, H, Dk, Dv);
+  return la::chunk_bwd_varlen_workspace_bytes(T, nseq, H, Dk, Dv, dtype == LA_FP32);
 }
 
 int lin_attn_chunk_bwd_varlen(const void* q, const void* k, const void* v, const float* gate,
@@ -673,7 +673,7 @@ int lin_attn_chunk_bwd_varlen(const void* q, const void* k, const void* v, const
   const int64_t es = dtype == LA_BF16 ? 2 : 4;
   const int64_t ntok = (int64_t)T * H;
   const int64_t nst = (int64_t)nseq * H * Dk * Dv;
-  const long long wsz = la::chunk_bwd_varlen_workspace_bytes(T, nseq, H, Dk, Dv);
+  const long long wsz = la::chunk_bwd_varlen_workspace_bytes(T, nseq, H, Dk, Dv, dtype == LA_FP32);
   if (T > 0) {
     // q, k are read and dq, dk, dv written in 16-byte vectors of a row;
     // everything else element-wise

@@ -384,10 +384,13 @@ int lin_attn_decode_step_channel(const void* q, const void* k, const void* v,
 
 /*
  * lin_attn_chunk_bwd_workspace_size -- device workspace bytes lin_attn_chunk_bwd
- * needs: for every 16-token tile and head a 3,200-byte record, the float32
- * state at the tile start and the float32 gradient of the tile's end state
- * (B * H * ceil(T / 16) * (3200 + 8 * Dk * Dv) bytes).  -1 on invalid sizes
- * (message in lin_attn_last_error).
+ * needs.  Every 16-token tile and head takes a 3,200-byte record.  With
+ * LA_BF16 and Dv <= 128, the state and the gradient of the state are kept
+ * only at every fourth tile, as packed bf16 (hi, lo) words: B * H *
+ * (ceil(T / 16) * 3200 + ceil(T / 64) * 8 * Dk * Dv) bytes.  Otherwise
+ * (LA_FP32, or Dv > 128) both are kept at every tile in float32: B * H *
+ * ceil(T / 16) * (3200 + 8 * Dk * Dv) bytes.  -1 on invalid sizes (message in
+ * lin_attn_last_error).
  */
 long long lin_attn_chunk_bwd_workspace_size(int B, int T, int H, int Dk, int Dv, int dtype);
 
@@ -398,8 +401,13 @@ long long lin_attn_chunk_bwd_workspace_size(int B, int T, int H, int Dk, int Dv,
  * ...", sec. 2.3) and give the tiled forward pass ("Deep Dive ...", sec. 3.2);
  * they print no backward pass.  This entry point returns the gradients of
  * L = <o, dout> + <hT, dhT> with respect to every input of the forward pass,
- * computed over 16-token tiles in float32 (the forward states are recomputed,
- * the state gradient is carried backwards tile by tile).
+ * computed over 16-token tiles with float32 accumulation and float32 carried
+ * states (the forward states are recomputed, the state gradient is carried
+ * backwards tile by tile).  LA_FP32 runs its products on the float32 matrix
+ * cores.  LA_BF16 with Dv <= 128 runs them on the bf16 matrix cores, every
+ * float32 operand split into bf16 hi + lo parts (relative error 2^-16 per
+ * operand; the bf16 inputs enter exactly), and keeps the states only at
+ * every fourth tile, rebuilding those between inside the gradient kernel.
  *
  *   q, k, v, gate, beta, h0, gate_mode, G, sizes, dtype: as lin_attn_chunk_fwd
  *     (q and k 16-byte aligned; h0 may be NULL = zeros)
@@ -430,7 +438,10 @@ int lin_attn_chunk_bwd(const void* q, const void* k, const void* v,
  * lin_attn_chunk_bwd_varlen needs: H * (T / 16 + nseq + 1) tile slots (one per
  * 16 tokens of each packed sequence plus one spare per sequence for its
  * ragged end), each holding what lin_attn_chunk_bwd keeps per tile (3200 +
- * 8 * Dk * Dv bytes); -1 (with lin_attn_last_error() set) for invalid sizes.
+ * 8 * Dk * Dv bytes; with LA_BF16 and Dv <= 128 only the 3200-byte record,
+ * plus H * (T / 64 + nseq + 1) group slots of 8 * Dk * Dv bytes for the
+ * states kept at every fourth tile); -1 (with lin_attn_last_error() set) for
+ * invalid sizes.
  */
 long long lin_attn_chunk_bwd_varlen_workspace_size(int T, int nseq, int H, int Dk, int Dv,
                                                    int dtype);

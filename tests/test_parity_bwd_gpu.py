@@ -4,10 +4,16 @@ against the oracle's fp64 adjoint of the recurrence.
 Small cases compare every gradient element; the 64K x 16-head shape compares
 the last three tiles of every head (their gradients depend only on the tokens
 after them and on dhT, so the oracle runs from the state the fp64 forward
-recurrence reaches there).  The reverse pass computes in float32 from the
-exact input values (bf16 inputs convert to float32 exactly), so both input
-dtypes are held to the float32 bar of the forward pass: max|x - ref| /
-max|ref| <= 1e-5 per gradient tensor.
+recurrence reaches there).
+
+Bars, max|x - ref| / max|ref| per gradient tensor:
+  float32 inputs: 1e-5, the float32 bar of the forward pass (float32
+    products on the float32 matrix cores throughout);
+  bf16 inputs: 5e-5.  These run on the bf16 matrix cores with every float32
+    operand split into bf16 hi + lo parts, each carrying a relative error of
+    at most 2^-16 ~ 1.5e-5 (the inputs themselves enter exactly), and the
+    products and sums over d_k, d_v and 16 tokens add a few of those.  The
+    forward pass holds bf16 inputs to 1e-2.
 """
 
 import numpy as np
@@ -24,7 +30,12 @@ from parity_util import host, make_case, relerr, say
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
-TOL_BWD = 1e-5
+TOL_BWD = 1e-5          # float32 inputs
+TOL_BWD_BF16 = 5e-5     # bf16 inputs (split bf16 products)
+
+
+def tol(dtype):
+    return TOL_BWD_BF16 if dtype == "bf16" else TOL_BWD
 NAMES = ("dq", "dk", "dv", "dgate", "dbeta", "dh0")
 
 
@@ -79,7 +90,7 @@ def test_bwd_parity(case):
         errs[name] = relerr(xh, r)
     say("  " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
     for name, e in errs.items():
-        assert e <= TOL_BWD, f"{name}: error {e}"
+        assert e <= tol(dtype), f"{name}: error {e}"
 
 
 def test_bwd_empty_sequence_copies_dhT():
@@ -120,7 +131,7 @@ def test_bwd_long_64k_tail_tiles():
     for name, x, r in zip(NAMES[:5], got[:5], ref[:5]):
         e = relerr(host(x[:, t0:]), r)
         say(f"  {name} tail err={e:.2e}")
-        assert e <= TOL_BWD, f"{name}: error {e}"
+        assert e <= TOL_BWD_BF16, f"{name}: error {e}"
 
 
 def test_bwd_graph_capture_replays():
@@ -213,7 +224,7 @@ def test_bwd_varlen_parity(case):
         errs[name] = relerr(xh, r)
     say("  " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
     for name, e in errs.items():
-        assert e <= TOL_BWD, f"{name}: error {e}"
+        assert e <= tol(dtype), f"{name}: error {e}"
     for s_, n_ in enumerate(lengths):
         if n_ == 0:
             assert torch.equal(got[5][s_], dhT[s_])
@@ -299,7 +310,7 @@ def test_bwd_every_gradient_long(shape):
     worst = _compare_heads(got, res)
     say("  " + " ".join(f"{n}={e:.2e}" for n, e in worst.items()))
     for name, e in worst.items():
-        assert e <= TOL_BWD, f"{name}: error {e}"
+        assert e <= TOL_BWD_BF16, f"{name}: error {e}"
 
 
 def test_bwd_train_8k_weak_sampled_heads():
@@ -315,7 +326,7 @@ def test_bwd_train_8k_weak_sampled_heads():
     worst = _compare_heads(got, res)
     say("  " + " ".join(f"{n}={e:.2e}" for n, e in worst.items()))
     for name, e in worst.items():
-        assert e <= TOL_BWD, f"{name}: error {e}"
+        assert e <= TOL_BWD_BF16, f"{name}: error {e}"
 
 
 def test_bwd_varlen_weak_8k():
@@ -357,4 +368,4 @@ def test_bwd_varlen_weak_8k():
                 worst[name] = max(worst[name], relerr(xg, r[i]))
     say("  " + " ".join(f"{n}={e:.2e}" for n, e in worst.items()))
     for name, e in worst.items():
-        assert e <= TOL_BWD, f"{name}: error {e}"
+        assert e <= TOL_BWD_BF16, f"{name}: error {e}"
