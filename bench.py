@@ -66,9 +66,12 @@ def source_hash(names):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(which, workload):
-    """Counter-derived HBM bytes per call, or None once the kernels changed."""
-    t = TRAFFIC_KIB[which]
+def measured_traffic(which, workload=None):
+    """Counter-derived HBM bytes per call, or None once the kernels changed (or
+    for a workload other than the one the counters were taken on)."""
+    t = TRAFFIC_KIB.get(which)
+    if t is None:
+        return None
     if which == "chunk" and workload != "long_64k":
         return None
     if source_hash(t["sources"]) != t["sha256_16"]:
@@ -322,6 +325,7 @@ def main():
             "roofline": {"bound": "hbm", "achieved": vbytes / (vms * 1e-3) / 1e9,
                          "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                          "frac": vbytes / (vms * 1e-3) / PEAK_HBM, "alg_bytes_per_launch": vbytes,
+                         "traffic": measured_traffic("varlen"),
                          "kernel": "chunk_prep_kernel + chunk_state_kernel (packed sequences)"},
         }
         del vin, ov, hv, wsv
@@ -357,6 +361,8 @@ def main():
             "roofline": {"bound": "hbm", "achieved": cbytes / (cms * 1e-3) / 1e9,
                          "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                          "frac": cbytes / (cms * 1e-3) / PEAK_HBM, "alg_bytes_per_launch": cbytes,
+                         "traffic": (measured_traffic("channel")
+                                     if args.workload == "long_64k" else None),
                          "kernel": ("chunk_channel_prep_kernel + chunk_fwd_channel_kernel "
                                     "(one lin_attn_chunk_fwd_channel call)")},
         }
@@ -439,9 +445,9 @@ def main():
             "roofline": {"bound": "hbm", "achieved": bbytes / (bms * 1e-3) / 1e9,
                          "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                          "frac": bbytes / (bms * 1e-3) / PEAK_HBM, "alg_bytes_per_launch": bbytes,
-                         "kernel": ("bwd_prep_kernel + bwd_hstates_mfma_kernel + "
-                                    "bwd_dh_mfma_kernel + bwd_grad_kernel "
-                                    "(one lin_attn_chunk_bwd call)")},
+                         "traffic": measured_traffic("backward"),
+                         "kernel": ("bwd_prep_kernel + bwd2_hstates_kernel + bwd2_dh_kernel + "
+                                    "bwd2_grad_kernel (one lin_attn_chunk_bwd call, bf16 inputs)")},
         }
         del bin_, up, wsb
 
