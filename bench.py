@@ -36,9 +36,21 @@ CSRC = os.path.join(ROOT, "chunked_gated_linear_amd", "csrc")
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC_KIB = {
     "chunk": {"sources": ("chunk_pair.hip", "la_device.h"),
-              "sha256_16": "a3eacd17eeebd0cb",
+              "sha256_16": "7cf6e8faa6274eb5",
               # one call: the intra-tile launch and the 16 state launches of 64K x 16 heads
-              "fetch": 776823, "write": 488454},
+              "fetch": 776882, "write": 488452},
+    "varlen": {"sources": ("chunk_pair.hip", "la_device.h"),
+               "sha256_16": "7cf6e8faa6274eb5",
+               # one call on the 64-request packed batch (64K tokens, 16 heads)
+               "fetch": 824416, "write": 545851},
+    "channel": {"sources": ("chunk_channel.hip", "la_device.h"),
+                "sha256_16": "ad7daa0b6f826b69",
+                # one call at 64K x 16 heads: tile preparation + serial kernel
+                "fetch": 1296908, "write": 1476361},
+    "backward": {"sources": ("chunk_bwd_bf16.hip", "la_bwd.h", "la_device.h"),
+                 "sha256_16": "b105806cf36da517",
+                 # one call at B=4 H=16 T=8192: prep, states, state gradients, gradients
+                 "fetch": 3296736, "write": 2372134},
     "decode": {"sources": ("decode.hip", "la_device.h"),
                "sha256_16": "07feb0a03453c841",
                "fetch": 265755, "write": 526841},
