@@ -52,8 +52,9 @@ TRAFFIC_KIB = {
                  # one call at B=4 H=16 T=8192: prep, states, state gradients, gradients
                  "fetch": 3296736, "write": 2372134},
     "decode": {"sources": ("decode.hip", "la_device.h"),
-               "sha256_16": "07feb0a03453c841",
-               "fetch": 265755, "write": 526841},
+               "sha256_16": "f8c6337c80342a66",
+               # one step at B=256 H=32 d=128 (median of six dispatches)
+               "fetch": 265754, "write": 526921},
 }
 
 
