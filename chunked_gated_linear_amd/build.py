@@ -21,6 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "liblinattn.so")
 SOURCES = ["chunk_fwd.hip", "chunk_pair.hip", "chunk_bwd.hip", "chunk_bwd_bf16.hip", "chunk_channel.hip",
+           "chunk_channel_pair.hip",
            "decode.hip",
            "noalloc.hip", "lin_attn_abi.cpp"]
 ARCH = "gfx950"

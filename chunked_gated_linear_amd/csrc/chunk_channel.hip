@@ -42,12 +42,11 @@
 //       slice of d_v): wave 0 ("chain") owns the fp32 state slice in
 //       registers and runs the serial part; waves 1..NP ("loaders") copy the
 //       records and the slice's v values into LDS, double-buffered by epochs
-//       of NP tiles, their global loads issued two epochs before the chain
-//       reads them.  bf16 inputs with few workgroups: NP = 3, and each loader
-//       also forms the output of the tile its slot held, one epoch later,
-//       from a hand-off of the tile's bf16 starting state and U; otherwise
-//       NP = 2 and the chain forms the output itself (for bf16 in 78 KB of
+//       of NP = 2 tiles, their global loads issued two epochs before the
+//       chain reads them; the chain forms the outputs (for bf16 in 78 KB of
 //       LDS, so that two workgroups share a compute unit).
+// bf16 inputs with fewer workgroups than two per compute unit (a few long
+// sequences) take the 32-token pair path of chunk_channel_pair.hip instead.
 #include "la_device.h"
 #include "la_launch.h"
 
@@ -86,16 +85,10 @@ constexpr int kScrA = 0, kScrB = 1024, kScr = 1024 + 64;
 constexpr int kGcs = 8 * 64 * 16;
 constexpr int kKts = kScr, kPrepWave = kScr + kGcs + 128 * 4;
 
-// Records of two epochs of NP tiles; with OUTL (loaders form the outputs, bf16
-// inputs only) also the hand-off from the chain to the loader wave that
-// computes a tile's output: the tile's bf16 starting state and U, two epochs
-// of NP tiles.
-template <typename E, int DK, int NP, bool OUTL>
+// Records of two epochs of NP tiles.
+template <typename E, int DK, int NP>
 struct ChCfg {
-  static_assert(!OUTL || sizeof(E) == 2, "loader outputs use the bf16 state copy");
-  static constexpr int HAND = OUTL ? (DK / 32 + 1) * 64 * 16 : 0;   // bytes per tile
-  static constexpr int HAND_AT = 2 * NP * ChRec<DK, sizeof(E)>::LDS;
-  static constexpr int LDS = HAND_AT + 2 * NP * HAND;
+  static constexpr int LDS = 2 * NP * ChRec<DK, sizeof(E)>::LDS;
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
@@ -402,13 +395,13 @@ struct ChCopy {
 };
 
 // ------------------------------------------------------------ chain kernel
-template <typename E, int DK, int NP, bool OUTL>
+template <typename E, int DK, int NP>
 __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_channel_kernel(
     const E* __restrict__ v, const char* __restrict__ ws, const float* h0,
     E* __restrict__ o, float* hT, int B, int TA, int H, int DV, const int* __restrict__ cu,
     int nslot) {
   using R = ChRec<DK, sizeof(E)>;
-  using C = ChCfg<E, DK, NP, OUTL>;
+  using C = ChCfg<E, DK, NP>;
   using X = Elt<float>;
   using F16 = X::F16;
   using F32 = X::F32;
@@ -442,9 +435,6 @@ __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_channel_kernel(
 
   auto rowk = [&](int t) -> int64_t { return (tok0 + t) * H + h; };
   auto rec_of = [&](int ep, int j) -> char* { return smem + ((ep & 1) * NP + j) * R::LDS; };
-  auto hand_of = [&](int ep, int j) -> char* {
-    return smem + C::HAND_AT + ((ep & 1) * NP + j) * C::HAND;
-  };
   const int64_t ostride = (int64_t)H * DV;
   E* const orow = o + rowk(4 * grp) * DV + v0 + n;   // token 4 grp of the tile, column v0 + n
 
@@ -541,26 +531,17 @@ __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_channel_kernel(
             for (int i = 0; i < 4; ++i) Hacc[t][i] *= gc[t][i];   // row 16t + 4grp + i
             Hacc[t] = XB::mma32(kt[t], ub, Hacc[t]);
           }
-          if constexpr (OUTL) {
-            // the output, O = (Q o Gam) H + P U, is the loader's: hand over
-            // the state the tile started from and U
-            char* hand = hand_of(ep, j);
+          // the output after the state update: O = (Q o Gam) H + P U
+          f32x4 QH = zero4();
 #pragma unroll
-            for (int s2 = 0; s2 < NS; ++s2) reinterpret_cast<XB::F32*>(hand)[s2 * 64 + lane] = hb[s2];
-            reinterpret_cast<f32x4*>(hand + NS * 1024)[lane] = U;
-          } else {
-            // the output after the state update: O = (Q o Gam) H + P U
-            f32x4 QH = zero4();
+          for (int s2 = 0; s2 < NS; ++s2)
+            QH = XB::mma32(reinterpret_cast<const XB::F32*>(rec + R::QF)[s2 * 64 + lane], hb[s2], QH);
+          const F16 pf = reinterpret_cast<const F16*>(rec + R::PF)[lane];
+          const f32x4 O = X::mma16(pf, X::from_acc(U), QH);
+          E* oc = orow + (int64_t)(16 * c) * ostride;
 #pragma unroll
-            for (int s2 = 0; s2 < NS; ++s2)
-              QH = XB::mma32(reinterpret_cast<const XB::F32*>(rec + R::QF)[s2 * 64 + lane], hb[s2], QH);
-            const F16 pf = reinterpret_cast<const F16*>(rec + R::PF)[lane];
-            const f32x4 O = X::mma16(pf, X::from_acc(U), QH);
-            E* oc = orow + (int64_t)(16 * c) * ostride;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (16 * c + 4 * grp + i < T) oc[i * ostride] = Elt<E>::from_f(O[i]);
-          }
+          for (int i = 0; i < 4; ++i)
+            if (16 * c + 4 * grp + i < T) oc[i * ostride] = Elt<E>::from_f(O[i]);
         }
       }
       __syncthreads();  // this epoch consumed, next epoch loaded
@@ -611,34 +592,8 @@ __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_channel_kernel(
     reinterpret_cast<F16*>(rec + R::VF)[lane] = vf;
   };
 
-  // bf16 inputs: the output of tile e NP + p, from the chain's hand-off and
-  // the record still in this loader's slot (it is refilled only afterwards,
-  // by this same wave): O = (Q o Gam) H + P U on this wave's matrix core.
-  auto output = [&](int e) {
-    if constexpr (OUTL) {
-      const int c = e * NP + p;
-      if (e < 0 || c >= NC) return;
-      using XB = Elt<__bf16>;
-      const char* rec = rec_of(e, p);
-      const char* hand = hand_of(e, p);
-      f32x4 QH = zero4();
-#pragma unroll
-      for (int s = 0; s < NS; ++s)
-        QH = XB::mma32(reinterpret_cast<const XB::F32*>(rec + R::QF)[s * 64 + lane],
-                       reinterpret_cast<const XB::F32*>(hand)[s * 64 + lane], QH);
-      const f32x4 U = reinterpret_cast<const f32x4*>(hand + NS * 1024)[lane];
-      const F16 pf = reinterpret_cast<const F16*>(rec + R::PF)[lane];
-      const f32x4 O = X::mma16(pf, X::from_acc(U), QH);
-      E* oc = orow + (int64_t)(16 * c) * ostride;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (16 * c + 4 * grp + i < T) oc[i * ostride] = Elt<E>::from_f(O[i]);
-    }
-  };
-
   // Two register sets alternating by epoch: while tile (ep+1)*NP + p is
-  // stored from one, the loads for tile (ep+2)*NP + p fill the other.  The
-  // slot being refilled held epoch ep - 1, whose output is formed first.
+  // stored from one, the loads for tile (ep+2)*NP + p fill the other.
   // (Loads issued two epochs ahead, from a third set, measured no faster.)
   ChCopy<E, DK> ra, rb;
   load(ra, p);
@@ -647,23 +602,20 @@ __global__ __launch_bounds__(64 * (NP + 1)) void chunk_fwd_channel_kernel(
   __syncthreads();
   for (int ep = 0; ep < NE; ep += 2) {
     load(rb, (ep + 2) * NP + p);
-    output(ep - 1);
     store(ra, (ep + 1) * NP + p);
     __syncthreads();
     if (ep + 1 < NE) {
       load(ra, (ep + 3) * NP + p);
-      output(ep);
       store(rb, (ep + 2) * NP + p);
       __syncthreads();
     }
   }
-  output(NE - 1);               // the last epoch: its slot is not refilled
 }
 
 
 // B sequences of T tokens (cu == nullptr), or B packed sequences with device
 // offsets cu in one sequence of T tokens.
-template <typename E, int DK, int NP, bool OUTL>
+template <typename E, int DK, int NP>
 hipError_t launch_ch(const void* q, const void* k, const void* v, const float* gate,
                      int gate_logit, float G, const float* beta, const float* h0, void* o,
                      float* hT, int B, int T, int H, int Dv, const int* cu, void* ws,
@@ -680,7 +632,7 @@ hipError_t launch_ch(const void* q, const void* k, const void* v, const float* g
     if (e != hipSuccess) return e;
   }
   const int blocks = B * H * (Dv / 16);
-  hipLaunchKernelGGL((chunk_fwd_channel_kernel<E, DK, NP, OUTL>), dim3(blocks), dim3(64 * (NP + 1)),
+  hipLaunchKernelGGL((chunk_fwd_channel_kernel<E, DK, NP>), dim3(blocks), dim3(64 * (NP + 1)),
                      0, st, (const E*)v, (const char*)ws, h0, (E*)o, hT, B, T, H, Dv, cu, nslot);
   return hipGetLastError();
 }
@@ -780,11 +732,17 @@ hipError_t launch_dec_ch(const void* q, const void* k, const void* v, const floa
 
 }  // namespace
 
+// bf16 inputs take either the 16-token path or the 32-token pair path
+// (chunk_channel_pair.hip), chosen at launch from the workgroup count: the
+// workspace covers both.
 long long chunk_channel_workspace_bytes(int B, int T, int H, int Dk, int fp32) {
   const long long nc = (T + 15) / 16;
   const long long rec = fp32 ? (Dk == 64 ? ChRec<64, 4>::GLOBAL : ChRec<128, 4>::GLOBAL)
                              : (Dk == 64 ? ChRec<64, 2>::GLOBAL : ChRec<128, 2>::GLOBAL);
-  return (long long)B * H * nc * rec;
+  const long long one = (long long)B * H * nc * rec;
+  if (fp32) return one;
+  const long long pair = chunk_channel_pair_workspace_bytes(B, T, H, Dk);
+  return one > pair ? one : pair;
 }
 
 hipError_t launch_chunk_fwd_channel(const void* q, const void* k, const void* v,
@@ -803,25 +761,23 @@ hipError_t launch_chunk_fwd_channel_varlen(const void* q, const void* k, const v
                                            int Dv, int fp32, void* ws, hipStream_t st) {
 // Tiles per epoch (= loader waves) and who forms the outputs.  fp32: two, the
 // chain (the fp32 records take 110 KB).  bf16 with fewer workgroups than two
-// per compute unit (a few long sequences): three, the loaders (147 KB, one
-// workgroup per unit, each as fast as it can go).  bf16 with more (many
-// sequences or heads): two, the chain (78 KB: two workgroups share a unit).
-#define LA_CH(E, DK, NP, OUTL) \
-  return launch_ch<E, DK, NP, OUTL>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, \
+// per compute unit (a few long sequences): the 32-token pair path (144 KB,
+// one workgroup per unit, each as fast as it can go).  bf16 with more (many
+// sequences or heads): two tiles, the chain (78 KB: two workgroups share a
+// unit).
+#define LA_CH(E, DK, NP) \
+  return launch_ch<E, DK, NP>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, \
                                     cu, ws, st)
   if (fp32) {
-    if (Dk == 64) LA_CH(float, 64, 2, false);
-    if (Dk == 128) LA_CH(float, 128, 2, false);
+    if (Dk == 64) LA_CH(float, 64, 2);
+    if (Dk == 128) LA_CH(float, 128, 2);
   } else {
     const bool dense = (int64_t)B * H * (Dv / 16) >= 2 * (int64_t)device_cus();
-    if (Dk == 64) {
-      if (dense) LA_CH(__bf16, 64, 2, false);
-      LA_CH(__bf16, 64, 3, true);
-    }
-    if (Dk == 128) {
-      if (dense) LA_CH(__bf16, 128, 2, false);
-      LA_CH(__bf16, 128, 3, true);
-    }
+    if (!dense)
+      return launch_chunk_fwd_channel_pair(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T,
+                                           H, Dk, Dv, cu, ws, st);
+    if (Dk == 64) LA_CH(__bf16, 64, 2);
+    if (Dk == 128) LA_CH(__bf16, 128, 2);
   }
 #undef LA_CH
   return hipErrorInvalidValue;
@@ -830,7 +786,10 @@ hipError_t launch_chunk_fwd_channel_varlen(const void* q, const void* k, const v
 long long chunk_channel_varlen_workspace_bytes(int T, int nseq, int H, int Dk, int fp32) {
   const long long rec = fp32 ? (Dk == 64 ? ChRec<64, 4>::GLOBAL : ChRec<128, 4>::GLOBAL)
                              : (Dk == 64 ? ChRec<64, 2>::GLOBAL : ChRec<128, 2>::GLOBAL);
-  return (long long)H * channel_varlen_slots(T, nseq) * rec;
+  const long long one = (long long)H * channel_varlen_slots(T, nseq) * rec;
+  if (fp32) return one;
+  const long long pair = chunk_channel_pair_varlen_workspace_bytes(T, nseq, H, Dk);
+  return one > pair ? one : pair;
 }
 
 hipError_t launch_decode_channel(const void* q, const void* k, const void* v,

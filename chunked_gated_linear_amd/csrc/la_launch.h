@@ -119,6 +119,17 @@ long long chunk_channel_varlen_workspace_bytes(int T, int nseq, int H, int Dk, i
 // Workspace bytes of the per-channel path: one record per tile and head.
 long long chunk_channel_workspace_bytes(int B, int T, int H, int Dk, int fp32);
 
+// The per-channel path for bf16 inputs with the state stepped over 32-token
+// pairs of tiles (cu == nullptr: B sequences of T tokens; else B = nseq packed
+// sequences); workspace bytes of its records, batched and packed.
+hipError_t launch_chunk_fwd_channel_pair(const void* q, const void* k, const void* v,
+                                         const float* gate, int gate_logit, float G,
+                                         const float* beta, const float* h0, void* o, float* hT,
+                                         int B, int T, int H, int Dk, int Dv, const int* cu,
+                                         void* ws, hipStream_t st);
+long long chunk_channel_pair_workspace_bytes(int B, int T, int H, int Dk);
+long long chunk_channel_pair_varlen_workspace_bytes(int T, int nseq, int H, int Dk);
+
 // Decode step with a per-channel gate (gate [B*H, Dk]), state in place.
 hipError_t launch_decode_channel(const void* q, const void* k, const void* v,
                                  const float* gate, int gate_logit, float G, const float* beta,

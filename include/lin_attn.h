@@ -235,8 +235,11 @@ int lin_attn_chunk_fwd_channel(const void* q, const void* k, const void* v,
 /*
  * lin_attn_chunk_fwd_channel_workspace_size -- device workspace bytes of
  * lin_attn_chunk_fwd_channel: B * H * ceil(T / 16) * R, with R (Dk = 128 / 64)
- * = 27,136 / 14,592 for LA_FP32 and 18,944 / 10,496 for LA_BF16 (the
- * state-independent operators of each 16-token tile, prepared once per head);
+ * = 27,136 / 14,592 for LA_FP32 (the state-independent operators of each
+ * 16-token tile, prepared once per head); for LA_BF16 the larger of that with
+ * R = 18,944 / 10,496 and B * H * ceil(T / 32) * R2 with R2 = 31,232 / 18,688
+ * (the operators of each 32-token pair of tiles: the pass steps the state
+ * over tiles or pairs of tiles, whichever fills the device better);
  * 0 when T = 0; -1 (with
  * lin_attn_last_error() set) for invalid or unsupported sizes.
  */
@@ -344,6 +347,8 @@ int lin_attn_decode_step(const void* q, const void* k, const void* v,
  * lin_attn_chunk_fwd_channel_varlen: H * (T / 16 + nseq + 1) * R with R as in
  * lin_attn_chunk_fwd_channel_workspace_size (one record slot per 16 tokens of
  * each packed sequence plus one spare slot per sequence for its ragged end);
+ * for LA_BF16 the larger of that and H * (T / 32 + nseq + 1) * R2 (slots of
+ * 32-token pairs);
  * -1 (with lin_attn_last_error() set) for invalid or unsupported sizes.
  */
 long long lin_attn_chunk_fwd_channel_varlen_workspace_size(int T, int nseq, int H, int Dk,

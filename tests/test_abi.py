@@ -379,7 +379,10 @@ def test_chunk_fwd_channel_workspace_size():
     L = N.lib()
     assert L.lin_attn_chunk_fwd_channel_workspace_size(1, 64, 2, 128, 128, 0) == 2 * 4 * 18944
     assert L.lin_attn_chunk_fwd_channel_workspace_size(1, 64, 2, 128, 128, 1) == 2 * 4 * 27136
-    assert L.lin_attn_chunk_fwd_channel_workspace_size(1, 16, 1, 64, 64, 0) == 10496
+    # bf16: the larger of the 16-token records and the 32-token pair records
+    # (31,232 / 18,688 bytes per pair at Dk = 128 / 64)
+    assert L.lin_attn_chunk_fwd_channel_workspace_size(1, 16, 1, 64, 64, 0) == 18688
+    assert L.lin_attn_chunk_fwd_channel_workspace_size(1, 32, 1, 128, 64, 0) == 37888
     assert L.lin_attn_chunk_fwd_channel_workspace_size(2, 17, 3, 64, 32, 1) == 2 * 3 * 2 * 14592
     assert L.lin_attn_chunk_fwd_channel_workspace_size(1, 0, 2, 128, 128, 0) == 0
     assert L.lin_attn_chunk_fwd_channel_workspace_size(1, 64, 2, 96, 128, 0) == -1
@@ -443,7 +446,9 @@ def test_channel_varlen_rejects(kw, code, needle):
 def test_channel_varlen_workspace_size_and_empty():
     L = N.lib()
     assert L.lin_attn_chunk_fwd_channel_varlen_workspace_size(100, 3, 2, 128, 128, 0) == \
-        2 * (100 // 16 + 3 + 1) * 18944
+        max(2 * (100 // 16 + 3 + 1) * 18944, 2 * (100 // 32 + 3 + 1) * 31232)
+    assert L.lin_attn_chunk_fwd_channel_varlen_workspace_size(1000, 1, 2, 128, 128, 0) == \
+        max(2 * (1000 // 16 + 1 + 1) * 18944, 2 * (1000 // 32 + 1 + 1) * 31232)
     assert L.lin_attn_chunk_fwd_channel_varlen_workspace_size(100, 3, 2, 64, 32, 1) == \
         2 * (100 // 16 + 3 + 1) * 14592
     assert channel_varlen(nseq=0)[0] == N.LA_OK
