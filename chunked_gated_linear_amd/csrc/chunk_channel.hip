@@ -735,13 +735,13 @@ hipError_t launch_dec_ch(const void* q, const void* k, const void* v, const floa
 // bf16 inputs take either the 16-token path or the 32-token pair path
 // (chunk_channel_pair.hip), chosen at launch from the workgroup count: the
 // workspace covers both.
-long long chunk_channel_workspace_bytes(int B, int T, int H, int Dk, int fp32) {
+long long chunk_channel_workspace_bytes(int B, int T, int H, int Dk, int Dv, int fp32) {
   const long long nc = (T + 15) / 16;
   const long long rec = fp32 ? (Dk == 64 ? ChRec<64, 4>::GLOBAL : ChRec<128, 4>::GLOBAL)
                              : (Dk == 64 ? ChRec<64, 2>::GLOBAL : ChRec<128, 2>::GLOBAL);
   const long long one = (long long)B * H * nc * rec;
   if (fp32) return one;
-  const long long pair = chunk_channel_pair_workspace_bytes(B, T, H, Dk);
+  const long long pair = chunk_channel_pair_workspace_bytes(B, T, H, Dk, Dv);
   return one > pair ? one : pair;
 }
 

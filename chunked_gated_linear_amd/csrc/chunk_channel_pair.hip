@@ -142,23 +142,50 @@ __device__ inline int cp_seq_end(const int* cu, int s, int TB) {
   return min(max(cu[s + 1], cp_seq_begin(cu, s, TB)), TB);
 }
 
-// One wave per (sequence, head, pair).  Batched (cu == nullptr): job =
-// (b H + h) NP + p.  Packed: job = h nslot + slot, slot(s, p) = floor(cu[s] /
-// 32) + s + p, found by binary search over the offsets (unused slots skipped).
+// Arguments of one pass over tokens [0, T) of each sequence.  Batched (cu ==
+// nullptr): B sequences whose token t is row (b TB + t) H + h of the arrays
+// (the pointers may be advanced to a later token of every sequence; TB is the
+// full sequence length), records [sequence, head, pair].  Packed: B = nseq
+// sequences at device offsets cu in one sequence of T tokens, records at
+// slot(s, p) = floor(cu[s] / 32) + s + p of nslot per head.
+struct CpArgs {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  const float* gate;
+  int gate_logit;
+  float G;
+  const float* beta;
+  char* ws;
+  const float* h0;
+  __bf16* o;
+  float* hT;
+  int B, T, TB, H, DV;
+  const int* cu;
+  int nslot;
+};
+
+// Jobs first, first + step, ... of the (sequence, head, pair) records, one
+// wave each, with scratch `scr` (CpPrep::WAVE bytes of LDS).  Batched: job =
+// (b H + h) NPR + p.  Packed: job = h nslot + slot, the sequence found by
+// binary search over the offsets (unused slots skipped).
 template <int DK>
-__global__ __launch_bounds__(64 * kCpWaves) void chunk_channel_prep_pair_kernel(
-    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const float* __restrict__ gate,
-    int gate_logit, float G, const float* __restrict__ beta, char* __restrict__ ws, int B, int T,
-    int H, const int* __restrict__ cu, int nslot) {
+__device__ __forceinline__ void cp_prep_jobs(char* scr, int64_t first, int64_t step,
+                                             const CpArgs& a) {
   using R = CpRec<DK>;
   using PL = CpPrep<DK>;
   using F = Elt<float>;
   constexpr int NS = R::NS, NT = R::NT;
-  __shared__ __attribute__((aligned(16))) char smem[PL::LDS];
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const __bf16* __restrict__ const q = a.q;
+  const __bf16* __restrict__ const k = a.k;
+  const float* __restrict__ const gate = a.gate;
+  const float* __restrict__ const beta = a.beta;
+  char* __restrict__ const ws = a.ws;
+  const int* __restrict__ const cu = a.cu;
+  const int gate_logit = a.gate_logit, B = a.B, T = a.T, H = a.H, nslot = a.nslot;
+  const float G = a.G;
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, grp = lane >> 4;
-  char* scr = smem + wave * PL::WAVE;
   float* sA0 = reinterpret_cast<float*>(scr + kCpA0);
   float* sA1 = reinterpret_cast<float*>(scr + kCpA1);
   float* sB = reinterpret_cast<float*>(scr + kCpB);
@@ -167,38 +194,66 @@ __global__ __launch_bounds__(64 * kCpWaves) void chunk_channel_prep_pair_kernel(
   float* sgc = reinterpret_cast<float*>(scr + PL::GC);
   const int NPR = (T + 31) >> 5;
   const int64_t jobs = cu ? (int64_t)H * nslot : (int64_t)B * H * NPR;
-  for (int64_t job = (int64_t)blockIdx.x * kCpWaves + wave; job < jobs;
-       job += (int64_t)gridDim.x * kCpWaves) {
-    int c, h, Ts;
-    int64_t tok0;
-    if (cu) {
-      h = (int)(job / nslot);
-      const int slot = (int)(job - (int64_t)h * nslot);
-      int lo = 0, hi = B - 1;                    // the last s with slot(s, 0) <= slot
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (cp_seq_begin(cu, mid, T) / 32 + mid <= slot) lo = mid;
-        else hi = mid - 1;
+  // Job j's rows: token n of tile x (0: a, 1: b) is row[x] of the arrays, ok[x]
+  // whether it lies inside the sequence (rows past the end read the last
+  // valid row and are zeroed); returns the first job at or after j that has
+  // a pair (jobs if none).
+  auto find = [&](int64_t j, bool* ok, int64_t* row) -> int64_t {
+    for (; j < jobs; j += step) {
+      int c, h, Ts;
+      int64_t tok0;
+      if (cu) {
+        h = (int)(j / nslot);
+        const int slot = (int)(j - (int64_t)h * nslot);
+        int lo = 0, hi = B - 1;                  // the last s with slot(s, 0) <= slot
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (cp_seq_begin(cu, mid, T) / 32 + mid <= slot) lo = mid;
+          else hi = mid - 1;
+        }
+        const int tb = cp_seq_begin(cu, lo, T);
+        Ts = cp_seq_end(cu, lo, T) - tb;
+        c = slot - (tb / 32 + lo);
+        if (c < 0 || c >= ((Ts + 31) >> 5)) continue;   // a slot no pair uses
+        tok0 = tb;
+      } else {
+        c = (int)(j % NPR);
+        const int64_t bh = j / NPR;
+        h = (int)(bh % H);
+        tok0 = (bh / H) * (int64_t)a.TB;
+        Ts = T;
       }
-      const int tb = cp_seq_begin(cu, lo, T);
-      Ts = cp_seq_end(cu, lo, T) - tb;
-      c = slot - (tb / 32 + lo);
-      if (c < 0 || c >= ((Ts + 31) >> 5)) continue;   // a slot no pair uses
-      tok0 = tb;
-    } else {
-      c = (int)(job % NPR);
-      const int64_t bh = job / NPR;
-      h = (int)(bh % H);
-      tok0 = (bh / H) * (int64_t)T;
-      Ts = T;
-    }
-    char* wr = ws + job * R::GLOBAL;
-    // token n of tile x (0: a, 1: b); rows past the end read the last valid
-    // row and are zeroed below
-    const bool ok[2] = {32 * c + n < Ts, 32 * c + 16 + n < Ts};
-    int64_t row[2];
 #pragma unroll
-    for (int x = 0; x < 2; ++x) row[x] = (tok0 + min(32 * c + 16 * x + n, Ts - 1)) * H + h;
+      for (int x = 0; x < 2; ++x) {
+        ok[x] = 32 * c + 16 * x + n < Ts;
+        row[x] = (tok0 + min(32 * c + 16 * x + n, Ts - 1)) * H + h;
+      }
+      return j;
+    }
+    return jobs;
+  };
+  // One 32-deep channel block s of a job's k, q and gate: lane (n, grp)
+  // register j is channel 32 s + 16 (j >> 2) + 4 grp + (j & 3) of token n of
+  // each tile.
+  struct Raw { bf16x4 k0, k1, q0, q1; f32x4 g0, g1; };
+  auto load_block = [&](int s, const int64_t* row, Raw* r) {
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int64_t base = row[x] * DK + 32 * s + 4 * grp;
+      r[x].k0 = *reinterpret_cast<const bf16x4*>(k + base);
+      r[x].k1 = *reinterpret_cast<const bf16x4*>(k + base + 16);
+      r[x].q0 = *reinterpret_cast<const bf16x4*>(q + base);
+      r[x].q1 = *reinterpret_cast<const bf16x4*>(q + base + 16);
+      r[x].g0 = *reinterpret_cast<const f32x4*>(gate + base);
+      r[x].g1 = *reinterpret_cast<const f32x4*>(gate + base + 16);
+    }
+  };
+  // The loads of block s + 1 are issued before block s is worked on, so
+  // that a job waits for memory about once rather than once per block.
+  bool ok[2];
+  int64_t row[2];
+  for (int64_t job = find(first, ok, row); job < jobs; job = find(job + step, ok, row)) {
+    char* wr = ws + job * R::GLOBAL;
     const float ba = ok[0] ? beta[row[0]] : 0.f, bb = ok[1] ? beta[row[1]] : 0.f;
     if (grp == 0) {
       sB[n] = ba;
@@ -206,20 +261,16 @@ __global__ __launch_bounds__(64 * kCpWaves) void chunk_channel_prep_pair_kernel(
     }
     f32x4 s00 = zero4(), s11 = zero4(), s10 = zero4();
     f32x4 p00 = zero4(), p11 = zero4(), p10 = zero4();
-    // One 32-deep channel block s at a time; lane (n, grp) register j is
-    // channel 32 s + 16 (j >> 2) + 4 grp + (j & 3) of token n of each tile.
+    Raw raw[NS][2];
+    load_block(0, row, raw[0]);
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
+      if (s + 1 < NS) load_block(s + 1, row, raw[s + 1]);
       float kv[2][8], qv[2][8], gv[2][8];
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
-        const int64_t base = row[x] * DK + 32 * s + 4 * grp;
-        const bf16x4 k0 = *reinterpret_cast<const bf16x4*>(k + base);
-        const bf16x4 k1 = *reinterpret_cast<const bf16x4*>(k + base + 16);
-        const bf16x4 q0 = *reinterpret_cast<const bf16x4*>(q + base);
-        const bf16x4 q1 = *reinterpret_cast<const bf16x4*>(q + base + 16);
-        const f32x4 g0 = *reinterpret_cast<const f32x4*>(gate + base);
-        const f32x4 g1 = *reinterpret_cast<const f32x4*>(gate + base + 16);
+        const bf16x4 k0 = raw[s][x].k0, k1 = raw[s][x].k1, q0 = raw[s][x].q0, q1 = raw[s][x].q1;
+        const f32x4 g0 = raw[s][x].g0, g1 = raw[s][x].g1;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           kv[x][j] = ok[x] ? (float)k0[j] : 0.f;
@@ -391,6 +442,14 @@ __global__ __launch_bounds__(64 * kCpWaves) void chunk_channel_prep_pair_kernel(
   }
 }
 
+template <int DK>
+__global__ __launch_bounds__(64 * kCpWaves) void chunk_channel_prep_pair_kernel(CpArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[CpPrep<DK>::LDS];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  cp_prep_jobs<DK>(smem + wave * CpPrep<DK>::WAVE, (int64_t)blockIdx.x * kCpWaves + wave,
+                   (int64_t)gridDim.x * kCpWaves, a);
+}
+
 // ------------------------------------------------------------ state kernel
 // Waves: chain 0, output 1, loaders 2 .. NL + 1.  A wave's direct-to-LDS
 // loads move about 8 bytes per cycle however many are in flight, so the 32 KB
@@ -437,17 +496,20 @@ __device__ inline void cp_map_block(int n, int NH, int NV, int& head, int& vt) {
 }
 
 template <int DK, int NL, bool ROT>
-__global__ __launch_bounds__(64 * (NL + 2)) void chunk_fwd_channel_pair_kernel(
-    const __bf16* __restrict__ v, const char* __restrict__ ws, const float* h0,
-    __bf16* __restrict__ o, float* hT, int B, int TA, int H, int DV, const int* __restrict__ cu,
-    int nslot) {
+__device__ __forceinline__ void cp_state_body(char* smem, int blk, const CpArgs& a) {
   using R = CpRec<DK>;
   using C = CpCfg<DK, NL>;
   constexpr int NT = C::NT, NS = C::NS, NBUF = C::NBUF;
-  __shared__ __attribute__((aligned(256))) char smem[C::LDS];
+  const __bf16* __restrict__ const v = a.v;
+  const char* __restrict__ const ws = a.ws;
+  const float* const h0 = a.h0;
+  __bf16* __restrict__ const o = a.o;
+  float* const hT = a.hT;
+  const int* __restrict__ const cu = a.cu;
+  const int B = a.B, TA = a.T, H = a.H, DV = a.DV, nslot = a.nslot;
   const int NV = DV / 16;
   int head, vt;
-  cp_map_block(blockIdx.x, B * H, NV, head, vt);
+  cp_map_block(blk, B * H, NV, head, vt);
   const int b = head / H, h = head % H;
   const int v0 = vt * 16;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -463,7 +525,7 @@ __global__ __launch_bounds__(64 * (NL + 2)) void chunk_fwd_channel_pair_kernel(
     wsh = ws + ((int64_t)h * nslot + tb / 32 + b) * R::GLOBAL;
   } else {
     T = TA;
-    tok0 = (int64_t)b * TA;
+    tok0 = (int64_t)b * a.TB;
     wsh = ws + (int64_t)head * ((TA + 31) >> 5) * R::GLOBAL;
   }
   const int NPR = (T + 31) >> 5;
@@ -696,31 +758,96 @@ __global__ __launch_bounds__(64 * (NL + 2)) void chunk_fwd_channel_pair_kernel(
   }
 }
 
+// Blocks [0, nstate) carry the state over one stretch of the sequences (a
+// d_v slice each); any blocks after them prepare the records of the next
+// stretch (every wave a job at a time) on the compute units the state blocks
+// leave idle.  The two share no data within a launch.
+template <int DK, int NL, bool ROT>
+__global__ __launch_bounds__(64 * (NL + 2)) void chunk_fwd_channel_pair_kernel(
+    CpArgs sa, CpArgs pa, int nstate) {
+  using C = CpCfg<DK, NL>;
+  static_assert(C::WAVES * CpPrep<DK>::WAVE <= C::LDS, "the prep blocks use the same LDS");
+  __shared__ __attribute__((aligned(256))) char smem[C::LDS];
+  if ((int)blockIdx.x < nstate) {
+    cp_state_body<DK, NL, ROT>(smem, blockIdx.x, sa);
+  } else {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    cp_prep_jobs<DK>(smem + wave * CpPrep<DK>::WAVE,
+                     (int64_t)((int)blockIdx.x - nstate) * C::WAVES + wave,
+                     (int64_t)((int)gridDim.x - nstate) * C::WAVES, pa);
+  }
+}
+
+// Long batched sequences are cut into stretches of whole pairs: the records
+// of stretch 0 are prepared alone, then launch s carries the state over
+// stretch s while its extra blocks prepare stretch s + 1.  The fp32 state
+// passes from one stretch to the next through the workspace (read and
+// written in place by the workgroup that owns each slice), so the results are
+// those of one pass.  Sequences of kCpStretchPairs pairs or more may be cut
+// (the workspace then holds the carried state); stretches have at least
+// kCpMinStretchPairs pairs, and there are at most kCpMaxStretches.
+constexpr int kCpStretchPairs = 512;
+constexpr int kCpMinStretchPairs = 128;
+constexpr int kCpMaxStretches = 16;
+
 template <int DK>
 hipError_t launch_cp_t(const void* q, const void* k, const void* v, const float* gate,
                        int gate_logit, float G, const float* beta, const float* h0, void* o,
                        float* hT, int B, int T, int H, int Dv, const int* cu, void* ws,
                        hipStream_t st) {
-  const int NPR = (T + 31) / 32;
-  const int nslot = T / 32 + B + 1;
-  const int64_t jobs = cu ? (int64_t)H * nslot : (int64_t)B * H * NPR;
-  const int prep_blocks = (int)((jobs + kCpWaves - 1) / kCpWaves < 4096
-                                    ? (jobs + kCpWaves - 1) / kCpWaves : 4096);
-  if (prep_blocks > 0) {
-    hipLaunchKernelGGL((chunk_channel_prep_pair_kernel<DK>), dim3(prep_blocks),
-                       dim3(64 * kCpWaves), 0, st, (const __bf16*)q, (const __bf16*)k, gate,
-                       gate_logit, G, beta, (char*)ws, B, T, H, cu, nslot);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
   // four loader waves, each moving about 8 bytes per cycle into LDS (six
   // measured no faster: the chain sets the pace)
   constexpr int NL = 4;
-  const int blocks = B * H * (Dv / 16);
-  hipLaunchKernelGGL((chunk_fwd_channel_pair_kernel<DK, NL, true>), dim3(blocks), dim3(64 * (NL + 2)), 0, st,
-                     (const __bf16*)v, (const char*)ws, h0, (__bf16*)o, hT, B, T, H, Dv, cu,
-                     nslot);
-  return hipGetLastError();
+  using C = CpCfg<DK, NL>;
+  const int NPR = (T + 31) / 32;
+  const int nslot = T / 32 + B + 1;
+  const int nstate = B * H * (Dv / 16);
+  const int cus = device_cus();
+  int S = 1;
+  if (!cu && NPR >= kCpStretchPairs && 2 * nstate <= cus)
+    S = min(kCpMaxStretches, NPR / kCpMinStretchPairs);
+  char* const wsb = static_cast<char*>(ws);
+  float* const carry = reinterpret_cast<float*>(wsb + (int64_t)B * H * NPR * CpRec<DK>::GLOBAL);
+  auto stretch = [&](int s) {
+    const int p0 = (int)((int64_t)NPR * s / S), p1 = (int)((int64_t)NPR * (s + 1) / S);
+    const int64_t t0 = cu ? 0 : 32 * (int64_t)p0;
+    const int Ts = cu ? T : min(32 * p1, T) - 32 * p0;
+    CpArgs a{(const __bf16*)q + t0 * H * DK, (const __bf16*)k + t0 * H * DK,
+             (const __bf16*)v + t0 * H * Dv, gate + t0 * H * DK, gate_logit, G, beta + t0 * H,
+             wsb + (int64_t)B * H * p0 * CpRec<DK>::GLOBAL, s == 0 ? h0 : carry,
+             (__bf16*)o + t0 * H * Dv, s == S - 1 ? hT : carry, B, Ts, T, H, Dv, cu, nslot};
+    return a;
+  };
+  auto jobs = [&](const CpArgs& a) {
+    return cu ? (int64_t)H * nslot : (int64_t)B * H * ((a.T + 31) / 32);
+  };
+  {
+    const CpArgs a = stretch(0);
+    const int64_t pb = (jobs(a) + kCpWaves - 1) / kCpWaves;
+    const int prep_blocks = (int)(pb < 4096 ? pb : 4096);
+    if (prep_blocks > 0) {
+      hipLaunchKernelGGL((chunk_channel_prep_pair_kernel<DK>), dim3(prep_blocks),
+                         dim3(64 * kCpWaves), 0, st, a);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
+  for (int s = 0; s < S; ++s) {
+    const CpArgs sa = stretch(s);
+    CpArgs pa{};
+    int resident = 0;
+    if (s + 1 < S) {
+      pa = stretch(s + 1);
+      const int64_t need = (jobs(pa) + C::WAVES - 1) / C::WAVES;
+      resident = (int)min((int64_t)(cus - nstate), need);
+      if (resident < 1) resident = 1;
+    }
+    hipLaunchKernelGGL((chunk_fwd_channel_pair_kernel<DK, NL, true>), dim3(nstate + resident),
+                       dim3(64 * C::WAVES), 0, st, sa, pa, nstate);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace
@@ -729,8 +856,11 @@ static long long cp_record_bytes(int Dk) {
   return Dk == 64 ? CpRec<64>::GLOBAL : CpRec<128>::GLOBAL;
 }
 
-long long chunk_channel_pair_workspace_bytes(int B, int T, int H, int Dk) {
-  return (long long)B * H * ((T + 31) / 32) * cp_record_bytes(Dk);
+long long chunk_channel_pair_workspace_bytes(int B, int T, int H, int Dk, int Dv) {
+  const long long npr = (T + 31) / 32;
+  long long n = (long long)B * H * npr * cp_record_bytes(Dk);
+  if (npr >= kCpStretchPairs) n += (long long)B * H * Dk * Dv * 4;   // the carried state
+  return n;
 }
 
 long long chunk_channel_pair_varlen_workspace_bytes(int T, int nseq, int H, int Dk) {

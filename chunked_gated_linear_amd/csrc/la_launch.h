@@ -116,8 +116,9 @@ hipError_t launch_chunk_fwd_channel_varlen(const void* q, const void* k, const v
 // Workspace bytes of the packed per-channel path: H * (T / 16 + nseq + 1) records.
 long long chunk_channel_varlen_workspace_bytes(int T, int nseq, int H, int Dk, int fp32);
 
-// Workspace bytes of the per-channel path: one record per tile and head.
-long long chunk_channel_workspace_bytes(int B, int T, int H, int Dk, int fp32);
+// Workspace bytes of the per-channel path: one record per tile (or pair) and
+// head, and the carried state of long sequences.
+long long chunk_channel_workspace_bytes(int B, int T, int H, int Dk, int Dv, int fp32);
 
 // The per-channel path for bf16 inputs with the state stepped over 32-token
 // pairs of tiles (cu == nullptr: B sequences of T tokens; else B = nseq packed
@@ -127,7 +128,7 @@ hipError_t launch_chunk_fwd_channel_pair(const void* q, const void* k, const voi
                                          const float* beta, const float* h0, void* o, float* hT,
                                          int B, int T, int H, int Dk, int Dv, const int* cu,
                                          void* ws, hipStream_t st);
-long long chunk_channel_pair_workspace_bytes(int B, int T, int H, int Dk);
+long long chunk_channel_pair_workspace_bytes(int B, int T, int H, int Dk, int Dv);
 long long chunk_channel_pair_varlen_workspace_bytes(int T, int nseq, int H, int Dk);
 
 // Decode step with a per-channel gate (gate [B*H, Dk]), state in place.

@@ -113,8 +113,8 @@ long long chunk_workspace(int B, int T, int H, int Dk, int Dv, int dtype) {
   return dtype == LA_BF16 ? la::chunk_pair_workspace_bytes(B, T, H, Dk, Dv) : 0;
 }
 
-long long channel_workspace(int B, int T, int H, int Dk, int dtype) {
-  return T > 0 ? la::chunk_channel_workspace_bytes(B, T, H, Dk, dtype == LA_FP32) : 0;
+long long channel_workspace(int B, int T, int H, int Dk, int Dv, int dtype) {
+  return T > 0 ? la::chunk_channel_workspace_bytes(B, T, H, Dk, Dv, dtype == LA_FP32) : 0;
 }
 
 }  // namespace
@@ -195,7 +195,7 @@ int chunk_fwd(const void* q, const void* k, const void* v, const float* gate, in
   if (B == 0 || H == 0) return ok();
   const unsigned ea = dtype == LA_BF16 ? 2u : 4u;
   const long long wsz = T <= 0 ? 0
-                        : channel ? channel_workspace(B, T, H, Dk, dtype)
+                        : channel ? channel_workspace(B, T, H, Dk, Dv, dtype)
                                   : chunk_workspace(B, T, H, Dk, Dv, dtype);
   const int64_t ngate = channel ? ntok * Dk : ntok;   // gate elements
   if (T > 0) {
@@ -291,7 +291,7 @@ long long lin_attn_chunk_fwd_channel_workspace_size(int B, int T, int H, int Dk,
                                                    int dtype) {
   if (check_chunk_sizes(B, T, H, Dk, Dv, dtype)) return -1;
   ok();
-  return channel_workspace(B, T, H, Dk, dtype);
+  return channel_workspace(B, T, H, Dk, Dv, dtype);
 }
 
 int lin_attn_chunk_fwd_channel(const void* q, const void* k, const void* v, const float* gate,

@@ -141,6 +141,23 @@ def test_channel_long_64k_every_head(regime):
     assert eo <= 1e-2 and eh <= 1e-2
 
 
+@pytest.mark.parametrize("B,H,T,Dv", [(2, 2, 16 * 1024 + 37, 64), (1, 3, 20000, 128)])
+def test_channel_stretched_long_sequences(B, H, T, Dv):
+    # bf16 sequences of 512 pairs or more with few heads run in stretches: the
+    # state crosses each cut through the workspace; every output and the final
+    # state against the C copy of the per-channel recurrence, with h0 and a
+    # ragged end
+    say(f"channel stretched B={B} H={H} T={T} Dv={Dv}")
+    inp, gate, host_args = make(B, T, H, 128, Dv, "bf16", "weak", "logit", 0.02, seed=1003)
+    o, hT = lin_attn_chunk_fwd_channel(inp["q"], inp["k"], inp["v"], gate, inp["beta"], inp["h0"],
+                                       gate_mode="logit", G=5.0)
+    torch.cuda.synchronize()
+    ro, rh = crec.recurrent_fwd_channel(*host_args, workers=16)
+    eo, eh = relerr(host(o), ro), relerr(host(hT), rh)
+    say(f"  err(o)={eo:.2e} err(hT)={eh:.2e}")
+    assert eo <= 1e-2 and eh <= 1e-2
+
+
 def test_channel_hT_in_place_of_h0():
     inp, gate, host_args = make(1, 70, 2, 128, 64, "fp32", "weak", "logit", 0.02, seed=45)
     h = inp["h0"].clone()
