@@ -43,10 +43,11 @@ TRAFFIC_KIB = {
                "sha256_16": "7cf6e8faa6274eb5",
                # one call on the 64-request packed batch (64K tokens, 16 heads)
                "fetch": 824416, "write": 545851},
-    "channel": {"sources": ("chunk_channel.hip", "la_device.h"),
-                "sha256_16": "ad7daa0b6f826b69",
-                # one call at 64K x 16 heads: tile preparation + serial kernel
-                "fetch": 1296908, "write": 1476361},
+    "channel": {"sources": ("chunk_channel.hip", "chunk_channel_pair.hip", "la_device.h"),
+                "sha256_16": "0f24b3a4c5929fde",
+                # one call at 64K x 16 heads: the pair preparation of stretch 0 and
+                # the 16 stretch launches (state + next stretch's preparation)
+                "fetch": 1224072, "write": 1277957},
     "backward": {"sources": ("chunk_bwd_bf16.hip", "la_bwd.h", "la_device.h"),
                  "sha256_16": "b105806cf36da517",
                  # one call at B=4 H=16 T=8192: prep, states, state gradients, gradients
@@ -376,8 +377,10 @@ def main():
                          "frac": cbytes / (cms * 1e-3) / PEAK_HBM, "alg_bytes_per_launch": cbytes,
                          "traffic": (measured_traffic("channel")
                                      if args.workload == "long_64k" else None),
-                         "kernel": ("chunk_channel_prep_kernel + chunk_fwd_channel_kernel "
-                                    "(one lin_attn_chunk_fwd_channel call)")},
+                         "kernel": ("chunk_channel_prep_pair_kernel + 16 x "
+                                    "chunk_fwd_channel_pair_kernel (one lin_attn_chunk_fwd_channel "
+                                    "call: stretch launches, each with the next stretch's "
+                                    "preparation beside the state)")},
         }
         del xc, oc, hc, wsc
 
