@@ -539,9 +539,20 @@ struct StateArgs {
   int B, T, TB, H, DV;
   const int* cu;     // packed sequences, as in PrepArgs
   int nslot;
+  // Transition slices (the segmented form of long sequences): ntr further
+  // slices of 16 columns after the DV / 16 value slices carry the state map
+  // of the pass applied to h0tr ([B, H, DK, DK]; the identity when null),
+  // with v = 0 (read from the zero block zv, 1 KB) and no outputs, and leave
+  // the result in htr ([B, H, DK, DK]).  o may be null: no outputs stored.
+  int ntr;
+  const float* h0tr;
+  float* htr;
+  const __bf16* zv;
 };
 
-template <int DK, int SPW>
+// TR: the launch may hold transition slices (sa.ntr > 0); otherwise that
+// code is compiled out.
+template <int DK, int SPW, bool TR>
 __device__ __forceinline__ void state_body(char* smem, int blk, const StateArgs& sa) {
   using C = CfgS<DK, SPW>;
   constexpr int NT = C::NT, NS = C::NS, NBUF = C::NBUF;
@@ -554,7 +565,8 @@ __device__ __forceinline__ void state_body(char* smem, int blk, const StateArgs&
   float* const hT = sa.hT;
   const int B = sa.B, H = sa.H, DV = sa.DV;
 
-  const int NV = DV / 16, NVG = NV / SPW;       // slices, slice groups per head
+  const int NVV = DV / 16;                      // value slices
+  const int NV = NVV + (TR ? sa.ntr : 0), NVG = NV / SPW;   // slices, slice groups per head
   int head, vg;
   map_block(blk, B * H, NVG, head, vg);
   const int b = head / H, h = head % H;
@@ -562,6 +574,8 @@ __device__ __forceinline__ void state_body(char* smem, int blk, const StateArgs&
   // the slice of a chain or output wave
   const int vt = vg * SPW + (wave < C::W_OUT ? wave : wave < C::W_LOADER ? wave - C::W_OUT : 0);
   const int v0 = vt * 16;
+  const bool tr = TR && vt >= NVV;                        // a transition slice
+  const int tcol = 16 * (vt - NVV);                       // its first column of the map
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, grp = lane >> 4;
   int T;
@@ -580,7 +594,13 @@ __device__ __forceinline__ void state_body(char* smem, int blk, const StateArgs&
   const int NSC = (T + 31) >> 5;                          // pairs of tiles
   if (NSC == 0) {
     // an empty packed sequence: hT = h0 (zeros without h0), by the chain waves
-    if (wave < C::W_OUT && hT) {
+    if (wave < C::W_OUT && tr && sa.htr) {
+      const int64_t tbase = ((int64_t)b * H + h) * DK * DK;
+      for (int r = 0; r < DK; r += 4) {
+        const int64_t e = tbase + (int64_t)(r + grp) * DK + tcol + n;
+        sa.htr[e] = sa.h0tr ? sa.h0tr[e] : (r + grp == tcol + n ? 1.f : 0.f);
+      }
+    } else if (wave < C::W_OUT && !tr && hT) {
       const int64_t sbase = ((int64_t)b * H + h) * DK * DV;
       for (int r = 0; r < DK; r += 4)
         hT[sbase + (int64_t)(r + grp) * DV + v0 + n] = h0 ? h0[sbase + (int64_t)(r + grp) * DV + v0 + n] : 0.f;
@@ -655,7 +675,11 @@ __device__ __forceinline__ void state_body(char* smem, int blk, const StateArgs&
     const int lrow = lane >> 2, lchunk = (lane & 3) ^ rsw(lane >> 2);
     const __bf16* const kb0 = k + tok0 * DK + 8 * lchunk;
     const __bf16* const qb0 = q + tok0 * DK + 8 * lchunk;
+    // a group of transition slices reads its zero v from zv (lane L: bytes
+    // 16 L .. 16 L + 15 of the 1 KB block)
+    const bool trg = TR && vg * SPW >= NVV;
     const __bf16* const vb0 = v + tok0 * DV + 16 * vg * SPW + 8 * (lane & 1);
+    const __bf16* const zvl = sa.zv + 8 * lane;
     auto issue = [&](int c) {
       c = min(c, NSC - 1);
       char* rec = rec_of(c);
@@ -671,7 +695,8 @@ __device__ __forceinline__ void state_body(char* smem, int blk, const StateArgs&
       {  // V of each slice: lane L fetches 8 columns (half L % 2) of token L / 2 of the pair
         const int t = min(32 * c + (lane >> 1), T - 1);
 #pragma unroll
-        for (int sl = 0; sl < SPW; ++sl) lds_dma16(vb0 + t * H * DV + 16 * sl, rec + C::VF + sl * 1024);
+        for (int sl = 0; sl < SPW; ++sl)
+          lds_dma16(trg ? zvl : vb0 + t * H * DV + 16 * sl, rec + C::VF + sl * 1024);
       }
       const char* wr = wsh + (int64_t)c * WsRec::BYTES + 16 * lane;
 #pragma unroll
@@ -697,12 +722,15 @@ __device__ __forceinline__ void state_body(char* smem, int blk, const StateArgs&
     // ------------------------------------------------------------ chain wave
     f32x4 Hacc[NT];
     const int64_t sbase = ((int64_t)b * H + h) * DK * DV;
+    const int64_t tbase = ((int64_t)b * H + h) * DK * DK;
     auto srow = [&](int t, int i) { return 32 * (t >> 1) + 8 * grp + 4 * (t & 1) + i; };
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        Hacc[t][i] = h0 ? h0[sbase + (int64_t)srow(t, i) * DV + v0 + n] : 0.f;
+        Hacc[t][i] = !tr ? (h0 ? h0[sbase + (int64_t)srow(t, i) * DV + v0 + n] : 0.f)
+                   : sa.h0tr ? sa.h0tr[tbase + (int64_t)srow(t, i) * DK + tcol + n]
+                             : (srow(t, i) == tcol + n ? 1.f : 0.f);
     bf16x8 Hb[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) Hb[s] = cat8(hi4(Hacc[2 * s]), hi4(Hacc[2 * s + 1]));
@@ -806,12 +834,18 @@ __device__ __forceinline__ void state_body(char* smem, int blk, const StateArgs&
       if (c + 1 < NSC) pair(c + 1, Bo, A);
     }
     wg_barrier();                  // the output wave's last pair
-    if (hT) {
+    if (!tr && hT) {
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           hT[sbase + (int64_t)srow(t, i) * DV + v0 + n] = Hacc[t][i];
+    } else if (tr && sa.htr) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          sa.htr[tbase + (int64_t)srow(t, i) * DK + tcol + n] = Hacc[t][i];
     }
     return;
   }
@@ -826,6 +860,7 @@ __device__ __forceinline__ void state_body(char* smem, int blk, const StateArgs&
   // ends with columns 4 grp .. 4 grp + 3 of token n: one 8-byte store per tile.
   {
     constexpr int kDepth = 4;
+    const bool store_o = o && !tr;
     __bf16* const orow = o + (tok0 + (int64_t)n * H) * DV + v0 + 4 * grp;
     const int ostride = H * DV;
     const char* const obh = smem + C::OFF_OB + 2 * (vt - vg * SPW) * C::OB + C::OB_H + 16 * lane;
@@ -866,8 +901,8 @@ __device__ __forceinline__ void state_body(char* smem, int blk, const StateArgs&
       Ob = mma32b(cat8(uah, ubh), x.pf1l, Ob);
       Ob = mma32b(cat8(ual, ubl), x.pf1h, Ob);
       __bf16* oc = orow + (int64_t)(32 * c) * ostride;
-      if (32 * c + n < T) *reinterpret_cast<bf16x4*>(oc) = hi4(Oa);
-      if (32 * c + 16 + n < T) *reinterpret_cast<bf16x4*>(oc + 16 * ostride) = hi4(Ob);
+      if (store_o && 32 * c + n < T) *reinterpret_cast<bf16x4*>(oc) = hi4(Oa);
+      if (store_o && 32 * c + 16 + n < T) *reinterpret_cast<bf16x4*>(oc + 16 * ostride) = hi4(Ob);
     };
     Oin s0, s1, s2, s3;
     static_assert(kDepth == 4, "four register sets below");
@@ -908,12 +943,35 @@ __global__ __launch_bounds__(64 * (2 * SPW + 2)) void chunk_state_kernel(
   static_assert(kPrepLDS <= CfgS<DK, SPW>::LDS, "the intra-tile blocks use the same LDS");
   __shared__ __attribute__((aligned(256))) char smem[CfgS<DK, SPW>::LDS];
   if ((int)blockIdx.x < nstate) {
-    state_body<DK, SPW>(smem, blockIdx.x, sa);
+    state_body<DK, SPW, false>(smem, blockIdx.x, sa);
   } else if ((threadIdx.x >> 6) < kPrepWaves) {
     // the intra-tile blocks (their first kPrepWaves waves) each walk the jobs
     // in steps of their number
     const int step = (int)gridDim.x - nstate;
     for (int pb = (int)blockIdx.x - nstate; pb < prep_blocks; pb += step) prep_body<DK>(smem, pb, pa);
+  }
+}
+
+// The segmented form's launch: blocks [0, nsa) carry the state over a stretch
+// of the sequences described by sa, blocks [nsa, nsa + nsb) over one of those
+// described by sb (two segments side by side, one slice per workgroup); any
+// blocks after them do the intra-tile work of the jobs of pba blocks of pa,
+// then pbb of pb.
+template <int DK>
+__global__ __launch_bounds__(64 * 4) void chunk_state_seg_kernel(
+    StateArgs sa, StateArgs sb, int nsa, int nsb, PrepArgs pa, PrepArgs pb, int pba, int pbb) {
+  static_assert(kPrepLDS <= CfgS<DK, 1>::LDS, "the intra-tile blocks use the same LDS");
+  __shared__ __attribute__((aligned(256))) char smem[CfgS<DK, 1>::LDS];
+  const int blk = blockIdx.x;
+  if (blk < nsa + nsb) {
+    const bool second = blk >= nsa;
+    state_body<DK, 1, true>(smem, second ? blk - nsa : blk, second ? sb : sa);
+  } else if ((threadIdx.x >> 6) < kPrepWaves) {
+    const int step = (int)gridDim.x - nsa - nsb;
+    for (int p = blk - nsa - nsb; p < pba + pbb; p += step) {
+      const bool second = p >= pba;
+      prep_body<DK>(smem, second ? p - pba : p, second ? pb : pa);
+    }
   }
 }
 
@@ -944,6 +1002,167 @@ constexpr int kPrepResidentMin = 16;
 static bool stretch_area(int NSC) { return NSC >= kStretchAreaPairs; }
 
 
+// ---------------------------------------------------- segmented long sequences
+// With few heads the state workgroups leave most compute units idle and the
+// serial length T / 32 pairs sets the time.  Long sequences are then cut into
+// three segments of pairs, and since the state map of a pair is affine,
+// H_out = M H_in + C, the middle segment's map can be formed before its
+// start state is known: pass A carries segment 0 from h0 and, side by side,
+// segment 1 from zero together with DK / 16 transition slices that carry M
+// (the identity stepped with v = 0); a combine step forms segment 2's start
+// state M_1 H_1 + C_1; pass B carries segments 1 and 2 from their true start
+// states and writes their outputs.  The serial length drops to about 2 T / 3
+// pairs.  Each pass runs in stretches with the next stretch's intra-tile work
+// beside it, as the one-segment form does.
+constexpr int kSegAreaPairs = 3 * kStretchAreaPairs;
+
+static bool seg_area(int NSC) { return NSC >= kSegAreaPairs; }
+
+// out = A Hs + Bv per (sequence, head): A [DK, DK], Hs, Bv, out [DK, DV]
+// float32.  One block per (sequence-head, 16 columns); thread: one row,
+// 16 / (256 / DK) columns.
+template <int DK>
+__global__ __launch_bounds__(256) void seg_combine_kernel(const float* __restrict__ A,
+                                                          const float* __restrict__ Hs,
+                                                          const float* __restrict__ Bv,
+                                                          float* __restrict__ out, int DV) {
+  constexpr int TPR = 256 / DK, CPT = 16 / TPR;
+  const int NVs = DV / 16;
+  const int64_t bh = blockIdx.x / NVs;
+  const int cs = (int)(blockIdx.x - bh * NVs);
+  const int r = threadIdx.x / TPR, c0 = 16 * cs + (threadIdx.x % TPR) * CPT;
+  const float* __restrict__ a = A + (bh * DK + r) * DK;
+  const float* __restrict__ hs = Hs + bh * DK * DV + c0;
+  float acc[CPT];
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) acc[j] = Bv[(bh * DK + r) * DV + c0 + j];
+  for (int kk = 0; kk < DK; ++kk) {
+    const float av = a[kk];
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) acc[j] = fmaf(av, hs[(int64_t)kk * DV + j], acc[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) out[(bh * DK + r) * DV + c0 + j] = acc[j];
+}
+
+__global__ void zero_block_kernel(uint4* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = uint4{0u, 0u, 0u, 0u};
+}
+
+// Workspace of the segmented form after the records: float32 carry0, carry1,
+// hs1, c1, hs2 [B, H, DK, Dv] each, carryT, m1 [B, H, DK, DK] each, then the
+// 1 KB zero block.
+template <int DK>
+static hipError_t launch_pair_seg_t(const void* q, const void* k, const void* v,
+                                    const float* gate, int gate_logit, float G, const float* beta,
+                                    const float* h0, void* o, float* hT, int B, int T, int H,
+                                    int Dv, int raw, void* ws, hipStream_t st, const float* gsc,
+                                    const float* gbi) {
+  const int NSC = (T + 31) / 32;
+  const int cus = device_cus();
+  const int NV = Dv / 16, NTR = DK / 16;
+  const int nst0 = B * H * NV, nst1 = B * H * (NV + NTR);
+  const int P[4] = {0, NSC / 3, 2 * (NSC / 3), NSC};
+  const int S = min(kMaxStretches, max(1, (P[1] - P[0]) / kStretchMinPairs));
+  char* const wsb = static_cast<char*>(ws);
+  const int64_t nst = (int64_t)B * H * DK * Dv, ntt = (int64_t)B * H * DK * DK;
+  float* const carry0 = reinterpret_cast<float*>(wsb + (int64_t)B * H * NSC * WsRec::BYTES);
+  float* const carry1 = carry0 + nst;
+  float* const hs1 = carry1 + nst;
+  float* const c1 = hs1 + nst;
+  float* const hs2 = c1 + nst;
+  float* const carryT = hs2 + nst;
+  float* const m1 = carryT + ntt;
+  __bf16* const zv = reinterpret_cast<__bf16*>(m1 + ntt);
+  // pairs [p0, p1) of stretch s of segment g
+  auto span = [&](int g, int s, int& p0, int& p1) {
+    const int len = P[g + 1] - P[g];
+    p0 = P[g] + (int)((int64_t)len * s / S);
+    p1 = P[g] + (int)((int64_t)len * (s + 1) / S);
+  };
+  auto prep_args = [&](int g, int s) {
+    int p0, p1;
+    span(g, s, p0, p1);
+    const int64_t t0 = 32 * (int64_t)p0;
+    PrepArgs a{(const __bf16*)q + t0 * H * DK, (const __bf16*)k + t0 * H * DK,
+               gate + t0 * H, beta + t0 * H, wsb + (int64_t)B * H * p0 * WsRec::BYTES,
+               gate_logit, G, B, min(32 * p1, T) - 32 * p0, T, H, raw};
+    a.gsc = gsc;
+    a.gbi = gbi;
+    return a;
+  };
+  auto prep_blocks = [&](int g, int s) {
+    int p0, p1;
+    span(g, s, p0, p1);
+    return (int)(((int64_t)B * H * (p1 - p0) + kPrepWaves - 1) / kPrepWaves);
+  };
+  auto state_args = [&](int g, int s, const float* hin, float* hout, bool out, int ntr,
+                        const float* tin, float* tout) {
+    int p0, p1;
+    span(g, s, p0, p1);
+    const int64_t t0 = 32 * (int64_t)p0;
+    StateArgs a{(const __bf16*)q + t0 * H * DK, (const __bf16*)k + t0 * H * DK,
+                (const __bf16*)v + t0 * H * Dv, wsb + (int64_t)B * H * p0 * WsRec::BYTES, hin,
+                out ? (__bf16*)o + t0 * H * Dv : nullptr, hout, B, min(32 * p1, T) - 32 * p0, T,
+                H, Dv};
+    a.ntr = ntr;
+    a.h0tr = tin;
+    a.htr = tout;
+    a.zv = zv;
+    return a;
+  };
+  constexpr int kThreads = CfgS<DK, 1>::THREADS;
+  auto launch = [&](const StateArgs& sa, const StateArgs& sb, int nsa, int nsb,
+                    const PrepArgs& pa, const PrepArgs& pb, int pba, int pbb) {
+    const int idle = cus - nsa - nsb;
+    const int resident = pba + pbb > 0 ? max(1, min(idle, pba + pbb)) : 0;
+    hipLaunchKernelGGL((chunk_state_seg_kernel<DK>), dim3(nsa + nsb + resident), dim3(kThreads),
+                       0, st, sa, sb, nsa, nsb, pa, pb, pba, pbb);
+    return hipGetLastError();
+  };
+  hipLaunchKernelGGL(zero_block_kernel, dim3(1), dim3(64), 0, st, reinterpret_cast<uint4*>(zv), 64);
+  for (int g = 0; g < 2; ++g) {
+    hipLaunchKernelGGL((chunk_prep_kernel<DK>), dim3((unsigned)prep_blocks(g, 0)),
+                       dim3(64 * kPrepWaves), 0, st, prep_args(g, 0));
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // pass A: segment 0 from h0, segment 1 from zero with its state map
+  for (int s = 0; s < S; ++s) {
+    const bool last = s == S - 1;
+    const StateArgs sa = state_args(0, s, s == 0 ? h0 : carry0, last ? hs1 : carry0, true, 0,
+                                    nullptr, nullptr);
+    const StateArgs sb = state_args(1, s, s == 0 ? nullptr : carry1, last ? c1 : carry1, false,
+                                    NTR, s == 0 ? nullptr : carryT, last ? m1 : carryT);
+    if (!last)
+      e = launch(sa, sb, nst0, nst1, prep_args(0, s + 1), prep_args(1, s + 1),
+                 prep_blocks(0, s + 1), prep_blocks(1, s + 1));
+    else   // beside the last stretch: segment 2's first stretch
+      e = launch(sa, sb, nst0, nst1, prep_args(2, 0), PrepArgs{}, prep_blocks(2, 0), 0);
+    if (e != hipSuccess) return e;
+  }
+  // segment 2's start state
+  hipLaunchKernelGGL((seg_combine_kernel<DK>), dim3(B * H * NV), dim3(256), 0, st,
+                     (const float*)m1, (const float*)hs1, (const float*)c1, hs2, Dv);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // pass B: segments 1 and 2 from their start states, with outputs
+  for (int s = 0; s < S; ++s) {
+    const bool last = s == S - 1;
+    const StateArgs sa = state_args(1, s, s == 0 ? hs1 : carry0, last ? nullptr : carry0, true,
+                                    0, nullptr, nullptr);
+    const StateArgs sb = state_args(2, s, s == 0 ? hs2 : carry1, last ? hT : carry1, true, 0,
+                                    nullptr, nullptr);
+    if (!last)
+      e = launch(sa, sb, nst0, nst0, prep_args(2, s + 1), PrepArgs{}, prep_blocks(2, s + 1), 0);
+    else
+      e = launch(sa, sb, nst0, nst0, PrepArgs{}, PrepArgs{}, 0, 0);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 template <int DK>
 static hipError_t launch_pair_t(const void* q, const void* k, const void* v, const float* gate,
                                 int gate_logit, float G, const float* beta, const float* h0,
@@ -956,6 +1175,9 @@ static hipError_t launch_pair_t(const void* q, const void* k, const void* v, con
   const int NV = Dv / 16;
   const int spw = (NV % 2 == 0 && (int64_t)B * H * NV > cus) ? 2 : 1;
   const int nstate = B * H * (NV / spw);
+  if (seg_area(NSC) && spw == 1 && B * H * (2 * NV + DK / 16) <= cus - 16)
+    return launch_pair_seg_t<DK>(q, k, v, gate, gate_logit, G, beta, h0, o, hT, B, T, H, Dv, raw,
+                                 ws, st, gsc, gbi);
   int S = 1;
   if (stretch_area(NSC) && 2 * nstate <= cus) S = min(kMaxStretches, NSC / kStretchMinPairs);
   const int per_head = raw ? kPrepResidentPerHeadRaw : kPrepResidentPerHead;
@@ -1019,6 +1241,8 @@ long long chunk_pair_workspace_bytes(int B, int T, int H, int Dk, int Dv) {
   const int NSC = (T + 31) / 32;
   long long n = (long long)B * H * NSC * WsRec::BYTES;
   if (stretch_area(NSC)) n += (long long)B * H * Dk * Dv * 4;
+  // the segmented form's further states, state maps and zero block
+  if (seg_area(NSC)) n += (long long)B * H * (4LL * Dk * Dv + 2LL * Dk * Dk) * 4 + 1024;
   return n;
 }
 

@@ -112,7 +112,14 @@ def test_workspace_size():
     # from 512 pairs of tiles on, one fp32 state per head follows the records
     assert ws(1, 32 * 511, 2, 128, 128, N.LA_BF16) == 2 * 511 * 6656
     assert ws(1, 32 * 511 + 1, 2, 128, 64, N.LA_BF16) == 2 * 512 * 6656 + 2 * 128 * 64 * 4
-    assert ws(1, 65536, 16, 128, 128, N.LA_BF16) == 16 * 2048 * 6656 + 16 * 128 * 128 * 4
+    assert ws(1, 32 * 1535, 2, 128, 64, N.LA_BF16) == 2 * 1535 * 6656 + 2 * 128 * 64 * 4
+    # from 1536 pairs on, the segmented form's further states, state maps
+    # and a 1 KB zero block follow
+    seg = lambda B, H, dk, dv: B * H * (4 * dk * dv + 2 * dk * dk) * 4 + 1024
+    assert ws(1, 32 * 1536, 2, 128, 64, N.LA_BF16) == \
+        2 * 1536 * 6656 + 2 * 128 * 64 * 4 + seg(1, 2, 128, 64)
+    assert ws(1, 65536, 16, 128, 128, N.LA_BF16) == \
+        16 * 2048 * 6656 + 16 * 128 * 128 * 4 + seg(1, 16, 128, 128)
     assert ws(2, 0, 4, 128, 64, N.LA_BF16) == 0
     # fp32 runs one fused kernel without a workspace
     assert ws(1, 4096, 8, 128, 128, N.LA_FP32) == 0

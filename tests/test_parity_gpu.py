@@ -225,6 +225,38 @@ def test_stretches(case):
     assert h3 is None and torch.equal(o3, o)
 
 
+SEG_CASES = [
+    # B, H, T, Dk, Dv, regime: few heads and 1536 pairs or more: three segments
+    (1, 2, 3 * 16384 + 37, 128, 128, "weak"),
+    (1, 3, 3 * 16400, 64, 64, "weak"),
+    (1, 2, 3 * 16384 + 37, 128, 128, "std"),
+]
+
+
+@pytest.mark.parametrize("case", SEG_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_segmented(case):
+    """Long sequences with few heads run as three segments: segment 1's state
+    map M_1 (DK / 16 transition slices stepped from the identity with v = 0)
+    and its state C_1 from zero are formed beside segment 0, segment 2 starts
+    from M_1 H_1 + C_1, and a second pass recomputes segments 1 and 2 with
+    their outputs.  Every output and the final state against the oracle (h0
+    given); hT in place of h0; no final state."""
+    B, H, T, Dk, Dv, regime = case
+    name = f"segmented B{B} H{H} T{T} dk{Dk} dv{Dv} bf16 {regime}, h0 given"
+    say(name)
+    dev, hst = make_case(B, T, H, Dk, Dv, "bf16", regime, "logit", 0.02, seed=17)
+    o, hT = run_gpu(dev)
+    ref_o, ref_h = oracle_full(hst)
+    check(name, "bf16", o, hT, ref_o, ref_h)
+    h = dev["h0"].clone()
+    o2, h2 = lin_attn_chunk_fwd(dev["q"], dev["k"], dev["v"], dev["gate"], dev["beta"], h,
+                                gate_mode="logit", hT=h)
+    torch.cuda.synchronize()
+    assert h2.data_ptr() == h.data_ptr() and torch.equal(o2, o) and torch.equal(h, hT)
+    o3, h3 = run_gpu(dev, hT=False)
+    assert h3 is None and torch.equal(o3, o)
+
+
 # ------------------------------------------------------- packed sequences
 VARLEN = [
     # sequence lengths, H, Dk, Dv, regime, gate mode, with h0
