@@ -83,6 +83,10 @@ extern "C" {
  * there between the two kernels of the pass.  When ceil(T / 32) >= 512 another
  * B * H * Dk * Dv * 4 bytes follow: long sequences may be processed in
  * stretches, and the fp32 state passes from one stretch to the next there.
+ * When ceil(T / 32) >= 1536 a further B * H * (4 Dk Dv + 2 Dk^2) * 4 + 1024
+ * bytes follow: with few heads a long sequence may run as three segments, the
+ * middle one's state map formed beside the first (float32 states and maps,
+ * and a zero block).
  */
 long long lin_attn_chunk_fwd_workspace_size(int B, int T, int H, int Dk, int Dv, int dtype);
 
