@@ -78,6 +78,10 @@ CASES = [
     # forms the outputs, two workgroups share a unit
     ("bf16", 128, 128, 4, 16, 70, "weak", "logit", 0.02),
     ("bf16", 64, 128, 2, 32, 40, "std", "log", None),
+    # pair path, one 16-column slice per head (the L2 prefetch lines and v rows
+    # of a narrow slice) and a ragged end
+    ("bf16", 128, 16, 1, 2, 100, "std", "logit", 0.02),
+    ("bf16", 64, 16, 2, 3, 77, "weak", "logit", None),
 ]
 
 
@@ -141,14 +145,15 @@ def test_channel_long_64k_every_head(regime):
     assert eo <= 1e-2 and eh <= 1e-2
 
 
-@pytest.mark.parametrize("B,H,T,Dv", [(2, 2, 16 * 1024 + 37, 64), (1, 3, 20000, 128)])
-def test_channel_stretched_long_sequences(B, H, T, Dv):
+@pytest.mark.parametrize("B,H,T,Dk,Dv", [(2, 2, 16 * 1024 + 37, 128, 64), (1, 3, 20000, 128, 128),
+                                         (1, 2, 17000, 64, 16)])
+def test_channel_stretched_long_sequences(B, H, T, Dk, Dv):
     # bf16 sequences of 512 pairs or more with few heads run in stretches: the
     # state crosses each cut through the workspace; every output and the final
     # state against the C copy of the per-channel recurrence, with h0 and a
     # ragged end
-    say(f"channel stretched B={B} H={H} T={T} Dv={Dv}")
-    inp, gate, host_args = make(B, T, H, 128, Dv, "bf16", "weak", "logit", 0.02, seed=1003)
+    say(f"channel stretched B={B} H={H} T={T} Dk={Dk} Dv={Dv}")
+    inp, gate, host_args = make(B, T, H, Dk, Dv, "bf16", "weak", "logit", 0.02, seed=1003)
     o, hT = lin_attn_chunk_fwd_channel(inp["q"], inp["k"], inp["v"], gate, inp["beta"], inp["h0"],
                                        gate_mode="logit", G=5.0)
     torch.cuda.synchronize()
