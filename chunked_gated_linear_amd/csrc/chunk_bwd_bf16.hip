@@ -154,6 +154,15 @@ __device__ inline bf16x4 tr_get(char* buf, int n, int grp) {
       (lds_s16x4*)(buf + 8 * (16 * (n & 3) + 4 * grp + (n >> 2))));
   return __builtin_bit_cast(bf16x4, r);
 }
+// Sum over each 16-lane row of the wave by an inclusive scan (DPP row_shr 1,
+// 2, 4, 8, zeros shifted in): lane 15 of the row ends with the row's total.
+__device__ inline float rowsum16(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x111, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x112, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x114, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x118, 0xf, 0xf, false));
+  return x;
+}
 __device__ inline void wave_fence() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -179,21 +188,6 @@ struct Rows {
     const s16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (lds_s16x4*)(rows + (4 * grp + (n >> 2)) * PITCH + 32 * t + 8 * (n & 3)));
     return __builtin_bit_cast(bf16x4, r);
-  }
-  // Cooperative copy of one tile's rows from global memory (zeros past the
-  // sequence end): `nthr` threads, thread `tid`.
-  template <typename Src>
-  __device__ static inline void stage(char* rows, const Src* src, const BSeq& sq, int c, int h,
-                                      int H, int tid, int nthr) {
-    constexpr int PER_ROW = 2 * DK / 16;
-    for (int x = tid; x < 16 * PER_ROW; x += nthr) {
-      const int r = x / PER_ROW, p = x % PER_ROW;
-      const int tok = 16 * c + r;
-      uint4 u = uint4{0u, 0u, 0u, 0u};
-      if (tok < sq.T)
-        u = *reinterpret_cast<const uint4*>(src + ((sq.tok0 + tok) * H + h) * DK + 8 * p);
-      *reinterpret_cast<uint4*>(rows + r * PITCH + 16 * p) = u;
-    }
   }
 };
 
@@ -629,7 +623,8 @@ struct G2Lds {
   static constexpr int EK = PM + kGS * 1088;           // E o K K^T float32, 16 x 16 per tile
   static constexpr int SC = EK + kGS * 1024;           // per tile G, beta, gamma, ec, dg/dg' [16] each
   static constexpr int XR = SC + kGS * 512;            // transposition tiles / reduction
-  static constexpr int XW = 9 * 512;                   // transposition bytes per wave
+  static constexpr int XT = 4 * NT / 2 > 9 ? 4 * NT / 2 : 9;   // transposition tiles per wave
+  static constexpr int XW = XT * 512;                  // transposition bytes per wave
   static constexpr int XBYTES = 8 * XW > 8 * NT * 1024 ? 8 * XW : 8 * NT * 1024;
   static constexpr int RS = XR + XBYTES;               // dP, dA partials: 8 waves x 2 x 1 KB
   static constexpr int RW = RS + 8 * 2 * 1024;         // row sums: 8 waves x 3 x 16 floats
@@ -660,65 +655,132 @@ __global__ __launch_bounds__(512) void bwd2_grad_kernel(BwdArgs a) {
   const __bf16* vp = static_cast<const __bf16*>(a.v);
   const __bf16* dop = static_cast<const __bf16*>(a.dout);
 
-  // ---- this wave's slice: the end-state gradient of the group, v and dO of
-  // its tiles (the start state is re-read per tile: an L2 hit after the first)
-  const uint4* const hp =
-      reinterpret_cast<const uint4*>(a.hw + gi * DK * a.Dv + (int64_t)w * DK * 16);
+  // ---- this wave's slice of the group's checkpoints (start state H and
+  // end-state gradient dH', packed words), requested before the staging
+  // loads; H is requested again at the end of each tile for the next one (an
+  // L2 hit)
+  const int64_t ckoff = gi * DK * a.Dv + (int64_t)w * DK * 16;
+  const uint4* const hp = reinterpret_cast<const uint4*>(a.hw + ckoff);
+  uint4 hw8[NT], dw8[NT];
+  // v and dO of the group's tiles in this wave's slice, read as rows (lane
+  // (n, grp): token n, columns 4 grp .. 4 grp + 3; zeros past the sequence end)
+  uint2 vrow[kGS], orow[kGS];
+  if (act) {
+    const uint4* const dp = reinterpret_cast<const uint4*>(a.dw + ckoff);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      hw8[t] = hp[t * 64 + lane];
+      dw8[t] = dp[t * 64 + lane];
+    }
+#pragma unroll
+    for (int m = 0; m < kGS; ++m) {
+      const int tok = 16 * (c0 + m) + n;
+      const int64_t e = ((sq.tok0 + tok) * a.H + h) * a.Dv + v0 + 4 * grp;
+      vrow[m] = tok < sq.T ? *reinterpret_cast<const uint2*>(vp + e) : uint2{0u, 0u};
+      orow[m] = tok < sq.T ? *reinterpret_cast<const uint2*>(dop + e) : uint2{0u, 0u};
+    }
+  }
+
+  // ---- stage the group's k and q rows (zeros past the sequence end) and
+  // tile operators; every global load is issued before the first LDS write
+  {
+    constexpr int PER_ROW = 2 * DK / 16;                 // 16-byte pieces of a row
+    constexpr int PER_T = 16 * PER_ROW;                  // pieces of a tile's rows
+    constexpr int NLD = (2 * kGS * PER_T + 511) / 512;   // k and q pieces per thread
+    constexpr int NRC = (kGS * 256 + 511) / 512;         // operator elements per thread
+    uint4 u[NLD];
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int x = tid + 512 * i;
+      const int qk = x / (kGS * PER_T), rem = x % (kGS * PER_T);
+      const int j = rem / PER_T, r = (rem % PER_T) / PER_ROW, p = rem % PER_ROW;
+      const int tok = 16 * (c0 + j) + r;
+      u[i] = uint4{0u, 0u, 0u, 0u};
+      if (qk < 2 && j < GSn && tok < sq.T) {
+        const __bf16* src = static_cast<const __bf16*>(qk ? a.q : a.k);
+        u[i] = *reinterpret_cast<const uint4*>(src + ((sq.tok0 + tok) * a.H + h) * DK + 8 * p);
+      }
+    }
+    float tv[NRC], pv[NRC], ev[NRC];
+#pragma unroll
+    for (int i = 0; i < NRC; ++i) {
+      const int x = tid + 512 * i;
+      if (x < GSn * 256) {
+        const float* rec = a.rec + (sq.rbase + c0 + (x >> 8)) * BRec::FLOATS;
+        tv[i] = rec[BRec::TINV + (x & 255)];
+        pv[i] = rec[BRec::P + (x & 255)];
+        ev[i] = rec[BRec::EKK + (x & 255)];
+      }
+    }
+    const bool small = tid < GSn * 16;
+    const int sj = tid >> 4, st = tid & 15, stok = 16 * (c0 + sj) + st;
+    float gv = 0.f, gC = 0.f, btv = 0.f, xg = 0.f;
+    if (small) {
+      const float* rec = a.rec + (sq.rbase + c0 + sj) * BRec::FLOATS;
+      gv = rec[BRec::G + st];
+      gC = rec[BRec::G + kT - 1];
+      btv = rec[BRec::BETA + st];
+      if (a.gate_logit && stok < sq.T) xg = a.gate[(sq.tok0 + stok) * a.H + h];
+    }
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int x = tid + 512 * i;
+      const int qk = x / (kGS * PER_T), rem = x % (kGS * PER_T);
+      const int j = rem / PER_T, r = (rem % PER_T) / PER_ROW, p = rem % PER_ROW;
+      if (qk < 2)
+        *reinterpret_cast<uint4*>(sm + (qk ? L::QR : L::KR) + j * L::ROWS + r * RW::PITCH + 16 * p) = u[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NRC; ++i) {
+      const int x = tid + 512 * i;
+      if (x < GSn * 256) {
+        const int j = x >> 8, e = x & 255, t = e >> 4, ii = e & 15;
+        put_op(sm + L::TF + j * 1024, t, ii, tv[i], false);
+        put_op(sm + L::TT + j * 1024, t, ii, tv[i], true);
+        put_op(sm + L::PT + j * 1024, t, ii, pv[i], true);
+        reinterpret_cast<float*>(sm + L::PM + j * 1088)[t * 17 + ii] = pv[i];
+        reinterpret_cast<float*>(sm + L::EK + j * 1024)[e] = ev[i];
+      }
+    }
+    if (small) {
+      float* sc = reinterpret_cast<float*>(sm + L::SC + sj * 512);
+      sc[st] = gv;
+      sc[16 + st] = btv;
+      sc[32 + st] = __expf(gv);
+      sc[48 + st] = __expf(gC - gv);
+      // dL/dx = dg/dx * dL/dg in logit mode (g = -G sigmoid(x)), 1 in log mode
+      float dgx = 1.f;
+      if (a.gate_logit && stok < sq.T) {
+        const float sg = sigmoid_f(xg);
+        dgx = -a.G * sg * (1.f - sg);
+      }
+      sc[64 + st] = dgx;
+    }
+  }
   // dH' of the tile in hand, as split fragments (carried backwards tile by
   // tile; each step rounds it to hi + lo, as the stored checkpoints are)
   bf16x8 Dh[NS], Dl[NS];
+  char* const xr = sm + L::XR + w * L::XW;         // this wave's transposition tiles
+  // v and dO in accumulator layout (lane (n, grp) holds rows 4 grp .. 4 grp + 3
+  // of column n): the row reads above, transposed through the wave's tiles
+  bf16x4 vg[kGS], og[kGS];
   if (act) {
-    const uint4* dp = reinterpret_cast<const uint4*>(a.dw + gi * DK * a.Dv + (int64_t)w * DK * 16);
-    words_state<NS>(dp + lane, 64, Dh, Dl);
-  }
-  // v or dO of tile c of this wave's slice, accumulator layout (zeros past the
-  // sequence end)
-  auto slice4 = [&](const __bf16* src, int c) {
-    bf16x4 x;
+    words_state<NS>(dw8, 1, Dh, Dl);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tok = 16 * c + 4 * grp + i;
-      x[i] = tok < sq.T ? src[((sq.tok0 + tok) * a.H + h) * a.Dv + v0 + n] : (__bf16)0.f;
+    for (int m = 0; m < kGS; ++m) {
+      tr_put(xr + m * 512, lane, __builtin_bit_cast(bf16x4, vrow[m]));
+      tr_put(xr + (kGS + m) * 512, lane, __builtin_bit_cast(bf16x4, orow[m]));
     }
-    return x;
-  };
-
-  // ---- stage the group's rows and tile operators
-  for (int j = 0; j < GSn; ++j) {
-    RW::stage(sm + L::KR + j * L::ROWS, static_cast<const __bf16*>(a.k), sq, c0 + j, h, a.H, tid, 512);
-    RW::stage(sm + L::QR + j * L::ROWS, static_cast<const __bf16*>(a.q), sq, c0 + j, h, a.H, tid, 512);
-  }
-  for (int x = tid; x < GSn * 256; x += 512) {
-    const int j = x >> 8, e = x & 255, t = e >> 4, i = e & 15;
-    const float* rec = a.rec + (sq.rbase + c0 + j) * BRec::FLOATS;
-    const float tv = rec[BRec::TINV + e], pv = rec[BRec::P + e];
-    put_op(sm + L::TF + j * 1024, t, i, tv, false);
-    put_op(sm + L::TT + j * 1024, t, i, tv, true);
-    put_op(sm + L::PT + j * 1024, t, i, pv, true);
-    reinterpret_cast<float*>(sm + L::PM + j * 1088)[t * 17 + i] = pv;
-    reinterpret_cast<float*>(sm + L::EK + j * 1024)[e] = rec[BRec::EKK + e];
-  }
-  if (tid < GSn * 16) {
-    const int j = tid >> 4, t = tid & 15;
-    const float* rec = a.rec + (sq.rbase + c0 + j) * BRec::FLOATS;
-    const float gv = rec[BRec::G + t], gC = rec[BRec::G + kT - 1];
-    float* sc = reinterpret_cast<float*>(sm + L::SC + j * 512);
-    sc[t] = gv;
-    sc[16 + t] = rec[BRec::BETA + t];
-    sc[32 + t] = __expf(gv);
-    sc[48 + t] = __expf(gC - gv);
-    // dL/dx = dg/dx * dL/dg in logit mode (g = -G sigmoid(x)), 1 in log mode
-    const int tok = 16 * (c0 + j) + t;
-    float dgx = 1.f;
-    if (a.gate_logit && tok < sq.T) {
-      const float sg = sigmoid_f(a.gate[(sq.tok0 + tok) * a.H + h]);
-      dgx = -a.G * sg * (1.f - sg);
+    wave_fence();
+#pragma unroll
+    for (int m = 0; m < kGS; ++m) {
+      vg[m] = tr_get(xr + m * 512, n, grp);
+      og[m] = tr_get(xr + (kGS + m) * 512, n, grp);
     }
-    sc[64 + t] = dgx;
   }
+  static_assert(2 * kGS <= L::XT, "v and dO tiles fit the wave's transposition area");
   __syncthreads();
 
-  char* const xr = sm + L::XR + w * L::XW;         // this wave's transposition tiles
   f32x4* const red = reinterpret_cast<f32x4*>(sm + L::XR);
   f32x4* const rs = reinterpret_cast<f32x4*>(sm + L::RS);
   float* const rw = reinterpret_cast<float*>(sm + L::RW);
@@ -733,6 +795,18 @@ __global__ __launch_bounds__(512) void bwd2_grad_kernel(BwdArgs a) {
   float* const sHdH = reinterpret_cast<float*>(sm + L::HD);
 
   for (int j = GSn - 1; j >= 0; --j) {
+    // The per-thread indices are re-derived every tile from an opaque copy of
+    // the lane, so that no hoisted per-thread address stays live across the
+    // loop (such addresses spill, and each reload waits for all memory
+    // operations in flight).
+    int lane_o = lane;
+    asm volatile("" : "+v"(lane_o));
+    const int lane = lane_o, n = lane_o & 15, grp = lane_o >> 4, tid = 64 * w + lane_o;
+    // v or dO of tile m of the group (m wave-uniform: selects, no indexing)
+    auto pick = [](const bf16x4* x, int m) {
+      static_assert(kGS == 4, "four tiles per group");
+      return m == 0 ? x[0] : m == 1 ? x[1] : m == 2 ? x[2] : x[3];
+    };
     const int c = c0 + j;
     const char* kr = sm + L::KR + j * L::ROWS;
     const char* qr = sm + L::QR + j * L::ROWS;
@@ -745,32 +819,29 @@ __global__ __launch_bounds__(512) void bwd2_grad_kernel(BwdArgs a) {
     bf16x8 Hh[NS], Hl[NS];       // H at the start of tile j, split
     if (act) {
       // H at the start of tile j: j forward steps from the group's checkpoint
-      // v of the next forward step and dO of this tile, requested ahead of use
-      bf16x4 vnext = slice4(vp, c0);
-      const bf16x4 dob = slice4(dop, c);
+      const bf16x4 dob = pick(og, j);
       f32x4 Hacc[NT];
-      {
-        uint4 hw8[NT];
+      words_state<NS>(hw8, 1, Hh, Hl);
+      if (j > 0) {
 #pragma unroll
-        for (int t = 0; t < NT; ++t) hw8[t] = hp[t * 64 + lane];
-        words_state<NS>(hw8, 1, Hh, Hl);
-        if (j > 0) {
-#pragma unroll
-          for (int t = 0; t < NT; ++t) Hacc[t] = words_f4(hw8[t]);
-        }
+        for (int t = 0; t < NT; ++t) Hacc[t] = words_f4(hw8[t]);
       }
       for (int m = 0; m < j; ++m) {
         const char* km = sm + L::KR + m * L::ROWS;
         const float* scm = reinterpret_cast<const float*>(sm + L::SC + m * 512);
-        f32x4 Rk = zero4();
+        // K H as two independent chains (hi and lo parts of H), every k
+        // fragment read first
+        bf16x8 ka[NS];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) ka[s] = RW::afrag(km, s, n, grp);
+        f32x4 Rl = zero4(), Rh = zero4();
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-          const bf16x8 ka = RW::afrag(km, s, n, grp);
-          Rk = mma32b(ka, Hl[s], Rk);
-          Rk = mma32b(ka, Hh[s], Rk);
+          Rl = mma32b(ka[s], Hl[s], Rl);
+          Rh = mma32b(ka[s], Hh[s], Rh);
         }
-        const f32x4 vf = to_f4(vnext);
-        vnext = slice4(vp, c0 + m + 1);
+        const f32x4 Rk = Rh + Rl;
+        const f32x4 vf = to_f4(pick(vg, m));
         const f32x4 gm = *reinterpret_cast<const f32x4*>(scm + 32 + 4 * grp);
         const f32x4 ec = *reinterpret_cast<const f32x4*>(scm + 48 + 4 * grp);
         const f32x4 bt = *reinterpret_cast<const f32x4*>(scm + 16 + 4 * grp);
@@ -816,7 +887,7 @@ __global__ __launch_bounds__(512) void bwd2_grad_kernel(BwdArgs a) {
       const f32x4 gm4 = *reinterpret_cast<const f32x4*>(sc + 32 + 4 * grp);
       const f32x4 bt4 = *reinterpret_cast<const f32x4*>(sc + 16 + 4 * grp);
       const f32x4 ec4 = *reinterpret_cast<const f32x4*>(sc + 48 + 4 * grp);
-      const f32x4 vf = to_f4(vnext), dd = to_f4(dob);
+      const f32x4 vf = to_f4(pick(vg, j)), dd = to_f4(dob);
       const bf16x8 tf = *reinterpret_cast<const bf16x8*>(sm + L::TF + j * 1024 + 16 * lane);
       const bf16x8 tt = *reinterpret_cast<const bf16x8*>(sm + L::TT + j * 1024 + 16 * lane);
       const bf16x8 pt = *reinterpret_cast<const bf16x8*>(sm + L::PT + j * 1024 + 16 * lane);
@@ -884,34 +955,49 @@ __global__ __launch_bounds__(512) void bwd2_grad_kernel(BwdArgs a) {
     }
 
     // ---- cross-wave reduction
+    // (row sums over the slice's 16 columns land in lane n = 15)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int m = 1; m < 16; m <<= 1) {
-        pB[i] += __shfl_xor(pB[i], m, 16);
-        pG[i] += __shfl_xor(pG[i], m, 16);
-        pW[i] += __shfl_xor(pW[i], m, 16);
-      }
+      pB[i] = rowsum16(pB[i]);
+      pG[i] = rowsum16(pG[i]);
+      pW[i] = rowsum16(pW[i]);
     }
-    for (int m = 1; m < 64; m <<= 1) hdh += __shfl_xor(hdh, m, 64);
+    hdh = rowsum16(hdh);
+    {
+      const int hb = __builtin_bit_cast(int, hdh);
+      hdh = __builtin_bit_cast(float, __builtin_amdgcn_readlane(hb, 15)) +
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(hb, 31)) +
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(hb, 47)) +
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(hb, 63));
+    }
     // dq partials over this wave's slice: dO H^T, through row fragments of H
-    // (one 32-row block of d_k per LDS round trip)
+    // (SQ 32-row blocks of d_k per LDS round trip)
+    constexpr int SQ = L::XT / 4, SK = L::XT / 8;
+    static_assert(NS % SQ == 0 && NS % SK == 0, "whole rounds of transposes");
     f32x4 dQp[NT];
 #pragma unroll
     for (int r = 0; r < NT; ++r) dQp[r] = zero4();
     if (act) {
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        tr_put(xr + 0 * 512, lane, first4(Hh[s]));
-        tr_put(xr + 1 * 512, lane, first4(Hl[s]));
-        tr_put(xr + 2 * 512, lane, second4(Hh[s]));
-        tr_put(xr + 3 * 512, lane, second4(Hl[s]));
+      for (int s0 = 0; s0 < NS; s0 += SQ) {
+#pragma unroll
+        for (int s = s0; s < s0 + SQ; ++s) {
+          char* const x4 = xr + 4 * (s - s0) * 512;
+          tr_put(x4 + 0 * 512, lane, first4(Hh[s]));
+          tr_put(x4 + 1 * 512, lane, first4(Hl[s]));
+          tr_put(x4 + 2 * 512, lane, second4(Hh[s]));
+          tr_put(x4 + 3 * 512, lane, second4(Hl[s]));
+        }
         wave_fence();
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const bf16x4 hrh = tr_get(xr + (2 * e) * 512, n, grp);
-          const bf16x4 hrl = tr_get(xr + (2 * e + 1) * 512, n, grp);
-          dQp[2 * s + e] = mma32b(dO8, cat8(hrh, hrl), dQp[2 * s + e]);
+        for (int s = s0; s < s0 + SQ; ++s) {
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            char* const x4 = xr + 4 * (s - s0) * 512;
+            const bf16x4 hrh = tr_get(x4 + (2 * e) * 512, n, grp);
+            const bf16x4 hrl = tr_get(x4 + (2 * e + 1) * 512, n, grp);
+            dQp[2 * s + e] = mma32b(dO8, cat8(hrh, hrl), dQp[2 * s + e]);
+          }
         }
         wave_fence();
       }
@@ -921,7 +1007,7 @@ __global__ __launch_bounds__(512) void bwd2_grad_kernel(BwdArgs a) {
     for (int r = 0; r < NT; ++r) red[(w * NT + r) * 64 + lane] = dQp[r];
     rs[(w * 2 + 0) * 64 + lane] = dPp;
     rs[(w * 2 + 1) * 64 + lane] = dAp;
-    if (n == 0) {
+    if (n == 15) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         rw[(w * 3 + 0) * 16 + 4 * grp + i] = pB[i];
@@ -954,27 +1040,35 @@ __global__ __launch_bounds__(512) void bwd2_grad_kernel(BwdArgs a) {
     for (int r = 0; r < NT; ++r) dKp[r] = zero4();
     if (act) {
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        tr_put(xr + 0 * 512, lane, first4(Hh[s]));
-        tr_put(xr + 1 * 512, lane, first4(Hl[s]));
-        tr_put(xr + 2 * 512, lane, first4(Dh[s]));
-        tr_put(xr + 3 * 512, lane, first4(Dl[s]));
-        tr_put(xr + 4 * 512, lane, second4(Hh[s]));
-        tr_put(xr + 5 * 512, lane, second4(Hl[s]));
-        tr_put(xr + 6 * 512, lane, second4(Dh[s]));
-        tr_put(xr + 7 * 512, lane, second4(Dl[s]));
+      for (int s0 = 0; s0 < NS; s0 += SK) {
+#pragma unroll
+        for (int s = s0; s < s0 + SK; ++s) {
+          char* const x8 = xr + 8 * (s - s0) * 512;
+          tr_put(x8 + 0 * 512, lane, first4(Hh[s]));
+          tr_put(x8 + 1 * 512, lane, first4(Hl[s]));
+          tr_put(x8 + 2 * 512, lane, first4(Dh[s]));
+          tr_put(x8 + 3 * 512, lane, first4(Dl[s]));
+          tr_put(x8 + 4 * 512, lane, second4(Hh[s]));
+          tr_put(x8 + 5 * 512, lane, second4(Hl[s]));
+          tr_put(x8 + 6 * 512, lane, second4(Dh[s]));
+          tr_put(x8 + 7 * 512, lane, second4(Dl[s]));
+        }
         wave_fence();
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int r = 2 * s + e;
-          const bf16x4 hrh = tr_get(xr + (4 * e + 0) * 512, n, grp);
-          const bf16x4 hrl = tr_get(xr + (4 * e + 1) * 512, n, grp);
-          const bf16x4 drh = tr_get(xr + (4 * e + 2) * 512, n, grp);
-          const bf16x4 drl = tr_get(xr + (4 * e + 3) * 512, n, grp);
-          dKp[r] = mma32b(aY8, cat8(hrh, hrh), dKp[r]);
-          dKp[r] = mma32b_lo(aY8, hrl, dKp[r]);
-          dKp[r] = mma32b(aU8, cat8(drh, drh), dKp[r]);
-          dKp[r] = mma32b_lo(aU8, drl, dKp[r]);
+        for (int s = s0; s < s0 + SK; ++s) {
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            char* const x8 = xr + 8 * (s - s0) * 512;
+            const int r = 2 * s + e;
+            const bf16x4 hrh = tr_get(x8 + (4 * e + 0) * 512, n, grp);
+            const bf16x4 hrl = tr_get(x8 + (4 * e + 1) * 512, n, grp);
+            const bf16x4 drh = tr_get(x8 + (4 * e + 2) * 512, n, grp);
+            const bf16x4 drl = tr_get(x8 + (4 * e + 3) * 512, n, grp);
+            dKp[r] = mma32b(aY8, cat8(hrh, hrh), dKp[r]);
+            dKp[r] = mma32b_lo(aY8, hrl, dKp[r]);
+            dKp[r] = mma32b(aU8, cat8(drh, drh), dKp[r]);
+            dKp[r] = mma32b_lo(aU8, drl, dKp[r]);
+          }
         }
         wave_fence();
       }
@@ -995,11 +1089,8 @@ __global__ __launch_bounds__(512) void bwd2_grad_kernel(BwdArgs a) {
       sPP[t][i] = dP * pm[17 * t + i];
       sAA[t][i] = dA * sc[16 + t] * ekk;
       float rak = dA * ekk;
-      rak += __shfl_xor(rak, 1, 16);
-      rak += __shfl_xor(rak, 2, 16);
-      rak += __shfl_xor(rak, 4, 16);
-      rak += __shfl_xor(rak, 8, 16);
-      if (jj == 0) {
+      rak = rowsum16(rak);               // the row's total in lane jj = 15
+      if (jj == 15) {
         float sb = 0.f, sg = 0.f, sw = 0.f;
         for (int v = 0; v < 8; ++v) {
           sb += rw[(v * 3 + 0) * 16 + t];
@@ -1052,12 +1143,9 @@ __global__ __launch_bounds__(512) void bwd2_grad_kernel(BwdArgs a) {
         const float y = sPP[t2][i] + sAA[t2][i];
         x += (t2 >= u && i < u) ? y : 0.f;
       }
-      x += __shfl_xor(x, 1, 16);
-      x += __shfl_xor(x, 2, 16);
-      x += __shfl_xor(x, 4, 16);
-      x += __shfl_xor(x, 8, 16);
+      x = rowsum16(x);                   // the row's total in lane i = 15
       const int tk = 16 * c + u;
-      if (i == 0 && tk < sq.T) {
+      if (i == 15 && tk < sq.T) {
         float hs = 0.f;
         for (int v = 0; v < 8; ++v) hs += sHdH[v];
         const float dg = gamC * hs + x;
@@ -1083,6 +1171,8 @@ __global__ __launch_bounds__(512) void bwd2_grad_kernel(BwdArgs a) {
         Dn[t] = mma32b(cat8(kt, kt), zb, Dn[t]);
       }
       split_state<NS>(Dn, Dh, Dl);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) hw8[t] = hp[t * 64 + lane];
     }
     __syncthreads();                       // the tile's shared values are consumed
   }
