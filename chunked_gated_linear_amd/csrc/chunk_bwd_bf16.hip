@@ -257,14 +257,13 @@ struct H2Raw {
 };
 
 template <int DK, int NP, int SPW>
-__global__ __launch_bounds__(64 * (NP + SPW)) void bwd2_hstates_kernel(BwdArgs a) {
+__device__ inline void hstates_body(const BwdArgs& a, int64_t blk, char* smem) {
   using R = H2Rec<DK, SPW>;
   using RW = Rows<DK>;
   constexpr int NS = DK / 32, NT = DK / 16;
-  __shared__ __attribute__((aligned(16))) char smem[2 * NP * R::BYTES];
   const int NW = a.Dv / (16 * SPW);
-  const int sl = (int)(blockIdx.x % NW);
-  const int64_t bh = blockIdx.x / NW;
+  const int sl = (int)(blk % NW);
+  const int64_t bh = blk / NW;
   const int h = (int)(bh % a.H), b = (int)(bh / a.H);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -433,14 +432,13 @@ struct D2Raw {
 };
 
 template <int DK, int NP, int SPW>
-__global__ __launch_bounds__(64 * (NP + SPW)) void bwd2_dh_kernel(BwdArgs a) {
+__device__ inline void dh_body(const BwdArgs& a, int64_t blk, char* smem) {
   using R = D2Rec<DK, SPW>;
   using RW = Rows<DK>;
   constexpr int NS = DK / 32, NT = DK / 16;
-  __shared__ __attribute__((aligned(16))) char smem[2 * NP * R::BYTES];
   const int NW = a.Dv / (16 * SPW);
-  const int sl = (int)(blockIdx.x % NW);
-  const int64_t bh = blockIdx.x / NW;
+  const int sl = (int)(blk % NW);
+  const int64_t bh = blk / NW;
   const int h = (int)(bh % a.H), b = (int)(bh / a.H);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -606,6 +604,17 @@ __global__ __launch_bounds__(64 * (NP + SPW)) void bwd2_dh_kernel(BwdArgs a) {
       __syncthreads();
     }
   }
+}
+
+// The forward states and the state gradients do not depend on each other: one
+// launch runs both, blocks [0, nblk) the first and [nblk, 2 nblk) the second,
+// so that the two serial chains share the compute units.
+template <int DK, int NP, int SPW>
+__global__ __launch_bounds__(64 * (NP + SPW)) void bwd2_states_kernel(BwdArgs a, int nblk) {
+  constexpr int HB = 2 * NP * H2Rec<DK, SPW>::BYTES, DB = 2 * NP * D2Rec<DK, SPW>::BYTES;
+  __shared__ __attribute__((aligned(16))) char smem[HB > DB ? HB : DB];
+  if ((int)blockIdx.x < nblk) hstates_body<DK, NP, SPW>(a, blockIdx.x, smem);
+  else dh_body<DK, NP, SPW>(a, blockIdx.x - nblk, smem);
 }
 
 // --------------------------------------------------- per-group gradients
@@ -1190,17 +1199,11 @@ hipError_t launch_bwd2_t(const BwdArgs& a, hipStream_t st) {
   // two column slices per workgroup when the slice count is even: the staged
   // tile then serves two chain waves
   if ((a.Dv / 16) % 2 == 0) {
-    hipLaunchKernelGGL((bwd2_hstates_kernel<DK, 2, 2>), dim3((unsigned)(slices / 2)), dim3(64 * 4),
-                       0, st, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd2_dh_kernel<DK, 2, 2>), dim3((unsigned)(slices / 2)), dim3(64 * 4), 0,
-                       st, a);
+    hipLaunchKernelGGL((bwd2_states_kernel<DK, 2, 2>), dim3((unsigned)slices), dim3(64 * 4), 0, st,
+                       a, (int)(slices / 2));
   } else {
-    hipLaunchKernelGGL((bwd2_hstates_kernel<DK, 2, 1>), dim3((unsigned)slices), dim3(64 * 3), 0,
-                       st, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd2_dh_kernel<DK, 2, 1>), dim3((unsigned)slices), dim3(64 * 3), 0, st,
-                       a);
+    hipLaunchKernelGGL((bwd2_states_kernel<DK, 2, 1>), dim3((unsigned)(2 * slices)), dim3(64 * 3), 0,
+                       st, a, (int)slices);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((bwd2_grad_kernel<DK>), dim3((unsigned)groups), dim3(512), 0, st, a);
