@@ -233,6 +233,86 @@ __device__ inline void put_op(char* frag, int t, int i, float x, bool transposed
   *reinterpret_cast<__bf16*>(p + 8) = (__bf16)(x - (float)hb);
 }
 
+// ------------------------------------------------------------- tile prep
+// The per-tile record (in-tile running sum G of the log-decay, beta, T =
+// (I + A)^{-1}, P = E o Q K^T, E o K K^T) with one wave per tile: K K^T and
+// Q K^T on the bf16 MFMA (the bf16 rows enter exactly; float32 sums), G summed
+// in token order, and T by forward substitution, one column per lane.
+template <int DK>
+__global__ __launch_bounds__(256) void bwd_prep_wave_kernel(BwdArgs a, int64_t ntiles) {
+  constexpr int NS = DK / 32;
+  __shared__ float sA[4][kT][kT + 1];
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, n = lane & 15, grp = lane >> 4;
+  const int64_t tile = (int64_t)blockIdx.x * 4 + w;
+  int b, h, c;
+  if (tile >= ntiles || !bwd_tile(a, tile, b, h, c)) return;   // the whole wave
+  const BSeq sq = bwd_seq(a, b, h);
+  // lane (n, grp): token n of the tile; elements 32 s + 8 grp .. + 7 of its
+  // k and q rows (one 32-deep fragment per s, the same for both operands)
+  const int tok = c * kT + n;
+  const bool in = tok < sq.T;
+  const int64_t row = (sq.tok0 + tok) * a.H + h;
+  bf16x8 kf[NS], qf[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    kf[s] = bf16x8{};
+    qf[s] = bf16x8{};
+    if (in) {
+      kf[s] = *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(a.k) + row * DK + 32 * s + 8 * grp);
+      qf[s] = *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(a.q) + row * DK + 32 * s + 8 * grp);
+    }
+  }
+  const float gx = in ? gate_at(a, row) : 0.f;
+  const float bx = in ? a.beta[row] : 0.f;
+  // K K^T and Q K^T: lane (n, grp) register r holds entry (4 grp + r, n)
+  f32x4 kk = zero4(), qk = zero4();
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    kk = mma32b(kf[s], kf[s], kk);
+    qk = mma32b(qf[s], kf[s], qk);
+  }
+  // G in token order (each lane: its column n and its rows 4 grp + r), beta of the rows
+  float Gc = 0.f, acc = 0.f;
+  f32x4 Gr = zero4(), Br = zero4();
+#pragma unroll
+  for (int t = 0; t < kT; ++t) {
+    acc += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gx), t));
+    const float bt = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bx), t));
+    Gc = t == n ? acc : Gc;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      Gr[r] = t == 4 * grp + r ? acc : Gr[r];
+      Br[r] = t == 4 * grp + r ? bt : Br[r];
+    }
+  }
+  float* const rec = a.rec + tile * BRec::FLOATS;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int t = 4 * grp + r;
+    const float e = n <= t ? __expf(Gr[r] - Gc) : 0.f;
+    const float ekk = n < t ? e * kk[r] : 0.f;
+    rec[BRec::EKK + kT * t + n] = ekk;
+    rec[BRec::P + kT * t + n] = e * qk[r];
+    sA[w][t][n] = Br[r] * ekk;
+  }
+  wave_fence();
+  // (I + A) T = I: lane j < 16 takes column j, row by row
+  if (lane < kT) {
+    float tc[kT];
+#pragma unroll
+    for (int r = 0; r < kT; ++r) {
+      float sacc = r == lane ? 1.f : 0.f;
+#pragma unroll
+      for (int m = 0; m < r; ++m) sacc -= sA[w][r][m] * tc[m];
+      tc[r] = sacc;
+      rec[BRec::TINV + kT * r + lane] = sacc;
+    }
+    rec[BRec::G + lane] = Gc;
+    rec[BRec::BETA + lane] = bx;
+  }
+}
+
 // ------------------------------------------- states at every group start
 // Record of one staged tile (bytes).
 template <int DK, int SPW>
@@ -440,7 +520,10 @@ __device__ inline void dh_body(const BwdArgs& a, int64_t blk, char* smem) {
   const int sl = (int)(blk % NW);
   const int64_t bh = blk / NW;
   const int h = (int)(bh % a.H), b = (int)(bh / a.H);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // roles rotated against the forward-state blocks (chain waves last), so that
+  // the chain waves of the two kinds of block sharing a compute unit tend to
+  // sit on different SIMDs
+  const int wave = (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) + SPW) % (NP + SPW);
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, grp = lane >> 4;
   const BSeq sq = bwd_seq(a, b, h);
@@ -1192,8 +1275,8 @@ hipError_t launch_bwd2_t(const BwdArgs& a, hipStream_t st) {
   const int64_t tiles = a.cu ? (int64_t)a.H * a.nslot : (int64_t)a.B * a.H * a.NT;
   const int64_t groups = a.cu ? (int64_t)a.H * a.nslotG : (int64_t)a.B * a.H * a.NG;
   const int64_t slices = (int64_t)a.B * a.H * (a.Dv / 16);
-  hipLaunchKernelGGL((bwd_prep_kernel<__bf16, DK>), dim3((unsigned)tiles), dim3(kBwdThreads), 0,
-                     st, a);
+  hipLaunchKernelGGL((bwd_prep_wave_kernel<DK>), dim3((unsigned)((tiles + 3) / 4)), dim3(256), 0, st,
+                     a, tiles);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // two column slices per workgroup when the slice count is even: the staged
