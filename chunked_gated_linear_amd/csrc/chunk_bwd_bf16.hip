@@ -1281,7 +1281,10 @@ hipError_t launch_bwd2_t(const BwdArgs& a, hipStream_t st) {
   if (e != hipSuccess) return e;
   // two column slices per workgroup when the slice count is even: the staged
   // tile then serves two chain waves
-  if ((a.Dv / 16) % 2 == 0) {
+  if ((a.Dv / 16) % 4 == 0) {
+    hipLaunchKernelGGL((bwd2_states_kernel<DK, 2, 4>), dim3((unsigned)(slices / 2)), dim3(64 * 6), 0, st,
+                       a, (int)(slices / 4));
+  } else if ((a.Dv / 16) % 2 == 0) {
     hipLaunchKernelGGL((bwd2_states_kernel<DK, 2, 2>), dim3((unsigned)slices), dim3(64 * 4), 0, st,
                        a, (int)(slices / 2));
   } else {
