@@ -49,9 +49,10 @@ TRAFFIC_KIB = {
                 # the 16 stretch launches (state + next stretch's preparation)
                 "fetch": 1224072, "write": 1277957},
     "backward": {"sources": ("chunk_bwd_bf16.hip", "la_bwd.h", "la_device.h"),
-                 "sha256_16": "b105806cf36da517",
-                 # one call at B=4 H=16 T=8192: prep, states, state gradients, gradients
-                 "fetch": 3296736, "write": 2372134},
+                 "sha256_16": "1d9d05a1154f653d",
+                 # one call at B=4 H=16 T=8192: tile records, states + state
+                 # gradients (one launch), gradients
+                 "fetch": 2044767, "write": 1969415},
     "decode": {"sources": ("decode.hip", "la_device.h"),
                "sha256_16": "f8c6337c80342a66",
                # one step at B=256 H=32 d=128 (median of six dispatches)
@@ -462,8 +463,8 @@ def main():
                          "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                          "frac": bbytes / (bms * 1e-3) / PEAK_HBM, "alg_bytes_per_launch": bbytes,
                          "traffic": measured_traffic("backward"),
-                         "kernel": ("bwd_prep_kernel + bwd2_hstates_kernel + bwd2_dh_kernel + "
-                                    "bwd2_grad_kernel (one lin_attn_chunk_bwd call, bf16 inputs)")},
+                         "kernel": ("bwd_prep_wave_kernel + bwd2_states_kernel + bwd2_grad_kernel "
+                                    "(one lin_attn_chunk_bwd call, bf16 inputs)")},
         }
         del bin_, up, wsb
 
