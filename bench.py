@@ -49,7 +49,7 @@ TRAFFIC_KIB = {
                 # the 16 stretch launches (state + next stretch's preparation)
                 "fetch": 1224072, "write": 1277957},
     "backward": {"sources": ("chunk_bwd_bf16.hip", "la_bwd.h", "la_device.h"),
-                 "sha256_16": "1d9d05a1154f653d",
+                 "sha256_16": "b78fe8188a76ca50",
                  # one call at B=4 H=16 T=8192: tile records, states + state
                  # gradients (one launch), gradients
                  "fetch": 2044767, "write": 1969415},

@@ -30,13 +30,16 @@
 //    from the group's stored end.  A quarter of the state traffic of storing
 //    both at every tile, for 1.5 extra forward steps per tile.
 //
-// Three kernels after the shared per-tile preparation (la_bwd.h):
-//   bwd2_hstates_kernel  per (sequence, head, SPW slices of 16 columns of
-//                        d_v), serial over tiles: H at every group start;
-//   bwd2_dh_kernel       same split, serial backwards: D at every group end,
-//                        and dh0;
-//   bwd2_grad_kernel     per group of kGS tiles, all of d_v (one 16-column
-//                        slice per wave): dq, dk, dv, dbeta, dg.
+// Three launches:
+//   bwd_prep_wave_kernel  the per-tile record of la_bwd.h, one wave per tile;
+//   bwd2_states_kernel    two kinds of block in one launch, per (sequence,
+//                         head, SPW slices of 16 columns of d_v): the forward
+//                         chain, serial over tiles (H at every group start),
+//                         and the gradient chain, serial backwards (D at every
+//                         group end, and dh0); the two do not depend on each
+//                         other;
+//   bwd2_grad_kernel      per group of kGS tiles, all of d_v (one 16-column
+//                         slice per wave): dq, dk, dv, dbeta, dg.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
