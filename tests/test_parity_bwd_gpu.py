@@ -72,6 +72,9 @@ CASES = [
     ("bf16", 128, 128, 1, 1, 1, "std", "logit", 0.02, True),
     ("bf16", 128, 128, 1, 2, 16, "std", "logit", 0.02, True),
     ("bf16", 128, 256, 1, 1, 40, "weak", "logit", 0.02, True),
+    # d_v / 16 even but not a multiple of 4: two slices per state block
+    ("bf16", 128, 96, 1, 2, 16 * 11 + 3, "weak", "logit", 0.02, True),
+    ("bf16", 64, 32, 2, 1, 77, "std", "log", None, True),
 ]
 
 
