@@ -36,13 +36,13 @@ CSRC = os.path.join(ROOT, "chunked_gated_linear_amd", "csrc")
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC_KIB = {
     "chunk": {"sources": ("chunk_pair.hip", "la_device.h"),
-              "sha256_16": "7cf6e8faa6274eb5",
+              "sha256_16": "0cafb7645a20fa6c",
               # one call: the intra-tile launch and the 16 state launches of 64K x 16 heads
-              "fetch": 776882, "write": 488452},
+              "fetch": 776930, "write": 488455},
     "varlen": {"sources": ("chunk_pair.hip", "la_device.h"),
-               "sha256_16": "7cf6e8faa6274eb5",
+               "sha256_16": "0cafb7645a20fa6c",
                # one call on the 64-request packed batch (64K tokens, 16 heads)
-               "fetch": 824416, "write": 545851},
+               "fetch": 824922, "write": 546356},
     "channel": {"sources": ("chunk_channel.hip", "chunk_channel_pair.hip", "la_device.h"),
                 "sha256_16": "0f24b3a4c5929fde",
                 # one call at 64K x 16 heads: the pair preparation of stretch 0 and
