@@ -48,6 +48,11 @@ TRAFFIC_KIB = {
                 # one call at 64K x 16 heads: the pair preparation of stretch 0 and
                 # the 16 stretch launches (state + next stretch's preparation)
                 "fetch": 1224072, "write": 1277957},
+    "channel_varlen": {"sources": ("chunk_channel.hip", "chunk_channel_pair.hip", "la_device.h"),
+                       "sha256_16": "0f24b3a4c5929fde",
+                       # one call on the 64-request packed batch with a per-channel
+                       # gate: the 16-token preparation and state launches
+                       "fetch": 1391772, "write": 1591826},
     "backward": {"sources": ("chunk_bwd_bf16.hip", "la_bwd.h", "la_device.h"),
                  "sha256_16": "b78fe8188a76ca50",
                  # one call at B=4 H=16 T=8192: tile records, states + state
@@ -422,6 +427,7 @@ def main():
                          "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                          "frac": cvbytes / (cvms * 1e-3) / PEAK_HBM,
                          "alg_bytes_per_launch": cvbytes,
+                         "traffic": measured_traffic("channel_varlen"),
                          "kernel": "chunk_channel_prep_kernel + chunk_fwd_channel_kernel (packed)"},
         }
         del vin, xv, ov, hv, wsv
