@@ -58,6 +58,10 @@ TRAFFIC_KIB = {
                  # one call at B=4 H=16 T=8192: tile records, states + state
                  # gradients (one launch), gradients
                  "fetch": 2044767, "write": 1969415},
+    "decode_channel": {"sources": ("chunk_channel.hip", "la_device.h"),
+                       "sha256_16": "7fa2297eef5c7589",
+                       # one step at B=256 H=32 d=128 with a per-channel gate (median of six)
+                       "fetch": 267548, "write": 527096},
     "decode": {"sources": ("decode.hip", "la_device.h"),
                "sha256_16": "f8c6337c80342a66",
                # one step at B=256 H=32 d=128 (median of six dispatches)
@@ -548,7 +552,9 @@ def main():
             "roofline": {"bound": "hbm", "achieved": cbytes / (cms * 1e-3) / 1e9,
                          "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                          "frac": cbytes / (cms * 1e-3) / PEAK_HBM,
-                         "alg_bytes_per_launch": cbytes, "kernel": "decode_channel_kernel"},
+                         "alg_bytes_per_launch": cbytes,
+                         "traffic": measured_traffic("decode_channel"),
+                         "kernel": "decode_channel_kernel"},
         }
         del d, S, xg
 
