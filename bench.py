@@ -43,6 +43,16 @@ TRAFFIC_KIB = {
                "sha256_16": "0cafb7645a20fa6c",
                # one call on the 64-request packed batch (64K tokens, 16 heads)
                "fetch": 824922, "write": 546356},
+    # the other rungs of the context ladder, one call each
+    "ladder_train_8k": {"sources": ("chunk_pair.hip", "la_device.h"),
+                        "sha256_16": "0cafb7645a20fa6c",
+                        "fetch": 398611, "write": 254224},
+    "ladder_long_256k": {"sources": ("chunk_pair.hip", "la_device.h"),
+                         "sha256_16": "0cafb7645a20fa6c",
+                         "fetch": 3150047, "write": 1905380},
+    "ladder_million_1m": {"sources": ("chunk_pair.hip", "la_device.h"),
+                          "sha256_16": "0cafb7645a20fa6c",
+                          "fetch": 7724248, "write": 3823233},
     "channel": {"sources": ("chunk_channel.hip", "chunk_channel_pair.hip", "la_device.h"),
                 "sha256_16": "0f24b3a4c5929fde",
                 # one call at 64K x 16 heads: the pair preparation of stretch 0 and
@@ -268,7 +278,8 @@ def main():
                 "steps": nsteps, "ms_per_call": lms, "tokens_per_s": lB * lT / lt,
                 "tflops": lfl / lt / 1e12, "mfma_pct_of_bf16_peak": 100.0 * lfl / lt / PEAK_BF16,
                 "roofline": {"bound": "hbm", "achieved": lby / lt / 1e9, "peak": PEAK_HBM / 1e9,
-                             "unit": "GB/s", "frac": lby / lt / PEAK_HBM, "traffic": None,
+                             "unit": "GB/s", "frac": lby / lt / PEAK_HBM,
+                             "traffic": measured_traffic("ladder_" + name),
                              "alg_bytes_per_launch": lby, "alg_flops_per_launch": lfl,
                              "kernel": "chunk_prep_kernel + chunk_state_kernel (one call)",
                              "attainable_frac": max(lby / PEAK_HBM, lfl / PEAK_BF16) / lt},
