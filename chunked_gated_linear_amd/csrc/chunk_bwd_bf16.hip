@@ -1,6 +1,6 @@
 // chunk_bwd_bf16.hip -- the reverse pass for bf16 q, k, v and dout on the bf16
-// matrix cores, with the forward states and the state gradients kept only at
-// every kGS-th tile.
+// matrix cores, with the forward states kept only at every kHS-th tile and the
+// state gradients at every kGS-th.
 //
 // Same algebra as chunk_bwd.hip (the adjoint of the tiled forward form; the
 // pages -- "Deep Dive: The Next Generation of Ultra-Long Context Sparse MoE
@@ -19,22 +19,23 @@
 //    Y_hi] then [X_hi | X_lo] . [Y_lo ; 0] with two.
 //    Accumulation is float32 throughout and the state and state gradient are
 //    carried in float32.
-//  * Checkpoints.  The state chain stores H only at the start of every group
-//    of kGS tiles and the gradient chain stores D = dL/dH' only at the end of
-//    every group, each as packed (hi, lo) bf16 words (4 bytes per element,
-//    the float32 size).  The gradient kernel takes one group per workgroup and
-//    walks its tiles backwards: it rebuilds H at the start of tile j by
-//    stepping the forward recurrence j times from the group's checkpoint, and
-//    carries D backwards tile by tile,
+//  * Checkpoints.  The state chain stores H only at the start of every kHS-th
+//    tile and the gradient chain stores D = dL/dH' only at the end of every
+//    group of kGS tiles, each as packed (hi, lo) bf16 words (4 bytes per
+//    element, the float32 size).  The gradient kernel takes one group per
+//    workgroup and walks its tiles backwards: it rebuilds H at the start of
+//    tile j by stepping the forward recurrence j % kHS times from the nearest
+//    stored state, and carries D backwards tile by tile,
 //        D_{j-1} = gamma_C D_j + Q^T diag(gamma) dO - K^T diag(beta gamma) dY,
-//    from the group's stored end.  A quarter of the state traffic of storing
-//    both at every tile, for 1.5 extra forward steps per tile.
+//    from the group's stored end.  With kHS = 2 and kGS = 4: 3/8 of the state
+//    traffic of storing both at every tile, for 0.5 extra forward steps per
+//    tile.
 //
 // Three launches:
 //   bwd_prep_wave_kernel  the per-tile record of la_bwd.h, one wave per tile;
 //   bwd2_states_kernel    two kinds of block in one launch, per (sequence,
 //                         head, SPW slices of 16 columns of d_v): the forward
-//                         chain, serial over tiles (H at every group start),
+//                         chain, serial over tiles (H at every kHS-th tile),
 //                         and the gradient chain, serial backwards (D at every
 //                         group end, and dh0); the two do not depend on each
 //                         other;
@@ -52,6 +53,8 @@ namespace la {
 namespace {
 
 constexpr int kGS = 4;          // tiles per checkpoint group
+constexpr int kHS = 2;          // tiles per stored start state (kGS / kHS of them per group)
+constexpr int kHPG = kGS / kHS;
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
@@ -367,15 +370,16 @@ __device__ inline void hstates_body(const BwdArgs& a, int64_t blk, char* smem) {
     }
     bf16x8 Hh[NS], Hl[NS];
     split_state<NS>(Hacc, Hh, Hl);
-    unsigned* const hw = a.hw + grp_base(a, b, h) * DK * a.Dv + (int64_t)(v0 / 16) * DK * 16;
+    unsigned* const hw =
+        a.hw + grp_base(a, b, h) * kHPG * DK * a.Dv + (int64_t)(v0 / 16) * DK * 16;
     __syncthreads();  // epoch 0 staged
     for (int ep = 0; ep < NE; ++ep) {
       for (int j = 0; j < NP; ++j) {
         const int c = ep * NP + j;
         if (c >= NC) break;
         const char* rec = rec_of(c);
-        if (c % kGS == 0) {
-          uint4* dst = reinterpret_cast<uint4*>(hw + (int64_t)(c / kGS) * DK * a.Dv);
+        if (c % kHS == 0) {
+          uint4* dst = reinterpret_cast<uint4*>(hw + (int64_t)(c / kHS) * DK * a.Dv);
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
             const bf16x8 hh = Hh[t >> 1], hl = Hl[t >> 1];
@@ -750,21 +754,26 @@ __global__ __launch_bounds__(512) void bwd2_grad_kernel(BwdArgs a) {
   const __bf16* vp = static_cast<const __bf16*>(a.v);
   const __bf16* dop = static_cast<const __bf16*>(a.dout);
 
-  // ---- this wave's slice of the group's checkpoints (start state H and
-  // end-state gradient dH', packed words), requested before the staging
-  // loads; H is requested again at the end of each tile for the next one (an
-  // L2 hit)
+  // ---- this wave's slice of the group's checkpoints (the states at tiles 0
+  // and kHS and the end-state gradient dH', packed words), requested before
+  // the staging loads; the start state of the next tile is requested at the
+  // end of each tile (an L2 hit)
   const int64_t ckoff = gi * DK * a.Dv + (int64_t)w * DK * 16;
-  const uint4* const hp = reinterpret_cast<const uint4*>(a.hw + ckoff);
+  // start state stored at tile kHS * (j / kHS) of the group
+  auto hp = [&](int j) {
+    return reinterpret_cast<const uint4*>(a.hw + (gi * kHPG + j / kHS) * DK * a.Dv +
+                                          (int64_t)w * DK * 16);
+  };
   uint4 hw8[NT], dw8[NT];
   // v and dO of the group's tiles in this wave's slice, read as rows (lane
   // (n, grp): token n, columns 4 grp .. 4 grp + 3; zeros past the sequence end)
   uint2 vrow[kGS], orow[kGS];
   if (act) {
     const uint4* const dp = reinterpret_cast<const uint4*>(a.dw + ckoff);
+    const uint4* const h0p = hp(GSn - 1);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      hw8[t] = hp[t * 64 + lane];
+      hw8[t] = h0p[t * 64 + lane];
       dw8[t] = dp[t * 64 + lane];
     }
 #pragma unroll
@@ -913,15 +922,17 @@ __global__ __launch_bounds__(512) void bwd2_grad_kernel(BwdArgs a) {
     bf16x8 dO8, aY8, aU8;        // row fragments: [dO, dO], [aY hi | lo], [aU hi | lo]
     bf16x8 Hh[NS], Hl[NS];       // H at the start of tile j, split
     if (act) {
-      // H at the start of tile j: j forward steps from the group's checkpoint
+      // H at the start of tile j: j % kHS forward steps from the state stored
+      // at tile kHS * (j / kHS)
       const bf16x4 dob = pick(og, j);
+      const int jb = j - j % kHS;
       f32x4 Hacc[NT];
       words_state<NS>(hw8, 1, Hh, Hl);
-      if (j > 0) {
+      if (j > jb) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) Hacc[t] = words_f4(hw8[t]);
       }
-      for (int m = 0; m < j; ++m) {
+      for (int m = jb; m < j; ++m) {
         const char* km = sm + L::KR + m * L::ROWS;
         const float* scm = reinterpret_cast<const float*>(sm + L::SC + m * 512);
         // K H as two independent chains (hi and lo parts of H), every k
@@ -1266,8 +1277,9 @@ __global__ __launch_bounds__(512) void bwd2_grad_kernel(BwdArgs a) {
         Dn[t] = mma32b(cat8(kt, kt), zb, Dn[t]);
       }
       split_state<NS>(Dn, Dh, Dl);
+      const uint4* const hn = hp(j - 1);
 #pragma unroll
-      for (int t = 0; t < NT; ++t) hw8[t] = hp[t * 64 + lane];
+      for (int t = 0; t < NT; ++t) hw8[t] = hn[t * 64 + lane];
     }
     __syncthreads();                       // the tile's shared values are consumed
   }
@@ -1311,13 +1323,13 @@ long long chunk_bwd_bf16_workspace_bytes(int B, int T, int H, int Dk, int Dv) {
   const long long nt = (T + kT - 1) / kT;
   const long long tiles = (long long)B * H * nt;
   const long long groups = (long long)B * H * ((nt + kGS - 1) / kGS);
-  return tiles * (BRec::FLOATS * 4LL) + groups * 2LL * Dk * Dv * 4LL;
+  return tiles * (BRec::FLOATS * 4LL) + groups * (kHPG + 1LL) * Dk * Dv * 4LL;
 }
 
 long long chunk_bwd_bf16_varlen_workspace_bytes(int T, int nseq, int H, int Dk, int Dv) {
   const long long tiles = (long long)H * (T / kT + nseq + 1);
   const long long groups = (long long)H * (T / (kT * kGS) + nseq + 1);
-  return tiles * (BRec::FLOATS * 4LL) + groups * 2LL * Dk * Dv * 4LL;
+  return tiles * (BRec::FLOATS * 4LL) + groups * (kHPG + 1LL) * Dk * Dv * 4LL;
 }
 
 hipError_t launch_chunk_bwd_bf16(const void* q, const void* k, const void* v, const void* dout,
@@ -1338,7 +1350,7 @@ hipError_t launch_chunk_bwd_bf16(const void* q, const void* k, const void* v, co
   a.dq = dq; a.dk = dk; a.dv = dv; a.dgate = dgate; a.dbeta = dbeta; a.dh0 = dh0;
   a.rec = reinterpret_cast<float*>(w);
   a.hw = reinterpret_cast<unsigned*>(w + tiles * BRec::FLOATS * 4);
-  a.dw = a.hw + groups * (int64_t)Dk * Dv;
+  a.dw = a.hw + groups * (int64_t)kHPG * Dk * Dv;
   a.gate_logit = gate_logit; a.G = G;
   a.B = B; a.T = T; a.H = H; a.Dv = Dv; a.NT = NT;
   a.cu = cu; a.nslot = nslot;

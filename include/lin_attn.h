@@ -394,9 +394,9 @@ int lin_attn_decode_step_channel(const void* q, const void* k, const void* v,
 /*
  * lin_attn_chunk_bwd_workspace_size -- device workspace bytes lin_attn_chunk_bwd
  * needs.  Every 16-token tile and head takes a 3,200-byte record.  With
- * LA_BF16 and Dv <= 128, the state and the gradient of the state are kept
- * only at every fourth tile, as packed bf16 (hi, lo) words: B * H *
- * (ceil(T / 16) * 3200 + ceil(T / 64) * 8 * Dk * Dv) bytes.  Otherwise
+ * LA_BF16 and Dv <= 128, the state is kept at every second tile and the
+ * gradient of the state at every fourth, as packed bf16 (hi, lo) words: B * H *
+ * (ceil(T / 16) * 3200 + ceil(T / 64) * 12 * Dk * Dv) bytes.  Otherwise
  * (LA_FP32, or Dv > 128) both are kept at every tile in float32: B * H *
  * ceil(T / 16) * (3200 + 8 * Dk * Dv) bytes.  -1 on invalid sizes (message in
  * lin_attn_last_error).
@@ -448,8 +448,9 @@ int lin_attn_chunk_bwd(const void* q, const void* k, const void* v,
  * 16 tokens of each packed sequence plus one spare per sequence for its
  * ragged end), each holding what lin_attn_chunk_bwd keeps per tile (3200 +
  * 8 * Dk * Dv bytes; with LA_BF16 and Dv <= 128 only the 3200-byte record,
- * plus H * (T / 64 + nseq + 1) group slots of 8 * Dk * Dv bytes for the
- * states kept at every fourth tile); -1 (with lin_attn_last_error() set) for
+ * plus H * (T / 64 + nseq + 1) group slots of 12 * Dk * Dv bytes for the
+ * states kept at every second and the state gradients at every fourth
+ * tile); -1 (with lin_attn_last_error() set) for
  * invalid sizes.
  */
 long long lin_attn_chunk_bwd_varlen_workspace_size(int T, int nseq, int H, int Dk, int Dv,

@@ -330,11 +330,11 @@ def test_chunk_bwd_workspace_size_and_empty():
     # record and two fp32 states
     assert ws(2, 17, 3, 64, 32, N.LA_FP32) == 2 * 3 * 2 * (3200 + 8 * 64 * 32)
     assert ws(1, 64, 2, 128, 144, N.LA_BF16) == 2 * 4 * (3200 + 8 * 128 * 144)
-    # bf16 inputs: the records, plus the state and its gradient as packed
-    # words at every group of four tiles (a partial group counts whole)
-    assert ws(1, 64, 2, 128, 128, N.LA_BF16) == 2 * 4 * 3200 + 2 * 1 * 8 * 128 * 128
-    assert ws(1, 65, 2, 128, 128, N.LA_BF16) == 2 * 5 * 3200 + 2 * 2 * 8 * 128 * 128
-    assert ws(3, 300, 2, 64, 48, N.LA_BF16) == 6 * 19 * 3200 + 6 * 5 * 8 * 64 * 48
+    # bf16 inputs: the records, plus per group of four tiles (a partial group
+    # counts whole) two states and one state gradient as packed words
+    assert ws(1, 64, 2, 128, 128, N.LA_BF16) == 2 * 4 * 3200 + 2 * 1 * 12 * 128 * 128
+    assert ws(1, 65, 2, 128, 128, N.LA_BF16) == 2 * 5 * 3200 + 2 * 2 * 12 * 128 * 128
+    assert ws(3, 300, 2, 64, 48, N.LA_BF16) == 6 * 19 * 3200 + 6 * 5 * 12 * 64 * 48
     assert ws(1, 0, 2, 128, 128, N.LA_BF16) == 0
     assert ws(1, 64, 2, 96, 128, N.LA_BF16) == -1
     for kw in (dict(B=0), dict(H=0)):
@@ -494,12 +494,12 @@ def test_bwd_varlen_workspace_size_and_empty():
     ws = N.lib().lin_attn_chunk_bwd_varlen_workspace_size
     per_tile = 3200 + 8 * 128 * 128
     assert ws(64, 3, 2, 128, 128, N.LA_FP32) == 2 * (64 // 16 + 3 + 1) * per_tile
-    # bf16: records per tile slot, packed states per group slot
-    # (H * (T / 64 + nseq + 1) of them)
+    # bf16: records per tile slot; per group slot (H * (T / 64 + nseq + 1)
+    # of them) two packed states and one packed state gradient
     assert ws(64, 3, 2, 128, 128, N.LA_BF16) == \
-        2 * (64 // 16 + 3 + 1) * 3200 + 2 * (64 // 64 + 3 + 1) * 8 * 128 * 128
+        2 * (64 // 16 + 3 + 1) * 3200 + 2 * (64 // 64 + 3 + 1) * 12 * 128 * 128
     assert ws(1000, 5, 3, 64, 32, N.LA_BF16) == \
-        3 * (1000 // 16 + 5 + 1) * 3200 + 3 * (1000 // 64 + 5 + 1) * 8 * 64 * 32
+        3 * (1000 // 16 + 5 + 1) * 3200 + 3 * (1000 // 64 + 5 + 1) * 12 * 64 * 32
     assert ws(64, -1, 2, 128, 128, N.LA_BF16) == -1
     # no sequences: nothing to do, nothing touched
     assert bwd_varlen(nseq=0, q=None, cu=None, ws=None)[0] == N.LA_OK
