@@ -64,10 +64,10 @@ TRAFFIC_KIB = {
                        # gate: the 16-token preparation and state launches
                        "fetch": 1391772, "write": 1591826},
     "backward": {"sources": ("chunk_bwd_bf16.hip", "la_bwd.h", "la_device.h"),
-                 "sha256_16": "b78fe8188a76ca50",
+                 "sha256_16": "5592444dfb9febf8",
                  # one call at B=4 H=16 T=8192: tile records, states + state
                  # gradients (one launch), gradients
-                 "fetch": 2044767, "write": 1969415},
+                 "fetch": 2162806, "write": 2493376},
     "decode_channel": {"sources": ("chunk_channel.hip", "la_device.h"),
                        "sha256_16": "7fa2297eef5c7589",
                        # one step at B=256 H=32 d=128 with a per-channel gate (median of six)
