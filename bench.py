@@ -64,7 +64,7 @@ TRAFFIC_KIB = {
                        # gate: the 16-token preparation and state launches
                        "fetch": 1391772, "write": 1591826},
     "backward": {"sources": ("chunk_bwd_bf16.hip", "la_bwd.h", "la_device.h"),
-                 "sha256_16": "5592444dfb9febf8",
+                 "sha256_16": "a7f7482c3dcd7948",
                  # one call at B=4 H=16 T=8192: tile records, states + state
                  # gradients (one launch), gradients
                  "fetch": 2162806, "write": 2493376},

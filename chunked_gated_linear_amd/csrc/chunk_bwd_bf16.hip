@@ -319,7 +319,7 @@ __global__ __launch_bounds__(256) void bwd_prep_wave_kernel(BwdArgs a, int64_t n
   }
 }
 
-// ------------------------------------------- states at every group start
+// ------------------------------------ states at every kHS-th tile
 // Record of one staged tile (bytes).
 template <int DK, int SPW>
 struct H2Rec {

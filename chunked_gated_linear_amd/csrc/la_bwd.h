@@ -56,9 +56,10 @@ struct BwdArgs {
   int B, T, H, Dv, NT;
   const int* cu;   // packed sequences: nseq + 1 device offsets (B = nseq), or NULL
   int nslot;       // packed sequences: tile slots per head
-  // bf16 path: states at every group start (hw) and state gradients at every
-  // group end (dw), as packed bf16 hi | lo << 16 words per element; NG groups
-  // per sequence (batched) or nslotG group slots per head (packed)
+  // bf16 path: states at the start of every second tile (hw, two per group)
+  // and state gradients at every group end (dw), as packed bf16 hi | lo << 16
+  // words per element; NG groups per sequence (batched) or nslotG group slots
+  // per head (packed)
   unsigned* hw;
   unsigned* dw;
   int NG, nslotG;
