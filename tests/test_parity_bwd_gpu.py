@@ -75,6 +75,9 @@ CASES = [
     # d_v / 16 even but not a multiple of 4: two slices per state block
     ("bf16", 128, 96, 1, 2, 16 * 11 + 3, "weak", "logit", 0.02, True),
     ("bf16", 64, 32, 2, 1, 77, "std", "log", None, True),
+    # d_k 64 with four slices per state block
+    ("bf16", 64, 128, 1, 2, 16 * 7 + 9, "weak", "logit", 0.02, True),
+    ("bf16", 64, 64, 2, 1, 200, "std", "logit", None, False),
 ]
 
 
