@@ -182,6 +182,7 @@ VARLEN_BWD = [
     # dtype, Dk, Dv, H, sequence lengths, gate mode
     ("bf16", 128, 128, 2, [0, 1, 17, 40, 100, 33, 64], "logit"),
     ("fp32", 64, 32, 3, [5, 0, 48, 77], "log"),
+    ("bf16", 64, 96, 3, [130, 0, 7, 64, 201], "log"),
 ]
 
 
