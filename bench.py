@@ -64,10 +64,10 @@ TRAFFIC_KIB = {
                        # gate: the 16-token preparation and state launches
                        "fetch": 1391772, "write": 1591826},
     "backward": {"sources": ("chunk_bwd_bf16.hip", "la_bwd.h", "la_device.h", "../build.py"),
-                 "sha256_16": "1240620f162fe601",
+                 "sha256_16": "722ec9096b9345aa",
                  # one call at B=4 H=16 T=8192: tile records, states + state
                  # gradients (one launch), gradients
-                 "fetch": 2136076, "write": 2493296},
+                 "fetch": 2159700, "write": 2492982},
     "decode_channel": {"sources": ("chunk_channel.hip", "la_device.h"),
                        "sha256_16": "7fa2297eef5c7589",
                        # one step at B=256 H=32 d=128 with a per-channel gate (median of six)
@@ -138,6 +138,9 @@ def main():
     ap.add_argument("--varlen-steps", type=int, default=20)
     ap.add_argument("--raw-steps", type=int, default=10)
     ap.add_argument("--bwd-steps", type=int, default=5)
+    ap.add_argument("--bwd-1m-steps", type=int, default=0,
+                    help="timed reverse passes at B=1 H=8 T=1M, in one pass and in segments "
+                         "of 64K tokens (off by default: ~50 GB of device memory)")
     ap.add_argument("--channel-steps", type=int, default=5)
     ap.add_argument("--ladder-steps", type=int, default=5,
                     help="timed calls per rung of the context ladder (8K, 256K, 1M); 0 skips it")
@@ -488,6 +491,48 @@ def main():
                                     "(one lin_attn_chunk_bwd call, bf16 inputs)")},
         }
         del bin_, up, wsb
+
+    # ---- the reverse pass at 1M tokens x 8 heads: one pass (workspace for the
+    # whole sequence) and the segmented form (workspace for 64K tokens)
+    if args.bwd_1m_steps > 0:
+        from chunked_gated_linear_amd import lin_attn_chunk_bwd, lin_attn_chunk_bwd_workspace_size
+        mw = I.WORKLOADS["million_1m"]
+        mB, mH, mT, mK, mV = mw["B"], mw["H"], mw["T"], mw["Dk"], mw["Dv"]
+        min_ = I.make_inputs(mB, mT, mH, mK, mV, dtype=mw["dtype"], seed=1003, device=dev,
+                             h0_std=mw.get("h0_std"))
+        mup = I.make_upstream_grads(mB, mT, mH, mK, mV, dtype=mw["dtype"], seed=1003, device=dev)
+        per_tok = 2 * (2 * mK + 2 * mV) + 8 + 4 * (2 * mK + mV) + 8
+        mbytes = mB * mT * mH * per_tok + 2 * mB * mH * mK * mV * 4
+        rows = {}
+        for name, seg in (("one_pass", None), ("segments_64k", 65536)):
+            nws = lin_attn_chunk_bwd_workspace_size(mB, mT, mH, mK, mV, torch.bfloat16, seg)
+            mws = torch.empty(nws, dtype=torch.uint8, device=dev)
+
+            def mstep():
+                return lin_attn_chunk_bwd(min_["q"], min_["k"], min_["v"], min_["x"], min_["beta"],
+                                          mup["dout"], min_["h0"], mup["dhT"], gate_mode="logit",
+                                          G=5.0, workspace=mws, segment_tokens=seg)
+
+            mstep()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(args.bwd_1m_steps):
+                mstep()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            mms = e0.elapsed_time(e1) / args.bwd_1m_steps
+            rows[name] = {"ms_per_call": mms, "workspace_bytes": nws,
+                          "tokens_per_s": mB * mT / (mms * 1e-3),
+                          "roofline": {"bound": "hbm", "achieved": mbytes / (mms * 1e-3) / 1e9,
+                                       "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                                       "frac": mbytes / (mms * 1e-3) / PEAK_HBM,
+                                       "alg_bytes_per_launch": mbytes}}
+            del mws
+            torch.cuda.empty_cache()
+        result["backward_1m"] = {
+            "workload": (f"million_1m B={mB} H={mH} T={mT} d={mK} bf16 inputs, fp32 gradients, "
+                         "dout and dhT ~ N(0,1)"), **rows}
+        del min_, mup
 
     # ---- optional calibration copy (reads and writes exactly copy_mib MiB)
     if args.copy_mib > 0:

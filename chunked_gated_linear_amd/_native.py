@@ -45,6 +45,10 @@ SIGNATURES = {
                                 _P, _P, _P, _P, _P, _P,
                                 _I, _I, _I, _I, _I, _I, _P, _LL, _P]),
     "lin_attn_chunk_bwd_workspace_size": (_LL, [_I, _I, _I, _I, _I, _I]),
+    "lin_attn_chunk_bwd_segmented": (_I, [_P, _P, _P, _P, _I, _F, _P, _P, _P, _P,
+                                          _P, _P, _P, _P, _P, _P,
+                                          _I, _I, _I, _I, _I, _I, _I, _P, _LL, _P]),
+    "lin_attn_chunk_bwd_segmented_workspace_size": (_LL, [_I, _I, _I, _I, _I, _I, _I]),
     "lin_attn_chunk_bwd_varlen": (_I, [_P, _P, _P, _P, _I, _F, _P, _P, _P, _P,
                                        _P, _P, _P, _P, _P, _P, _P,
                                        _I, _I, _I, _I, _I, _I, _P, _LL, _P]),

@@ -250,9 +250,14 @@ def lin_attn_chunk_fwd_channel_varlen(q, k, v, gate, beta, cu_seqlens, h0=None, 
     return o, hT
 
 
-def lin_attn_chunk_bwd_workspace_size(B, T, H, Dk, Dv, dtype=torch.bfloat16):
-    """Workspace bytes lin_attn_chunk_bwd needs for these sizes."""
-    n = N.lib().lin_attn_chunk_bwd_workspace_size(B, T, H, Dk, Dv, _DTYPES[dtype])
+def lin_attn_chunk_bwd_workspace_size(B, T, H, Dk, Dv, dtype=torch.bfloat16, segment_tokens=None):
+    """Workspace bytes lin_attn_chunk_bwd needs for these sizes (of the
+    segmented form when segment_tokens is given)."""
+    if segment_tokens is None:
+        n = N.lib().lin_attn_chunk_bwd_workspace_size(B, T, H, Dk, Dv, _DTYPES[dtype])
+    else:
+        n = N.lib().lin_attn_chunk_bwd_segmented_workspace_size(B, T, H, Dk, Dv, _DTYPES[dtype],
+                                                               int(segment_tokens))
     if n < 0:
         raise N.LinAttnError(N.LA_EINVAL, N.lib().lin_attn_last_error().decode())
     return n
@@ -260,11 +265,14 @@ def lin_attn_chunk_bwd_workspace_size(B, T, H, Dk, Dv, dtype=torch.bfloat16):
 
 @_on_stream
 def lin_attn_chunk_bwd(q, k, v, gate, beta, dout, h0=None, dhT=None, *, gate_mode="log",
-                       G=5.0, output_dh0=True, workspace=None, stream=None):
+                       G=5.0, output_dh0=True, workspace=None, stream=None, segment_tokens=None):
     """Gradients of <o, dout> + <hT, dhT> for lin_attn_chunk_fwd's inputs.
 
     Returns float32 tensors (dq, dk, dv, dgate, dbeta, dh0): dgate is dL/dg in
-    "log" mode and dL/dx in "logit" mode; dh0 is None unless output_dh0."""
+    "log" mode and dL/dx in "logit" mode; dh0 is None unless output_dh0.
+    segment_tokens (a multiple of 64; bf16 inputs, d_v <= 128) selects the
+    segmented form (lin_attn_chunk_bwd_segmented): the same results with a
+    workspace bounded by the segment length."""
     _need(q, "q")
     if q.dtype not in _DTYPES:
         raise TypeError("q, k, v, dout must be bfloat16 or float32")
@@ -286,16 +294,19 @@ def lin_attn_chunk_bwd(q, k, v, gate, beta, dout, h0=None, dhT=None, *, gate_mod
     dgate = torch.empty((B, T, H), **f32)
     dbeta = torch.empty((B, T, H), **f32)
     dh0 = torch.empty((B, H, Dk, Dv), **f32) if output_dh0 else None
-    nws = lin_attn_chunk_bwd_workspace_size(B, T, H, Dk, Dv, q.dtype)
+    nws = lin_attn_chunk_bwd_workspace_size(B, T, H, Dk, Dv, q.dtype, segment_tokens)
     if workspace is None and nws > 0:
         workspace = torch.empty(nws, dtype=torch.uint8, device=q.device)
     if workspace is not None:
         _need(workspace, "workspace", torch.uint8)
-    N.check(N.lib().lin_attn_chunk_bwd(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _GATE[gate_mode], float(G), _ptr(beta),
-        _ptr(h0), _ptr(dout), _ptr(dhT), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dgate),
-        _ptr(dbeta), _ptr(dh0), B, T, H, Dk, Dv, _DTYPES[q.dtype], _ptr(workspace),
-        0 if workspace is None else workspace.numel(), _stream(q, stream)))
+    args = [_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _GATE[gate_mode], float(G), _ptr(beta),
+            _ptr(h0), _ptr(dout), _ptr(dhT), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dgate),
+            _ptr(dbeta), _ptr(dh0), B, T, H, Dk, Dv, _DTYPES[q.dtype]]
+    tail = [_ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(q, stream)]
+    if segment_tokens is None:
+        N.check(N.lib().lin_attn_chunk_bwd(*args, *tail))
+    else:
+        N.check(N.lib().lin_attn_chunk_bwd_segmented(*args, int(segment_tokens), *tail))
     return dq, dk, dv, dgate, dbeta, dh0
 
 

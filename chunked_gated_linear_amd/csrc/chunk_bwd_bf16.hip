@@ -43,6 +43,7 @@
 //                         slice per wave): dq, dk, dv, dbeta, dg.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 
 #include "la_bwd.h"
@@ -421,6 +422,14 @@ __device__ inline void hstates_body(const BwdArgs& a, int64_t blk, char* smem) {
         split_state<NS>(Hacc, Hh, Hl);
       }
       __syncthreads();  // this epoch consumed, the next one staged
+    }
+    if (a.hTo) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          a.hTo[(bh * DK + 16 * t + 4 * grp + i) * a.Dv + v0 + n] = Hacc[t][i];
+      }
     }
     return;
   }
@@ -1285,8 +1294,11 @@ __global__ __launch_bounds__(512) void bwd2_grad_kernel(BwdArgs a) {
   }
 }
 
+// The reverse pass over the tiles of `a`: tile records, both state chains,
+// gradients.  With forward_only, the records and the forward chain only (the
+// segmented form's first pass: it needs the state after the last tile, a.hTo).
 template <int DK>
-hipError_t launch_bwd2_t(const BwdArgs& a, hipStream_t st) {
+hipError_t launch_bwd2_t(const BwdArgs& a, hipStream_t st, bool forward_only = false) {
   const int64_t tiles = a.cu ? (int64_t)a.H * a.nslot : (int64_t)a.B * a.H * a.NT;
   const int64_t groups = a.cu ? (int64_t)a.H * a.nslotG : (int64_t)a.B * a.H * a.NG;
   const int64_t slices = (int64_t)a.B * a.H * (a.Dv / 16);
@@ -1294,19 +1306,19 @@ hipError_t launch_bwd2_t(const BwdArgs& a, hipStream_t st) {
                      a, tiles);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // two column slices per workgroup when the slice count is even: the staged
-  // tile then serves two chain waves
-  if ((a.Dv / 16) % 4 == 0) {
-    hipLaunchKernelGGL((bwd2_states_kernel<DK, 2, 4>), dim3((unsigned)(slices / 2)), dim3(64 * 6), 0, st,
-                       a, (int)(slices / 4));
-  } else if ((a.Dv / 16) % 2 == 0) {
-    hipLaunchKernelGGL((bwd2_states_kernel<DK, 2, 2>), dim3((unsigned)slices), dim3(64 * 4), 0, st,
-                       a, (int)(slices / 2));
-  } else {
-    hipLaunchKernelGGL((bwd2_states_kernel<DK, 2, 1>), dim3((unsigned)(2 * slices)), dim3(64 * 3), 0,
-                       st, a, (int)slices);
-  }
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // four (or two) column slices per workgroup when the slice count allows:
+  // the staged tile then serves that many chain waves; blocks [0, nblk) carry
+  // the forward chain, [nblk, 2 nblk) the gradient chain
+  const int spw = (a.Dv / 16) % 4 == 0 ? 4 : (a.Dv / 16) % 2 == 0 ? 2 : 1;
+  const int nblk = (int)(slices / spw);
+  const unsigned grid = (unsigned)(forward_only ? nblk : 2 * nblk);
+  if (spw == 4)
+    hipLaunchKernelGGL((bwd2_states_kernel<DK, 2, 4>), dim3(grid), dim3(64 * 6), 0, st, a, nblk);
+  else if (spw == 2)
+    hipLaunchKernelGGL((bwd2_states_kernel<DK, 2, 2>), dim3(grid), dim3(64 * 4), 0, st, a, nblk);
+  else
+    hipLaunchKernelGGL((bwd2_states_kernel<DK, 2, 1>), dim3(grid), dim3(64 * 3), 0, st, a, nblk);
+  if ((e = hipGetLastError()) != hipSuccess || forward_only) return e;
   hipLaunchKernelGGL((bwd2_grad_kernel<DK>), dim3((unsigned)groups), dim3(512), 0, st, a);
   return hipGetLastError();
 }
@@ -1332,11 +1344,14 @@ long long chunk_bwd_bf16_varlen_workspace_bytes(int T, int nseq, int H, int Dk, 
   return tiles * (BRec::FLOATS * 4LL) + groups * (kHPG + 1LL) * Dk * Dv * 4LL;
 }
 
-hipError_t launch_chunk_bwd_bf16(const void* q, const void* k, const void* v, const void* dout,
-                                 const float* gate, int gate_logit, float G, const float* beta,
-                                 const float* h0, const float* dhT, float* dq, float* dk,
-                                 float* dv, float* dgate, float* dbeta, float* dh0, const int* cu,
-                                 int B, int T, int H, int Dk, int Dv, void* ws, hipStream_t st) {
+// Arguments of one reverse pass (batched, or packed when cu is set), with the
+// workspace laid out as the records, then the start-state words, then the
+// state-gradient words.
+static BwdArgs bwd_args(const void* q, const void* k, const void* v, const void* dout,
+                        const float* gate, int gate_logit, float G, const float* beta,
+                        const float* h0, const float* dhT, float* dq, float* dk, float* dv,
+                        float* dgate, float* dbeta, float* dh0, const int* cu, int B, int T,
+                        int H, int Dk, int Dv, void* ws) {
   const int NT = (T + kT - 1) / kT;
   const int nslot = cu ? T / kT + B + 1 : 0;
   const int64_t tiles = cu ? (int64_t)H * nslot : (int64_t)B * H * NT;
@@ -1355,7 +1370,84 @@ hipError_t launch_chunk_bwd_bf16(const void* q, const void* k, const void* v, co
   a.B = B; a.T = T; a.H = H; a.Dv = Dv; a.NT = NT;
   a.cu = cu; a.nslot = nslot;
   a.NG = NG; a.nslotG = nslotG;
+  a.hTo = nullptr;
+  return a;
+}
+
+hipError_t launch_chunk_bwd_bf16(const void* q, const void* k, const void* v, const void* dout,
+                                 const float* gate, int gate_logit, float G, const float* beta,
+                                 const float* h0, const float* dhT, float* dq, float* dk,
+                                 float* dv, float* dgate, float* dbeta, float* dh0, const int* cu,
+                                 int B, int T, int H, int Dk, int Dv, void* ws, hipStream_t st) {
+  const BwdArgs a = bwd_args(q, k, v, dout, gate, gate_logit, G, beta, h0, dhT, dq, dk, dv, dgate,
+                             dbeta, dh0, cu, B, T, H, Dk, Dv, ws);
   return Dk == 128 ? launch_bwd2_t<128>(a, st) : launch_bwd2_t<64>(a, st);
+}
+
+// Segmented form (batched only): per sequence, segments of L tokens (a
+// multiple of kT * kGS, so that every tile, group and stored state falls where
+// it falls in one pass over the whole sequence).  Workspace: one segment's
+// reverse-pass workspace (B = 1, T = L), then float32 [H, Dk, Dv] states at
+// the start of segments 1 .. S-1, then two [H, Dk, Dv] state-gradient buffers.
+static long long seg_area_bytes(int L, int H, int Dk, int Dv) {
+  return (chunk_bwd_bf16_workspace_bytes(1, L, H, Dk, Dv) + 255) / 256 * 256;
+}
+
+long long chunk_bwd_bf16_segmented_workspace_bytes(int T, int H, int Dk, int Dv, int L) {
+  const long long S = (T + L - 1) / L;
+  const long long st = (long long)H * Dk * Dv * 4;
+  return seg_area_bytes(std::min(L, T), H, Dk, Dv) + (S > 1 ? S - 1 : 0) * st + 2 * st;
+}
+
+hipError_t launch_chunk_bwd_bf16_segmented(const void* q, const void* k, const void* v,
+                                           const void* dout, const float* gate, int gate_logit,
+                                           float G, const float* beta, const float* h0,
+                                           const float* dhT, float* dq, float* dk, float* dv,
+                                           float* dgate, float* dbeta, float* dh0, int B, int T,
+                                           int H, int Dk, int Dv, int L, void* ws,
+                                           hipStream_t st) {
+  const int S = (T + L - 1) / L;
+  const int64_t nst = (int64_t)H * Dk * Dv;
+  char* const w = static_cast<char*>(ws);
+  float* const hs = reinterpret_cast<float*>(w + seg_area_bytes(std::min(L, T), H, Dk, Dv));
+  float* const dc[2] = {hs + (S > 1 ? S - 1 : 0) * nst, hs + (S > 1 ? S : 1) * nst};
+  const __bf16* qb = static_cast<const __bf16*>(q);
+  const __bf16* kb = static_cast<const __bf16*>(k);
+  const __bf16* vb = static_cast<const __bf16*>(v);
+  const __bf16* ob = static_cast<const __bf16*>(dout);
+  auto run = [&](const BwdArgs& a, bool forward_only) {
+    return Dk == 128 ? launch_bwd2_t<128>(a, st, forward_only)
+                     : launch_bwd2_t<64>(a, st, forward_only);
+  };
+  for (int b = 0; b < B; ++b) {
+    // segment s of sequence b: tokens [t0, t0 + Ls), its start state and the
+    // gradient of its end state
+    auto seg = [&](int s, const float* hin, const float* din, float* dout0) {
+      const int64_t t0 = (int64_t)b * T + (int64_t)s * L;
+      const int Ls = std::min(L, T - s * L);
+      return bwd_args(qb + t0 * H * Dk, kb + t0 * H * Dk, vb + t0 * H * Dv, ob + t0 * H * Dv,
+                      gate + t0 * H, gate_logit, G, beta + t0 * H, hin, din,
+                      dq + t0 * H * Dk, dk + t0 * H * Dk, dv + t0 * H * Dv, dgate + t0 * H,
+                      dbeta + t0 * H, dout0, nullptr, 1, Ls, H, Dk, Dv, ws);
+    };
+    const float* h0b = h0 ? h0 + b * nst : nullptr;
+    auto start = [&](int s) { return s == 0 ? h0b : hs + (int64_t)(s - 1) * nst; };
+    // pass 1: the state at every segment start, carried forward
+    for (int s = 0; s + 1 < S; ++s) {
+      BwdArgs a = seg(s, start(s), nullptr, nullptr);
+      a.hTo = hs + (int64_t)s * nst;
+      const hipError_t e = run(a, true);
+      if (e != hipSuccess) return e;
+    }
+    // pass 2: the segments backwards, the state gradient carried backwards
+    for (int s = S - 1; s >= 0; --s) {
+      const float* din = s == S - 1 ? (dhT ? dhT + b * nst : nullptr) : dc[(s + 1) & 1];
+      float* dout0 = s == 0 ? (dh0 ? dh0 + b * nst : nullptr) : dc[s & 1];
+      const hipError_t e = run(seg(s, start(s), din, dout0), false);
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
 }
 
 }  // namespace la

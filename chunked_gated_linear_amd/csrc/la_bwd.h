@@ -63,6 +63,9 @@ struct BwdArgs {
   unsigned* hw;
   unsigned* dw;
   int NG, nslotG;
+  // bf16 path: the forward state after the last tile, float32 [B, H, Dk, Dv],
+  // or NULL (the segmented reverse pass carries it to the next segment)
+  float* hTo;
 };
 
 // One sequence of the call: T tokens from token tok0 of the token axis, NC

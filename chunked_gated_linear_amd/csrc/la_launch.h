@@ -63,8 +63,8 @@ hipError_t launch_chunk_bwd(const void* q, const void* k, const void* v, const v
 
 // Workspace bytes of the reverse pass: per tile and head a 3200-byte record
 // and, for float32 inputs (or d_v > 128), the fp32 state at the tile start and
-// the fp32 gradient of its end state; for bf16 inputs those two only at every
-// fourth tile, as packed bf16 hi / lo words.
+// the fp32 gradient of its end state; for bf16 inputs the state only at every
+// second tile and the gradient at every fourth, as packed bf16 hi / lo words.
 long long chunk_bwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int fp32);
 
 // The reverse pass over packed sequences: sequence s is tokens
@@ -83,9 +83,10 @@ long long chunk_bwd_varlen_workspace_bytes(int T, int nseq, int H, int Dk, int D
 
 // The reverse pass for bf16 inputs on the bf16 matrix cores (chunk_bwd_bf16.hip),
 // taken by launch_chunk_bwd / launch_chunk_bwd_varlen whenever
-// chunk_bwd_bf16_path says so: states and state gradients kept at every fourth
-// tile as packed bf16 hi / lo words, the tiles between rebuilt in the gradient
-// kernel.  cu == NULL: B sequences of T tokens; else B packed sequences.
+// chunk_bwd_bf16_path says so: states kept at every second tile and state
+// gradients at every fourth as packed bf16 hi / lo words, the tiles between
+// rebuilt in the gradient kernel.  cu == NULL: B sequences of T tokens; else
+// B packed sequences.
 bool chunk_bwd_bf16_path(int Dk, int Dv, int fp32);
 long long chunk_bwd_bf16_workspace_bytes(int B, int T, int H, int Dk, int Dv);
 long long chunk_bwd_bf16_varlen_workspace_bytes(int T, int nseq, int H, int Dk, int Dv);
@@ -94,6 +95,19 @@ hipError_t launch_chunk_bwd_bf16(const void* q, const void* k, const void* v, co
                                  const float* h0, const float* dhT, float* dq, float* dk,
                                  float* dv, float* dgate, float* dbeta, float* dh0, const int* cu,
                                  int B, int T, int H, int Dk, int Dv, void* ws, hipStream_t st);
+// The same in segments of L tokens (L a multiple of 64; batched sequences):
+// a forward pass keeps the states at segment starts, then each segment runs
+// the reverse pass from its start state with the state gradient carried from
+// the segment after it.  Workspace: one segment's, plus per head (S + 1)
+// float32 states.
+long long chunk_bwd_bf16_segmented_workspace_bytes(int T, int H, int Dk, int Dv, int L);
+hipError_t launch_chunk_bwd_bf16_segmented(const void* q, const void* k, const void* v,
+                                           const void* dout, const float* gate, int gate_logit,
+                                           float G, const float* beta, const float* h0,
+                                           const float* dhT, float* dq, float* dk, float* dv,
+                                           float* dgate, float* dbeta, float* dh0, int B, int T,
+                                           int H, int Dk, int Dv, int L, void* ws,
+                                           hipStream_t st);
 
 // Per-channel gate (gate [B, T, H, Dk]); q, k, v, o bf16 or fp32 as `fp32`
 // says: a parallel tile-preparation kernel into the workspace, then the

@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdarg>
+#include <algorithm>
 #include <cstdint>
 #include <cstdio>
 #include <string>
@@ -583,12 +584,12 @@ long long lin_attn_chunk_bwd_workspace_size(int B, int T, int H, int Dk, int Dv,
   return la::chunk_bwd_workspace_bytes(B, T, H, Dk, Dv, dtype == LA_FP32);
 }
 
-int lin_attn_chunk_bwd(const void* q, const void* k, const void* v, const float* gate,
-                       int gate_mode, float G, const float* beta, const float* h0,
+static int chunk_bwd_call(const void* q, const void* k, const void* v, const float* gate,
+                          int gate_mode, float G, const float* beta, const float* h0,
                        const void* dout, const float* dhT, float* dq, float* dk, float* dv,
                        float* dgate, float* dbeta, float* dh0, int B, int T, int H, int Dk,
                        int Dv, int dtype, void* workspace, long long workspace_bytes,
-                       void* stream) {
+                       void* stream, int seg) {
   if (int rc = check_chunk_sizes(B, T, H, Dk, Dv, dtype)) return rc;
   if (int rc = check_gate_scalars(gate_mode, G)) return rc;
   if ((int64_t)B * H * ((T + 15) / 16) > INT32_MAX)
@@ -597,7 +598,10 @@ int lin_attn_chunk_bwd(const void* q, const void* k, const void* v, const float*
   const int64_t es = dtype == LA_BF16 ? 2 : 4;
   const int64_t ntok = (int64_t)B * T * H;
   const int64_t nst = (int64_t)B * H * Dk * Dv;
-  const long long wsz = T > 0 ? la::chunk_bwd_workspace_bytes(B, T, H, Dk, Dv, dtype == LA_FP32) : 0;
+  const long long wsz =
+      T == 0 ? 0
+      : seg  ? la::chunk_bwd_bf16_segmented_workspace_bytes(T, H, Dk, Dv, seg)
+             : la::chunk_bwd_workspace_bytes(B, T, H, Dk, Dv, dtype == LA_FP32);
   if (T > 0) {
     // q, k are read and dq, dk, dv written in 16-byte vectors of a row;
     // everything else element-wise
@@ -639,10 +643,59 @@ int lin_attn_chunk_bwd(const void* q, const void* k, const void* v, const float*
     if (!dh0) return ok();
     return hip_status(la::launch_state_init(dhT, dh0, nst, st), "state init launch");
   }
-  hipError_t e = la::launch_chunk_bwd(q, k, v, dout, gate, gate_mode == LA_GATE_BOUNDED_LOGIT, G,
-                                      beta, h0, dhT, dq, dk, dv, dgate, dbeta, dh0, B, T, H, Dk,
-                                      Dv, dtype == LA_FP32, workspace, st);
+  const hipError_t e =
+      seg ? la::launch_chunk_bwd_bf16_segmented(q, k, v, dout, gate,
+                                                gate_mode == LA_GATE_BOUNDED_LOGIT, G, beta, h0,
+                                                dhT, dq, dk, dv, dgate, dbeta, dh0, B, T, H, Dk,
+                                                Dv, seg, workspace, st)
+          : la::launch_chunk_bwd(q, k, v, dout, gate, gate_mode == LA_GATE_BOUNDED_LOGIT, G,
+                                 beta, h0, dhT, dq, dk, dv, dgate, dbeta, dh0, B, T, H, Dk, Dv,
+                                 dtype == LA_FP32, workspace, st);
   return hip_status(e, "chunk_bwd launch");
+}
+
+int lin_attn_chunk_bwd(const void* q, const void* k, const void* v, const float* gate,
+                       int gate_mode, float G, const float* beta, const float* h0,
+                       const void* dout, const float* dhT, float* dq, float* dk, float* dv,
+                       float* dgate, float* dbeta, float* dh0, int B, int T, int H, int Dk,
+                       int Dv, int dtype, void* workspace, long long workspace_bytes,
+                       void* stream) {
+  return chunk_bwd_call(q, k, v, gate, gate_mode, G, beta, h0, dout, dhT, dq, dk, dv, dgate,
+                        dbeta, dh0, B, T, H, Dk, Dv, dtype, workspace, workspace_bytes, stream, 0);
+}
+
+// The segmented form is for the bf16 matrix-core path with segments of whole
+// groups of four tiles.
+static int check_segment(int T, int H, int Dk, int Dv, int dtype, int segment_tokens) {
+  if (!la::chunk_bwd_bf16_path(Dk, Dv, dtype == LA_FP32))
+    return fail(LA_EINVAL, "segmented reverse pass needs dtype LA_BF16, Dk 64 or 128 and Dv <= 128");
+  if (segment_tokens <= 0 || segment_tokens % 64 != 0)
+    return fail(LA_EINVAL, "segment_tokens must be a positive multiple of 64 (got %d)",
+                segment_tokens);
+  if ((int64_t)H * ((std::min(T, segment_tokens) + 15) / 16) > INT32_MAX)
+    return fail(LA_EINVAL, "segment too large (H*segment_tokens/16 exceeds 2^31)");
+  return LA_OK;
+}
+
+long long lin_attn_chunk_bwd_segmented_workspace_size(int B, int T, int H, int Dk, int Dv,
+                                                      int dtype, int segment_tokens) {
+  if (check_chunk_sizes(B, T, H, Dk, Dv, dtype)) return -1;
+  if (check_segment(T, H, Dk, Dv, dtype, segment_tokens)) return -1;
+  ok();
+  return T > 0 ? la::chunk_bwd_bf16_segmented_workspace_bytes(T, H, Dk, Dv, segment_tokens) : 0;
+}
+
+int lin_attn_chunk_bwd_segmented(const void* q, const void* k, const void* v, const float* gate,
+                                 int gate_mode, float G, const float* beta, const float* h0,
+                                 const void* dout, const float* dhT, float* dq, float* dk,
+                                 float* dv, float* dgate, float* dbeta, float* dh0, int B, int T,
+                                 int H, int Dk, int Dv, int dtype, int segment_tokens,
+                                 void* workspace, long long workspace_bytes, void* stream) {
+  if (int rc = check_chunk_sizes(B, T, H, Dk, Dv, dtype)) return rc;
+  if (int rc = check_segment(T, H, Dk, Dv, dtype, segment_tokens)) return rc;
+  return chunk_bwd_call(q, k, v, gate, gate_mode, G, beta, h0, dout, dhT, dq, dk, dv, dgate,
+                        dbeta, dh0, B, T, H, Dk, Dv, dtype, workspace, workspace_bytes, stream,
+                        segment_tokens);
 }
 
 long long lin_attn_chunk_bwd_varlen_workspace_size(int T, int nseq, int H, int Dk, int Dv,

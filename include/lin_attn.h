@@ -443,6 +443,49 @@ int lin_attn_chunk_bwd(const void* q, const void* k, const void* v,
                        void* workspace, long long workspace_bytes, void* stream);
 
 /*
+ * lin_attn_chunk_bwd_segmented_workspace_size -- device workspace bytes of
+ * lin_attn_chunk_bwd_segmented: what lin_attn_chunk_bwd needs for one
+ * sequence of min(T, segment_tokens) tokens (rounded up to 256 bytes), plus
+ * H * Dk * Dv * 4 bytes for each of the ceil(T / segment_tokens) + 1 carried
+ * states (the states at segment starts and two state-gradient buffers),
+ * whatever B.  -1 (message in lin_attn_last_error) on invalid sizes, for
+ * anything but LA_BF16 with Dk 64 or 128 and Dv <= 128, or when
+ * segment_tokens is not a positive multiple of 64.
+ */
+long long lin_attn_chunk_bwd_segmented_workspace_size(int B, int T, int H, int Dk, int Dv,
+                                                      int dtype, int segment_tokens);
+
+/*
+ * lin_attn_chunk_bwd_segmented -- lin_attn_chunk_bwd with a workspace bounded
+ * by the segment length instead of the sequence length (for long sequences:
+ * at B=1 H=8 T=1048576 d=128 the one-pass workspace is 27.4 GB; with
+ * segments of 65536 tokens it is 1.7 GB).  Each sequence is cut into segments
+ * of segment_tokens tokens (a multiple of 64, so that every tile, group of
+ * four tiles and stored state falls where it falls in one pass): a first pass
+ * carries the forward state through the segments and keeps it only at
+ * segment starts; a second pass takes the segments backwards, each one a
+ * reverse pass from its start state with the gradient of its end state
+ * carried from the segment after it.  The results are bitwise those of
+ * lin_attn_chunk_bwd; the forward states are computed twice.
+ *
+ *   arguments: as lin_attn_chunk_bwd (dtype LA_BF16, Dk 64 or 128,
+ *     Dv <= 128), plus segment_tokens
+ *   workspace >= lin_attn_chunk_bwd_segmented_workspace_size(...) bytes,
+ *     256-byte aligned, caller-owned, clobbered.
+ * Errors: as lin_attn_chunk_bwd; LA_EINVAL for another dtype or shape, or a
+ * segment length that is not a positive multiple of 64.
+ */
+int lin_attn_chunk_bwd_segmented(const void* q, const void* k, const void* v,
+                                 const float* gate, int gate_mode, float G,
+                                 const float* beta, const float* h0,
+                                 const void* dout, const float* dhT,
+                                 float* dq, float* dk, float* dv,
+                                 float* dgate, float* dbeta, float* dh0,
+                                 int B, int T, int H, int Dk, int Dv, int dtype,
+                                 int segment_tokens, void* workspace,
+                                 long long workspace_bytes, void* stream);
+
+/*
  * lin_attn_chunk_bwd_varlen_workspace_size -- bytes of device workspace that
  * lin_attn_chunk_bwd_varlen needs: H * (T / 16 + nseq + 1) tile slots (one per
  * 16 tokens of each packed sequence plus one spare per sequence for its

@@ -490,6 +490,24 @@ def test_bwd_varlen_rejects(kw, code, needle):
     assert needle in msg
 
 
+def test_bwd_segmented_workspace_size_and_validation():
+    L = N.lib()
+    ws = L.lin_attn_chunk_bwd_segmented_workspace_size
+    one = L.lin_attn_chunk_bwd_workspace_size
+    # one segment's workspace (rounded up to 256 bytes), then ceil(T / seg) + 1
+    # float32 states per head, whatever B
+    seg = one(1, 256, 2, 128, 128, N.LA_BF16)
+    assert ws(3, 1000, 2, 128, 128, N.LA_BF16, 256) == (seg + 255) // 256 * 256 + 5 * 2 * 128 * 128 * 4
+    short = one(1, 100, 2, 64, 32, N.LA_BF16)
+    assert ws(1, 100, 2, 64, 32, N.LA_BF16, 256) == (short + 255) // 256 * 256 + 2 * 2 * 64 * 32 * 4
+    assert ws(1, 0, 2, 128, 128, N.LA_BF16, 256) == 0
+    for bad in (0, -64, 100, 32):
+        assert ws(1, 1000, 2, 128, 128, N.LA_BF16, bad) == -1
+    assert ws(1, 1000, 2, 128, 128, N.LA_FP32, 256) == -1
+    assert ws(1, 1000, 2, 128, 144, N.LA_BF16, 256) == -1
+    assert ws(1, 1000, 2, 96, 128, N.LA_BF16, 256) == -1
+
+
 def test_bwd_varlen_workspace_size_and_empty():
     ws = N.lib().lin_attn_chunk_bwd_varlen_workspace_size
     per_tile = 3200 + 8 * 128 * 128

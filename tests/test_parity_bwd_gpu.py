@@ -376,3 +376,39 @@ def test_bwd_varlen_weak_8k():
     say("  " + " ".join(f"{n}={e:.2e}" for n, e in worst.items()))
     for name, e in worst.items():
         assert e <= TOL_BWD_BF16, f"{name}: error {e}"
+
+
+# ------------------------------------------- segmented form (bounded workspace)
+SEG_CASES = [
+    # Dk, Dv, B, H, T, regime, mode, h0_std, dhT, segment_tokens
+    (128, 128, 2, 2, 1000, "weak", "logit", 0.02, True, 256),
+    (64, 96, 1, 3, 777, "std", "log", None, True, 192),
+    (128, 48, 1, 2, 130, "weak", "logit", 0.02, True, 64),
+    (128, 64, 1, 2, 300, "weak", "logit", 0.02, False, 512),     # one segment
+]
+
+
+@pytest.mark.parametrize("case", SEG_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_bwd_segmented_matches_one_pass_bitwise(case):
+    """Segments of whole groups of four tiles put every tile, group and stored
+    state where one pass over the sequence puts them, and the carried states
+    are the float32 chain states themselves: the segmented reverse pass
+    reproduces lin_attn_chunk_bwd bit for bit; the first case is also held to
+    the oracle's adjoint."""
+    Dk, Dv, B, H, T, regime, mode, h0_std, with_dhT, L = case
+    say(f"bwd segmented {case}")
+    dev_args, host_args = make_case(B, T, H, Dk, Dv, "bf16", regime, mode, h0_std=h0_std, seed=T)
+    up = I.make_upstream_grads(B, T, H, Dk, Dv, dtype="bf16", seed=T, device="cuda", dhT=with_dhT)
+    one = run_bwd(dev_args, up)
+    seg = lin_attn_chunk_bwd(dev_args["q"], dev_args["k"], dev_args["v"], dev_args["gate"],
+                             dev_args["beta"], up["dout"], dev_args["h0"], up["dhT"],
+                             gate_mode=dev_args["gate_mode"], G=5.0, segment_tokens=L)
+    torch.cuda.synchronize()
+    for name, x, y in zip(NAMES, one, seg):
+        assert torch.equal(x, y), name
+    if case is SEG_CASES[0]:
+        ref = oracle_grads(host_args, dev_args, up)
+        errs = {name: relerr(host(x), r) for name, x, r in zip(NAMES, seg, ref)}
+        say("  " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+        for name, e in errs.items():
+            assert e <= TOL_BWD_BF16, f"{name}: error {e}"
