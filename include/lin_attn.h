@@ -416,7 +416,8 @@ long long lin_attn_chunk_bwd_workspace_size(int B, int T, int H, int Dk, int Dv,
  * cores.  LA_BF16 with Dv <= 128 runs them on the bf16 matrix cores, every
  * float32 operand split into bf16 hi + lo parts (relative error 2^-16 per
  * operand; the bf16 inputs enter exactly), and keeps the states only at
- * every fourth tile, rebuilding those between inside the gradient kernel.
+ * every second tile and the state gradients at every fourth, rebuilding
+ * those between inside the gradient kernel.
  *
  *   q, k, v, gate, beta, h0, gate_mode, G, sizes, dtype: as lin_attn_chunk_fwd
  *     (q and k 16-byte aligned; h0 may be NULL = zeros)
