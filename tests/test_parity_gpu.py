@@ -230,6 +230,7 @@ SEG_CASES = [
     (1, 2, 3 * 16384 + 37, 128, 128, "weak"),
     (1, 3, 3 * 16400, 64, 64, "weak"),
     (1, 2, 3 * 16384 + 37, 128, 128, "std"),
+    (2, 2, 3 * 16384 + 100, 128, 64, "weak"),     # two sequences, narrower d_v
 ]
 
 
