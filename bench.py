@@ -63,11 +63,12 @@ TRAFFIC_KIB = {
                        # one call on the 64-request packed batch with a per-channel
                        # gate: the 16-token preparation and state launches
                        "fetch": 1391772, "write": 1591826},
-    "backward": {"sources": ("chunk_bwd_bf16.hip", "la_bwd.h", "la_device.h", "../build.py"),
-                 "sha256_16": "722ec9096b9345aa",
+    "backward": {"sources": ("chunk_bwd_bf16.hip", "chunk_bwd_bf16_states.hip", "la_bwd_bf16.h", "la_bwd.h",
+                             "la_device.h", "../build.py"),
+                 "sha256_16": "b54f3bc62c83e947",
                  # one call at B=4 H=16 T=8192: tile records, states + state
                  # gradients (one launch), gradients
-                 "fetch": 2159700, "write": 2492982},
+                 "fetch": 2128513, "write": 2493310},
     "decode_channel": {"sources": ("chunk_channel.hip", "la_device.h"),
                        "sha256_16": "7fa2297eef5c7589",
                        # one step at B=256 H=32 d=128 with a per-channel gate (median of six)

@@ -20,7 +20,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "liblinattn.so")
-SOURCES = ["chunk_fwd.hip", "chunk_pair.hip", "chunk_bwd.hip", "chunk_bwd_bf16.hip", "chunk_channel.hip",
+SOURCES = ["chunk_fwd.hip", "chunk_pair.hip", "chunk_bwd.hip", "chunk_bwd_bf16.hip",
+           "chunk_bwd_bf16_states.hip", "chunk_channel.hip",
            "chunk_channel_pair.hip",
            "decode.hip",
            "noalloc.hip", "lin_attn_abi.cpp"]
@@ -44,11 +45,12 @@ def flags() -> list[str]:
             "-I", INCLUDE, "-I", CSRC]
 
 
-# Per-file additions.  The reverse-pass kernels are latency-bound at one
-# workgroup per compute unit (their LDS); the scheduler that favours
-# instruction-level parallelism over occupancy measured 2 % faster there
-# (2.24 -> 2.19 ms per call at B=4 H=16 T=8192) and no better on the forward
-# files.
+# Per-file additions.  The reverse-pass gradient kernel is latency-bound at
+# one workgroup per compute unit (its LDS); the scheduler that favours
+# instruction-level parallelism over occupancy measured 2-3 % faster there
+# and no better on the forward files.  It stops the compiler (a crash in
+# register allocation) on the serial-chain kernel, which therefore sits in a
+# file of its own, chunk_bwd_bf16_states.hip, with the default scheduler.
 SRC_FLAGS = {
     "chunk_bwd_bf16.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
 }

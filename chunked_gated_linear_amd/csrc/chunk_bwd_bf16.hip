@@ -33,212 +33,28 @@
 //
 // Three launches:
 //   bwd_prep_wave_kernel  the per-tile record of la_bwd.h, one wave per tile;
-//   bwd2_states_kernel    two kinds of block in one launch, per (sequence,
-//                         head, SPW slices of 16 columns of d_v): the forward
-//                         chain, serial over tiles (H at every kHS-th tile),
-//                         and the gradient chain, serial backwards (D at every
-//                         group end, and dh0); the two do not depend on each
-//                         other;
+//   bwd2_states_kernel    (chunk_bwd_bf16_states.hip) two kinds of block in
+//                         one launch, per (sequence, head, SPW slices of 16
+//                         columns of d_v): the forward chain, serial over
+//                         tiles (H at every kHS-th tile), and the gradient
+//                         chain, serial backwards over pairs of tiles (D at
+//                         every group end, and dh0); the two do not depend on
+//                         each other;
 //   bwd2_grad_kernel      per group of kGS tiles, all of d_v (one 16-column
 //                         slice per wave): dq, dk, dv, dbeta, dg.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <cstdint>
+#include <type_traits>
 
 #include "la_bwd.h"
+#include "la_bwd_bf16.h"
 #include "la_device.h"
 #include "la_launch.h"
 
 namespace la {
 namespace {
-
-constexpr int kGS = 4;          // tiles per checkpoint group
-constexpr int kHS = 2;          // tiles per stored start state (kGS / kHS of them per group)
-constexpr int kHPG = kGS / kHS;
-
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
-
-// ------------------------------------------------------------- helpers
-__device__ inline bf16x4 hi4(f32x4 x) {
-  return bf16x4{(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
-}
-__device__ inline bf16x4 lo4(f32x4 x, bf16x4 h) {
-  return bf16x4{(__bf16)(x[0] - (float)h[0]), (__bf16)(x[1] - (float)h[1]),
-                (__bf16)(x[2] - (float)h[2]), (__bf16)(x[3] - (float)h[3])};
-}
-__device__ inline bf16x8 cat8(bf16x4 a, bf16x4 b) {
-  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
-__device__ inline bf16x4 first4(bf16x8 a) { return bf16x4{a[0], a[1], a[2], a[3]}; }
-__device__ inline bf16x4 second4(bf16x8 a) { return bf16x4{a[4], a[5], a[6], a[7]}; }
-__device__ inline f32x4 mma32b(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-// [A_hi | A_lo] . [B_lo ; 0] = A_hi B_lo: the third term of a split-by-split
-// 16-deep product, as a 32-deep MFMA with a zero half.  Every product here is
-// a 16x16x32 MFMA: a 16x16x16 one reading, as its accumulator, the result of a
-// 16x16x32 MFMA issued just before came out wrong in accumulator registers 0
-// and 1 in this build (the instructions between them did not cover the
-// dependency).
-__device__ inline f32x4 mma32b_lo(bf16x8 a, bf16x4 blo, f32x4 c) {
-  return mma32b(a, cat8(blo, bf16x4{(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f}), c);
-}
-__device__ inline f32x4 to_f4(bf16x4 x) {
-  return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
-}
-
-// A float32 fragment as bf16 hi + lo parts.
-struct Sp4 {
-  bf16x4 h, l;
-};
-__device__ inline Sp4 split4(f32x4 x) {
-  Sp4 r;
-  r.h = hi4(x);
-  r.l = lo4(x, r.h);
-  return r;
-}
-
-// Packed checkpoint words: element = bf16 hi in bits 0..15, bf16 lo in 16..31.
-__device__ inline uint4 pack_words(bf16x4 h, bf16x4 l) {
-  const s16x4 hs = __builtin_bit_cast(s16x4, h), ls = __builtin_bit_cast(s16x4, l);
-  uint4 w;
-  w.x = (unsigned)(unsigned short)hs[0] | ((unsigned)(unsigned short)ls[0] << 16);
-  w.y = (unsigned)(unsigned short)hs[1] | ((unsigned)(unsigned short)ls[1] << 16);
-  w.z = (unsigned)(unsigned short)hs[2] | ((unsigned)(unsigned short)ls[2] << 16);
-  w.w = (unsigned)(unsigned short)hs[3] | ((unsigned)(unsigned short)ls[3] << 16);
-  return w;
-}
-__device__ inline float word_f(unsigned w) {
-  return __uint_as_float(w << 16) + __uint_as_float(w & 0xffff0000u);
-}
-__device__ inline f32x4 words_f4(uint4 w) {
-  return f32x4{word_f(w.x), word_f(w.y), word_f(w.z), word_f(w.w)};
-}
-
-// Packed words -> the bf16 hi and lo parts of four elements.
-__device__ inline void words_split(uint4 w, bf16x4& h, bf16x4& l) {
-  const unsigned h01 = (w.x & 0xffffu) | (w.y << 16), h23 = (w.z & 0xffffu) | (w.w << 16);
-  const unsigned l01 = (w.x >> 16) | (w.y & 0xffff0000u), l23 = (w.z >> 16) | (w.w & 0xffff0000u);
-  h = __builtin_bit_cast(bf16x4, uint2{h01, h23});
-  l = __builtin_bit_cast(bf16x4, uint2{l01, l23});
-}
-// The split fragments of a state stored as packed words (tile t at w[t]).
-template <int NS>
-__device__ inline void words_state(const uint4* w, int stride, bf16x8* sh, bf16x8* sl) {
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    bf16x4 ah, al, bh, bl;
-    words_split(w[(2 * s) * stride], ah, al);
-    words_split(w[(2 * s + 1) * stride], bh, bl);
-    sh[s] = cat8(ah, bh);
-    sl[s] = cat8(al, bl);
-  }
-}
-
-// The split fragments of a d_k x 16 state held as NT float32 accumulator
-// tiles: 32-deep B fragments of contraction block s (tiles 2s and 2s + 1).
-template <int NS>
-__device__ inline void split_state(const f32x4* acc, bf16x8* sh, bf16x8* sl) {
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    const Sp4 a = split4(acc[2 * s]), b = split4(acc[2 * s + 1]);
-    sh[s] = cat8(a.h, b.h);
-    sl[s] = cat8(a.l, b.l);
-  }
-}
-
-// 16 x 16 bf16 tile, accumulator layout (lane (n, grp) holds X[4 grp + i][n])
-// -> row layout (lane (n, grp) holds X[n][4 grp + j]) through 512 bytes of
-// this wave's LDS: a lane-order write, then a transposing read in which lane
-// (n, grp) points at the 8 bytes written by lane (4 grp + n / 4, n % 4).
-__device__ inline void tr_put(char* buf, int lane, bf16x4 x) {
-  *reinterpret_cast<bf16x4*>(buf + 8 * lane) = x;
-}
-__device__ inline bf16x4 tr_get(char* buf, int n, int grp) {
-  const s16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_s16x4*)(buf + 8 * (16 * (n & 3) + 4 * grp + (n >> 2))));
-  return __builtin_bit_cast(bf16x4, r);
-}
-// Sum over each 16-lane row of the wave by an inclusive scan (DPP row_shr 1,
-// 2, 4, 8, zeros shifted in): lane 15 of the row ends with the row's total.
-__device__ inline float rowsum16(float x) {
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x111, 0xf, 0xf, false));
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x112, 0xf, 0xf, false));
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x114, 0xf, 0xf, false));
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x118, 0xf, 0xf, false));
-  return x;
-}
-__device__ inline void wave_fence() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// Token rows of one tile of k or q in LDS, bf16, row pitch 2 DK + 16 bytes
-// (the pad spreads the rows of a fragment read over the banks).
-//   A fragment of block s (32-deep over d_k): lane (n, grp) holds
-//     K[n][32 s + kappa32(grp, j)]: two 8-byte reads of row n;
-//   transposed A fragment of 16-row block t (16-deep over tokens): lane
-//     (n, grp) holds K[4 grp + j][16 t + n]: one transposing read in which
-//     lane (n, grp) points at row 4 grp + n / 4, columns 16 t + 4 (n % 4).
-template <int DK>
-struct Rows {
-  static constexpr int PITCH = 2 * DK + 16;
-  static constexpr int BYTES = 16 * PITCH;
-  __device__ static inline bf16x8 afrag(const char* rows, int s, int n, int grp) {
-    const char* p = rows + n * PITCH + 2 * (32 * s + 4 * grp);
-    return cat8(*reinterpret_cast<const bf16x4*>(p), *reinterpret_cast<const bf16x4*>(p + 32));
-  }
-  __device__ static inline bf16x4 tfrag(const char* rows, int t, int n, int grp) {
-    const s16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_s16x4*)(rows + (4 * grp + (n >> 2)) * PITCH + 32 * t + 8 * (n & 3)));
-    return __builtin_bit_cast(bf16x4, r);
-  }
-};
-
-// Index of group 0 of sequence b, head h in the checkpoint arrays.
-__device__ inline int64_t grp_base(const BwdArgs& a, int b, int h) {
-  if (a.cu) return (int64_t)h * a.nslotG + bwd_begin(a, b) / (16 * kGS) + b;
-  return ((int64_t)b * a.H + h) * a.NG;
-}
-
-// A group slot of the gradient grid -> (sequence b, head h, group g); false
-// for a slot no group uses.
-__device__ inline bool bwd2_group(const BwdArgs& a, int64_t blk, int& b, int& h, int& g) {
-  if (!a.cu) {
-    g = (int)(blk % a.NG);
-    const int64_t bh = blk / a.NG;
-    h = (int)(bh % a.H);
-    b = (int)(bh / a.H);
-    return 16 * kGS * g < a.T;
-  }
-  h = (int)(blk / a.nslotG);
-  const int slot = (int)(blk - (int64_t)h * a.nslotG);
-  int lo = 0, hi = a.B - 1;                  // the last s whose group 0 sits at or before slot
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (bwd_begin(a, mid) / (16 * kGS) + mid <= slot) lo = mid;
-    else hi = mid - 1;
-  }
-  b = lo;
-  const BSeq sq = bwd_seq(a, b, h);
-  g = slot - (bwd_begin(a, b) / (16 * kGS) + b);
-  return g >= 0 && kGS * g < sq.NC;
-}
-
-// Per-tile operator fragments built from the record's row-major float32 16 x
-// 16 matrices: element (t, i) of M as a split A fragment [M_hi | M_lo] (lane
-// (n = t, grp = i / 4), register i % 4), or of M^T (lane (n = i, grp = t / 4),
-// register t % 4).  `frag` is 64 lanes x 16 bytes.
-__device__ inline void put_op(char* frag, int t, int i, float x, bool transposed) {
-  const int n = transposed ? i : t, c = transposed ? t : i;
-  char* p = frag + 16 * (16 * (c >> 2) + n) + 2 * (c & 3);
-  const __bf16 hb = (__bf16)x;
-  *reinterpret_cast<__bf16*>(p) = hb;
-  *reinterpret_cast<__bf16*>(p + 8) = (__bf16)(x - (float)hb);
-}
 
 // ------------------------------------------------------------- tile prep
 // The per-tile record (in-tile running sum G of the log-decay, beta, T =
@@ -318,402 +134,6 @@ __global__ __launch_bounds__(256) void bwd_prep_wave_kernel(BwdArgs a, int64_t n
     rec[BRec::G + lane] = Gc;
     rec[BRec::BETA + lane] = bx;
   }
-}
-
-// ------------------------------------ states at every kHS-th tile
-// Record of one staged tile (bytes).
-template <int DK, int SPW>
-struct H2Rec {
-  static constexpr int KR = 0;                       // K rows
-  static constexpr int TF = Rows<DK>::BYTES;         // [T hi | T lo] A fragments
-  static constexpr int VF = TF + 1024;               // V slices, accumulator layout, bf16
-  static constexpr int GM = VF + SPW * 512;          // gamma[16]
-  static constexpr int EC = GM + 64;                 // ec[16]
-  static constexpr int BT = EC + 64;                 // beta[16]
-  static constexpr int GC = BT + 64;                 // gamma_C
-  static constexpr int BYTES = GC + 16;
-  static_assert(BYTES % 16 == 0, "alignment");
-};
-
-template <int DK, int SPW>
-struct H2Raw {
-  uint4 kr[DK / 32];     // K row pieces (2 DK / 16 pieces per row, 16 rows, 64 lanes)
-  f32x4 ti;
-  bf16x4 vv[SPW];
-  float g, bt, gC;
-};
-
-template <int DK, int NP, int SPW>
-__device__ inline void hstates_body(const BwdArgs& a, int64_t blk, char* smem) {
-  using R = H2Rec<DK, SPW>;
-  using RW = Rows<DK>;
-  constexpr int NS = DK / 32, NT = DK / 16;
-  const int NW = a.Dv / (16 * SPW);
-  const int sl = (int)(blk % NW);
-  const int64_t bh = blk / NW;
-  const int h = (int)(bh % a.H), b = (int)(bh / a.H);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int n = lane & 15, grp = lane >> 4;
-  const BSeq sq = bwd_seq(a, b, h);
-  const int NC = sq.NC;
-  const int NE = (NC + NP - 1) / NP;
-  auto rec_of = [&](int c) -> char* { return smem + (((c / NP) & 1) * NP + c % NP) * R::BYTES; };
-
-  if (wave < SPW) {
-    const int v0 = 16 * (SPW * sl + wave);
-    f32x4 Hacc[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        Hacc[t][i] = a.h0 ? a.h0[(bh * DK + 16 * t + 4 * grp + i) * a.Dv + v0 + n] : 0.f;
-    }
-    bf16x8 Hh[NS], Hl[NS];
-    split_state<NS>(Hacc, Hh, Hl);
-    unsigned* const hw =
-        a.hw + grp_base(a, b, h) * kHPG * DK * a.Dv + (int64_t)(v0 / 16) * DK * 16;
-    __syncthreads();  // epoch 0 staged
-    for (int ep = 0; ep < NE; ++ep) {
-      for (int j = 0; j < NP; ++j) {
-        const int c = ep * NP + j;
-        if (c >= NC) break;
-        const char* rec = rec_of(c);
-        if (c % kHS == 0) {
-          uint4* dst = reinterpret_cast<uint4*>(hw + (int64_t)(c / kHS) * DK * a.Dv);
-#pragma unroll
-          for (int t = 0; t < NT; ++t) {
-            const bf16x8 hh = Hh[t >> 1], hl = Hl[t >> 1];
-            dst[t * 64 + lane] = (t & 1) ? pack_words(second4(hh), second4(hl))
-                                         : pack_words(first4(hh), first4(hl));
-          }
-        }
-        // R = K H
-        f32x4 Rk = zero4();
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          const bf16x8 ka = RW::afrag(rec + R::KR, s, n, grp);
-          Rk = mma32b(ka, Hl[s], Rk);
-          Rk = mma32b(ka, Hh[s], Rk);
-        }
-        const f32x4 vf = to_f4(*reinterpret_cast<const bf16x4*>(rec + R::VF + wave * 512 + 8 * lane));
-        const f32x4 gm = *reinterpret_cast<const f32x4*>(rec + R::GM + 16 * grp);
-        const f32x4 ec = *reinterpret_cast<const f32x4*>(rec + R::EC + 16 * grp);
-        const f32x4 bt = *reinterpret_cast<const f32x4*>(rec + R::BT + 16 * grp);
-        const float gC = *reinterpret_cast<const float*>(rec + R::GC);
-        const bf16x8 tf = *reinterpret_cast<const bf16x8*>(rec + R::TF + 16 * lane);
-        f32x4 Y;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) Y[i] = bt[i] * (vf[i] - gm[i] * Rk[i]);
-        const Sp4 sy = split4(Y);
-        f32x4 U = mma32b(tf, cat8(sy.h, sy.h), zero4());
-        U = mma32b_lo(tf, sy.l, U);
-        f32x4 Up;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) Up[i] = ec[i] * U[i];
-        const Sp4 su = split4(Up);
-        const bf16x8 ub = cat8(su.h, su.l);
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const bf16x4 kt = RW::tfrag(rec + R::KR, t, n, grp);
-          Hacc[t] = Hacc[t] * gC;
-          Hacc[t] = mma32b(cat8(kt, kt), ub, Hacc[t]);
-        }
-        split_state<NS>(Hacc, Hh, Hl);
-      }
-      __syncthreads();  // this epoch consumed, the next one staged
-    }
-    if (a.hTo) {
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          a.hTo[(bh * DK + 16 * t + 4 * grp + i) * a.Dv + v0 + n] = Hacc[t][i];
-      }
-    }
-    return;
-  }
-
-  // ---------------------------------------------------------------- loaders
-  const int p = wave - SPW;
-  const __bf16* kp = static_cast<const __bf16*>(a.k);
-  const __bf16* vp = static_cast<const __bf16*>(a.v);
-  const int v0 = 16 * SPW * sl;
-  constexpr int PER_ROW = 2 * DK / 16;
-  auto load = [&](H2Raw<DK, SPW>& r, int c) {
-    if (NC == 0) return;          // an empty sequence loads nothing
-    c = min(c, NC - 1);
-#pragma unroll
-    for (int x = 0; x < DK / 32; ++x) {
-      const int idx = 64 * x + lane, row = idx / PER_ROW, pc = idx % PER_ROW;
-      const int tok = 16 * c + row;
-      r.kr[x] = tok < sq.T
-                    ? *reinterpret_cast<const uint4*>(kp + ((sq.tok0 + tok) * a.H + h) * DK + 8 * pc)
-                    : uint4{0u, 0u, 0u, 0u};
-    }
-    const float* rec = a.rec + (sq.rbase + c) * BRec::FLOATS;
-    r.ti = reinterpret_cast<const f32x4*>(rec + BRec::TINV)[lane];
-    r.g = rec[BRec::G + n];
-    r.bt = rec[BRec::BETA + n];
-    r.gC = rec[BRec::G + kT - 1];
-#pragma unroll
-    for (int w = 0; w < SPW; ++w) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tok = 16 * c + 4 * grp + i;
-        r.vv[w][i] = tok < sq.T ? vp[((sq.tok0 + tok) * a.H + h) * a.Dv + v0 + 16 * w + n]
-                                : (__bf16)0.f;
-      }
-    }
-  };
-  auto store = [&](const H2Raw<DK, SPW>& r, int c) {
-    if (c >= NC) return;
-    char* rec = rec_of(c);
-#pragma unroll
-    for (int x = 0; x < DK / 32; ++x) {
-      const int idx = 64 * x + lane, row = idx / PER_ROW, pc = idx % PER_ROW;
-      *reinterpret_cast<uint4*>(rec + R::KR + row * RW::PITCH + 16 * pc) = r.kr[x];
-    }
-    // T arrives row-major: lane l holds T[l / 4][4 (l % 4) + e]
-#pragma unroll
-    for (int e = 0; e < 4; ++e) put_op(rec + R::TF, lane >> 2, 4 * (lane & 3) + e, r.ti[e], false);
-#pragma unroll
-    for (int w = 0; w < SPW; ++w) *reinterpret_cast<bf16x4*>(rec + R::VF + w * 512 + 8 * lane) = r.vv[w];
-    if (grp == 0) {
-      reinterpret_cast<float*>(rec + R::GM)[n] = __expf(r.g);
-      reinterpret_cast<float*>(rec + R::EC)[n] = __expf(r.gC - r.g);
-      reinterpret_cast<float*>(rec + R::BT)[n] = r.bt;
-      if (n == 0) *reinterpret_cast<float*>(rec + R::GC) = __expf(r.gC);
-    }
-  };
-  H2Raw<DK, SPW> ra, rb;
-  load(ra, p);
-  store(ra, p);                 // epoch 0
-  load(ra, NP + p);             // epoch 1, staged during epoch 0
-  __syncthreads();
-  for (int ep = 0; ep < NE; ep += 2) {
-    load(rb, (ep + 2) * NP + p);
-    store(ra, (ep + 1) * NP + p);
-    __syncthreads();
-    if (ep + 1 < NE) {
-      load(ra, (ep + 3) * NP + p);
-      store(rb, (ep + 2) * NP + p);
-      __syncthreads();
-    }
-  }
-}
-
-// ------------------------------------ state gradients at every group end
-template <int DK, int SPW>
-struct D2Rec {
-  static constexpr int KR = 0;                       // K rows
-  static constexpr int QR = Rows<DK>::BYTES;         // Q rows
-  static constexpr int PT = 2 * Rows<DK>::BYTES;     // [P^T hi | P^T lo] A fragments
-  static constexpr int TT = PT + 1024;               // [T^T hi | T^T lo]
-  static constexpr int DO = TT + 1024;               // dO slices, accumulator layout, bf16
-  static constexpr int GM = DO + SPW * 512;          // gamma[16]
-  static constexpr int EC = GM + 64;                 // ec[16]
-  static constexpr int BT = EC + 64;                 // beta[16]
-  static constexpr int GC = BT + 64;                 // gamma_C
-  static constexpr int BYTES = GC + 16;
-  static_assert(BYTES % 16 == 0, "alignment");
-};
-
-template <int DK, int SPW>
-struct D2Raw {
-  uint4 kr[DK / 32], qr[DK / 32];
-  f32x4 pm, tm;
-  bf16x4 dd[SPW];
-  float g, bt, gC;
-};
-
-template <int DK, int NP, int SPW>
-__device__ inline void dh_body(const BwdArgs& a, int64_t blk, char* smem) {
-  using R = D2Rec<DK, SPW>;
-  using RW = Rows<DK>;
-  constexpr int NS = DK / 32, NT = DK / 16;
-  const int NW = a.Dv / (16 * SPW);
-  const int sl = (int)(blk % NW);
-  const int64_t bh = blk / NW;
-  const int h = (int)(bh % a.H), b = (int)(bh / a.H);
-  // roles rotated against the forward-state blocks (chain waves last), so that
-  // the chain waves of the two kinds of block sharing a compute unit tend to
-  // sit on different SIMDs
-  const int wave = (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) + SPW) % (NP + SPW);
-  const int lane = threadIdx.x & 63;
-  const int n = lane & 15, grp = lane >> 4;
-  const BSeq sq = bwd_seq(a, b, h);
-  const int NC = sq.NC;
-  const int NE = (NC + NP - 1) / NP;
-  // records by processing index m (tile NC - 1 - m)
-  auto rec_of = [&](int m) -> char* { return smem + (((m / NP) & 1) * NP + m % NP) * R::BYTES; };
-
-  if (wave < SPW) {
-    const int v0 = 16 * (SPW * sl + wave);
-    f32x4 D[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        D[t][i] = a.dhT ? a.dhT[(bh * DK + 16 * t + 4 * grp + i) * a.Dv + v0 + n] : 0.f;
-    }
-    bf16x8 Dh[NS], Dl[NS];
-    split_state<NS>(D, Dh, Dl);
-    unsigned* const dw = a.dw + grp_base(a, b, h) * DK * a.Dv + (int64_t)(v0 / 16) * DK * 16;
-    __syncthreads();  // epoch 0 staged
-    for (int ep = 0; ep < NE; ++ep) {
-      for (int j = 0; j < NP; ++j) {
-        const int m = ep * NP + j;
-        if (m >= NC) break;
-        const int c = NC - 1 - m;
-        const char* rec = rec_of(m);
-        if (c % kGS == kGS - 1 || c == NC - 1) {
-          uint4* dst = reinterpret_cast<uint4*>(dw + (int64_t)(c / kGS) * DK * a.Dv);
-#pragma unroll
-          for (int t = 0; t < NT; ++t) {
-            const bf16x8 dh = Dh[t >> 1], dl = Dl[t >> 1];
-            dst[t * 64 + lane] = (t & 1) ? pack_words(second4(dh), second4(dl))
-                                         : pack_words(first4(dh), first4(dl));
-          }
-        }
-        f32x4 KD = zero4();
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          const bf16x8 ka = RW::afrag(rec + R::KR, s, n, grp);
-          KD = mma32b(ka, Dl[s], KD);
-          KD = mma32b(ka, Dh[s], KD);
-        }
-        const bf16x4 dob = *reinterpret_cast<const bf16x4*>(rec + R::DO + wave * 512 + 8 * lane);
-        const f32x4 dO = to_f4(dob);
-        const f32x4 gm = *reinterpret_cast<const f32x4*>(rec + R::GM + 16 * grp);
-        const f32x4 ec = *reinterpret_cast<const f32x4*>(rec + R::EC + 16 * grp);
-        const f32x4 bt = *reinterpret_cast<const f32x4*>(rec + R::BT + 16 * grp);
-        const float gC = *reinterpret_cast<const float*>(rec + R::GC);
-        const bf16x8 pt = *reinterpret_cast<const bf16x8*>(rec + R::PT + 16 * lane);
-        const bf16x8 tt = *reinterpret_cast<const bf16x8*>(rec + R::TT + 16 * lane);
-        f32x4 eKD;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) eKD[i] = ec[i] * KD[i];
-        const f32x4 dU = mma32b(pt, cat8(dob, dob), eKD);
-        const Sp4 su = split4(dU);
-        f32x4 dY = mma32b(tt, cat8(su.h, su.h), zero4());
-        dY = mma32b_lo(tt, su.l, dY);
-        f32x4 Og, Z;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          Og[i] = gm[i] * dO[i];
-          Z[i] = -(bt[i] * gm[i] * dY[i]);
-        }
-        const Sp4 so = split4(Og), sz = split4(Z);
-        const bf16x8 ob = cat8(so.h, so.l), zb = cat8(sz.h, sz.l);
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const bf16x4 qt = RW::tfrag(rec + R::QR, t, n, grp);
-          const bf16x4 kt = RW::tfrag(rec + R::KR, t, n, grp);
-          D[t] = D[t] * gC;
-          D[t] = mma32b(cat8(qt, qt), ob, D[t]);
-          D[t] = mma32b(cat8(kt, kt), zb, D[t]);
-        }
-        split_state<NS>(D, Dh, Dl);
-      }
-      __syncthreads();  // this epoch consumed, the next one staged
-    }
-    if (a.dh0) {
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          a.dh0[(bh * DK + 16 * t + 4 * grp + i) * a.Dv + v0 + n] = D[t][i];
-      }
-    }
-    return;
-  }
-
-  // ---------------------------------------------------------------- loaders
-  const int p = wave - SPW;
-  const __bf16* kp = static_cast<const __bf16*>(a.k);
-  const __bf16* qp = static_cast<const __bf16*>(a.q);
-  const __bf16* dp = static_cast<const __bf16*>(a.dout);
-  const int v0 = 16 * SPW * sl;
-  constexpr int PER_ROW = 2 * DK / 16;
-  auto load = [&](D2Raw<DK, SPW>& r, int m) {
-    if (NC == 0) return;          // an empty sequence loads nothing
-    const int c = NC - 1 - min(m, NC - 1);
-#pragma unroll
-    for (int x = 0; x < DK / 32; ++x) {
-      const int idx = 64 * x + lane, row = idx / PER_ROW, pc = idx % PER_ROW;
-      const int tok = 16 * c + row;
-      const int64_t off = ((sq.tok0 + tok) * a.H + h) * DK + 8 * pc;
-      const bool ok = tok < sq.T;
-      r.kr[x] = ok ? *reinterpret_cast<const uint4*>(kp + off) : uint4{0u, 0u, 0u, 0u};
-      r.qr[x] = ok ? *reinterpret_cast<const uint4*>(qp + off) : uint4{0u, 0u, 0u, 0u};
-    }
-    const float* rec = a.rec + (sq.rbase + c) * BRec::FLOATS;
-    r.pm = reinterpret_cast<const f32x4*>(rec + BRec::P)[lane];
-    r.tm = reinterpret_cast<const f32x4*>(rec + BRec::TINV)[lane];
-    r.g = rec[BRec::G + n];
-    r.bt = rec[BRec::BETA + n];
-    r.gC = rec[BRec::G + kT - 1];
-#pragma unroll
-    for (int w = 0; w < SPW; ++w) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tok = 16 * c + 4 * grp + i;
-        r.dd[w][i] = tok < sq.T ? dp[((sq.tok0 + tok) * a.H + h) * a.Dv + v0 + 16 * w + n]
-                                : (__bf16)0.f;
-      }
-    }
-  };
-  auto store = [&](const D2Raw<DK, SPW>& r, int m) {
-    if (m >= NC) return;
-    char* rec = rec_of(m);
-#pragma unroll
-    for (int x = 0; x < DK / 32; ++x) {
-      const int idx = 64 * x + lane, row = idx / PER_ROW, pc = idx % PER_ROW;
-      *reinterpret_cast<uint4*>(rec + R::KR + row * RW::PITCH + 16 * pc) = r.kr[x];
-      *reinterpret_cast<uint4*>(rec + R::QR + row * RW::PITCH + 16 * pc) = r.qr[x];
-    }
-    // P and T arrive row-major (lane l holds row l / 4, columns 4 (l % 4) + e)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      put_op(rec + R::PT, lane >> 2, 4 * (lane & 3) + e, r.pm[e], true);
-      put_op(rec + R::TT, lane >> 2, 4 * (lane & 3) + e, r.tm[e], true);
-    }
-#pragma unroll
-    for (int w = 0; w < SPW; ++w) *reinterpret_cast<bf16x4*>(rec + R::DO + w * 512 + 8 * lane) = r.dd[w];
-    if (grp == 0) {
-      reinterpret_cast<float*>(rec + R::GM)[n] = __expf(r.g);
-      reinterpret_cast<float*>(rec + R::EC)[n] = __expf(r.gC - r.g);
-      reinterpret_cast<float*>(rec + R::BT)[n] = r.bt;
-      if (n == 0) *reinterpret_cast<float*>(rec + R::GC) = __expf(r.gC);
-    }
-  };
-  D2Raw<DK, SPW> ra, rb;
-  load(ra, p);
-  store(ra, p);                 // epoch 0
-  load(ra, NP + p);             // epoch 1, staged during epoch 0
-  __syncthreads();
-  for (int ep = 0; ep < NE; ep += 2) {
-    load(rb, (ep + 2) * NP + p);
-    store(ra, (ep + 1) * NP + p);
-    __syncthreads();
-    if (ep + 1 < NE) {
-      load(ra, (ep + 3) * NP + p);
-      store(rb, (ep + 2) * NP + p);
-      __syncthreads();
-    }
-  }
-}
-
-// The forward states and the state gradients do not depend on each other: one
-// launch runs both, blocks [0, nblk) the first and [nblk, 2 nblk) the second,
-// so that the two serial chains share the compute units.
-template <int DK, int NP, int SPW>
-__global__ __launch_bounds__(64 * (NP + SPW)) void bwd2_states_kernel(BwdArgs a, int nblk) {
-  constexpr int HB = 2 * NP * H2Rec<DK, SPW>::BYTES, DB = 2 * NP * D2Rec<DK, SPW>::BYTES;
-  __shared__ __attribute__((aligned(16))) char smem[HB > DB ? HB : DB];
-  if ((int)blockIdx.x < nblk) hstates_body<DK, NP, SPW>(a, blockIdx.x, smem);
-  else dh_body<DK, NP, SPW>(a, blockIdx.x - nblk, smem);
 }
 
 // --------------------------------------------------- per-group gradients
@@ -1312,13 +732,7 @@ hipError_t launch_bwd2_t(const BwdArgs& a, hipStream_t st, bool forward_only = f
   const int spw = (a.Dv / 16) % 4 == 0 ? 4 : (a.Dv / 16) % 2 == 0 ? 2 : 1;
   const int nblk = (int)(slices / spw);
   const unsigned grid = (unsigned)(forward_only ? nblk : 2 * nblk);
-  if (spw == 4)
-    hipLaunchKernelGGL((bwd2_states_kernel<DK, 2, 4>), dim3(grid), dim3(64 * 6), 0, st, a, nblk);
-  else if (spw == 2)
-    hipLaunchKernelGGL((bwd2_states_kernel<DK, 2, 2>), dim3(grid), dim3(64 * 4), 0, st, a, nblk);
-  else
-    hipLaunchKernelGGL((bwd2_states_kernel<DK, 2, 1>), dim3(grid), dim3(64 * 3), 0, st, a, nblk);
-  if ((e = hipGetLastError()) != hipSuccess || forward_only) return e;
+  if ((e = launch_bwd_bf16_states(&a, sizeof a, DK, spw, grid, nblk, st)) != hipSuccess || forward_only) return e;
   hipLaunchKernelGGL((bwd2_grad_kernel<DK>), dim3((unsigned)groups), dim3(512), 0, st, a);
   return hipGetLastError();
 }
