@@ -212,9 +212,10 @@ __device__ inline void hstates_body(const BwdArgs& a, int64_t blk, char* smem) {
 //   D_start = gC_{c-1} D_mid + Q_{c-1}^T diag(gamma_{c-1}) dO_{c-1}
 //             - K_{c-1}^T diag(beta_{c-1} gamma_{c-1}) dY_{c-1},
 // so that the products with the state (K_c D, K_{c-1} D) and its split happen
-// once per pair; the 16 x 16 operators M1 and M2 depend on the inputs only and
-// are built by the loader of the pair's earlier tile.  An odd tile count puts
-// an empty tile NC in front (no rows, unit decay: the identity step).
+// once per pair; the 16 x 16 operators M1 and M2 depend on the inputs only
+// (each chain wave forms them from the staged rows, on the matrix cores,
+// beside its K D products).  An odd tile count puts an empty tile NC in front
+// (no rows, unit decay: the identity step).
 template <int DK, int SPW>
 struct D2Rec {
   static constexpr int KR = 0;                       // K rows
@@ -226,15 +227,12 @@ struct D2Rec {
   static constexpr int EC = GM + 64;                 // ec[16]
   static constexpr int BT = EC + 64;                 // beta[16]
   static constexpr int GC = BT + 64;                 // gamma_C
-  static constexpr int M1 = GC + 16;                 // [M1 hi | M1 lo] (earlier tile of a pair)
-  static constexpr int M2 = M1 + 1024;               // [M2 hi | M2 lo]
-  static constexpr int BYTES = M2 + 1024;
+  static constexpr int BYTES = GC + 16;
   static_assert(BYTES % 16 == 0, "alignment");
 };
 
 // Row pieces of a tile as the loaders hold them: lane (n, grp), piece x, has
-// columns 32 x + 8 grp .. + 7 of row n, which is also the lane's part of a
-// 32-deep MFMA operand over d_k block x (as the rows of A, or of B^T).
+// columns 32 x + 8 grp .. + 7 of row n.
 template <int DK, int SPW>
 struct D2Raw {
   uint4 kr[DK / 32], qr[DK / 32];
@@ -297,16 +295,22 @@ __device__ inline void dh_body(const BwdArgs& a, int64_t blk, char* smem) {
                                          : pack_words(first4(dh), first4(dl));
           }
         }
-        // K_c D and K_{c-1} D
-        f32x4 KA = zero4(), KB = zero4();
+        // K_c D and K_{c-1} D; beside them Q_c K_{c-1}^T and K_c K_{c-1}^T,
+        // whose accumulators hold, at lane (n, grp) register i, (K_{c-1}
+        // Q_c^T)[n][4 grp + i] and (K_{c-1} K_c^T)[n][4 grp + i]: the lane's
+        // parts of the split A fragments of M1 and M2 once scaled
+        f32x4 KA = zero4(), KB = zero4(), A1 = zero4(), A2 = zero4();
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
           const bf16x8 ka = RW::afrag(ra + R::KR, s, n, grp);
           const bf16x8 kb = RW::afrag(rb + R::KR, s, n, grp);
+          const bf16x8 qa = RW::afrag(ra + R::QR, s, n, grp);
           KA = mma32b(ka, Dl[s], KA);
           KB = mma32b(kb, Dl[s], KB);
+          A1 = mma32b(qa, kb, A1);
           KA = mma32b(ka, Dh[s], KA);
           KB = mma32b(kb, Dh[s], KB);
+          A2 = mma32b(ka, kb, A2);
         }
         const float gCa = *reinterpret_cast<const float*>(ra + R::GC);
         const float gCb = *reinterpret_cast<const float*>(rb + R::GC);
@@ -340,8 +344,13 @@ __device__ inline void dh_body(const BwdArgs& a, int64_t blk, char* smem) {
         const Sp4 soa = split4(Oa), sza = split4(Za);
         const bf16x8 ozha = cat8(soa.h, sza.h), ozla = cat8(soa.l, sza.l);
         // K_{c-1} D_mid = gC_c K_{c-1} D + M1 dO_c + M2 dY_c
-        const bf16x8 m1 = *reinterpret_cast<const bf16x8*>(rb + R::M1 + 16 * lane);
-        const bf16x8 m2 = *reinterpret_cast<const bf16x8*>(rb + R::M2 + 16 * lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          A1[i] *= gma[i];
+          A2[i] *= -(bta[i] * gma[i]);
+        }
+        const Sp4 s1 = split4(A1), s2 = split4(A2);
+        const bf16x8 m1 = cat8(s1.h, s1.l), m2 = cat8(s2.h, s2.l);
         KB = KB * gCa;
         KB = mma32b(m1, cat8(doa, doa), KB);
         KB = mma32b(m2, cat8(sya.h, sya.h), KB);
@@ -443,23 +452,8 @@ __device__ inline void dh_body(const BwdArgs& a, int64_t blk, char* smem) {
     r.gC = rec[BRec::G + kT - 1];
     Slab<SPW>::load(r.dr, tile_base(dp, c, a.Dv) + v0, tsv, sq.T - 1 - 16 * c, lane);
   };
-  // the later tile's rows and gates, for the pair operators of the earlier
-  // tile (processing index m odd; L2 reads of what the other loader fetched)
-  struct Partner {
-    uint4 kn[DK / 32], qn[DK / 32];
-    f32x4 gn, bn;
-  };
-  auto partner = [&](Partner& pt, int m) {
-    if (!(m & 1) || m >= NCe) return;
-    const int cn = NCe - m;       // the earlier tile is NCe - 1 - m
-    rows(kp, cn, pt.kn);
-    rows(qp, cn, pt.qn);
-    const float* rn = a.rec + (sq.rbase + min(cn, NC - 1)) * BRec::FLOATS;
-    pt.gn = *reinterpret_cast<const f32x4*>(rn + BRec::G + 4 * grp);
-    pt.bn = *reinterpret_cast<const f32x4*>(rn + BRec::BETA + 4 * grp);
-  };
-  // CHK: the pair reaches past the sequence end, and loads there are zeroed
-  auto stage = [&](const D2Raw<DK, SPW>& r, const Partner& pt, int m, auto chk) {
+  // CHK: the tile reaches past the sequence end, and loads there are zeroed
+  auto stage = [&](const D2Raw<DK, SPW>& r, int m, auto chk) {
     constexpr bool CHK = decltype(chk)::value;
     char* rec = rec_of(m);
     const int c = NCe - 1 - m;
@@ -485,53 +479,25 @@ __device__ inline void dh_body(const BwdArgs& a, int64_t blk, char* smem) {
       reinterpret_cast<float*>(rec + R::BT)[n] = real ? r.bt : 0.f;
       if (n == 0) *reinterpret_cast<float*>(rec + R::GC) = __expf(gC);
     }
-    if (m & 1) {
-      // the earlier tile c of a pair: M1 = K_c Q_{c+1}^T diag(gamma_{c+1}),
-      // M2 = -K_c K_{c+1}^T diag(beta_{c+1} gamma_{c+1}).  The accumulator of
-      // Q_{c+1} K_c^T holds, at lane (n, grp) register i, (K_c Q_{c+1}^T)[n][4
-      // grp + i]: the lane's part of the split A fragment as it stands.
-      const bool nok = !CHK || 16 * (c + 1) + n < sq.T, nreal = !CHK || c + 1 < NC;
-      f32x4 A1 = zero4(), A2 = zero4();
-#pragma unroll
-      for (int x = 0; x < DK / 32; ++x) {
-        const bf16x8 kc = u4_bf8(zero_if(rok, r.kr[x]));
-        A1 = mma32b(u4_bf8(zero_if(nok, pt.qn[x])), kc, A1);
-        A2 = mma32b(u4_bf8(zero_if(nok, pt.kn[x])), kc, A2);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float e = nreal ? __expf(pt.gn[i]) : 0.f;
-        A1[i] *= e;
-        A2[i] *= -(pt.bn[i] * e);
-      }
-      const Sp4 s1 = split4(A1), s2 = split4(A2);
-      *reinterpret_cast<bf16x8*>(rec + R::M1 + 16 * lane) = cat8(s1.h, s1.l);
-      *reinterpret_cast<bf16x8*>(rec + R::M2 + 16 * lane) = cat8(s2.h, s2.l);
-    }
   };
-  auto store = [&](const D2Raw<DK, SPW>& r, const Partner& pt, int m) {
+  auto store = [&](const D2Raw<DK, SPW>& r, int m) {
     if (m >= NCe) return;
-    // only the pairs at the sequence end need zeroing (a uniform test): a
-    // pair whose later tile ends inside the sequence has every row in it
-    if (16 * (NCe - m) + 16 <= sq.T) stage(r, pt, m, std::false_type{});
-    else stage(r, pt, m, std::true_type{});
+    // only the tiles at the sequence end need zeroing (a uniform test)
+    if (16 * (NCe - 1 - m) + 16 <= sq.T) stage(r, m, std::false_type{});
+    else stage(r, m, std::true_type{});
   };
   D2Raw<DK, SPW> r;
-  Partner pt;
   load(r, q * NP + p);
-  partner(pt, q * NP + p);
   if (q == 0) {
-    store(r, pt, p);            // epoch 0
+    store(r, p);                // epoch 0
     load(r, 2 * NP + p);
-    partner(pt, 2 * NP + p);
   }
   __syncthreads();
   for (int ep = 0; ep < NE; ++ep) {
     // the chain runs epoch ep; epoch ep + 1 is staged by the loaders of its parity
     if (((ep + 1) & 1) == q) {
-      store(r, pt, (ep + 1) * NP + p);
+      store(r, (ep + 1) * NP + p);
       load(r, (ep + 3) * NP + p);
-      partner(pt, (ep + 3) * NP + p);
     }
     __syncthreads();
   }
