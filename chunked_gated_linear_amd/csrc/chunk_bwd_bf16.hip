@@ -347,8 +347,8 @@ __global__ __launch_bounds__(512) void bwd2_grad_kernel(BwdArgs a) {
     const float gamC = __expf(sc[kT - 1]);
     f32x4 pB = zero4(), pG = zero4(), pW = zero4(), dPp = zero4(), dAp = zero4();
     float hdh = 0.f;
-    bf16x8 ob, zb;               // [gamma dO] and [-beta gamma dY] split, for the step to j - 1
-    bf16x8 dO8, aY8, aU8;        // row fragments: [dO, dO], [aY hi | lo], [aU hi | lo]
+    bf16x8 ozh, ozl;             // [gamma dO ; -beta gamma dY], hi and lo parts, for the step to j - 1
+    bf16x8 dO8, ayuh, ayul;      // row fragments: [dO, dO], [aY | aU] hi and lo parts
     bf16x8 Hh[NS], Hl[NS];       // H at the start of tile j, split
     if (act) {
       // H at the start of tile j: j % kHS forward steps from the state stored
@@ -462,8 +462,8 @@ __global__ __launch_bounds__(512) void bwd2_grad_kernel(BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) Og[i] = gm4[i] * dd[i];
         const Sp4 so = split4(Og);
-        ob = cat8(so.h, so.l);
-        zb = cat8(say.h, say.l);
+        ozh = cat8(so.h, say.h);
+        ozl = cat8(so.l, say.l);
       }
       tr_put(xr + 0 * 512, lane, dob);
       tr_put(xr + 1 * 512, lane, su.h);
@@ -484,8 +484,8 @@ __global__ __launch_bounds__(512) void bwd2_grad_kernel(BwdArgs a) {
       dPp = mma32b(cat8(dOr, dOr), cat8(Urh, Url), dPp);
       dAp = mma32b(cat8(dYrh, dYrl), cat8(Urh, Urh), dAp);
       dAp = mma32b_lo(cat8(dYrh, dYrl), Url, dAp);
-      aY8 = cat8(aYrh, aYrl);
-      aU8 = cat8(aUrh, aUrl);
+      ayuh = cat8(aYrh, aUrh);
+      ayul = cat8(aYrl, aUrl);
       dO8 = cat8(dOr, dOr);
     }
 
@@ -599,10 +599,12 @@ __global__ __launch_bounds__(512) void bwd2_grad_kernel(BwdArgs a) {
             const bf16x4 hrl = tr_get(x8 + (4 * e + 1) * 512, n, grp);
             const bf16x4 drh = tr_get(x8 + (4 * e + 2) * 512, n, grp);
             const bf16x4 drl = tr_get(x8 + (4 * e + 3) * 512, n, grp);
-            dKp[r] = mma32b(aY8, cat8(hrh, hrh), dKp[r]);
-            dKp[r] = mma32b_lo(aY8, hrl, dKp[r]);
-            dKp[r] = mma32b(aU8, cat8(drh, drh), dKp[r]);
-            dKp[r] = mma32b_lo(aU8, drl, dKp[r]);
+            // aY H^T + aU D^T as [aY | aU] [H ; D], split by split: hi.hi,
+            // lo.hi, hi.lo
+            const bf16x8 hdh = cat8(hrh, drh);
+            dKp[r] = mma32b(ayuh, hdh, dKp[r]);
+            dKp[r] = mma32b(ayul, hdh, dKp[r]);
+            dKp[r] = mma32b(ayuh, cat8(hrl, drl), dKp[r]);
           }
         }
         wave_fence();
@@ -655,8 +657,9 @@ __global__ __launch_bounds__(512) void bwd2_grad_kernel(BwdArgs a) {
       const bf16x4 kt = RW::tfrag(kr, w, n, grp);
       const bf16x4 qt = RW::tfrag(qr, w, n, grp);
       dQa = mma32b(cat8(spe.h, spe.l), cat8(kt, kt), dQa);
-      dKa = mma32b(cat8(spet.h, spet.l), cat8(qt, qt), dKa);
-      dKa = mma32b(cat8(smm.h, smm.l), cat8(kt, kt), dKa);
+      const bf16x8 qk = cat8(qt, kt);
+      dKa = mma32b(cat8(spet.h, smm.h), qk, dKa);
+      dKa = mma32b(cat8(spet.l, smm.l), qk, dKa);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tok = 16 * c + 4 * grp + i;
@@ -702,8 +705,9 @@ __global__ __launch_bounds__(512) void bwd2_grad_kernel(BwdArgs a) {
       for (int t = 0; t < NT; ++t) {
         const bf16x4 qt = RW::tfrag(qr, t, n, grp);
         const bf16x4 kt = RW::tfrag(kr, t, n, grp);
-        Dn[t] = mma32b(cat8(qt, qt), ob, Dn[t]);
-        Dn[t] = mma32b(cat8(kt, kt), zb, Dn[t]);
+        const bf16x8 qk = cat8(qt, kt);
+        Dn[t] = mma32b(qk, ozh, Dn[t]);
+        Dn[t] = mma32b(qk, ozl, Dn[t]);
       }
       split_state<NS>(Dn, Dh, Dl);
       const uint4* const hn = hp(j - 1);
