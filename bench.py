@@ -65,10 +65,10 @@ TRAFFIC_KIB = {
                        "fetch": 1391772, "write": 1591826},
     "backward": {"sources": ("chunk_bwd_bf16.hip", "chunk_bwd_bf16_states.hip", "la_bwd_bf16.h", "la_bwd.h",
                              "la_device.h", "../build.py"),
-                 "sha256_16": "27234f5fb2669896",
+                 "sha256_16": "4877d8e4d34356d2",
                  # one call at B=4 H=16 T=8192: tile records, states + state
                  # gradients (one launch), gradients
-                 "fetch": 2171521, "write": 2494678},
+                 "fetch": 2153326, "write": 2493887},
     "decode_channel": {"sources": ("chunk_channel.hip", "la_device.h"),
                        "sha256_16": "7fa2297eef5c7589",
                        # one step at B=256 H=32 d=128 with a per-channel gate (median of six)

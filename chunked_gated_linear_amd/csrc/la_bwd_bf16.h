@@ -45,26 +45,25 @@ __device__ inline f32x4 to_f4(bf16x4 x) {
   return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
 }
 
-// A float32 fragment as bf16 hi + lo parts: hi is x cut to its top 16 bits
-// (|x - hi| < 2^-7 |x|, and x - hi is exact in float32), lo is x - hi rounded
-// to bf16, so |x - hi - lo| <= 2^-16 |x|.  Three instructions per element:
-// a mask, a subtraction, and half each of a byte permute (the hi pairs) and a
-// packed conversion (the lo pairs).
+// A float32 fragment as bf16 hi + lo parts: hi is x rounded to bf16, lo is
+// the remainder x - hi (exact in float32) rounded to bf16, so |x - hi - lo|
+// <= 2^-17 |x|.  Three instructions per element: each pair is converted to a
+// packed bf16 word once, its halves are widened back by a shift and a mask
+// for the subtraction, and the remainders are converted as a pair.
 struct Sp4 {
   bf16x4 h, l;
 };
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 __device__ inline Sp4 split4(f32x4 x) {
-  unsigned u[4];
-  float r[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    u[i] = __float_as_uint(x[i]);
-    r[i] = x[i] - __uint_as_float(u[i] & 0xffff0000u);
-  }
+  const unsigned p01 = __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2{x[0], x[1]}), bf16x2));
+  const unsigned p23 = __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2{x[2], x[3]}), bf16x2));
+  const f32x2 r01 = f32x2{x[0] - __uint_as_float(p01 << 16), x[1] - __uint_as_float(p01 & 0xffff0000u)};
+  const f32x2 r23 = f32x2{x[2] - __uint_as_float(p23 << 16), x[3] - __uint_as_float(p23 & 0xffff0000u)};
   Sp4 s;
-  s.h = __builtin_bit_cast(bf16x4, uint2{__builtin_amdgcn_perm(u[1], u[0], 0x07060302u),
-                                         __builtin_amdgcn_perm(u[3], u[2], 0x07060302u)});
-  s.l = bf16x4{(__bf16)r[0], (__bf16)r[1], (__bf16)r[2], (__bf16)r[3]};
+  s.h = __builtin_bit_cast(bf16x4, uint2{p01, p23});
+  s.l = __builtin_bit_cast(bf16x4, uint2{__builtin_bit_cast(unsigned, __builtin_convertvector(r01, bf16x2)),
+                                         __builtin_bit_cast(unsigned, __builtin_convertvector(r23, bf16x2))});
   return s;
 }
 
