@@ -65,7 +65,7 @@ TRAFFIC_KIB = {
                        "fetch": 1391772, "write": 1591826},
     "backward": {"sources": ("chunk_bwd_bf16.hip", "chunk_bwd_bf16_states.hip", "la_bwd_bf16.h", "la_bwd.h",
                              "la_device.h", "../build.py"),
-                 "sha256_16": "4877d8e4d34356d2",
+                 "sha256_16": "5bf4829476362ab1",
                  # one call at B=4 H=16 T=8192: tile records, states + state
                  # gradients (one launch), gradients
                  "fetch": 2153326, "write": 2493887},

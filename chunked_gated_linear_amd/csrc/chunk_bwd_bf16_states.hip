@@ -36,7 +36,7 @@ struct H2Rec {
 
 template <int DK, int SPW>
 struct H2Raw {
-  uint4 kr[DK / 32];     // K row pieces (2 DK / 16 pieces per row, 16 rows, 64 lanes)
+  uint4 kr[DK / 32];     // K row pieces: lane (n, grp), piece x = columns 32 x + 8 grp .. + 7 of row n
   f32x4 ti;
   uint4 vr[Slab<SPW>::NPC];
   float g, bt, gC;
@@ -505,7 +505,8 @@ __device__ inline void dh_body(const BwdArgs& a, int64_t blk, char* smem) {
 
 // The forward states and the state gradients do not depend on each other: one
 // launch runs both, blocks [0, nblk) the first and [nblk, 2 nblk) the second,
-// so that the two serial chains share the compute units.
+// so that the two serial chains share the compute units.  Each block has SPW
+// chain waves (one per 16-column slice) and 2 NP loader waves.
 template <int DK, int NP, int SPW>
 __global__ __launch_bounds__(64 * (2 * NP + SPW)) void bwd2_states_kernel(BwdArgs a, int nblk) {
   constexpr int HB = 2 * NP * H2Rec<DK, SPW>::BYTES, DB = 2 * NP * D2Rec<DK, SPW>::BYTES;
