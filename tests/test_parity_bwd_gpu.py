@@ -78,6 +78,10 @@ CASES = [
     # d_k 64 with four slices per state block
     ("bf16", 64, 128, 1, 2, 16 * 7 + 9, "weak", "logit", 0.02, True),
     ("bf16", 64, 64, 2, 1, 200, "std", "logit", None, False),
+    # more state workgroups than compute units: 68 heads at d_v = 128 make
+    # 272 chain workgroups of one per unit, so the launch takes two rounds;
+    # 7 tiles, the last ragged (the gradient chain's empty front tile)
+    ("bf16", 128, 128, 1, 68, 16 * 6 + 4, "weak", "logit", 0.02, True),
 ]
 
 
